@@ -1,0 +1,175 @@
+/*
+ * moelora.h -- C ABI of the routed MoE expert layer with rank-r side-LoRA
+ * (forward and backward) on one AMD MI355X (gfx950).
+ *
+ * What the calls compute follows DeepGEMM PR #9 "feat(mega): add fused shared
+ * side-LoRA kernels" (section "Historical implementation": Summary and
+ * Correctness coverage) and PR #17 "Align MegaMoE training with upgraded
+ * K-grouped TMA and layouts" (Summary):
+ *   - routes are dispatched into an expert-contiguous pool, each expert padded
+ *     to BLOCK_M rows, padding rows zeroed;
+ *   - per route (t, j) with expert e and u = x_t:
+ *       g = W1_e u + s B1_e (A1 u),  v = W3_e u + s B3_e (A3 u),
+ *       h = silu(g) * v,             y = W2_e h + s B2 (A2_e h),
+ *       out_t = sum_j w[t, j] y_(t, j)
+ *     with A1, A3, B2 shared by all experts and B1, B3, A2 expert-local;
+ *   - the backward returns grad-x and the router gradients in source-token
+ *     order and the six adapter gradients (no frozen-weight gradients unless
+ *     asked for), with padding rows kept out of every reduction;
+ *   - unsupported modes and short workspaces are rejected before any launch.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, and
+ *     16-byte aligned.  bf16 is stored as uint16 bit patterns.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     keeps a pointer after a call returns.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting for the device.
+ *   - Arguments are validated on the host first.  On any error nothing is
+ *     written and no kernel is launched.
+ *   - Outputs are overwritten, never accumulated; empty experts and dropped
+ *     routes get exact zeros.
+ *   - Calls that share a workspace or outputs must be ordered on one stream.
+ */
+#ifndef MOELORA_H
+#define MOELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)     /* bad shape, pointer, alignment or pool */
+#define MOE_ERR_UNSUPPORTED (-2) /* a mode this build does not implement */
+#define MOE_ERR_WORKSPACE (-3)   /* saved/scratch buffer smaller than required */
+#define MOE_ERR_HIP (-4)         /* a HIP launch or attribute call failed */
+
+#define MOE_ACT_SWIGLU 0         /* h = silu(g) * v; other activations: UNSUPPORTED */
+#define MOE_BASE_BF16 0          /* W13 / W2 in bf16 */
+#define MOE_BASE_MXFP4 1         /* W13 / W2 as e2m1 with e8m0 scales per 32 along K */
+
+/* Shape and options of one layer call.
+ *   T tokens, H hidden, I intermediate, E local experts, topk routes per token,
+ *   rank r of the side adapters, scale s of the adapter deltas (0 => plain MoE).
+ *   block_m: pool padding granularity; 0 asks the library (see moe_lora_block_m),
+ *     otherwise one of 16, 32, 64, 96, 128, 192, 240.
+ *   activation: MOE_ACT_SWIGLU.  clamp: must be <= 0 or +inf (no clamp).
+ * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
+ *   1 <= topk <= 16, 1 <= rank <= 128.  Other values: MOE_ERR_UNSUPPORTED
+ *   (non-positive sizes: MOE_ERR_INVALID). */
+typedef struct moe_lora_desc {
+  int32_t T, H, I, E, topk, rank;
+  int32_t block_m;
+  float scale;
+  int32_t activation;
+  float clamp;
+  int32_t base_format;
+} moe_lora_desc;
+
+/* The dispatch pool written by build_pool (device int32 arrays).
+ *   counts[E]          routes per expert
+ *   offsets[E+1]       first pool row of each expert; offsets[E] = pool rows in use
+ *   route_to_row[T*k]  pool row of route f = t*k + j, -1 if dropped
+ *   row_to_route[capacity]  route of each pool row, -1 for padding and unused rows
+ *   capacity           rows of row_to_route; must equal moe_lora_pool_capacity()
+ *   block_m            the resolved BLOCK_M the pool was built with */
+typedef struct moe_pool {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* route_to_row;
+  const int32_t* row_to_route;
+  int64_t capacity;
+  int32_t block_m;
+} moe_pool;
+
+/* Layer parameters (device, bf16 unless noted; nn.Linear [out, in] layout):
+ *   W13 [E, 2I, H]  rows 0..I-1 = W1 (gate), rows I..2I-1 = W3 (up)
+ *   W2  [E, H, I]
+ *   A1, A3 [r, H]   shared;   B1, B3 [E, I, r] expert-local
+ *   A2  [E, r, I]   expert-local;   B2 [H, r] shared
+ *   W13_scale, W2_scale: e8m0 block scales for MOE_BASE_MXFP4, NULL for bf16. */
+typedef struct moe_lora_params {
+  const void* W13;
+  const void* W2;
+  const uint8_t* W13_scale;
+  const uint8_t* W2_scale;
+  const void *A1, *A3, *B1, *B3, *A2, *B2;
+} moe_lora_params;
+
+/* Gradient outputs (device bf16, same layouts as the parameters).  The six
+ * adapter gradients are required.  dW13 / dW2 are optional ("ordinary" MoE
+ * training): NULL skips them. */
+typedef struct moe_lora_grads {
+  void *dA1, *dA3, *dB1, *dB3, *dA2, *dB2;
+  void *dW13, *dW2;
+} moe_lora_grads;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_lora_status_string(moe_status status);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int32_t moe_lora_version(void);
+
+/* BLOCK_M used for `desc` (resolves block_m == 0 to the library's choice).
+ * PR #17 Summary: the block size is queried from the library, not duplicated
+ * by callers; forward and backward use the same pool. */
+moe_status moe_lora_block_m(const moe_lora_desc* desc, int32_t* block_m);
+
+/* Rows of row_to_route to allocate: T*k + min(E, T*k) * (BLOCK_M - 1), the
+ * largest pool any routing can produce. */
+moe_status moe_lora_pool_capacity(const moe_lora_desc* desc, int64_t* rows);
+
+/* Bytes of the two workspaces:
+ *   saved   -- written by moe_lora_forward, read by moe_lora_backward; holds
+ *              the gathered expert input (the saved-X reuse of PR #9,
+ *              "2026-09-20" -> What changed), the gate/up pre-activations in
+ *              fp32, the activations and the unweighted expert outputs.
+ *   scratch -- temporary space of moe_lora_backward (forward needs none). */
+moe_status moe_lora_workspace_size(const moe_lora_desc* desc, size_t* saved_bytes,
+                                   size_t* scratch_bytes);
+
+/* Build the dispatch pool from top-k expert ids (PR #9, "2026-09-21: restore
+ * wide-K wgrad safely" -> Implementation: true physical expert offsets, groups
+ * never rounded into a neighbour; "Historical implementation" -> Summary:
+ * padding zeroed).
+ *   topk_idx [T, k] int32: expert id, or -1 for a dropped route.  Ids outside
+ *     [-1, E) are dropped as well and counted into *device_error (device
+ *     int32, may be NULL), which the call overwrites.
+ *   Rows of one expert follow ascending route index t*k + j (deterministic).
+ *   counts, offsets, route_to_row, row_to_route: outputs as in moe_pool. */
+moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_t* counts,
+                      int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
+                      int64_t capacity, int32_t* device_error, void* stream);
+
+/* Forward of the layer.
+ *   x [T, H] bf16, topk_w [T, k] fp32 router weights (used as given),
+ *   out [T, H] bf16 (overwritten), saved / scratch per moe_lora_workspace_size.
+ *   `pool` must come from build_pool with the same desc and topk ids.
+ *   x, out and the workspaces must not overlap. */
+moe_status moe_lora_forward(const moe_lora_desc* desc, const moe_pool* pool, const void* x,
+                            const float* topk_w, const moe_lora_params* params, void* out,
+                            void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                            void* stream);
+
+/* Backward of the layer for L = <grad_out, out>.
+ *   grad_out [T, H] bf16; topk_w and params as given to the forward; `saved`
+ *   as the forward left it (read only, may be reused by repeated calls).
+ *   grad_x [T, H] bf16, grad_topk_w [T, k] fp32 (0 for dropped routes) and the
+ *   gradients in `grads` are overwritten.  The result is a deterministic
+ *   function of the inputs (bitwise repeatable). */
+moe_status moe_lora_backward(const moe_lora_desc* desc, const moe_pool* pool,
+                             const void* grad_out, const float* topk_w,
+                             const moe_lora_params* params, const void* saved,
+                             size_t saved_bytes, void* grad_x, float* grad_topk_w,
+                             const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOELORA_H */

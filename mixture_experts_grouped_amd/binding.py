@@ -1,0 +1,281 @@
+"""Python binding of libmoelora (ctypes).  Argument marshalling only: every
+step of the layer runs in the HIP library; PyTorch provides device memory and
+streams.  The functions carry the C ABI's names (``build_pool``,
+``moe_lora_forward``, ``moe_lora_backward``, ...); see include/moelora.h for
+the contract of each call.
+
+If the shared library is missing or fails to load, every call raises: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import build as _build
+
+LIB_PATH = _build.OUT
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ACT_SWIGLU = 0
+MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
+
+EXPORTS = (
+    "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
+    "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_backward",
+)
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} ({status})")
+
+
+class MoeLoraDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("activation", ctypes.c_int32), ("clamp", ctypes.c_float),
+                ("base_format", ctypes.c_int32)]
+
+
+class MoePool(ctypes.Structure):
+    _fields_ = [("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("route_to_row", ctypes.c_void_p), ("row_to_route", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64), ("block_m", ctypes.c_int32)]
+
+
+class MoeLoraParams(ctypes.Structure):
+    _fields_ = [("W13", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("W13_scale", ctypes.c_void_p), ("W2_scale", ctypes.c_void_p),
+                ("A1", ctypes.c_void_p), ("A3", ctypes.c_void_p), ("B1", ctypes.c_void_p),
+                ("B3", ctypes.c_void_p), ("A2", ctypes.c_void_p), ("B2", ctypes.c_void_p)]
+
+
+class MoeLoraGrads(ctypes.Structure):
+    _fields_ = [("dA1", ctypes.c_void_p), ("dA3", ctypes.c_void_p), ("dB1", ctypes.c_void_p),
+                ("dB3", ctypes.c_void_p), ("dA2", ctypes.c_void_p), ("dB2", ctypes.c_void_p),
+                ("dW13", ctypes.c_void_p), ("dW2", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmoelora (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmoelora is not built ({p} missing): run "
+                           "python -m mixture_experts_grouped_amd.build")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.moe_lora_status_string.argtypes = [ctypes.c_int32]
+    lib.moe_lora_status_string.restype = ctypes.c_char_p
+    lib.moe_lora_version.argtypes = []
+    lib.moe_lora_version.restype = ctypes.c_int32
+    lib.moe_lora_block_m.argtypes = [P(MoeLoraDesc), P(ctypes.c_int32)]
+    lib.moe_lora_pool_capacity.argtypes = [P(MoeLoraDesc), P(ctypes.c_int64)]
+    lib.moe_lora_workspace_size.argtypes = [P(MoeLoraDesc), P(ctypes.c_size_t), P(ctypes.c_size_t)]
+    lib.build_pool.argtypes = [P(MoeLoraDesc), vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp]
+    lib.moe_lora_forward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
+                                     vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_backward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
+                                      ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
+                                      ctypes.c_size_t, vp]
+    for fn in ("moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
+               "build_pool", "moe_lora_forward", "moe_lora_backward"):
+        getattr(lib, fn).restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return library().moe_lora_status_string(status).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "status"
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        raise MoeLoraError(status, what)
+
+
+def make_desc(T: int, H: int, I: int, E: int, topk: int, rank: int, scale: float = 1.0,
+              block_m: int = 0, activation: int = MOE_ACT_SWIGLU, clamp: float = 0.0,
+              base_format: int = MOE_BASE_BF16) -> MoeLoraDesc:
+    return MoeLoraDesc(T, H, I, E, topk, rank, block_m, scale, activation, clamp, base_format)
+
+
+def moe_lora_block_m(desc: MoeLoraDesc) -> int:
+    v = ctypes.c_int32()
+    _check(library().moe_lora_block_m(ctypes.byref(desc), ctypes.byref(v)), "moe_lora_block_m")
+    return v.value
+
+
+def moe_lora_pool_capacity(desc: MoeLoraDesc) -> int:
+    v = ctypes.c_int64()
+    _check(library().moe_lora_pool_capacity(ctypes.byref(desc), ctypes.byref(v)),
+           "moe_lora_pool_capacity")
+    return v.value
+
+
+def moe_lora_workspace_size(desc: MoeLoraDesc) -> Tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(library().moe_lora_workspace_size(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(b)),
+           "moe_lora_workspace_size")
+    return a.value, b.value
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, shape=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def build_pool(desc: MoeLoraDesc, topk_idx: torch.Tensor, counts: torch.Tensor,
+               offsets: torch.Tensor, route_to_row: torch.Tensor, row_to_route: torch.Tensor,
+               device_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, k, E = desc.T, desc.topk, desc.E
+    cap = row_to_route.numel()
+    i32 = torch.int32
+    st = library().build_pool(
+        ctypes.byref(desc), _ptr(topk_idx, i32, (T, k), "topk_idx"), _ptr(counts, i32, (E,), "counts"),
+        _ptr(offsets, i32, (E + 1,), "offsets"), _ptr(route_to_row, i32, (T * k,), "route_to_row"),
+        _ptr(row_to_route, i32, (cap,), "row_to_route"), cap,
+        _ptr(device_error, i32, (1,), "device_error"), _stream(stream))
+    _check(st, "build_pool")
+
+
+def _pool_struct(pool: Dict[str, torch.Tensor], bm: int) -> MoePool:
+    return MoePool(pool["counts"].data_ptr(), pool["offsets"].data_ptr(),
+                   pool["route_to_row"].data_ptr(), pool["row_to_route"].data_ptr(),
+                   pool["row_to_route"].numel(), bm)
+
+
+def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraParams:
+    E, H, I, r = desc.E, desc.H, desc.I, desc.rank
+    bf = torch.bfloat16
+    shapes = {"W13": (E, 2 * I, H), "W2": (E, H, I), "A1": (r, H), "A3": (r, H),
+              "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I), "B2": (H, r)}
+    ptrs = {n: _ptr(p[n], bf, s, n) for n, s in shapes.items()}
+    return MoeLoraParams(ptrs["W13"], ptrs["W2"], None, None, ptrs["A1"], ptrs["A3"], ptrs["B1"],
+                         ptrs["B3"], ptrs["A2"], ptrs["B2"])
+
+
+def moe_lora_forward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], x: torch.Tensor,
+                     topk_w: torch.Tensor, params: Dict[str, torch.Tensor], out: torch.Tensor,
+                     saved: torch.Tensor, scratch: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    T, H, k = desc.T, desc.H, desc.topk
+    bm = moe_lora_block_m(desc)
+    ps = _pool_struct(pool, bm)
+    pp = _params_struct(params, desc)
+    st = library().moe_lora_forward(
+        ctypes.byref(desc), ctypes.byref(ps), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(pp),
+        _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(saved, torch.uint8, None, "saved"),
+        saved.numel(), _ptr(scratch, torch.uint8, None, "scratch"),
+        0 if scratch is None else scratch.numel(), _stream(stream))
+    _check(st, "moe_lora_forward")
+
+
+def moe_lora_backward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], grad_out: torch.Tensor,
+                      topk_w: torch.Tensor, params: Dict[str, torch.Tensor], saved: torch.Tensor,
+                      grad_x: torch.Tensor, grad_topk_w: torch.Tensor,
+                      grads: Dict[str, torch.Tensor], scratch: torch.Tensor, stream=None) -> None:
+    T, H, I, E, k, r = desc.T, desc.H, desc.I, desc.E, desc.topk, desc.rank
+    bm = moe_lora_block_m(desc)
+    ps = _pool_struct(pool, bm)
+    pp = _params_struct(params, desc)
+    bf = torch.bfloat16
+    gshape = {"dA1": (r, H), "dA3": (r, H), "dB1": (E, I, r), "dB3": (E, I, r),
+              "dA2": (E, r, I), "dB2": (H, r), "dW13": (E, 2 * I, H), "dW2": (E, H, I)}
+    gp = {n: _ptr(grads.get(n), bf, s, n) for n, s in gshape.items()}
+    gs = MoeLoraGrads(gp["dA1"], gp["dA3"], gp["dB1"], gp["dB3"], gp["dA2"], gp["dB2"],
+                      gp["dW13"], gp["dW2"])
+    st = library().moe_lora_backward(
+        ctypes.byref(desc), ctypes.byref(ps), _ptr(grad_out, bf, (T, H), "grad_out"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(pp),
+        _ptr(saved, torch.uint8, None, "saved"), saved.numel(),
+        _ptr(grad_x, bf, (T, H), "grad_x"), _ptr(grad_topk_w, torch.float32, (T, k), "grad_topk_w"),
+        ctypes.byref(gs), _ptr(scratch, torch.uint8, None, "scratch"), scratch.numel(),
+        _stream(stream))
+    _check(st, "moe_lora_backward")
+
+
+class MoeLoraLayer:
+    """Device buffers for one layer shape (pool arrays, workspaces, outputs)
+    and the three calls in order.  Convenience for tests and the benchmark."""
+
+    def __init__(self, desc: MoeLoraDesc, device="cuda"):
+        self.desc = desc
+        self.device = device
+        self.block_m = moe_lora_block_m(desc)
+        self.capacity = moe_lora_pool_capacity(desc)
+        self.saved_bytes, self.scratch_bytes = moe_lora_workspace_size(desc)
+        T, H, I, E, k, r = desc.T, desc.H, desc.I, desc.E, desc.topk, desc.rank
+        i32 = torch.int32
+        self.pool = {
+            "counts": torch.empty(E, dtype=i32, device=device),
+            "offsets": torch.empty(E + 1, dtype=i32, device=device),
+            "route_to_row": torch.empty(T * k, dtype=i32, device=device),
+            "row_to_route": torch.empty(self.capacity, dtype=i32, device=device),
+        }
+        self.device_error = torch.empty(1, dtype=i32, device=device)
+        self.saved = torch.empty(self.saved_bytes, dtype=torch.uint8, device=device)
+        self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+        bf = torch.bfloat16
+        self.out = torch.empty(T, H, dtype=bf, device=device)
+        self.grad_x = torch.empty(T, H, dtype=bf, device=device)
+        self.grad_topk_w = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.grads = {
+            "dA1": torch.empty(r, H, dtype=bf, device=device),
+            "dA3": torch.empty(r, H, dtype=bf, device=device),
+            "dB1": torch.empty(E, I, r, dtype=bf, device=device),
+            "dB3": torch.empty(E, I, r, dtype=bf, device=device),
+            "dA2": torch.empty(E, r, I, dtype=bf, device=device),
+            "dB2": torch.empty(H, r, dtype=bf, device=device),
+        }
+
+    def build_pool(self, topk_idx: torch.Tensor, stream=None) -> None:
+        build_pool(self.desc, topk_idx, self.pool["counts"], self.pool["offsets"],
+                   self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
+
+    def forward(self, x, topk_w, params, stream=None) -> torch.Tensor:
+        moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, None, stream)
+        return self.out
+
+    def backward(self, grad_out, topk_w, params, stream=None):
+        moe_lora_backward(self.desc, self.pool, grad_out, topk_w, params, self.saved,
+                          self.grad_x, self.grad_topk_w, self.grads, self.scratch, stream)
+        return self.grad_x, self.grad_topk_w, self.grads
+
+    def step(self, topk_idx, x, topk_w, params, grad_out, stream=None):
+        """One pass of the whole path: pool, forward, backward."""
+        self.build_pool(topk_idx, stream)
+        self.forward(x, topk_w, params, stream)
+        return self.backward(grad_out, topk_w, params, stream)

@@ -1,0 +1,307 @@
+// api.hip -- the C ABI of libmoelora: host-side validation, workspace plan and
+// launch order.  All checks run before any device work; on error nothing is
+// launched and nothing is written.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moelora.h"
+#include "layer.hpp"
+
+using namespace moelora;
+
+namespace {
+
+constexpr int kVersion = 100;
+constexpr int kBlockMs[] = {16, 32, 64, 96, 128, 192, 240};
+constexpr int kSharedSplit = 1024;  // tokens per split of the shared-factor reductions
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+moe_status check_desc(const moe_lora_desc* d) {
+  if (d == nullptr) return MOE_ERR_INVALID;
+  if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->topk < 1 || d->rank < 1)
+    return MOE_ERR_INVALID;
+  if (!std::isfinite(d->scale)) return MOE_ERR_INVALID;
+  if (d->block_m != 0) {
+    bool ok = false;
+    for (int b : kBlockMs) ok |= (b == d->block_m);
+    if (!ok) return MOE_ERR_INVALID;
+  }
+  if (d->H % 256 != 0 || d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->E > 512 || d->topk > 16 || d->rank > 128 || d->rank % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (!(d->clamp <= 0.0f || std::isinf(d->clamp))) return MOE_ERR_UNSUPPORTED;
+  if (d->base_format != MOE_BASE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int64_t routes = (int64_t)d->T * d->topk;
+  const int64_t cap = routes + std::min<int64_t>(d->E, routes) * 239;
+  if (cap >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int resolve_bm(const moe_lora_desc* d) {
+  // The grouped-GEMM tiles start at each expert's first row and mask at its
+  // count, so BLOCK_M changes only the padding; the smallest value wastes least.
+  return d->block_m != 0 ? d->block_m : 16;
+}
+
+int64_t capacity_of(const moe_lora_desc* d, int bm) {
+  const int64_t routes = (int64_t)d->T * d->topk;
+  return routes + std::min<int64_t>(d->E, routes) * (bm - 1);
+}
+
+struct Plan {
+  int64_t cap;
+  int maxtiles, nsplit;
+  size_t saved, scratch;
+  // byte offsets
+  size_t o_tiles, o_ntiles, o_Xp, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
+  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part;
+};
+
+Plan make_plan(const moe_lora_desc* d) {
+  Plan p{};
+  const int bm = resolve_bm(d);
+  p.cap = capacity_of(d, bm);
+  const int64_t routes = (int64_t)d->T * d->topk;
+  p.maxtiles = (int)((routes + TMG - 1) / TMG + std::min<int64_t>(d->E, routes));
+  p.nsplit = (d->T + kSharedSplit - 1) / kSharedSplit;
+  const size_t T = d->T, H = d->H, I = d->I, r = d->rank, cap = (size_t)p.cap;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
+  p.o_tiles = take(sizeof(TileInfo) * p.maxtiles);
+  p.o_ntiles = take(sizeof(int));
+  p.o_Xp = take(cap * H * 2);
+  p.o_ZA = take(T * 4 * r * 2);
+  p.o_G = take(cap * I * 4);
+  p.o_V = take(cap * I * 4);
+  p.o_Hh = take(cap * I * 2);
+  p.o_Z2 = take(cap * r * 4);
+  p.o_Yb = take(cap * H * 2);
+  p.o_zc = take(T * 2 * r * 2);
+  p.saved = o;
+  o = 0;
+  p.o_q = take(T * r * 4);
+  p.o_sq = take(T * 2 * r * 2);
+  p.o_wsq = take(cap * 2 * r * 2);
+  p.o_dGV = take(cap * 2 * I * 2);
+  p.o_dU = take(cap * H * 2);
+  p.o_P = take(cap * 2 * r * 4);
+  p.o_pc = take(T * 4 * r * 2);
+  p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
+  p.scratch = o;
+  return p;
+}
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+moe_status check_pool(const moe_lora_desc* d, const moe_pool* pool, const Plan& p) {
+  if (pool == nullptr || pool->counts == nullptr || pool->offsets == nullptr ||
+      pool->route_to_row == nullptr || pool->row_to_route == nullptr)
+    return MOE_ERR_INVALID;
+  if (pool->block_m != resolve_bm(d) || pool->capacity != p.cap) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status check_params(const moe_lora_params* w) {
+  if (w == nullptr) return MOE_ERR_INVALID;
+  const void* ps[] = {w->W13, w->W2, w->A1, w->A3, w->B1, w->B3, w->A2, w->B2};
+  for (const void* q : ps)
+    if (!aligned16(q)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, const Plan& p,
+                 const moe_lora_params* w) {
+  std::memset(&a, 0, sizeof(a));
+  a.T = d->T;
+  a.H = d->H;
+  a.I = d->I;
+  a.E = d->E;
+  a.k = d->topk;
+  a.r = d->rank;
+  a.s = d->scale;
+  a.cap = p.cap;
+  a.maxtiles = p.maxtiles;
+  a.nsplit = p.nsplit;
+  a.kspl = kSharedSplit;
+  a.counts = pool->counts;
+  a.offsets = pool->offsets;
+  a.r2row = pool->route_to_row;
+  a.row2r = pool->row_to_route;
+  a.W13 = (const uint16_t*)w->W13;
+  a.W2 = (const uint16_t*)w->W2;
+  a.A1 = (const uint16_t*)w->A1;
+  a.A3 = (const uint16_t*)w->A3;
+  a.B1 = (const uint16_t*)w->B1;
+  a.B3 = (const uint16_t*)w->B3;
+  a.A2 = (const uint16_t*)w->A2;
+  a.B2 = (const uint16_t*)w->B2;
+}
+
+void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
+  char* b = (char*)saved;
+  a.tiles = (TileInfo*)(b + p.o_tiles);
+  a.ntiles = (int*)(b + p.o_ntiles);
+  a.Xp = (uint16_t*)(b + p.o_Xp);
+  a.ZA = (uint16_t*)(b + p.o_ZA);
+  a.G = (float*)(b + p.o_G);
+  a.V = (float*)(b + p.o_V);
+  a.Hh = (uint16_t*)(b + p.o_Hh);
+  a.Z2 = (float*)(b + p.o_Z2);
+  a.Yb = (uint16_t*)(b + p.o_Yb);
+  a.zc = (uint16_t*)(b + p.o_zc);
+}
+
+void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
+  char* b = (char*)scratch;
+  a.q = (float*)(b + p.o_q);
+  a.sq = (uint16_t*)(b + p.o_sq);
+  a.wsq = (uint16_t*)(b + p.o_wsq);
+  a.dGV = (uint16_t*)(b + p.o_dGV);
+  a.dU = (uint16_t*)(b + p.o_dU);
+  a.P = (float*)(b + p.o_P);
+  a.pc = (uint16_t*)(b + p.o_pc);
+  a.part = (float*)(b + p.o_part);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_lora_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported option";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_lora_version(void) { return kVersion; }
+
+moe_status moe_lora_block_m(const moe_lora_desc* d, int32_t* block_m) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (block_m == nullptr) return MOE_ERR_INVALID;
+  *block_m = resolve_bm(d);
+  return MOE_OK;
+}
+
+moe_status moe_lora_pool_capacity(const moe_lora_desc* d, int64_t* rows) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (rows == nullptr) return MOE_ERR_INVALID;
+  *rows = capacity_of(d, resolve_bm(d));
+  return MOE_OK;
+}
+
+moe_status moe_lora_workspace_size(const moe_lora_desc* d, size_t* saved_bytes,
+                                   size_t* scratch_bytes) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (saved_bytes == nullptr || scratch_bytes == nullptr) return MOE_ERR_INVALID;
+  const Plan p = make_plan(d);
+  *saved_bytes = p.saved;
+  *scratch_bytes = p.scratch;
+  return MOE_OK;
+}
+
+moe_status build_pool(const moe_lora_desc* d, const int32_t* topk_idx, int32_t* counts,
+                      int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
+                      int64_t capacity, int32_t* device_error, void* stream) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (topk_idx == nullptr || counts == nullptr || offsets == nullptr || route_to_row == nullptr ||
+      row_to_route == nullptr)
+    return MOE_ERR_INVALID;
+  const int bm = resolve_bm(d);
+  if (capacity != capacity_of(d, bm)) return MOE_ERR_INVALID;
+  const hipError_t e = launch_build_pool(topk_idx, d->T * d->topk, d->E, bm, capacity, counts,
+                                         offsets, route_to_row, row_to_route, device_error,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const void* x,
+                            const float* topk_w, const moe_lora_params* params, void* out,
+                            void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                            void* stream) {
+  (void)scratch;
+  (void)scratch_bytes;
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(d);
+  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
+  if ((st = check_params(params)) != MOE_OK) return st;
+  if (params->W13_scale != nullptr || params->W2_scale != nullptr) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
+    return MOE_ERR_INVALID;
+  if (saved_bytes < p.saved) return MOE_ERR_WORKSPACE;
+  const size_t act = (size_t)d->T * d->H * 2;
+  const Range rx = rng(x, act), ro = rng(out, act), rs = rng(saved, p.saved);
+  if (overlap(rx, ro) || overlap(ro, rs) || overlap(rx, rs)) return MOE_ERR_INVALID;
+  LayerArgs a;
+  fill_common(a, d, pool, p, params);
+  fill_saved(a, p, saved);
+  a.x = (const uint16_t*)x;
+  a.w = topk_w;
+  a.out = (uint16_t*)out;
+  const hipError_t e = launch_forward(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
+                             const void* grad_out, const float* topk_w,
+                             const moe_lora_params* params, const void* saved,
+                             size_t saved_bytes, void* grad_x, float* grad_topk_w,
+                             const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
+                             void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(d);
+  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
+  if ((st = check_params(params)) != MOE_OK) return st;
+  if (params->W13_scale != nullptr || params->W2_scale != nullptr) return MOE_ERR_INVALID;
+  if (!aligned16(grad_out) || !aligned16(grad_x) || !aligned16(saved) || !aligned16(scratch) ||
+      topk_w == nullptr || grad_topk_w == nullptr || grads == nullptr)
+    return MOE_ERR_INVALID;
+  const void* gs[] = {grads->dA1, grads->dA3, grads->dB1, grads->dB3, grads->dA2, grads->dB2};
+  for (const void* g : gs)
+    if (!aligned16(g)) return MOE_ERR_INVALID;
+  if (grads->dW13 != nullptr || grads->dW2 != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (saved_bytes < p.saved || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
+  const size_t act = (size_t)d->T * d->H * 2;
+  const Range rgo = rng(grad_out, act), rgx = rng(grad_x, act), rs = rng(saved, p.saved),
+              rsc = rng(scratch, p.scratch);
+  if (overlap(rgo, rgx) || overlap(rgx, rs) || overlap(rgx, rsc) || overlap(rs, rsc) ||
+      overlap(rgo, rsc))
+    return MOE_ERR_INVALID;
+  LayerArgs a;
+  fill_common(a, d, pool, p, params);
+  fill_saved(a, p, const_cast<void*>(saved));
+  fill_scratch(a, p, scratch);
+  a.go = (const uint16_t*)grad_out;
+  a.w = topk_w;
+  a.gx = (uint16_t*)grad_x;
+  a.gw = grad_topk_w;
+  a.dA1 = (uint16_t*)grads->dA1;
+  a.dA3 = (uint16_t*)grads->dA3;
+  a.dB1 = (uint16_t*)grads->dB1;
+  a.dB3 = (uint16_t*)grads->dB3;
+  a.dA2 = (uint16_t*)grads->dA2;
+  a.dB2 = (uint16_t*)grads->dB2;
+  const hipError_t e = launch_backward(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,568 @@
+// backward.hip -- backward of the MoE side-LoRA expert layer.
+//
+// DeepGEMM PR #9, "Historical implementation" -> Summary: the backward
+// returns grad-x, router gradients and the six adapter gradients (no frozen
+// weight gradients, no full-width side-delta scratch); padding never enters
+// the shared reductions.  Steps:
+//   k_q             q_t = B2^T go_t, once per token (B2 is shared)
+//   k_dw            grad_w[t,j] = <go_t, Ybase> + <q_t, Z2>  (= <go_t, y>),
+//                   and s w q_t per route for dA2
+//   k_w2dgrad       dh = w (W2_e^T go_t + A2_e^T s q_t) (K-extended), then
+//                   the SwiGLU backward from the saved fp32 G, V
+//   k_w13dgrad      dU = W1_e^T dg + W3_e^T dv
+//   k_p13           P = [B1_e^T dg ; B3_e^T dv]
+//   k_pc            pc_t = s sum_j P_(t,j)
+//   k_dx            grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
+//   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
+//   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
+//   k_reduce_shared fixed-order sum of the split-K partials
+#include "layer.hpp"
+
+namespace moelora {
+
+using G256 = Geo<4, 4, 2, 2>;
+using G128 = Geo<4, 2, 2, 2>;
+
+// ----------------------------------------------------------------------------
+// a8: q = B2^T go per token, router gradients
+// ----------------------------------------------------------------------------
+struct LdQ {
+  RowsK<256> m;
+  TransK<128, KStrided> n;
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_q(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int t0 = blockIdx.x * 256;
+  const int r = a.r;
+  LdQ L;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + RowsK<256>::row_of(i);
+    L.m.rp[i] = (t < a.T) ? a.go + (long)t * a.H : nullptr;
+    L.m.lo[i] = 0;
+  }
+  L.m.span = a.H;
+  L.m.period = 0;
+  L.n.kp = KStrided{a.B2, r, 0, a.H, 0};
+  L.n.n0 = 0;
+  L.n.nvalid = r;
+  L.n.hilo_half = 0;
+  L.n.lo_off = 0;
+  f32x16 acc[G128::NB][G128::MB];
+  mainloop<G128>(L, a.H / KT, 1 << 30, acc, smem);
+  Epi<G128> ep;
+#pragma unroll
+  for (int mb = 0; mb < G128::MB; ++mb) {
+    const int t = t0 + ep.row(mb);
+    if (t >= a.T) continue;
+#pragma unroll
+    for (int nb = 0; nb < G128::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= r) continue;
+        f32x4 v;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[nb][mb][4 * g + q];
+          split_hl(a.s * v[q], hi[q], lo[q]);
+        }
+        *(f32x4*)(a.q + (long)t * r + c) = v;
+        uint16_t* d = a.sq + (long)t * 2 * r + c;
+        *(u32x2*)d = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *(u32x2*)(d + r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      }
+  }
+}
+
+// one wave per route (t, j)
+__global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
+  const long f = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (f >= (long)a.T * a.k) return;
+  const int t = (int)(f / a.k);
+  const int row = a.r2row[f];
+  if (row < 0) {
+    if (lane == 0) a.gw[f] = 0.0f;
+    return;
+  }
+  const u32x4* gp = (const u32x4*)(a.go + (long)t * a.H);
+  const u32x4* yp = (const u32x4*)(a.Yb + (long)row * a.H);
+  float acc = 0.0f;
+  for (int c = lane; c < a.H / 8; c += 64) {
+    const u32x4 g = gp[c], y = yp[c];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc += bf2f(g[d] & 0xffffu) * bf2f(y[d] & 0xffffu);
+      acc += bf2f(g[d] >> 16) * bf2f(y[d] >> 16);
+    }
+  }
+  const float wr = a.w[f];
+  for (int c = lane; c < a.r; c += 64) {
+    const float qv = a.q[(long)t * a.r + c];
+    acc += qv * a.Z2[(long)row * a.r + c];
+    uint32_t hi, lo;
+    split_hl(a.s * wr * qv, hi, lo);
+    a.wsq[(long)row * 2 * a.r + c] = (uint16_t)hi;
+    a.wsq[(long)row * 2 * a.r + a.r + c] = (uint16_t)lo;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) a.gw[f] = acc;
+}
+
+// ----------------------------------------------------------------------------
+// a9: dh = w (W2_e^T go + A2_e^T s q), SwiGLU backward -> dG, dV
+// ----------------------------------------------------------------------------
+struct LdW2d {
+  RowsK<256> m;
+  TransK<256, KStrided> n;
+  int nmain, r, topk, row0, row_end;
+  const int32_t* row2r;
+  const uint16_t* sq;
+  const uint16_t* A2e;
+  long ldn;
+  __device__ void load(int s) {
+    if (s < nmain) {
+      m.load(s * KT, 0, false);
+      n.load(s * KT);
+      return;
+    }
+    if (s == nmain) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const long row = row0 + RowsK<256>::row_of(i);
+        m.rp[i] = (row < row_end) ? sq + (long)(row2r[row] / topk) * 2 * r : nullptr;
+      }
+      m.span = 2 * r;
+      n.kp = KStrided{A2e, ldn, 0, 2 * r, r};
+    }
+    const int se = s - nmain;
+    m.load(se * KT, 0, false);
+    n.load(se * KT);
+  }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_w2dgrad(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int ntn = a.I / 256;
+  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (mt >= *a.ntiles) return;
+  const TileInfo ti = a.tiles[mt];
+  const int i0 = nt * 256;
+  LdW2d L;
+  L.r = a.r;
+  L.topk = a.k;
+  L.row0 = ti.row0;
+  L.row_end = ti.row_end;
+  L.row2r = a.row2r;
+  L.sq = a.sq;
+  L.A2e = a.A2 + (long)ti.e * a.r * a.I;
+  L.ldn = a.I;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long row = ti.row0 + RowsK<256>::row_of(i);
+    L.m.rp[i] = (row < ti.row_end) ? a.go + (long)(a.row2r[row] / a.k) * a.H : nullptr;
+    L.m.lo[i] = 0;
+  }
+  L.m.span = a.H;
+  L.m.period = 0;
+  L.n.kp = KStrided{a.W2 + (long)ti.e * a.H * a.I, a.I, 0, a.H, 0};
+  L.n.n0 = i0;
+  L.n.nvalid = 256;
+  L.n.hilo_half = 0;
+  L.n.lo_off = 0;
+  L.nmain = a.H / KT;
+  const int next = (2 * a.r + KT - 1) / KT;
+  f32x16 acc[G256::NB][G256::MB];
+  mainloop<G256>(L, L.nmain + next, 1 << 30, acc, smem);
+  Epi<G256> ep;
+#pragma unroll
+  for (int mb = 0; mb < G256::MB; ++mb) {
+    const long row = ti.row0 + ep.row(mb);
+    if (row >= ti.row_end) continue;
+    const float wr = a.w[a.row2r[row]];
+#pragma unroll
+    for (int nb = 0; nb < G256::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = i0 + ep.col(nb, g);
+        const f32x4 gg = *(const f32x4*)(a.G + row * a.I + i);
+        const f32x4 vv = *(const f32x4*)(a.V + row * a.I + i);
+        uint32_t dgb[4], dvb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dh = wr * acc[nb][mb][4 * g + q];
+          const float sg = sigmoidf_(gg[q]);
+          const float dg = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          const float dv = dh * gg[q] * sg;
+          dgb[q] = f2bf(dg);
+          dvb[q] = f2bf(dv);
+        }
+        uint16_t* d = a.dGV + row * 2 * a.I + i;
+        *(u32x2*)d = u32x2{dgb[0] | (dgb[1] << 16), dgb[2] | (dgb[3] << 16)};
+        *(u32x2*)(d + a.I) = u32x2{dvb[0] | (dvb[1] << 16), dvb[2] | (dvb[3] << 16)};
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// a10: dU = W13_e^T [dg; dv]   (K = 2I, weights read K-outer)
+// ----------------------------------------------------------------------------
+struct LdW13d {
+  RowsK<256> m;
+  TransK<256, KStrided> n;
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_w13dgrad(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int ntn = a.H / 256;
+  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (mt >= *a.ntiles) return;
+  const TileInfo ti = a.tiles[mt];
+  const int h0 = nt * 256;
+  LdW13d L;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long row = ti.row0 + RowsK<256>::row_of(i);
+    L.m.rp[i] = (row < ti.row_end) ? a.dGV + row * 2 * a.I : nullptr;
+    L.m.lo[i] = 0;
+  }
+  L.m.span = 2 * a.I;
+  L.m.period = 0;
+  L.n.kp = KStrided{a.W13 + (long)ti.e * 2 * a.I * a.H, a.H, 0, 2 * a.I, 0};
+  L.n.n0 = h0;
+  L.n.nvalid = 256;
+  L.n.hilo_half = 0;
+  L.n.lo_off = 0;
+  f32x16 acc[G256::NB][G256::MB];
+  mainloop<G256>(L, 2 * a.I / KT, 1 << 30, acc, smem);
+  Epi<G256> ep;
+#pragma unroll
+  for (int mb = 0; mb < G256::MB; ++mb) {
+    const long row = ti.row0 + ep.row(mb);
+    if (row >= ti.row_end) continue;
+#pragma unroll
+    for (int nb = 0; nb < G256::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int h = h0 + ep.col(nb, g);
+        u32x2 o = {pack2(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1]),
+                   pack2(acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3])};
+        *(u32x2*)(a.dU + row * a.H + h) = o;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// a11: P1 = B1_e^T dg, P3 = B3_e^T dv   (blockIdx.y selects)
+// ----------------------------------------------------------------------------
+struct LdP {
+  RowsK<256> m;
+  TransK<128, KStrided> n;
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int mt = blockIdx.x, which = blockIdx.y;
+  if (mt >= *a.ntiles) return;
+  const TileInfo ti = a.tiles[mt];
+  const int r = a.r;
+  LdP L;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long row = ti.row0 + RowsK<256>::row_of(i);
+    L.m.rp[i] = (row < ti.row_end) ? a.dGV + row * 2 * a.I + which * a.I : nullptr;
+    L.m.lo[i] = 0;
+  }
+  L.m.span = a.I;
+  L.m.period = 0;
+  const uint16_t* Be = (which ? a.B3 : a.B1) + (long)ti.e * a.I * r;
+  L.n.kp = KStrided{Be, r, 0, a.I, 0};
+  L.n.n0 = 0;
+  L.n.nvalid = r;
+  L.n.hilo_half = 0;
+  L.n.lo_off = 0;
+  f32x16 acc[G128::NB][G128::MB];
+  mainloop<G128>(L, a.I / KT, 1 << 30, acc, smem);
+  Epi<G128> ep;
+#pragma unroll
+  for (int mb = 0; mb < G128::MB; ++mb) {
+    const long row = ti.row0 + ep.row(mb);
+    if (row >= ti.row_end) continue;
+#pragma unroll
+    for (int nb = 0; nb < G128::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= r) continue;
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[nb][mb][4 * g + q];
+        *(f32x4*)(a.P + row * 2 * r + which * r + c) = v;
+      }
+  }
+}
+
+// pc_t = s * sum_j P_(t,j), written as hi/lo [pc1 hi | pc1 lo | pc3 hi | pc3 lo]
+__global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int r2 = 2 * a.r;
+  if (i >= (long)a.T * r2) return;
+  const int t = (int)(i / r2), c = (int)(i % r2);
+  float z = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    const int row = a.r2row[t * a.k + j];
+    if (row >= 0) z += a.P[(long)row * r2 + c];
+  }
+  uint32_t hi, lo;
+  split_hl(a.s * z, hi, lo);
+  const int fac = c / a.r, cc = c - fac * a.r;
+  uint16_t* d = a.pc + (long)t * 4 * a.r + fac * 2 * a.r + cc;
+  d[0] = (uint16_t)hi;
+  d[a.r] = (uint16_t)lo;
+}
+
+// ----------------------------------------------------------------------------
+// a12: grad_x = [A1; A3]^T pc + sum_j dU
+// ----------------------------------------------------------------------------
+struct LdDx {
+  RowsK<256> m;
+  TransK<256, KTwoMats> n;
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_dx(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int t0 = blockIdx.x * 256, h0 = blockIdx.y * 256;
+  const int r = a.r;
+  LdDx L;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + RowsK<256>::row_of(i);
+    L.m.rp[i] = (t < a.T) ? a.pc + (long)t * 4 * r : nullptr;
+    L.m.lo[i] = 0;
+  }
+  L.m.span = 4 * r;
+  L.m.period = 0;
+  L.n.kp = KTwoMats{a.A1, a.A3, a.H, r};
+  L.n.n0 = h0;
+  L.n.nvalid = 256;
+  L.n.hilo_half = 0;
+  L.n.lo_off = 0;
+  f32x16 acc[G256::NB][G256::MB];
+  mainloop<G256>(L, (4 * r + KT - 1) / KT, 1 << 30, acc, smem);
+  Epi<G256> ep;
+#pragma unroll
+  for (int mb = 0; mb < G256::MB; ++mb) {
+    const int t = t0 + ep.row(mb);
+    if (t >= a.T) continue;
+#pragma unroll
+    for (int nb = 0; nb < G256::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int h = h0 + ep.col(nb, g);
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = acc[nb][mb][4 * g + q];
+        for (int j = 0; j < a.k; ++j) {
+          const int row = a.r2row[t * a.k + j];
+          if (row < 0) continue;
+          const u32x2 u = *(const u32x2*)(a.dU + (long)row * a.H + h);
+          o[0] += bf2f(u[0] & 0xffffu);
+          o[1] += bf2f(u[0] >> 16);
+          o[2] += bf2f(u[1] & 0xffffu);
+          o[3] += bf2f(u[1] >> 16);
+        }
+        u32x2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+        *(u32x2*)(a.gx + (long)t * a.H + h) = ov;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// a13: expert-local adapter gradients, contracted over each expert's rows.
+//   which 0: dB1_e[i][c] = sum_rows dg[row][i] * (s A1 u)[c]
+//   which 1: dB3_e[i][c] = sum_rows dv[row][i] * (s A3 u)[c]
+//   which 2: dA2_e[c][i] = sum_rows (s w q)[c] * h[row][i]
+// K tiles start at the expert's first row and rows past its count read zero,
+// so the sum never touches another expert and does not depend on BLOCK_M.
+// The rank-r operand is hi/lo split along N (columns c and c + 128); the two
+// halves are added in the epilogue.  An expert with no rows writes zeros.
+// ----------------------------------------------------------------------------
+struct LdWg {
+  TransK<256, KRows> m, n;
+  __device__ void load(int s) { m.load(s * KT); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+__global__ __launch_bounds__(256) void k_wgrad_local(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int nti = a.I / 256;
+  const int e = blockIdx.x / nti, i0 = (blockIdx.x % nti) * 256, which = blockIdx.y;
+  const int r = a.r;
+  const int ne = a.counts[e], off = a.offsets[e];
+  LdWg L;
+  if (which < 2)
+    L.m.kp = KRows{a.dGV + which * a.I, 2L * a.I, nullptr, 1, off, ne, 0};
+  else
+    L.m.kp = KRows{a.Hh, (long)a.I, nullptr, 1, off, ne, 0};
+  L.m.n0 = i0;
+  L.m.nvalid = 256;
+  L.m.hilo_half = 0;
+  L.m.lo_off = 0;
+  if (which < 2) {
+    L.n.kp = KRows{a.ZA, 4L * r, a.row2r, a.k, off, ne, 1};
+    L.n.n0 = which * 2 * r;
+  } else {
+    L.n.kp = KRows{a.wsq, 2L * r, nullptr, 1, off, ne, 0};
+    L.n.n0 = 0;
+  }
+  L.n.nvalid = r;
+  L.n.hilo_half = 128;
+  L.n.lo_off = r;
+  f32x16 acc[G256::NB][G256::MB];
+  mainloop<G256>(L, (ne + KT - 1) / KT, 1 << 30, acc, smem);
+  Epi<G256> ep;
+#pragma unroll
+  for (int mb = 0; mb < G256::MB; ++mb) {
+    const int i = i0 + ep.row(mb);
+#pragma unroll
+    for (int nb = 0; nb < G256::NB / 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= r) continue;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = acc[nb][mb][4 * g + q] + acc[nb + G256::NB / 2][mb][4 * g + q];
+        if (which < 2) {
+          uint16_t* d = (which ? a.dB3 : a.dB1) + ((long)e * a.I + i) * r + c;
+          *(u32x2*)d = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+        } else {
+          uint16_t* d = a.dA2 + ((long)e * r + c) * a.I + i;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[(long)q * a.I] = (uint16_t)f2bf(v[q]);
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// a14: shared-factor gradients over tokens (no pool rows involved):
+//   which 0: dA1[c][h] = sum_t (s pc1)[t][c] x[t][h]   (x_t from the saved pool)
+//   which 1: dA3[c][h] = sum_t (s pc3)[t][c] x[t][h]
+//   which 2: dB2[h][c] = sum_t go[t][h] zc[t][c]
+// Token range split in fixed chunks; partials summed in chunk order.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_wgrad_shared(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int ntm = a.H / 256;
+  const int h0 = (blockIdx.x % ntm) * 256, sp = blockIdx.x / ntm, which = blockIdx.y;
+  const int r = a.r;
+  const int tb = sp * a.kspl;
+  const int nt = min(a.kspl, a.T - tb);
+  LdWg L;
+  if (which < 2)
+    L.m.kp = KRows{a.Xp, (long)a.H, a.r2row, a.k, tb, nt, 2};  // x_t read from the saved pool
+  else
+    L.m.kp = KRows{a.go, (long)a.H, nullptr, 1, tb, nt, 0};
+  L.m.n0 = h0;
+  L.m.nvalid = 256;
+  L.m.hilo_half = 0;
+  L.m.lo_off = 0;
+  if (which < 2) {
+    L.n.kp = KRows{a.pc, 4L * r, nullptr, 1, tb, nt, 0};
+    L.n.n0 = which * 2 * r;
+  } else {
+    L.n.kp = KRows{a.zc, 2L * r, nullptr, 1, tb, nt, 0};
+    L.n.n0 = 0;
+  }
+  L.n.nvalid = r;
+  L.n.hilo_half = 128;
+  L.n.lo_off = r;
+  f32x16 acc[G256::NB][G256::MB];
+  mainloop<G256>(L, (nt + KT - 1) / KT, 1 << 30, acc, smem);
+  Epi<G256> ep;
+  float* part = a.part + ((long)which * a.nsplit + sp) * (long)a.H * r;
+#pragma unroll
+  for (int mb = 0; mb < G256::MB; ++mb) {
+    const int h = h0 + ep.row(mb);
+#pragma unroll
+    for (int nb = 0; nb < G256::NB / 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= r) continue;
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = acc[nb][mb][4 * g + q] + acc[nb + G256::NB / 2][mb][4 * g + q];
+        if (which < 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) part[(long)(c + q) * a.H + h] = v[q];  // [c][h]
+        } else {
+          *(f32x4*)(part + (long)h * r + c) = v;  // [h][c]
+        }
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_reduce_shared(LayerArgs a) {
+  const long n = (long)a.H * a.r;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int which = blockIdx.y;
+  if (i >= n) return;
+  const float* p = a.part + (long)which * a.nsplit * n + i;
+  float s = 0.0f;
+  for (int sp = 0; sp < a.nsplit; ++sp) s += p[(long)sp * n];
+  uint16_t* d = which == 0 ? a.dA1 : (which == 1 ? a.dA3 : a.dB2);
+  d[i] = (uint16_t)f2bf(s);
+}
+
+// ----------------------------------------------------------------------------
+static void set_lds(const void* fn, int bytes) {
+  hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
+  static bool init = false;
+  if (!init) {
+    set_lds((const void*)k_q, G128::LDS_BYTES);
+    set_lds((const void*)k_w2dgrad, G256::LDS_BYTES);
+    set_lds((const void*)k_w13dgrad, G256::LDS_BYTES);
+    set_lds((const void*)k_p13, G128::LDS_BYTES);
+    set_lds((const void*)k_dx, G256::LDS_BYTES);
+    set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
+    set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
+    init = true;
+  }
+  const int tm = (a.T + 255) / 256;
+  hipLaunchKernelGGL(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
+  const long nr = (long)a.T * a.k;
+  hipLaunchKernelGGL(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_w2dgrad, dim3(a.maxtiles * (a.I / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  hipLaunchKernelGGL(k_w13dgrad, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  hipLaunchKernelGGL(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
+  const long npc = (long)a.T * 2 * a.r;
+  hipLaunchKernelGGL(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_dx, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
+  hipLaunchKernelGGL(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(256), G256::LDS_BYTES, st, a);
+  hipLaunchKernelGGL(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
+  const long nsh = (long)a.H * a.r;
+  hipLaunchKernelGGL(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moelora

@@ -1,0 +1,311 @@
+// engine.hpp -- bf16 MFMA tile engine for gfx950 (CDNA4).
+//
+// One workgroup = 256 threads = 4 wave64s.  A block computes a TM x TN tile of
+//   C[m][n] = sum_k M[m][k] * N[n][k]
+// where the "M side" supplies output rows (pool rows, tokens) and the "N side"
+// supplies output columns (weight rows, adapter columns).  Both operands are
+// staged into LDS as K-contiguous bf16 tiles (64 k per stage, 128 bytes per
+// row, 16-byte chunks XOR-swizzled so that both the staging writes and the
+// MFMA fragment reads are free of bank conflicts), double-buffered with one
+// barrier per stage; global loads of stage s+1 are in flight while the MFMAs
+// of stage s run.
+//
+// v_mfma_f32_32x32x16_bf16 is fed with the N-side fragment as its first
+// operand and the M-side fragment as its second, so every lane owns one output
+// row (m = lane % 32) and each group of four accumulator registers holds four
+// consecutive output columns: epilogues store 16-byte (fp32) or 8-byte (bf16)
+// runs per lane.  Lane layout (probed on the device): operand lane l carries
+// row l % 32, k = 8 * (l / 32) .. +7; accumulator v of lane l is
+// D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+//
+// Two staging patterns:
+//   RowsK  -- the source is K-contiguous (x, weights in [out, in] layout used
+//             as the N side of a forward GEMM); a thread moves 16-byte chunks.
+//   TransK -- the source is K-outer ([k][n], n contiguous: weights in dgrad,
+//             token rows in weight gradients); a thread loads an 8 x 8 block
+//             (8 rows of 16 bytes), transposes it in registers and writes 8
+//             K-contiguous chunks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NTHREADS = 256;
+constexpr int KT = 64;     // k per stage
+constexpr int LROW = 128;  // bytes per LDS tile row (KT bf16)
+
+__device__ __forceinline__ int lds_off(int row, int c) {
+  return row * LROW + ((c ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+// two-term bf16 split of an fp32 value: v ~= hi + lo to about 16 significant bits
+__device__ __forceinline__ void split_hl(float v, uint32_t& hi, uint32_t& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// tile geometry: WM x WN waves, each wave MB x NB blocks of 32 x 32
+// ---------------------------------------------------------------------------
+template <int MB_, int NB_, int WM_, int WN_>
+struct Geo {
+  static constexpr int MB = MB_, NB = NB_, WM = WM_, WN = WN_;
+  static constexpr int TM = WM * MB * 32, TN = WN * NB * 32;
+  static constexpr int LDS_STAGE = (TM + TN) * LROW;
+  static constexpr int LDS_BYTES = 2 * LDS_STAGE;
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(NB % 2 == 0, "N blocks come in pairs");
+  // rows of the M tile owned by (wave row wm, block mb)
+  __device__ static constexpr int m_local(int wm, int mb) { return (wm * MB + mb) * 32; }
+  // columns of the N tile owned by (wave column wn, block nb): the first NB/2
+  // blocks lie in the first half of the tile, the rest at the same offset in
+  // the second half, so a wave holds column n and its partner n + TN/2.
+  __device__ static constexpr int n_local(int wn, int nb) {
+    return (nb < NB / 2 ? 0 : TN / 2) + (wn * (NB / 2) + (nb % (NB / 2))) * 32;
+  }
+};
+
+// One stage of MFMAs.  SPLIT: the first half of the N tile contracts only the
+// first 32 k of the stage, the second half only the last 32 k (two independent
+// K ranges packed into one stage).
+template <class G, bool SPLIT>
+__device__ __forceinline__ void mma_stage(const char* sM, const char* sN,
+                                          f32x16 (&acc)[G::NB][G::MB], int wm, int wn,
+                                          int lane) {
+  const int r = lane & 31, hb = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk * 2 + hb;
+    bf16x8 b[G::MB];
+    bf16x8 a[G::NB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+      b[mb] = *(const bf16x8*)(sM + lds_off(G::m_local(wm, mb) + r, c));
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+      if (SPLIT && ((nb < G::NB / 2) != (kk < 2))) continue;
+      a[nb] = *(const bf16x8*)(sN + lds_off(G::n_local(wn, nb) + r, c));
+    }
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+      if (SPLIT && ((nb < G::NB / 2) != (kk < 2))) continue;
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RowsK: K-contiguous bf16 rows.  Thread t moves chunk c = t % 8 of tile rows
+// t / 8 + 32 i.  Each row has a window [lo, lo + span) of the stage's k
+// coordinate; inside it the source column is k - lo, folded by `period` when
+// non-zero (used to repeat a rank-r row for the hi and lo halves of a split
+// operand).  Rows with a null pointer and k outside the window read zero.
+// In SPLIT stages chunk c < 4 reads k = k0 + 8c and chunk c >= 4 reads
+// k = khalf + k0 + 8(c - 4).
+// ---------------------------------------------------------------------------
+template <int R>
+struct RowsK {
+  static constexpr int NI = R / 32;
+  const uint16_t* rp[NI];
+  int lo[NI];
+  int span, period;
+  u32x4 v[NI];
+
+  __device__ __forceinline__ void load(int k0, int khalf, bool split) {
+    const int c = threadIdx.x & 7;
+    const int kc = split ? ((c < 4) ? k0 + 8 * c : khalf + k0 + 8 * (c - 4)) : k0 + 8 * c;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int k = kc - lo[i];
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (rp[i] != nullptr && k >= 0 && k < span) {
+        if (period != 0 && k >= period) k -= period;
+        x = *(const u32x4*)(rp[i] + k);
+      }
+      v[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(char* s) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) *(u32x4*)(s + lds_off((t >> 3) + 32 * i, t & 7)) = v[i];
+  }
+  // tile row owned by slot i of this thread
+  __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x >> 3) + 32 * i; }
+};
+
+// ---------------------------------------------------------------------------
+// TransK: K-outer source rows ([k][n], n contiguous).  Tile = R columns x 64 k,
+// made of 8 x 8 blocks; thread t < R handles block (nb = t % (R/8),
+// kb = t / (R/8)).  The k-row pointer comes from the policy KP; the n window
+// is [0, nvalid) of the tile, read from source column n0 + n.  With
+// `hilo_half` > 0 the tile holds two halves: columns [0, half) read source
+// column n0 + n and columns [half, 2 half) read source column n0 + lo_off +
+// (n - half), each valid for n % half < nvalid.
+// ---------------------------------------------------------------------------
+template <int R, class KP>
+struct TransK {
+  KP kp;
+  int n0, nvalid, hilo_half, lo_off;
+  u32x4 v[8];
+
+  __device__ __forceinline__ const uint16_t* col_ptr(const uint16_t* row, int nl) const {
+    int n = nl, extra = 0;
+    if (hilo_half > 0 && nl >= hilo_half) { n = nl - hilo_half; extra = lo_off; }
+    if (n >= nvalid) return nullptr;
+    return row + n0 + extra + n;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int t = threadIdx.x;
+    if (t >= R) return;
+    const int nb = t % (R / 8), kb = t / (R / 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t* row = kp.row(k0 + kb * 8 + i);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row != nullptr) {
+        const uint16_t* p = col_ptr(row, nb * 8);
+        if (p != nullptr) x = *(const u32x4*)p;
+      }
+      v[i] = x;
+    }
+  }
+  __device__ __forceinline__ void store(char* s) const {
+    const int t = threadIdx.x;
+    if (t >= R) return;
+    const int nb = t % (R / 8), kb = t / (R / 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t a = v[2 * d][j >> 1], b = v[2 * d + 1][j >> 1];
+        o[d] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      *(u32x4*)(s + lds_off(nb * 8 + j, kb)) = o;
+    }
+  }
+};
+
+// k-row policies for TransK
+struct KStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) folded by period
+  const uint16_t* base;
+  long ld;
+  int lo, span, period;
+  __device__ __forceinline__ const uint16_t* row(int k) const {
+    int kk = k - lo;
+    if (kk < 0 || kk >= span) return nullptr;
+    if (period != 0 && kk >= period) kk -= period;
+    return base + (long)kk * ld;
+  }
+};
+struct KTwoMats {  // k in [0, 2r) -> rows of A (period r), [2r, 4r) -> rows of B (period r)
+  const uint16_t* a;
+  const uint16_t* b;
+  long ld;
+  int r;
+  __device__ __forceinline__ const uint16_t* row(int k) const {
+    if (k < 0 || k >= 4 * r) return nullptr;
+    const uint16_t* m = (k < 2 * r) ? a : b;
+    int kk = (k < 2 * r) ? k : k - 2 * r;
+    if (kk >= r) kk -= r;
+    return m + (long)kk * ld;
+  }
+};
+struct KRows {  // k-th row of a contiguous range of pool rows or tokens
+  // mode 0: row (row0 + k) of `base`
+  // mode 1: pool row (row0 + k) -> its token's row of `base` (map = row -> route)
+  // mode 2: token (row0 + k) -> the pool row of its first live route
+  //         (map = route -> row); a token with no live route reads zero
+  const uint16_t* base;
+  long ld;
+  const int32_t* map;
+  int topk;
+  int row0, nrows, mode;
+  __device__ __forceinline__ const uint16_t* row(int k) const {
+    if (k >= nrows) return nullptr;
+    long r = row0 + k;
+    if (mode == 1) {
+      r = map[r] / topk;
+    } else if (mode == 2) {
+      long pr = -1;
+      for (int j = 0; j < topk && pr < 0; ++j) pr = map[r * topk + j];
+      if (pr < 0) return nullptr;
+      r = pr;
+    }
+    return base + r * ld;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// main loop: `L` provides load(stage) (global -> registers) and
+// store(sM, sN) (registers -> LDS); stages >= split_from use SPLIT MFMAs.
+// ---------------------------------------------------------------------------
+template <class G, class L>
+__device__ __forceinline__ void mainloop(L& ld, int nstages, int split_from,
+                                         f32x16 (&acc)[G::NB][G::MB], char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / G::WN, wn = w % G::WN;
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[nb][mb][q] = 0.0f;
+  if (nstages <= 0) return;
+  ld.load(0);
+  for (int s = 0; s < nstages; ++s) {
+    char* sM = smem + (s & 1) * G::LDS_STAGE;
+    char* sN = sM + G::TM * LROW;
+    ld.store(sM, sN);
+    __syncthreads();
+    if (s + 1 < nstages) ld.load(s + 1);
+    if (s >= split_from)
+      mma_stage<G, true>(sM, sN, acc, wm, wn, lane);
+    else
+      mma_stage<G, false>(sM, sN, acc, wm, wn, lane);
+  }
+}
+
+// Epilogue coordinates of accumulator (nb, mb, group g) for this lane:
+// output row m_local + (lane & 31), columns n .. n + 3.
+template <class G>
+struct Epi {
+  int wm, wn, lane;
+  __device__ Epi() {
+    const int w = threadIdx.x >> 6;
+    wm = w / G::WN;
+    wn = w % G::WN;
+    lane = threadIdx.x & 63;
+  }
+  __device__ __forceinline__ int row(int mb) const { return G::m_local(wm, mb) + (lane & 31); }
+  __device__ __forceinline__ int col(int nb, int g) const {
+    return G::n_local(wn, nb) + 8 * g + 4 * (lane >> 5);
+  }
+};
+
+// Grouped-GEMM M tile: rows [row0, row_end) of expert e in the pool.
+struct TileInfo {
+  int e, row0, row_end, pad;
+};
+
+}  // namespace moelora

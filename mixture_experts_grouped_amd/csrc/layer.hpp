@@ -1,0 +1,68 @@
+// layer.hpp -- arguments shared by every kernel of one layer call, and the
+// launchers the C ABI calls.  Internal to libmoelora.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engine.hpp"
+
+namespace moelora {
+
+constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
+
+// Everything a kernel may touch, passed by value as the kernel argument.
+// Pool-shaped tensors have `cap` rows; token-shaped tensors have T rows.
+// bf16 tensors are uint16 bit patterns.  "_hl" tensors hold an fp32 quantity
+// as two bf16 terms: [hi (r) | lo (r)] per rank-r factor.
+struct LayerArgs {
+  int T, H, I, E, k, r;
+  float s;
+  long cap;
+  int maxtiles;
+  // pool
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* r2row;  // route -> pool row
+  const int32_t* row2r;  // pool row -> route
+  // inputs
+  const uint16_t* x;
+  const float* w;
+  const uint16_t* go;
+  // parameters
+  const uint16_t *W13, *W2, *A1, *A3, *B1, *B3, *A2, *B2;
+  // saved by the forward
+  TileInfo* tiles;   // [maxtiles]
+  int* ntiles;       // [1]
+  uint16_t* Xp;      // [cap, H]  gathered expert input, padding rows zero
+  uint16_t* ZA;      // [T, 4r]   s*A1 x, s*A3 x as hi/lo
+  float* G;          // [cap, I]  gate pre-activation
+  float* V;          // [cap, I]  up pre-activation
+  uint16_t* Hh;      // [cap, I]  silu(G) * V
+  float* Z2;         // [cap, r]  s * A2_e h
+  uint16_t* Yb;      // [cap, H]  W2_e h (unweighted base output)
+  uint16_t* zc;      // [T, 2r]   sum_j w Z2 as hi/lo
+  // forward output
+  uint16_t* out;     // [T, H]
+  // backward scratch
+  float* q;          // [T, r]    B2^T grad_out
+  uint16_t* sq;      // [T, 2r]   s*q as hi/lo
+  uint16_t* wsq;     // [cap, 2r] s*w*q per route as hi/lo
+  uint16_t* dGV;     // [cap, 2I] dgate | dup
+  uint16_t* dU;      // [cap, H]  W13_e^T [dg; dv]
+  float* P;          // [cap, 2r] B1_e^T dg | B3_e^T dv
+  uint16_t* pc;      // [T, 4r]   s * sum_j P as hi/lo (pc1 | pc3)
+  float* part;       // [3, nsplit, H*r] split-K partials of the shared-factor gradients
+  int nsplit, kspl;
+  // backward outputs
+  uint16_t* gx;
+  float* gw;
+  uint16_t *dA1, *dA3, *dB1, *dB3, *dA2, *dB2, *dW13, *dW2;
+};
+
+hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,
+                             int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
+                             int32_t* err, hipStream_t st);
+hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
+hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
+
+}  // namespace moelora

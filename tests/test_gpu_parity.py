@@ -1,0 +1,124 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on the
+same seeded inputs.  Pool metadata must match bit for bit; every float tensor
+must meet cosine >= 0.99999 and relative L2 <= 5e-3 against the oracle."""
+import numpy as np
+import pytest
+
+from mixture_experts_grouped_amd import inputs as I
+from oracle import pool as OP
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    Hn.ensure_built()
+
+
+def _case(shape, key, routing="softmax_topk", mask=0.0):
+    return I.layer_inputs(shape, key, routing=routing, mask_prob=mask)
+
+
+def _check_pool(res, case, shape, bm):
+    ref = OP.build_pool(case["topk_idx"], shape.E, bm)
+    for n in ("counts", "offsets", "route_to_row", "row_to_route"):
+        assert np.array_equal(res[n], ref[n]), n
+    assert res["device_error"] == int(ref["bad_routes"])
+
+
+CASES = {
+    # the small oracle shape (T 256, H 512, I 256, E 16, top-2, rank 8)
+    "tiny": (I.TINY, (0,), "softmax_topk", 0.0),
+    # rank 128, 20 % dropped routes, ragged expert tails, two N tiles
+    "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (10,), "softmax_topk", 0.2),
+    # three M tiles per expert, the last one ragged
+    "multi_tile": (I.Shape(T=1100, H=256, I=256, E=4, topk=2, rank=16), (11,), "softmax_topk", 0.0),
+    # one token, six of 64 experts (most experts empty)
+    "single_token": (I.Shape(T=1, H=512, I=256, E=64, topk=6, rank=128), (12,), "softmax_topk", 0.2),
+    # skewed routing with forced-empty experts and duplicate experts per token
+    "zipf_small": (I.Shape(T=200, H=256, I=256, E=16, topk=6, rank=32), (13,), "zipf", 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_against_oracle(name):
+    shape, key, routing, mask = CASES[name]
+    Hn.log(f"[parity] case={name} shape={shape} routing={routing} mask={mask}")
+    case = _case(shape, key, routing, mask)
+    run = Hn.GpuRun(shape, case)
+    res = run.run()
+    _check_pool(res, case, shape, run.layer.block_m)
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale)
+    rep = Hn.compare_all(res, ref_out, ref_g, tag=name + ":")
+    # dropped routes have exactly zero router gradient
+    assert (res["grad_w"][case["topk_idx"] < 0] == 0).all()
+    # experts without rows have exactly zero local adapter gradients
+    counts = np.bincount(case["topk_idx"][case["topk_idx"] >= 0], minlength=shape.E)
+    for e in np.nonzero(counts == 0)[0]:
+        for n in ("dB1", "dB3", "dA2"):
+            assert not np.any(res[n][e]), (n, e)
+    Hn.log(f"[parity] {name}: " + ", ".join(f"{k} cos={v['cos']:.8f} rel={v['rel_l2']:.2e}"
+                                           for k, v in rep.items()))
+
+
+def test_zero_scale_matches_base_and_zero_adapter_grads():
+    shape = I.TINY
+    case = _case(shape, (1,))
+    res = Hn.GpuRun(shape, case, scale=0.0).run()
+    ref_out, ref_g = Hn.oracle_run(case, 0.0)
+    Hn.compare_all(res, ref_out, ref_g, tag="s0:")
+    for n in Hn.GRAD_NAMES:
+        assert not np.any(res[n]), n
+    # zero adapters at scale 1 give bitwise the same output and input gradients
+    case0 = dict(case)
+    for n in ("A1", "A3", "B1", "B3", "A2", "B2"):
+        case0[n] = np.zeros_like(case[n])
+    res0 = Hn.GpuRun(shape, case0, scale=1.0).run()
+    for n in ("out", "grad_x", "grad_w"):
+        assert np.array_equal(res0[n], res[n]), n
+
+
+def test_block_m_sweep_bitwise_identical():
+    """Every BLOCK_M gives the oracle's pool and bitwise identical results."""
+    shape = I.Shape(T=200, H=256, I=256, E=16, topk=6, rank=32)
+    case = _case(shape, (14,), "zipf")
+    first = None
+    for bm in I.BLOCK_M_SET:
+        Hn.log(f"[bm-sweep] block_m={bm}")
+        res = Hn.GpuRun(shape, case, block_m=bm).run()
+        _check_pool(res, case, shape, bm)
+        if first is None:
+            first = res
+            ref_out, ref_g = Hn.oracle_run(case, shape.scale)
+            Hn.compare_all(res, ref_out, ref_g, tag=f"bm{bm}:")
+            continue
+        for n in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+            assert np.array_equal(res[n], first[n]), (bm, n)
+
+
+def test_repeatable_and_nan_poison_inert():
+    """Two runs are bitwise equal, and NaN-filled workspaces and outputs do not
+    change any result (padding never reaches a reduction)."""
+    shape = I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128)
+    case = _case(shape, (15,), "softmax_topk", 0.2)
+    run = Hn.GpuRun(shape, case)
+    a = run.run(fill=(0,))
+    b = run.run(fill=(0xFF,))
+    c = run.run()
+    for n in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(a[n], b[n]), n
+        assert np.array_equal(a[n], c[n]), n
+
+
+def test_invalid_route_ids_counted():
+    shape = I.Shape(T=64, H=256, I=256, E=8, topk=2, rank=8)
+    case = _case(shape, (16,))
+    case["topk_idx"] = case["topk_idx"].copy()
+    case["topk_idx"][3, 0] = 9      # out of range
+    case["topk_idx"][5, 1] = -7     # out of range
+    case["topk_w"] = case["topk_w"].copy()
+    run = Hn.GpuRun(shape, case)
+    res = run.run()
+    assert res["device_error"] == 2
+    _check_pool(res, case, shape, run.layer.block_m)
