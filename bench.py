@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE side-LoRA expert layer, forward + backward, on one
+MI355X.
+
+One step = build_pool + moe_lora_forward + moe_lora_backward over one batch of
+seeded synthetic inputs already resident in HBM.  Default workload: one EP4
+rank's production share, 16,384 tokens x top-6 = 98,304 routed rows dispatched
+uniformly over 64 local experts, H=4096, I=2048, side-LoRA rank 128 (shared
+A1/A3/B2, expert-local B1/B3/A2), SwiGLU, bf16 data with fp32 accumulation.
+
+Prints one JSON line.  `value` is the whole step's algorithmic throughput in
+TFLOP/s (shared factors counted once per token, hi/lo split work not counted);
+`ms_per_step` is the F+B time.  Per-kernel times come from HIP events the
+library records on its launch stream during the timed steps.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--tokens T]
+                    [--cpu-seconds S | --no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE side-LoRA F+B ms and grouped-GEMM TFLOP/s (64 experts, 98K rows, H4096)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+GEMM_KERNELS = ("k_shrink", "k_w13", "k_a2", "k_w2", "k_combine", "k_q", "k_w2dgrad",
+                "k_w13dgrad", "k_p13", "k_dx", "k_wgrad_local", "k_wgrad_shared")
+
+
+def kernel_flops(T, M, H, I, r):
+    """Algorithmic FLOPs per launch of each contraction kernel."""
+    return {
+        "k_shrink": 4.0 * T * H * r,
+        "k_w13": M * (4.0 * H * I + 4.0 * I * r),
+        "k_a2": 2.0 * M * I * r,
+        "k_w2": 2.0 * M * H * I,
+        "k_combine": 2.0 * T * H * r,
+        "k_q": 2.0 * T * H * r,
+        "k_w2dgrad": M * (2.0 * H * I + 2.0 * I * r),
+        "k_w13dgrad": 4.0 * M * H * I,
+        "k_p13": 4.0 * M * I * r,
+        "k_dx": 4.0 * T * H * r,
+        "k_wgrad_local": 6.0 * M * I * r,
+        "k_wgrad_shared": 6.0 * T * H * r,
+    }
+
+
+def step_flops(T, M, H, I, r):
+    fwd = M * (6.0 * H * I + 6.0 * I * r) + 6.0 * T * H * r
+    bwd = M * (6.0 * H * I + 12.0 * I * r) + 12.0 * T * H * r
+    return fwd, bwd
+
+
+def make_inputs(shape, key, threads):
+    from mixture_experts_grouped_amd import inputs as I
+    with cf.ThreadPoolExecutor(threads) as ex:
+        fut_e = [ex.submit(I.expert_weights, shape, key, e) for e in range(shape.E)]
+        fut_x = ex.submit(I.tokens, shape, key)
+        fut_g = ex.submit(I.grad_out, shape, key)
+        idx, w = I.route_balanced(shape, key)
+        shared = I.shared_weights(shape, key)
+        experts = [f.result() for f in fut_e]
+        return experts, shared, fut_x.result(), fut_g.result(), idx, w
+
+
+def cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, target_s):
+    """The float64 oracle as it stands, timed on this host on the routes of
+    the first n experts (n chosen so the run takes about target_s)."""
+    import numpy as np
+    from mixture_experts_grouped_amd import inputs as I
+    from oracle import moe_lora as OM
+
+    def run(n):
+        sel = idx < n
+        tok = np.nonzero(sel.any(axis=1))[0]
+        sidx = np.where(sel, idx, -1)[tok]
+        sw = np.where(sel, w, 0.0)[tok].astype(np.float64)
+        p = {nm: np.stack([I.bf16_bits_to_f32(experts[e][nm]) for e in range(n)])
+             for nm in ("W13", "W2", "B1", "B3", "A2")}
+        p.update({nm: I.bf16_bits_to_f32(shared[nm]) for nm in ("A1", "A3", "B2")})
+        xs = I.bf16_bits_to_f32(x_bits[tok]).astype(np.float64)
+        gs = I.bf16_bits_to_f32(go_bits[tok]).astype(np.float64)
+        t0 = time.perf_counter()
+        OM.forward(xs, sidx, sw, p, shape.scale)
+        OM.backward(gs, xs, sidx, sw, p, shape.scale)
+        dt = time.perf_counter() - t0
+        M = int(sel.sum())
+        f, b = step_flops(len(tok), M, shape.H, shape.I, shape.rank)
+        return dt, f + b, M, len(tok)
+
+    dt1, fl1, _, _ = run(1)
+    n = int(max(1, min(shape.E, round(target_s / max(dt1, 1e-3)))))
+    dt, fl, M, ntok = run(n) if n > 1 else (dt1, fl1, int((idx < 1).sum()), 0)
+    cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OMP_NUM_THREADS")
+    return {
+        "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads) if threads else cores,
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle, forward+backward of the routes of experts 0..{n - 1} "
+                  f"({M} routed rows, {ntok} tokens) of the same workload; {dt:.2f} s",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=16384)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixture_experts_grouped_amd import binding as B
+    from mixture_experts_grouped_amd import inputs as I
+
+    if not os.path.exists(B.LIB_PATH):
+        from mixture_experts_grouped_amd import build
+        build.build()
+    shape = I.Shape(T=args.tokens, H=4096, I=2048, E=64, topk=6, rank=128, scale=1.0)
+    key = (2,)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    t0 = time.time()
+    experts, shared, x_bits, go_bits, idx, w = make_inputs(shape, key, threads)
+    print(f"[bench] inputs generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    dev = "cuda"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    params = {nm: torch.empty(0) for nm in ("W13", "W2", "B1", "B3", "A2")}
+    for nm in ("W13", "W2", "B1", "B3", "A2"):
+        first = experts[0][nm]
+        t = torch.empty((shape.E, *first.shape), dtype=torch.bfloat16, device=dev)
+        for e in range(shape.E):
+            t[e].copy_(bf(experts[e][nm]))
+        params[nm] = t
+    for nm in ("A1", "A3", "B2"):
+        params[nm] = bf(shared[nm])
+    x = bf(x_bits)
+    go = bf(go_bits)
+    tidx = torch.from_numpy(idx).to(dev)
+    tw = torch.from_numpy(w).to(dev)
+
+    desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale)
+    layer = B.MoeLoraLayer(desc, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.step(tidx, x, tw, params, go, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    trace = not args.no_trace
+    if trace:
+        B.moe_lora_trace_reset()
+        B.moe_lora_trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = {}
+    if trace:
+        B.moe_lora_trace_enable(False)
+        kernels = B.moe_lora_trace_collect()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    # forward and backward timed directly (outside the timed steps)
+    def timed(fn, n=5):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - a) * 1e3 / n
+
+    fwd_ms = timed(lambda: (layer.build_pool(tidx, stream), layer.forward(x, tw, params, stream)))
+    bwd_ms = timed(lambda: layer.backward(go, tw, params, stream))
+
+    M = int((idx >= 0).sum())
+    T, H, Idim, r = shape.T, shape.H, shape.I, shape.rank
+    fwd_fl, bwd_fl = step_flops(T, M, H, Idim, r)
+    tflops = (fwd_fl + bwd_fl) / (ms * 1e-3) / 1e12
+    kfl = kernel_flops(T, M, H, Idim, r)
+    per_kernel = {}
+    gemm_fl = gemm_ms = 0.0
+    for name, (n, tot) in kernels.items():
+        avg = tot / max(n, 1)
+        ent = {"avg_ms": round(avg, 4), "launches": n}
+        if name in kfl:
+            ent["tflops"] = round(kfl[name] / (avg * 1e-3) / 1e12, 1)
+            gemm_fl += kfl[name] * n
+            gemm_ms += tot
+        per_kernel[name] = ent
+    roofline = None
+    if kernels:
+        dom = max((nm for nm in kernels if nm in kfl), key=lambda nm: kernels[nm][1])
+        n, tot = kernels[dom]
+        avg_s = tot / n * 1e-3
+        ach = kfl[dom] / avg_s / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, args.cpu_seconds)
+        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s",
+              file=sys.stderr, flush=True)
+        cpu.pop("seconds", None)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
+                         f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, SwiGLU, s=1"),
+            "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
+            "block_m": layer.block_m,
+        },
+        "fwd_ms": round(fwd_ms, 3),
+        "bwd_ms": round(bwd_ms, 3),
+        "algorithmic_tflop_per_step": round((fwd_fl + bwd_fl) / 1e12, 4),
+        "gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": per_kernel,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,6 +168,23 @@ moe_status moe_lora_backward(const moe_lora_desc* desc, const moe_pool* pool,
                              const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
                              void* stream);
 
+/* Optional per-kernel timing (the pages' backward carries an optional kernel
+ * trace: PR #9 review-bot Overview).  When enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on its launch stream; the
+ * events are created on first use and reused.  Off by default.
+ *   moe_lora_trace_enable(1 / 0)  turn recording on / off (process-wide)
+ *   moe_lora_trace_collect()      wait for the recorded events and add their
+ *                                 elapsed times to per-kernel totals
+ *   moe_lora_trace_count()        number of kernels with totals
+ *   moe_lora_trace_entry(i, ...)  name (static storage until the next reset),
+ *                                 launch count and total milliseconds of entry i
+ *   moe_lora_trace_reset()        clear the totals */
+void moe_lora_trace_enable(int32_t on);
+moe_status moe_lora_trace_collect(void);
+int32_t moe_lora_trace_count(void);
+moe_status moe_lora_trace_entry(int32_t i, const char** name, int64_t* launches, double* total_ms);
+void moe_lora_trace_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,8 @@ MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
     "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_backward",
+    "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
+    "moe_lora_trace_entry", "moe_lora_trace_reset",
 )
 
 
@@ -90,7 +92,16 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_backward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
-    for fn in ("moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
+    lib.moe_lora_trace_enable.argtypes = [ctypes.c_int32]
+    lib.moe_lora_trace_enable.restype = None
+    lib.moe_lora_trace_collect.argtypes = []
+    lib.moe_lora_trace_count.argtypes = []
+    lib.moe_lora_trace_count.restype = ctypes.c_int32
+    lib.moe_lora_trace_entry.argtypes = [ctypes.c_int32, P(ctypes.c_char_p), P(ctypes.c_int64),
+                                         P(ctypes.c_double)]
+    lib.moe_lora_trace_reset.argtypes = []
+    lib.moe_lora_trace_reset.restype = None
+    for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
                "build_pool", "moe_lora_forward", "moe_lora_backward"):
         getattr(lib, fn).restype = ctypes.c_int32
     if path is None:
@@ -225,6 +236,27 @@ def moe_lora_backward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], grad_out
         ctypes.byref(gs), _ptr(scratch, torch.uint8, None, "scratch"), scratch.numel(),
         _stream(stream))
     _check(st, "moe_lora_backward")
+
+
+def moe_lora_trace_enable(on: bool) -> None:
+    library().moe_lora_trace_enable(1 if on else 0)
+
+
+def moe_lora_trace_reset() -> None:
+    library().moe_lora_trace_reset()
+
+
+def moe_lora_trace_collect() -> Dict[str, Tuple[int, float]]:
+    """Wait for recorded events; return {kernel: (launches, total_ms)}."""
+    lib = library()
+    _check(lib.moe_lora_trace_collect(), "moe_lora_trace_collect")
+    out = {}
+    for i in range(lib.moe_lora_trace_count()):
+        name, n, ms = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        _check(lib.moe_lora_trace_entry(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+               "moe_lora_trace_entry")
+        out[name.value.decode()] = (n.value, ms.value)
+    return out
 
 
 class MoeLoraLayer:

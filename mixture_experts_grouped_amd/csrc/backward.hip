@@ -17,6 +17,7 @@
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
 #include "layer.hpp"
+#include "trace.hpp"
 
 namespace moelora {
 
@@ -38,21 +39,12 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
   const int t0 = blockIdx.x * 256;
   const int r = a.r;
   LdQ L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (t < a.T) ? a.go + (long)t * a.H : nullptr;
-    L.m.lo[i] = 0;
-  }
-  L.m.span = a.H;
-  L.m.period = 0;
-  L.n.kp = KStrided{a.B2, r, 0, a.H, 0};
-  L.n.n0 = 0;
-  L.n.nvalid = r;
-  L.n.hilo_half = 0;
-  L.n.lo_off = 0;
+  L.m.contig(a.go, t0, a.T - t0, a.H);
+  L.m.window(a.H);
+  L.n.kp = KStrided{make_rsrc(a.B2, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
+  L.n.cols(0, r);
   f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.H / KT, 1 << 30, acc, smem);
+  mainloop<G128>(L, a.H / KT, acc, smem);
   Epi<G128> ep;
 #pragma unroll
   for (int mb = 0; mb < G128::MB; ++mb) {
@@ -118,77 +110,57 @@ __global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a9: dh = w (W2_e^T go + A2_e^T s q), SwiGLU backward -> dG, dV
 // ----------------------------------------------------------------------------
+using GW2D = G128;
 struct LdW2d {
   RowsK<256> m;
-  TransK<256, KStrided> n;
-  int nmain, r, topk, row0, row_end;
-  const int32_t* row2r;
-  const uint16_t* sq;
-  const uint16_t* A2e;
-  long ldn;
+  TransK<GW2D::TN, KStrided> n;
   __device__ void load(int s) {
-    if (s < nmain) {
-      m.load(s * KT, 0, false);
-      n.load(s * KT);
-      return;
-    }
-    if (s == nmain) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const long row = row0 + RowsK<256>::row_of(i);
-        m.rp[i] = (row < row_end) ? sq + (long)(row2r[row] / topk) * 2 * r : nullptr;
-      }
-      m.span = 2 * r;
-      n.kp = KStrided{A2e, ldn, 0, 2 * r, r};
-    }
-    const int se = s - nmain;
-    m.load(se * KT, 0, false);
-    n.load(se * KT);
+    m.load(s * KT, 0, false);
+    n.load(s * KT);
   }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
 __global__ __launch_bounds__(256) void k_w2dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int ntn = a.I / 256;
+  using G = GW2D;
+  const int ntn = a.I / G::TN;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
-  const int i0 = nt * 256;
-  LdW2d L;
-  L.r = a.r;
-  L.topk = a.k;
-  L.row0 = ti.row0;
-  L.row_end = ti.row_end;
-  L.row2r = a.row2r;
-  L.sq = a.sq;
-  L.A2e = a.A2 + (long)ti.e * a.r * a.I;
-  L.ldn = a.I;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.go + (long)(a.row2r[row] / a.k) * a.H : nullptr;
-    L.m.lo[i] = 0;
+  const int i0 = nt * G::TN;
+  const int nrows = ti.row_end - ti.row0;
+  int tk[8];
+  RowsK<256>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  {  // A2^T (s q) extension first (rank-r K), then the base K = H
+    const int r = a.r;
+    LdW2d L;
+    L.m.from_tokens(a.sq, a.T, 2 * r, tk);
+    L.m.window(2 * r);
+    L.n.kp = KStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+                      (uint32_t)(2 * a.I), 0, 2 * r, r};
+    L.n.cols(i0, G::TN);
+    run_stages<G, false>(L, (2 * r + KT - 1) / KT, acc, smem);
   }
-  L.m.span = a.H;
-  L.m.period = 0;
-  L.n.kp = KStrided{a.W2 + (long)ti.e * a.H * a.I, a.I, 0, a.H, 0};
-  L.n.n0 = i0;
-  L.n.nvalid = 256;
-  L.n.hilo_half = 0;
-  L.n.lo_off = 0;
-  L.nmain = a.H / KT;
-  const int next = (2 * a.r + KT - 1) / KT;
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, L.nmain + next, 1 << 30, acc, smem);
-  Epi<G256> ep;
+  {
+    LdW2d L;
+    L.m.from_tokens(a.go, a.T, a.H, tk);
+    L.m.window(a.H);
+    L.n.kp = KStrided{make_rsrc(a.W2 + (long)ti.e * a.H * a.I, (uint64_t)a.H * a.I * 2),
+                      (uint32_t)(2 * a.I), 0, a.H, 0};
+    L.n.cols(i0, G::TN);
+    run_stages<G, false>(L, a.H / KT, acc, smem);
+  }
+  Epi<G> ep;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
+  for (int mb = 0; mb < G::MB; ++mb) {
     const long row = ti.row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
     const float wr = a.w[a.row2r[row]];
 #pragma unroll
-    for (int nb = 0; nb < G256::NB; ++nb)
+    for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int i = i0 + ep.col(nb, g);
@@ -229,21 +201,13 @@ __global__ __launch_bounds__(256) void k_w13dgrad(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * 256;
   LdW13d L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.dGV + row * 2 * a.I : nullptr;
-    L.m.lo[i] = 0;
-  }
-  L.m.span = 2 * a.I;
-  L.m.period = 0;
-  L.n.kp = KStrided{a.W13 + (long)ti.e * 2 * a.I * a.H, a.H, 0, 2 * a.I, 0};
-  L.n.n0 = h0;
-  L.n.nvalid = 256;
-  L.n.hilo_half = 0;
-  L.n.lo_off = 0;
+  L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
+  L.m.window(2 * a.I);
+  L.n.kp = KStrided{make_rsrc(a.W13 + (long)ti.e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2),
+                    (uint32_t)(2 * a.H), 0, 2 * a.I, 0};
+  L.n.cols(h0, 256);
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, 2 * a.I / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, 2 * a.I / KT, acc, smem);
   Epi<G256> ep;
 #pragma unroll
   for (int mb = 0; mb < G256::MB; ++mb) {
@@ -278,22 +242,13 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const int r = a.r;
   LdP L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.dGV + row * 2 * a.I + which * a.I : nullptr;
-    L.m.lo[i] = 0;
-  }
-  L.m.span = a.I;
-  L.m.period = 0;
+  L.m.contig(a.dGV + which * a.I, ti.row0, ti.row_end - ti.row0, 2 * a.I);
+  L.m.window(a.I);
   const uint16_t* Be = (which ? a.B3 : a.B1) + (long)ti.e * a.I * r;
-  L.n.kp = KStrided{Be, r, 0, a.I, 0};
-  L.n.n0 = 0;
-  L.n.nvalid = r;
-  L.n.hilo_half = 0;
-  L.n.lo_off = 0;
+  L.n.kp = KStrided{make_rsrc(Be, (uint64_t)a.I * r * 2), (uint32_t)(2 * r), 0, a.I, 0};
+  L.n.cols(0, r);
   f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.I / KT, 1 << 30, acc, smem);
+  mainloop<G128>(L, a.I / KT, acc, smem);
   Epi<G128> ep;
 #pragma unroll
   for (int mb = 0; mb < G128::MB; ++mb) {
@@ -347,21 +302,13 @@ __global__ __launch_bounds__(256) void k_dx(LayerArgs a) {
   const int t0 = blockIdx.x * 256, h0 = blockIdx.y * 256;
   const int r = a.r;
   LdDx L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (t < a.T) ? a.pc + (long)t * 4 * r : nullptr;
-    L.m.lo[i] = 0;
-  }
-  L.m.span = 4 * r;
-  L.m.period = 0;
-  L.n.kp = KTwoMats{a.A1, a.A3, a.H, r};
-  L.n.n0 = h0;
-  L.n.nvalid = 256;
-  L.n.hilo_half = 0;
-  L.n.lo_off = 0;
+  L.m.contig(a.pc, t0, a.T - t0, 4 * r);
+  L.m.window(4 * r);
+  L.n.kp = KTwoMats{make_rsrc(a.A1, (uint64_t)r * a.H * 2), make_rsrc(a.A3, (uint64_t)r * a.H * 2),
+                    (uint32_t)(2 * a.H), r};
+  L.n.cols(h0, 256);
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (4 * r + KT - 1) / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, (4 * r + KT - 1) / KT, acc, smem);
   Epi<G256> ep;
 #pragma unroll
   for (int mb = 0; mb < G256::MB; ++mb) {
@@ -414,25 +361,23 @@ __global__ __launch_bounds__(256) void k_wgrad_local(LayerArgs a) {
   const int ne = a.counts[e], off = a.offsets[e];
   LdWg L;
   if (which < 2)
-    L.m.kp = KRows{a.dGV + which * a.I, 2L * a.I, nullptr, 1, off, ne, 0};
+    L.m.kp = KRows{make_rsrc(a.dGV + (long)off * 2 * a.I, (uint64_t)ne * 4 * a.I),
+                   (uint32_t)(4 * a.I), nullptr, nullptr, 1, off, ne, 0};
   else
-    L.m.kp = KRows{a.Hh, (long)a.I, nullptr, 1, off, ne, 0};
-  L.m.n0 = i0;
-  L.m.nvalid = 256;
-  L.m.hilo_half = 0;
-  L.m.lo_off = 0;
+    L.m.kp = KRows{make_rsrc(a.Hh + (long)off * a.I, (uint64_t)ne * 2 * a.I), (uint32_t)(2 * a.I),
+                   nullptr, nullptr, 1, off, ne, 0};
+  L.m.cols((which < 2 ? which * a.I : 0) + i0, 256);
   if (which < 2) {
-    L.n.kp = KRows{a.ZA, 4L * r, a.row2r, a.k, off, ne, 1};
-    L.n.n0 = which * 2 * r;
+    L.n.kp = KRows{make_rsrc(a.ZA, (uint64_t)a.T * 8 * r), (uint32_t)(8 * r), a.row2r, nullptr, a.k,
+                   off, ne, 1};
+    L.n.cols(which * 2 * r, r, 128, r);
   } else {
-    L.n.kp = KRows{a.wsq, 2L * r, nullptr, 1, off, ne, 0};
-    L.n.n0 = 0;
+    L.n.kp = KRows{make_rsrc(a.wsq + (long)off * 2 * r, (uint64_t)ne * 4 * r), (uint32_t)(4 * r),
+                   nullptr, nullptr, 1, off, ne, 0};
+    L.n.cols(0, r, 128, r);
   }
-  L.n.nvalid = r;
-  L.n.hilo_half = 128;
-  L.n.lo_off = r;
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (ne + KT - 1) / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, (ne + KT - 1) / KT, acc, smem);
   Epi<G256> ep;
 #pragma unroll
   for (int mb = 0; mb < G256::MB; ++mb) {
@@ -474,26 +419,23 @@ __global__ __launch_bounds__(256) void k_wgrad_shared(LayerArgs a) {
   const int tb = sp * a.kspl;
   const int nt = min(a.kspl, a.T - tb);
   LdWg L;
-  if (which < 2)
-    L.m.kp = KRows{a.Xp, (long)a.H, a.r2row, a.k, tb, nt, 2};  // x_t read from the saved pool
+  if (which < 2)  // x_t read from the saved pool through the token's first live route
+    L.m.kp = KRows{make_rsrc(a.Xp, 0), (uint32_t)(2 * a.H), a.r2row, a.Xp, a.k, tb, nt, 2};
   else
-    L.m.kp = KRows{a.go, (long)a.H, nullptr, 1, tb, nt, 0};
-  L.m.n0 = h0;
-  L.m.nvalid = 256;
-  L.m.hilo_half = 0;
-  L.m.lo_off = 0;
+    L.m.kp = KRows{make_rsrc(a.go + (long)tb * a.H, (uint64_t)nt * 2 * a.H), (uint32_t)(2 * a.H),
+                   nullptr, nullptr, 1, tb, nt, 0};
+  L.m.cols(h0, 256);
   if (which < 2) {
-    L.n.kp = KRows{a.pc, 4L * r, nullptr, 1, tb, nt, 0};
-    L.n.n0 = which * 2 * r;
+    L.n.kp = KRows{make_rsrc(a.pc + (long)tb * 4 * r, (uint64_t)nt * 8 * r), (uint32_t)(8 * r),
+                   nullptr, nullptr, 1, tb, nt, 0};
+    L.n.cols(which * 2 * r, r, 128, r);
   } else {
-    L.n.kp = KRows{a.zc, 2L * r, nullptr, 1, tb, nt, 0};
-    L.n.n0 = 0;
+    L.n.kp = KRows{make_rsrc(a.zc + (long)tb * 2 * r, (uint64_t)nt * 4 * r), (uint32_t)(4 * r),
+                   nullptr, nullptr, 1, tb, nt, 0};
+    L.n.cols(0, r, 128, r);
   }
-  L.n.nvalid = r;
-  L.n.hilo_half = 128;
-  L.n.lo_off = r;
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (nt + KT - 1) / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, (nt + KT - 1) / KT, acc, smem);
   Epi<G256> ep;
   float* part = a.part + ((long)which * a.nsplit + sp) * (long)a.H * r;
 #pragma unroll
@@ -540,7 +482,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, G128::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad, G256::LDS_BYTES);
+    set_lds((const void*)k_w2dgrad, GW2D::LDS_BYTES);
     set_lds((const void*)k_w13dgrad, G256::LDS_BYTES);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, G256::LDS_BYTES);
@@ -549,19 +491,19 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     init = true;
   }
   const int tm = (a.T + 255) / 256;
-  hipLaunchKernelGGL(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
   const long nr = (long)a.T * a.k;
-  hipLaunchKernelGGL(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_w2dgrad, dim3(a.maxtiles * (a.I / 256)), dim3(256), G256::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_w13dgrad, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(256), GW2D::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
-  hipLaunchKernelGGL(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_dx, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(256), G256::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_dx, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;
-  hipLaunchKernelGGL(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -86,62 +86,99 @@ struct Geo {
 // first 32 k of the stage, the second half only the last 32 k (two independent
 // K ranges packed into one stage).
 template <class G, bool SPLIT>
+__device__ __forceinline__ void load_frags(const char* sM, const char* sN, bf16x8 (&a)[G::NB],
+                                           bf16x8 (&b)[G::MB], int kk, int wm, int wn, int lane) {
+  const int r = lane & 31, c = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+    b[mb] = *(const bf16x8*)(sM + lds_off(G::m_local(wm, mb) + r, c));
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb) {
+    if (SPLIT && ((nb < G::NB / 2) != (kk < 2))) continue;
+    a[nb] = *(const bf16x8*)(sN + lds_off(G::n_local(wn, nb) + r, c));
+  }
+}
+
+// One stage of MFMAs.  SPLIT: the first half of the N tile contracts only the
+// first 32 k of the stage, the second half only the last 32 k (two independent
+// K ranges packed into one stage).  Fragments of step kk + 1 are read from LDS
+// while the MFMAs of step kk run.
+template <class G, bool SPLIT>
 __device__ __forceinline__ void mma_stage(const char* sM, const char* sN,
                                           f32x16 (&acc)[G::NB][G::MB], int wm, int wn,
                                           int lane) {
-  const int r = lane & 31, hb = lane >> 5;
+  bf16x8 a[2][G::NB], b[2][G::MB];
+  load_frags<G, SPLIT>(sM, sN, a[0], b[0], 0, wm, wn, lane);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int c = kk * 2 + hb;
-    bf16x8 b[G::MB];
-    bf16x8 a[G::NB];
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
-      b[mb] = *(const bf16x8*)(sM + lds_off(G::m_local(wm, mb) + r, c));
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) {
-      if (SPLIT && ((nb < G::NB / 2) != (kk < 2))) continue;
-      a[nb] = *(const bf16x8*)(sN + lds_off(G::n_local(wn, nb) + r, c));
-    }
+    const int cur = kk & 1;
+    if (kk + 1 < 4) load_frags<G, SPLIT>(sM, sN, a[cur ^ 1], b[cur ^ 1], kk + 1, wm, wn, lane);
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) {
       if (SPLIT && ((nb < G::NB / 2) != (kk < 2))) continue;
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+        acc[nb][mb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][nb], b[cur][mb], acc[nb][mb], 0, 0, 0);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
+// Global loads go through buffer resource descriptors: the base address and
+// the byte extent live in scalar registers, every lane supplies a 32-bit byte
+// offset, and an offset past the extent reads zero in hardware.  Masked rows
+// and k outside a window therefore cost a select, not a branch.  One
+// descriptor covers at most 2 GB; callers base it at the expert, tile or
+// tensor they read.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OFF_NONE = 0x80000000u;
+constexpr uint64_t RSRC_MAX = 0x7FFFFFF0ull;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = (uint32_t)(bytes < RSRC_MAX ? bytes : RSRC_MAX);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
 // RowsK: K-contiguous bf16 rows.  Thread t moves chunk c = t % 8 of tile rows
-// t / 8 + 32 i.  Each row has a window [lo, lo + span) of the stage's k
-// coordinate; inside it the source column is k - lo, folded by `period` when
-// non-zero (used to repeat a rank-r row for the hi and lo halves of a split
-// operand).  Rows with a null pointer and k outside the window read zero.
+// t / 8 + 32 i.  roff[i] is the byte offset of that row in `rs` (OFF_NONE:
+// the row reads zero).  The stage's k coordinate is read through a window
+// [lo, lo + span) where lo = (row >= lo_split ? lo_b : 0); inside it the
+// source column is k - lo, folded by `period` when non-zero (a rank-r row
+// repeated for the hi and lo halves of a split operand).
 // In SPLIT stages chunk c < 4 reads k = k0 + 8c and chunk c >= 4 reads
 // k = khalf + k0 + 8(c - 4).
 // ---------------------------------------------------------------------------
 template <int R>
 struct RowsK {
   static constexpr int NI = R / 32;
-  const uint16_t* rp[NI];
-  int lo[NI];
-  int span, period;
+  rsrc_t rs, rs2;  // rs2 serves tile rows >= R/2 when two_rs (two source tensors)
+  bool two_rs;
+  uint32_t roff[NI];
+  int span, period, lo_split, lo_b;
   u32x4 v[NI];
 
+  __device__ __forceinline__ void window(int span_, int period_ = 0, int lo_split_ = 1 << 30,
+                                         int lo_b_ = 0) {
+    span = span_;
+    period = period_;
+    lo_split = lo_split_;
+    lo_b = lo_b_;
+  }
   __device__ __forceinline__ void load(int k0, int khalf, bool split) {
     const int c = threadIdx.x & 7;
     const int kc = split ? ((c < 4) ? k0 + 8 * c : khalf + k0 + 8 * (c - 4)) : k0 + 8 * c;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      int k = kc - lo[i];
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (rp[i] != nullptr && k >= 0 && k < span) {
-        if (period != 0 && k >= period) k -= period;
-        x = *(const u32x4*)(rp[i] + k);
-      }
-      v[i] = x;
+      const int k = kc - (row_of(i) >= lo_split ? lo_b : 0);
+      const int kk = (period != 0 && k >= period) ? k - period : k;
+      const bool ok = (k >= 0) && (k < span) && (roff[i] != OFF_NONE);
+      v[i] = bload((two_rs && i >= NI / 2) ? rs2 : rs, ok ? roff[i] + 2u * (uint32_t)kk : OFF_NONE);
     }
   }
   __device__ __forceinline__ void store(char* s) const {
@@ -151,16 +188,49 @@ struct RowsK {
   }
   // tile row owned by slot i of this thread
   __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x >> 3) + 32 * i; }
+
+  // rows row0 + j (j < nvalid) of a row-major tensor with `ld` elements per row
+  __device__ __forceinline__ void contig(const uint16_t* base, long row0, long nvalid, long ld) {
+    rs = make_rsrc(base + row0 * ld, (uint64_t)(nvalid > 0 ? nvalid : 0) * ld * 2);
+    two_rs = false;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      roff[i] = (row_of(i) < nvalid) ? (uint32_t)(row_of(i) * ld * 2) : OFF_NONE;
+  }
+  // token of each owned pool row row0 + j (-1 past nvalid), loaded once
+  __device__ static __forceinline__ void tokens(int (&tk)[NI], const int32_t* row2r, int topk,
+                                                long row0, long nvalid) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) tk[i] = (row_of(i) < nvalid) ? row2r[row0 + row_of(i)] / topk : -1;
+  }
+  // rows tk[i] of a token-major tensor (no memory access)
+  __device__ __forceinline__ void from_tokens(const uint16_t* base, long ntok, long ld,
+                                              const int (&tk)[NI]) {
+    rs = make_rsrc(base, (uint64_t)ntok * ld * 2);
+    two_rs = false;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) roff[i] = (tk[i] >= 0) ? (uint32_t)((long)tk[i] * ld * 2) : OFF_NONE;
+  }
+  // pool rows row0 + j (j < nvalid) -> rows (token of the route) of `base`
+  __device__ __forceinline__ void gather(const uint16_t* base, long ntok, long ld,
+                                         const int32_t* row2r, int topk, long row0, long nvalid) {
+    rs = make_rsrc(base, (uint64_t)ntok * ld * 2);
+    two_rs = false;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      roff[i] = (row_of(i) < nvalid) ? (uint32_t)((long)(row2r[row0 + row_of(i)] / topk) * ld * 2)
+                                     : OFF_NONE;
+  }
 };
 
 // ---------------------------------------------------------------------------
 // TransK: K-outer source rows ([k][n], n contiguous).  Tile = R columns x 64 k,
 // made of 8 x 8 blocks; thread t < R handles block (nb = t % (R/8),
-// kb = t / (R/8)).  The k-row pointer comes from the policy KP; the n window
-// is [0, nvalid) of the tile, read from source column n0 + n.  With
-// `hilo_half` > 0 the tile holds two halves: columns [0, half) read source
-// column n0 + n and columns [half, 2 half) read source column n0 + lo_off +
-// (n - half), each valid for n % half < nvalid.
+// kb = t / (R/8)).  The policy KP fetches 16 bytes of k-row k at a column
+// byte offset (zero for rows or columns outside the source).  Tile column n reads source column n0 + n for
+// n < nvalid.  With hilo_half > 0 the tile holds two halves: columns
+// [0, half) read source column n0 + n and columns [half, 2 half) read source
+// column n0 + lo_off + (n - half), each valid for n % half < nvalid.
 // ---------------------------------------------------------------------------
 template <int R, class KP>
 struct TransK {
@@ -168,26 +238,27 @@ struct TransK {
   int n0, nvalid, hilo_half, lo_off;
   u32x4 v[8];
 
-  __device__ __forceinline__ const uint16_t* col_ptr(const uint16_t* row, int nl) const {
+  __device__ __forceinline__ void cols(int n0_, int nvalid_, int hilo_half_ = 0, int lo_off_ = 0) {
+    n0 = n0_;
+    nvalid = nvalid_;
+    hilo_half = hilo_half_;
+    lo_off = lo_off_;
+  }
+  __device__ __forceinline__ uint32_t col_off(int nl) const {
     int n = nl, extra = 0;
-    if (hilo_half > 0 && nl >= hilo_half) { n = nl - hilo_half; extra = lo_off; }
-    if (n >= nvalid) return nullptr;
-    return row + n0 + extra + n;
+    if (hilo_half > 0 && nl >= hilo_half) {
+      n = nl - hilo_half;
+      extra = lo_off;
+    }
+    return (n < nvalid) ? 2u * (uint32_t)(n0 + extra + n) : OFF_NONE;
   }
   __device__ __forceinline__ void load(int k0) {
     const int t = threadIdx.x;
     if (t >= R) return;
     const int nb = t % (R / 8), kb = t / (R / 8);
+    const uint32_t co = col_off(nb * 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t* row = kp.row(k0 + kb * 8 + i);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row != nullptr) {
-        const uint16_t* p = col_ptr(row, nb * 8);
-        if (p != nullptr) x = *(const u32x4*)p;
-      }
-      v[i] = x;
-    }
+    for (int i = 0; i < 8; ++i) v[i] = kp.fetch(k0 + kb * 8 + i, co);
   }
   __device__ __forceinline__ void store(char* s) const {
     const int t = threadIdx.x;
@@ -207,83 +278,101 @@ struct TransK {
 };
 
 // k-row policies for TransK
+__device__ __forceinline__ u32x4 fetch_at(rsrc_t rs, uint32_t ro, uint32_t co) {
+  return bload(rs, (ro != OFF_NONE && co != OFF_NONE) ? ro + co : OFF_NONE);
+}
 struct KStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) folded by period
-  const uint16_t* base;
-  long ld;
+  rsrc_t rs;
+  uint32_t ldb;  // row pitch in bytes
   int lo, span, period;
-  __device__ __forceinline__ const uint16_t* row(int k) const {
+  __device__ __forceinline__ u32x4 fetch(int k, uint32_t co) const {
     int kk = k - lo;
-    if (kk < 0 || kk >= span) return nullptr;
+    const bool ok = kk >= 0 && kk < span;
     if (period != 0 && kk >= period) kk -= period;
-    return base + (long)kk * ld;
+    return fetch_at(rs, ok ? (uint32_t)kk * ldb : OFF_NONE, co);
   }
 };
 struct KTwoMats {  // k in [0, 2r) -> rows of A (period r), [2r, 4r) -> rows of B (period r)
-  const uint16_t* a;
-  const uint16_t* b;
-  long ld;
+  rsrc_t ra, rb;
+  uint32_t ldb;
   int r;
-  __device__ __forceinline__ const uint16_t* row(int k) const {
-    if (k < 0 || k >= 4 * r) return nullptr;
-    const uint16_t* m = (k < 2 * r) ? a : b;
+  __device__ __forceinline__ u32x4 fetch(int k, uint32_t co) const {
+    const bool ok = k >= 0 && k < 4 * r;
     int kk = (k < 2 * r) ? k : k - 2 * r;
     if (kk >= r) kk -= r;
-    return m + (long)kk * ld;
+    const uint32_t ro = ok ? (uint32_t)kk * ldb : OFF_NONE;
+    return (k < 2 * r) ? fetch_at(ra, ro, co) : fetch_at(rb, ro, co);
   }
 };
 struct KRows {  // k-th row of a contiguous range of pool rows or tokens
-  // mode 0: row (row0 + k) of `base`
-  // mode 1: pool row (row0 + k) -> its token's row of `base` (map = row -> route)
-  // mode 2: token (row0 + k) -> the pool row of its first live route
-  //         (map = route -> row); a token with no live route reads zero
-  const uint16_t* base;
-  long ld;
+  // mode 0: row k of the range (rs based at the range's first row)
+  // mode 1: pool row (row0 + k) -> its token's row (rs based at the tensor;
+  //         map = row -> route)
+  // mode 2: token (row0 + k) -> pool row of its first live route, read from
+  //         `base` with a plain load (the whole pool may exceed one
+  //         descriptor); map = route -> row; no live route reads zero
+  rsrc_t rs;
+  uint32_t ldb;
   const int32_t* map;
+  const uint16_t* base;
   int topk;
   int row0, nrows, mode;
-  __device__ __forceinline__ const uint16_t* row(int k) const {
-    if (k >= nrows) return nullptr;
-    long r = row0 + k;
-    if (mode == 1) {
-      r = map[r] / topk;
-    } else if (mode == 2) {
-      long pr = -1;
-      for (int j = 0; j < topk && pr < 0; ++j) pr = map[r * topk + j];
-      if (pr < 0) return nullptr;
-      r = pr;
+  __device__ __forceinline__ u32x4 fetch(int k, uint32_t co) const {
+    if (mode == 2) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k < nrows && co != OFF_NONE) {
+        const long t = row0 + k;
+        long pr = -1;
+        for (int j = 0; j < topk && pr < 0; ++j) pr = map[t * topk + j];
+        if (pr >= 0) v = *(const u32x4*)((const char*)base + pr * (long)ldb + co);
+      }
+      return v;
     }
-    return base + r * ld;
+    uint32_t ro = OFF_NONE;
+    if (k < nrows) ro = (uint32_t)((mode == 1) ? (long)(map[row0 + k] / topk) : (long)k) * ldb;
+    return fetch_at(rs, ro, co);
   }
 };
 
 // ---------------------------------------------------------------------------
 // main loop: `L` provides load(stage) (global -> registers) and
-// store(sM, sN) (registers -> LDS); stages >= split_from use SPLIT MFMAs.
+// store(sM, sN) (registers -> LDS).  run_stages accumulates `nst` stages into
+// acc; consecutive runs (e.g. the base K range, then a low-rank extension with
+// its own loader) share the accumulators.  Each run ends with a barrier so
+// the next run may overwrite the LDS buffers.
 // ---------------------------------------------------------------------------
-template <class G, class L>
-__device__ __forceinline__ void mainloop(L& ld, int nstages, int split_from,
-                                         f32x16 (&acc)[G::NB][G::MB], char* smem) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w / G::WN, wn = w % G::WN;
+template <class G>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[G::NB][G::MB]) {
 #pragma unroll
   for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[nb][mb][q] = 0.0f;
-  if (nstages <= 0) return;
+}
+
+template <class G, bool SPLIT, class L>
+__device__ __forceinline__ void run_stages(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB],
+                                           char* smem) {
+  if (nst <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / G::WN, wn = w % G::WN;
   ld.load(0);
-  for (int s = 0; s < nstages; ++s) {
+  for (int s = 0; s < nst; ++s) {
     char* sM = smem + (s & 1) * G::LDS_STAGE;
     char* sN = sM + G::TM * LROW;
     ld.store(sM, sN);
     __syncthreads();
-    if (s + 1 < nstages) ld.load(s + 1);
-    if (s >= split_from)
-      mma_stage<G, true>(sM, sN, acc, wm, wn, lane);
-    else
-      mma_stage<G, false>(sM, sN, acc, wm, wn, lane);
+    if (s + 1 < nst) ld.load(s + 1);
+    mma_stage<G, SPLIT>(sM, sN, acc, wm, wn, lane);
   }
+  __syncthreads();
+}
+
+template <class G, class L>
+__device__ __forceinline__ void mainloop(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB], char* smem) {
+  zero_acc<G>(acc);
+  run_stages<G, false>(ld, nst, acc, smem);
 }
 
 // Epilogue coordinates of accumulator (nb, mb, group g) for this lane:

@@ -14,6 +14,7 @@
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
 #include "layer.hpp"
+#include "trace.hpp"
 
 namespace moelora {
 
@@ -21,8 +22,6 @@ hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st);
 
 using G256 = Geo<4, 4, 2, 2>;  // 256 x 256 tile, wave 128 x 128
 using G128 = Geo<4, 2, 2, 2>;  // 256 x 128 tile, wave 128 x 64
-
-__device__ __forceinline__ int tok_of_row(const LayerArgs& a, long row) { return a.row2r[row] / a.k; }
 
 // ----------------------------------------------------------------------------
 // a3: ZA = s [A1; A3] x  (dense over tokens; N = 2r)
@@ -36,27 +35,15 @@ struct LdPlain {
 
 __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * G128::TM, n0 = blockIdx.y * G128::TN;
+  const int t0 = blockIdx.x * G128::TM, fac = blockIdx.y;  // fac 0: A1, 1: A3
   const int r = a.r;
   LdPlain L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (t < a.T) ? a.x + (long)t * a.H : nullptr;
-    L.m.lo[i] = 0;
-  }
-  L.m.span = a.H;
-  L.m.period = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = n0 + RowsK<128>::row_of(i);
-    L.n.rp[i] = (c < r) ? a.A1 + (long)c * a.H : (c < 2 * r ? a.A3 + (long)(c - r) * a.H : nullptr);
-    L.n.lo[i] = 0;
-  }
-  L.n.span = a.H;
-  L.n.period = 0;
+  L.m.contig(a.x, t0, a.T - t0, a.H);
+  L.m.window(a.H);
+  L.n.contig(fac ? a.A3 : a.A1, 0, r, a.H);
+  L.n.window(a.H);
   f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.H / KT, 1 << 30, acc, smem);
+  mainloop<G128>(L, a.H / KT, acc, smem);
   Epi<G128> ep;
 #pragma unroll
   for (int nb = 0; nb < G128::NB; ++nb)
@@ -65,18 +52,16 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
       const int t = t0 + ep.row(mb);
       if (t >= a.T) continue;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= r) continue;
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = n0 + ep.col(nb, g) + q;
-          if (c >= 2 * r) continue;
-          uint32_t hi, lo;
-          split_hl(a.s * acc[nb][mb][4 * g + q], hi, lo);
-          const int fac = c / r, cc = c - fac * r;  // 0: A1, 1: A3
-          uint16_t* dst = a.ZA + (long)t * 4 * r + fac * 2 * r + cc;
-          dst[0] = (uint16_t)hi;
-          dst[r] = (uint16_t)lo;
-        }
+        for (int q = 0; q < 4; ++q) split_hl(a.s * acc[nb][mb][4 * g + q], hi[q], lo[q]);
+        uint16_t* dst = a.ZA + (long)t * 4 * r + fac * 2 * r + c;
+        *(u32x2*)dst = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *(u32x2*)(dst + r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      }
     }
 }
 
@@ -84,82 +69,85 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
 // a4: W13 grouped GEMM (+ B1/B3 via K-extension) + SwiGLU
 // N tile = 128 gate columns i0.. and the 128 up columns with the same i.
 // ----------------------------------------------------------------------------
-struct LdW13 {
+struct LdSq {
   RowsK<256> m, n;
-  int nmain, r, topk, row0, row_end, i0;
-  const int32_t* row2r;
-  const uint16_t *ZA, *B1e, *B3e;
-  __device__ void to_ext() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const long row = row0 + RowsK<256>::row_of(i);
-      m.rp[i] = (row < row_end) ? ZA + (long)(row2r[row] / topk) * 4 * r : nullptr;
-      m.lo[i] = 0;
-      const int nl = RowsK<256>::row_of(i);
-      const bool gate = nl < 128;
-      n.rp[i] = (gate ? B1e : B3e) + (long)(i0 + (nl & 127)) * r;
-      n.lo[i] = gate ? 0 : 2 * r;
-    }
-    m.span = 4 * r;
-    m.period = 0;
-    n.span = 2 * r;
-    n.period = r;
-  }
-  __device__ void load(int s) {
-    if (s < nmain) {
-      m.load(s * KT, 0, false);
-      n.load(s * KT, 0, false);
-      return;
-    }
-    if (s == nmain) to_ext();
-    const int se = s - nmain;
-    m.load(se * 32, 2 * r, true);
-    n.load(se * 32, 2 * r, true);
-  }
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
+template <int TN>
+struct LdW13Ext {  // the B1/B3 extension: SPLIT stages of 32 k per half
+  RowsK<256> m;
+  RowsK<TN> n;
+  int r;
+  __device__ void load(int s) {
+    m.load(s * 32, 2 * r, true);
+    n.load(s * 32, 2 * r, true);
+  }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+template <int TN>
+struct LdW13Main {
+  RowsK<256> m;
+  RowsK<TN> n;
+  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
+// N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i.
+using GW13 = G128;
+
 __global__ __launch_bounds__(256) void k_w13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int ntn = a.I / 128;
+  using G = GW13;
+  constexpr int TN = G::TN, HALF = TN / 2;
+  const int ntn = a.I / HALF;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
-  const int e = ti.e, i0 = nt * 128;
-  LdW13 L;
-  L.r = a.r;
-  L.topk = a.k;
-  L.row0 = ti.row0;
-  L.row_end = ti.row_end;
-  L.i0 = i0;
-  L.row2r = a.row2r;
-  L.ZA = a.ZA;
-  L.B1e = a.B1 + (long)e * a.I * a.r;
-  L.B3e = a.B3 + (long)e * a.I * a.r;
-  const uint16_t* W = a.W13 + (long)e * 2 * a.I * a.H;
+  const int e = ti.e, i0 = nt * HALF;
+  const int nrows = ti.row_end - ti.row0;
+  int tk[8];
+  RowsK<256>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  {  // B1/B3 extension first (rank-r K), then the base K = H
+    const int r = a.r;
+    LdW13Ext<TN> L;
+    L.r = r;
+    L.m.from_tokens(a.ZA, a.T, 4 * r, tk);
+    L.m.window(4 * r);
+    L.n.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.n.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.n.two_rs = true;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.Xp + row * a.H : nullptr;
-    L.m.lo[i] = 0;
-    const int nl = RowsK<256>::row_of(i);
-    const int wrow = (nl < 128) ? i0 + nl : a.I + i0 + (nl - 128);
-    L.n.rp[i] = W + (long)wrow * a.H;
-    L.n.lo[i] = 0;
+    for (int i = 0; i < TN / 32; ++i)
+      L.n.roff[i] = (uint32_t)((i0 + (RowsK<TN>::row_of(i) % HALF)) * r * 2);
+    L.n.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
+    run_stages<G, true>(L, (2 * r + 31) / 32, acc, smem);
   }
-  L.m.span = L.n.span = a.H;
-  L.m.period = L.n.period = 0;
-  L.nmain = a.H / KT;
-  const int next = (2 * a.r + 31) / 32;
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, L.nmain + next, L.nmain, acc, smem);
-  Epi<G256> ep;
+  {
+    LdW13Main<TN> L;
+    L.m.contig(a.Xp, ti.row0, nrows, a.H);
+    L.m.window(a.H);
+    L.n.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+    L.n.two_rs = false;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
+    for (int i = 0; i < TN / 32; ++i) {
+      const int nl = RowsK<TN>::row_of(i);
+      const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
+      L.n.roff[i] = (uint32_t)((long)wrow * a.H * 2);
+    }
+    L.n.window(a.H);
+    run_stages<G, false>(L, a.H / KT, acc, smem);
+  }
+  Epi<G> ep;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
     const long row = ti.row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
 #pragma unroll
-    for (int nb = 0; nb < G256::NB / 2; ++nb)
+    for (int nb = 0; nb < G::NB / 2; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int i = i0 + ep.col(nb, g);
@@ -168,7 +156,7 @@ __global__ __launch_bounds__(256) void k_w13(LayerArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float gg = acc[nb][mb][4 * g + q];
-          const float v = acc[nb + G256::NB / 2][mb][4 * g + q];
+          const float v = acc[nb + G::NB / 2][mb][4 * g + q];
           gv[q] = gg;
           vv[q] = v;
           hb[q] = f2bf(gg * sigmoidf_(gg) * v);
@@ -192,22 +180,12 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const uint16_t* A2e = a.A2 + (long)ti.e * a.r * a.I;
   LdPlain L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.Hh + row * a.I : nullptr;
-    L.m.lo[i] = 0;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = RowsK<128>::row_of(i);
-    L.n.rp[i] = (c < a.r) ? A2e + (long)c * a.I : nullptr;
-    L.n.lo[i] = 0;
-  }
-  L.m.span = L.n.span = a.I;
-  L.m.period = L.n.period = 0;
+  L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
+  L.m.window(a.I);
+  L.n.contig(A2e, 0, a.r, a.I);
+  L.n.window(a.I);
   f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.I / KT, 1 << 30, acc, smem);
+  mainloop<G128>(L, a.I / KT, acc, smem);
   Epi<G128> ep;
 #pragma unroll
   for (int mb = 0; mb < G128::MB; ++mb) {
@@ -227,12 +205,6 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   }
 }
 
-struct LdSq {
-  RowsK<256> m, n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
-};
-
 __global__ __launch_bounds__(256) void k_w2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int ntn = a.H / 256;
@@ -242,18 +214,12 @@ __global__ __launch_bounds__(256) void k_w2(LayerArgs a) {
   const int h0 = nt * 256;
   const uint16_t* W = a.W2 + (long)ti.e * a.H * a.I;
   LdSq L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const long row = ti.row0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (row < ti.row_end) ? a.Hh + row * a.I : nullptr;
-    L.m.lo[i] = 0;
-    L.n.rp[i] = W + (long)(h0 + RowsK<256>::row_of(i)) * a.I;
-    L.n.lo[i] = 0;
-  }
-  L.m.span = L.n.span = a.I;
-  L.m.period = L.n.period = 0;
+  L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
+  L.m.window(a.I);
+  L.n.contig(W, h0, 256, a.I);
+  L.n.window(a.I);
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, a.I / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, a.I / KT, acc, smem);
   Epi<G256> ep;
 #pragma unroll
   for (int mb = 0; mb < G256::MB; ++mb) {
@@ -294,20 +260,12 @@ __global__ __launch_bounds__(256) void k_combine(LayerArgs a) {
   const int t0 = blockIdx.x * 256, h0 = blockIdx.y * 256;
   const int r = a.r;
   LdSq L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + RowsK<256>::row_of(i);
-    L.m.rp[i] = (t < a.T) ? a.zc + (long)t * 2 * r : nullptr;
-    L.m.lo[i] = 0;
-    L.n.rp[i] = a.B2 + (long)(h0 + RowsK<256>::row_of(i)) * r;
-    L.n.lo[i] = 0;
-  }
-  L.m.span = 2 * r;
-  L.m.period = 0;
-  L.n.span = 2 * r;
-  L.n.period = r;
+  L.m.contig(a.zc, t0, a.T - t0, 2 * r);
+  L.m.window(2 * r);
+  L.n.contig(a.B2, h0, 256, r);
+  L.n.window(2 * r, r);
   f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (2 * r + KT - 1) / KT, 1 << 30, acc, smem);
+  mainloop<G256>(L, (2 * r + KT - 1) / KT, acc, smem);
   Epi<G256> ep;
 #pragma unroll
   for (int mb = 0; mb < G256::MB; ++mb) {
@@ -350,7 +308,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_shrink, G128::LDS_BYTES);
-    set_lds((const void*)k_w13, G256::LDS_BYTES);
+    set_lds((const void*)k_w13, GW13::LDS_BYTES);
     set_lds((const void*)k_a2, G128::LDS_BYTES);
     set_lds((const void*)k_w2, G256::LDS_BYTES);
     set_lds((const void*)k_combine, G256::LDS_BYTES);
@@ -359,13 +317,13 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   hipError_t err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
   const int tm = (a.T + 255) / 256;
-  hipLaunchKernelGGL(k_shrink, dim3(tm, (2 * a.r + 127) / 128), dim3(256), G128::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_w13, dim3(a.maxtiles * (a.I / 128)), dim3(256), G256::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
-  hipLaunchKernelGGL(k_w2, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(256), GW13::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
   const long nzc = (long)a.T * a.r;
-  hipLaunchKernelGGL(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_combine, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_combine, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 // expert follow ascending route index t*k + j, so the pool is a deterministic
 // function of the routing (the pages' atomic dispatch order is not).
 #include "layer.hpp"
+#include "trace.hpp"
 
 namespace moelora {
 
@@ -112,7 +113,7 @@ hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, lon
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
                              int32_t* err, hipStream_t st) {
   const size_t lds = sizeof(int) * (size_t)(2 * E + 1 + POOL_WAVES * E);
-  hipLaunchKernelGGL(k_build_pool, dim3(1), dim3(POOL_THREADS), lds, st, idx, nroutes, E, bm, cap,
+  MOE_LAUNCH(k_build_pool, dim3(1), dim3(POOL_THREADS), lds, st, idx, nroutes, E, bm, cap,
                      counts, offsets, r2row, row2r, err);
   return hipGetLastError();
 }
@@ -162,9 +163,9 @@ __global__ __launch_bounds__(256) void k_gather(LayerArgs a) {
 }
 
 hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(64), 0, st, a);
+  MOE_LAUNCH(k_tile_map, dim3(1), dim3(64), 0, st, a);
   const long blocks = (a.cap + GATHER_ROWS - 1) / GATHER_ROWS;
-  hipLaunchKernelGGL(k_gather, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_gather, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,18 @@
+// trace.hpp -- per-kernel HIP-event tracing hooks (see trace.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace moelora {
+bool trace_on();
+void trace_begin(hipStream_t st);
+void trace_end(const char* name, hipStream_t st);
+}  // namespace moelora
+
+// Launch a kernel; with tracing on, bracket it with events on its stream.
+#define MOE_LAUNCH(kern, grid, block, lds, st, ...)                  \
+  do {                                                               \
+    const bool moe_tr_ = ::moelora::trace_on();                      \
+    if (moe_tr_) ::moelora::trace_begin(st);                         \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, __VA_ARGS__);     \
+    if (moe_tr_) ::moelora::trace_end(#kern, st);                    \
+  } while (0)

@@ -67,11 +67,14 @@ def _rng(key: Sequence[int], name: str, *extra: int) -> np.random.Generator:
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits.
+    Finite inputs only (uint32 arithmetic cannot overflow for them)."""
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = (u >> 16) & 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

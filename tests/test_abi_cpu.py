@@ -1,0 +1,136 @@
+"""The C ABI on the host (no GPU, no kernel launches): the library loads,
+exports every function include/moelora.h declares, sizes its workspaces as
+documented and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_grouped_amd import binding as B
+from oracle import pool as OP
+from tests import harness as Hn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moelora.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    Hn.ensure_built()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", txt, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_exports_every_declared_function():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    names = declared_functions()
+    assert {"build_pool", "moe_lora_forward", "moe_lora_backward"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTS) <= set(names)
+
+
+def test_version_and_status_strings():
+    lib = B.library()
+    assert lib.moe_lora_version() >= 100
+    for st, text in ((0, "ok"), (-1, "invalid argument"), (-2, "unsupported option"),
+                     (-3, "workspace too small"), (-4, "HIP error")):
+        assert lib.moe_lora_status_string(st).decode() == text
+
+
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 96, 128, 192, 240])
+def test_capacity_matches_the_pool_bound(bm):
+    d = B.make_desc(256, 512, 256, 16, 2, 8, block_m=bm)
+    got_bm = B.moe_lora_block_m(d)
+    assert got_bm == (bm or 16)
+    assert B.moe_lora_pool_capacity(d) == OP.capacity(256, 2, 16, got_bm)
+
+
+def test_workspace_sizes_grow_with_the_problem():
+    small = B.moe_lora_workspace_size(B.make_desc(256, 512, 256, 16, 2, 8))
+    big = B.moe_lora_workspace_size(B.make_desc(16384, 4096, 2048, 64, 6, 128))
+    assert all(s > 0 for s in small)
+    assert big[0] > 3e9 and big[1] > 1e9          # saved holds fp32 G/V for every pool row
+    assert all(b > s for b, s in zip(big, small))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", 0, B.MOE_ERR_INVALID), ("H", -4, B.MOE_ERR_INVALID), ("rank", 0, B.MOE_ERR_INVALID),
+    ("block_m", 48, B.MOE_ERR_INVALID), ("H", 300, B.MOE_ERR_UNSUPPORTED),
+    ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 12, B.MOE_ERR_UNSUPPORTED),
+    ("rank", 256, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
+    ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 1, B.MOE_ERR_UNSUPPORTED),
+    ("clamp", 10.0, B.MOE_ERR_UNSUPPORTED), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
+    ("scale", float("nan"), B.MOE_ERR_INVALID),
+])
+def test_desc_rejections(field, value, status):
+    d = B.make_desc(256, 512, 256, 16, 2, 8)
+    setattr(d, field, value)
+    with pytest.raises(B.MoeLoraError) as ei:
+        B.moe_lora_workspace_size(d)
+    assert ei.value.status == status
+
+
+def test_calls_reject_before_any_launch():
+    """Null or misaligned pointers and short workspaces come back as status
+    codes from the host; nothing reaches the device (there is none here)."""
+    lib = B.library()
+    d = B.make_desc(64, 256, 256, 8, 2, 8)
+    saved, scratch = B.moe_lora_workspace_size(d)
+    cap = B.moe_lora_pool_capacity(d)
+    fake = 1 << 20   # never dereferenced: validation fails first
+    pool = B.MoePool(fake, fake, fake, fake, cap, 16)
+    prm = B.MoeLoraParams(*([fake] * 2 + [None, None] + [fake] * 6))
+    byref = ctypes.byref
+    # null desc
+    assert lib.moe_lora_forward(None, byref(pool), fake, fake, byref(prm), fake + 2 * 64 * 256 * 4,
+                                fake, saved, None, 0, None) == B.MOE_ERR_INVALID
+    # pool capacity that does not match the descriptor
+    bad_pool = B.MoePool(fake, fake, fake, fake, cap - 1, 16)
+    assert lib.moe_lora_forward(byref(d), byref(bad_pool), fake, fake, byref(prm), fake * 64,
+                                fake * 128, saved, None, 0, None) == B.MOE_ERR_INVALID
+    # misaligned x
+    assert lib.moe_lora_forward(byref(d), byref(pool), fake + 2, fake, byref(prm), fake * 64,
+                                fake * 128, saved, None, 0, None) == B.MOE_ERR_INVALID
+    # short saved workspace
+    assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm), fake * 64,
+                                fake * 128, saved - 1, None, 0, None) == B.MOE_ERR_WORKSPACE
+    # MXFP4 scales passed with a bf16 base
+    prm_sc = B.MoeLoraParams(*([fake] * 2 + [fake, None] + [fake] * 6))
+    assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm_sc), fake * 64,
+                                fake * 128, saved, None, 0, None) == B.MOE_ERR_INVALID
+    grads = B.MoeLoraGrads(*([fake * 3] * 6), None, None)
+    # short scratch
+    assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128, saved,
+                                 fake * 64, fake * 200, byref(grads), fake * 256, scratch - 1,
+                                 None) == B.MOE_ERR_WORKSPACE
+    # overlapping grad_x and saved
+    assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128, saved,
+                                 fake * 128, fake * 200, byref(grads), fake * 4096, scratch,
+                                 None) == B.MOE_ERR_INVALID
+    # build_pool with a capacity that does not match
+    assert lib.build_pool(byref(d), fake, fake, fake, fake, fake, cap + 1, None, None) == B.MOE_ERR_INVALID
+
+
+def test_binding_checks_shapes_before_calling():
+    """The Python binding refuses host tensors (no silent CPU path)."""
+    import torch
+    d = B.make_desc(64, 256, 256, 8, 2, 8)
+    idx = torch.zeros(64, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.build_pool(d, idx, torch.zeros(8, dtype=torch.int32), torch.zeros(9, dtype=torch.int32),
+                     torch.zeros(128, dtype=torch.int32), torch.zeros(10, dtype=torch.int32))
+
+
+def test_flop_model_matches_the_closed_form():
+    """bench.py's algorithmic FLOP count: per-kernel sums equal the F+B total."""
+    import bench
+    T, M, H, Id, r = 16384, 98304, 4096, 2048, 128
+    f, b = bench.step_flops(T, M, H, Id, r)
+    assert abs(f / 1e12 - 5.154) < 2e-3 and abs(b / 1e12 - 5.360) < 2e-3
+    assert abs(sum(bench.kernel_flops(T, M, H, Id, r).values()) - (f + b)) < 1.0
