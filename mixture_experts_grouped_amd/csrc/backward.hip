@@ -16,6 +16,7 @@
 //   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
+#include "engine2.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
 
@@ -110,49 +111,58 @@ __global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a9: dh = w (W2_e^T go + A2_e^T s q), SwiGLU backward -> dG, dV
 // ----------------------------------------------------------------------------
-using GW2D = G128;
+using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
+// Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
 struct LdW2d {
-  RowsK<256> m;
-  TransK<GW2D::TN, KStrided> n;
-  __device__ void load(int s) {
-    m.load(s * KT, 0, false);
-    n.load(s * KT);
+  using KL = v2::KLoad<256, GW2D::KT, GW2D::NW>;
+  using TL = v2::TLoad<256, v2::TStrided, GW2D::KT, GW2D::NW>;
+  using KA = v2::KLoadA<256, GW2D::KT, GW2D::NW>;
+  using TA = v2::TLoadA<256, GW2D::KT, GW2D::NW>;
+  static constexpr int INSTS = KL::NJ + TL::NJ;
+  KL me;
+  KA mm;
+  TL ne;
+  TA nm;
+  int next;
+  static constexpr int nsplit = 0;
+  __device__ void issue(int s, char* sM, char* sN) const {
+    if (s < next) {
+      me.issue(s * GW2D::KT, 0, false, sM);
+      ne.issue(s * GW2D::KT, sN);
+    } else {
+      mm.issue((s - next) * GW2D::KT, sM);
+      nm.issue((s - next) * GW2D::KT, sN);
+    }
   }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
-__global__ __launch_bounds__(256) void k_w2dgrad(LayerArgs a) {
+__global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2D;
+  using KL = LdW2d::KL;
   const int ntn = a.I / G::TN;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
   const int i0 = nt * G::TN;
   const int nrows = ti.row_end - ti.row0;
-  int tk[8];
-  RowsK<256>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  const int r = a.r;
+  LdW2d L;
+  L.next = (2 * r + G::KT - 1) / G::KT;
+  {
+    int tk[KL::NJ];
+    KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+    L.me.from_tokens(a.sq, a.T, 2 * r, tk);
+    L.mm.from_tokens(a.go, a.T, a.H, tk);
+  }
+  L.me.window(2 * r);
+  L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+                         (uint32_t)(2 * a.I), 0, 2 * r, r};
+  L.ne.cols(i0, G::TN);
+  L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  {  // A2^T (s q) extension first (rank-r K), then the base K = H
-    const int r = a.r;
-    LdW2d L;
-    L.m.from_tokens(a.sq, a.T, 2 * r, tk);
-    L.m.window(2 * r);
-    L.n.kp = KStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
-                      (uint32_t)(2 * a.I), 0, 2 * r, r};
-    L.n.cols(i0, G::TN);
-    run_stages<G, false>(L, (2 * r + KT - 1) / KT, acc, smem);
-  }
-  {
-    LdW2d L;
-    L.m.from_tokens(a.go, a.T, a.H, tk);
-    L.m.window(a.H);
-    L.n.kp = KStrided{make_rsrc(a.W2 + (long)ti.e * a.H * a.I, (uint64_t)a.H * a.I * 2),
-                      (uint32_t)(2 * a.I), 0, a.H, 0};
-    L.n.cols(i0, G::TN);
-    run_stages<G, false>(L, a.H / KT, acc, smem);
-  }
+  v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
   Epi<G> ep;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
@@ -166,19 +176,17 @@ __global__ __launch_bounds__(256) void k_w2dgrad(LayerArgs a) {
         const int i = i0 + ep.col(nb, g);
         const f32x4 gg = *(const f32x4*)(a.G + row * a.I + i);
         const f32x4 vv = *(const f32x4*)(a.V + row * a.I + i);
-        uint32_t dgb[4], dvb[4];
+        float dg[4], dv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float dh = wr * acc[nb][mb][4 * g + q];
           const float sg = sigmoidf_(gg[q]);
-          const float dg = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
-          const float dv = dh * gg[q] * sg;
-          dgb[q] = f2bf(dg);
-          dvb[q] = f2bf(dv);
+          dg[q] = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          dv[q] = dh * gg[q] * sg;
         }
         uint16_t* d = a.dGV + row * 2 * a.I + i;
-        *(u32x2*)d = u32x2{dgb[0] | (dgb[1] << 16), dgb[2] | (dgb[3] << 16)};
-        *(u32x2*)(d + a.I) = u32x2{dvb[0] | (dvb[1] << 16), dvb[2] | (dvb[3] << 16)};
+        *(u32x2*)d = u32x2{pack2(dg[0], dg[1]), pack2(dg[2], dg[3])};
+        *(u32x2*)(d + a.I) = u32x2{pack2(dv[0], dv[1]), pack2(dv[2], dv[3])};
       }
   }
 }
@@ -186,35 +194,41 @@ __global__ __launch_bounds__(256) void k_w2dgrad(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a10: dU = W13_e^T [dg; dv]   (K = 2I, weights read K-outer)
 // ----------------------------------------------------------------------------
+using GW13D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 struct LdW13d {
-  RowsK<256> m;
-  TransK<256, KStrided> n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+  using KL = v2::KLoad<256, GW13D::KT, GW13D::NW>;
+  using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
+  using TA = v2::TLoadA<256, GW13D::KT, GW13D::NW>;
+  static constexpr int INSTS = KA::NJ + TA::NJ;
+  KA m;
+  TA n;
+  __device__ void issue(int s, char* sM, char* sN) const {
+    m.issue(s * GW13D::KT, sM);
+    n.issue(s * GW13D::KT, sN);
+  }
 };
 
-__global__ __launch_bounds__(256) void k_w13dgrad(LayerArgs a) {
+__global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int ntn = a.H / 256;
+  using G = GW13D;
+  const int ntn = a.H / G::TN;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
-  const int h0 = nt * 256;
+  const int h0 = nt * G::TN;
   LdW13d L;
   L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
-  L.m.window(2 * a.I);
-  L.n.kp = KStrided{make_rsrc(a.W13 + (long)ti.e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2),
-                    (uint32_t)(2 * a.H), 0, 2 * a.I, 0};
-  L.n.cols(h0, 256);
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, 2 * a.I / KT, acc, smem);
-  Epi<G256> ep;
+  L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  Epi<G> ep;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
+  for (int mb = 0; mb < G::MB; ++mb) {
     const long row = ti.row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
 #pragma unroll
-    for (int nb = 0; nb < G256::NB; ++nb)
+    for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int h = h0 + ep.col(nb, g);
@@ -483,7 +497,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   if (!init) {
     set_lds((const void*)k_q, G128::LDS_BYTES);
     set_lds((const void*)k_w2dgrad, GW2D::LDS_BYTES);
-    set_lds((const void*)k_w13dgrad, G256::LDS_BYTES);
+    set_lds((const void*)k_w13dgrad, GW13D::LDS_BYTES);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, G256::LDS_BYTES);
     set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
@@ -494,8 +508,8 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
   const long nr = (long)a.T * a.k;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(256), GW2D::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), GW2D::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), GW13D::LDS_BYTES, st, a);
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);

@@ -45,14 +45,14 @@ __device__ __forceinline__ int lds_off(int row, int c) {
   return row * LROW + ((c ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16, round to nearest even (NaN stays NaN): v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack2(f, 0.0f) & 0xffffu; }
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
 // two-term bf16 split of an fp32 value: v ~= hi + lo to about 16 significant bits
 __device__ __forceinline__ void split_hl(float v, uint32_t& hi, uint32_t& lo) {
   hi = f2bf(v);
@@ -391,6 +391,26 @@ struct Epi {
     return G::n_local(wn, nb) + 8 * g + 4 * (lane >> 5);
   }
 };
+
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8) and each XCD has its own L2.  xcd_remap turns the hardware id into a
+// logical id such that every XCD walks a contiguous range of logical tiles.
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  const int x = b & 7, j = b >> 3;
+  const int q = nblocks >> 3, rem = nblocks & 7;
+  return x * q + (x < rem ? x : rem) + j;
+}
+// Logical tile L of an (nm x nn) grid, visited in groups of gm M tiles: inside
+// a group the M index runs fastest, so concurrent tiles share both the row
+// slabs (M) and the weight slabs (N) in L2.
+__device__ __forceinline__ void grouped_tile(int L, int nm, int nn, int gm, int& mt, int& nt) {
+  const int per = gm * nn;
+  const int g = L / per, r = L - g * per;
+  const int size = (nm - g * gm < gm) ? nm - g * gm : gm;
+  mt = g * gm + r % size;
+  nt = r / size;
+}
+constexpr int GROUP_M = 8;
 
 // Grouped-GEMM M tile: rows [row0, row_end) of expert e in the pool.
 struct TileInfo {

@@ -1,0 +1,428 @@
+// engine2.hpp -- bf16 MFMA tile engine for gfx950 with direct-to-LDS loads.
+//
+// Same tile geometry and accumulator layout as engine.hpp (256 threads, four
+// wave64s, v_mfma_f32_32x32x16_bf16, lanes own output rows, four consecutive
+// output columns per register group), but the operands travel from global
+// memory straight into LDS with `buffer_load_dwordx4 ... lds`: no staging
+// registers, no LDS write instructions.  A stage is KT = 32 or 64 k deep;
+// NBUF = 4 or 2 stages live in LDS (NBUF - 1 stages of loads in flight while
+// one is multiplied).  The barrier between stages carries no memory fence:
+// each wave first waits (vmcnt) for its own loads of the stage it is about to
+// read, so prefetched stages stay in flight across the barrier.
+//
+// A wave's direct load writes 64 lanes x 16 bytes = 1 KB contiguous at a
+// wave-uniform LDS address (lane L at +16 L); an out-of-range buffer offset
+// writes zeros.  Tiles are therefore laid out so that every 1 KB is a run of
+// whole rows, and each lane picks the global chunk that its slot must hold.
+//
+// Two tile layouts:
+//   K tile  [rows][KT k], 2 KT bytes per row, 16-byte chunk c of row r stored
+//           in slot c ^ f(r): for KT = 32, f(r) = ((r>>1 ^ r>>3) & 1) |
+//           ((r>>2 & 1) << 1); for KT = 64, f(r) = (r ^ r>>3) & 7.  Fragment
+//           reads (ds_read_b128, 32 rows x 8 k per lane group) hit distinct
+//           banks under both 8-lane and 16-lane service.
+//   T tile  [KT k][cols] (K-outer source), pitch 2*cols bytes, chunk j of
+//           row k in slot j ^ 2(k & 3); fragments come from two
+//           ds_read_b64_tr_b16 per lane: inside every 16-lane group lane i
+//           receives element (i & 3) of the 8-byte reads of lanes
+//           4q + (i >> 2), q = 0..3 (probed on the device), which turns four
+//           k-rows of 16 columns into four consecutive k of one column.
+#pragma once
+#include "engine.hpp"
+
+namespace moelora {
+namespace v2 {
+
+template <int KT>
+struct Depth {
+  static_assert(KT == 32 || KT == 64, "stage depth");
+  static constexpr int NBUF = (KT == 32) ? 4 : 2;
+  static constexpr int KROW = 2 * KT;     // bytes per K-tile row
+  static constexpr int CPR = KT / 8;      // 16-byte chunks per K-tile row
+  static constexpr int RPI = 64 / CPR;    // K-tile rows per 1 KB wave instruction
+  static constexpr int KSTEPS = KT / 16;  // MFMA k16 steps per stage
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int KT>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (KT == 32)
+    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+  else
+    return (r ^ (r >> 3)) & 7;
+}
+template <int KT>
+__device__ __forceinline__ int koff(int r, int c) {
+  return r * Depth<KT>::KROW + ((c ^ kswz<KT>(r)) << 4);
+}
+__device__ __forceinline__ int toff(int k, int j, int pitch) {
+  return k * pitch + ((j ^ ((k & 3) << 1)) << 4);
+}
+
+__device__ __forceinline__ void lds_load16(rsrc_t rs, char* lds_wave_base, uint32_t off,
+                                           uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave_base, 16, off, soff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// geometry
+// ---------------------------------------------------------------------------
+template <int MB_, int NB_, int WM_, int WN_, bool MTR_ = false, bool NTR_ = false, int KT_ = 64>
+struct Geo2 {
+  static constexpr int MB = MB_, NB = NB_, WM = WM_, WN = WN_, KT = KT_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;  // waves and threads per workgroup
+  static constexpr int NBUF = Depth<KT>::NBUF;
+  static constexpr bool MTR = MTR_, NTR = NTR_;  // operand tile stored K-outer (T tile)
+  static constexpr int TM = WM * MB * 32, TN = WN * NB * 32;
+  static constexpr int SM_BYTES = TM * 2 * KT, SN_BYTES = TN * 2 * KT;  // same for both layouts
+  static constexpr int STAGE = SM_BYTES + SN_BYTES;
+  static constexpr int LDS_BYTES = NBUF * STAGE;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NB % 2 == 0, "N blocks come in pairs");
+  __device__ static constexpr int m_local(int wm, int mb) { return (wm * MB + mb) * 32; }
+  __device__ static constexpr int n_local(int wn, int nb) {
+    return (nb < NB / 2 ? 0 : TN / 2) + (wn * (NB / 2) + (nb % (NB / 2))) * 32;
+  }
+};
+
+// MFMA operand for 32 rows/columns starting at `base` and k16 step kk.
+template <bool TR, int COLS, int KT>
+__device__ __forceinline__ bf16x8 frag(const char* tile, int base, int kk, int lane) {
+  if constexpr (!TR) {
+    const int r = base + (lane & 31);
+    return *(const bf16x8*)(tile + koff<KT>(r, 2 * kk + (lane >> 5)));
+  } else {
+    constexpr int P = COLS * 2;
+    const int g = lane >> 4, i = lane & 15;
+    const int n = base + 16 * (g & 1) + 4 * (i & 3);
+    const int kb = 16 * kk + 8 * (g >> 1) + (i >> 2);
+    s16x4 v0, v1;
+    {
+      const int k = kb;
+      v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + toff(k, n >> 3, P) + (n & 7) * 2));
+    }
+    {
+      const int k = kb + 4;
+      v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + toff(k, n >> 3, P) + (n & 7) * 2));
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 w = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+template <class G, bool SPLIT>
+__device__ __forceinline__ void load_frags2(const char* sM, const char* sN, bf16x8 (&a)[G::NB],
+                                            bf16x8 (&b)[G::MB], int kk, int wm, int wn, int lane) {
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+    b[mb] = frag<G::MTR, G::TM, G::KT>(sM, G::m_local(wm, mb), kk, lane);
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb) {
+    if (SPLIT && ((nb < G::NB / 2) != (kk < G::KT / 32))) continue;
+    a[nb] = frag<G::NTR, G::TN, G::KT>(sN, G::n_local(wn, nb), kk, lane);
+  }
+}
+
+// KT/16 k16 steps; fragments of step kk + 1 are read while step kk
+// multiplies.  SPLIT: the first half of the N tile contracts only the first
+// half of the stage's k, the second half only the second (two K ranges in one
+// stage).
+template <class G, bool SPLIT>
+__device__ __forceinline__ void mma_stage2(const char* sM, const char* sN,
+                                           f32x16 (&acc)[G::NB][G::MB], int wm, int wn, int lane) {
+  constexpr int KS = G::KT / 16;
+  bf16x8 a[2][G::NB], b[2][G::MB];
+  load_frags2<G, SPLIT>(sM, sN, a[0], b[0], 0, wm, wn, lane);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < KS) load_frags2<G, SPLIT>(sM, sN, a[cur ^ 1], b[cur ^ 1], kk + 1, wm, wn, lane);
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+      if (SPLIT && ((nb < G::NB / 2) != (kk < KS / 2))) continue;
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[nb][mb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][nb], b[cur][mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// loaders.  `issue(stage, tile)` queues this thread's direct loads of one
+// stage into `tile` (the operand's LDS tile of that stage).
+// ---------------------------------------------------------------------------
+
+// K tile of R rows (K-contiguous source).  Wave w's instruction j covers tile
+// rows RPI (w + 4j) .. +RPI-1; lane L holds row RPI (w + 4j) + L/CPR, slot
+// L % CPR.  Row window and folding as in RowsK.  SPLIT stages are KT/2 k per
+// half: chunks c < CPR/2 read k = k0 + 8c, the others khalf + k0 + 8(c - CPR/2).
+template <int R, int KT = 64, int NW = 4, bool TWO = false>
+struct KLoad {
+  static constexpr int CPR = Depth<KT>::CPR, RPI = Depth<KT>::RPI;
+  static constexpr int NJ = R / (NW * RPI);
+  static_assert(NJ >= 1 && NJ * NW * RPI == R, "tile rows per stage");
+  static_assert(!TWO || NJ % 2 == 0, "two descriptors split the tile rows in halves");
+  rsrc_t rs, rs2;  // with TWO, rs2 serves tile rows >= R/2 (a second source tensor)
+  uint32_t roff[NJ];
+  int span, period, lo_split, lo_b;
+
+  __device__ static __forceinline__ int row_of(int j) {
+    return RPI * ((threadIdx.x >> 6) + NW * j) + (threadIdx.x & 63) / CPR;
+  }
+  __device__ __forceinline__ void window(int span_, int period_ = 0, int lo_split_ = 1 << 30,
+                                         int lo_b_ = 0) {
+    span = span_;
+    period = period_;
+    lo_split = lo_split_;
+    lo_b = lo_b_;
+  }
+  __device__ __forceinline__ void contig(const uint16_t* base, long row0, long nvalid, long ld) {
+    rs = make_rsrc(base + row0 * ld, (uint64_t)(nvalid > 0 ? nvalid : 0) * ld * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      roff[j] = (row_of(j) < nvalid) ? (uint32_t)(row_of(j) * ld * 2) : OFF_NONE;
+  }
+  __device__ static __forceinline__ void tokens(int (&tk)[NJ], const int32_t* row2r, int topk,
+                                                long row0, long nvalid) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) tk[j] = (row_of(j) < nvalid) ? row2r[row0 + row_of(j)] / topk : -1;
+  }
+  __device__ __forceinline__ void from_tokens(const uint16_t* base, long ntok, long ld,
+                                              const int (&tk)[NJ]) {
+    rs = make_rsrc(base, (uint64_t)ntok * ld * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) roff[j] = (tk[j] >= 0) ? (uint32_t)((long)tk[j] * ld * 2) : OFF_NONE;
+  }
+  __device__ __forceinline__ void issue(int k0, int khalf, bool split, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = row_of(j);
+      const int c = (threadIdx.x % CPR) ^ kswz<KT>(r);
+      const int kc = split ? ((c < CPR / 2) ? k0 + 8 * c : khalf + k0 + 8 * (c - CPR / 2))
+                           : k0 + 8 * c;
+      const int k = kc - (r >= lo_split ? lo_b : 0);
+      const int kk = (period != 0 && k >= period) ? k - period : k;
+      const bool ok = (k >= 0) && (k < span) && (roff[j] != OFF_NONE);
+      lds_load16((TWO && 2 * j >= NJ) ? rs2 : rs, tile + 1024 * (w + NW * j),
+                 ok ? roff[j] + 2u * (uint32_t)kk : OFF_NONE);
+    }
+  }
+};
+
+// K tile loader for a K range made of whole stages (every stage reads k0 ..
+// k0 + KT - 1 of each row, all in range): each lane's byte offset is fixed
+// at set-up and the stage's k0 travels in the scalar offset, so an issue
+// costs no vector arithmetic.  A row outside the range has offset OFF_NONE,
+// which stays beyond the descriptor's size whatever the scalar offset adds.
+template <int R, int KT = 64, int NW = 4>
+struct KLoadA {
+  static constexpr int CPR = Depth<KT>::CPR, RPI = Depth<KT>::RPI;
+  static constexpr int NJ = R / (NW * RPI);
+  static_assert(NJ >= 1 && NJ * NW * RPI == R, "tile rows per stage");
+  rsrc_t rs;
+  uint32_t voff[NJ];
+
+  __device__ static __forceinline__ int row_of(int j) { return KLoad<R, KT, NW>::row_of(j); }
+  __device__ static __forceinline__ uint32_t chunk(int j) {
+    return 16u * (uint32_t)((threadIdx.x % CPR) ^ kswz<KT>(row_of(j)));
+  }
+  // rows row0 .. row0 + nvalid - 1 of a row-major matrix with ld elements a row
+  __device__ __forceinline__ void contig(const uint16_t* base, long row0, long nvalid, long ld) {
+    rs = make_rsrc(base + row0 * ld, (uint64_t)(nvalid > 0 ? nvalid : 0) * ld * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      voff[j] = (row_of(j) < nvalid) ? (uint32_t)(row_of(j) * ld * 2) + chunk(j) : OFF_NONE;
+  }
+  // tile row j of this lane reads the row at byte offset roff (OFF_NONE: zeros)
+  __device__ __forceinline__ void set_row(int j, uint32_t roff) {
+    voff[j] = (roff != OFF_NONE) ? roff + chunk(j) : OFF_NONE;
+  }
+  // tile row j reads token tk[j]'s row of a [ntok, ld] matrix (tk < 0: zeros)
+  __device__ __forceinline__ void from_tokens(const uint16_t* base, long ntok, long ld,
+                                              const int (&tk)[NJ]) {
+    rs = make_rsrc(base, (uint64_t)ntok * ld * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) set_row(j, (tk[j] >= 0) ? (uint32_t)((long)tk[j] * ld * 2) : OFF_NONE);
+  }
+  __device__ __forceinline__ void issue(int k0, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) lds_load16(rs, tile + 1024 * (w + NW * j), voff[j], 2u * (uint32_t)k0);
+  }
+};
+
+// T tile of R columns x KT k (K-outer source).  1 KB holds 512/R k-rows;
+// wave w's instruction j covers k-rows RPI (w + 4j) .. +RPI-1 with
+// RPI = 512 / R; lane L holds k-row RPI (w + 4j) + L / (R/8), slot L % (R/8).
+// Column mapping as in TransK (window, hi/lo halves).
+template <int R, class KP, int KT = 64, int NW = 4>
+struct TLoad {
+  static constexpr int CPR = R / 8;           // 16-byte chunks per k-row
+  static constexpr int RPI = 64 / CPR;        // k-rows per wave instruction
+  static constexpr int NJ = KT / (NW * RPI);  // instructions per wave per stage
+  static_assert(NJ >= 1 && NJ * NW * RPI == KT, "k-rows per stage");
+  KP kp;
+  int n0, nvalid, hilo_half, lo_off;
+
+  __device__ __forceinline__ void cols(int n0_, int nvalid_, int hilo_half_ = 0, int lo_off_ = 0) {
+    n0 = n0_;
+    nvalid = nvalid_;
+    hilo_half = hilo_half_;
+    lo_off = lo_off_;
+  }
+  __device__ __forceinline__ uint32_t col_off(int nl) const {
+    int n = nl, extra = 0;
+    if (hilo_half > 0 && nl >= hilo_half) {
+      n = nl - hilo_half;
+      extra = lo_off;
+    }
+    return (n < nvalid) ? 2u * (uint32_t)(n0 + extra + n) : OFF_NONE;
+  }
+  __device__ __forceinline__ void issue(int k0, char* tile) const {
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kr = RPI * (w + NW * j) + L / CPR;
+      const int jc = (L % CPR) ^ ((kr & 3) << 1);
+      kp.issue_lds(k0 + kr, col_off(8 * jc), tile + 1024 * (w + NW * j));
+    }
+  }
+};
+
+// T tile loader for a K range made of whole stages of a row-major [K, ld]
+// matrix, columns n0 .. n0 + R - 1 (all in range): offsets fixed at set-up,
+// the stage's first k-row in the scalar offset (as KLoadA).
+template <int R, int KT = 64, int NW = 4>
+struct TLoadA {
+  static constexpr int CPR = R / 8, RPI = 64 / CPR, NJ = KT / (NW * RPI);
+  static_assert(NJ >= 1 && NJ * NW * RPI == KT, "k-rows per stage");
+  rsrc_t rs;
+  uint32_t ldb;  // bytes per k-row
+  uint32_t voff[NJ];
+  __device__ __forceinline__ void set(const uint16_t* base, long nk, long ld, int n0) {
+    rs = make_rsrc(base, (uint64_t)nk * ld * 2);
+    ldb = (uint32_t)(ld * 2);
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kr = RPI * (w + NW * j) + L / CPR;
+      const int jc = (L % CPR) ^ ((kr & 3) << 1);
+      voff[j] = (uint32_t)kr * ldb + 2u * (uint32_t)(n0 + 8 * jc);
+    }
+  }
+  __device__ __forceinline__ void issue(int k0, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) lds_load16(rs, tile + 1024 * (w + NW * j), voff[j], (uint32_t)k0 * ldb);
+  }
+};
+
+// k-row policies of TLoad (the K-outer source's row for k)
+struct TStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) folded by period
+  rsrc_t rs;
+  uint32_t ldb;
+  int lo, span, period;
+  __device__ __forceinline__ void issue_lds(int k, uint32_t co, char* lds) const {
+    int kk = k - lo;
+    const bool ok = kk >= 0 && kk < span && co != OFF_NONE;
+    if (period != 0 && kk >= period) kk -= period;
+    lds_load16(rs, lds, ok ? (uint32_t)kk * ldb + co : OFF_NONE);
+  }
+};
+struct TRows {  // k-th row of a contiguous range of pool rows or tokens
+  // mode 0: row k of the range (rs based at the range's first row)
+  // mode 1: pool row (row0 + k) -> its token's row (map = row -> route)
+  // mode 2: token (row0 + k) -> pool row of its first live route
+  //         (map = route -> row); no live route reads zero
+  rsrc_t rs;
+  uint32_t ldb;
+  const int32_t* map;
+  int topk;
+  int row0, nrows, mode;
+  __device__ __forceinline__ void issue_lds(int k, uint32_t co, char* lds) const {
+    uint32_t ro = OFF_NONE;
+    if (k < nrows) {
+      long r = k;
+      if (mode == 1) {
+        r = map[row0 + k] / topk;
+      } else if (mode == 2) {
+        const long t = row0 + k;
+        long pr = -1;
+        for (int j = 0; j < topk && pr < 0; ++j) pr = map[t * topk + j];
+        r = pr;
+      }
+      if (r >= 0) ro = (uint32_t)r * ldb;
+    }
+    lds_load16(rs, lds, (ro != OFF_NONE && co != OFF_NONE) ? ro + co : OFF_NONE);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// main loop: `L` provides issue(stage, sM, sN) and the compile-time count
+// INSTS of direct-load instructions one wave issues per stage.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose fence
+// waits for every outstanding load, including stages prefetched ahead).  The
+// caller has already waited for the loads the next stage needs.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+// One pipeline step: wait for stage s, release the buffer stage s - 1 used,
+// queue stage s + NBUF - 1 into it, multiply stage s.
+template <class G, bool SPLIT, class L>
+__device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB][G::MB],
+                                      char* smem, int wm, int wn, int lane) {
+  constexpr int IN = L::INSTS, NBUF = G::NBUF;
+  const int left = nst - 1 - s;  // stages issued after s that may stay in flight
+  if (NBUF >= 4 && left >= 2)
+    wait_vm<2 * IN>();
+  else if (NBUF >= 3 && left >= 1)
+    wait_vm<IN>();
+  else
+    wait_vm<0>();
+  bar();
+  if (s + NBUF - 1 < nst) {
+    const int b = (s + NBUF - 1) % NBUF;
+    ld.issue(s + NBUF - 1, smem + b * G::STAGE, smem + b * G::STAGE + G::SM_BYTES);
+  }
+  const char* sM = smem + (s % NBUF) * G::STAGE;
+  mma_stage2<G, SPLIT>(sM, sM + G::SM_BYTES, acc, wm, wn, lane);
+}
+
+// SPLIT: 0 = no stage is split, 1 = every stage, 2 = stages s < ld.nsplit
+// (a low-rank extension run first, in the same pipeline as the base K range;
+// the two kinds of stage run in loops of their own so that each loop body
+// holds one fragment schedule).
+template <class G, int SPLIT, class L>
+__device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB],
+                                            char* smem) {
+  if (nst <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / G::WN, wn = w % G::WN;
+  constexpr int NBUF = G::NBUF;
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nst) ld.issue(p, smem + p * G::STAGE, smem + p * G::STAGE + G::SM_BYTES);
+  int s = 0;
+  if constexpr (SPLIT == 2) {
+    const int ns = ld.nsplit < nst ? ld.nsplit : nst;
+    for (; s < ns; ++s) step2<G, true>(ld, s, nst, acc, smem, wm, wn, lane);
+  }
+  for (; s < nst; ++s) step2<G, SPLIT == 1>(ld, s, nst, acc, smem, wm, wn, lane);
+  __syncthreads();
+}
+
+}  // namespace v2
+}  // namespace moelora

@@ -13,6 +13,7 @@
 //   k_combine   out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
+#include "engine2.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
 
@@ -75,31 +76,36 @@ struct LdSq {
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
-template <int TN>
-struct LdW13Ext {  // the B1/B3 extension: SPLIT stages of 32 k per half
-  RowsK<256> m;
-  RowsK<TN> n;
-  int r;
-  __device__ void load(int s) {
-    m.load(s * 32, 2 * r, true);
-    n.load(s * 32, 2 * r, true);
+// N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i;
+// each wave holds a gate block and its up partner, so SwiGLU runs in registers.
+using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
+
+// Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
+// stage); stages [nsplit, ...): the base K = H.
+struct LdW13 {
+  using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
+  using KL2 = v2::KLoad<256, GW13::KT, GW13::NW, true>;
+  using KA = v2::KLoadA<256, GW13::KT, GW13::NW>;
+  static constexpr int INSTS = 2 * KL::NJ;
+  KL me;
+  KL2 ne;
+  KA mm, nm;
+  int r, nsplit;
+  __device__ void issue(int s, char* sM, char* sN) const {
+    if (s < nsplit) {
+      me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
+      ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
+    } else {
+      mm.issue((s - nsplit) * GW13::KT, sM);
+      nm.issue((s - nsplit) * GW13::KT, sN);
+    }
   }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
-};
-template <int TN>
-struct LdW13Main {
-  RowsK<256> m;
-  RowsK<TN> n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
-// N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i.
-using GW13 = G128;
-
-__global__ __launch_bounds__(256) void k_w13(LayerArgs a) {
+__global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13;
+  using KL = LdW13::KL;
   constexpr int TN = G::TN, HALF = TN / 2;
   const int ntn = a.I / HALF;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
@@ -107,40 +113,32 @@ __global__ __launch_bounds__(256) void k_w13(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const int e = ti.e, i0 = nt * HALF;
   const int nrows = ti.row_end - ti.row0;
-  int tk[8];
-  RowsK<256>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  const int r = a.r;
+  LdW13 L;
+  L.r = r;
+  L.nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
+  {
+    int tk[KL::NJ];
+    KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+    L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
+  }
+  L.me.window(4 * r);
+  L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+  L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+#pragma unroll
+  for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
+  L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
+  L.mm.contig(a.Xp, ti.row0, nrows, a.H);
+  L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+#pragma unroll
+  for (int j = 0; j < KL::NJ; ++j) {
+    const int nl = KL::row_of(j);
+    const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
+    L.nm.set_row(j, (uint32_t)((long)wrow * a.H * 2));
+  }
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  {  // B1/B3 extension first (rank-r K), then the base K = H
-    const int r = a.r;
-    LdW13Ext<TN> L;
-    L.r = r;
-    L.m.from_tokens(a.ZA, a.T, 4 * r, tk);
-    L.m.window(4 * r);
-    L.n.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-    L.n.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-    L.n.two_rs = true;
-#pragma unroll
-    for (int i = 0; i < TN / 32; ++i)
-      L.n.roff[i] = (uint32_t)((i0 + (RowsK<TN>::row_of(i) % HALF)) * r * 2);
-    L.n.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
-    run_stages<G, true>(L, (2 * r + 31) / 32, acc, smem);
-  }
-  {
-    LdW13Main<TN> L;
-    L.m.contig(a.Xp, ti.row0, nrows, a.H);
-    L.m.window(a.H);
-    L.n.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
-    L.n.two_rs = false;
-#pragma unroll
-    for (int i = 0; i < TN / 32; ++i) {
-      const int nl = RowsK<TN>::row_of(i);
-      const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
-      L.n.roff[i] = (uint32_t)((long)wrow * a.H * 2);
-    }
-    L.n.window(a.H);
-    run_stages<G, false>(L, a.H / KT, acc, smem);
-  }
+  v2::run_stages2<G, 2>(L, L.nsplit + a.H / G::KT, acc, smem);
   Epi<G> ep;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
@@ -152,19 +150,18 @@ __global__ __launch_bounds__(256) void k_w13(LayerArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int i = i0 + ep.col(nb, g);
         f32x4 gv, vv;
-        uint32_t hb[4];
+        float hv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float gg = acc[nb][mb][4 * g + q];
           const float v = acc[nb + G::NB / 2][mb][4 * g + q];
           gv[q] = gg;
           vv[q] = v;
-          hb[q] = f2bf(gg * sigmoidf_(gg) * v);
+          hv[q] = gg * sigmoidf_(gg) * v;
         }
         *(f32x4*)(a.G + row * a.I + i) = gv;
         *(f32x4*)(a.V + row * a.I + i) = vv;
-        u32x2 hp = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-        *(u32x2*)(a.Hh + row * a.I + i) = hp;
+        *(u32x2*)(a.Hh + row * a.I + i) = u32x2{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
       }
   }
 }
@@ -205,28 +202,39 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_w2(LayerArgs a) {
+using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
+struct LdW2 {
+  using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
+  static constexpr int INSTS = 2 * KL::NJ;
+  KL m, n;
+  __device__ void issue(int s, char* sM, char* sN) const {
+    m.issue(s * GW2::KT, sM);
+    n.issue(s * GW2::KT, sN);
+  }
+};
+
+__global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int ntn = a.H / 256;
+  using G = GW2;
+  const int ntn = a.H / G::TN;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
-  const int h0 = nt * 256;
+  const int h0 = nt * G::TN;
   const uint16_t* W = a.W2 + (long)ti.e * a.H * a.I;
-  LdSq L;
+  LdW2 L;
   L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
-  L.m.window(a.I);
-  L.n.contig(W, h0, 256, a.I);
-  L.n.window(a.I);
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, a.I / KT, acc, smem);
-  Epi<G256> ep;
+  L.n.contig(W, h0, G::TN, a.I);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  Epi<G> ep;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
+  for (int mb = 0; mb < G::MB; ++mb) {
     const long row = ti.row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
 #pragma unroll
-    for (int nb = 0; nb < G256::NB; ++nb)
+    for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int h = h0 + ep.col(nb, g);
@@ -310,7 +318,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_shrink, G128::LDS_BYTES);
     set_lds((const void*)k_w13, GW13::LDS_BYTES);
     set_lds((const void*)k_a2, G128::LDS_BYTES);
-    set_lds((const void*)k_w2, G256::LDS_BYTES);
+    set_lds((const void*)k_w2, GW2::LDS_BYTES);
     set_lds((const void*)k_combine, G256::LDS_BYTES);
     init = true;
   }
@@ -318,9 +326,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   const int tm = (a.T + 255) / 256;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(256), GW13::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), GW13::LDS_BYTES, st, a);
   MOE_LAUNCH(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / 256)), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), GW2::LDS_BYTES, st, a);
   const long nzc = (long)a.T * a.r;
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_combine, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
