@@ -17,6 +17,7 @@
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
 #include "engine2.hpp"
+#include "gather_sum.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
 
@@ -305,50 +306,40 @@ __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
 // a12: grad_x = [A1; A3]^T pc + sum_j dU
 // ----------------------------------------------------------------------------
 struct LdDx {
-  RowsK<256> m;
-  TransK<256, KTwoMats> n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+  using KM = v2::KLoad<GGS_T::TM, GGS_T::KT, GGS_T::NW>;
+  using TN = v2::TLoad<GGS_T::TN, v2::TStrided, GGS_T::KT, GGS_T::NW>;
+  static constexpr int INSTS = KM::NJ + TN::NJ;
+  KM m;
+  TN n;
+  int koff;  // first pc column of the pass
+  __device__ void issue(int s, char* sM, char* sN) const {
+    m.issue(koff + s * GGS_T::KT, 0, false, sM);
+    n.issue(s * GGS_T::KT, sN);
+  }
 };
 
-__global__ __launch_bounds__(256) void k_dx(LayerArgs a) {
+// Two passes over the rank space: pc columns [0, 2r) against A1 (hi/lo
+// halves fold onto the same r rows), then [2r, 4r) against A3.
+__global__ __launch_bounds__(GGS_T::NT) void k_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * 256, h0 = blockIdx.y * 256;
+  const int t0 = blockIdx.x * GGS_T::TM, h0 = blockIdx.y * GGS_T::TN;
   const int r = a.r;
+  const int nst = (2 * r + GGS_T::KT - 1) / GGS_T::KT;
   LdDx L;
   L.m.contig(a.pc, t0, a.T - t0, 4 * r);
+  L.n.cols(h0, GGS_T::TN);
+  f32x16 acc[GGS_T::NB][GGS_T::MB];
+  zero_acc<GGS_T>(acc);
+  L.m.window(2 * r);
+  L.koff = 0;
+  L.n.kp = v2::TStrided{make_rsrc(a.A1, (uint64_t)r * a.H * 2), (uint32_t)(2 * a.H), 0, 2 * r, r};
+  v2::run_stages2<GGS_T, 0>(L, nst, acc, smem);
   L.m.window(4 * r);
-  L.n.kp = KTwoMats{make_rsrc(a.A1, (uint64_t)r * a.H * 2), make_rsrc(a.A3, (uint64_t)r * a.H * 2),
-                    (uint32_t)(2 * a.H), r};
-  L.n.cols(h0, 256);
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (4 * r + KT - 1) / KT, acc, smem);
-  Epi<G256> ep;
-#pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
-    const int t = t0 + ep.row(mb);
-    if (t >= a.T) continue;
-#pragma unroll
-    for (int nb = 0; nb < G256::NB; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int h = h0 + ep.col(nb, g);
-        float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = acc[nb][mb][4 * g + q];
-        for (int j = 0; j < a.k; ++j) {
-          const int row = a.r2row[t * a.k + j];
-          if (row < 0) continue;
-          const u32x2 u = *(const u32x2*)(a.dU + (long)row * a.H + h);
-          o[0] += bf2f(u[0] & 0xffffu);
-          o[1] += bf2f(u[0] >> 16);
-          o[2] += bf2f(u[1] & 0xffffu);
-          o[3] += bf2f(u[1] >> 16);
-        }
-        u32x2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-        *(u32x2*)(a.gx + (long)t * a.H + h) = ov;
-      }
-  }
+  L.koff = 2 * r;
+  L.n.kp = v2::TStrided{make_rsrc(a.A3, (uint64_t)r * a.H * 2), (uint32_t)(2 * a.H), 0, 2 * r, r};
+  v2::run_stages2<GGS_T, 0>(L, nst, acc, smem);
+  park_tile(acc, smem);
+  gather_rows<false>(smem, a, a.dU, a.gx, t0, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -499,7 +490,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_w2dgrad, GW2D::LDS_BYTES);
     set_lds((const void*)k_w13dgrad, GW13D::LDS_BYTES);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
-    set_lds((const void*)k_dx, G256::LDS_BYTES);
+    set_lds((const void*)k_dx, GS_LDS);
     set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
     set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
     init = true;
@@ -513,7 +504,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_dx, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_dx, dim3((a.T + GGS_T::TM - 1) / GGS_T::TM, a.H / GGS_T::TN), dim3(GGS_T::NT), GS_LDS, st, a);
   MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(256), G256::LDS_BYTES, st, a);
   MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;

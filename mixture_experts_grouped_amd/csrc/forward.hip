@@ -14,6 +14,7 @@
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
 #include "engine2.hpp"
+#include "gather_sum.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
 
@@ -263,48 +264,32 @@ __global__ __launch_bounds__(256) void k_zc(LayerArgs a) {
   a.zc[(long)t * 2 * a.r + a.r + c] = (uint16_t)lo;
 }
 
-__global__ __launch_bounds__(256) void k_combine(LayerArgs a) {
+struct LdComb {
+  using KM = v2::KLoad<GGS::TM, GGS::KT, GGS::NW>;
+  using KN = v2::KLoad<GGS::TN, GGS::KT, GGS::NW>;
+  static constexpr int INSTS = KM::NJ + KN::NJ;
+  KM m;
+  KN n;
+  __device__ void issue(int s, char* sM, char* sN) const {
+    m.issue(s * GGS::KT, 0, false, sM);
+    n.issue(s * GGS::KT, 0, false, sN);
+  }
+};
+
+__global__ __launch_bounds__(GGS::NT) void k_combine(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * 256, h0 = blockIdx.y * 256;
+  const int t0 = blockIdx.x * GGS::TM, h0 = blockIdx.y * GGS::TN;
   const int r = a.r;
-  LdSq L;
+  LdComb L;
   L.m.contig(a.zc, t0, a.T - t0, 2 * r);
   L.m.window(2 * r);
-  L.n.contig(a.B2, h0, 256, r);
+  L.n.contig(a.B2, h0, GGS::TN, r);
   L.n.window(2 * r, r);
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (2 * r + KT - 1) / KT, acc, smem);
-  Epi<G256> ep;
-#pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
-    const int t = t0 + ep.row(mb);
-    if (t >= a.T) continue;
-    int rows[16];
-    float ws[16];
-    for (int j = 0; j < a.k; ++j) {
-      rows[j] = a.r2row[t * a.k + j];
-      ws[j] = a.w[t * a.k + j];
-    }
-#pragma unroll
-    for (int nb = 0; nb < G256::NB; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int h = h0 + ep.col(nb, g);
-        float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = acc[nb][mb][4 * g + q];
-        for (int j = 0; j < a.k; ++j) {
-          if (rows[j] < 0) continue;
-          const u32x2 y = *(const u32x2*)(a.Yb + (long)rows[j] * a.H + h);
-          o[0] += ws[j] * bf2f(y[0] & 0xffffu);
-          o[1] += ws[j] * bf2f(y[0] >> 16);
-          o[2] += ws[j] * bf2f(y[1] & 0xffffu);
-          o[3] += ws[j] * bf2f(y[1] >> 16);
-        }
-        u32x2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-        *(u32x2*)(a.out + (long)t * a.H + h) = ov;
-      }
-  }
+  f32x16 acc[GGS::NB][GGS::MB];
+  zero_acc<GGS>(acc);
+  v2::run_stages2<GGS, 0>(L, (2 * r + GGS::KT - 1) / GGS::KT, acc, smem);
+  park_tile(acc, smem);
+  gather_rows<true>(smem, a, a.Yb, a.out, t0, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -319,7 +304,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_w13, GW13::LDS_BYTES);
     set_lds((const void*)k_a2, G128::LDS_BYTES);
     set_lds((const void*)k_w2, GW2::LDS_BYTES);
-    set_lds((const void*)k_combine, G256::LDS_BYTES);
+    set_lds((const void*)k_combine, GS_LDS);
     init = true;
   }
   hipError_t err = launch_pool_prologue(a, st);
@@ -331,7 +316,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), GW2::LDS_BYTES, st, a);
   const long nzc = (long)a.T * a.r;
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_combine, dim3(tm, a.H / 256), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_combine, dim3((a.T + GGS::TM - 1) / GGS::TM, a.H / GGS::TN), dim3(GGS::NT), GS_LDS, st, a);
   return hipGetLastError();
 }
 
