@@ -142,8 +142,8 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   using G = GW2D;
   using KL = LdW2d::KL;
   const int ntn = a.I / G::TN;
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (mt >= *a.ntiles) return;
+  int mt, nt;
+  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int i0 = nt * G::TN;
   const int nrows = ti.row_end - ti.row0;
@@ -196,6 +196,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 // a10: dU = W13_e^T [dg; dv]   (K = 2I, weights read K-outer)
 // ----------------------------------------------------------------------------
 using GW13D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
+constexpr int W13D_LDS = cmax(GW13D::LDS_BYTES, v2::TileImage<GW13D, GW13D::TN, uint16_t>::BYTES);
 struct LdW13d {
   using KL = v2::KLoad<256, GW13D::KT, GW13D::NW>;
   using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
@@ -213,8 +214,8 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13D;
   const int ntn = a.H / G::TN;
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (mt >= *a.ntiles) return;
+  int mt, nt;
+  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
   LdW13d L;
@@ -223,21 +224,19 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
-    if (row >= ti.row_end) continue;
+  for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int h = h0 + ep.col(nb, g);
-        u32x2 o = {pack2(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1]),
-                   pack2(acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3])};
-        *(u32x2*)(a.dU + row * a.H + h) = o;
-      }
-  }
+      for (int g = 0; g < 4; ++g)
+        Img::put(smem, ep.row(mb), ep.col(nb, g),
+                 f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                       acc[nb][mb][4 * g + 3]});
+  __syncthreads();
+  Img::flush(smem, a.dU + ti.row0 * (long)a.H + h0, a.H, ti.row_end - ti.row0);
 }
 
 // ----------------------------------------------------------------------------
@@ -488,7 +487,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   if (!init) {
     set_lds((const void*)k_q, G128::LDS_BYTES);
     set_lds((const void*)k_w2dgrad, GW2D::LDS_BYTES);
-    set_lds((const void*)k_w13dgrad, GW13D::LDS_BYTES);
+    set_lds((const void*)k_w13dgrad, W13D_LDS);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, GS_LDS);
     set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
@@ -500,7 +499,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   const long nr = (long)a.T * a.k;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), GW2D::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), GW13D::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);

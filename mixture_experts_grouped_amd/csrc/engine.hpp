@@ -132,6 +132,8 @@ __device__ __forceinline__ void mma_stage(const char* sM, const char* sN,
 // descriptor covers at most 2 GB; callers base it at the expert, tile or
 // tensor they read.
 // ---------------------------------------------------------------------------
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t OFF_NONE = 0x80000000u;
 constexpr uint64_t RSRC_MAX = 0x7FFFFFF0ull;
@@ -411,6 +413,23 @@ __device__ __forceinline__ void grouped_tile(int L, int nm, int nn, int gm, int&
   nt = r / size;
 }
 constexpr int GROUP_M = 8;
+
+// Workgroup b of a grid over (at most) maxtiles x nn tiles, of which the first
+// ntm M tiles are live: false for a dead workgroup; else the live tiles are
+// dealt so that each XCD owns a contiguous range of them, visited in groups of
+// gm M tiles.  The ranges are cut from the live count, not the grid size, so
+// every XCD gets the same share.  gm <= 0 keeps the plain row-major order.
+__device__ __forceinline__ bool live_tile(int b, int ntm, int nn, int gm, int& mt, int& nt) {
+  const int n = ntm * nn;
+  if (b >= n) return false;
+  if (gm <= 0) {
+    mt = b / nn;
+    nt = b - mt * nn;
+  } else {
+    grouped_tile(xcd_remap(b, n), ntm, nn, gm, mt, nt);
+  }
+  return true;
+}
 
 // Grouped-GEMM M tile: rows [row0, row_end) of expert e in the pool.
 struct TileInfo {

@@ -401,6 +401,39 @@ __device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB
   mma_stage2<G, SPLIT>(sM, sM + G::SM_BYTES, acc, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Epilogue through LDS.  A lane's accumulators are four consecutive columns
+// of one row, so a direct store instruction touches 32 rows.  Instead the
+// waves park their values in an LDS image of the tile (rows padded by 16
+// bytes) and the workgroup then writes whole rows, 16 bytes a lane.  Use
+// after run_stages2, whose closing barrier frees LDS.
+// ---------------------------------------------------------------------------
+template <class G, int COLS, typename OUT>
+struct TileImage {
+  static constexpr int ES = sizeof(OUT);
+  static_assert(ES == 2 || ES == 4, "bf16 bits or fp32");
+  static constexpr int PITCH = COLS * ES + 16;  // bytes per image row
+  static constexpr int BYTES = G::TM * PITCH;
+  static constexpr int CPRW = COLS * ES / 16;   // 16-byte chunks per row
+  // values of (row, col .. col + 3), tile coordinates
+  __device__ static __forceinline__ void put(char* smem, int row, int col, f32x4 v) {
+    char* p = smem + row * PITCH + col * ES;
+    if constexpr (ES == 4)
+      *(f32x4*)p = v;
+    else
+      *(u32x2*)p = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+  }
+  // rows [0, nrows) of the image -> out (ld elements per row); call between
+  // two barriers (after the puts, before LDS is reused)
+  __device__ static __forceinline__ void flush(const char* smem, OUT* out, long ld, int nrows) {
+    const int lim = (nrows < G::TM ? nrows : G::TM) * CPRW;
+    for (int idx = threadIdx.x; idx < lim; idx += G::NT) {
+      const int r = idx / CPRW, c = idx - r * CPRW;
+      *(u32x4*)((char*)(out + (long)r * ld) + 16 * c) = *(const u32x4*)(smem + r * PITCH + 16 * c);
+    }
+  }
+};
+
 // SPLIT: 0 = no stage is split, 1 = every stage, 2 = stages s < ld.nsplit
 // (a low-rank extension run first, in the same pipeline as the base K range;
 // the two kinds of stage run in loops of their own so that each loop body

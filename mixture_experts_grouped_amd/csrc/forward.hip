@@ -80,6 +80,7 @@ struct LdSq {
 // N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i;
 // each wave holds a gate block and its up partner, so SwiGLU runs in registers.
 using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
+constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, float>::BYTES);
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
 // stage); stages [nsplit, ...): the base K = H.
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   using KL = LdW13::KL;
   constexpr int TN = G::TN, HALF = TN / 2;
   const int ntn = a.I / HALF;
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (mt >= *a.ntiles) return;
+  int mt, nt;
+  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int e = ti.e, i0 = nt * HALF;
   const int nrows = ti.row_end - ti.row0;
@@ -140,30 +141,36 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 2>(L, L.nsplit + a.H / G::KT, acc, smem);
+  // G and V (fp32) and h (bf16) leave through LDS images of the tile
+  using ImgF = v2::TileImage<G, HALF, float>;
+  using ImgH = v2::TileImage<G, HALF, uint16_t>;
   Epi<G> ep;
+  constexpr int NH = G::NB / 2;
+  const long base = ti.row0 * (long)a.I + i0;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
-    if (row >= ti.row_end) continue;
+  for (int part = 0; part < 3; ++part) {
 #pragma unroll
-    for (int nb = 0; nb < G::NB / 2; ++nb)
+    for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i = i0 + ep.col(nb, g);
-        f32x4 gv, vv;
-        float hv[4];
+      for (int nb = 0; nb < NH; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float gg = acc[nb][mb][4 * g + q];
-          const float v = acc[nb + G::NB / 2][mb][4 * g + q];
-          gv[q] = gg;
-          vv[q] = v;
-          hv[q] = gg * sigmoidf_(gg) * v;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gg = acc[nb][mb][4 * g + q], vv = acc[nb + NH][mb][4 * g + q];
+            v[q] = part == 0 ? gg : part == 1 ? vv : gg * sigmoidf_(gg) * vv;
+          }
+          if (part < 2)
+            ImgF::put(smem, ep.row(mb), ep.col(nb, g), v);
+          else
+            ImgH::put(smem, ep.row(mb), ep.col(nb, g), v);
         }
-        *(f32x4*)(a.G + row * a.I + i) = gv;
-        *(f32x4*)(a.V + row * a.I + i) = vv;
-        *(u32x2*)(a.Hh + row * a.I + i) = u32x2{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
-      }
+    __syncthreads();
+    if (part == 0) ImgF::flush(smem, a.G + base, a.I, nrows);
+    if (part == 1) ImgF::flush(smem, a.V + base, a.I, nrows);
+    if (part == 2) ImgH::flush(smem, a.Hh + base, a.I, nrows);
+    __syncthreads();
   }
 }
 
@@ -204,6 +211,7 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
 }
 
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
+constexpr int W2_LDS = cmax(GW2::LDS_BYTES, v2::TileImage<GW2, GW2::TN, uint16_t>::BYTES);
 struct LdW2 {
   using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
   static constexpr int INSTS = 2 * KL::NJ;
@@ -218,8 +226,8 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2;
   const int ntn = a.H / G::TN;
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (mt >= *a.ntiles) return;
+  int mt, nt;
+  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
   const uint16_t* W = a.W2 + (long)ti.e * a.H * a.I;
@@ -229,21 +237,19 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
-    if (row >= ti.row_end) continue;
+  for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int h = h0 + ep.col(nb, g);
-        u32x2 o = {pack2(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1]),
-                   pack2(acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3])};
-        *(u32x2*)(a.Yb + row * a.H + h) = o;
-      }
-  }
+      for (int g = 0; g < 4; ++g)
+        Img::put(smem, ep.row(mb), ep.col(nb, g),
+                 f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                       acc[nb][mb][4 * g + 3]});
+  __syncthreads();
+  Img::flush(smem, a.Yb + ti.row0 * (long)a.H + h0, a.H, ti.row_end - ti.row0);
 }
 
 // ----------------------------------------------------------------------------
@@ -301,9 +307,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_shrink, G128::LDS_BYTES);
-    set_lds((const void*)k_w13, GW13::LDS_BYTES);
+    set_lds((const void*)k_w13, W13_LDS);
     set_lds((const void*)k_a2, G128::LDS_BYTES);
-    set_lds((const void*)k_w2, GW2::LDS_BYTES);
+    set_lds((const void*)k_w2, W2_LDS);
     set_lds((const void*)k_combine, GS_LDS);
     init = true;
   }
@@ -311,9 +317,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   const int tm = (a.T + 255) / 256;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), GW13::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
   MOE_LAUNCH(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), GW2::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   const long nzc = (long)a.T * a.r;
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_combine, dim3((a.T + GGS::TM - 1) / GGS::TM, a.H / GGS::TN), dim3(GGS::NT), GS_LDS, st, a);

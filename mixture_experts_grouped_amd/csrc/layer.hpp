@@ -9,6 +9,7 @@
 namespace moelora {
 
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
+constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
 
 // Everything a kernel may touch, passed by value as the kernel argument.
 // Pool-shaped tensors have `cap` rows; token-shaped tensors have T rows.
