@@ -74,8 +74,8 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_ntiles = take(sizeof(int));
   p.o_Xp = take(cap * H * 2);
   p.o_ZA = take(T * 4 * r * 2);
-  p.o_G = take(cap * I * 4);
-  p.o_V = take(cap * I * 4);
+  p.o_G = take((size_t)p.maxtiles * TMG * I * 4);  // accumulator-blocked per M tile
+  p.o_V = take((size_t)p.maxtiles * TMG * I * 4);
   p.o_Hh = take(cap * I * 2);
   p.o_Z2 = take(cap * r * 4);
   p.o_Yb = take(cap * H * 2);

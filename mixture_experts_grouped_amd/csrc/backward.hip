@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
 // a9: dh = w (W2_e^T go + A2_e^T s q), SwiGLU backward -> dG, dV
 // ----------------------------------------------------------------------------
 using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
+constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES);
 // Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
 struct LdW2d {
   using KL = v2::KLoad<256, GW2D::KT, GW2D::NW>;
@@ -164,31 +165,49 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
+  // G and V come in accumulator-blocked (as the forward wrote them); dg and
+  // dv leave row-major through LDS images, one half of the tile's columns
+  // (one accumulator block column per wave) at a time
+  using Img = v2::TileImage<G, G::TN / 2, uint16_t>;
+  static_assert(G::NB == 2, "one block column per half");
   Epi<G> ep;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform block offsets
+  const int wm = wv / G::WN, wn = wv % G::WN, lane = threadIdx.x & 63;
+  float wr[G::MB];
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
-    if (row >= ti.row_end) continue;
-    const float wr = a.w[a.row2r[row]];
+    const int lr = ep.row(mb);
+    wr[mb] = lr < nrows ? a.w[a.row2r[ti.row0 + lr]] : 0.0f;
+  }
+  char* img_g = smem;
+  char* img_v = smem + Img::BYTES;
+  uint16_t* out = a.dGV + ti.row0 * 2 * (long)a.I + i0;
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb)
+  for (int nb = 0; nb < G::NB; ++nb) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const long ob = acc_block(mt, G::m_local(wm, mb) / 32, (i0 + G::n_local(wn, nb)) / 32, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int i = i0 + ep.col(nb, g);
-        const f32x4 gg = *(const f32x4*)(a.G + row * a.I + i);
-        const f32x4 vv = *(const f32x4*)(a.V + row * a.I + i);
-        float dg[4], dv[4];
+        const f32x4 gg = *(const f32x4*)(a.G + ob + 256 * g);
+        const f32x4 vv = *(const f32x4*)(a.V + ob + 256 * g);
+        f32x4 dg, dv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float dh = wr * acc[nb][mb][4 * g + q];
+          const float dh = wr[mb] * acc[nb][mb][4 * g + q];
           const float sg = sigmoidf_(gg[q]);
-          dg[q] = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
           dv[q] = dh * gg[q] * sg;
+          dg[q] = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
         }
-        uint16_t* d = a.dGV + row * 2 * a.I + i;
-        *(u32x2*)d = u32x2{pack2(dg[0], dg[1]), pack2(dg[2], dg[3])};
-        *(u32x2*)(d + a.I) = u32x2{pack2(dv[0], dv[1]), pack2(dv[2], dv[3])};
+        const int col = ep.col(nb, g) - nb * (G::TN / 2);
+        Img::put(img_g, ep.row(mb), col, dg);
+        Img::put(img_v, ep.row(mb), col, dv);
       }
+    }
+    __syncthreads();
+    Img::flush(img_g, out + nb * (G::TN / 2), 2 * a.I, nrows);
+    Img::flush(img_v, out + a.I + nb * (G::TN / 2), 2 * a.I, nrows);
+    __syncthreads();
   }
 }
 
@@ -486,7 +505,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, G128::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad, GW2D::LDS_BYTES);
+    set_lds((const void*)k_w2dgrad, W2D_LDS);
     set_lds((const void*)k_w13dgrad, W13D_LDS);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, GS_LDS);
@@ -498,7 +517,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
   const long nr = (long)a.T * a.k;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), GW2D::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
   MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;

@@ -57,8 +57,13 @@ template <int KT>
 __device__ __forceinline__ int koff(int r, int c) {
   return r * Depth<KT>::KROW + ((c ^ kswz<KT>(r)) << 4);
 }
+// T tiles: 16-byte chunk j of k-row k sits in slot j ^ tswz(k).  A transposed
+// fragment read touches chunks c .. c + 3 of k-rows k0 .. k0 + 3 and
+// k0 + 8 .. k0 + 11; shifting by 4 chunks per k-row spreads the four rows of
+// each half over all sixteen 16-byte bank groups (rows at least 16 chunks wide).
+__device__ __forceinline__ int tswz(int k) { return (k & 3) << 2; }
 __device__ __forceinline__ int toff(int k, int j, int pitch) {
-  return k * pitch + ((j ^ ((k & 3) << 1)) << 4);
+  return k * pitch + ((j ^ tswz(k)) << 4);
 }
 
 __device__ __forceinline__ void lds_load16(rsrc_t rs, char* lds_wave_base, uint32_t off,
@@ -265,6 +270,7 @@ struct KLoadA {
 template <int R, class KP, int KT = 64, int NW = 4>
 struct TLoad {
   static constexpr int CPR = R / 8;           // 16-byte chunks per k-row
+  static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per k-row");
   static constexpr int RPI = 64 / CPR;        // k-rows per wave instruction
   static constexpr int NJ = KT / (NW * RPI);  // instructions per wave per stage
   static_assert(NJ >= 1 && NJ * NW * RPI == KT, "k-rows per stage");
@@ -290,7 +296,7 @@ struct TLoad {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int kr = RPI * (w + NW * j) + L / CPR;
-      const int jc = (L % CPR) ^ ((kr & 3) << 1);
+      const int jc = (L % CPR) ^ tswz(kr);
       kp.issue_lds(k0 + kr, col_off(8 * jc), tile + 1024 * (w + NW * j));
     }
   }
@@ -302,6 +308,7 @@ struct TLoad {
 template <int R, int KT = 64, int NW = 4>
 struct TLoadA {
   static constexpr int CPR = R / 8, RPI = 64 / CPR, NJ = KT / (NW * RPI);
+  static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per k-row");
   static_assert(NJ >= 1 && NJ * NW * RPI == KT, "k-rows per stage");
   rsrc_t rs;
   uint32_t ldb;  // bytes per k-row
@@ -313,7 +320,7 @@ struct TLoadA {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int kr = RPI * (w + NW * j) + L / CPR;
-      const int jc = (L % CPR) ^ ((kr & 3) << 1);
+      const int jc = (L % CPR) ^ tswz(kr);
       voff[j] = (uint32_t)kr * ldb + 2u * (uint32_t)(n0 + 8 * jc);
     }
   }

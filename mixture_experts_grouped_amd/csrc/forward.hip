@@ -80,7 +80,7 @@ struct LdSq {
 // N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i;
 // each wave holds a gate block and its up partner, so SwiGLU runs in registers.
 using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
-constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, float>::BYTES);
+constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, uint16_t>::BYTES);
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
 // stage); stages [nsplit, ...): the base K = H.
@@ -141,37 +141,35 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 2>(L, L.nsplit + a.H / G::KT, acc, smem);
-  // G and V (fp32) and h (bf16) leave through LDS images of the tile
-  using ImgF = v2::TileImage<G, HALF, float>;
+  // G and V go out in the accumulator-blocked layout (1 KB per wave access);
+  // h (bf16, row-major for the next GEMM) through an LDS image of the tile
   using ImgH = v2::TileImage<G, HALF, uint16_t>;
   Epi<G> ep;
   constexpr int NH = G::NB / 2;
-  const long base = ti.row0 * (long)a.I + i0;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform block offsets
+  const int wm = wv / G::WN, wn = wv % G::WN, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int part = 0; part < 3; ++part) {
+  for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
+    for (int nb = 0; nb < NH; ++nb) {
+      const int cb = (i0 + G::n_local(wn, nb)) / 32;
+      const long ob = acc_block(mt, G::m_local(wm, mb) / 32, cb, a.I) + 4 * lane;
 #pragma unroll
-      for (int nb = 0; nb < NH; ++nb)
+      for (int g = 0; g < 4; ++g) {
+        f32x4 gv, vv, hv;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gg = acc[nb][mb][4 * g + q], vv = acc[nb + NH][mb][4 * g + q];
-            v[q] = part == 0 ? gg : part == 1 ? vv : gg * sigmoidf_(gg) * vv;
-          }
-          if (part < 2)
-            ImgF::put(smem, ep.row(mb), ep.col(nb, g), v);
-          else
-            ImgH::put(smem, ep.row(mb), ep.col(nb, g), v);
+        for (int q = 0; q < 4; ++q) {
+          gv[q] = acc[nb][mb][4 * g + q];
+          vv[q] = acc[nb + NH][mb][4 * g + q];
+          hv[q] = gv[q] * sigmoidf_(gv[q]) * vv[q];
         }
-    __syncthreads();
-    if (part == 0) ImgF::flush(smem, a.G + base, a.I, nrows);
-    if (part == 1) ImgF::flush(smem, a.V + base, a.I, nrows);
-    if (part == 2) ImgH::flush(smem, a.Hh + base, a.I, nrows);
-    __syncthreads();
-  }
+        *(f32x4*)(a.G + ob + 256 * g) = gv;
+        *(f32x4*)(a.V + ob + 256 * g) = vv;
+        ImgH::put(smem, ep.row(mb), ep.col(nb, g), hv);
+      }
+    }
+  __syncthreads();
+  ImgH::flush(smem, a.Hh + ti.row0 * (long)a.I + i0, a.I, nrows);
 }
 
 // ----------------------------------------------------------------------------

@@ -11,6 +11,15 @@ namespace moelora {
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
 constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
 
+// Accumulator-blocked layout of a [tiles x 256, I] fp32 tensor that is written
+// and read only by kernels holding it in 32 x 32 MFMA accumulator blocks: block
+// (M tile mt, row block rb of 8, column block cb of I/32) is 1024 floats,
+// ordered [g (4)][lane (64)][q (4)] so that the lane's accumulator values
+// 4g .. 4g + 3 are one 16-byte access and a wave's access is 1 KB contiguous.
+__device__ __forceinline__ long acc_block(int mt, int rb, int cb, int I) {
+  return ((long)(mt * 8 + rb) * (I / 32) + cb) * 1024;
+}
+
 // Everything a kernel may touch, passed by value as the kernel argument.
 // Pool-shaped tensors have `cap` rows; token-shaped tensors have T rows.
 // bf16 tensors are uint16 bit patterns.  "_hl" tensors hold an fp32 quantity
@@ -36,8 +45,8 @@ struct LayerArgs {
   int* ntiles;       // [1]
   uint16_t* Xp;      // [cap, H]  gathered expert input, padding rows zero
   uint16_t* ZA;      // [T, 4r]   s*A1 x, s*A3 x as hi/lo
-  float* G;          // [cap, I]  gate pre-activation
-  float* V;          // [cap, I]  up pre-activation
+  float* G;          // gate pre-activation, accumulator-blocked (acc_block)
+  float* V;          // up pre-activation, same layout
   uint16_t* Hh;      // [cap, I]  silu(G) * V
   float* Z2;         // [cap, r]  s * A2_e h
   uint16_t* Yb;      // [cap, H]  W2_e h (unweighted base output)
