@@ -112,6 +112,21 @@ def cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, target_s)
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """A plain copy of COPY_BYTES: it reads and writes exactly that many bytes of
+    HBM, so byte counters read over it give the counter's scale."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +136,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--base", choices=("bf16", "mxfp4"), default="bf16",
+                    help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
+                         "quantised from the same seeded bf16 weights")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -129,6 +150,9 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     from mixture_experts_grouped_amd import binding as B
     from mixture_experts_grouped_amd import inputs as I
 
@@ -147,13 +171,24 @@ def main():
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    params = {nm: torch.empty(0) for nm in ("W13", "W2", "B1", "B3", "A2")}
-    for nm in ("W13", "W2", "B1", "B3", "A2"):
+    mx = args.base == "mxfp4"
+    params = {}
+    for nm in ("B1", "B3", "A2") if mx else ("W13", "W2", "B1", "B3", "A2"):
         first = experts[0][nm]
         t = torch.empty((shape.E, *first.shape), dtype=torch.bfloat16, device=dev)
         for e in range(shape.E):
             t[e].copy_(bf(experts[e][nm]))
         params[nm] = t
+    if mx:
+        t0 = time.time()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            quant = {nm: list(ex.map(lambda e, nm=nm: I.mxfp4_quantize(I.bf16_bits_to_f32(experts[e][nm])),
+                                     range(shape.E))) for nm in ("W13", "W2")}
+        for nm in ("W13", "W2"):
+            params[nm] = torch.from_numpy(np.stack([q for q, _ in quant[nm]])).to(dev)
+            params[nm + "_scale"] = torch.from_numpy(np.stack([sc for _, sc in quant[nm]])).to(dev)
+        del quant
+        print(f"[bench] MXFP4 base quantised in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     for nm in ("A1", "A3", "B2"):
         params[nm] = bf(shared[nm])
     x = bf(x_bits)
@@ -161,7 +196,8 @@ def main():
     tidx = torch.from_numpy(idx).to(dev)
     tw = torch.from_numpy(w).to(dev)
 
-    desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale)
+    desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale,
+                       base_format=B.MOE_BASE_MXFP4 if mx else B.MOE_BASE_BF16)
     layer = B.MoeLoraLayer(desc, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -226,7 +262,7 @@ def main():
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                     "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx:
         cpu = cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, args.cpu_seconds)
         print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s",
               file=sys.stderr, flush=True)
@@ -246,10 +282,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
+            "workload": (("MXFP4 base (e2m1 + e8m0/32), " if mx else "") +
+                         f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
                          f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, SwiGLU, s=1"),
             "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
-            "block_m": layer.block_m,
+            "block_m": layer.block_m, "base": args.base,
         },
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),

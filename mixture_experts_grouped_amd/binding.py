@@ -188,13 +188,27 @@ def _pool_struct(pool: Dict[str, torch.Tensor], bm: int) -> MoePool:
 
 
 def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraParams:
+    """bf16 base: W13, W2 bf16.  MXFP4 base (desc.base_format == MOE_BASE_MXFP4):
+    W13 uint8 [E, 2I, H/2] and W2 uint8 [E, H, I/2] packed e2m1 (element 2i in
+    the low nibble of byte i), W13_scale uint8 [E, 2I, H/32], W2_scale uint8
+    [E, H, I/32] e8m0."""
     E, H, I, r = desc.E, desc.H, desc.I, desc.rank
     bf = torch.bfloat16
-    shapes = {"W13": (E, 2 * I, H), "W2": (E, H, I), "A1": (r, H), "A3": (r, H),
-              "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I), "B2": (H, r)}
+    shapes = {"A1": (r, H), "A3": (r, H), "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I),
+              "B2": (H, r)}
     ptrs = {n: _ptr(p[n], bf, s, n) for n, s in shapes.items()}
-    return MoeLoraParams(ptrs["W13"], ptrs["W2"], None, None, ptrs["A1"], ptrs["A3"], ptrs["B1"],
-                         ptrs["B3"], ptrs["A2"], ptrs["B2"])
+    if desc.base_format == MOE_BASE_MXFP4:
+        u8 = torch.uint8
+        w13 = _ptr(p["W13"], u8, (E, 2 * I, H // 2), "W13")
+        w2 = _ptr(p["W2"], u8, (E, H, I // 2), "W2")
+        s13 = _ptr(p["W13_scale"], u8, (E, 2 * I, H // 32), "W13_scale")
+        s2 = _ptr(p["W2_scale"], u8, (E, H, I // 32), "W2_scale")
+    else:
+        w13 = _ptr(p["W13"], bf, (E, 2 * I, H), "W13")
+        w2 = _ptr(p["W2"], bf, (E, H, I), "W2")
+        s13 = s2 = None
+    return MoeLoraParams(w13, w2, s13, s2, ptrs["A1"], ptrs["A3"], ptrs["B1"], ptrs["B3"],
+                         ptrs["A2"], ptrs["B2"])
 
 
 def moe_lora_forward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], x: torch.Tensor,

@@ -33,7 +33,7 @@ moe_status check_desc(const moe_lora_desc* d) {
   if (d->E > 512 || d->topk > 16 || d->rank > 128 || d->rank % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (!(d->clamp <= 0.0f || std::isinf(d->clamp))) return MOE_ERR_UNSUPPORTED;
-  if (d->base_format != MOE_BASE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->base_format != MOE_BASE_BF16 && d->base_format != MOE_BASE_MXFP4) return MOE_ERR_UNSUPPORTED;
   const int64_t routes = (int64_t)d->T * d->topk;
   const int64_t cap = routes + std::min<int64_t>(d->E, routes) * 239;
   if (cap >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -110,11 +110,14 @@ moe_status check_pool(const moe_lora_desc* d, const moe_pool* pool, const Plan& 
   return MOE_OK;
 }
 
-moe_status check_params(const moe_lora_params* w) {
+moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
   if (w == nullptr) return MOE_ERR_INVALID;
   const void* ps[] = {w->W13, w->W2, w->A1, w->A3, w->B1, w->B3, w->A2, w->B2};
   for (const void* q : ps)
     if (!aligned16(q)) return MOE_ERR_INVALID;
+  // scales: present exactly for an MXFP4 base (byte arrays, no alignment needed)
+  const bool mx = d->base_format == MOE_BASE_MXFP4;
+  if (mx != (w->W13_scale != nullptr) || mx != (w->W2_scale != nullptr)) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -138,6 +141,13 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.row2r = pool->row_to_route;
   a.W13 = (const uint16_t*)w->W13;
   a.W2 = (const uint16_t*)w->W2;
+  a.mx = d->base_format == MOE_BASE_MXFP4;
+  if (a.mx) {
+    a.W13q = (const uint8_t*)w->W13;
+    a.W2q = (const uint8_t*)w->W2;
+    a.W13s = w->W13_scale;
+    a.W2s = w->W2_scale;
+  }
   a.A1 = (const uint16_t*)w->A1;
   a.A3 = (const uint16_t*)w->A3;
   a.B1 = (const uint16_t*)w->B1;
@@ -242,8 +252,7 @@ moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const 
   if (st != MOE_OK) return st;
   const Plan p = make_plan(d);
   if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
-  if ((st = check_params(params)) != MOE_OK) return st;
-  if (params->W13_scale != nullptr || params->W2_scale != nullptr) return MOE_ERR_INVALID;
+  if ((st = check_params(d, params)) != MOE_OK) return st;
   if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
     return MOE_ERR_INVALID;
   if (saved_bytes < p.saved) return MOE_ERR_WORKSPACE;
@@ -270,8 +279,7 @@ moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
   if (st != MOE_OK) return st;
   const Plan p = make_plan(d);
   if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
-  if ((st = check_params(params)) != MOE_OK) return st;
-  if (params->W13_scale != nullptr || params->W2_scale != nullptr) return MOE_ERR_INVALID;
+  if ((st = check_params(d, params)) != MOE_OK) return st;
   if (!aligned16(grad_out) || !aligned16(grad_x) || !aligned16(saved) || !aligned16(scratch) ||
       topk_w == nullptr || grad_topk_w == nullptr || grads == nullptr)
     return MOE_ERR_INVALID;

@@ -16,6 +16,8 @@
 //   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
+#include <type_traits>
+
 #include "engine2.hpp"
 #include "gather_sum.hpp"
 #include "layer.hpp"
@@ -115,19 +117,19 @@ __global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
 using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES);
 // Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
-struct LdW2d {
+struct LdW2dBase {
   using KL = v2::KLoad<256, GW2D::KT, GW2D::NW>;
   using TL = v2::TLoad<256, v2::TStrided, GW2D::KT, GW2D::NW>;
   using KA = v2::KLoadA<256, GW2D::KT, GW2D::NW>;
-  using TA = v2::TLoadA<256, GW2D::KT, GW2D::NW>;
   static constexpr int INSTS = KL::NJ + TL::NJ;
   KL me;
   KA mm;
   TL ne;
-  TA nm;
   int next;
-  static constexpr int nsplit = 0;
-  __device__ void issue(int s, char* sM, char* sN) const {
+};
+struct LdW2d : LdW2dBase {
+  v2::TLoadA<256, GW2D::KT, GW2D::NW> nm;
+  __device__ void issue(int s, char* sM, char* sN) {
     if (s < next) {
       me.issue(s * GW2D::KT, 0, false, sM);
       ne.issue(s * GW2D::KT, sN);
@@ -137,11 +139,27 @@ struct LdW2d {
     }
   }
 };
+struct LdW2dMX : LdW2dBase {
+  v2::TLoadMX<GW2D::NT> nq;
+  __device__ void issue(int s, char* sM, char* sN) {
+    if (s < next) {
+      me.issue(s * GW2D::KT, 0, false, sM);
+      ne.issue(s * GW2D::KT, sN);
+    } else {
+      mm.issue((s - next) * GW2D::KT, sM);
+      nq.issue((s - next) * GW2D::KT);
+    }
+  }
+  __device__ void finish(int s, char* sN) const {
+    if (s >= next) nq.finish(sN);
+  }
+};
 
+template <bool MX>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2D;
-  using KL = LdW2d::KL;
+  using KL = LdW2dBase::KL;
   const int ntn = a.I / G::TN;
   int mt, nt;
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
@@ -149,7 +167,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   const int i0 = nt * G::TN;
   const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
-  LdW2d L;
+  typename std::conditional<MX, LdW2dMX, LdW2d>::type L;
   L.next = (2 * r + G::KT - 1) / G::KT;
   {
     int tk[KL::NJ];
@@ -161,7 +179,10 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
                          (uint32_t)(2 * a.I), 0, 2 * r, r};
   L.ne.cols(i0, G::TN);
-  L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
+  if constexpr (MX)
+    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
+  else
+    L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
@@ -217,18 +238,29 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 using GW13D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 constexpr int W13D_LDS = cmax(GW13D::LDS_BYTES, v2::TileImage<GW13D, GW13D::TN, uint16_t>::BYTES);
 struct LdW13d {
-  using KL = v2::KLoad<256, GW13D::KT, GW13D::NW>;
   using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
   using TA = v2::TLoadA<256, GW13D::KT, GW13D::NW>;
   static constexpr int INSTS = KA::NJ + TA::NJ;
   KA m;
   TA n;
-  __device__ void issue(int s, char* sM, char* sN) const {
+  __device__ void issue(int s, char* sM, char* sN) {
     m.issue(s * GW13D::KT, sM);
     n.issue(s * GW13D::KT, sN);
   }
 };
+struct LdW13dMX {
+  using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
+  static constexpr int INSTS = KA::NJ;
+  KA m;
+  v2::TLoadMX<GW13D::NT> nq;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GW13D::KT, sM);
+    nq.issue(s * GW13D::KT);
+  }
+  __device__ void finish(int, char* sN) const { nq.finish(sN); }
+};
 
+template <bool MX>
 __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13D;
@@ -237,9 +269,13 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
-  LdW13d L;
+  typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
   L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
-  L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
+  if constexpr (MX)
+    L.nq.set(a.W13q + (long)ti.e * 2 * a.I * (a.H / 2), a.W13s + (long)ti.e * 2 * a.I * (a.H / 32), 2 * a.I,
+             a.H, h0);
+  else
+    L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
@@ -505,8 +541,10 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, G128::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad, W2D_LDS);
-    set_lds((const void*)k_w13dgrad, W13D_LDS);
+    set_lds((const void*)k_w2dgrad<false>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<true>, W2D_LDS);
+    set_lds((const void*)k_w13dgrad<false>, W13D_LDS);
+    set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, GS_LDS);
     set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
@@ -517,8 +555,14 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
   const long nr = (long)a.T * a.k;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_w2dgrad, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
-  MOE_LAUNCH(k_w13dgrad, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
+  if (a.mx)
+    MOE_LAUNCH(k_w2dgrad<true>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
+  else
+    MOE_LAUNCH(k_w2dgrad<false>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
+  if (a.mx)
+    MOE_LAUNCH(k_w13dgrad<true>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
+  else
+    MOE_LAUNCH(k_w13dgrad<false>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);

@@ -331,6 +331,98 @@ struct TLoadA {
   }
 };
 
+// ---------------------------------------------------------------------------
+// MXFP4 weights (OCP MX v1.0): e2m1 elements, two per byte with element 2i in
+// the low nibble of byte i, and one e8m0 scale per 32 elements along the
+// weight's own K axis (the forward contraction axis).  The loaders read the
+// packed bytes into registers when a stage is queued and, after the stage
+// before it has been multiplied, expand them to bf16 into the same LDS layout
+// the bf16 loaders produce: e2m1 x 2^(e-127) is exact in bf16, so the
+// matrix-core path is the bf16 one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  // 2^(e-127); e = 0 is the denormal 2^-127
+  return __builtin_bit_cast(float, e ? (e << 23) : 0x00400000u);
+}
+// 8 e2m1 values (one 32-bit word) times sc -> 8 bf16 (one 16-byte chunk)
+__device__ __forceinline__ u32x4 fp4x8_bf16(uint32_t w, float sc) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  return o;
+}
+__device__ __forceinline__ uint32_t bload_u8(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0), others untouched
+}
+
+// K tile of R = NT/2 weight rows x 64 k from MXFP4: thread t takes row t/2,
+// k half t%2 (32 values = 16 bytes and their one scale).
+template <int R, int NT>
+struct KLoadMX {
+  static_assert(NT == 2 * R, "two threads per weight row");
+  rsrc_t rq, rs;         // packed values, scales
+  uint32_t qoff, soff;   // this thread's row: byte offsets at k = 0
+  u32x4 q;               // staged values of the queued stage
+  uint32_t e;            // staged scale
+  // weight row `row` (absolute) of a [*, K] MXFP4 matrix
+  __device__ __forceinline__ void set(const uint8_t* q_base, const uint8_t* s_base, long nrows, long K,
+                                      int row) {
+    rq = make_rsrc(q_base, (uint64_t)nrows * (K / 2));
+    rs = make_rsrc(s_base, (uint64_t)nrows * (K / 32));
+    qoff = (uint32_t)(row * (K / 2)) + 16u * (threadIdx.x & 1);
+    soff = (uint32_t)(row * (K / 32)) + (threadIdx.x & 1);
+  }
+  __device__ __forceinline__ void issue(int k0) {
+    q = bload(rq, qoff + (uint32_t)(k0 / 2));
+    e = bload_u8(rs, soff + (uint32_t)(k0 / 32));
+  }
+  // after the loads landed (vmcnt 0): expand into the K tile
+  __device__ __forceinline__ void finish(char* tile) const {
+    const float sc = e8m0_value(e);
+    const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + koff<64>(row, 4 * h + c)) = fp4x8_bf16(q[c], sc);
+  }
+};
+
+// T tile of 256 columns x 64 k-rows from an MXFP4 matrix stored [K rows][N]
+// with N the packed axis: thread t takes k-row t/8 and columns 32 (t%8) ..
+// +31 (16 bytes and one scale).
+template <int NT>
+struct TLoadMX {
+  static_assert(NT == 512, "eight threads per k-row, 64 k-rows");
+  rsrc_t rq, rs;
+  uint32_t qoff, soff;   // at stage k-row 0
+  uint32_t qld, sld;     // bytes per k-row
+  u32x4 q;
+  uint32_t e;
+  // columns n0 .. n0 + 255 of a [nk, N] MXFP4 matrix
+  __device__ __forceinline__ void set(const uint8_t* q_base, const uint8_t* s_base, long nk, long N, int n0) {
+    rq = make_rsrc(q_base, (uint64_t)nk * (N / 2));
+    rs = make_rsrc(s_base, (uint64_t)nk * (N / 32));
+    qld = (uint32_t)(N / 2);
+    sld = (uint32_t)(N / 32);
+    const int kr = threadIdx.x >> 3, cg = threadIdx.x & 7;
+    qoff = kr * qld + (uint32_t)(n0 / 2) + 16u * cg;
+    soff = kr * sld + (uint32_t)(n0 / 32) + cg;
+  }
+  __device__ __forceinline__ void issue(int k0) {
+    q = bload(rq, qoff + (uint32_t)k0 * qld);
+    e = bload_u8(rs, soff + (uint32_t)k0 * sld);
+  }
+  __device__ __forceinline__ void finish(char* tile) const {
+    const float sc = e8m0_value(e);
+    const int kr = threadIdx.x >> 3, cg = threadIdx.x & 7;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + toff(kr, 4 * cg + c, 512)) = fp4x8_bf16(q[c], sc);
+  }
+};
+
 // k-row policies of TLoad (the K-outer source's row for k)
 struct TStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) folded by period
   rsrc_t rs;
@@ -386,6 +478,16 @@ __device__ __forceinline__ void wait_vm() {
 // caller has already waited for the loads the next stage needs.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
+// Loaders with register-staged operands also provide finish(stage, sN).
+template <class T, class = void>
+struct HasFinish {
+  static constexpr bool value = false;
+};
+template <class T>
+struct HasFinish<T, decltype((void)&T::finish)> {
+  static constexpr bool value = true;
+};
+
 // One pipeline step: wait for stage s, release the buffer stage s - 1 used,
 // queue stage s + NBUF - 1 into it, multiply stage s.
 template <class G, bool SPLIT, class L>
@@ -406,6 +508,14 @@ __device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB
   }
   const char* sM = smem + (s % NBUF) * G::STAGE;
   mma_stage2<G, SPLIT>(sM, sM + G::SM_BYTES, acc, wm, wn, lane);
+  if constexpr (HasFinish<L>::value) {
+    static_assert(NBUF == 2, "register-staged operands expand one stage ahead");
+    if (s + 1 < nst) {
+      wait_vm<0>();
+      ld.finish(s + 1, smem + ((s + 1) % NBUF) * G::STAGE + G::SM_BYTES);
+      wait_lgkm0();  // the next step's barrier publishes the expanded tile
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -455,6 +565,11 @@ __device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB]
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
     if (p < nst) ld.issue(p, smem + p * G::STAGE, smem + p * G::STAGE + G::SM_BYTES);
+  if constexpr (HasFinish<L>::value) {
+    wait_vm<0>();
+    ld.finish(0, smem + G::SM_BYTES);
+    wait_lgkm0();
+  }
   int s = 0;
   if constexpr (SPLIT == 2) {
     const int ns = ld.nsplit < nst ? ld.nsplit : nst;

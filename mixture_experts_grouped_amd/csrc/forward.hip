@@ -13,6 +13,8 @@
 //   k_combine   out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
+#include <type_traits>
+
 #include "engine2.hpp"
 #include "gather_sum.hpp"
 #include "layer.hpp"
@@ -83,17 +85,21 @@ using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight w
 constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, uint16_t>::BYTES);
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
-// stage); stages [nsplit, ...): the base K = H.
-struct LdW13 {
+// stage); stages [nsplit, ...): the base K = H.  With an MXFP4 base the W13
+// tile is register-staged and expanded to bf16 (finish).
+struct LdW13Base {
   using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
   using KL2 = v2::KLoad<256, GW13::KT, GW13::NW, true>;
   using KA = v2::KLoadA<256, GW13::KT, GW13::NW>;
   static constexpr int INSTS = 2 * KL::NJ;
   KL me;
   KL2 ne;
-  KA mm, nm;
+  KA mm;
   int r, nsplit;
-  __device__ void issue(int s, char* sM, char* sN) const {
+};
+struct LdW13 : LdW13Base {
+  KA nm;
+  __device__ void issue(int s, char* sM, char* sN) {
     if (s < nsplit) {
       me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
       ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
@@ -103,11 +109,27 @@ struct LdW13 {
     }
   }
 };
+struct LdW13MX : LdW13Base {
+  v2::KLoadMX<256, GW13::NT> nq;
+  __device__ void issue(int s, char* sM, char* sN) {
+    if (s < nsplit) {
+      me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
+      ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
+    } else {
+      mm.issue((s - nsplit) * GW13::KT, sM);
+      nq.issue((s - nsplit) * GW13::KT);
+    }
+  }
+  __device__ void finish(int s, char* sN) const {
+    if (s >= nsplit) nq.finish(sN);
+  }
+};
 
+template <bool MX>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13;
-  using KL = LdW13::KL;
+  using KL = LdW13Base::KL;
   constexpr int TN = G::TN, HALF = TN / 2;
   const int ntn = a.I / HALF;
   int mt, nt;
@@ -116,7 +138,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   const int e = ti.e, i0 = nt * HALF;
   const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
-  LdW13 L;
+  typename std::conditional<MX, LdW13MX, LdW13>::type L;
   L.r = r;
   L.nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
   {
@@ -131,12 +153,19 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
   L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
   L.mm.contig(a.Xp, ti.row0, nrows, a.H);
-  L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
-#pragma unroll
-  for (int j = 0; j < KL::NJ; ++j) {
-    const int nl = KL::row_of(j);
+  if constexpr (MX) {
+    const int nl = threadIdx.x >> 1;  // this thread's W13 tile row
     const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
-    L.nm.set_row(j, (uint32_t)((long)wrow * a.H * 2));
+    L.nq.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2 * a.I,
+             a.H, wrow);
+  } else {
+    L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+#pragma unroll
+    for (int j = 0; j < KL::NJ; ++j) {
+      const int nl = KL::row_of(j);
+      const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
+      L.nm.set_row(j, (uint32_t)((long)wrow * a.H * 2));
+    }
   }
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
@@ -214,12 +243,24 @@ struct LdW2 {
   using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
   static constexpr int INSTS = 2 * KL::NJ;
   KL m, n;
-  __device__ void issue(int s, char* sM, char* sN) const {
+  __device__ void issue(int s, char* sM, char* sN) {
     m.issue(s * GW2::KT, sM);
     n.issue(s * GW2::KT, sN);
   }
 };
+struct LdW2MX {
+  using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
+  static constexpr int INSTS = KL::NJ;
+  KL m;
+  v2::KLoadMX<256, GW2::NT> nq;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GW2::KT, sM);
+    nq.issue(s * GW2::KT);
+  }
+  __device__ void finish(int, char* sN) const { nq.finish(sN); }
+};
 
+template <bool MX>
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2;
@@ -228,10 +269,13 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
-  const uint16_t* W = a.W2 + (long)ti.e * a.H * a.I;
-  LdW2 L;
+  typename std::conditional<MX, LdW2MX, LdW2>::type L;
   L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
-  L.n.contig(W, h0, G::TN, a.I);
+  if constexpr (MX)
+    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I,
+             h0 + (threadIdx.x >> 1));
+  else
+    L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
@@ -305,9 +349,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_shrink, G128::LDS_BYTES);
-    set_lds((const void*)k_w13, W13_LDS);
+    set_lds((const void*)k_w13<false>, W13_LDS);
+    set_lds((const void*)k_w13<true>, W13_LDS);
     set_lds((const void*)k_a2, G128::LDS_BYTES);
-    set_lds((const void*)k_w2, W2_LDS);
+    set_lds((const void*)k_w2<false>, W2_LDS);
+    set_lds((const void*)k_w2<true>, W2_LDS);
     set_lds((const void*)k_combine, GS_LDS);
     init = true;
   }
@@ -315,9 +361,15 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   const int tm = (a.T + 255) / 256;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w13, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
+  if (a.mx)
+    MOE_LAUNCH(k_w13<true>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
+  else
+    MOE_LAUNCH(k_w13<false>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
   MOE_LAUNCH(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
-  MOE_LAUNCH(k_w2, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+  if (a.mx)
+    MOE_LAUNCH(k_w2<true>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+  else
+    MOE_LAUNCH(k_w2<false>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   const long nzc = (long)a.T * a.r;
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_combine, dim3((a.T + GGS::TM - 1) / GGS::TM, a.H / GGS::TN), dim3(GGS::NT), GS_LDS, st, a);

@@ -40,6 +40,10 @@ struct LayerArgs {
   const uint16_t* go;
   // parameters
   const uint16_t *W13, *W2, *A1, *A3, *B1, *B3, *A2, *B2;
+  // MXFP4 base (mx != 0): packed e2m1 W13 [E, 2I, H/2], W2 [E, H, I/2] and
+  // their e8m0 scales [E, 2I, H/32], [E, H, I/32]
+  int mx;
+  const uint8_t *W13q, *W13s, *W2q, *W2s;
   // saved by the forward
   TileInfo* tiles;   // [maxtiles]
   int* ntiles;       // [1]

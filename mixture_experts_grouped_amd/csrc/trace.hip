@@ -74,10 +74,12 @@ moe_status moe_lora_trace_collect(void) {
     if (hipEventSynchronize(p.b) != hipSuccess) return MOE_ERR_HIP;
     float ms = 0.0f;
     if (hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) return MOE_ERR_HIP;
-    auto it = g_stats.find(p.name);
+    std::string key(p.name);
+    key = key.substr(0, key.find('<'));  // template instances count under the kernel's name
+    auto it = g_stats.find(key);
     if (it == g_stats.end()) {
-      g_order.push_back(p.name);
-      it = g_stats.emplace(p.name, Stat{}).first;
+      g_order.push_back(key);
+      it = g_stats.emplace(key, Stat{}).first;
     }
     it->second.launches += 1;
     it->second.ms += ms;

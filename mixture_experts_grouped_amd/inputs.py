@@ -207,45 +207,36 @@ def route_zipf(shape: Shape, key: Sequence[int], s: float = 1.2,
 # MXFP4 packing of base weights (input preparation, OCP MX v1.0 layout)
 # --------------------------------------------------------------------------
 
-_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
-
-
 def mxfp4_quantize(w_f32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise a [..., K] float array to e2m1 with one e8m0 scale per 32
     consecutive elements along K.  Shared exponent floor(log2 amax) - 2,
     clamped to the e8m0 range (an all-zero block gets 2^-127); elements round
     to nearest e2m1 value with ties to even and saturate at 6.  Returns
     (packed uint8 [..., K/2] with the even element in the low nibble,
-    scales uint8 [..., K/32])."""
+    scales uint8 [..., K/32]).
+
+    Rounding is done per binade of the grid: spacing 0.5 below 2, 1 below 4,
+    2 up to 6; rint (half to even) on the spacing-scaled magnitude picks the
+    nearest grid value and, on a tie, the one with the even code."""
     a = np.asarray(w_f32, dtype=np.float64)
     K = a.shape[-1]
     assert K % 32 == 0
     blk = a.reshape(*a.shape[:-1], K // 32, 32)
     amax = np.abs(blk).max(axis=-1)
-    with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
-    e = np.clip(e, -127, 127).astype(np.int64)
-    scaled = blk / np.ldexp(1.0, e)[..., None]
-    mag = np.minimum(np.abs(scaled), 6.0)
-    # nearest grid point, ties to the even code (codes 0..7; even code = even mantissa)
-    d = np.abs(mag[..., None] - _E2M1_GRID)
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    codes = np.arange(8)
-    pick_even = cand & (codes % 2 == 0)
-    has_even = pick_even.any(axis=-1, keepdims=True)
-    choose = np.where(has_even, pick_even, cand)
-    code = np.argmax(choose, axis=-1).astype(np.uint8)
-    sign = ((scaled < 0) & (code > 0)).astype(np.uint8) << 3
+    _, ex = np.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    e = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)
+    e = np.clip(e, -127, 127)
+    mag = np.minimum(np.abs(blk) * np.ldexp(1.0, -e)[..., None], 6.0)
+    val = np.where(mag < 2.0, np.rint(mag * 2.0) * 0.5,
+                   np.where(mag < 4.0, np.rint(mag), np.rint(mag * 0.5) * 2.0))
+    # value -> code: 0,.5,1,1.5 -> 0..3 (2v); 2,3,4 -> 4,5,6 (v+2); 6 -> 7
+    code = np.where(val < 2.0, val * 2.0, np.where(val <= 4.0, val + 2.0, 7.0)).astype(np.uint8)
+    sign = ((blk < 0) & (code > 0)).astype(np.uint8) << 3
     nib = (code | sign).reshape(*a.shape[:-1], K)
     packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
     scales = (e + 127).astype(np.uint8)
     return packed, scales
 
-
-# --------------------------------------------------------------------------
-# bundles and manifests
-# --------------------------------------------------------------------------
 
 def layer_inputs(shape: Shape, key: Sequence[int], routing: str = "softmax_topk",
                  mask_prob: float = 0.0, with_weights: bool = True) -> Dict[str, np.ndarray]:

@@ -67,14 +67,17 @@ class GpuRun:
     download everything."""
 
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None):
+        """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
+        then case's W13/W2 are not uploaded."""
         import torch
         from mixture_experts_grouped_amd import binding as B
         self.torch = torch
         self.B = B
         s = shape.scale if scale is None else scale
+        fmt = B.MOE_BASE_MXFP4 if mx is not None else B.MOE_BASE_BF16
         self.desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank,
-                                scale=s, block_m=block_m)
+                                scale=s, block_m=block_m, base_format=fmt)
         self.layer = B.MoeLoraLayer(self.desc)
         dev = "cuda"
 
@@ -85,7 +88,10 @@ class GpuRun:
         self.go = bf(case["grad_out"])
         self.idx = torch.from_numpy(np.ascontiguousarray(case["topk_idx"], dtype=np.int32)).to(dev)
         self.w = torch.from_numpy(np.ascontiguousarray(case["topk_w"], dtype=np.float32)).to(dev)
-        self.params = {n: bf(case[n]) for n in PARAMS}
+        self.params = {n: bf(case[n]) for n in PARAMS if mx is None or n not in ("W13", "W2")}
+        if mx is not None:
+            for n in ("W13", "W13_scale", "W2", "W2_scale"):
+                self.params[n] = torch.from_numpy(np.ascontiguousarray(mx[n], dtype=np.uint8)).to(dev)
 
     def run(self, fill=None):
         L = self.layer
@@ -116,6 +122,23 @@ class GpuRun:
         for n in GRAD_NAMES:
             res[n] = u16(L.grads[n])
         return res
+
+
+def mxfp4_base(case: Dict[str, np.ndarray]):
+    """Quantise the case's bf16 W13/W2 to MXFP4 along their K axis (H for W13,
+    I for W2).  Returns (mx, deq): the packed bytes and scales for the GPU, and
+    the dequantised weights as bf16 bits (exact: e2m1 x 2^k fits bf16), which
+    are the oracle's weights and the bf16 path's equivalent input."""
+    from oracle import mxfp4 as OMX
+    mx, deq = {}, {}
+    for n in ("W13", "W2"):
+        q, sc = I.mxfp4_quantize(I.bf16_bits_to_f32(case[n]))
+        mx[n], mx[n + "_scale"] = q, sc
+        d = OMX.dequantize(q, sc)
+        bits = I.f32_to_bf16_bits(d.astype(np.float32))
+        assert np.array_equal(I.bf16_bits_to_f32(bits).astype(np.float64), d), "dequantised weight not exact in bf16"
+        deq[n] = bits
+    return mx, deq
 
 
 def compare_all(res, ref_out, ref_g, tag=""):

@@ -134,3 +134,23 @@ def test_flop_model_matches_the_closed_form():
     f, b = bench.step_flops(T, M, H, Id, r)
     assert abs(f / 1e12 - 5.154) < 2e-3 and abs(b / 1e12 - 5.360) < 2e-3
     assert abs(sum(bench.kernel_flops(T, M, H, Id, r).values()) - (f + b)) < 1.0
+
+
+def test_mxfp4_base_needs_both_scales():
+    """An MXFP4 base is accepted by the descriptor check and needs both e8m0
+    scale arrays; missing either is rejected on the host."""
+    lib = B.library()
+    d = B.make_desc(64, 256, 256, 8, 2, 8, base_format=B.MOE_BASE_MXFP4)
+    saved, scratch = B.moe_lora_workspace_size(d)   # descriptor accepted
+    cap = B.moe_lora_pool_capacity(d)
+    fake = 1 << 20
+    pool = B.MoePool(fake, fake, fake, fake, cap, 16)
+    byref = ctypes.byref
+    for s13, s2 in ((None, None), (fake, None), (None, fake)):
+        prm = B.MoeLoraParams(fake, fake, s13, s2, *([fake] * 6))
+        assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm), fake * 64,
+                                    fake * 128, saved, None, 0, None) == B.MOE_ERR_INVALID
+        grads = B.MoeLoraGrads(*([fake * 3] * 6), None, None)
+        assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128,
+                                     saved, fake * 64, fake * 200, byref(grads), fake * 256,
+                                     scratch, None) == B.MOE_ERR_INVALID

@@ -91,3 +91,41 @@ def test_mxfp4_round_trip_on_grid_and_error_bound():
     mag = np.abs(x).reshape(16, 4, 32) / scale[..., None]
     assert (err[mag <= 6] <= scale[..., None].repeat(32, -1)[mag <= 6] + 1e-12).all()
     assert (err <= 2 * scale[..., None] + 1e-12).all()
+
+
+def _quantize_brute(x):
+    """Nearest e2m1 code by exhaustive search over the eight magnitudes, ties to
+    the even code, same shared exponent rule: a direct restatement of the
+    quantiser's definition for small arrays."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    blk = x.reshape(-1, 32)
+    codes = np.zeros(blk.shape, np.uint8)
+    exps = np.zeros(len(blk), np.int64)
+    for i, b in enumerate(blk):
+        amax = np.abs(b).max()
+        e = int(np.floor(np.log2(amax))) - 2 if amax > 0 else -127
+        e = min(max(e, -127), 127)
+        exps[i] = e
+        for j, v in enumerate(b):
+            mag = min(abs(v) / 2.0 ** e, 6.0)
+            d = np.abs(grid - mag)
+            best = [c for c in range(8) if d[c] == d.min()]
+            c = [c for c in best if c % 2 == 0][0] if len(best) > 1 else best[0]
+            codes[i, j] = c | (8 if (v < 0 and c > 0) else 0)
+    nib = codes.reshape(x.shape)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8), (exps + 127).astype(np.uint8).reshape(*x.shape[:-1], -1)
+
+
+def test_mxfp4_quantizer_matches_exhaustive_search_on_ties():
+    rng = np.random.default_rng(7)
+    # every midpoint of the grid, both signs, saturation, at assorted binades
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.9, 0.0, 1.9, 3.9, 5.9, 4.0, 0.5])
+    x = rng.choice(mids, size=(24, 64)) * rng.choice([-1.0, 1.0], size=(24, 64))
+    x[:, 0] = 6.0
+    x[:, 32] = rng.choice([4.0, 7.5], size=24)
+    x *= 2.0 ** rng.integers(-30, 30, size=(24, 1))
+    x[3] = 0.0                               # all-zero blocks -> 2^-127
+    x[4, :32] = rng.standard_normal(32)      # ordinary data
+    q, s = I.mxfp4_quantize(x)
+    qb, sb = _quantize_brute(x)
+    assert np.array_equal(s, sb) and np.array_equal(q, qb)
