@@ -1,0 +1,105 @@
+"""Parity at the full production share (16,384 tokens x top-6 over 64 experts,
+H 4096, I 2048, rank 128, uniform routing), in the launch configuration the
+benchmark times (library-chosen BLOCK_M).
+
+The oracle cannot run the whole layer in seconds, so it checks exactly
+computable samples:
+- tokens: out, grad_x and grad_w of a token depend only on that token's
+  routes, so the oracle runs on the sub-batch of sampled tokens (with just
+  their experts' weights) and must match those rows;
+- experts: dB1_e, dB3_e, dA2_e depend only on expert e's routes, so the oracle
+  runs on the tokens routed to e with every other route masked;
+and one identity over the whole output: sum_tj w_tj grad_w_tj = <grad_out,
+out> (the loss is linear in the weights' combine).
+"""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+
+from mixture_experts_grouped_amd import inputs as I
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = I.PROD
+KEY = (2,)
+SAMPLE_TOKENS = (0, 1, 4097, 9999, 16383)
+SAMPLE_EXPERTS = (0, 37, 63)
+
+
+@pytest.fixture(scope="module")
+def run():
+    Hn.ensure_built()
+    threads = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(threads) as ex:
+        fut_e = [ex.submit(I.expert_weights, SHAPE, KEY, e) for e in range(SHAPE.E)]
+        fut_x = ex.submit(I.tokens, SHAPE, KEY)
+        fut_g = ex.submit(I.grad_out, SHAPE, KEY)
+        idx, w = I.route_balanced(SHAPE, KEY)
+        shared = I.shared_weights(SHAPE, KEY)
+        experts = [f.result() for f in fut_e]
+        case = {"x": fut_x.result(), "grad_out": fut_g.result(), "topk_idx": idx, "topk_w": w}
+    for n in ("W13", "W2", "B1", "B3", "A2"):
+        case[n] = np.stack([experts[e][n] for e in range(SHAPE.E)])
+    del experts
+    case.update(shared)
+    Hn.log(f"[fullsize] inputs ready, shape={SHAPE}")
+    res = Hn.GpuRun(SHAPE, case).run()
+    Hn.log("[fullsize] GPU step done")
+    return case, res
+
+
+def _sub_problem(case, tokens, only_expert=None):
+    """Inputs of the oracle restricted to `tokens` (and, with only_expert, to
+    that expert's routes), experts renumbered to the ones used."""
+    idx = case["topk_idx"][tokens].copy()
+    if only_expert is not None:
+        idx[idx != only_expert] = -1
+    used = np.unique(idx[idx >= 0])
+    remap = np.full(SHAPE.E, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    idx_s = np.where(idx >= 0, remap[np.maximum(idx, 0)], -1).astype(np.int32)
+    sub = {"x": case["x"][tokens], "grad_out": case["grad_out"][tokens], "topk_idx": idx_s,
+           "topk_w": case["topk_w"][tokens]}
+    for n in ("W13", "W2", "B1", "B3", "A2"):
+        sub[n] = case[n][used]
+    for n in ("A1", "A3", "B2"):
+        sub[n] = case[n]
+    return sub, used
+
+
+def test_sampled_tokens_match_oracle(run):
+    case, res = run
+    toks = np.array(SAMPLE_TOKENS)
+    sub, _ = _sub_problem(case, toks)
+    ref_out, ref_g = Hn.oracle_run(sub, SHAPE.scale)
+    Hn.assert_close("out[sample]", Hn.f64(res["out"][toks]), ref_out)
+    Hn.assert_close("grad_x[sample]", Hn.f64(res["grad_x"][toks]), ref_g["grad_x"])
+    Hn.assert_close("grad_w[sample]", res["grad_w"][toks], ref_g["grad_w"])
+
+
+@pytest.mark.parametrize("e", SAMPLE_EXPERTS)
+def test_sampled_expert_adapter_grads_match_oracle(run, e):
+    case, res = run
+    toks = np.nonzero((case["topk_idx"] == e).any(axis=1))[0]
+    assert len(toks) == 1536  # uniform routing: exactly 1536 routes per expert, distinct tokens
+    sub, used = _sub_problem(case, toks, only_expert=e)
+    assert used.tolist() == [e]
+    _, ref_g = Hn.oracle_run(sub, SHAPE.scale)
+    for n in ("dB1", "dB3", "dA2"):
+        Hn.assert_close(f"{n}[{e}]", Hn.f64(res[n][e]), ref_g[n][0])
+
+
+def test_router_grad_identity_over_all_tokens(run):
+    case, res = run
+    w = case["topk_w"].astype(np.float64)
+    lhs = float(np.sum(w * res["grad_w"].astype(np.float64)))
+    prod = Hn.f64(case["grad_out"]) * Hn.f64(res["out"])
+    rhs = float(np.sum(prod))
+    # both sides see bf16 roundings (out itself, the routes' base outputs):
+    # random errors of at most 2^-8 relative per term add in quadrature; a
+    # wrong weight or a lost route moves the sum by O(|rhs|)
+    tol = 16 * 2.0 ** -8 * float(np.sqrt(np.sum(prod * prod)))
+    assert abs(lhs - rhs) <= tol, (lhs, rhs, tol)
