@@ -113,6 +113,21 @@ def cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, target_s)
 
 
 COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_lora_fb_98k_rows_hbm_traffic.json")
+
+
+def stored_traffic(kernel, args):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when it was measured on another build (its source hash differs) or
+    another base format."""
+    from mixture_experts_grouped_amd import build
+    if args.base != "bf16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    doc = json.load(open(TRAFFIC_FILE))
+    if doc.get("source_hash") != build.source_hash() or kernel not in doc.get("kernels", {}):
+        return None
+    k = doc["kernels"][kernel]
+    return int(k["fetch_bytes"] + k["write_bytes"])
 
 
 def copy_calibration(torch):
@@ -259,7 +274,9 @@ def main():
         ach = kfl[dom] / avg_s / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": stored_traffic(dom, args) if T == 16384 else None,
+                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
     cpu = None
     if not args.no_cpu_baseline and not mx:

@@ -8,6 +8,7 @@ into ``mixture_experts_grouped_amd/libmoelora.so``.  Every call rebuilds.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -28,6 +29,21 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+
+
+def source_hash() -> str:
+    """sha256 over the device sources, the ABI header and the compile flags:
+    measurements stored beside the code (HBM byte counts) name the hash of the
+    build they were taken on, and are void once it changes."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    for f in files + ["../../include/moelora.h"]:
+        path = os.path.normpath(os.path.join(CSRC, f))
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(HIPCC_FLAGS[:-1]).encode())  # the include path is machine-specific
+    return h.hexdigest()[:16]
 
 
 def hipcc() -> str:
