@@ -57,7 +57,7 @@ struct Plan {
   size_t saved, scratch;
   // byte offsets
   size_t o_tiles, o_ntiles, o_Xp, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
-  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part;
+  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -90,6 +90,7 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_P = take(cap * 2 * r * 4);
   p.o_pc = take(T * 4 * r * 2);
   p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
+  p.o_ZAp = take(cap * 4 * r * 2);
   p.scratch = o;
   return p;
 }
@@ -180,6 +181,7 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.P = (float*)(b + p.o_P);
   a.pc = (uint16_t*)(b + p.o_pc);
   a.part = (float*)(b + p.o_part);
+  a.ZAp = (uint16_t*)(b + p.o_ZAp);
 }
 
 }  // namespace

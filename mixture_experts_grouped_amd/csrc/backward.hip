@@ -406,60 +406,100 @@ __global__ __launch_bounds__(GGS_T::NT) void k_dx(LayerArgs a) {
 // The rank-r operand is hi/lo split along N (columns c and c + 128); the two
 // halves are added in the epilogue.  An expert with no rows writes zeros.
 // ----------------------------------------------------------------------------
-struct LdWg {
-  TransK<256, KRows> m, n;
-  __device__ void load(int s) { m.load(s * KT); n.load(s * KT); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
-};
+// ZA rows in pool order, so the weight-gradient kernel reads its rank
+// operand as contiguous rows of each expert.  One wave per pool row.
+__global__ __launch_bounds__(256) void k_gather_za(LayerArgs a) {
+  const long p = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= a.offsets[a.E]) return;
+  const int f = a.row2r[p];
+  if (f < 0) return;  // padding rows are never read
+  const u32x4* src = (const u32x4*)(a.ZA + (long)(f / a.k) * 4 * a.r);
+  u32x4* dst = (u32x4*)(a.ZAp + p * 4 * a.r);
+  for (int c = lane; c < a.r / 2; c += 64) dst[c] = src[c];  // 4r bf16 = r/2 chunks of 16 bytes
+}
 
-__global__ __launch_bounds__(256) void k_wgrad_local(LayerArgs a) {
+// Both operands K-outer (K = the expert's rows): T tiles with a k window of
+// the expert's row count (rows past it read zero).
+using GWG = v2::Geo2<4, 2, 2, 4, true, true, 64>;
+struct LdWg2 {
+  using TL = v2::TLoad<256, v2::TStrided, GWG::KT, GWG::NW>;
+  static constexpr int INSTS = 2 * TL::NJ;
+  TL m, n;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GWG::KT, sM);
+    n.issue(s * GWG::KT, sN);
+  }
+};
+constexpr int WG_LDS = cmax(GWG::LDS_BYTES, 128 * (256 * 2 + 16));
+
+__global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
+  using G = GWG;
   const int nti = a.I / 256;
   const int e = blockIdx.x / nti, i0 = (blockIdx.x % nti) * 256, which = blockIdx.y;
   const int r = a.r;
   const int ne = a.counts[e], off = a.offsets[e];
-  LdWg L;
-  if (which < 2)
-    L.m.kp = KRows{make_rsrc(a.dGV + (long)off * 2 * a.I, (uint64_t)ne * 4 * a.I),
-                   (uint32_t)(4 * a.I), nullptr, nullptr, 1, off, ne, 0};
-  else
-    L.m.kp = KRows{make_rsrc(a.Hh + (long)off * a.I, (uint64_t)ne * 2 * a.I), (uint32_t)(2 * a.I),
-                   nullptr, nullptr, 1, off, ne, 0};
-  L.m.cols((which < 2 ? which * a.I : 0) + i0, 256);
+  LdWg2 L;
   if (which < 2) {
-    L.n.kp = KRows{make_rsrc(a.ZA, (uint64_t)a.T * 8 * r), (uint32_t)(8 * r), a.row2r, nullptr, a.k,
-                   off, ne, 1};
+    L.m.kp = v2::TStrided{make_rsrc(a.dGV + (long)off * 2 * a.I, (uint64_t)ne * 4 * a.I),
+                          (uint32_t)(4 * a.I), 0, ne, 0};
+    L.m.cols(which * a.I + i0, 256);
+    L.n.kp = v2::TStrided{make_rsrc(a.ZAp + (long)off * 4 * r, (uint64_t)ne * 8 * r), (uint32_t)(8 * r),
+                          0, ne, 0};
     L.n.cols(which * 2 * r, r, 128, r);
   } else {
-    L.n.kp = KRows{make_rsrc(a.wsq + (long)off * 2 * r, (uint64_t)ne * 4 * r), (uint32_t)(4 * r),
-                   nullptr, nullptr, 1, off, ne, 0};
+    L.m.kp = v2::TStrided{make_rsrc(a.Hh + (long)off * a.I, (uint64_t)ne * 2 * a.I), (uint32_t)(2 * a.I),
+                          0, ne, 0};
+    L.m.cols(i0, 256);
+    L.n.kp = v2::TStrided{make_rsrc(a.wsq + (long)off * 2 * r, (uint64_t)ne * 4 * r), (uint32_t)(4 * r),
+                          0, ne, 0};
     L.n.cols(0, r, 128, r);
   }
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (ne + KT - 1) / KT, acc, smem);
-  Epi<G256> ep;
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, (ne + G::KT - 1) / G::KT, acc, smem);
+  // hi + lo halves of the rank operand (tile columns c and c + 128) add up
+  Epi<G> ep;
+  static_assert(G::NB == 2, "one hi and one lo block per wave");
+  const int cpr = r / 8;  // 16-byte chunks per output row of r bf16
+  if (which < 2) {
+    // dB[e][i][c]: image rows i, columns c (pitch 128 + 8 bf16)
+    constexpr int P = 128 * 2 + 16;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
-    const int i = i0 + ep.row(mb);
-#pragma unroll
-    for (int nb = 0; nb < G256::NB / 2; ++nb)
+    for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
-        if (c >= r) continue;
-        float v[4];
+        const int c = ep.col(0, g);
+        u32x2 v;
+        v[0] = pack2(acc[0][mb][4 * g] + acc[1][mb][4 * g], acc[0][mb][4 * g + 1] + acc[1][mb][4 * g + 1]);
+        v[1] = pack2(acc[0][mb][4 * g + 2] + acc[1][mb][4 * g + 2], acc[0][mb][4 * g + 3] + acc[1][mb][4 * g + 3]);
+        *(u32x2*)(smem + ep.row(mb) * P + c * 2) = v;
+      }
+    __syncthreads();
+    uint16_t* d = (which ? a.dB3 : a.dB1) + ((long)e * a.I + i0) * r;
+    for (int idx = threadIdx.x; idx < 256 * cpr; idx += G::NT) {
+      const int row = idx / cpr, ch = idx - row * cpr;
+      *(u32x4*)(d + (long)row * r + 8 * ch) = *(const u32x4*)(smem + row * P + 16 * ch);
+    }
+  } else {
+    // dA2[e][c][i]: image rows c, columns i (pitch 256 + 8 bf16)
+    constexpr int P = 256 * 2 + 16;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(0, g), i = ep.row(mb);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          v[q] = acc[nb][mb][4 * g + q] + acc[nb + G256::NB / 2][mb][4 * g + q];
-        if (which < 2) {
-          uint16_t* d = (which ? a.dB3 : a.dB1) + ((long)e * a.I + i) * r + c;
-          *(u32x2*)d = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
-        } else {
-          uint16_t* d = a.dA2 + ((long)e * r + c) * a.I + i;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) d[(long)q * a.I] = (uint16_t)f2bf(v[q]);
-        }
+          *(uint16_t*)(smem + (c + q) * P + i * 2) = (uint16_t)f2bf(acc[0][mb][4 * g + q] + acc[1][mb][4 * g + q]);
       }
+    __syncthreads();
+    uint16_t* d = a.dA2 + (long)e * r * a.I + i0;
+    for (int idx = threadIdx.x; idx < r * 32; idx += G::NT) {
+      const int c = idx / 32, ch = idx - c * 32;
+      *(u32x4*)(d + (long)c * a.I + 8 * ch) = *(const u32x4*)(smem + c * P + 16 * ch);
+    }
   }
 }
 
@@ -470,6 +510,12 @@ __global__ __launch_bounds__(256) void k_wgrad_local(LayerArgs a) {
 //   which 2: dB2[h][c] = sum_t go[t][h] zc[t][c]
 // Token range split in fixed chunks; partials summed in chunk order.
 // ----------------------------------------------------------------------------
+struct LdWg {
+  TransK<256, KRows> m, n;
+  __device__ void load(int s) { m.load(s * KT); n.load(s * KT); }
+  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
+};
+
 __global__ __launch_bounds__(256) void k_wgrad_shared(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int ntm = a.H / 256;
@@ -547,7 +593,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
     set_lds((const void*)k_dx, GS_LDS);
-    set_lds((const void*)k_wgrad_local, G256::LDS_BYTES);
+    set_lds((const void*)k_wgrad_local, WG_LDS);
     set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
     init = true;
   }
@@ -567,7 +613,9 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_dx, dim3((a.T + GGS_T::TM - 1) / GGS_T::TM, a.H / GGS_T::TN), dim3(GGS_T::NT), GS_LDS, st, a);
-  MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(256), G256::LDS_BYTES, st, a);
+  const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
+  MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);
   MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;
   MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
