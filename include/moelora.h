@@ -128,7 +128,8 @@ moe_status moe_lora_pool_capacity(const moe_lora_desc* desc, int64_t* rows);
  *              the gathered expert input (the saved-X reuse of PR #9,
  *              "2026-09-20" -> What changed), the gate/up pre-activations in
  *              fp32, the activations and the unweighted expert outputs.
- *   scratch -- temporary space of moe_lora_backward (forward needs none). */
+ *   scratch -- temporary space of moe_lora_forward and moe_lora_backward
+ *              (nothing in it survives a call; both need the full size). */
 moe_status moe_lora_workspace_size(const moe_lora_desc* desc, size_t* saved_bytes,
                                    size_t* scratch_bytes);
 
@@ -147,7 +148,8 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
 
 /* Forward of the layer.
  *   x [T, H] bf16, topk_w [T, k] fp32 router weights (used as given),
- *   out [T, H] bf16 (overwritten), saved / scratch per moe_lora_workspace_size.
+ *   out [T, H] bf16 (overwritten), saved / scratch per moe_lora_workspace_size
+ *   (16-byte aligned; a short one returns MOE_ERR_WORKSPACE).
  *   `pool` must come from build_pool with the same desc and topk ids.
  *   x, out and the workspaces must not overlap. */
 moe_status moe_lora_forward(const moe_lora_desc* desc, const moe_pool* pool, const void* x,

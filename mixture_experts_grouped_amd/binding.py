@@ -312,7 +312,7 @@ class MoeLoraLayer:
                    self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
 
     def forward(self, x, topk_w, params, stream=None) -> torch.Tensor:
-        moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, None, stream)
+        moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, self.scratch, stream)
         return self.out
 
     def backward(self, grad_out, topk_w, params, stream=None):

@@ -57,7 +57,7 @@ struct Plan {
   size_t saved, scratch;
   // byte offsets
   size_t o_tiles, o_ntiles, o_Xp, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
-  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp;
+  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -82,6 +82,7 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
   o = 0;
+  p.o_Pt = take(T * H * 4);  // used by the forward and the backward
   p.o_q = take(T * r * 4);
   p.o_sq = take(T * 2 * r * 2);
   p.o_wsq = take(cap * 2 * r * 2);
@@ -182,6 +183,7 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.pc = (uint16_t*)(b + p.o_pc);
   a.part = (float*)(b + p.o_part);
   a.ZAp = (uint16_t*)(b + p.o_ZAp);
+  a.Pt = (float*)(b + p.o_Pt);
 }
 
 }  // namespace
@@ -248,8 +250,6 @@ moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const 
                             const float* topk_w, const moe_lora_params* params, void* out,
                             void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
                             void* stream) {
-  (void)scratch;
-  (void)scratch_bytes;
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   const Plan p = make_plan(d);
@@ -258,12 +258,17 @@ moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const 
   if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
     return MOE_ERR_INVALID;
   if (saved_bytes < p.saved) return MOE_ERR_WORKSPACE;
+  if (!aligned16(scratch) || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
   const size_t act = (size_t)d->T * d->H * 2;
-  const Range rx = rng(x, act), ro = rng(out, act), rs = rng(saved, p.saved);
-  if (overlap(rx, ro) || overlap(ro, rs) || overlap(rx, rs)) return MOE_ERR_INVALID;
+  const Range rx = rng(x, act), ro = rng(out, act), rs = rng(saved, p.saved),
+              rsc = rng(scratch, p.scratch);
+  if (overlap(rx, ro) || overlap(ro, rs) || overlap(rx, rs) || overlap(rsc, rx) || overlap(rsc, ro) ||
+      overlap(rsc, rs))
+    return MOE_ERR_INVALID;
   LayerArgs a;
   fill_common(a, d, pool, p, params);
   fill_saved(a, p, saved);
+  fill_scratch(a, p, scratch);
   a.x = (const uint16_t*)x;
   a.w = topk_w;
   a.out = (uint16_t*)out;

@@ -12,7 +12,7 @@
 //   k_w13dgrad      dU = W1_e^T dg + W3_e^T dv
 //   k_p13           P = [B1_e^T dg ; B3_e^T dv]
 //   k_pc            pc_t = s sum_j P_(t,j)
-//   k_dx            grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
+//   k_rank_dx, k_token_sum   grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
 //   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
@@ -359,41 +359,44 @@ __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a12: grad_x = [A1; A3]^T pc + sum_j dU
 // ----------------------------------------------------------------------------
-struct LdDx {
-  using KM = v2::KLoad<GGS_T::TM, GGS_T::KT, GGS_T::NW>;
-  using TN = v2::TLoad<GGS_T::TN, v2::TStrided, GGS_T::KT, GGS_T::NW>;
+// Stages [0, nst): pc columns [0, 2r) against A1 (hi/lo halves fold onto the
+// same r rows); stages [nst, 2 nst): pc columns [2r, 4r) against A3.  The pc
+// window covers all 4r columns: past 2r in a pass the A rows read zero.
+struct LdRankDx {
+  using KM = v2::KLoad<GRK_T::TM, GRK_T::KT, GRK_T::NW>;
+  using TN = v2::TLoad<GRK_T::TN, v2::TStrided, GRK_T::KT, GRK_T::NW>;
   static constexpr int INSTS = KM::NJ + TN::NJ;
   KM m;
   TN n;
-  int koff;  // first pc column of the pass
-  __device__ void issue(int s, char* sM, char* sN) const {
-    m.issue(koff + s * GGS_T::KT, 0, false, sM);
-    n.issue(s * GGS_T::KT, sN);
+  rsrc_t rs1, rs3;
+  int nst, r;
+  __device__ void issue(int s, char* sM, char* sN) {
+    const bool second = s >= nst;
+    const int k0 = (second ? s - nst : s) * GRK_T::KT;
+    m.issue((second ? 2 * r : 0) + k0, 0, false, sM);
+    n.kp.rs = second ? rs3 : rs1;
+    n.issue(k0, sN);
   }
 };
 
-// Two passes over the rank space: pc columns [0, 2r) against A1 (hi/lo
-// halves fold onto the same r rows), then [2r, 4r) against A3.
-__global__ __launch_bounds__(GGS_T::NT) void k_dx(LayerArgs a) {
+// P = [A1; A3]^T pc_t for 256 tokens x 256 columns
+__global__ __launch_bounds__(GRK_T::NT) void k_rank_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GGS_T::TM, h0 = blockIdx.y * GGS_T::TN;
+  const int t0 = blockIdx.x * GRK_T::TM, h0 = blockIdx.y * GRK_T::TN;
   const int r = a.r;
-  const int nst = (2 * r + GGS_T::KT - 1) / GGS_T::KT;
-  LdDx L;
+  LdRankDx L;
+  L.r = r;
+  L.nst = (2 * r + GRK_T::KT - 1) / GRK_T::KT;
   L.m.contig(a.pc, t0, a.T - t0, 4 * r);
-  L.n.cols(h0, GGS_T::TN);
-  f32x16 acc[GGS_T::NB][GGS_T::MB];
-  zero_acc<GGS_T>(acc);
-  L.m.window(2 * r);
-  L.koff = 0;
-  L.n.kp = v2::TStrided{make_rsrc(a.A1, (uint64_t)r * a.H * 2), (uint32_t)(2 * a.H), 0, 2 * r, r};
-  v2::run_stages2<GGS_T, 0>(L, nst, acc, smem);
   L.m.window(4 * r);
-  L.koff = 2 * r;
-  L.n.kp = v2::TStrided{make_rsrc(a.A3, (uint64_t)r * a.H * 2), (uint32_t)(2 * a.H), 0, 2 * r, r};
-  v2::run_stages2<GGS_T, 0>(L, nst, acc, smem);
-  park_tile(acc, smem);
-  gather_rows<false>(smem, a, a.dU, a.gx, t0, h0);
+  L.rs1 = make_rsrc(a.A1, (uint64_t)r * a.H * 2);
+  L.rs3 = make_rsrc(a.A3, (uint64_t)r * a.H * 2);
+  L.n.kp = v2::TStrided{L.rs1, (uint32_t)(2 * a.H), 0, 2 * r, r};
+  L.n.cols(h0, GRK_T::TN);
+  f32x16 acc[GRK_T::NB][GRK_T::MB];
+  zero_acc<GRK_T>(acc);
+  v2::run_stages2<GRK_T, 0>(L, 2 * L.nst, acc, smem);
+  store_rank_tile<GRK_T>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
 }
 
 // ----------------------------------------------------------------------------
@@ -592,7 +595,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_w13dgrad<false>, W13D_LDS);
     set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
     set_lds((const void*)k_p13, G128::LDS_BYTES);
-    set_lds((const void*)k_dx, GS_LDS);
+    set_lds((const void*)k_rank_dx, RK_LDS);
     set_lds((const void*)k_wgrad_local, WG_LDS);
     set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
     init = true;
@@ -612,7 +615,10 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_dx, dim3((a.T + GGS_T::TM - 1) / GGS_T::TM, a.H / GGS_T::TN), dim3(GGS_T::NT), GS_LDS, st, a);
+  MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK_T::TM - 1) / GRK_T::TM, a.H / GRK_T::TN), dim3(GRK_T::NT), RK_LDS, st,
+             a);
+  MOE_LAUNCH_AS("k_dx_sum", k_token_sum<false>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a,
+             a.dU, a.Pt, a.gx);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);

@@ -10,7 +10,7 @@
 //   k_a2        Z2 = s A2_e h
 //   k_w2        Ybase = W2_e h
 //   k_zc        zc_t = sum_j w_tj Z2_(t,j)          (slot order, fp32)
-//   k_combine   out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
+//   k_rank_combine, k_token_sum   out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
 #include <type_traits>
@@ -312,32 +312,31 @@ __global__ __launch_bounds__(256) void k_zc(LayerArgs a) {
   a.zc[(long)t * 2 * a.r + a.r + c] = (uint16_t)lo;
 }
 
-struct LdComb {
-  using KM = v2::KLoad<GGS::TM, GGS::KT, GGS::NW>;
-  using KN = v2::KLoad<GGS::TN, GGS::KT, GGS::NW>;
-  static constexpr int INSTS = KM::NJ + KN::NJ;
-  KM m;
-  KN n;
-  __device__ void issue(int s, char* sM, char* sN) const {
-    m.issue(s * GGS::KT, 0, false, sM);
-    n.issue(s * GGS::KT, 0, false, sN);
+struct LdRankC {
+  using KL = v2::KLoad<GRK::TM, GRK::KT, GRK::NW>;
+  static constexpr int INSTS = 2 * KL::NJ;
+  KL m, n;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GRK::KT, 0, false, sM);
+    n.issue(s * GRK::KT, 0, false, sN);
   }
 };
 
-__global__ __launch_bounds__(GGS::NT) void k_combine(LayerArgs a) {
+// P = B2 zc_t for 256 tokens x 256 columns (zc carries s and the routing
+// weights; hi/lo halves fold onto B2's r columns)
+__global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GGS::TM, h0 = blockIdx.y * GGS::TN;
+  const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
-  LdComb L;
+  LdRankC L;
   L.m.contig(a.zc, t0, a.T - t0, 2 * r);
   L.m.window(2 * r);
-  L.n.contig(a.B2, h0, GGS::TN, r);
+  L.n.contig(a.B2, h0, GRK::TN, r);
   L.n.window(2 * r, r);
-  f32x16 acc[GGS::NB][GGS::MB];
-  zero_acc<GGS>(acc);
-  v2::run_stages2<GGS, 0>(L, (2 * r + GGS::KT - 1) / GGS::KT, acc, smem);
-  park_tile(acc, smem);
-  gather_rows<true>(smem, a, a.Yb, a.out, t0, h0);
+  f32x16 acc[GRK::NB][GRK::MB];
+  zero_acc<GRK>(acc);
+  v2::run_stages2<GRK, 0>(L, (2 * r + GRK::KT - 1) / GRK::KT, acc, smem);
+  store_rank_tile<GRK>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
 }
 
 // ----------------------------------------------------------------------------
@@ -354,7 +353,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_a2, G128::LDS_BYTES);
     set_lds((const void*)k_w2<false>, W2_LDS);
     set_lds((const void*)k_w2<true>, W2_LDS);
-    set_lds((const void*)k_combine, GS_LDS);
+    set_lds((const void*)k_rank_combine, RK_LDS);
     init = true;
   }
   hipError_t err = launch_pool_prologue(a, st);
@@ -372,7 +371,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     MOE_LAUNCH(k_w2<false>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   const long nzc = (long)a.T * a.r;
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_combine, dim3((a.T + GGS::TM - 1) / GGS::TM, a.H / GGS::TN), dim3(GGS::NT), GS_LDS, st, a);
+  MOE_LAUNCH(k_rank_combine, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
+  MOE_LAUNCH_AS("k_combine_sum", k_token_sum<true>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a, a.Yb,
+             a.Pt, a.out);
   return hipGetLastError();
 }
 

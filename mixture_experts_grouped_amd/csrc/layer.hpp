@@ -67,6 +67,7 @@ struct LayerArgs {
   uint16_t* pc;      // [T, 4r]   s * sum_j P as hi/lo (pc1 | pc3)
   float* part;       // [3, nsplit, H*r] split-K partials of the shared-factor gradients
   uint16_t* ZAp;     // [cap, 4r] ZA gathered to pool rows (real rows only)
+  float* Pt;         // [T, H]    per-token rank term of the combine / grad-x (scratch)
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;

@@ -100,6 +100,9 @@ def test_calls_reject_before_any_launch():
     # short saved workspace
     assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm), fake * 64,
                                 fake * 128, saved - 1, None, 0, None) == B.MOE_ERR_WORKSPACE
+    # forward without its scratch
+    assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm), fake * 64,
+                                fake * 128, saved, fake * 4096, scratch - 1, None) == B.MOE_ERR_WORKSPACE
     # MXFP4 scales passed with a bf16 base
     prm_sc = B.MoeLoraParams(*([fake] * 2 + [fake, None] + [fake] * 6))
     assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm_sc), fake * 64,
