@@ -59,8 +59,10 @@ typedef int32_t moe_status;
  *     otherwise one of 16, 32, 64, 96, 128, 192, 240.
  *   activation: MOE_ACT_SWIGLU.  clamp: must be <= 0 or +inf (no clamp).
  * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
- *   1 <= topk <= 16, 1 <= rank <= 128.  Other values: MOE_ERR_UNSUPPORTED
- *   (non-positive sizes: MOE_ERR_INVALID). */
+ *   1 <= topk <= 16, 1 <= rank <= 128 with rank % 8 == 0, T*H*2 and 4*I*H
+ *   below 2^31 bytes (one 32-bit buffer offset per token-row tensor and per
+ *   expert's weights).  Other values: MOE_ERR_UNSUPPORTED (non-positive sizes:
+ *   MOE_ERR_INVALID).  base_format: MOE_BASE_BF16 or MOE_BASE_MXFP4. */
 typedef struct moe_lora_desc {
   int32_t T, H, I, E, topk, rank;
   int32_t block_m;
@@ -125,7 +127,7 @@ moe_status moe_lora_pool_capacity(const moe_lora_desc* desc, int64_t* rows);
 
 /* Bytes of the two workspaces:
  *   saved   -- written by moe_lora_forward, read by moe_lora_backward; holds
- *              the gathered expert input (the saved-X reuse of PR #9,
+ *              a copy of the layer input (the saved-X reuse of PR #9,
  *              "2026-09-20" -> What changed), the gate/up pre-activations in
  *              fp32, the activations and the unweighted expert outputs.
  *   scratch -- temporary space of moe_lora_forward and moe_lora_backward

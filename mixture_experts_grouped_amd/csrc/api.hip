@@ -37,6 +37,10 @@ moe_status check_desc(const moe_lora_desc* d) {
   const int64_t routes = (int64_t)d->T * d->topk;
   const int64_t cap = routes + std::min<int64_t>(d->E, routes) * 239;
   if (cap >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  // token-indexed rows (x, grad_out) and one expert's weights are each read
+  // through one 32-bit-offset buffer descriptor
+  if ((int64_t)d->T * d->H * 2 > 0x7FFFFFF0LL || (int64_t)4 * d->I * d->H > 0x7FFFFFF0LL)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -56,7 +60,7 @@ struct Plan {
   int maxtiles, nsplit;
   size_t saved, scratch;
   // byte offsets
-  size_t o_tiles, o_ntiles, o_Xp, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
+  size_t o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp;
 };
 
@@ -72,7 +76,7 @@ Plan make_plan(const moe_lora_desc* d) {
   auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
   p.o_tiles = take(sizeof(TileInfo) * p.maxtiles);
   p.o_ntiles = take(sizeof(int));
-  p.o_Xp = take(cap * H * 2);
+  p.o_Xs = take(T * H * 2);
   p.o_ZA = take(T * 4 * r * 2);
   p.o_G = take((size_t)p.maxtiles * TMG * I * 4);  // accumulator-blocked per M tile
   p.o_V = take((size_t)p.maxtiles * TMG * I * 4);
@@ -162,7 +166,7 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   char* b = (char*)saved;
   a.tiles = (TileInfo*)(b + p.o_tiles);
   a.ntiles = (int*)(b + p.o_ntiles);
-  a.Xp = (uint16_t*)(b + p.o_Xp);
+  a.Xs = (uint16_t*)(b + p.o_Xs);
   a.ZA = (uint16_t*)(b + p.o_ZA);
   a.G = (float*)(b + p.o_G);
   a.V = (float*)(b + p.o_V);

@@ -508,7 +508,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
 
 // ----------------------------------------------------------------------------
 // a14: shared-factor gradients over tokens (no pool rows involved):
-//   which 0: dA1[c][h] = sum_t (s pc1)[t][c] x[t][h]   (x_t from the saved pool)
+//   which 0: dA1[c][h] = sum_t (s pc1)[t][c] x[t][h]   (x_t from the saved copy)
 //   which 1: dA3[c][h] = sum_t (s pc3)[t][c] x[t][h]
 //   which 2: dB2[h][c] = sum_t go[t][h] zc[t][c]
 // Token range split in fixed chunks; partials summed in chunk order.
@@ -527,8 +527,9 @@ __global__ __launch_bounds__(256) void k_wgrad_shared(LayerArgs a) {
   const int tb = sp * a.kspl;
   const int nt = min(a.kspl, a.T - tb);
   LdWg L;
-  if (which < 2)  // x_t read from the saved pool through the token's first live route
-    L.m.kp = KRows{make_rsrc(a.Xp, 0), (uint32_t)(2 * a.H), a.r2row, a.Xp, a.k, tb, nt, 2};
+  if (which < 2)  // x_t from the forward's saved copy
+    L.m.kp = KRows{make_rsrc(a.Xs + (long)tb * a.H, (uint64_t)nt * 2 * a.H), (uint32_t)(2 * a.H),
+                   nullptr, nullptr, 1, tb, nt, 0};
   else
     L.m.kp = KRows{make_rsrc(a.go + (long)tb * a.H, (uint64_t)nt * 2 * a.H), (uint32_t)(2 * a.H),
                    nullptr, nullptr, 1, tb, nt, 0};

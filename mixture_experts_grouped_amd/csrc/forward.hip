@@ -142,9 +142,12 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   L.r = r;
   L.nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
   {
+    // the tile's rows are gathered from x (and ZA) by token: rows past the
+    // expert's count read zero
     int tk[KL::NJ];
     KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
     L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
+    L.mm.from_tokens(a.x, a.T, a.H, tk);
   }
   L.me.window(4 * r);
   L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
@@ -152,7 +155,6 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
 #pragma unroll
   for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
   L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
-  L.mm.contig(a.Xp, ti.row0, nrows, a.H);
   if constexpr (MX) {
     const int nl = threadIdx.x >> 1;  // this thread's W13 tile row
     const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);

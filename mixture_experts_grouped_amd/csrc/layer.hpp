@@ -47,7 +47,7 @@ struct LayerArgs {
   // saved by the forward
   TileInfo* tiles;   // [maxtiles]
   int* ntiles;       // [1]
-  uint16_t* Xp;      // [cap, H]  gathered expert input, padding rows zero
+  uint16_t* Xs;      // [T, H]    copy of x for the backward (the W13 GEMM gathers x rows itself)
   uint16_t* ZA;      // [T, 4r]   s*A1 x, s*A3 x as hi/lo
   float* G;          // gate pre-activation, accumulator-blocked (acc_block)
   float* V;          // up pre-activation, same layout

@@ -1,4 +1,5 @@
-// pool.hip -- dispatch pool builder and the saved expert input.
+// pool.hip -- dispatch pool builder, the grouped-GEMM tile map and the saved
+// copy of the layer input.
 //
 // The pool is expert-contiguous and padded per expert to BLOCK_M rows, each
 // expert starting at its true offset (DeepGEMM PR #9, "2026-09-21: restore
@@ -142,30 +143,18 @@ __global__ __launch_bounds__(64) void k_tile_map(LayerArgs a) {
   if (lane == 0) *a.ntiles = carry;
 }
 
-// Saved expert input: Xp[p] = x[token of row p], zero for padding rows.
-// Rows past the last expert's padded end are not touched.
-constexpr int GATHER_ROWS = 4;
-__global__ __launch_bounds__(256) void k_gather(LayerArgs a) {
-  const int nchunk = a.H / 8;
-  const long used = a.offsets[a.E];
-  for (int rr = 0; rr < GATHER_ROWS; ++rr) {
-    const long p = (long)blockIdx.x * GATHER_ROWS + rr;
-    if (p >= used) return;
-    const int f = a.row2r[p];
-    const u32x4* src = (f >= 0) ? (const u32x4*)(a.x + (long)(f / a.k) * a.H) : nullptr;
-    u32x4* dst = (u32x4*)(a.Xp + p * a.H);
-    for (int c = threadIdx.x; c < nchunk; c += 256) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (src != nullptr) v = src[c];
-      dst[c] = v;
-    }
-  }
+// Saved copy of the layer input for the backward (which is not given x):
+// a plain 16-byte-per-lane copy, T x H bf16.
+__global__ __launch_bounds__(256) void k_save_x(LayerArgs a) {
+  const long n = (long)a.T * a.H / 8;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ((u32x4*)a.Xs)[i] = ((const u32x4*)a.x)[i];
 }
 
 hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_tile_map, dim3(1), dim3(64), 0, st, a);
-  const long blocks = (a.cap + GATHER_ROWS - 1) / GATHER_ROWS;
-  MOE_LAUNCH(k_gather, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  const long n = (long)a.T * a.H / 8;  // H % 256 == 0
+  MOE_LAUNCH(k_save_x, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
