@@ -237,9 +237,13 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 // ----------------------------------------------------------------------------
 using GW13D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 constexpr int W13D_LDS = cmax(GW13D::LDS_BYTES, v2::TileImage<GW13D, GW13D::TN, uint16_t>::BYTES);
+#ifndef DGRAD_PINGPONG
+#define DGRAD_PINGPONG 1
+#endif
+constexpr int PPW = DGRAD_PINGPONG ? 4 : 8;  // waves that queue a stage
 struct LdW13d {
-  using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
-  using TA = v2::TLoadA<256, GW13D::KT, GW13D::NW>;
+  using KA = v2::KLoadS<256, GW13D::KT, PPW>;
+  using TA = v2::TLoadA<256, GW13D::KT, PPW>;
   static constexpr int INSTS = KA::NJ + TA::NJ;
   KA m;
   TA n;
@@ -249,7 +253,7 @@ struct LdW13d {
   }
 };
 struct LdW13dMX {
-  using KA = v2::KLoadA<256, GW13D::KT, GW13D::NW>;
+  using KA = v2::KLoadS<256, GW13D::KT, GW13D::NW>;
   static constexpr int INSTS = KA::NJ;
   KA m;
   v2::TLoadMX<GW13D::NT> nq;
@@ -278,7 +282,10 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
     L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  if constexpr (!MX && DGRAD_PINGPONG)
+    v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
+  else
+    v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
   using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll

@@ -302,32 +302,61 @@ struct TLoad {
   }
 };
 
+// KLoadA for R consecutive rows of a row-major matrix: tile row j of a lane
+// is its row 0 plus j * RPI * NW rows, so the lane keeps two byte offsets (the
+// chunk swizzle alternates with j when NW = 4) and each instruction adds its
+// row step in the scalar offset.  Rows past nvalid fall outside the
+// descriptor (sized to nvalid rows) and read zero: the range check covers
+// the scalar offset too.
+template <int R, int KT = 64, int NW = 4>
+struct KLoadS {
+  static constexpr int CPR = Depth<KT>::CPR, RPI = Depth<KT>::RPI;
+  static constexpr int NJ = R / (NW * RPI);
+  static_assert(NJ >= 1 && NJ * NW * RPI == R, "tile rows per stage");
+  rsrc_t rs;
+  uint32_t v0, v1;   // lane offsets for even / odd j
+  uint32_t jstep;    // bytes between consecutive j (RPI * NW rows)
+  __device__ __forceinline__ void contig(const uint16_t* base, long row0, long nvalid, long ld) {
+    rs = make_rsrc(base + row0 * ld, (uint64_t)(nvalid > 0 ? nvalid : 0) * ld * 2);
+    const uint32_t ldb = (uint32_t)(ld * 2);
+    jstep = (uint32_t)(RPI * NW) * ldb;
+    const int r0 = KLoad<R, KT, NW>::row_of(0);
+    v0 = (uint32_t)r0 * ldb + KLoadA<R, KT, NW>::chunk(0);
+    v1 = (uint32_t)r0 * ldb + (NJ > 1 ? KLoadA<R, KT, NW>::chunk(1) : KLoadA<R, KT, NW>::chunk(0));
+  }
+  __device__ __forceinline__ void issue(int k0, char* tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      lds_load16(rs, tile + 1024 * (w + NW * j), (j & 1) ? v1 : v0, 2u * (uint32_t)k0 + (uint32_t)j * jstep);
+  }
+};
+
 // T tile loader for a K range made of whole stages of a row-major [K, ld]
 // matrix, columns n0 .. n0 + R - 1 (all in range): offsets fixed at set-up,
 // the stage's first k-row in the scalar offset (as KLoadA).
 template <int R, int KT = 64, int NW = 4>
 struct TLoadA {
   static constexpr int CPR = R / 8, RPI = 64 / CPR, NJ = KT / (NW * RPI);
-  static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per k-row");
   static_assert(NJ >= 1 && NJ * NW * RPI == KT, "k-rows per stage");
+  static_assert(CPR >= 16, "the chunk swizzle needs 16 chunks per k-row");
   rsrc_t rs;
-  uint32_t ldb;  // bytes per k-row
-  uint32_t voff[NJ];
+  uint32_t ldb;    // bytes per k-row
+  uint32_t voff;   // this lane's offset for instruction 0; instruction j adds j RPI NW k-rows
+  // (the chunk swizzle depends on k-row mod 4, which j does not change)
   __device__ __forceinline__ void set(const uint16_t* base, long nk, long ld, int n0) {
     rs = make_rsrc(base, (uint64_t)nk * ld * 2);
     ldb = (uint32_t)(ld * 2);
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int kr = RPI * (w + NW * j) + L / CPR;
-      const int jc = (L % CPR) ^ tswz(kr);
-      voff[j] = (uint32_t)kr * ldb + 2u * (uint32_t)(n0 + 8 * jc);
-    }
+    const int kr = RPI * w + L / CPR;
+    const int jc = (L % CPR) ^ tswz(kr);
+    voff = (uint32_t)kr * ldb + 2u * (uint32_t)(n0 + 8 * jc);
   }
   __device__ __forceinline__ void issue(int k0, char* tile) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) lds_load16(rs, tile + 1024 * (w + NW * j), voff[j], (uint32_t)k0 * ldb);
+    for (int j = 0; j < NJ; ++j)
+      lds_load16(rs, tile + 1024 * (w + NW * j), voff, ((uint32_t)k0 + (uint32_t)(j * RPI * NW)) * ldb);
   }
 };
 
@@ -516,6 +545,62 @@ __device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB
       wait_lgkm0();  // the next step's barrier publishes the expanded tile
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong stage loop (eight waves, WM = 2): waves 0-3 (group A, rows
+// 0..TM/2-1) and 4-7 (group B, the other rows) alternate between a memory
+// phase -- group A queues the next stage's direct loads, each group reads all
+// of the current stage's fragments into registers -- and a compute phase of
+// back-to-back MFMAs, one barrier between phases.  Each SIMD then has one wave
+// issuing MFMAs while its other wave issues memory instructions.  Group B
+// runs one phase behind A:
+//   A: mem(0) | comp(0) | mem(1) | comp(1) | ...          | (tail)
+//   B:        | mem(0)  | comp(0)| mem(1)  | ... comp(n-1) |
+// The loader's issue(s, sM, sN) is called by group A only (it maps the stage
+// over four waves).  Both groups pass the same number of barriers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void pbar() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class G, class L>
+__device__ __forceinline__ void run_pingpong(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB], char* smem) {
+  static_assert(G::NW == 8 && G::WM == 2 && G::NBUF == 2, "two groups of four waves, two buffers");
+  constexpr int KS = G::KT / 16;
+  if (nst <= 0) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = w / G::WN, wn = w % G::WN;
+  const bool ga = wm == 0;
+  if (ga) ld.issue(0, smem, smem + G::SM_BYTES);
+  wait_vm<0>();
+  pbar();                 // stage 0 visible to both groups
+  if (!ga) pbar();        // group B starts one phase behind
+  bf16x8 fa[KS][G::NB], fb[KS][G::MB];
+  for (int s = 0; s < nst; ++s) {
+    char* cur = smem + (s & 1) * G::STAGE;
+    if (ga && s + 1 < nst) {
+      char* nxt = smem + ((s + 1) & 1) * G::STAGE;
+      ld.issue(s + 1, nxt, nxt + G::SM_BYTES);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) load_frags2<G, false>(cur, cur + G::SM_BYTES, fa[kk], fb[kk], kk, wm, wn, lane);
+    wait_lgkm0();
+    pbar();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][nb], fb[kk][mb], acc[nb][mb], 0, 0, 0);
+    if (ga) wait_vm<0>();   // stage s+1 has landed before the phase that reads it
+    pbar();
+  }
+  if (ga) pbar();         // match group B's last barrier
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------

@@ -241,8 +241,12 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
 
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
 constexpr int W2_LDS = cmax(GW2::LDS_BYTES, v2::TileImage<GW2, GW2::TN, uint16_t>::BYTES);
+#ifndef W2_PINGPONG
+#define W2_PINGPONG 1
+#endif
 struct LdW2 {
-  using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
+  // with the ping-pong loop the four waves of group A queue a whole stage
+  using KL = v2::KLoadS<256, GW2::KT, W2_PINGPONG ? 4 : GW2::NW>;
   static constexpr int INSTS = 2 * KL::NJ;
   KL m, n;
   __device__ void issue(int s, char* sM, char* sN) {
@@ -280,7 +284,10 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
     L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  if constexpr (!MX && W2_PINGPONG)
+    v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
+  else
+    v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
   using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll
