@@ -117,17 +117,23 @@ __global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
 using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES);
 // Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
+#ifndef DGRAD_PINGPONG
+#define DGRAD_PINGPONG 1
+#endif
+constexpr int PPW = DGRAD_PINGPONG ? 4 : 8;  // waves that queue a stage
+
+template <int NWL>
 struct LdW2dBase {
-  using KL = v2::KLoad<256, GW2D::KT, GW2D::NW>;
-  using TL = v2::TLoad<256, v2::TStrided, GW2D::KT, GW2D::NW>;
-  using KA = v2::KLoadA<256, GW2D::KT, GW2D::NW>;
+  using KL = v2::KLoad<256, GW2D::KT, NWL>;
+  using TL = v2::TLoad<256, v2::TStrided, GW2D::KT, NWL>;
+  using KA = v2::KLoadA<256, GW2D::KT, NWL>;
   static constexpr int INSTS = KL::NJ + TL::NJ;
   KL me;
   KA mm;
   TL ne;
   int next;
 };
-struct LdW2d : LdW2dBase {
+struct LdW2d : LdW2dBase<GW2D::NW> {
   v2::TLoadA<256, GW2D::KT, GW2D::NW> nm;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < next) {
@@ -139,7 +145,31 @@ struct LdW2d : LdW2dBase {
     }
   }
 };
-struct LdW2dMX : LdW2dBase {
+// ping-pong form: the rank-space extension (K = 2r) runs first through the
+// plain pipeline (LdW2dExt), then the base K = H through the ping-pong loop
+// (LdW2dMain, queued by four waves)
+struct LdW2dExt {
+  using KL = v2::KLoad<256, GW2D::KT, GW2D::NW>;
+  using TL = v2::TLoad<256, v2::TStrided, GW2D::KT, GW2D::NW>;
+  static constexpr int INSTS = KL::NJ + TL::NJ;
+  KL me;
+  TL ne;
+  __device__ void issue(int s, char* sM, char* sN) {
+    me.issue(s * GW2D::KT, 0, false, sM);
+    ne.issue(s * GW2D::KT, sN);
+  }
+};
+struct LdW2dMain {
+  using KA = v2::KLoadA<256, GW2D::KT, 4>;
+  static constexpr int INSTS = 2 * KA::NJ;
+  KA mm;
+  v2::TLoadA<256, GW2D::KT, 4> nm;
+  __device__ void issue(int s, char* sM, char* sN) {
+    mm.issue(s * GW2D::KT, sM);
+    nm.issue(s * GW2D::KT, sN);
+  }
+};
+struct LdW2dMX : LdW2dBase<GW2D::NW> {
   v2::TLoadMX<GW2D::NT> nq;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < next) {
@@ -159,7 +189,8 @@ template <bool MX>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2D;
-  using KL = LdW2dBase::KL;
+  using LD = typename std::conditional<MX, LdW2dMX, LdW2d>::type;
+  using KL = typename LD::KL;
   const int ntn = a.I / G::TN;
   int mt, nt;
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
@@ -167,25 +198,48 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   const int i0 = nt * G::TN;
   const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
-  typename std::conditional<MX, LdW2dMX, LdW2d>::type L;
-  L.next = (2 * r + G::KT - 1) / G::KT;
-  {
-    int tk[KL::NJ];
-    KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
-    L.me.from_tokens(a.sq, a.T, 2 * r, tk);
-    L.mm.from_tokens(a.go, a.T, a.H, tk);
-  }
-  L.me.window(2 * r);
-  L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
-                         (uint32_t)(2 * a.I), 0, 2 * r, r};
-  L.ne.cols(i0, G::TN);
-  if constexpr (MX)
-    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
-  else
-    L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
+  const int next = (2 * r + G::KT - 1) / G::KT;
+  if constexpr (!MX && DGRAD_PINGPONG) {
+    {
+      LdW2dExt X;
+      int tk[LdW2dExt::KL::NJ];
+      LdW2dExt::KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+      X.me.from_tokens(a.sq, a.T, 2 * r, tk);
+      X.me.window(2 * r);
+      X.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+                             (uint32_t)(2 * a.I), 0, 2 * r, r};
+      X.ne.cols(i0, G::TN);
+      v2::run_stages2<G, 0>(X, next, acc, smem);
+    }
+    LdW2dMain Mn;
+    {
+      int tk[LdW2dMain::KA::NJ];
+      v2::KLoad<256, G::KT, 4>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+      Mn.mm.from_tokens(a.go, a.T, a.H, tk);
+    }
+    Mn.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
+    v2::run_pingpong<G>(Mn, a.H / G::KT, acc, smem);
+  } else {
+    LD L;
+    L.next = next;
+    {
+      int tk[KL::NJ];
+      KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+      L.me.from_tokens(a.sq, a.T, 2 * r, tk);
+      L.mm.from_tokens(a.go, a.T, a.H, tk);
+    }
+    L.me.window(2 * r);
+    L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+                           (uint32_t)(2 * a.I), 0, 2 * r, r};
+    L.ne.cols(i0, G::TN);
+    if constexpr (MX)
+      L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
+    else
+      L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
+    v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
+  }
   // G and V come in accumulator-blocked (as the forward wrote them); dg and
   // dv leave row-major through LDS images, one half of the tile's columns
   // (one accumulator block column per wave) at a time
@@ -237,10 +291,6 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 // ----------------------------------------------------------------------------
 using GW13D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
 constexpr int W13D_LDS = cmax(GW13D::LDS_BYTES, v2::TileImage<GW13D, GW13D::TN, uint16_t>::BYTES);
-#ifndef DGRAD_PINGPONG
-#define DGRAD_PINGPONG 1
-#endif
-constexpr int PPW = DGRAD_PINGPONG ? 4 : 8;  // waves that queue a stage
 struct LdW13d {
   using KA = v2::KLoadS<256, GW13D::KT, PPW>;
   using TA = v2::TLoadA<256, GW13D::KT, PPW>;
