@@ -61,7 +61,7 @@ struct Plan {
   size_t saved, scratch;
   // byte offsets
   size_t o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
-  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp;
+  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -81,8 +81,6 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_G = take((size_t)p.maxtiles * TMG * I * 4);  // accumulator-blocked per M tile
   p.o_V = take((size_t)p.maxtiles * TMG * I * 4);
   p.o_Hh = take(cap * I * 2);
-  p.o_Z2 = take(cap * r * 4);
-  p.o_Yb = take(cap * H * 2);
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
   o = 0;
@@ -96,6 +94,11 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_pc = take(T * 4 * r * 2);
   p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
   p.o_ZAp = take(cap * 4 * r * 2);
+  p.o_dwp = take((size_t)(I / 256) * cap * 4);
+  // forward-only tensors share space with backward-only ones: the base
+  // outputs and Z2 are read only by the forward's combine
+  p.o_Yb = p.o_dU;  // [cap, H] bf16, same size
+  p.o_Z2 = p.o_P;   // [cap, r] fp32 inside [cap, 2r] fp32
   p.scratch = o;
   return p;
 }
@@ -171,8 +174,6 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   a.G = (float*)(b + p.o_G);
   a.V = (float*)(b + p.o_V);
   a.Hh = (uint16_t*)(b + p.o_Hh);
-  a.Z2 = (float*)(b + p.o_Z2);
-  a.Yb = (uint16_t*)(b + p.o_Yb);
   a.zc = (uint16_t*)(b + p.o_zc);
 }
 
@@ -188,6 +189,9 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.part = (float*)(b + p.o_part);
   a.ZAp = (uint16_t*)(b + p.o_ZAp);
   a.Pt = (float*)(b + p.o_Pt);
+  a.Z2 = (float*)(b + p.o_Z2);
+  a.Yb = (uint16_t*)(b + p.o_Yb);
+  a.dwp = (float*)(b + p.o_dwp);
 }
 
 }  // namespace

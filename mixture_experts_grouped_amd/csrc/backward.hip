@@ -5,10 +5,11 @@
 // weight gradients, no full-width side-delta scratch); padding never enters
 // the shared reductions.  Steps:
 //   k_q             q_t = B2^T go_t, once per token (B2 is shared)
-//   k_dw            grad_w[t,j] = <go_t, Ybase> + <q_t, Z2>  (= <go_t, y>),
-//                   and s w q_t per route for dA2
 //   k_w2dgrad       dh = w (W2_e^T go_t + A2_e^T s q_t) (K-extended), then
-//                   the SwiGLU backward from the saved fp32 G, V
+//                   the SwiGLU backward from the saved fp32 G, V; per column
+//                   tile, the partial router gradient <W2_e^T go + A2_e^T s q, h>
+//   k_dw            grad_w[t,j] = sum of those partials (= <go_t, y_tj>), and
+//                   s w q_t per route for dA2
 //   k_w13dgrad      dU = W1_e^T dg + W3_e^T dv
 //   k_p13           P = [B1_e^T dg ; B3_e^T dv]
 //   k_pc            pc_t = s sum_j P_(t,j)
@@ -76,46 +77,14 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
 }
 
 // one wave per route (t, j)
-__global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
-  const long f = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (f >= (long)a.T * a.k) return;
-  const int t = (int)(f / a.k);
-  const int row = a.r2row[f];
-  if (row < 0) {
-    if (lane == 0) a.gw[f] = 0.0f;
-    return;
-  }
-  const u32x4* gp = (const u32x4*)(a.go + (long)t * a.H);
-  const u32x4* yp = (const u32x4*)(a.Yb + (long)row * a.H);
-  float acc = 0.0f;
-  for (int c = lane; c < a.H / 8; c += 64) {
-    const u32x4 g = gp[c], y = yp[c];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      acc += bf2f(g[d] & 0xffffu) * bf2f(y[d] & 0xffffu);
-      acc += bf2f(g[d] >> 16) * bf2f(y[d] >> 16);
-    }
-  }
-  const float wr = a.w[f];
-  for (int c = lane; c < a.r; c += 64) {
-    const float qv = a.q[(long)t * a.r + c];
-    acc += qv * a.Z2[(long)row * a.r + c];
-    uint32_t hi, lo;
-    split_hl(a.s * wr * qv, hi, lo);
-    a.wsq[(long)row * 2 * a.r + c] = (uint16_t)hi;
-    a.wsq[(long)row * 2 * a.r + a.r + c] = (uint16_t)lo;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) a.gw[f] = acc;
-}
-
 // ----------------------------------------------------------------------------
 // a9: dh = w (W2_e^T go + A2_e^T s q), SwiGLU backward -> dG, dV
 // ----------------------------------------------------------------------------
 using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-outer
-constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES);
+// epilogue: two LDS images (dg, dv) and the router-gradient row sums of the
+// WN column-wave groups
+constexpr int W2D_IMG = v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES;
+constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * W2D_IMG + GW2D::WN * GW2D::TM * 4);
 // Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
 #ifndef DGRAD_PINGPONG
 #define DGRAD_PINGPONG 1
@@ -257,6 +226,12 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   char* img_g = smem;
   char* img_v = smem + Img::BYTES;
   uint16_t* out = a.dGV + ti.row0 * 2 * (long)a.I + i0;
+  // router gradient: grad_w = <go, W2 h + s B2 A2 h> = <W2^T go + A2^T s q, h>,
+  // i.e. the row dot product of the (unweighted) accumulator with h, which
+  // the SwiGLU below recomputes in fp32 from G and V
+  float dw[G::MB];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) dw[mb] = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < G::NB; ++nb) {
 #pragma unroll
@@ -269,11 +244,16 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
         f32x4 dg, dv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float dh = wr[mb] * acc[nb][mb][4 * g + q];
+          const float av = acc[nb][mb][4 * g + q];
           const float sg = sigmoidf_(gg[q]);
-          dv[q] = dh * gg[q] * sg;
-          dg[q] = dh * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          const float u = av * gg[q] * sg;  // unweighted dv
+          dw[mb] += u * vv[q];
+          dv[q] = wr[mb] * u;
+          dg[q] = wr[mb] * av * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
         }
+        // keep the running sum in place: otherwise the compiler sinks the
+        // whole dot product past the loop and holds its operands meanwhile
+        asm volatile("" : "+v"(dw[mb]));
         const int col = ep.col(nb, g) - nb * (G::TN / 2);
         Img::put(img_g, ep.row(mb), col, dg);
         Img::put(img_v, ep.row(mb), col, dv);
@@ -283,6 +263,67 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     Img::flush(img_g, out + nb * (G::TN / 2), 2 * a.I, nrows);
     Img::flush(img_v, out + a.I + nb * (G::TN / 2), 2 * a.I, nrows);
     __syncthreads();
+  }
+  // a row's 256 columns: two lanes (lane, lane ^ 32) in each of the WN waves
+  // of its row group; summed in a fixed order
+  float* red = (float*)(smem + 2 * Img::BYTES);  // [WN][TM]
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const float v = dw[mb] + __shfl_xor(dw[mb], 32, 64);
+    if (lane < 32) red[wn * G::TM + ep.row(mb)] = v;
+  }
+  __syncthreads();
+  // (nrows counts to the expert's end; this tile holds at most TM of them)
+  for (int lr = threadIdx.x; lr < nrows && lr < G::TM; lr += G::NT) {
+    float t = 0.0f;
+#pragma unroll
+    for (int c = 0; c < G::WN; ++c) t += red[c * G::TM + lr];
+    a.dwp[(long)nt * a.cap + ti.row0 + lr] = t;
+  }
+}
+
+// Sixteen lanes per route: grad_w = the column tiles' partials summed in
+// tile order; s w q (hi/lo) for the rank-space gradients, 8 columns a lane.
+constexpr int DW_LANES = 16;
+__global__ __launch_bounds__(256) void k_dw(LayerArgs a) {
+  const long f = (long)blockIdx.x * (256 / DW_LANES) + (threadIdx.x / DW_LANES);
+  const int sl = threadIdx.x % DW_LANES;
+  if (f >= (long)a.T * a.k) return;
+  const int t = (int)(f / a.k);
+  const int row = a.r2row[f];
+  if (row < 0) {
+    if (sl == 0) a.gw[f] = 0.0f;
+    return;
+  }
+  if (sl == 0) {
+    const int ntn = a.I / GW2D::TN;
+    const float* p = a.dwp + row;
+    float acc = 0.0f;
+    int n = 0;
+    for (; n + 8 <= ntn; n += 8) {  // eight loads in flight, added in order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p[(long)(n + j) * a.cap];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+    for (; n < ntn; ++n) acc += p[(long)n * a.cap];
+    a.gw[f] = acc;
+  }
+  const float sw = a.s * a.w[f];
+  for (int c = 8 * sl; c < a.r; c += 8 * DW_LANES) {  // r % 8 == 0
+    const f32x4* qp = (const f32x4*)(a.q + (long)t * a.r + c);
+    const f32x4 q0 = qp[0], q1 = qp[1];
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      split_hl(sw * q0[j], hi[j], lo[j]);
+      split_hl(sw * q1[j], hi[4 + j], lo[4 + j]);
+    }
+    uint16_t* d = a.wsq + (long)row * 2 * a.r + c;
+    *(u32x4*)d = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+    *(u32x4*)(d + a.r) =
+        u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
   }
 }
 
@@ -660,12 +701,12 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   }
   const int tm = (a.T + 255) / 256;
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
-  const long nr = (long)a.T * a.k;
-  MOE_LAUNCH(k_dw, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w2dgrad<true>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
   else
     MOE_LAUNCH(k_w2dgrad<false>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
+  const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
+  MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w13dgrad<true>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
   else

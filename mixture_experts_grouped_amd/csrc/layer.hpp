@@ -52,8 +52,8 @@ struct LayerArgs {
   float* G;          // gate pre-activation, accumulator-blocked (acc_block)
   float* V;          // up pre-activation, same layout
   uint16_t* Hh;      // [cap, I]  silu(G) * V
-  float* Z2;         // [cap, r]  s * A2_e h
-  uint16_t* Yb;      // [cap, H]  W2_e h (unweighted base output)
+  float* Z2;         // [cap, r]  s * A2_e h (scratch, forward only)
+  uint16_t* Yb;      // [cap, H]  W2_e h, unweighted base output (scratch, forward only)
   uint16_t* zc;      // [T, 2r]   sum_j w Z2 as hi/lo
   // forward output
   uint16_t* out;     // [T, H]
@@ -68,6 +68,7 @@ struct LayerArgs {
   float* part;       // [3, nsplit, H*r] split-K partials of the shared-factor gradients
   uint16_t* ZAp;     // [cap, 4r] ZA gathered to pool rows (real rows only)
   float* Pt;         // [T, H]    per-token rank term of the combine / grad-x (scratch)
+  float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;

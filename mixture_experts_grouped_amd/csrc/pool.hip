@@ -14,108 +14,145 @@ namespace moelora {
 
 constexpr int POOL_THREADS = 1024;
 constexpr int POOL_WAVES = POOL_THREADS / 64;
+constexpr int POOL_V = 16;                            // routes per thread per chunk
+constexpr int POOL_CHUNK = POOL_THREADS * POOL_V;     // routes per chunk
 
-// One workgroup builds the whole pool: an LDS histogram, a wave scan of the
-// padded counts, then the routes in chunks of 1024.  Inside a chunk every wave
-// ranks its lanes among equal expert ids with ballots over the id bits; the
-// per-wave counts are scanned per expert, giving each route its row in
-// ascending route order.  Integer-only and deterministic.
+__device__ __forceinline__ int pool_pad(int n, int bm) { return ((n + bm - 1) / bm) * bm; }
+
+// Sum of v over the workgroup (every thread gets it).  `red` holds
+// POOL_WAVES ints; the call ends with a barrier, so `red` can be reused.
+__device__ __forceinline__ int pool_block_sum(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < POOL_WAVES; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Workgroup e counts the routes of expert e (workgroup 0 also the invalid
+// ids): compares and a workgroup sum, no atomics.
+__global__ __launch_bounds__(POOL_THREADS) void k_pool_count(const int32_t* __restrict__ idx, int nroutes,
+                                                             int E, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ err) {
+  __shared__ int red[POOL_WAVES];
+  const int tid = threadIdx.x, e = blockIdx.x;
+  int m = 0, bad = 0;
+  for (int c0 = 0; c0 < nroutes; c0 += POOL_CHUNK) {
+    int ids[POOL_V];  // all of a chunk's loads in flight at once
+#pragma unroll
+    for (int v = 0; v < POOL_V; ++v) {
+      const int f = c0 + v * POOL_THREADS + tid;
+      ids[v] = (f < nroutes) ? idx[f] : -1;
+    }
+#pragma unroll
+    for (int v = 0; v < POOL_V; ++v) {
+      m += ids[v] == e;
+      bad += !(ids[v] >= -1 && ids[v] < E);
+    }
+  }
+  const int n = pool_block_sum(m, red);
+  if (tid == 0) counts[e] = n;
+  if (e == 0) {
+    const int nbad = pool_block_sum(bad, red);
+    if (tid == 0 && err != nullptr) *err = nbad;
+  }
+}
+
+// Workgroup e places the routes of expert e: its padded offset is the sum of
+// the padded counts before it; then it walks the routes in chunks of
+// POOL_CHUNK (thread tid reads routes c0 + v * POOL_THREADS + tid, coalesced)
+// and gives the routes of expert e consecutive rows in ascending route order:
+// a route's row is the matches before it, counted with one ballot per (v,
+// wave) and an exclusive scan of those counts in (v, wave) order, which is
+// route order.  Workgroup 0 also marks dropped routes; the last workgroup
+// clears the unused suffix of the pool.
 __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
     const int32_t* __restrict__ idx, int nroutes, int E, int bm, long cap,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ r2row,
-    int32_t* __restrict__ row2r, int32_t* __restrict__ err) {
-  extern __shared__ int sm[];
-  int* cnt = sm;                   // [E]   counts, later the running row of each expert
-  int* base = sm + E;              // [E+1] padded offsets
-  int* wcnt = sm + 2 * E + 1;      // [POOL_WAVES][E]
-  __shared__ int bad;
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ r2row,
+    int32_t* __restrict__ row2r) {
+  constexpr int NC = POOL_V * POOL_WAVES;  // (v, wave) counts per chunk
+  static_assert(NC <= POOL_THREADS && NC % 64 == 0 && POOL_V <= 64, "scan layout");
+  __shared__ int red[POOL_WAVES];
+  __shared__ int cnt[NC];   // [v][wave] matches
+  __shared__ int pre[NC];   // exclusive prefix of cnt
+  __shared__ int wsum[NC / 64];
+  __shared__ int total;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += POOL_THREADS) cnt[e] = 0;
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  for (int f = tid; f < nroutes; f += POOL_THREADS) {
-    const int e = idx[f];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else if (e != -1)
-      atomicAdd(&bad, 1);
+  const int e = blockIdx.x;
+  int before = 0;
+  for (int i = tid; i < e; i += POOL_THREADS) before += pool_pad(counts[i], bm);
+  const int off = pool_block_sum(before, red);
+  const int n = counts[e], padded = pool_pad(n, bm);
+  if (tid == 0) {
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = off + padded;
   }
-  __syncthreads();
-  if (wv == 0) {
-    int carry = 0;
-    for (int b0 = 0; b0 < E; b0 += 64) {
-      const int e = b0 + lane;
-      const int v = (e < E) ? ((cnt[e] + bm - 1) / bm) * bm : 0;
-      int x = v;
+  for (int p = off + n + tid; p < off + padded; p += POOL_THREADS) row2r[p] = -1;  // padding rows
+  if (e == E - 1)
+    for (long p = off + padded + tid; p < cap; p += POOL_THREADS) row2r[p] = -1;  // unused suffix
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int run = off;  // next row of expert e (uniform)
+  for (int c0 = 0; c0 < nroutes; c0 += POOL_CHUNK) {
+    int ids[POOL_V];
+    unsigned long long bal[POOL_V];
+#pragma unroll
+    for (int v = 0; v < POOL_V; ++v) {
+      const int f = c0 + v * POOL_THREADS + tid;
+      ids[v] = (f < nroutes) ? idx[f] : -1;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int v = 0; v < POOL_V; ++v) {
+      bal[v] = __ballot(ids[v] == e);
+      if (lane == v) mine = __popcll(bal[v]);
+    }
+    if (lane < POOL_V) cnt[lane * POOL_WAVES + wv] = mine;
+    __syncthreads();
+    int x = 0, c = 0;
+    if (tid < NC) {
+      c = cnt[tid];
+      x = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
       }
-      if (e < E) base[e] = carry + x - v;
-      carry += __shfl(x, 63, 64);
+      if (lane == 63) wsum[wv] = x;
     }
-    if (lane == 0) base[E] = carry;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += POOL_THREADS) {
-    counts[e] = cnt[e];
-    offsets[e] = base[e];
-    for (int p = base[e] + cnt[e]; p < base[e + 1]; ++p) row2r[p] = -1;  // padding rows
-  }
-  if (tid == 0) {
-    offsets[E] = base[E];
-    if (err != nullptr) *err = bad;
-  }
-  for (long p = base[E] + tid; p < cap; p += POOL_THREADS) row2r[p] = -1;  // unused suffix
-  __syncthreads();
-  for (int e = tid; e < E; e += POOL_THREADS) cnt[e] = base[e];
-  int nbits = 1;
-  while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = "no expert") fit in nbits
-  for (int c0 = 0; c0 < nroutes; c0 += POOL_THREADS) {
-    for (int i = tid; i < POOL_WAVES * E; i += POOL_THREADS) wcnt[i] = 0;
     __syncthreads();
-    const int f = c0 + tid;
-    const int e = (f < nroutes) ? idx[f] : -1;
-    const bool ok = (e >= 0 && e < E);
-    const int key = ok ? e : E;
-    unsigned long long same = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const unsigned long long m = __ballot(bit);
-      same &= bit ? m : ~m;
+    if (tid < NC) {
+      int carry = 0;
+      for (int w = 0; w < wv; ++w) carry += wsum[w];
+      pre[tid] = carry + x - c;
+      if (tid == NC - 1) total = carry + x;
     }
-    const int rank = __popcll(same & ((1ull << lane) - 1ull));
-    const int nsame = __popcll(same);
-    if (ok && rank == nsame - 1) wcnt[wv * E + e] = nsame;
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += POOL_THREADS) {
-      int run = cnt[e2];
-      for (int w2 = 0; w2 < POOL_WAVES; ++w2) {
-        const int c = wcnt[w2 * E + e2];
-        wcnt[w2 * E + e2] = run;
-        run += c;
+#pragma unroll
+    for (int v = 0; v < POOL_V; ++v) {
+      const int f = c0 + v * POOL_THREADS + tid;
+      if (ids[v] == e) {
+        const int pos = run + pre[v * POOL_WAVES + wv] + __popcll(bal[v] & below);
+        r2row[f] = pos;
+        row2r[pos] = f;
+      } else if (e == 0 && f < nroutes && !(ids[v] >= 0 && ids[v] < E)) {
+        r2row[f] = -1;  // dropped or invalid route
       }
-      cnt[e2] = run;
     }
-    __syncthreads();
-    if (ok) {
-      const int row = wcnt[wv * E + e] + rank;
-      r2row[f] = row;
-      row2r[row] = f;
-    } else if (f < nroutes) {
-      r2row[f] = -1;
-    }
-    __syncthreads();
+    run += total;
+    __syncthreads();  // cnt / pre / total are rewritten by the next chunk
   }
 }
 
 hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
                              int32_t* err, hipStream_t st) {
-  const size_t lds = sizeof(int) * (size_t)(2 * E + 1 + POOL_WAVES * E);
-  MOE_LAUNCH(k_build_pool, dim3(1), dim3(POOL_THREADS), lds, st, idx, nroutes, E, bm, cap,
-                     counts, offsets, r2row, row2r, err);
+  MOE_LAUNCH(k_pool_count, dim3((unsigned)E), dim3(POOL_THREADS), 0, st, idx, nroutes, E, counts, err);
+  MOE_LAUNCH(k_build_pool, dim3((unsigned)E), dim3(POOL_THREADS), 0, st, idx, nroutes, E, bm, cap, counts,
+             offsets, r2row, row2r);
   return hipGetLastError();
 }
 
