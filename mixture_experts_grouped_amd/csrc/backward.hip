@@ -27,13 +27,16 @@
 namespace moelora {
 
 using G256 = Geo<4, 4, 2, 2>;
-using G128 = Geo<4, 2, 2, 2>;
+// thin GEMMs (N = r): smaller M tiles so the grid fills the 256 CUs
+using GS64 = Geo<1, 2, 2, 2>;   // 64 x 128 tile, wave 32 x 64
+using GS128 = Geo<2, 2, 2, 2>;  // 128 x 128 tile, wave 64 x 64
+constexpr int P13_SUB = TMG / GS128::TM;  // sub-tiles per pool M tile
 
 // ----------------------------------------------------------------------------
 // a8: q = B2^T go per token, router gradients
 // ----------------------------------------------------------------------------
 struct LdQ {
-  RowsK<256> m;
+  RowsK<GS64::TM> m;
   TransK<128, KStrided> n;
   __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
@@ -41,22 +44,22 @@ struct LdQ {
 
 __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * 256;
+  const int t0 = blockIdx.x * GS64::TM;
   const int r = a.r;
   LdQ L;
   L.m.contig(a.go, t0, a.T - t0, a.H);
   L.m.window(a.H);
   L.n.kp = KStrided{make_rsrc(a.B2, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
   L.n.cols(0, r);
-  f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.H / KT, acc, smem);
-  Epi<G128> ep;
+  f32x16 acc[GS64::NB][GS64::MB];
+  mainloop<GS64>(L, a.H / KT, acc, smem);
+  Epi<GS64> ep;
 #pragma unroll
-  for (int mb = 0; mb < G128::MB; ++mb) {
+  for (int mb = 0; mb < GS64::MB; ++mb) {
     const int t = t0 + ep.row(mb);
     if (t >= a.T) continue;
 #pragma unroll
-    for (int nb = 0; nb < G128::NB; ++nb)
+    for (int nb = 0; nb < GS64::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
 // a11: P1 = B1_e^T dg, P3 = B3_e^T dv   (blockIdx.y selects)
 // ----------------------------------------------------------------------------
 struct LdP {
-  RowsK<256> m;
+  RowsK<GS128::TM> m;
   TransK<128, KStrided> n;
   __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
@@ -404,25 +407,27 @@ struct LdP {
 
 __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int mt = blockIdx.x, which = blockIdx.y;
+  const int mt = blockIdx.x / P13_SUB, which = blockIdx.y;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
+  const long row0 = ti.row0 + (long)(blockIdx.x % P13_SUB) * GS128::TM;  // this sub-tile's rows
+  if (row0 >= ti.row_end) return;
   const int r = a.r;
   LdP L;
-  L.m.contig(a.dGV + which * a.I, ti.row0, ti.row_end - ti.row0, 2 * a.I);
+  L.m.contig(a.dGV + which * a.I, row0, ti.row_end - row0, 2 * a.I);
   L.m.window(a.I);
   const uint16_t* Be = (which ? a.B3 : a.B1) + (long)ti.e * a.I * r;
   L.n.kp = KStrided{make_rsrc(Be, (uint64_t)a.I * r * 2), (uint32_t)(2 * r), 0, a.I, 0};
   L.n.cols(0, r);
-  f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.I / KT, acc, smem);
-  Epi<G128> ep;
+  f32x16 acc[GS128::NB][GS128::MB];
+  mainloop<GS128>(L, a.I / KT, acc, smem);
+  Epi<GS128> ep;
 #pragma unroll
-  for (int mb = 0; mb < G128::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
+  for (int mb = 0; mb < GS128::MB; ++mb) {
+    const long row = row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
 #pragma unroll
-    for (int nb = 0; nb < G128::NB; ++nb)
+    for (int nb = 0; nb < GS128::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
@@ -688,19 +693,19 @@ static void set_lds(const void* fn, int bytes) {
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
-    set_lds((const void*)k_q, G128::LDS_BYTES);
+    set_lds((const void*)k_q, GS64::LDS_BYTES);
     set_lds((const void*)k_w2dgrad<false>, W2D_LDS);
     set_lds((const void*)k_w2dgrad<true>, W2D_LDS);
     set_lds((const void*)k_w13dgrad<false>, W13D_LDS);
     set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
-    set_lds((const void*)k_p13, G128::LDS_BYTES);
+    set_lds((const void*)k_p13, GS128::LDS_BYTES);
     set_lds((const void*)k_rank_dx, RK_LDS);
     set_lds((const void*)k_wgrad_local, WG_LDS);
     set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
     init = true;
   }
-  const int tm = (a.T + 255) / 256;
-  MOE_LAUNCH(k_q, dim3(tm), dim3(256), G128::LDS_BYTES, st, a);
+  const int tm = (a.T + GS64::TM - 1) / GS64::TM;
+  MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w2dgrad<true>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
   else
@@ -711,7 +716,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     MOE_LAUNCH(k_w13dgrad<true>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
   else
     MOE_LAUNCH(k_w13dgrad<false>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
-  MOE_LAUNCH(k_p13, dim3(a.maxtiles, 2), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK_T::TM - 1) / GRK_T::TM, a.H / GRK_T::TN), dim3(GRK_T::NT), RK_LDS, st,

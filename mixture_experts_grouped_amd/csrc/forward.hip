@@ -24,14 +24,17 @@ namespace moelora {
 
 hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st);
 
-using G256 = Geo<4, 4, 2, 2>;  // 256 x 256 tile, wave 128 x 128
-using G128 = Geo<4, 2, 2, 2>;  // 256 x 128 tile, wave 128 x 64
+// thin GEMMs (N = r): smaller M tiles so the grid fills the 256 CUs
+using GS64 = Geo<1, 2, 2, 2>;   // 64 x 128 tile, wave 32 x 64
+using GS128 = Geo<2, 2, 2, 2>;  // 128 x 128 tile, wave 64 x 64
+constexpr int A2_SUB = TMG / GS128::TM;  // sub-tiles per pool M tile
 
 // ----------------------------------------------------------------------------
 // a3: ZA = s [A1; A3] x  (dense over tokens; N = 2r)
 // ----------------------------------------------------------------------------
+template <int R>
 struct LdPlain {
-  RowsK<256> m;
+  RowsK<R> m;
   RowsK<128> n;
   __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
@@ -39,20 +42,20 @@ struct LdPlain {
 
 __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * G128::TM, fac = blockIdx.y;  // fac 0: A1, 1: A3
+  const int t0 = blockIdx.x * GS64::TM, fac = blockIdx.y;  // fac 0: A1, 1: A3
   const int r = a.r;
-  LdPlain L;
+  LdPlain<GS64::TM> L;
   L.m.contig(a.x, t0, a.T - t0, a.H);
   L.m.window(a.H);
   L.n.contig(fac ? a.A3 : a.A1, 0, r, a.H);
   L.n.window(a.H);
-  f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.H / KT, acc, smem);
-  Epi<G128> ep;
+  f32x16 acc[GS64::NB][GS64::MB];
+  mainloop<GS64>(L, a.H / KT, acc, smem);
+  Epi<GS64> ep;
 #pragma unroll
-  for (int nb = 0; nb < G128::NB; ++nb)
+  for (int nb = 0; nb < GS64::NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < G128::MB; ++mb) {
+    for (int mb = 0; mb < GS64::MB; ++mb) {
       const int t = t0 + ep.row(mb);
       if (t >= a.T) continue;
 #pragma unroll
@@ -209,24 +212,26 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int mt = blockIdx.x;
+  const int mt = blockIdx.x / A2_SUB;
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
+  const long row0 = ti.row0 + (long)(blockIdx.x % A2_SUB) * GS128::TM;  // this sub-tile's rows
+  if (row0 >= ti.row_end) return;
   const uint16_t* A2e = a.A2 + (long)ti.e * a.r * a.I;
-  LdPlain L;
-  L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
+  LdPlain<GS128::TM> L;
+  L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
   L.m.window(a.I);
   L.n.contig(A2e, 0, a.r, a.I);
   L.n.window(a.I);
-  f32x16 acc[G128::NB][G128::MB];
-  mainloop<G128>(L, a.I / KT, acc, smem);
-  Epi<G128> ep;
+  f32x16 acc[GS128::NB][GS128::MB];
+  mainloop<GS128>(L, a.I / KT, acc, smem);
+  Epi<GS128> ep;
 #pragma unroll
-  for (int mb = 0; mb < G128::MB; ++mb) {
-    const long row = ti.row0 + ep.row(mb);
+  for (int mb = 0; mb < GS128::MB; ++mb) {
+    const long row = row0 + ep.row(mb);
     if (row >= ti.row_end) continue;
 #pragma unroll
-    for (int nb = 0; nb < G128::NB; ++nb)
+    for (int nb = 0; nb < GS128::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
@@ -356,10 +361,10 @@ static void set_lds(const void* fn, int bytes) {
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
-    set_lds((const void*)k_shrink, G128::LDS_BYTES);
+    set_lds((const void*)k_shrink, GS64::LDS_BYTES);
     set_lds((const void*)k_w13<false>, W13_LDS);
     set_lds((const void*)k_w13<true>, W13_LDS);
-    set_lds((const void*)k_a2, G128::LDS_BYTES);
+    set_lds((const void*)k_a2, GS128::LDS_BYTES);
     set_lds((const void*)k_w2<false>, W2_LDS);
     set_lds((const void*)k_w2<true>, W2_LDS);
     set_lds((const void*)k_rank_combine, RK_LDS);
@@ -367,13 +372,13 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   }
   hipError_t err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
-  const int tm = (a.T + 255) / 256;
-  MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), G128::LDS_BYTES, st, a);
+  const int tm = (a.T + GS64::TM - 1) / GS64::TM;
+  MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w13<true>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
   else
     MOE_LAUNCH(k_w13<false>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
-  MOE_LAUNCH(k_a2, dim3(a.maxtiles), dim3(256), G128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w2<true>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   else
