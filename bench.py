@@ -33,8 +33,9 @@ METRIC = "MoE side-LoRA F+B ms and grouped-GEMM TFLOP/s (64 experts, 98K rows, H
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
-GEMM_KERNELS = ("k_shrink", "k_w13", "k_a2", "k_w2", "k_combine", "k_q", "k_w2dgrad",
-                "k_w13dgrad", "k_p13", "k_dx", "k_wgrad_local", "k_wgrad_shared")
+GEMM_KERNELS = ("k_shrink", "k_w13", "k_a2", "k_w2", "k_rank_combine", "k_q", "k_w2dgrad",
+                "k_w13dgrad", "k_p13", "k_rank_dx", "k_wgrad_local", "k_wgrad_shared",
+                "k_wgrad_w13", "k_wgrad_w2")
 
 
 def kernel_flops(T, M, H, I, r):
@@ -44,20 +45,24 @@ def kernel_flops(T, M, H, I, r):
         "k_w13": M * (4.0 * H * I + 4.0 * I * r),
         "k_a2": 2.0 * M * I * r,
         "k_w2": 2.0 * M * H * I,
-        "k_combine": 2.0 * T * H * r,
+        "k_rank_combine": 2.0 * T * H * r,
         "k_q": 2.0 * T * H * r,
         "k_w2dgrad": M * (2.0 * H * I + 2.0 * I * r),
         "k_w13dgrad": 4.0 * M * H * I,
         "k_p13": 4.0 * M * I * r,
-        "k_dx": 4.0 * T * H * r,
+        "k_rank_dx": 4.0 * T * H * r,
         "k_wgrad_local": 6.0 * M * I * r,
         "k_wgrad_shared": 6.0 * T * H * r,
+        "k_wgrad_w13": 4.0 * M * H * I,  # optional frozen-weight gradients
+        "k_wgrad_w2": 2.0 * M * H * I,
     }
 
 
-def step_flops(T, M, H, I, r):
+def step_flops(T, M, H, I, r, base_grads=False):
     fwd = M * (6.0 * H * I + 6.0 * I * r) + 6.0 * T * H * r
     bwd = M * (6.0 * H * I + 12.0 * I * r) + 12.0 * T * H * r
+    if base_grads:
+        bwd += 6.0 * M * H * I  # dW13 and dW2
     return fwd, bwd
 
 
@@ -154,6 +159,9 @@ def main():
     ap.add_argument("--base", choices=("bf16", "mxfp4"), default="bf16",
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
+    ap.add_argument("--base-grads", action="store_true",
+                    help="also compute the frozen-weight gradients dW13, dW2 (the ordinary path; "
+                         "not the headline workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -213,7 +221,7 @@ def main():
 
     desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale,
                        base_format=B.MOE_BASE_MXFP4 if mx else B.MOE_BASE_BF16)
-    layer = B.MoeLoraLayer(desc, device=dev)
+    layer = B.MoeLoraLayer(desc, device=dev, base_grads=args.base_grads)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -253,7 +261,7 @@ def main():
 
     M = int((idx >= 0).sum())
     T, H, Idim, r = shape.T, shape.H, shape.I, shape.rank
-    fwd_fl, bwd_fl = step_flops(T, M, H, Idim, r)
+    fwd_fl, bwd_fl = step_flops(T, M, H, Idim, r, args.base_grads)
     tflops = (fwd_fl + bwd_fl) / (ms * 1e-3) / 1e12
     kfl = kernel_flops(T, M, H, Idim, r)
     per_kernel = {}
@@ -279,7 +287,7 @@ def main():
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
     cpu = None
-    if not args.no_cpu_baseline and not mx:
+    if not args.no_cpu_baseline and not mx and not args.base_grads:
         cpu = cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, args.cpu_seconds)
         print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s",
               file=sys.stderr, flush=True)
@@ -300,10 +308,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (("MXFP4 base (e2m1 + e8m0/32), " if mx else "") +
+                         ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
                          f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, SwiGLU, s=1"),
             "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
-            "block_m": layer.block_m, "base": args.base,
+            "block_m": layer.block_m, "base": args.base, "base_grads": args.base_grads,
         },
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),

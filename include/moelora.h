@@ -103,8 +103,14 @@ typedef struct moe_lora_params {
 } moe_lora_params;
 
 /* Gradient outputs (device bf16, same layouts as the parameters).  The six
- * adapter gradients are required.  dW13 / dW2 are optional ("ordinary" MoE
- * training): NULL skips them. */
+ * adapter gradients are required.  dW13 [E, 2I, H] and dW2 [E, H, I] are the
+ * optional frozen-weight gradients of the ordinary path (PR #9, "Matched
+ * old/new performance"): dW13_e = sum over e's routes of [dg; dv] x_t^T,
+ * dW2_e = sum of (w go_t) h^T, contracted over the expert's rows in pool
+ * order; an expert without routes gets exact zeros.  NULL skips each; a
+ * non-NULL pointer must be 16-byte aligned (else MOE_ERR_INVALID).  With an
+ * MXFP4 base they are the gradients with respect to the dequantised
+ * weights. */
 typedef struct moe_lora_grads {
   void *dA1, *dA3, *dB1, *dB3, *dA2, *dB2;
   void *dW13, *dW2;

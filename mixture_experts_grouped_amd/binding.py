@@ -277,7 +277,8 @@ class MoeLoraLayer:
     """Device buffers for one layer shape (pool arrays, workspaces, outputs)
     and the three calls in order.  Convenience for tests and the benchmark."""
 
-    def __init__(self, desc: MoeLoraDesc, device="cuda"):
+    def __init__(self, desc: MoeLoraDesc, device="cuda", base_grads: bool = False):
+        """base_grads: also compute the frozen-weight gradients dW13, dW2."""
         self.desc = desc
         self.device = device
         self.block_m = moe_lora_block_m(desc)
@@ -306,6 +307,9 @@ class MoeLoraLayer:
             "dA2": torch.empty(E, r, I, dtype=bf, device=device),
             "dB2": torch.empty(H, r, dtype=bf, device=device),
         }
+        if base_grads:
+            self.grads["dW13"] = torch.empty(E, 2 * I, H, dtype=bf, device=device)
+            self.grads["dW2"] = torch.empty(E, H, I, dtype=bf, device=device)
 
     def build_pool(self, topk_idx: torch.Tensor, stream=None) -> None:
         build_pool(self.desc, topk_idx, self.pool["counts"], self.pool["offsets"],

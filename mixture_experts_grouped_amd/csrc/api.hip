@@ -301,7 +301,9 @@ moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
   const void* gs[] = {grads->dA1, grads->dA3, grads->dB1, grads->dB3, grads->dA2, grads->dB2};
   for (const void* g : gs)
     if (!aligned16(g)) return MOE_ERR_INVALID;
-  if (grads->dW13 != nullptr || grads->dW2 != nullptr) return MOE_ERR_UNSUPPORTED;
+  // the frozen-weight gradients are optional (NULL: not computed)
+  if ((grads->dW13 != nullptr && !aligned16(grads->dW13)) || (grads->dW2 != nullptr && !aligned16(grads->dW2)))
+    return MOE_ERR_INVALID;
   if (saved_bytes < p.saved || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
   const size_t act = (size_t)d->T * d->H * 2;
   const Range rgo = rng(grad_out, act), rgx = rng(grad_x, act), rs = rng(saved, p.saved),
@@ -323,6 +325,8 @@ moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
   a.dB3 = (uint16_t*)grads->dB3;
   a.dA2 = (uint16_t*)grads->dA2;
   a.dB2 = (uint16_t*)grads->dB2;
+  a.dW13 = (uint16_t*)grads->dW13;
+  a.dW2 = (uint16_t*)grads->dW2;
   const hipError_t e = launch_backward(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

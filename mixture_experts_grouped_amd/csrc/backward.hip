@@ -526,15 +526,32 @@ __global__ __launch_bounds__(256) void k_gather_za(LayerArgs a) {
 }
 
 // Both operands K-outer (K = the expert's rows): T tiles with a k window of
-// the expert's row count (rows past it read zero).
+// the expert's row count (rows past it read zero).  Each stage re-bases the
+// two descriptors at its first row, so the byte offsets stay small whatever
+// the expert's row count.
 using GWG = v2::Geo2<4, 2, 2, 4, true, true, 64>;
 struct LdWg2 {
   using TL = v2::TLoad<256, v2::TStrided, GWG::KT, GWG::NW>;
   static constexpr int INSTS = 2 * TL::NJ;
   TL m, n;
+  const char *mbase, *nbase;  // the expert's first row of each operand
+  int ne;                     // the expert's row count
+  // row-major sources with mld / nld bytes a row
+  __device__ void set(const void* mrow0, uint32_t mld, const void* nrow0, uint32_t nld, int ne_) {
+    mbase = (const char*)mrow0;
+    nbase = (const char*)nrow0;
+    ne = ne_;
+    m.kp = v2::TStrided{make_rsrc(mbase, 0), mld, 0, 0, 0};  // per stage in issue
+    n.kp = v2::TStrided{make_rsrc(nbase, 0), nld, 0, 0, 0};
+  }
   __device__ void issue(int s, char* sM, char* sN) {
-    m.issue(s * GWG::KT, sM);
-    n.issue(s * GWG::KT, sN);
+    const int k0 = s * GWG::KT, left = ne - k0;
+    m.kp.rs = make_rsrc(mbase + (long)k0 * m.kp.ldb, (uint64_t)left * m.kp.ldb);
+    n.kp.rs = make_rsrc(nbase + (long)k0 * n.kp.ldb, (uint64_t)left * n.kp.ldb);
+    m.kp.span = left;
+    n.kp.span = left;
+    m.issue(0, sM);
+    n.issue(0, sN);
   }
 };
 constexpr int WG_LDS = cmax(GWG::LDS_BYTES, 128 * (256 * 2 + 16));
@@ -548,18 +565,12 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   const int ne = a.counts[e], off = a.offsets[e];
   LdWg2 L;
   if (which < 2) {
-    L.m.kp = v2::TStrided{make_rsrc(a.dGV + (long)off * 2 * a.I, (uint64_t)ne * 4 * a.I),
-                          (uint32_t)(4 * a.I), 0, ne, 0};
+    L.set(a.dGV + (long)off * 2 * a.I, (uint32_t)(4 * a.I), a.ZAp + (long)off * 4 * r, (uint32_t)(8 * r), ne);
     L.m.cols(which * a.I + i0, 256);
-    L.n.kp = v2::TStrided{make_rsrc(a.ZAp + (long)off * 4 * r, (uint64_t)ne * 8 * r), (uint32_t)(8 * r),
-                          0, ne, 0};
     L.n.cols(which * 2 * r, r, 128, r);
   } else {
-    L.m.kp = v2::TStrided{make_rsrc(a.Hh + (long)off * a.I, (uint64_t)ne * 2 * a.I), (uint32_t)(2 * a.I),
-                          0, ne, 0};
+    L.set(a.Hh + (long)off * a.I, (uint32_t)(2 * a.I), a.wsq + (long)off * 2 * r, (uint32_t)(4 * r), ne);
     L.m.cols(i0, 256);
-    L.n.kp = v2::TStrided{make_rsrc(a.wsq + (long)off * 2 * r, (uint64_t)ne * 4 * r), (uint32_t)(4 * r),
-                          0, ne, 0};
     L.n.cols(0, r, 128, r);
   }
   f32x16 acc[G::NB][G::MB];
@@ -686,6 +697,76 @@ __global__ __launch_bounds__(256) void k_reduce_shared(LayerArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// a13, optional (the frozen-weight gradients of the ordinary path):
+//   dW13_e = sum over e's rows of [dg; dv] u^T     ([2I, H])
+//   dW2_e  = sum over e's rows of (w go) h^T       ([H, I])
+// K-grouped over the expert's rows like the adapter gradients.  The token
+// operand is first laid out in pool order -- x rows, or w * go rounded to
+// bf16 -- in the dU space, which nothing reads after the grad-x sum.
+// ----------------------------------------------------------------------------
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_pool_rows(LayerArgs a, const uint16_t* src, uint16_t* dst) {
+  const long p = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= a.offsets[a.E]) return;
+  const int f = a.row2r[p];
+  if (f < 0) return;  // padding rows are never read
+  const u32x4* s = (const u32x4*)(src + (long)(f / a.k) * a.H);
+  u32x4* d = (u32x4*)(dst + p * a.H);
+  const float wr = WEIGHTED ? a.w[f] : 1.0f;
+  for (int c = lane; c < a.H / 8; c += 64) {
+    u32x4 v = s[c];
+    if (WEIGHTED) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = pack2(wr * bf2f(v[q] & 0xffffu), wr * bf2f(v[q] >> 16));
+    }
+    d[c] = v;
+  }
+}
+
+using BaseImg = v2::TileImage<GWG, GWG::TN / 2, uint16_t>;
+static_assert(BaseImg::BYTES <= WG_LDS, "epilogue image fits the pipeline's LDS");
+
+// which 0: dW13 (M = 2I columns of dG|dV, N = H columns of x in pool order);
+// which 1: dW2 (M = H columns of w go in pool order, N = I columns of h).
+// Tiles of one expert are consecutive, N fastest, and each XCD walks a
+// contiguous range of them.
+__global__ __launch_bounds__(GWG::NT) void k_wgrad_base(LayerArgs a, int which) {
+  extern __shared__ __align__(16) char smem[];
+  using G = GWG;
+  const int M = which == 0 ? 2 * a.I : a.H, N = which == 0 ? a.H : a.I;
+  const int ntn = N / G::TN, per = (M / G::TM) * ntn;
+  const int b = xcd_remap(blockIdx.x, a.E * per);
+  const int e = b / per, mt = (b % per) / ntn, nt = b % ntn;
+  const int ne = a.counts[e], off = a.offsets[e];
+  const uint16_t* ms = which == 0 ? a.dGV : a.dU;  // pool-ordered [rows, M]
+  const uint16_t* ns = which == 0 ? a.dU : a.Hh;   // pool-ordered [rows, N]
+  LdWg2 L;
+  L.set(ms + (long)off * M, (uint32_t)(2 * M), ns + (long)off * N, (uint32_t)(2 * N), ne);
+  L.m.cols(mt * G::TM, G::TM);
+  L.n.cols(nt * G::TN, G::TN);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, (ne + G::KT - 1) / G::KT, acc, smem);  // an empty expert writes zeros
+  uint16_t* out = (which == 0 ? a.dW13 : a.dW2) + (long)e * M * N + (long)mt * G::TM * N + nt * G::TN;
+  Epi<G> ep;
+  static_assert(G::NB == 2, "one block column per half");
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        BaseImg::put(smem, ep.row(mb), ep.col(nb, g) - nb * (G::TN / 2),
+                     f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                           acc[nb][mb][4 * g + 3]});
+    __syncthreads();
+    BaseImg::flush(smem, out + nb * (G::TN / 2), N, G::TM);
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------
 static void set_lds(const void* fn, int bytes) {
   hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
@@ -701,6 +782,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     set_lds((const void*)k_p13, GS128::LDS_BYTES);
     set_lds((const void*)k_rank_dx, RK_LDS);
     set_lds((const void*)k_wgrad_local, WG_LDS);
+    set_lds((const void*)k_wgrad_base, WG_LDS);
     set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
     init = true;
   }
@@ -729,6 +811,19 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;
   MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
+  if (a.dW13 != nullptr || a.dW2 != nullptr) {
+    const unsigned prow = (unsigned)((a.cap + 3) / 4);  // rows past the pool's end return at once
+    if (a.dW13 != nullptr) {
+      MOE_LAUNCH(k_pool_rows<false>, dim3(prow), dim3(256), 0, st, a, a.Xs, a.dU);
+      MOE_LAUNCH_AS("k_wgrad_w13", k_wgrad_base, dim3(a.E * (2 * a.I / GWG::TM) * (a.H / GWG::TN)), dim3(GWG::NT),
+                    WG_LDS, st, a, 0);
+    }
+    if (a.dW2 != nullptr) {
+      MOE_LAUNCH(k_pool_rows<true>, dim3(prow), dim3(256), 0, st, a, a.go, a.dU);
+      MOE_LAUNCH_AS("k_wgrad_w2", k_wgrad_base, dim3(a.E * (a.H / GWG::TM) * (a.I / GWG::TN)), dim3(GWG::NT),
+                    WG_LDS, st, a, 1);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -67,9 +67,11 @@ class GpuRun:
     download everything."""
 
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
-                 scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None):
+                 scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None,
+                 base_grads: bool = False):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
-        then case's W13/W2 are not uploaded."""
+        then case's W13/W2 are not uploaded.  base_grads: also request the
+        frozen-weight gradients dW13, dW2."""
         import torch
         from mixture_experts_grouped_amd import binding as B
         self.torch = torch
@@ -78,7 +80,7 @@ class GpuRun:
         fmt = B.MOE_BASE_MXFP4 if mx is not None else B.MOE_BASE_BF16
         self.desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank,
                                 scale=s, block_m=block_m, base_format=fmt)
-        self.layer = B.MoeLoraLayer(self.desc)
+        self.layer = B.MoeLoraLayer(self.desc, base_grads=base_grads)
         dev = "cuda"
 
         def bf(a):
@@ -119,7 +121,7 @@ class GpuRun:
         res["out"] = u16(L.out)
         res["grad_x"] = u16(L.grad_x)
         res["grad_w"] = L.grad_topk_w.cpu().numpy()
-        for n in GRAD_NAMES:
+        for n in L.grads:  # the six adapter gradients (and dW13, dW2 when requested)
             res[n] = u16(L.grads[n])
         return res
 

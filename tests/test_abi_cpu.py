@@ -136,7 +136,12 @@ def test_flop_model_matches_the_closed_form():
     T, M, H, Id, r = 16384, 98304, 4096, 2048, 128
     f, b = bench.step_flops(T, M, H, Id, r)
     assert abs(f / 1e12 - 5.154) < 2e-3 and abs(b / 1e12 - 5.360) < 2e-3
-    assert abs(sum(bench.kernel_flops(T, M, H, Id, r).values()) - (f + b)) < 1.0
+    kf = bench.kernel_flops(T, M, H, Id, r)
+    base = ("k_wgrad_w13", "k_wgrad_w2")  # the optional frozen-weight gradients
+    assert abs(sum(v for k, v in kf.items() if k not in base) - (f + b)) < 1.0
+    f2, b2 = bench.step_flops(T, M, H, Id, r, base_grads=True)
+    assert f2 == f and abs(b2 - b - sum(kf[k] for k in base)) < 1.0
+    assert abs(sum(kf[k] for k in base) / 1e12 - 4.948) < 2e-3
 
 
 def test_mxfp4_base_needs_both_scales():
@@ -154,6 +159,23 @@ def test_mxfp4_base_needs_both_scales():
         assert lib.moe_lora_forward(byref(d), byref(pool), fake, fake, byref(prm), fake * 64,
                                     fake * 128, saved, None, 0, None) == B.MOE_ERR_INVALID
         grads = B.MoeLoraGrads(*([fake * 3] * 6), None, None)
+        assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128,
+                                     saved, fake * 64, fake * 200, byref(grads), fake * 256,
+                                     scratch, None) == B.MOE_ERR_INVALID
+
+
+def test_frozen_weight_grad_pointers_must_be_aligned():
+    """dW13 / dW2 are optional; a misaligned one is rejected on the host."""
+    lib = B.library()
+    d = B.make_desc(64, 256, 256, 8, 2, 8)
+    saved, scratch = B.moe_lora_workspace_size(d)
+    cap = B.moe_lora_pool_capacity(d)
+    fake = 1 << 20
+    pool = B.MoePool(fake, fake, fake, fake, cap, 16)
+    prm = B.MoeLoraParams(fake, fake, None, None, *([fake] * 6))
+    byref = ctypes.byref
+    for w13, w2 in ((fake + 2, None), (None, fake + 8)):
+        grads = B.MoeLoraGrads(*([fake * 3] * 6), w13, w2)
         assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128,
                                      saved, fake * 64, fake * 200, byref(grads), fake * 256,
                                      scratch, None) == B.MOE_ERR_INVALID

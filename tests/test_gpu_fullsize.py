@@ -7,8 +7,9 @@ computable samples:
 - tokens: out, grad_x and grad_w of a token depend only on that token's
   routes, so the oracle runs on the sub-batch of sampled tokens (with just
   their experts' weights) and must match those rows;
-- experts: dB1_e, dB3_e, dA2_e depend only on expert e's routes, so the oracle
-  runs on the tokens routed to e with every other route masked;
+- experts: dB1_e, dB3_e, dA2_e (and dW13_e, dW2_e, checked on one expert)
+  depend only on expert e's routes, so the oracle runs on the tokens routed
+  to e with every other route masked;
 and one identity over the whole output: sum_tj w_tj grad_w_tj = <grad_out,
 out> (the loss is linear in the weights' combine).
 """
@@ -46,7 +47,7 @@ def run():
     del experts
     case.update(shared)
     Hn.log(f"[fullsize] inputs ready, shape={SHAPE}")
-    res = Hn.GpuRun(SHAPE, case).run()
+    res = Hn.GpuRun(SHAPE, case, base_grads=True).run()
     Hn.log("[fullsize] GPU step done")
     return case, res
 
@@ -87,8 +88,9 @@ def test_sampled_expert_adapter_grads_match_oracle(run, e):
     assert len(toks) == 1536  # uniform routing: exactly 1536 routes per expert, distinct tokens
     sub, used = _sub_problem(case, toks, only_expert=e)
     assert used.tolist() == [e]
-    _, ref_g = Hn.oracle_run(sub, SHAPE.scale)
-    for n in ("dB1", "dB3", "dA2"):
+    base = e == SAMPLE_EXPERTS[1]  # the frozen-weight gradients on one expert
+    _, ref_g = Hn.oracle_run(sub, SHAPE.scale, base_grads=base)
+    for n in ("dB1", "dB3", "dA2") + (("dW13", "dW2") if base else ()):
         Hn.assert_close(f"{n}[{e}]", Hn.f64(res[n][e]), ref_g[n][0])
 
 

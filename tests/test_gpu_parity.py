@@ -62,6 +62,26 @@ def test_parity_against_oracle(name):
                                            for k, v in rep.items()))
 
 
+@pytest.mark.parametrize("name", ["r128_masked", "multi_tile", "zipf_small"])
+def test_frozen_weight_grads_against_oracle(name):
+    """The optional dW13 / dW2 of the ordinary path: against the oracle, exact
+    zeros for experts without routes, and no effect on any other output."""
+    shape, key, routing, mask = CASES[name]
+    Hn.log(f"[parity] frozen-weight grads, case={name} shape={shape}")
+    case = _case(shape, key, routing, mask)
+    res = Hn.GpuRun(shape, case, base_grads=True).run()
+    _, ref_g = Hn.oracle_run(case, shape.scale, base_grads=True)
+    for n in ("dW13", "dW2"):
+        Hn.assert_close(f"{name}:{n}", Hn.f64(res[n]), ref_g[n])
+    counts = np.bincount(case["topk_idx"][case["topk_idx"] >= 0], minlength=shape.E)
+    for e in np.nonzero(counts == 0)[0]:
+        for n in ("dW13", "dW2"):
+            assert not np.any(res[n][e]), (n, e)
+    plain = Hn.GpuRun(shape, case).run()
+    for n in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(plain[n], res[n]), n
+
+
 def test_zero_scale_matches_base_and_zero_adapter_grads():
     shape = I.TINY
     case = _case(shape, (1,))
