@@ -385,11 +385,6 @@ __device__ __forceinline__ u32x4 fp4x8_bf16(uint32_t w, float sc) {
 __device__ __forceinline__ uint32_t bload_u8(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
-}
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0), others untouched
 }
@@ -571,15 +566,14 @@ __device__ __forceinline__ void pbar() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// PRE: k-steps whose fragments the memory phase reads (KS: all of them; KS/2:
-// half, the other half is read during the compute phase into the registers of
-// the k-steps already multiplied -- fewer registers, for kernels that need
-// them elsewhere).
-template <class G, class L, int PRE = G::KT / 16>
+// All four k-steps' fragments are read in the memory phase: the group that
+// runs one phase behind (B) must be done with a buffer before the barrier at
+// which group A starts refilling it, so no LDS read may move into the
+// compute phase with two buffers.
+template <class G, class L>
 __device__ __forceinline__ void run_pingpong(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB], char* smem) {
   static_assert(G::NW == 8 && G::WM == 2 && G::NBUF == 2, "two groups of four waves, two buffers");
   constexpr int KS = G::KT / 16;
-  static_assert(PRE == KS || 2 * PRE == KS, "all or half of the k-steps up front");
   if (nst <= 0) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = w / G::WN, wn = w % G::WN;
@@ -588,7 +582,7 @@ __device__ __forceinline__ void run_pingpong(L& ld, int nst, f32x16 (&acc)[G::NB
   wait_vm<0>();
   pbar();                 // stage 0 visible to both groups
   if (!ga) pbar();        // group B starts one phase behind
-  bf16x8 fa[PRE][G::NB], fb[PRE][G::MB];
+  bf16x8 fa[KS][G::NB], fb[KS][G::MB];
   for (int s = 0; s < nst; ++s) {
     char* cur = smem + (s & 1) * G::STAGE;
     if (ga && s + 1 < nst) {
@@ -596,29 +590,16 @@ __device__ __forceinline__ void run_pingpong(L& ld, int nst, f32x16 (&acc)[G::NB
       ld.issue(s + 1, nxt, nxt + G::SM_BYTES);
     }
 #pragma unroll
-    for (int kk = 0; kk < PRE; ++kk) load_frags2<G, false>(cur, cur + G::SM_BYTES, fa[kk], fb[kk], kk, wm, wn, lane);
+    for (int kk = 0; kk < KS; ++kk) load_frags2<G, false>(cur, cur + G::SM_BYTES, fa[kk], fb[kk], kk, wm, wn, lane);
     wait_lgkm0();
     pbar();
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int slot = kk % PRE;
-      if (PRE < KS && kk > 0 && kk + 1 < KS) {
-        // the fragments of step kk + 1 replace those of step kk - 1 (multiplied)
-        if (kk + 1 >= PRE) load_frags2<G, false>(cur, cur + G::SM_BYTES, fa[(kk + 1) % PRE], fb[(kk + 1) % PRE],
-                                                 kk + 1, wm, wn, lane);
-      }
-      if constexpr (PRE < KS) {
-        // step kk's reads were issued one step ago; step kk + 1's may stay in flight
-        constexpr int NRD = G::MB * (G::MTR ? 2 : 1) + G::NB * (G::NTR ? 2 : 1);
-        if (kk >= PRE && kk + 1 < KS) wait_lgkm<NRD>();
-        if (kk >= PRE && kk + 1 == KS) wait_lgkm0();
-      }
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][nb], fb[slot][mb], acc[nb][mb], 0, 0, 0);
-    }
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][nb], fb[kk][mb], acc[nb][mb], 0, 0, 0);
     if (ga) wait_vm<0>();   // stage s+1 has landed before the phase that reads it
     pbar();
   }
