@@ -560,7 +560,10 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GWG;
   const int nti = a.I / 256;
-  const int e = blockIdx.x / nti, i0 = (blockIdx.x % nti) * 256, which = blockIdx.y;
+  // an expert's column tiles share its rank operand rows: keep them on one
+  // XCD (each XCD walks a contiguous range of tiles), so its L2 serves them
+  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int e = b / nti, i0 = (b % nti) * 256, which = blockIdx.y;
   const int r = a.r;
   const int ne = a.counts[e], off = a.offsets[e];
   LdWg2 L;
