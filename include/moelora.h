@@ -135,7 +135,7 @@ moe_status moe_lora_pool_capacity(const moe_lora_desc* desc, int64_t* rows);
  *   saved   -- written by moe_lora_forward, read by moe_lora_backward; holds
  *              a copy of the layer input (the saved-X reuse of PR #9,
  *              "2026-09-20" -> What changed), the gate/up pre-activations in
- *              fp32 and the activations.
+ *              fp16 and the activations.
  *   scratch -- temporary space of moe_lora_forward and moe_lora_backward
  *              (nothing in it survives a call; both need the full size). */
 moe_status moe_lora_workspace_size(const moe_lora_desc* desc, size_t* saved_bytes,

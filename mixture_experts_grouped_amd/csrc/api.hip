@@ -78,8 +78,8 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_ntiles = take(sizeof(int));
   p.o_Xs = take(T * H * 2);
   p.o_ZA = take(T * 4 * r * 2);
-  p.o_G = take((size_t)p.maxtiles * TMG * I * 4);  // accumulator-blocked per M tile
-  p.o_V = take((size_t)p.maxtiles * TMG * I * 4);
+  p.o_G = take((size_t)p.maxtiles * TMG * I * 2);  // fp16, accumulator-blocked per M tile
+  p.o_V = take((size_t)p.maxtiles * TMG * I * 2);
   p.o_Hh = take(cap * I * 2);
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
@@ -171,8 +171,8 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   a.ntiles = (int*)(b + p.o_ntiles);
   a.Xs = (uint16_t*)(b + p.o_Xs);
   a.ZA = (uint16_t*)(b + p.o_ZA);
-  a.G = (float*)(b + p.o_G);
-  a.V = (float*)(b + p.o_V);
+  a.G = (_Float16*)(b + p.o_G);
+  a.V = (_Float16*)(b + p.o_V);
   a.Hh = (uint16_t*)(b + p.o_Hh);
   a.zc = (uint16_t*)(b + p.o_zc);
 }

@@ -6,7 +6,7 @@
 // the shared reductions.  Steps:
 //   k_q             q_t = B2^T go_t, once per token (B2 is shared)
 //   k_w2dgrad       dh = w (W2_e^T go_t + A2_e^T s q_t) (K-extended), then
-//                   the SwiGLU backward from the saved fp32 G, V; per column
+//                   the SwiGLU backward from the saved fp16 G, V; per column
 //                   tile, the partial router gradient <W2_e^T go + A2_e^T s q, h>
 //   k_dw            grad_w[t,j] = sum of those partials (= <go_t, y_tj>), and
 //                   s w q_t per route for dA2
@@ -242,8 +242,8 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
       const long ob = acc_block(mt, G::m_local(wm, mb) / 32, (i0 + G::n_local(wn, nb)) / 32, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 gg = *(const f32x4*)(a.G + ob + 256 * g);
-        const f32x4 vv = *(const f32x4*)(a.V + ob + 256 * g);
+        const f32x4 gg = __builtin_convertvector(*(const f16x4*)(a.G + ob + 256 * g), f32x4);
+        const f32x4 vv = __builtin_convertvector(*(const f16x4*)(a.V + ob + 256 * g), f32x4);
         f32x4 dg, dv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   v2::run_stages2<G, 2>(L, L.nsplit + a.H / G::KT, acc, smem);
-  // G and V go out in the accumulator-blocked layout (1 KB per wave access);
+  // G and V go out as fp16 in the accumulator-blocked layout (512 bytes per
+  // wave access);
   // h (bf16, row-major for the next GEMM) through an LDS image of the tile
   using ImgH = v2::TileImage<G, HALF, uint16_t>;
   Epi<G> ep;
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
           vv[q] = acc[nb + NH][mb][4 * g + q];
           hv[q] = gv[q] * sigmoidf_(gv[q]) * vv[q];
         }
-        *(f32x4*)(a.G + ob + 256 * g) = gv;
-        *(f32x4*)(a.V + ob + 256 * g) = vv;
+        *(f16x4*)(a.G + ob + 256 * g) = __builtin_convertvector(gv, f16x4);  // round to nearest even
+        *(f16x4*)(a.V + ob + 256 * g) = __builtin_convertvector(vv, f16x4);
         ImgH::put(smem, ep.row(mb), ep.col(nb, g), hv);
       }
     }

@@ -49,8 +49,8 @@ struct LayerArgs {
   int* ntiles;       // [1]
   uint16_t* Xs;      // [T, H]    copy of x for the backward (the W13 GEMM gathers x rows itself)
   uint16_t* ZA;      // [T, 4r]   s*A1 x, s*A3 x as hi/lo
-  float* G;          // gate pre-activation, accumulator-blocked (acc_block)
-  float* V;          // up pre-activation, same layout
+  _Float16* G;       // gate pre-activation, fp16, accumulator-blocked (acc_block)
+  _Float16* V;       // up pre-activation, same layout
   uint16_t* Hh;      // [cap, I]  silu(G) * V
   float* Z2;         // [cap, r]  s * A2_e h (scratch, forward only)
   uint16_t* Yb;      // [cap, H]  W2_e h, unweighted base output (scratch, forward only)
