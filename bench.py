@@ -147,6 +147,74 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
+SWEEP_T = (1, 15, 16, 17, 90, 91, 176, 177, 346, 347, 688, 689, 1029, 1030, 2048)
+
+
+def token_sweep(torch, args):
+    """F+B time over the token sweep.  At these sizes the layer reads every
+    active expert's base weights (W13 + W2, 50.3 MB bf16) once in the forward
+    and once in the backward, so the rate reported is those bytes over the F+B
+    time, against the 8 TB/s HBM peak.  Weights are generated once for all 64
+    experts (the sweep shape's seeds); routing, x and grad_out per T."""
+    import numpy as np
+    from mixture_experts_grouped_amd import binding as B
+    from mixture_experts_grouped_amd import inputs as I
+    base = I.sweep_shape(1)
+    key = (1,)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    dev = "cuda"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        experts = list(ex.map(lambda e: I.expert_weights(base, key, e), range(base.E)))
+    params = {}
+    for nm in ("W13", "W2", "B1", "B3", "A2"):
+        t = torch.empty((base.E, *experts[0][nm].shape), dtype=torch.bfloat16, device=dev)
+        for e in range(base.E):
+            t[e].copy_(bf(experts[e][nm]))
+        params[nm] = t
+    del experts
+    for nm, a in I.shared_weights(base, key).items():
+        params[nm] = bf(a)
+    per_expert = 2 * base.I * base.H * 2 + base.H * base.I * 2  # W13 + W2 bytes
+    rows = []
+    for T in SWEEP_T:
+        shape = I.sweep_shape(T)
+        skey = I.config_key(1, T)
+        idx, w = I.route_softmax_topk(shape, skey, mask_prob=0.2)
+        x, go = bf(I.tokens(shape, skey)), bf(I.grad_out(shape, skey))
+        tidx, tw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+        desc = B.make_desc(T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale)
+        layer = B.MoeLoraLayer(desc, device=dev)
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            layer.step(tidx, x, tw, params, go, stream)
+        samples = []
+        for _ in range(3):  # three rounds of ten steps, per-step median
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(10):
+                layer.step(tidx, x, tw, params, go, stream)
+            torch.cuda.synchronize()
+            samples.append((time.perf_counter() - t0) * 1e3 / 10)
+        ms = float(np.median(samples))
+        active = int(len(np.unique(idx[idx >= 0])))
+        gbs = 2.0 * active * per_expert / (ms * 1e-3) / 1e9
+        rows.append({"T": T, "routes": int((idx >= 0).sum()), "active_experts": active, "ms": round(ms, 4),
+                     "ms_min": round(min(samples), 4), "ms_max": round(max(samples), 4),
+                     "weight_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / 8000.0, 4),
+                     "floor_ms": round(2.0 * active * per_expert / 8e12 * 1e3, 4)})
+        print(f"[sweep] T={T} {rows[-1]}", file=sys.stderr, flush=True)
+        del layer
+    print(json.dumps({"metric": "token sweep: F+B ms and base-weight read rate vs 8 TB/s",
+                      "unit": "ms", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+                      "config": {"workload": "H 4096, I 2048, 64 experts, top-6, rank 128, 20% of routes "
+                                             "dropped, softmax routing; T per row"},
+                      "sweep": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +230,10 @@ def main():
     ap.add_argument("--base-grads", action="store_true",
                     help="also compute the frozen-weight gradients dW13, dW2 (the ordinary path; "
                          "not the headline workload)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline: time F+B over the token sweep (H 4096, I 2048, "
+                         "64 experts, top-6, rank 128, 20%% of routes dropped) and report the "
+                         "weight-read rate against HBM; prints one JSON line with a table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -175,6 +247,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.sweep:
+        token_sweep(torch, args)
         return
     from mixture_experts_grouped_amd import binding as B
     from mixture_experts_grouped_amd import inputs as I
