@@ -51,3 +51,62 @@ def test_mxfp4_bitwise_vs_bf16_dequantised_and_oracle(name):
     ref_out, ref_g = Hn.oracle_run(case_deq, shape.scale)
     rep = Hn.compare_all(res_mx, ref_out, ref_g, tag=name + ":mx:")
     Hn.log(f"[mxfp4] {name} " + " ".join(f"{k}={v['rel_l2']:.2e}" for k, v in rep.items()))
+
+
+def test_mxfp4_production_share_bitwise_vs_dequantised():
+    """The production share (16,384 tokens x top-6 over 64 experts, H 4096,
+    I 2048, rank 128) with an MXFP4 base, in the benchmark's launch
+    configuration: bitwise equal to the bf16 path on the dequantised weights,
+    and sampled tokens against the oracle on them."""
+    import concurrent.futures as cf
+    import os
+    from oracle import mxfp4 as OMX
+
+    shape = I.PROD
+    key = I.config_key(4)
+    threads = min(16, len(os.sched_getaffinity(0)))
+
+    def expert(e):
+        w = I.expert_weights(shape, key, e)
+        out = {n: w[n] for n in ("B1", "B3", "A2")}
+        for n in ("W13", "W2"):
+            q, sc = I.mxfp4_quantize(I.bf16_bits_to_f32(w[n]))
+            out[n + "_q"], out[n + "_s"] = q, sc
+            out[n] = I.f32_to_bf16_bits(OMX.dequantize(q, sc).astype(np.float32))
+        return out
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        ex_fut = ex.map(expert, range(shape.E))
+        fx, fg = ex.submit(I.tokens, shape, key), ex.submit(I.grad_out, shape, key)
+        experts = list(ex_fut)
+        case = {"x": fx.result(), "grad_out": fg.result()}
+    case["topk_idx"], case["topk_w"] = I.route_balanced(shape, key)
+    for n in ("W13", "W2", "B1", "B3", "A2"):
+        case[n] = np.stack([d[n] for d in experts])  # W13/W2: the dequantised bf16 weights
+    mx = {n: np.stack([d[n + "_q"] for d in experts]) for n in ("W13", "W2")}
+    mx.update({n + "_scale": np.stack([d[n + "_s"] for d in experts]) for n in ("W13", "W2")})
+    del experts
+    case.update(I.shared_weights(shape, key))
+    Hn.log("[mxfp4] production share: inputs ready")
+
+    res_mx = Hn.GpuRun(shape, case, mx=mx).run()
+    res_bf = Hn.GpuRun(shape, case).run()
+    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(np.asarray(res_mx[k]).view(np.uint8), np.asarray(res_bf[k]).view(np.uint8)), \
+            f"production:{k} MXFP4 differs from the bf16 path on the dequantised weights"
+
+    toks = np.array([0, 1, 4097, 9999, 16383])
+    idx = case["topk_idx"][toks]
+    used = np.unique(idx[idx >= 0])
+    remap = np.full(shape.E, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    sub = {"x": case["x"][toks], "grad_out": case["grad_out"][toks], "topk_w": case["topk_w"][toks],
+           "topk_idx": np.where(idx >= 0, remap[np.maximum(idx, 0)], -1).astype(np.int32)}
+    for n in ("W13", "W2", "B1", "B3", "A2"):
+        sub[n] = case[n][used]
+    for n in ("A1", "A3", "B2"):
+        sub[n] = case[n]
+    ref_out, ref_g = Hn.oracle_run(sub, shape.scale)
+    Hn.assert_close("production:mx:out[sample]", Hn.f64(res_mx["out"][toks]), ref_out)
+    Hn.assert_close("production:mx:grad_x[sample]", Hn.f64(res_mx["grad_x"][toks]), ref_g["grad_x"])
+    Hn.assert_close("production:mx:grad_w[sample]", res_mx["grad_w"][toks], ref_g["grad_w"])
