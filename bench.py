@@ -189,14 +189,25 @@ def token_sweep(torch, args):
         desc = B.make_desc(T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale)
         layer = B.MoeLoraLayer(desc, device=dev)
         stream = torch.cuda.current_stream()
-        for _ in range(args.warmup):
+        for _ in range(max(1, args.warmup)):
             layer.step(tidx, x, tw, params, go, stream)
+        torch.cuda.synchronize()
+        run = lambda: layer.step(tidx, x, tw, params, go, stream)  # noqa: E731
+        if args.graph:  # the library records kernel launches only
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+                layer.step(tidx, x, tw, params, go, torch.cuda.current_stream())
+            torch.cuda.current_stream().wait_stream(side)
+            graph.replay()
+            run = graph.replay
         samples = []
         for _ in range(3):  # three rounds of ten steps, per-step median
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(10):
-                layer.step(tidx, x, tw, params, go, stream)
+                run()
             torch.cuda.synchronize()
             samples.append((time.perf_counter() - t0) * 1e3 / 10)
         ms = float(np.median(samples))
@@ -208,7 +219,10 @@ def token_sweep(torch, args):
                      "floor_ms": round(2.0 * active * per_expert / 8e12 * 1e3, 4)})
         print(f"[sweep] T={T} {rows[-1]}", file=sys.stderr, flush=True)
         del layer
+        if args.graph:
+            del graph
     print(json.dumps({"metric": "token sweep: F+B ms and base-weight read rate vs 8 TB/s",
+                      "graph": args.graph,
                       "unit": "ms", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
                       "config": {"workload": "H 4096, I 2048, 64 experts, top-6, rank 128, 20% of routes "
                                              "dropped, softmax routing; T per row"},
@@ -234,6 +248,8 @@ def main():
                     help="instead of the headline: time F+B over the token sweep (H 4096, I 2048, "
                          "64 experts, top-6, rank 128, 20%% of routes dropped) and report the "
                          "weight-read rate against HBM; prints one JSON line with a table")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --sweep: capture each step once in a HIP graph and time its replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
