@@ -295,18 +295,6 @@ struct KStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) fol
     return fetch_at(rs, ok ? (uint32_t)kk * ldb : OFF_NONE, co);
   }
 };
-struct KTwoMats {  // k in [0, 2r) -> rows of A (period r), [2r, 4r) -> rows of B (period r)
-  rsrc_t ra, rb;
-  uint32_t ldb;
-  int r;
-  __device__ __forceinline__ u32x4 fetch(int k, uint32_t co) const {
-    const bool ok = k >= 0 && k < 4 * r;
-    int kk = (k < 2 * r) ? k : k - 2 * r;
-    if (kk >= r) kk -= r;
-    const uint32_t ro = ok ? (uint32_t)kk * ldb : OFF_NONE;
-    return (k < 2 * r) ? fetch_at(ra, ro, co) : fetch_at(rb, ro, co);
-  }
-};
 struct KRows {  // k-th row of a contiguous range of pool rows or tokens
   // mode 0: row k of the range (rs based at the range's first row)
   // mode 1: pool row (row0 + k) -> its token's row (rs based at the tensor;
@@ -413,7 +401,6 @@ __device__ __forceinline__ void grouped_tile(int L, int nm, int nn, int gm, int&
   mt = g * gm + r % size;
   nt = r / size;
 }
-constexpr int GROUP_M = 8;
 
 // Workgroup b of a grid over (at most) maxtiles x nn tiles, of which the first
 // ntm M tiles are live: false for a dead workgroup; else the live tiles are

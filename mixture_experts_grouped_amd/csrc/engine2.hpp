@@ -464,34 +464,6 @@ struct TStrided {  // rows of a matrix: k in [lo, lo + span) -> row (k - lo) fol
     lds_load16(rs, lds, ok ? (uint32_t)kk * ldb + co : OFF_NONE);
   }
 };
-struct TRows {  // k-th row of a contiguous range of pool rows or tokens
-  // mode 0: row k of the range (rs based at the range's first row)
-  // mode 1: pool row (row0 + k) -> its token's row (map = row -> route)
-  // mode 2: token (row0 + k) -> pool row of its first live route
-  //         (map = route -> row); no live route reads zero
-  rsrc_t rs;
-  uint32_t ldb;
-  const int32_t* map;
-  int topk;
-  int row0, nrows, mode;
-  __device__ __forceinline__ void issue_lds(int k, uint32_t co, char* lds) const {
-    uint32_t ro = OFF_NONE;
-    if (k < nrows) {
-      long r = k;
-      if (mode == 1) {
-        r = map[row0 + k] / topk;
-      } else if (mode == 2) {
-        const long t = row0 + k;
-        long pr = -1;
-        for (int j = 0; j < topk && pr < 0; ++j) pr = map[t * topk + j];
-        r = pr;
-      }
-      if (r >= 0) ro = (uint32_t)r * ldb;
-    }
-    lds_load16(rs, lds, (ro != OFF_NONE && co != OFF_NONE) ? ro + co : OFF_NONE);
-  }
-};
-
 // ---------------------------------------------------------------------------
 // main loop: `L` provides issue(stage, sM, sN) and the compile-time count
 // INSTS of direct-load instructions one wave issues per stage.

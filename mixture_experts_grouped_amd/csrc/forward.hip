@@ -76,12 +76,6 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
 // a4: W13 grouped GEMM (+ B1/B3 via K-extension) + SwiGLU
 // N tile = 128 gate columns i0.. and the 128 up columns with the same i.
 // ----------------------------------------------------------------------------
-struct LdSq {
-  RowsK<256> m, n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
-};
-
 // N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i;
 // each wave holds a gate block and its up partner, so SwiGLU runs in registers.
 using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
