@@ -14,6 +14,8 @@ What the layer computes, as the pages state it:
   reproduces the plain MoE bit for bit.
 * PR #9, "Matched old/new performance": the "ordinary" MoE path also returns
   full W13/W2 weight gradients (optional here).
+* PR #17 Summary and PR #9 "Correctness coverage" list GeGLU next to SwiGLU
+  as the layer's gated activation.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   1. every adapted projection is W x + s * B (A x), s the adapter scale;
@@ -22,7 +24,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
   3. the router weights are used as given: out_t = sum_j w[t,j] * y_(t,j),
      and the router gradient is d out / d w[t,j] = <grad_out_t, y_(t,j)>;
   4. a route id of -1 is dropped: no contribution, router gradient 0;
-  5. gradients are returned, not accumulated.
+  5. gradients are returned, not accumulated;
+  6. GeGLU is h = gelu(g) * v with the same gate/up split and the exact GELU,
+     gelu(g) = g Phi(g), Phi the standard normal distribution function (the
+     pages do not define GELU further; the tanh form is an approximation of
+     this one).
 
 Arithmetic: float64 numpy on the exact values of the bf16 inputs; per-route
 evaluation, one loop over experts.  No blocking or regrouping of the shared
@@ -37,6 +43,7 @@ from __future__ import annotations
 from typing import Dict
 
 import numpy as np
+from scipy.special import erf
 
 PARAM_NAMES = ("W13", "W2", "A1", "A3", "B1", "B3", "A2", "B2")
 
@@ -56,6 +63,20 @@ def silu_grad(g: np.ndarray) -> np.ndarray:
     return sg * (1.0 + g * (1.0 - sg))
 
 
+def gelu(g: np.ndarray) -> np.ndarray:
+    """g * Phi(g), Phi(g) = (1 + erf(g / sqrt 2)) / 2."""
+    return g * 0.5 * (1.0 + erf(g / np.sqrt(2.0)))
+
+
+def gelu_grad(g: np.ndarray) -> np.ndarray:
+    """d gelu / d g = Phi(g) + g phi(g), phi the standard normal density."""
+    return 0.5 * (1.0 + erf(g / np.sqrt(2.0))) + g * np.exp(-0.5 * g * g) / np.sqrt(2.0 * np.pi)
+
+
+# gated activation: name -> (f, f'); h = f(g) * v
+ACTIVATIONS = {"swiglu": (silu, silu_grad), "geglu": (gelu, gelu_grad)}
+
+
 def _as64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
@@ -66,11 +87,12 @@ def _expert_routes(topk_idx: np.ndarray, e: int):
     return tt, jj
 
 
-def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float):
+def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float,
+                   act: str = "swiglu"):
     """One expert on a batch of its routes' inputs u [n, H].
 
-    g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);  h = silu(g) v;
-    y = W2_e h + s B2 (A2_e h).
+    g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);  h = f(g) v
+    (f = silu for SwiGLU, gelu for GeGLU);  y = W2_e h + s B2 (A2_e h).
     """
     I = p["W13"].shape[1] // 2
     W1 = p["W13"][e, :I]
@@ -79,14 +101,14 @@ def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float
     a3u = u @ p["A3"].T
     g = u @ W1.T + scale * (a1u @ p["B1"][e].T)
     v = u @ W3.T + scale * (a3u @ p["B3"][e].T)
-    h = silu(g) * v
+    h = ACTIVATIONS[act][0](g) * v
     a2h = h @ p["A2"][e].T
     y = h @ p["W2"][e].T + scale * (a2h @ p["B2"].T)
     return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "h": h, "a2h": a2h, "y": y}
 
 
 def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-            keep: bool = False):
+            keep: bool = False, act: str = "swiglu"):
     """out [T, H] = sum over unmasked slots j of w[t, j] * y_(t, j).
 
     With ``keep`` also returns per-route values Y [T, k, H], G/V/Hh [T, k, I]
@@ -107,7 +129,7 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
         tt, jj = _expert_routes(idx, e)
         if len(tt) == 0:
             continue
-        f = expert_forward(x[tt], e, p, scale)
+        f = expert_forward(x[tt], e, p, scale, act)
         Y[tt, jj] = f["y"]
         if keep:
             G[tt, jj] = f["g"]
@@ -122,14 +144,14 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
 
 
 def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-             base_grads: bool = False) -> Dict[str, np.ndarray]:
+             base_grads: bool = False, act: str = "swiglu") -> Dict[str, np.ndarray]:
     """Gradients of L = <grad_out, out> with respect to x, the router weights
     and the six adapter factors (and, with ``base_grads``, W13 and W2).
 
     Per route (t, j) to expert e with u = x_t, dy = w[t,j] grad_out_t:
       grad_w[t,j] = <grad_out_t, y>
       dh = W2_e^T dy + s A2_e^T (B2^T dy)
-      dg = dh * v * silu'(g);   dv = dh * silu(g)
+      dg = dh * v * f'(g);   dv = dh * f(g)     (f = silu or gelu)
       du = W1_e^T dg + W3_e^T dv + s A1^T (B1_e^T dg) + s A3^T (B3_e^T dv)
       grad_x_t += du
       dB1_e += s dg (A1 u)^T      dB3_e += s dv (A3 u)^T
@@ -163,15 +185,16 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         if len(tt) == 0:
             continue
         u = x[tt]
-        f = expert_forward(u, e, p, s)
+        f = expert_forward(u, e, p, s, act)
+        fa, fa_grad = ACTIVATIONS[act]
         gw[tt, jj] = np.sum(go[tt] * f["y"], axis=1)
         dy = w[tt, jj][:, None] * go[tt]
         W1 = p["W13"][e, :I]
         W3 = p["W13"][e, I:]
         b2dy = dy @ p["B2"]                       # B2^T dy      [n, r]
         dh = dy @ p["W2"][e] + s * (b2dy @ p["A2"][e])
-        dg = dh * f["v"] * silu_grad(f["g"])
-        dv = dh * silu(f["g"])
+        dg = dh * f["v"] * fa_grad(f["g"])
+        dv = dh * fa(f["g"])
         b1dg = dg @ p["B1"][e]                    # B1_e^T dg    [n, r]
         b3dv = dv @ p["B3"][e]                    # B3_e^T dv    [n, r]
         du = dg @ W1 + dv @ W3 + s * (b1dg @ p["A1"]) + s * (b3dv @ p["A3"])
@@ -202,9 +225,9 @@ def params_f64(arrs: Dict[str, np.ndarray], widen=None) -> Dict[str, np.ndarray]
 
 
 def forward_backward(x, topk_idx, topk_w, params, scale, grad_out,
-                     base_grads: bool = False, keep: bool = False):
-    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep)
-    bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads)
+                     base_grads: bool = False, keep: bool = False, act: str = "swiglu"):
+    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act)
+    bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads, act=act)
     if keep:
         out, inter = fwd
         return out, bwd, inter

@@ -17,6 +17,11 @@ formulas with the oracle's own code:
   float64 for every input and parameter.
 * ``pin_merged``: the side-LoRA layer equals a plain MoE whose weights absorb
   the low-rank deltas (W' = W + s B A with the sharing contract).
+
+The torch and finite-difference pins run for both gated activations (SwiGLU
+and GeGLU, torch's exact ``F.gelu``); ``pin_closed_form_geglu`` works the
+scalar layer with GeGLU from the normal distribution's tabulated values
+Phi(1) and phi(1).
 """
 from __future__ import annotations
 
@@ -131,12 +136,12 @@ def _torch_params(p, requires_grad=True):
     return {n: torch.tensor(p[n], dtype=torch.float64, requires_grad=requires_grad) for n in NAMES}
 
 
-def _torch_expert(u, e, tp, s):
+def _torch_expert(u, e, tp, s, act="swiglu"):
     I = tp["W13"].shape[1] // 2
     W1, W3 = tp["W13"][e, :I], tp["W13"][e, I:]
     g = F.linear(u, W1) + s * F.linear(F.linear(u, tp["A1"]), tp["B1"][e])
     v = F.linear(u, W3) + s * F.linear(F.linear(u, tp["A3"]), tp["B3"][e])
-    h = F.silu(g) * v
+    h = (F.silu(g) if act == "swiglu" else F.gelu(g, approximate="none")) * v
     return F.linear(h, tp["W2"][e]) + s * F.linear(F.linear(h, tp["A2"][e]), tp["B2"])
 
 
@@ -146,8 +151,8 @@ def _rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def pin_textbook(m=M, seed=1) -> float:
-    """E = 1, k = 1, w = 1: a dense SwiGLU MLP with LoRA on all three
+def pin_textbook(m=M, seed=1, act="swiglu") -> float:
+    """E = 1, k = 1, w = 1: a dense gated MLP with LoRA on all three
     projections (torch library ops, autograd)."""
     x, _, _, p, go = micro_case(seed, E=1, k=1, mask=False)
     T = x.shape[0]
@@ -156,17 +161,17 @@ def pin_textbook(m=M, seed=1) -> float:
     s = 0.7
     tp = _torch_params(p)
     tx = torch.tensor(x, requires_grad=True)
-    ty = _torch_expert(tx, 0, tp, s)
+    ty = _torch_expert(tx, 0, tp, s, act)
     (ty * torch.tensor(go)).sum().backward()
-    out = m.forward(x, idx, w, p, s)
-    g = m.backward(go, x, idx, w, p, s)
+    out = m.forward(x, idx, w, p, s, act=act)
+    g = m.backward(go, x, idx, w, p, s, act=act)
     errs = [_rel(out, ty.detach().numpy()), _rel(g["grad_x"], tx.grad.numpy())]
     for n in ("A1", "A3", "B1", "B3", "A2", "B2"):
         errs.append(_rel(g["d" + n], tp[n].grad.numpy()))
     return max(errs)
 
 
-def pin_torch_moe_autograd(m=M, seed=2, base=True) -> float:
+def pin_torch_moe_autograd(m=M, seed=2, base=True, act="swiglu") -> float:
     """Route-by-route torch graph of the routed layer, differentiated by
     autograd: every gradient including the router weights and the optional
     base weights."""
@@ -183,12 +188,12 @@ def pin_torch_moe_autograd(m=M, seed=2, base=True) -> float:
             e = int(idx[t, j])
             if e < 0:
                 continue
-            acc = acc + tw[t, j] * _torch_expert(tx[t:t + 1], e, tp, s)[0]
+            acc = acc + tw[t, j] * _torch_expert(tx[t:t + 1], e, tp, s, act)[0]
         rows.append(acc)
     tout = torch.stack(rows)
     (tout * torch.tensor(go)).sum().backward()
-    out = m.forward(x, idx, w, p, s)
-    g = m.backward(go, x, idx, w, p, s, base_grads=base)
+    out = m.forward(x, idx, w, p, s, act=act)
+    g = m.backward(go, x, idx, w, p, s, base_grads=base, act=act)
     errs = [_rel(out, tout.detach().numpy()), _rel(g["grad_x"], tx.grad.numpy()),
             _rel(g["grad_w"], tw.grad.numpy())]
     for n in ("A1", "A3", "B1", "B3", "A2", "B2"):
@@ -199,16 +204,16 @@ def pin_torch_moe_autograd(m=M, seed=2, base=True) -> float:
     return max(errs)
 
 
-def pin_finite_difference(m=M, seed=3, h=1e-5) -> float:
+def pin_finite_difference(m=M, seed=3, h=1e-5, act="swiglu") -> float:
     """Central differences of L = <grad_out, out> for every element of x, w and
     all eight parameters; relative max error over each gradient tensor."""
     x, idx, w, p, go = micro_case(seed, T=4, H=5, I=3, E=3, k=2, r=2)
     s = 0.7
 
     def loss(x_, w_, p_):
-        return float(np.sum(go * m.forward(x_, idx, w_, p_, s)))
+        return float(np.sum(go * m.forward(x_, idx, w_, p_, s, act=act)))
 
-    g = m.backward(go, x, idx, w, p, s, base_grads=True)
+    g = m.backward(go, x, idx, w, p, s, base_grads=True, act=act)
     worst = 0.0
 
     def fd_of(arr_get, arr_set, shape):
@@ -241,6 +246,56 @@ def pin_finite_difference(m=M, seed=3, h=1e-5) -> float:
         scale = max(np.abs(num).max(), 1e-12)
         worst = max(worst, float(np.abs(num - ana).max() / scale))
     return worst
+
+
+def pin_closed_form_geglu(m=M) -> float:
+    """The scalar layer of ``pin_closed_form`` with GeGLU and expert 0's gate
+    moved to g = 1: H = I = r = 1, E = 2, T = 1, k = 2, x = 1, s = 1/2.
+
+    Standard normal values (tables): Phi(1) = 0.8413447460685429,
+    phi(1) = 0.24197072451914337; Phi(0) = 1/2, so gelu(0) = 0, gelu'(0) = 1/2.
+    expert 0: W1 = 3/4 (+ s B1 A1 = 1/4) -> g = 1, gelu = Phi(1),
+              gelu' = Phi(1) + phi(1); W3 = 1, A3 = 2, B3 = 1/2 -> v = 3/2;
+              h = (3/2) Phi(1); W2 = 2, A2 = 1, B2 = 4 -> y = 4 h = 6 Phi(1)
+    expert 1: W1 = -1/4 -> g = 0, h = 0, y = 0; W3 = 3 -> v = 7/2
+    w = (1/3, 2/3): out = 2 Phi(1); grad_out = 1: grad_w = (6 Phi(1), 0).
+    expert 0: dh = (1/3)(2 + 1/2 * 4) = 4/3; dg = 4/3 * 3/2 * gelu'(1) = 2 gelu'(1);
+              dv = 4/3 * Phi(1); du = 1 * dg + (1 + 1/2 * 1/2 * 2) dv = dg + (3/2) dv
+    expert 1: dh = (2/3)(1 + 2) = 2, dg = 2 * 7/2 * 1/2 = 7/2, dv = 0,
+              du = (-1/4 + 1/4) dg = 0
+    dB1_0 = s dg (A1 x) = dg / 2; dB1_1 = 7/4; dB3_0 = s dv (A3 x) = dv;
+    dA2_0 = s (B2^T dy) h = 1/2 * 4/3 * (3/2) Phi(1) = Phi(1);
+    dB2 = s dy (A2 h) = 1/2 * 1/3 * (3/2) Phi(1) = Phi(1) / 4.
+    """
+    Phi1, phi1 = 0.8413447460685429, 0.24197072451914337
+    p = {
+        "W13": np.array([[[0.75], [1.0]], [[-0.25], [3.0]]]),
+        "W2": np.array([[[2.0]], [[1.0]]]),
+        "A1": np.array([[1.0]]), "A3": np.array([[2.0]]),
+        "B1": np.array([[[0.5]], [[0.5]]]), "B3": np.array([[[0.5]], [[0.5]]]),
+        "A2": np.array([[[1.0]], [[1.0]]]), "B2": np.array([[4.0]]),
+    }
+    x = np.array([[1.0]])
+    idx = np.array([[0, 1]], dtype=np.int32)
+    w = np.array([[1.0 / 3.0, 2.0 / 3.0]])
+    go = np.array([[1.0]])
+    s = 0.5
+    out = m.forward(x, idx, w, p, s, act="geglu")
+    g = m.backward(go, x, idx, w, p, s, act="geglu")
+    dg0 = 2.0 * (Phi1 + phi1)
+    dv0 = 4.0 / 3.0 * Phi1
+    expect = {
+        "out": 2.0 * Phi1, "gw0": 6.0 * Phi1, "gw1": 0.0,
+        "gx": dg0 + 1.5 * dv0,
+        "dB1_0": dg0 / 2.0, "dB1_1": 1.75, "dB3_0": dv0,
+        "dA2_0": Phi1, "dB2": Phi1 / 4.0,
+    }
+    got = {
+        "out": out[0, 0], "gw0": g["grad_w"][0, 0], "gw1": g["grad_w"][0, 1],
+        "gx": g["grad_x"][0, 0], "dB1_0": g["dB1"][0, 0, 0], "dB1_1": g["dB1"][1, 0, 0],
+        "dB3_0": g["dB3"][0, 0, 0], "dA2_0": g["dA2"][0, 0, 0], "dB2": g["dB2"][0, 0],
+    }
+    return max(abs(got[n] - expect[n]) for n in expect)
 
 
 def pin_merged(m=M, seed=4) -> float:
@@ -281,6 +336,10 @@ ALL_PINS = {
     "torch_autograd": (pin_torch_moe_autograd, 1e-12),
     "finite_difference": (pin_finite_difference, 1e-6),
     "merged": (pin_merged, 1e-12),
+    "closed_form_geglu": (pin_closed_form_geglu, 1e-12),
+    "textbook_geglu": (lambda m: pin_textbook(m, act="geglu"), 1e-12),
+    "torch_autograd_geglu": (lambda m: pin_torch_moe_autograd(m, act="geglu"), 1e-12),
+    "finite_difference_geglu": (lambda m: pin_finite_difference(m, act="geglu"), 1e-6),
 }
 
 

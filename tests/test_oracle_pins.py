@@ -99,7 +99,11 @@ MUTANTS = {
     "router_grad_sign": [("gw[tt, jj] = np.sum(go[tt] * f[\"y\"], axis=1)",
                           "gw[tt, jj] = -np.sum(go[tt] * f[\"y\"], axis=1)")],
     "dh_missing_lora": [("dh = dy @ p[\"W2\"][e] + s * (b2dy @ p[\"A2\"][e])", "dh = dy @ p[\"W2\"][e]")],
-    "dv_uses_gate_grad": [("dv = dh * silu(f[\"g\"])", "dv = dh * silu_grad(f[\"g\"])")],
+    "dv_uses_gate_grad": [("dv = dh * fa(f[\"g\"])", "dv = dh * fa_grad(f[\"g\"])")],
+    "gelu_tanh_approximation": [("return g * 0.5 * (1.0 + erf(g / np.sqrt(2.0)))",
+                                 "return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))")],
+    "gelu_grad_drops_density": [("+ g * np.exp(-0.5 * g * g) / np.sqrt(2.0 * np.pi)", "")],
+    "geglu_uses_silu": [("\"geglu\": (gelu, gelu_grad)", "\"geglu\": (silu, silu_grad)")],
     "du_drops_A3": [("+ s * (b3dv @ p[\"A3\"])", "")],
     "dB1_missing_scale": [("g[\"dB1\"][e] = s * (dg.T @ f[\"a1u\"])", "g[\"dB1\"][e] = (dg.T @ f[\"a1u\"])")],
     "dA1_uses_dv": [("g[\"dA1\"] += s * (b1dg.T @ u)", "g[\"dA1\"] += s * (b3dv.T @ u)")],
