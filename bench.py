@@ -241,6 +241,8 @@ def main():
     ap.add_argument("--base", choices=("bf16", "mxfp4"), default="bf16",
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
+    ap.add_argument("--activation", choices=("swiglu", "geglu"), default="swiglu",
+                    help="gated activation (GeGLU: exact GELU)")
     ap.add_argument("--base-grads", action="store_true",
                     help="also compute the frozen-weight gradients dW13, dW2 (the ordinary path; "
                          "not the headline workload)")
@@ -311,7 +313,8 @@ def main():
     tw = torch.from_numpy(w).to(dev)
 
     desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale,
-                       base_format=B.MOE_BASE_MXFP4 if mx else B.MOE_BASE_BF16)
+                       base_format=B.MOE_BASE_MXFP4 if mx else B.MOE_BASE_BF16,
+                       activation=B.MOE_ACT_GEGLU if args.activation == "geglu" else B.MOE_ACT_SWIGLU)
     layer = B.MoeLoraLayer(desc, device=dev, base_grads=args.base_grads)
     stream = torch.cuda.current_stream()
 
@@ -378,7 +381,7 @@ def main():
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
     cpu = None
-    if not args.no_cpu_baseline and not mx and not args.base_grads:
+    if not args.no_cpu_baseline and not mx and not args.base_grads and args.activation == "swiglu":
         cpu = cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, args.cpu_seconds)
         print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s",
               file=sys.stderr, flush=True)
@@ -401,9 +404,11 @@ def main():
             "workload": (("MXFP4 base (e2m1 + e8m0/32), " if mx else "") +
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
-                         f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, SwiGLU, s=1"),
+                         f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, "
+                         f"{'GeGLU' if args.activation == 'geglu' else 'SwiGLU'}, s=1"),
             "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
             "block_m": layer.block_m, "base": args.base, "base_grads": args.base_grads,
+            "activation": args.activation,
         },
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),

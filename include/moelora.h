@@ -48,7 +48,10 @@ typedef int32_t moe_status;
 #define MOE_ERR_WORKSPACE (-3)   /* saved/scratch buffer smaller than required */
 #define MOE_ERR_HIP (-4)         /* a HIP launch or attribute call failed */
 
-#define MOE_ACT_SWIGLU 0         /* h = silu(g) * v; other activations: UNSUPPORTED */
+#define MOE_ACT_SWIGLU 0         /* h = silu(g) * v, silu(g) = g sigmoid(g) */
+#define MOE_ACT_GEGLU 1          /* h = gelu(g) * v, gelu(g) = g Phi(g) (exact GELU,
+                                    Phi the standard normal distribution function);
+                                    other values: UNSUPPORTED */
 #define MOE_BASE_BF16 0          /* W13 / W2 in bf16 */
 #define MOE_BASE_MXFP4 1         /* W13 / W2 as e2m1 with e8m0 scales per 32 along K */
 
@@ -57,7 +60,9 @@ typedef int32_t moe_status;
  *   rank r of the side adapters, scale s of the adapter deltas (0 => plain MoE).
  *   block_m: pool padding granularity; 0 asks the library (see moe_lora_block_m),
  *     otherwise one of 16, 32, 64, 96, 128, 192, 240.
- *   activation: MOE_ACT_SWIGLU.  clamp: must be <= 0 or +inf (no clamp).
+ *   activation: MOE_ACT_SWIGLU or MOE_ACT_GEGLU (the gated activations the
+ *     pages list: PR #17 Summary; PR #9, "Correctness coverage").
+ *   clamp: must be <= 0 or +inf (no clamp; the pages do not define one).
  * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
  *   1 <= topk <= 16, 1 <= rank <= 128 with rank % 8 == 0, T*H*2 and 4*I*H
  *   below 2^31 bytes (one 32-bit buffer offset per token-row tensor and per

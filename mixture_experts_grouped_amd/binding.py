@@ -21,6 +21,7 @@ LIB_PATH = _build.OUT
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_ACT_SWIGLU = 0
+MOE_ACT_GEGLU = 1
 MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
 
 EXPORTS = (

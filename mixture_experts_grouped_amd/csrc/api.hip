@@ -19,6 +19,8 @@ constexpr size_t kAlign = 256;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+static_assert(MOE_ACT_SWIGLU == 0 && MOE_ACT_GEGLU == 1, "kernels take the activation as template 0 / 1");
+
 moe_status check_desc(const moe_lora_desc* d) {
   if (d == nullptr) return MOE_ERR_INVALID;
   if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->topk < 1 || d->rank < 1)
@@ -31,7 +33,7 @@ moe_status check_desc(const moe_lora_desc* d) {
   }
   if (d->H % 256 != 0 || d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->E > 512 || d->topk > 16 || d->rank > 128 || d->rank % 8 != 0) return MOE_ERR_UNSUPPORTED;
-  if (d->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
   if (!(d->clamp <= 0.0f || std::isinf(d->clamp))) return MOE_ERR_UNSUPPORTED;
   if (d->base_format != MOE_BASE_BF16 && d->base_format != MOE_BASE_MXFP4) return MOE_ERR_UNSUPPORTED;
   const int64_t routes = (int64_t)d->T * d->topk;
@@ -151,6 +153,7 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.W13 = (const uint16_t*)w->W13;
   a.W2 = (const uint16_t*)w->W2;
   a.mx = d->base_format == MOE_BASE_MXFP4;
+  a.act = d->activation;
   if (a.mx) {
     a.W13q = (const uint8_t*)w->W13;
     a.W2q = (const uint8_t*)w->W2;

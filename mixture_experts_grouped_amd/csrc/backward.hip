@@ -157,7 +157,8 @@ struct LdW2dMX : LdW2dBase<GW2D::NW> {
   }
 };
 
-template <bool MX>
+// ACT: 0 SwiGLU, 1 GeGLU (exact GELU): f'(g) = Phi(g) + g phi(g)
+template <bool MX, int ACT>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW2D;
@@ -248,11 +249,19 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float av = acc[nb][mb][4 * g + q];
-          const float sg = sigmoidf_(gg[q]);
-          const float u = av * gg[q] * sg;  // unweighted dv
-          dw[mb] += u * vv[q];
-          dv[q] = wr[mb] * u;
-          dg[q] = wr[mb] * av * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          if constexpr (ACT == 0) {
+            const float sg = sigmoidf_(gg[q]);
+            const float u = av * gg[q] * sg;  // unweighted dv
+            dw[mb] += u * vv[q];
+            dv[q] = wr[mb] * u;
+            dg[q] = wr[mb] * av * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          } else {
+            const float cdf = norm_cdf(gg[q]);
+            const float u = av * gg[q] * cdf;  // unweighted dv
+            dw[mb] += u * vv[q];
+            dv[q] = wr[mb] * u;
+            dg[q] = wr[mb] * av * vv[q] * (cdf + gg[q] * norm_pdf(gg[q]));
+          }
         }
         // keep the running sum in place: otherwise the compiler sinks the
         // whole dot product past the loop and holds its operands meanwhile
@@ -778,8 +787,10 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, GS64::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad<false>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<true>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 0>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<true, 0>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 1>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<true, 1>, W2D_LDS);
     set_lds((const void*)k_w13dgrad<false>, W13D_LDS);
     set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
     set_lds((const void*)k_p13, GS128::LDS_BYTES);
@@ -791,10 +802,17 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   }
   const int tm = (a.T + GS64::TM - 1) / GS64::TM;
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
-  if (a.mx)
-    MOE_LAUNCH(k_w2dgrad<true>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
-  else
-    MOE_LAUNCH(k_w2dgrad<false>, dim3(a.maxtiles * (a.I / GW2D::TN)), dim3(GW2D::NT), W2D_LDS, st, a);
+  {
+    const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
+    if (a.mx && a.act == 1)
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 1>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    else if (a.mx)
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 0>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    else if (a.act == 1)
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    else
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+  }
   const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
   if (a.mx)

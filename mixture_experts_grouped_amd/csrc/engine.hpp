@@ -62,6 +62,10 @@ __device__ __forceinline__ void split_hl(float v, uint32_t& hi, uint32_t& lo) {
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// standard normal distribution function and density (exact GELU = g Phi(g))
+__device__ __forceinline__ float norm_cdf(float g) { return 0.5f * (1.0f + erff(g * 0.70710678118654752f)); }
+__device__ __forceinline__ float norm_pdf(float g) { return 0.39894228040143268f * __expf(-0.5f * g * g); }
+
 // ---------------------------------------------------------------------------
 // tile geometry: WM x WN waves, each wave MB x NB blocks of 32 x 32
 // ---------------------------------------------------------------------------

@@ -122,7 +122,8 @@ struct LdW13MX : LdW13Base {
   }
 };
 
-template <bool MX>
+// ACT: 0 SwiGLU (h = silu(g) v), 1 GeGLU (h = gelu(g) v, exact GELU)
+template <bool MX, int ACT>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13;
@@ -190,7 +191,10 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
         for (int q = 0; q < 4; ++q) {
           gv[q] = acc[nb][mb][4 * g + q];
           vv[q] = acc[nb + NH][mb][4 * g + q];
-          hv[q] = gv[q] * sigmoidf_(gv[q]) * vv[q];
+          if constexpr (ACT == 0)
+            hv[q] = gv[q] * sigmoidf_(gv[q]) * vv[q];
+          else
+            hv[q] = gv[q] * norm_cdf(gv[q]) * vv[q];
         }
         *(f16x4*)(a.G + ob + 256 * g) = __builtin_convertvector(gv, f16x4);  // round to nearest even
         *(f16x4*)(a.V + ob + 256 * g) = __builtin_convertvector(vv, f16x4);
@@ -357,8 +361,10 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_lds((const void*)k_w13<false>, W13_LDS);
-    set_lds((const void*)k_w13<true>, W13_LDS);
+    set_lds((const void*)k_w13<false, 0>, W13_LDS);
+    set_lds((const void*)k_w13<true, 0>, W13_LDS);
+    set_lds((const void*)k_w13<false, 1>, W13_LDS);
+    set_lds((const void*)k_w13<true, 1>, W13_LDS);
     set_lds((const void*)k_a2, GS128::LDS_BYTES);
     set_lds((const void*)k_w2<false>, W2_LDS);
     set_lds((const void*)k_w2<true>, W2_LDS);
@@ -369,10 +375,17 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   const int tm = (a.T + GS64::TM - 1) / GS64::TM;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);
-  if (a.mx)
-    MOE_LAUNCH(k_w13<true>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
-  else
-    MOE_LAUNCH(k_w13<false>, dim3(a.maxtiles * (a.I / (GW13::TN / 2))), dim3(GW13::NT), W13_LDS, st, a);
+  {
+    const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
+    if (a.mx && a.act == 1)
+      MOE_LAUNCH_AS("k_w13", (k_w13<true, 1>), grid, dim3(GW13::NT), W13_LDS, st, a);
+    else if (a.mx)
+      MOE_LAUNCH_AS("k_w13", (k_w13<true, 0>), grid, dim3(GW13::NT), W13_LDS, st, a);
+    else if (a.act == 1)
+      MOE_LAUNCH_AS("k_w13", (k_w13<false, 1>), grid, dim3(GW13::NT), W13_LDS, st, a);
+    else
+      MOE_LAUNCH_AS("k_w13", (k_w13<false, 0>), grid, dim3(GW13::NT), W13_LDS, st, a);
+  }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)
     MOE_LAUNCH(k_w2<true>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);

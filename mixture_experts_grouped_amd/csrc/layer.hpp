@@ -43,6 +43,7 @@ struct LayerArgs {
   // MXFP4 base (mx != 0): packed e2m1 W13 [E, 2I, H/2], W2 [E, H, I/2] and
   // their e8m0 scales [E, 2I, H/32], [E, H, I/32]
   int mx;
+  int act;          // MOE_ACT_SWIGLU or MOE_ACT_GEGLU
   const uint8_t *W13q, *W13s, *W2q, *W2s;
   // saved by the forward
   TileInfo* tiles;   // [maxtiles]

@@ -51,14 +51,14 @@ def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX):
     return m
 
 
-def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False):
+def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False, act: str = "swiglu"):
     from oracle import moe_lora as OM
     x = f64(case["x"])
     go = f64(case["grad_out"])
     p = {n: f64(case[n]) for n in PARAMS}
-    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale)
+    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act)
     g = OM.backward(go, x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale,
-                    base_grads=base_grads)
+                    base_grads=base_grads, act=act)
     return out, g
 
 
@@ -68,7 +68,7 @@ class GpuRun:
 
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
                  scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None,
-                 base_grads: bool = False):
+                 base_grads: bool = False, activation: str = "swiglu"):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
         then case's W13/W2 are not uploaded.  base_grads: also request the
         frozen-weight gradients dW13, dW2."""
@@ -78,8 +78,9 @@ class GpuRun:
         self.B = B
         s = shape.scale if scale is None else scale
         fmt = B.MOE_BASE_MXFP4 if mx is not None else B.MOE_BASE_BF16
+        act = {"swiglu": B.MOE_ACT_SWIGLU, "geglu": B.MOE_ACT_GEGLU}[activation]
         self.desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank,
-                                scale=s, block_m=block_m, base_format=fmt)
+                                scale=s, block_m=block_m, base_format=fmt, activation=act)
         self.layer = B.MoeLoraLayer(self.desc, base_grads=base_grads)
         dev = "cuda"
 

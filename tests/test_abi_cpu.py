@@ -64,7 +64,7 @@ def test_workspace_sizes_grow_with_the_problem():
     ("block_m", 48, B.MOE_ERR_INVALID), ("H", 300, B.MOE_ERR_UNSUPPORTED),
     ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 12, B.MOE_ERR_UNSUPPORTED),
     ("rank", 256, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
-    ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 1, B.MOE_ERR_UNSUPPORTED),
+    ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 2, B.MOE_ERR_UNSUPPORTED),
     ("clamp", 10.0, B.MOE_ERR_UNSUPPORTED), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
     ("scale", float("nan"), B.MOE_ERR_INVALID),
 ])

@@ -110,3 +110,18 @@ def test_mxfp4_production_share_bitwise_vs_dequantised():
     Hn.assert_close("production:mx:out[sample]", Hn.f64(res_mx["out"][toks]), ref_out)
     Hn.assert_close("production:mx:grad_x[sample]", Hn.f64(res_mx["grad_x"][toks]), ref_g["grad_x"])
     Hn.assert_close("production:mx:grad_w[sample]", res_mx["grad_w"][toks], ref_g["grad_w"])
+
+
+def test_mxfp4_geglu_bitwise_vs_dequantised():
+    """GeGLU with an MXFP4 base: bitwise equal to the bf16 path on the
+    dequantised weights, and within the gates of the oracle on them."""
+    shape, key, routing, mask = CASES["r128_masked"]
+    case = I.layer_inputs(shape, key, routing=routing, mask_prob=mask)
+    mx, deq = Hn.mxfp4_base(case)
+    case_deq = dict(case, W13=deq["W13"], W2=deq["W2"])
+    res_mx = Hn.GpuRun(shape, case, mx=mx, activation="geglu").run()
+    res_bf = Hn.GpuRun(shape, case_deq, activation="geglu").run()
+    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(np.asarray(res_mx[k]).view(np.uint8), np.asarray(res_bf[k]).view(np.uint8)), k
+    ref_out, ref_g = Hn.oracle_run(case_deq, shape.scale, act="geglu")
+    Hn.compare_all(res_mx, ref_out, ref_g, tag="mx:geglu:")

@@ -82,6 +82,29 @@ def test_frozen_weight_grads_against_oracle(name):
         assert np.array_equal(plain[n], res[n]), n
 
 
+@pytest.mark.parametrize("name", ["tiny", "r128_masked", "multi_tile", "zipf_small"])
+def test_geglu_against_oracle(name):
+    """GeGLU (exact GELU) instead of SwiGLU: every output against the oracle
+    with the same activation, exact zeros for dropped routes and empty
+    experts."""
+    shape, key, routing, mask = CASES[name]
+    Hn.log(f"[parity] geglu case={name} shape={shape}")
+    case = _case(shape, key, routing, mask)
+    res = Hn.GpuRun(shape, case, activation="geglu").run()
+    _check_pool(res, case, shape, Hn.GpuRun(shape, case).layer.block_m)
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale, act="geglu")
+    Hn.compare_all(res, ref_out, ref_g, tag=name + ":geglu:")
+    assert (res["grad_w"][case["topk_idx"] < 0] == 0).all()
+    counts = np.bincount(case["topk_idx"][case["topk_idx"] >= 0], minlength=shape.E)
+    for e in np.nonzero(counts == 0)[0]:
+        for n in ("dB1", "dB3", "dA2"):
+            assert not np.any(res[n][e]), (n, e)
+    # the two activations differ (a kernel that ignored the option would pass
+    # only one of the two oracle comparisons)
+    sw = Hn.GpuRun(shape, case).run()
+    assert not np.array_equal(sw["out"], res["out"])
+
+
 def test_zero_scale_matches_base_and_zero_adapter_grads():
     shape = I.TINY
     case = _case(shape, (1,))
