@@ -11,11 +11,12 @@ namespace moelora {
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
 constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
 
-// Accumulator-blocked layout of a [tiles x 256, I] fp32 tensor that is written
-// and read only by kernels holding it in 32 x 32 MFMA accumulator blocks: block
-// (M tile mt, row block rb of 8, column block cb of I/32) is 1024 floats,
-// ordered [g (4)][lane (64)][q (4)] so that the lane's accumulator values
-// 4g .. 4g + 3 are one 16-byte access and a wave's access is 1 KB contiguous.
+// Accumulator-blocked layout of a [tiles x 256, I] tensor (fp16 here) that is
+// written and read only by kernels holding it in 32 x 32 MFMA accumulator
+// blocks: block (M tile mt, row block rb of 8, column block cb of I/32) is
+// 1024 elements, ordered [g (4)][lane (64)][q (4)] so that the lane's
+// accumulator values 4g .. 4g + 3 are one access (8 bytes in fp16) and a
+// wave's access is contiguous (512 bytes).
 __device__ __forceinline__ long acc_block(int mt, int rb, int cb, int I) {
   return ((long)(mt * 8 + rb) * (I / 32) + cb) * 1024;
 }
