@@ -38,6 +38,10 @@ CASES = {
     "single_token": (I.Shape(T=1, H=512, I=256, E=64, topk=6, rank=128), (12,), "softmax_topk", 0.2),
     # skewed routing with forced-empty experts and duplicate experts per token
     "zipf_small": (I.Shape(T=200, H=256, I=256, E=16, topk=6, rank=32), (13,), "zipf", 0.0),
+    # a single expert, top-1: every token in one group of two tiles
+    "one_expert": (I.Shape(T=300, H=256, I=256, E=1, topk=1, rank=16), (14,), "softmax_topk", 0.0),
+    # the largest top-k (16 routes per token over 32 experts), 20 % dropped
+    "topk16": (I.Shape(T=96, H=256, I=512, E=32, topk=16, rank=64), (15,), "softmax_topk", 0.2),
 }
 
 
