@@ -396,8 +396,8 @@ struct KLoadMX {
   static_assert(NT == 2 * R, "two threads per weight row");
   rsrc_t rq, rs;         // packed values, scales
   uint32_t qoff, soff;   // this thread's row: byte offsets at k = 0
-  u32x4 q;               // staged values of the queued stage
-  uint32_t e;            // staged scale
+  u32x4 q[2];            // staged values, two stages (buffer = stage parity)
+  uint32_t e[2];         // staged scales
   // weight row `row` (absolute) of a [*, K] MXFP4 matrix
   __device__ __forceinline__ void set(const uint8_t* q_base, const uint8_t* s_base, long nrows, long K,
                                       int row) {
@@ -406,16 +406,18 @@ struct KLoadMX {
     qoff = (uint32_t)(row * (K / 2)) + 16u * (threadIdx.x & 1);
     soff = (uint32_t)(row * (K / 32)) + (threadIdx.x & 1);
   }
+  template <int B = 0>
   __device__ __forceinline__ void issue(int k0) {
-    q = bload(rq, qoff + (uint32_t)(k0 / 2));
-    e = bload_u8(rs, soff + (uint32_t)(k0 / 32));
+    q[B] = bload(rq, qoff + (uint32_t)(k0 / 2));
+    e[B] = bload_u8(rs, soff + (uint32_t)(k0 / 32));
   }
-  // after the loads landed (vmcnt 0): expand into the K tile
+  // expand buffer B into the K tile (the compiler waits for exactly its loads)
+  template <int B = 0>
   __device__ __forceinline__ void finish(char* tile) const {
-    const float sc = e8m0_value(e);
+    const float sc = e8m0_value(e[B]);
     const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + koff<64>(row, 4 * h + c)) = fp4x8_bf16(q[c], sc);
+    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + koff<64>(row, 4 * h + c)) = fp4x8_bf16(q[B][c], sc);
   }
 };
 
@@ -428,8 +430,8 @@ struct TLoadMX {
   rsrc_t rq, rs;
   uint32_t qoff, soff;   // at stage k-row 0
   uint32_t qld, sld;     // bytes per k-row
-  u32x4 q;
-  uint32_t e;
+  u32x4 q[2];            // two stages (buffer = stage parity)
+  uint32_t e[2];
   // columns n0 .. n0 + 255 of a [nk, N] MXFP4 matrix
   __device__ __forceinline__ void set(const uint8_t* q_base, const uint8_t* s_base, long nk, long N, int n0) {
     rq = make_rsrc(q_base, (uint64_t)nk * (N / 2));
@@ -440,15 +442,17 @@ struct TLoadMX {
     qoff = kr * qld + (uint32_t)(n0 / 2) + 16u * cg;
     soff = kr * sld + (uint32_t)(n0 / 32) + cg;
   }
+  template <int B = 0>
   __device__ __forceinline__ void issue(int k0) {
-    q = bload(rq, qoff + (uint32_t)k0 * qld);
-    e = bload_u8(rs, soff + (uint32_t)k0 * sld);
+    q[B] = bload(rq, qoff + (uint32_t)k0 * qld);
+    e[B] = bload_u8(rs, soff + (uint32_t)k0 * sld);
   }
+  template <int B = 0>
   __device__ __forceinline__ void finish(char* tile) const {
-    const float sc = e8m0_value(e);
+    const float sc = e8m0_value(e[B]);
     const int kr = threadIdx.x >> 3, cg = threadIdx.x & 7;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + toff(kr, 4 * cg + c, 512)) = fp4x8_bf16(q[c], sc);
+    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + toff(kr, 4 * cg + c, 512)) = fp4x8_bf16(q[B][c], sc);
   }
 };
 
@@ -479,13 +483,23 @@ __device__ __forceinline__ void wait_vm() {
 // caller has already waited for the loads the next stage needs.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-// Loaders with register-staged operands also provide finish(stage, sN).
+// Loaders with register-staged operands either provide finish(stage, sN),
+// run one stage ahead by step2, or declare MXI and run two stages ahead by
+// step_mx.
 template <class T, class = void>
 struct HasFinish {
   static constexpr bool value = false;
 };
 template <class T>
 struct HasFinish<T, decltype((void)&T::finish)> {
+  static constexpr bool value = true;
+};
+template <class T, class = void>
+struct HasMX {
+  static constexpr bool value = false;
+};
+template <class T>
+struct HasMX<T, decltype((void)T::MXI)> {
   static constexpr bool value = true;
 };
 
@@ -517,6 +531,47 @@ __device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB
       wait_lgkm0();  // the next step's barrier publishes the expanded tile
     }
   }
+}
+
+// Loaders with MXI split a stage into
+// issue_dma(s, sM, sN) (its direct loads), issue_mx<B>(t) (the register loads
+// of stage t into buffer B = t & 1) and finish<B>(t, sN) (expand buffer B into
+// stage t's N tile); mx(t) tells whether stage t has such an operand.  The
+// register loads run two stages ahead of their expansion: step s queues the
+// direct loads of stage s + 1, then the register loads of stage s + 2, and
+// after its MFMAs expands stage s + 1 (loaded during step s - 1).  P = s & 1.
+template <class G, bool SPLIT, int P, class L>
+__device__ __forceinline__ void step_mx(L& ld, int s, int nst, f32x16 (&acc)[G::NB][G::MB],
+                                        char* smem, int wm, int wn, int lane) {
+  static_assert(G::NBUF == 2, "register-staged operands expand one stage ahead");
+  // stage s's direct loads were queued before the register loads of stage s + 1
+  if (s + 1 < nst && ld.mx(s + 1))
+    wait_vm<L::MXI>();
+  else
+    wait_vm<0>();
+  bar();
+  char* nxt = smem + ((s + 1) & 1) * G::STAGE;
+  if (s + 1 < nst) {
+    ld.issue_dma(s + 1, nxt, nxt + G::SM_BYTES);
+    if (s + 2 < nst && ld.mx(s + 2)) ld.template issue_mx<P>(s + 2);
+  }
+  const char* sM = smem + (s & 1) * G::STAGE;
+  mma_stage2<G, SPLIT>(sM, sM + G::SM_BYTES, acc, wm, wn, lane);
+  if (s + 1 < nst && ld.mx(s + 1)) {
+    ld.template finish<1 - P>(s + 1, nxt + G::SM_BYTES);
+    wait_lgkm0();  // the next step's barrier publishes the expanded tile
+  }
+}
+
+template <class G, bool SPLIT, class L>
+__device__ __forceinline__ void steps_mx(L& ld, int& s, int end, int nst, f32x16 (&acc)[G::NB][G::MB],
+                                         char* smem, int wm, int wn, int lane) {
+  if (s < end && (s & 1)) step_mx<G, SPLIT, 1>(ld, s++, nst, acc, smem, wm, wn, lane);
+  for (; s + 1 < end; s += 2) {
+    step_mx<G, SPLIT, 0>(ld, s, nst, acc, smem, wm, wn, lane);
+    step_mx<G, SPLIT, 1>(ld, s + 1, nst, acc, smem, wm, wn, lane);
+  }
+  if (s < end) step_mx<G, SPLIT, 0>(ld, s++, nst, acc, smem, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,20 +678,33 @@ __device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / G::WN, wn = w % G::WN;
   constexpr int NBUF = G::NBUF;
+  if constexpr (HasMX<L>::value) {
+    if (ld.mx(0)) ld.template issue_mx<0>(0);
+    ld.issue_dma(0, smem, smem + G::SM_BYTES);
+    if (nst > 1 && ld.mx(1)) ld.template issue_mx<1>(1);
+    if (ld.mx(0)) {
+      ld.template finish<0>(0, smem + G::SM_BYTES);
+      wait_lgkm0();
+    }
+    int s = 0;
+    if constexpr (SPLIT == 2) steps_mx<G, true>(ld, s, ld.nsplit < nst ? ld.nsplit : nst, nst, acc, smem, wm, wn, lane);
+    steps_mx<G, SPLIT == 1>(ld, s, nst, nst, acc, smem, wm, wn, lane);
+  } else {
 #pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nst) ld.issue(p, smem + p * G::STAGE, smem + p * G::STAGE + G::SM_BYTES);
-  if constexpr (HasFinish<L>::value) {
-    wait_vm<0>();
-    ld.finish(0, smem + G::SM_BYTES);
-    wait_lgkm0();
+    for (int p = 0; p < NBUF - 1; ++p)
+      if (p < nst) ld.issue(p, smem + p * G::STAGE, smem + p * G::STAGE + G::SM_BYTES);
+    if constexpr (HasFinish<L>::value) {
+      wait_vm<0>();
+      ld.finish(0, smem + G::SM_BYTES);
+      wait_lgkm0();
+    }
+    int s = 0;
+    if constexpr (SPLIT == 2) {
+      const int ns = ld.nsplit < nst ? ld.nsplit : nst;
+      for (; s < ns; ++s) step2<G, true>(ld, s, nst, acc, smem, wm, wn, lane);
+    }
+    for (; s < nst; ++s) step2<G, SPLIT == 1>(ld, s, nst, acc, smem, wm, wn, lane);
   }
-  int s = 0;
-  if constexpr (SPLIT == 2) {
-    const int ns = ld.nsplit < nst ? ld.nsplit : nst;
-    for (; s < ns; ++s) step2<G, true>(ld, s, nst, acc, smem, wm, wn, lane);
-  }
-  for (; s < nst; ++s) step2<G, SPLIT == 1>(ld, s, nst, acc, smem, wm, wn, lane);
   __syncthreads();
 }
 

@@ -83,7 +83,10 @@ constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, 
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
 // stage); stages [nsplit, ...): the base K = H.  With an MXFP4 base the W13
-// tile is register-staged and expanded to bf16 (finish).
+// tile is register-staged and expanded to bf16 (finish), its loads queued two
+// stages ahead (step_mx): one stage ahead leaves their latency exposed here
+// (4.0 vs 3.5 ms at T = 32768, H = 4096, I = 2048, E = 64, k = 8), while the
+// backward's MX kernels run 5-8% slower two ahead (register pressure).
 struct LdW13Base {
   using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
   using KL2 = v2::KLoad<256, GW13::KT, GW13::NW, true>;
@@ -107,19 +110,21 @@ struct LdW13 : LdW13Base {
   }
 };
 struct LdW13MX : LdW13Base {
+  static constexpr int MXI = 2;  // register loads per stage (values, scales)
   v2::KLoadMX<256, GW13::NT> nq;
-  __device__ void issue(int s, char* sM, char* sN) {
+  __device__ bool mx(int t) const { return t >= nsplit; }
+  __device__ void issue_dma(int s, char* sM, char* sN) {
     if (s < nsplit) {
       me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
       ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
     } else {
       mm.issue((s - nsplit) * GW13::KT, sM);
-      nq.issue((s - nsplit) * GW13::KT);
     }
   }
-  __device__ void finish(int s, char* sN) const {
-    if (s >= nsplit) nq.finish(sN);
-  }
+  template <int B>
+  __device__ void issue_mx(int t) { nq.template issue<B>((t - nsplit) * GW13::KT); }
+  template <int B>
+  __device__ void finish(int, char* sN) const { nq.template finish<B>(sN); }
 };
 
 // ACT: 0 SwiGLU (h = silu(g) v), 1 GeGLU (h = gelu(g) v, exact GELU)
