@@ -85,7 +85,7 @@ constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, 
 // stage); stages [nsplit, ...): the base K = H.  With an MXFP4 base the W13
 // tile is register-staged and expanded to bf16 (finish), its loads queued two
 // stages ahead (step_mx): one stage ahead leaves their latency exposed here
-// (4.0 vs 3.5 ms at T = 32768, H = 4096, I = 2048, E = 64, k = 8), while the
+// (4.0 vs 3.5 ms at T = 16384, H = 4096, I = 2048, E = 64, k = 6), while the
 // backward's MX kernels run 5-8% slower two ahead (register pressure).
 struct LdW13Base {
   using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
