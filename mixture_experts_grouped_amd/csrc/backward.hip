@@ -221,11 +221,16 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   Epi<G> ep;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform block offsets
   const int wm = wv / G::WN, wn = wv % G::WN, lane = threadIdx.x & 63;
+  // router weights of the lane's rows; the row index is clamped to the
+  // tile's last real row (nrows >= 1) so that all loads issue together
+  int rr[G::MB];
   float wr[G::MB];
 #pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) rr[mb] = a.row2r[ti.row0 + min(ep.row(mb), nrows - 1)];
+#pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
-    const int lr = ep.row(mb);
-    wr[mb] = lr < nrows ? a.w[a.row2r[ti.row0 + lr]] : 0.0f;
+    const float wt = a.w[rr[mb]];
+    wr[mb] = ep.row(mb) < nrows ? wt : 0.0f;
   }
   char* img_g = smem;
   char* img_v = smem + Img::BYTES;
@@ -238,13 +243,25 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   for (int mb = 0; mb < G::MB; ++mb) dw[mb] = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < G::NB; ++nb) {
+    // all of this half's G and V loads first: one memory round trip per half
+    // (the asm statement below orders memory operations, so loads issued
+    // inside the loop would each wait for the previous step)
+    f16x4 gq[G::MB][4], vq[G::MB][4];
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
       const long ob = acc_block(mt, G::m_local(wm, mb) / 32, (i0 + G::n_local(wn, nb)) / 32, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 gg = __builtin_convertvector(*(const f16x4*)(a.G + ob + 256 * g), f32x4);
-        const f32x4 vv = __builtin_convertvector(*(const f16x4*)(a.V + ob + 256 * g), f32x4);
+        gq[mb][g] = *(const f16x4*)(a.G + ob + 256 * g);
+        vq[mb][g] = *(const f16x4*)(a.V + ob + 256 * g);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 gg = __builtin_convertvector(gq[mb][g], f32x4);
+        const f32x4 vv = __builtin_convertvector(vq[mb][g], f32x4);
         f32x4 dg, dv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
