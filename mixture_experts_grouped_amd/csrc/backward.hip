@@ -267,11 +267,13 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
         for (int q = 0; q < 4; ++q) {
           const float av = acc[nb][mb][4 * g + q];
           if constexpr (ACT == 0) {
+            // silu'(g) = sg (1 + g (1 - sg)), so av silu'(g) = t + u - u sg
             const float sg = sigmoidf_(gg[q]);
-            const float u = av * gg[q] * sg;  // unweighted dv
+            const float t = av * sg;
+            const float u = t * gg[q];  // unweighted dv = av silu(g)
             dw[mb] += u * vv[q];
             dv[q] = wr[mb] * u;
-            dg[q] = wr[mb] * av * vv[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+            dg[q] = wr[mb] * vv[q] * (t + fmaf(-u, sg, u));
           } else {
             const float cdf = norm_cdf(gg[q]);
             const float u = av * gg[q] * cdf;  // unweighted dv

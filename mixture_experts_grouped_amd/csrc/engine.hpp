@@ -60,7 +60,9 @@ __device__ __forceinline__ void split_hl(float v, uint32_t& hi, uint32_t& lo) {
   lo = f2bf(v - bf2f(hi));
 }
 
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// logistic sigmoid; the reciprocal is v_rcp_f32 (1 ulp) rather than an IEEE
+// division (about ten instructions), which dominated the activation epilogues
+__device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // standard normal distribution function and density (exact GELU = g Phi(g))
 __device__ __forceinline__ float norm_cdf(float g) { return 0.5f * (1.0f + erff(g * 0.70710678118654752f)); }
