@@ -241,6 +241,10 @@ def main():
     ap.add_argument("--base", choices=("bf16", "mxfp4"), default="bf16",
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
+    ap.add_argument("--base-layout", choices=("plain", "transformed"), default="plain",
+                    help="transformed: also hold the frozen bf16 base as W13^T / W2^T per expert "
+                         "(written once by moe_lora_transform_base before the timed steps), so "
+                         "the backward's data-gradient GEMMs read it in contraction order")
     ap.add_argument("--activation", choices=("swiglu", "geglu"), default="swiglu",
                     help="gated activation (GeGLU: exact GELU)")
     ap.add_argument("--base-grads", action="store_true",
@@ -317,6 +321,10 @@ def main():
                        activation=B.MOE_ACT_GEGLU if args.activation == "geglu" else B.MOE_ACT_SWIGLU)
     layer = B.MoeLoraLayer(desc, device=dev, base_grads=args.base_grads)
     stream = torch.cuda.current_stream()
+    transformed = args.base_layout == "transformed" and not mx
+    if transformed:  # once, outside the timed steps: the base weights are frozen
+        params.update(B.transform_base(desc, params, stream))
+        torch.cuda.synchronize()
 
     def step():
         layer.step(tidx, x, tw, params, go, stream)
@@ -408,6 +416,7 @@ def main():
                          f"{'GeGLU' if args.activation == 'geglu' else 'SwiGLU'}, s=1"),
             "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
             "block_m": layer.block_m, "base": args.base, "base_grads": args.base_grads,
+            "base_layout": "transformed" if transformed else "plain",
             "activation": args.activation,
         },
         "fwd_ms": round(fwd_ms, 3),

@@ -98,13 +98,24 @@ typedef struct moe_pool {
  *   W2  [E, H, I]
  *   A1, A3 [r, H]   shared;   B1, B3 [E, I, r] expert-local
  *   A2  [E, r, I]   expert-local;   B2 [H, r] shared
- *   W13_scale, W2_scale: e8m0 block scales for MOE_BASE_MXFP4, NULL for bf16. */
+ *   W13_scale, W2_scale: e8m0 block scales for MOE_BASE_MXFP4, NULL for bf16.
+ *   W13T [E, H, 2I], W2T [E, I, H]: optional transformed copies of the frozen
+ *     bf16 base (W13T[e] = W13[e]^T, W2T[e] = W2[e]^T), written once by
+ *     moe_lora_transform_base and reused by every backward (PR #9 Summary:
+ *     reusable transformed weights).  With them the two data-gradient GEMMs
+ *     read the weights in the order they contract them; without them (NULL)
+ *     the backward transposes W13 / W2 on the fly.  Results are bitwise the
+ *     same either way; the contents must match W13 / W2.  Each may be given
+ *     alone; 16-byte aligned; MOE_BASE_MXFP4 with either: UNSUPPORTED.
+ *     The forward ignores them. */
 typedef struct moe_lora_params {
   const void* W13;
   const void* W2;
   const uint8_t* W13_scale;
   const uint8_t* W2_scale;
   const void *A1, *A3, *B1, *B3, *A2, *B2;
+  const void* W13T;
+  const void* W2T;
 } moe_lora_params;
 
 /* Gradient outputs (device bf16, same layouts as the parameters).  The six
@@ -158,6 +169,14 @@ moe_status moe_lora_workspace_size(const moe_lora_desc* desc, size_t* saved_byte
 moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_t* counts,
                       int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
                       int64_t capacity, int32_t* device_error, void* stream);
+
+/* Write the transformed base weights of moe_lora_params (bf16 base only):
+ * W13T[e] = W13[e]^T ([E, H, 2I]) and W2T[e] = W2[e]^T ([E, I, H]) from
+ * params->W13 / params->W2.  Either output may be NULL (skipped); outputs are
+ * 16-byte aligned device buffers that overlap neither input nor each other.
+ * MOE_BASE_MXFP4: UNSUPPORTED.  Queued on `stream` like every call. */
+moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
+                                   void* W2T, void* stream);
 
 /* Forward of the layer.
  *   x [T, H] bf16, topk_w [T, k] fp32 router weights (used as given),

@@ -27,7 +27,7 @@ MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
     "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_backward",
-    "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
+    "moe_lora_transform_base", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
     "moe_lora_trace_entry", "moe_lora_trace_reset",
 )
 
@@ -56,7 +56,8 @@ class MoeLoraParams(ctypes.Structure):
     _fields_ = [("W13", ctypes.c_void_p), ("W2", ctypes.c_void_p),
                 ("W13_scale", ctypes.c_void_p), ("W2_scale", ctypes.c_void_p),
                 ("A1", ctypes.c_void_p), ("A3", ctypes.c_void_p), ("B1", ctypes.c_void_p),
-                ("B3", ctypes.c_void_p), ("A2", ctypes.c_void_p), ("B2", ctypes.c_void_p)]
+                ("B3", ctypes.c_void_p), ("A2", ctypes.c_void_p), ("B2", ctypes.c_void_p),
+                ("W13T", ctypes.c_void_p), ("W2T", ctypes.c_void_p)]
 
 
 class MoeLoraGrads(ctypes.Structure):
@@ -93,6 +94,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_backward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
+    lib.moe_lora_transform_base.argtypes = [P(MoeLoraDesc), P(MoeLoraParams), vp, vp, vp]
     lib.moe_lora_trace_enable.argtypes = [ctypes.c_int32]
     lib.moe_lora_trace_enable.restype = None
     lib.moe_lora_trace_collect.argtypes = []
@@ -103,7 +105,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_trace_reset.argtypes = []
     lib.moe_lora_trace_reset.restype = None
     for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
-               "build_pool", "moe_lora_forward", "moe_lora_backward"):
+               "build_pool", "moe_lora_forward", "moe_lora_backward", "moe_lora_transform_base"):
         getattr(lib, fn).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -192,7 +194,8 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraPara
     """bf16 base: W13, W2 bf16.  MXFP4 base (desc.base_format == MOE_BASE_MXFP4):
     W13 uint8 [E, 2I, H/2] and W2 uint8 [E, H, I/2] packed e2m1 (element 2i in
     the low nibble of byte i), W13_scale uint8 [E, 2I, H/32], W2_scale uint8
-    [E, H, I/32] e8m0."""
+    [E, H, I/32] e8m0.  Optional "W13T" [E, H, 2I] and "W2T" [E, I, H] bf16: the
+    transformed base (transform_base), read by the backward."""
     E, H, I, r = desc.E, desc.H, desc.I, desc.rank
     bf = torch.bfloat16
     shapes = {"A1": (r, H), "A3": (r, H), "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I),
@@ -208,8 +211,36 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraPara
         w13 = _ptr(p["W13"], bf, (E, 2 * I, H), "W13")
         w2 = _ptr(p["W2"], bf, (E, H, I), "W2")
         s13 = s2 = None
+    w13t = _ptr(p.get("W13T"), bf, (E, H, 2 * I), "W13T")
+    w2t = _ptr(p.get("W2T"), bf, (E, I, H), "W2T")
     return MoeLoraParams(w13, w2, s13, s2, ptrs["A1"], ptrs["A3"], ptrs["B1"], ptrs["B3"],
-                         ptrs["A2"], ptrs["B2"])
+                         ptrs["A2"], ptrs["B2"], w13t, w2t)
+
+
+def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
+                            W13T: Optional[torch.Tensor], W2T: Optional[torch.Tensor],
+                            stream=None) -> None:
+    """W13T[e] = W13[e]^T, W2T[e] = W2[e]^T (bf16 base; either may be None)."""
+    E, H, I = desc.E, desc.H, desc.I
+    bf = torch.bfloat16
+    base = {n: params[n] for n in ("W13", "W2", "A1", "A3", "B1", "B3", "A2", "B2")}
+    pp = _params_struct(base, desc)
+    st = library().moe_lora_transform_base(
+        ctypes.byref(desc), ctypes.byref(pp), _ptr(W13T, bf, (E, H, 2 * I), "W13T"),
+        _ptr(W2T, bf, (E, I, H), "W2T"), _stream(stream))
+    _check(st, "moe_lora_transform_base")
+
+
+def transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor], stream=None) -> Dict[str, torch.Tensor]:
+    """Allocate and fill the transformed base weights; merge the result into
+    the params dict given to moe_lora_backward.  Redo it whenever W13 / W2
+    change (they are frozen in the side-LoRA setting)."""
+    E, H, I = desc.E, desc.H, desc.I
+    dev = params["W13"].device
+    out = {"W13T": torch.empty(E, H, 2 * I, dtype=torch.bfloat16, device=dev),
+           "W2T": torch.empty(E, I, H, dtype=torch.bfloat16, device=dev)}
+    moe_lora_transform_base(desc, params, out["W13T"], out["W2T"], stream)
+    return out
 
 
 def moe_lora_forward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], x: torch.Tensor,

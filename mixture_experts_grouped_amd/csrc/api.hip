@@ -63,7 +63,7 @@ struct Plan {
   size_t saved, scratch;
   // byte offsets
   size_t o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
-  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp;
+  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -97,6 +97,7 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
   p.o_ZAp = take(cap * 4 * r * 2);
   p.o_dwp = take((size_t)(I / 256) * cap * 4);
+  p.o_A2T = take((size_t)d->E * I * r * 2);  // A2_e^T, with transformed base weights
   // forward-only tensors share space with backward-only ones: the base
   // outputs and Z2 are read only by the forward's combine
   p.o_Yb = p.o_dU;  // [cap, H] bf16, same size
@@ -129,6 +130,10 @@ moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
   // scales: present exactly for an MXFP4 base (byte arrays, no alignment needed)
   const bool mx = d->base_format == MOE_BASE_MXFP4;
   if (mx != (w->W13_scale != nullptr) || mx != (w->W2_scale != nullptr)) return MOE_ERR_INVALID;
+  // transformed base weights: optional, bf16 base only
+  if ((w->W13T != nullptr && !aligned16(w->W13T)) || (w->W2T != nullptr && !aligned16(w->W2T)))
+    return MOE_ERR_INVALID;
+  if (mx && (w->W13T != nullptr || w->W2T != nullptr)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -152,6 +157,8 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.row2r = pool->row_to_route;
   a.W13 = (const uint16_t*)w->W13;
   a.W2 = (const uint16_t*)w->W2;
+  a.W13T = (const uint16_t*)w->W13T;
+  a.W2T = (const uint16_t*)w->W2T;
   a.mx = d->base_format == MOE_BASE_MXFP4;
   a.act = d->activation;
   if (a.mx) {
@@ -195,6 +202,7 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.Z2 = (float*)(b + p.o_Z2);
   a.Yb = (uint16_t*)(b + p.o_Yb);
   a.dwp = (float*)(b + p.o_dwp);
+  a.A2T = (uint16_t*)(b + p.o_A2T);
 }
 
 }  // namespace
@@ -332,6 +340,32 @@ moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
   a.dW2 = (uint16_t*)grads->dW2;
   const hipError_t e = launch_backward(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params* params, void* W13T,
+                                   void* W2T, void* stream) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (params == nullptr) return MOE_ERR_INVALID;
+  if (d->base_format != MOE_BASE_BF16) return MOE_ERR_UNSUPPORTED;
+  const size_t b13 = (size_t)d->E * 2 * d->I * d->H * 2, b2 = (size_t)d->E * d->H * d->I * 2;
+  if (W13T != nullptr) {
+    if (!aligned16(W13T) || !aligned16(params->W13)) return MOE_ERR_INVALID;
+    if (overlap(rng(W13T, b13), rng(params->W13, b13))) return MOE_ERR_INVALID;
+  }
+  if (W2T != nullptr) {
+    if (!aligned16(W2T) || !aligned16(params->W2)) return MOE_ERR_INVALID;
+    if (overlap(rng(W2T, b2), rng(params->W2, b2))) return MOE_ERR_INVALID;
+  }
+  if (W13T != nullptr && W2T != nullptr && overlap(rng(W13T, b13), rng(W2T, b2))) return MOE_ERR_INVALID;
+  const hipStream_t s = (hipStream_t)stream;
+  if (W13T != nullptr &&
+      launch_transpose((const uint16_t*)params->W13, (uint16_t*)W13T, d->E, 2 * d->I, d->H, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (W2T != nullptr &&
+      launch_transpose((const uint16_t*)params->W2, (uint16_t*)W2T, d->E, d->H, d->I, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -157,11 +157,42 @@ struct LdW2dMX : LdW2dBase<GW2D::NW> {
   }
 };
 
-// ACT: 0 SwiGLU, 1 GeGLU (exact GELU): f'(g) = Phi(g) + g phi(g)
-template <bool MX, int ACT>
+// With the transformed base weights (W2T = W2_e^T per expert, [E, I, H]) both
+// operands are K tiles read with ds_read_b128 instead of transposing reads:
+// stages [0, next) contract s q with A2T = A2_e^T (rows i0.., K = r folded
+// twice for the hi and lo halves), then go with W2T rows i0.. (K = H); one
+// plain pipeline (the ping-pong form spills here).
+using GW2DK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
+static_assert(GW2DK::TM == GW2D::TM && GW2DK::TN == GW2D::TN && GW2DK::STAGE == GW2D::STAGE,
+              "same tile and stage as the transposing form");
+struct LdW2dK {
+  using KL = v2::KLoad<256, GW2DK::KT, GW2DK::NW>;
+  using KA = v2::KLoadA<256, GW2DK::KT, GW2DK::NW>;
+  using KS = v2::KLoadS<256, GW2DK::KT, GW2DK::NW>;
+  static_assert(KA::NJ == KL::NJ && KS::NJ == KL::NJ, "one instruction count per stage");
+  static constexpr int INSTS = 2 * KL::NJ;
+  KL me, ne;  // s q by token | A2T rows
+  KA mm;      // go by token
+  KS nm;      // W2T rows
+  int next;
+  __device__ void issue(int s, char* sM, char* sN) {
+    if (s < next) {
+      me.issue(s * GW2DK::KT, 0, false, sM);
+      ne.issue(s * GW2DK::KT, 0, false, sN);
+    } else {
+      mm.issue((s - next) * GW2DK::KT, sM);
+      nm.issue((s - next) * GW2DK::KT, sN);
+    }
+  }
+};
+
+// ACT: 0 SwiGLU, 1 GeGLU (exact GELU): f'(g) = Phi(g) + g phi(g).
+// TW: read the transformed weights (bf16 base only).
+template <bool MX, int ACT, bool TW>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
+  static_assert(!(MX && TW), "transformed weights are bf16");
   extern __shared__ __align__(16) char smem[];
-  using G = GW2D;
+  using G = typename std::conditional<TW, GW2DK, GW2D>::type;
   using LD = typename std::conditional<MX, LdW2dMX, LdW2d>::type;
   using KL = typename LD::KL;
   const int ntn = a.I / G::TN;
@@ -174,7 +205,21 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   const int next = (2 * r + G::KT - 1) / G::KT;
-  if constexpr (!MX && DGRAD_PINGPONG) {
+  if constexpr (TW) {
+    LdW2dK L;
+    L.next = next;
+    {
+      int tk[LdW2dK::KL::NJ];
+      LdW2dK::KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+      L.me.from_tokens(a.sq, a.T, 2 * r, tk);
+      L.mm.from_tokens(a.go, a.T, a.H, tk);
+    }
+    L.me.window(2 * r);
+    L.ne.contig(a.A2T + (long)ti.e * a.I * r, i0, G::TN, r);
+    L.ne.window(2 * r, r);  // k in [r, 2r) reads A2T column k - r again (lo half)
+    L.nm.contig(a.W2T + (long)ti.e * a.I * a.H, i0, G::TN, a.H);
+    v2::run_stages2<G, 0>(L, next + a.H / G::KT, acc, smem);
+  } else if constexpr (!MX && DGRAD_PINGPONG) {
     {
       LdW2dExt X;
       int tk[LdW2dExt::KL::NJ];
@@ -386,28 +431,55 @@ struct LdW13dMX {
   __device__ void finish(int, char* sN) const { nq.finish(sN); }
 };
 
-template <bool MX>
+// With the transformed base weights (W13T = W13_e^T per expert, [E, H, 2I])
+// the weight operand is a K tile: W13T rows h0.. (K = 2I contiguous).
+using GW13DK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
+static_assert(GW13DK::TM == GW13D::TM && GW13DK::TN == GW13D::TN && GW13DK::STAGE == GW13D::STAGE,
+              "same tile and stage as the transposing form");
+struct LdW13dK {
+  using KA = v2::KLoadS<256, GW13DK::KT, PPW>;
+  static constexpr int INSTS = 2 * KA::NJ;
+  KA m, n;  // dGV rows | W13T rows
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GW13DK::KT, sM);
+    n.issue(s * GW13DK::KT, sN);
+  }
+};
+
+// TW: read the transformed weights (bf16 base only)
+template <bool MX, bool TW>
 __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
+  static_assert(!(MX && TW), "transformed weights are bf16");
   extern __shared__ __align__(16) char smem[];
-  using G = GW13D;
+  using G = typename std::conditional<TW, GW13DK, GW13D>::type;
   const int ntn = a.H / G::TN;
   int mt, nt;
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
-  typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
-  L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
-  if constexpr (MX)
-    L.nq.set(a.W13q + (long)ti.e * 2 * a.I * (a.H / 2), a.W13s + (long)ti.e * 2 * a.I * (a.H / 32), 2 * a.I,
-             a.H, h0);
-  else
-    L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (!MX && DGRAD_PINGPONG)
-    v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
-  else
-    v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  if constexpr (TW) {
+    LdW13dK L;
+    L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
+    L.n.contig(a.W13T + (long)ti.e * a.H * 2 * a.I, h0, G::TN, 2 * a.I);
+    if constexpr (DGRAD_PINGPONG)
+      v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
+    else
+      v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  } else {
+    typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
+    L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
+    if constexpr (MX)
+      L.nq.set(a.W13q + (long)ti.e * 2 * a.I * (a.H / 2), a.W13s + (long)ti.e * 2 * a.I * (a.H / 32),
+               2 * a.I, a.H, h0);
+    else
+      L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
+    if constexpr (!MX && DGRAD_PINGPONG)
+      v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
+    else
+      v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  }
   using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll
@@ -798,6 +870,53 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_base(LayerArgs a, int which) 
 }
 
 // ----------------------------------------------------------------------------
+// [B, R, C] -> [B, C, R] (bf16 bits) through a 64 x 64 LDS tile: the
+// transformed base weights (PR #9 Summary: reusable transformed weights) and
+// A2T = A2_e^T for the transformed-weight W2 dgrad.  16-byte row accesses
+// where the row is whole, element accesses at ragged edges.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t* dst, int R, int C) {
+  __shared__ uint16_t t[64][72];  // padded rows: 144 bytes, keeps the 16-byte writes aligned
+  const long b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  src += b * (long)R * C;
+  dst += b * (long)R * C;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rr = threadIdx.x / 8 + 32 * p, cc = (threadIdx.x % 8) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    if (r < R && c + 8 <= C && C % 8 == 0) {
+      *(u32x4*)&t[rr][cc] = *(const u32x4*)(src + (long)r * C + c);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[rr][cc + q] = (r < R && c + q < C) ? src[(long)r * C + c + q] : 0;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cr = threadIdx.x / 8 + 32 * p, rc = (threadIdx.x % 8) * 8;
+    const int c = c0 + cr, r = r0 + rc;
+    if (c >= C) continue;
+    if (r + 8 <= R && R % 8 == 0) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = (uint32_t)t[rc + 2 * q][cr] | ((uint32_t)t[rc + 2 * q + 1][cr] << 16);
+      *(u32x4*)(dst + (long)c * R + r) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (r + q < R) dst[(long)c * R + r + q] = t[rc + q][cr];
+    }
+  }
+}
+
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st) {
+  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  MOE_LAUNCH(k_transpose, dim3((C + 63) / 64, (R + 63) / 64, B), dim3(256), 0, st, src, dst, R, C);
+  return hipGetLastError();
+}
+
 static void set_lds(const void* fn, int bytes) {
   hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
@@ -806,12 +925,15 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, GS64::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad<false, 0>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<true, 0>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<false, 1>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<true, 1>, W2D_LDS);
-    set_lds((const void*)k_w13dgrad<false>, W13D_LDS);
-    set_lds((const void*)k_w13dgrad<true>, W13D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 0, false>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<true, 0, false>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 1, false>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<true, 1, false>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 0, true>, W2D_LDS);
+    set_lds((const void*)k_w2dgrad<false, 1, true>, W2D_LDS);
+    set_lds((const void*)k_w13dgrad<false, false>, W13D_LDS);
+    set_lds((const void*)k_w13dgrad<true, false>, W13D_LDS);
+    set_lds((const void*)k_w13dgrad<false, true>, W13D_LDS);
     set_lds((const void*)k_p13, GS128::LDS_BYTES);
     set_lds((const void*)k_rank_dx, RK_LDS);
     set_lds((const void*)k_wgrad_local, WG_LDS);
@@ -823,21 +945,36 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
+    const bool tw = !a.mx && a.W2T != nullptr;
+    if (tw) {
+      // A2T = A2_e^T per expert ([E, I, r]), the K-tile rank operand
+      const hipError_t e = launch_transpose(a.A2, a.A2T, a.E, a.r, a.I, st);
+      if (e != hipSuccess) return e;
+    }
     if (a.mx && a.act == 1)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 1>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 1, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
     else if (a.mx)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 0>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 0, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    else if (tw && a.act == 1)
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1, true>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    else if (tw)
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0, true>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
     else if (a.act == 1)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
     else
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
   }
   const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
-  if (a.mx)
-    MOE_LAUNCH(k_w13dgrad<true>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
-  else
-    MOE_LAUNCH(k_w13dgrad<false>, dim3(a.maxtiles * (a.H / GW13D::TN)), dim3(GW13D::NT), W13D_LDS, st, a);
+  {
+    const dim3 grid(a.maxtiles * (a.H / GW13D::TN));
+    if (a.mx)
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<true, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+    else if (a.W13T != nullptr)
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, true>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+    else
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+  }
   MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
   const long npc = (long)a.T * 2 * a.r;
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);

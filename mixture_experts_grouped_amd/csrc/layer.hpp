@@ -46,6 +46,9 @@ struct LayerArgs {
   int mx;
   int act;          // MOE_ACT_SWIGLU or MOE_ACT_GEGLU
   const uint8_t *W13q, *W13s, *W2q, *W2s;
+  // transformed bf16 base weights (optional, nullptr = read W13 / W2
+  // transposed): W13T [E, H, 2I] = W13_e^T, W2T [E, I, H] = W2_e^T
+  const uint16_t *W13T, *W2T;
   // saved by the forward
   TileInfo* tiles;   // [maxtiles]
   int* ntiles;       // [1]
@@ -71,6 +74,7 @@ struct LayerArgs {
   uint16_t* ZAp;     // [cap, 4r] ZA gathered to pool rows (real rows only)
   float* Pt;         // [T, H]    per-token rank term of the combine / grad-x (scratch)
   float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
+  uint16_t* A2T;     // [E, I, r]  A2_e^T (backward scratch, with W2T only)
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;
@@ -82,6 +86,8 @@ hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, lon
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
                              int32_t* err, hipStream_t st);
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
+// [B, R, C] -> [B, C, R] bf16 bits
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st);
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
 
 }  // namespace moelora

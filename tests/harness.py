@@ -68,10 +68,11 @@ class GpuRun:
 
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
                  scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None,
-                 base_grads: bool = False, activation: str = "swiglu"):
+                 base_grads: bool = False, activation: str = "swiglu", transformed: bool = False):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
         then case's W13/W2 are not uploaded.  base_grads: also request the
-        frozen-weight gradients dW13, dW2."""
+        frozen-weight gradients dW13, dW2.  transformed: give the backward the
+        transformed base weights (W13T, W2T) written by moe_lora_transform_base."""
         import torch
         from mixture_experts_grouped_amd import binding as B
         self.torch = torch
@@ -95,6 +96,8 @@ class GpuRun:
         if mx is not None:
             for n in ("W13", "W13_scale", "W2", "W2_scale"):
                 self.params[n] = torch.from_numpy(np.ascontiguousarray(mx[n], dtype=np.uint8)).to(dev)
+        if transformed:
+            self.params.update(B.transform_base(self.desc, self.params))
 
     def run(self, fill=None):
         L = self.layer

@@ -179,3 +179,38 @@ def test_frozen_weight_grad_pointers_must_be_aligned():
         assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128,
                                      saved, fake * 64, fake * 200, byref(grads), fake * 256,
                                      scratch, None) == B.MOE_ERR_INVALID
+
+
+def test_transformed_base_checks_before_any_launch():
+    """The transformed base weights (W13T, W2T) are optional bf16 copies:
+    misaligned ones are rejected, an MXFP4 base refuses them, and
+    moe_lora_transform_base validates its outputs on the host (with both
+    outputs NULL it has nothing to do and returns ok without a launch)."""
+    lib = B.library()
+    byref = ctypes.byref
+    fake = 1 << 20
+    d = B.make_desc(64, 256, 256, 8, 2, 8)
+    saved, scratch = B.moe_lora_workspace_size(d)
+    cap = B.moe_lora_pool_capacity(d)
+    pool = B.MoePool(fake, fake, fake, fake, cap, 16)
+    grads = B.MoeLoraGrads(*([fake * 3] * 6), None, None)
+    for w13t, w2t in ((fake * 5 + 2, None), (None, fake * 6 + 4)):
+        prm = B.MoeLoraParams(fake, fake, None, None, *([fake] * 6), w13t, w2t)
+        assert lib.moe_lora_backward(byref(d), byref(pool), fake, fake, byref(prm), fake * 128,
+                                     saved, fake * 64, fake * 200, byref(grads), fake * 256,
+                                     scratch, None) == B.MOE_ERR_INVALID
+    dm = B.make_desc(64, 256, 256, 8, 2, 8, base_format=B.MOE_BASE_MXFP4)
+    savm, scrm = B.moe_lora_workspace_size(dm)
+    prm = B.MoeLoraParams(fake, fake, fake, fake, *([fake] * 6), fake * 5, None)
+    assert lib.moe_lora_backward(byref(dm), byref(pool), fake, fake, byref(prm), fake * 128,
+                                 savm, fake * 64, fake * 200, byref(grads), fake * 256,
+                                 scrm, None) == B.MOE_ERR_UNSUPPORTED
+    base = B.MoeLoraParams(fake * 2, fake * 3, None, None, *([fake] * 6))
+    assert lib.moe_lora_transform_base(byref(dm), byref(base), fake * 5, None, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_lora_transform_base(None, byref(base), fake * 5, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), None, fake * 5, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 5 + 8, None, None) == B.MOE_ERR_INVALID
+    # W13T overlapping W13 ([E, 2I, H] bf16 = 2 MiB here) or W2T overlapping W13T
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 2 + 4096, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, fake * 8 + 1024, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), None, None, None) == B.MOE_OK

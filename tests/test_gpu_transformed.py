@@ -1,0 +1,65 @@
+"""Transformed base weights (W13T = W13_e^T, W2T = W2_e^T per expert, the
+reusable transformed weights of DeepGEMM PR #9's Summary): GPU checks.
+
+- moe_lora_transform_base writes exactly the transposes (bit for bit);
+- the layer given them returns bit for bit what it returns without them:
+  the two data-gradient GEMMs then read the weights (and A2) as K tiles
+  instead of transposing them through LDS, with the same products summed in
+  the same order.  Cases span rank 8 and 128, masked routes, ragged M tiles,
+  one expert at top-1, top-16, GeGLU and the frozen-weight gradients.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_grouped_amd import inputs as I
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    Hn.ensure_built()
+
+
+def test_transform_base_writes_the_transposes():
+    import torch
+    from mixture_experts_grouped_amd import binding as B
+    E, H, Id = 3, 512, 256
+    d = B.make_desc(64, H, Id, E, 2, 8)
+    g = torch.Generator().manual_seed(5)
+    p = {"W13": torch.randn(E, 2 * Id, H, generator=g).to(torch.bfloat16).cuda(),
+         "W2": torch.randn(E, H, Id, generator=g).to(torch.bfloat16).cuda()}
+    for n, shp in (("A1", (8, H)), ("A3", (8, H)), ("B1", (E, Id, 8)), ("B3", (E, Id, 8)),
+                   ("A2", (E, 8, Id)), ("B2", (H, 8))):
+        p[n] = torch.zeros(shp, dtype=torch.bfloat16, device="cuda")
+    t = B.transform_base(d, p)
+    torch.cuda.synchronize()
+    for n, nt in (("W13", "W13T"), ("W2", "W2T")):
+        want = p[n].transpose(1, 2).contiguous().view(torch.int16).cpu().numpy()
+        got = t[nt].view(torch.int16).cpu().numpy()
+        assert np.array_equal(got, want), nt
+
+
+CASES = {
+    "tiny": (I.Shape(T=256, H=512, I=256, E=16, topk=2, rank=8), (31,), 0.0, {}),
+    "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (32,), 0.2, {}),
+    "one_expert": (I.Shape(T=300, H=256, I=256, E=1, topk=1, rank=16), (33,), 0.0, {}),
+    "topk16": (I.Shape(T=96, H=256, I=512, E=32, topk=16, rank=64), (34,), 0.2, {}),
+    "geglu": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (35,), 0.1, {"activation": "geglu"}),
+    "base_grads": (I.Shape(T=300, H=512, I=256, E=8, topk=2, rank=32), (36,), 0.1, {"base_grads": True}),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_transformed_base_is_bitwise_the_same(name):
+    shape, key, mask, kw = CASES[name]
+    Hn.log(f"[transformed] case={name} shape={shape}")
+    case = I.layer_inputs(shape, key, routing="softmax_topk", mask_prob=mask)
+    plain = Hn.GpuRun(shape, case, **kw).run()
+    tw = Hn.GpuRun(shape, case, transformed=True, **kw).run()
+    keys = [k for k in plain if k != "device_error"]
+    assert set(keys) <= set(tw)
+    for k in keys:
+        a, b = np.asarray(plain[k]), np.asarray(tw[k])
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{name}:{k} differs with the transformed base"
