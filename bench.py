@@ -178,6 +178,10 @@ def token_sweep(torch, args):
     del experts
     for nm, a in I.shared_weights(base, key).items():
         params[nm] = bf(a)
+    if args.base_layout == "transformed":  # once: the base weights are frozen
+        d0 = B.make_desc(1, base.H, base.I, base.E, base.topk, base.rank, base.scale)
+        params.update(B.transform_base(d0, params))
+        torch.cuda.synchronize()
     per_expert = 2 * base.I * base.H * 2 + base.H * base.I * 2  # W13 + W2 bytes
     rows = []
     for T in SWEEP_T:
@@ -222,7 +226,7 @@ def token_sweep(torch, args):
         if args.graph:
             del graph
     print(json.dumps({"metric": "token sweep: F+B ms and base-weight read rate vs 8 TB/s",
-                      "graph": args.graph,
+                      "graph": args.graph, "base_layout": args.base_layout,
                       "unit": "ms", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
                       "config": {"workload": "H 4096, I 2048, 64 experts, top-6, rank 128, 20% of routes "
                                              "dropped, softmax routing; T per row"},
@@ -241,10 +245,12 @@ def main():
     ap.add_argument("--base", choices=("bf16", "mxfp4"), default="bf16",
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
-    ap.add_argument("--base-layout", choices=("plain", "transformed"), default="plain",
-                    help="transformed: also hold the frozen bf16 base as W13^T / W2^T per expert "
-                         "(written once by moe_lora_transform_base before the timed steps), so "
-                         "the backward's data-gradient GEMMs read it in contraction order")
+    ap.add_argument("--base-layout", choices=("plain", "transformed"), default="transformed",
+                    help="transformed (default): also hold the frozen bf16 base as W13^T / W2^T "
+                         "per expert (the reusable transformed weights of the pages' backward), "
+                         "written once by moe_lora_transform_base before the timed steps, so the "
+                         "backward's data-gradient GEMMs read it in contraction order; plain: "
+                         "transpose through LDS on every backward (same bits)")
     ap.add_argument("--activation", choices=("swiglu", "geglu"), default="swiglu",
                     help="gated activation (GeGLU: exact GELU)")
     ap.add_argument("--base-grads", action="store_true",
@@ -410,6 +416,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (("MXFP4 base (e2m1 + e8m0/32), " if mx else "") +
+                         ("bf16 base also held transposed for the backward (written once), "
+                          if transformed else "") +
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
                          f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, "

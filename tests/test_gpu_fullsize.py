@@ -1,6 +1,7 @@
 """Parity at the full production share (16,384 tokens x top-6 over 64 experts,
 H 4096, I 2048, rank 128, uniform routing), in the launch configuration the
-benchmark times (library-chosen BLOCK_M).
+benchmark times (library-chosen BLOCK_M, the transformed base W13^T / W2^T
+given to the backward); the plain base layout must give the same bits.
 
 The oracle cannot run the whole layer in seconds, so it checks exactly
 computable samples:
@@ -47,9 +48,18 @@ def run():
     del experts
     case.update(shared)
     Hn.log(f"[fullsize] inputs ready, shape={SHAPE}")
-    res = Hn.GpuRun(SHAPE, case, base_grads=True).run()
+    res = Hn.GpuRun(SHAPE, case, base_grads=True, transformed=True).run()
     Hn.log("[fullsize] GPU step done")
     return case, res
+
+
+def test_plain_base_layout_gives_the_same_bits(run):
+    case, res = run
+    plain = Hn.GpuRun(SHAPE, case, base_grads=True).run()
+    for k in res:
+        if k == "device_error":
+            continue
+        assert np.array_equal(np.asarray(res[k]).view(np.uint8), np.asarray(plain[k]).view(np.uint8)), k
 
 
 def _sub_problem(case, tokens, only_expert=None):
