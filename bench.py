@@ -123,13 +123,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_lora_fb_98k_rows_hbm_traffic.
 
 def stored_traffic(kernel, args):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when it was measured on another build (its source hash differs) or
-    another base format."""
+    None when it was measured on another build (its source hash differs),
+    another base format or another base layout."""
     from mixture_experts_grouped_amd import build
     if args.base != "bf16" or not os.path.exists(TRAFFIC_FILE):
         return None
     doc = json.load(open(TRAFFIC_FILE))
     if doc.get("source_hash") != build.source_hash() or kernel not in doc.get("kernels", {}):
+        return None
+    if doc.get("base_layout", "plain") != args.base_layout:
         return None
     k = doc["kernels"][kernel]
     return int(k["fetch_bytes"] + k["write_bytes"])

@@ -130,6 +130,8 @@ def main() -> None:
                "note": "per-dispatch HBM bytes: counter KiB x 1024 x scale; scale = copied bytes / "
                        "counter reading of a plain 1 GiB device copy",
                "kernels": kern}
+        if bench:  # the counted runs use bench.py's defaults, as the bench line does
+            doc["base_layout"] = bench.get("config", {}).get("base_layout", "plain")
         with open(os.path.join(args.out, f"{args.name}_hbm_traffic.json"), "w") as f:
             json.dump(doc, f, indent=1, sort_keys=True)
         t = [f"# HBM traffic per dispatch: {args.workload or args.name}", "",

@@ -21,13 +21,16 @@ def _snapshot(run):
     return {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in run.fetch().items()}
 
 
+@pytest.mark.parametrize("transformed", [False, True], ids=["plain", "transformed"])
 @pytest.mark.parametrize("shape", [I.TINY, I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128)])
-def test_graph_replay_matches_eager(shape):
+def test_graph_replay_matches_eager(shape, transformed):
+    """transformed: the backward reads the transformed base (and transposes A2
+    inside the captured step)."""
     import torch
     case = I.layer_inputs(shape, (31,), mask_prob=0.2)
     other = I.layer_inputs(shape, (32,), mask_prob=0.2)
-    run = Hn.GpuRun(shape, case)
-    noise = Hn.GpuRun(shape, other)
+    run = Hn.GpuRun(shape, case, transformed=transformed)
+    noise = Hn.GpuRun(shape, other, transformed=transformed)
     L = run.layer
     eager = run.run()  # also the warm-up (kernel attributes are set on first use)
     eager_other = noise.run()

@@ -45,6 +45,8 @@ CASES = {
     "tiny": (I.Shape(T=256, H=512, I=256, E=16, topk=2, rank=8), (31,), 0.0, {}),
     "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (32,), 0.2, {}),
     "one_expert": (I.Shape(T=300, H=256, I=256, E=1, topk=1, rank=16), (33,), 0.0, {}),
+    "single_token": (I.Shape(T=1, H=512, I=256, E=64, topk=6, rank=128), (37,), 0.2, {}),
+    "multi_tile": (I.Shape(T=1100, H=256, I=256, E=4, topk=2, rank=16), (38,), 0.0, {}),
     "topk16": (I.Shape(T=96, H=256, I=512, E=32, topk=16, rank=64), (34,), 0.2, {}),
     "geglu": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (35,), 0.1, {"activation": "geglu"}),
     "base_grads": (I.Shape(T=300, H=512, I=256, E=8, topk=2, rank=32), (36,), 0.1, {"base_grads": True}),
