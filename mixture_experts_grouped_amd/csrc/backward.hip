@@ -320,11 +320,12 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
             dv[q] = wr[mb] * u;
             dg[q] = wr[mb] * vv[q] * (t + fmaf(-u, sg, u));
           } else {
-            const float cdf = norm_cdf(gg[q]);
+            float cdf, pdf;
+            norm_cdf_pdf(gg[q], cdf, pdf);
             const float u = av * gg[q] * cdf;  // unweighted dv
             dw[mb] += u * vv[q];
             dv[q] = wr[mb] * u;
-            dg[q] = wr[mb] * av * vv[q] * (cdf + gg[q] * norm_pdf(gg[q]));
+            dg[q] = wr[mb] * av * vv[q] * fmaf(gg[q], pdf, cdf);
           }
         }
         // keep the running sum in place: otherwise the compiler sinks the

@@ -64,9 +64,33 @@ __device__ __forceinline__ void split_hl(float v, uint32_t& hi, uint32_t& lo) {
 // division (about ten instructions), which dominated the activation epilogues
 __device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// standard normal distribution function and density (exact GELU = g Phi(g))
-__device__ __forceinline__ float norm_cdf(float g) { return 0.5f * (1.0f + erff(g * 0.70710678118654752f)); }
-__device__ __forceinline__ float norm_pdf(float g) { return 0.39894228040143268f * __expf(-0.5f * g * g); }
+// erfc(x) for x >= 0 given ex2 = exp(-x^2): Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (erf to within 1.5e-7 absolute):
+// erfc(x) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1/(1 + p x).
+__device__ __forceinline__ float erfc_as7126(float x, float ex2) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = 1.061405429f;
+  q = fmaf(q, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  return q * t * ex2;
+}
+// Phi(g) and phi(g) of the standard normal distribution (exact GELU = g Phi(g),
+// gelu' = Phi + g phi) with one exponential:
+// Phi(g) = erfc(-g / sqrt2) / 2, the tail taken directly (no 1 - erf
+// cancellation for g < 0); exp(-x^2) at x = |g| / sqrt2 is exp(-g^2 / 2).
+__device__ __forceinline__ void norm_cdf_pdf(float g, float& cdf, float& pdf) {
+  const float e2 = __expf(-0.5f * g * g);
+  const float half_tail = 0.5f * erfc_as7126(fabsf(g) * 0.70710678118654752f, e2);
+  cdf = g < 0.0f ? half_tail : 1.0f - half_tail;
+  pdf = 0.39894228040143268f * e2;
+}
+__device__ __forceinline__ float norm_cdf(float g) {
+  float c, p;
+  norm_cdf_pdf(g, c, p);
+  return c;
+}
 
 // ---------------------------------------------------------------------------
 // tile geometry: WM x WN waves, each wave MB x NB blocks of 32 x 32
