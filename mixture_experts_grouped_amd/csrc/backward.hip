@@ -5,12 +5,15 @@
 // weight gradients, no full-width side-delta scratch); padding never enters
 // the shared reductions.  Steps:
 //   k_q             q_t = B2^T go_t, once per token (B2 is shared)
+//   k_transpose     A2T = A2_e^T, when the caller passes the transformed base
+//                   (W13T, W2T: PR #9 Summary, reusable transformed weights)
 //   k_w2dgrad       dh = w (W2_e^T go_t + A2_e^T s q_t) (K-extended), then
 //                   the SwiGLU backward from the saved fp16 G, V; per column
 //                   tile, the partial router gradient <W2_e^T go + A2_e^T s q, h>
 //   k_dw            grad_w[t,j] = sum of those partials (= <go_t, y_tj>), and
 //                   s w q_t per route for dA2
 //   k_w13dgrad      dU = W1_e^T dg + W3_e^T dv
+//   (with the transformed base both dgrads read the weights as K tiles)
 //   k_p13           P = [B1_e^T dg ; B3_e^T dv]
 //   k_pc            pc_t = s sum_j P_(t,j)
 //   k_rank_dx, k_token_sum   grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
