@@ -28,7 +28,14 @@ Readings taken where the pages are silent (each also listed in the design doc):
   6. GeGLU is h = gelu(g) * v with the same gate/up split and the exact GELU,
      gelu(g) = g Phi(g), Phi the standard normal distribution function (the
      pages do not define GELU further; the tanh form is an approximation of
-     this one).
+     this one);
+  7. the activation clamp c (PR #9 "Correctness coverage" and the production
+     runs name one, clamp = 10, without defining it) limits both
+     pre-activations entering the gated activation to [-c, c]:
+     h = f(clip(g, -c, c)) * clip(v, -c, c); the derivative of clip is 1 for
+     |x| <= c and 0 outside.  c = inf (the default) is no clamp.  The reading
+     itself is parity unpinned against the pages (they define no clamp);
+     the pins below fix this oracle to it.
 
 Arithmetic: float64 numpy on the exact values of the bf16 inputs; per-route
 evaluation, one loop over experts.  No blocking or regrouping of the shared
@@ -88,11 +95,12 @@ def _expert_routes(topk_idx: np.ndarray, e: int):
 
 
 def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float,
-                   act: str = "swiglu"):
+                   act: str = "swiglu", clamp: float = np.inf):
     """One expert on a batch of its routes' inputs u [n, H].
 
-    g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);  h = f(g) v
-    (f = silu for SwiGLU, gelu for GeGLU);  y = W2_e h + s B2 (A2_e h).
+    g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);
+    h = f(clip(g, -c, c)) clip(v, -c, c) (f = silu for SwiGLU, gelu for
+    GeGLU; c = clamp);  y = W2_e h + s B2 (A2_e h).
     """
     I = p["W13"].shape[1] // 2
     W1 = p["W13"][e, :I]
@@ -101,14 +109,16 @@ def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float
     a3u = u @ p["A3"].T
     g = u @ W1.T + scale * (a1u @ p["B1"][e].T)
     v = u @ W3.T + scale * (a3u @ p["B3"][e].T)
-    h = ACTIVATIONS[act][0](g) * v
+    gc = np.clip(g, -clamp, clamp)
+    vc = np.clip(v, -clamp, clamp)
+    h = ACTIVATIONS[act][0](gc) * vc
     a2h = h @ p["A2"][e].T
     y = h @ p["W2"][e].T + scale * (a2h @ p["B2"].T)
-    return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "h": h, "a2h": a2h, "y": y}
+    return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "gc": gc, "vc": vc, "h": h, "a2h": a2h, "y": y}
 
 
 def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-            keep: bool = False, act: str = "swiglu"):
+            keep: bool = False, act: str = "swiglu", clamp: float = np.inf):
     """out [T, H] = sum over unmasked slots j of w[t, j] * y_(t, j).
 
     With ``keep`` also returns per-route values Y [T, k, H], G/V/Hh [T, k, I]
@@ -129,7 +139,7 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
         tt, jj = _expert_routes(idx, e)
         if len(tt) == 0:
             continue
-        f = expert_forward(x[tt], e, p, scale, act)
+        f = expert_forward(x[tt], e, p, scale, act, clamp)
         Y[tt, jj] = f["y"]
         if keep:
             G[tt, jj] = f["g"]
@@ -144,14 +154,15 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
 
 
 def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-             base_grads: bool = False, act: str = "swiglu") -> Dict[str, np.ndarray]:
+             base_grads: bool = False, act: str = "swiglu", clamp: float = np.inf) -> Dict[str, np.ndarray]:
     """Gradients of L = <grad_out, out> with respect to x, the router weights
     and the six adapter factors (and, with ``base_grads``, W13 and W2).
 
     Per route (t, j) to expert e with u = x_t, dy = w[t,j] grad_out_t:
       grad_w[t,j] = <grad_out_t, y>
       dh = W2_e^T dy + s A2_e^T (B2^T dy)
-      dg = dh * v * f'(g);   dv = dh * f(g)     (f = silu or gelu)
+      dg = dh * v' * f'(g') [|g| <= c];   dv = dh * f(g') [|v| <= c]
+      (f = silu or gelu; g' = clip(g, -c, c), v' = clip(v, -c, c))
       du = W1_e^T dg + W3_e^T dv + s A1^T (B1_e^T dg) + s A3^T (B3_e^T dv)
       grad_x_t += du
       dB1_e += s dg (A1 u)^T      dB3_e += s dv (A3 u)^T
@@ -185,7 +196,7 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         if len(tt) == 0:
             continue
         u = x[tt]
-        f = expert_forward(u, e, p, s, act)
+        f = expert_forward(u, e, p, s, act, clamp)
         fa, fa_grad = ACTIVATIONS[act]
         gw[tt, jj] = np.sum(go[tt] * f["y"], axis=1)
         dy = w[tt, jj][:, None] * go[tt]
@@ -193,8 +204,8 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         W3 = p["W13"][e, I:]
         b2dy = dy @ p["B2"]                       # B2^T dy      [n, r]
         dh = dy @ p["W2"][e] + s * (b2dy @ p["A2"][e])
-        dg = dh * f["v"] * fa_grad(f["g"])
-        dv = dh * fa(f["g"])
+        dg = dh * f["vc"] * fa_grad(f["gc"]) * (np.abs(f["g"]) <= clamp)
+        dv = dh * fa(f["gc"]) * (np.abs(f["v"]) <= clamp)
         b1dg = dg @ p["B1"][e]                    # B1_e^T dg    [n, r]
         b3dv = dv @ p["B3"][e]                    # B3_e^T dv    [n, r]
         du = dg @ W1 + dv @ W3 + s * (b1dg @ p["A1"]) + s * (b3dv @ p["A3"])
@@ -225,9 +236,11 @@ def params_f64(arrs: Dict[str, np.ndarray], widen=None) -> Dict[str, np.ndarray]
 
 
 def forward_backward(x, topk_idx, topk_w, params, scale, grad_out,
-                     base_grads: bool = False, keep: bool = False, act: str = "swiglu"):
-    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act)
-    bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads, act=act)
+                     base_grads: bool = False, keep: bool = False, act: str = "swiglu",
+                     clamp: float = np.inf):
+    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act, clamp=clamp)
+    bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads, act=act,
+                   clamp=clamp)
     if keep:
         out, inter = fwd
         return out, bwd, inter

@@ -21,7 +21,11 @@ formulas with the oracle's own code:
 The torch and finite-difference pins run for both gated activations (SwiGLU
 and GeGLU, torch's exact ``F.gelu``); ``pin_closed_form_geglu`` works the
 scalar layer with GeGLU from the normal distribution's tabulated values
-Phi(1) and phi(1).
+Phi(1) and phi(1).  With the activation clamp (the layer's reading: both
+pre-activations clipped to [-c, c] before the gated activation) the torch
+pins use ``torch.clamp`` and autograd, the finite differences run with a
+clamp that cuts about a third of the values, and ``pin_closed_form_clamp``
+works a scalar case with both pre-activations outside the clamp by hand.
 """
 from __future__ import annotations
 
@@ -136,11 +140,14 @@ def _torch_params(p, requires_grad=True):
     return {n: torch.tensor(p[n], dtype=torch.float64, requires_grad=requires_grad) for n in NAMES}
 
 
-def _torch_expert(u, e, tp, s, act="swiglu"):
+def _torch_expert(u, e, tp, s, act="swiglu", clamp=None):
     I = tp["W13"].shape[1] // 2
     W1, W3 = tp["W13"][e, :I], tp["W13"][e, I:]
     g = F.linear(u, W1) + s * F.linear(F.linear(u, tp["A1"]), tp["B1"][e])
     v = F.linear(u, W3) + s * F.linear(F.linear(u, tp["A3"]), tp["B3"][e])
+    if clamp is not None:
+        g = torch.clamp(g, -clamp, clamp)
+        v = torch.clamp(v, -clamp, clamp)
     h = (F.silu(g) if act == "swiglu" else F.gelu(g, approximate="none")) * v
     return F.linear(h, tp["W2"][e]) + s * F.linear(F.linear(h, tp["A2"][e]), tp["B2"])
 
@@ -171,7 +178,7 @@ def pin_textbook(m=M, seed=1, act="swiglu") -> float:
     return max(errs)
 
 
-def pin_torch_moe_autograd(m=M, seed=2, base=True, act="swiglu") -> float:
+def pin_torch_moe_autograd(m=M, seed=2, base=True, act="swiglu", clamp=None) -> float:
     """Route-by-route torch graph of the routed layer, differentiated by
     autograd: every gradient including the router weights and the optional
     base weights."""
@@ -188,12 +195,13 @@ def pin_torch_moe_autograd(m=M, seed=2, base=True, act="swiglu") -> float:
             e = int(idx[t, j])
             if e < 0:
                 continue
-            acc = acc + tw[t, j] * _torch_expert(tx[t:t + 1], e, tp, s, act)[0]
+            acc = acc + tw[t, j] * _torch_expert(tx[t:t + 1], e, tp, s, act, clamp)[0]
         rows.append(acc)
     tout = torch.stack(rows)
     (tout * torch.tensor(go)).sum().backward()
-    out = m.forward(x, idx, w, p, s, act=act)
-    g = m.backward(go, x, idx, w, p, s, base_grads=base, act=act)
+    kw = {"act": act} if clamp is None else {"act": act, "clamp": clamp}
+    out = m.forward(x, idx, w, p, s, **kw)
+    g = m.backward(go, x, idx, w, p, s, base_grads=base, **kw)
     errs = [_rel(out, tout.detach().numpy()), _rel(g["grad_x"], tx.grad.numpy()),
             _rel(g["grad_w"], tw.grad.numpy())]
     for n in ("A1", "A3", "B1", "B3", "A2", "B2"):
@@ -204,16 +212,17 @@ def pin_torch_moe_autograd(m=M, seed=2, base=True, act="swiglu") -> float:
     return max(errs)
 
 
-def pin_finite_difference(m=M, seed=3, h=1e-5, act="swiglu") -> float:
+def pin_finite_difference(m=M, seed=3, h=1e-5, act="swiglu", clamp=None) -> float:
     """Central differences of L = <grad_out, out> for every element of x, w and
     all eight parameters; relative max error over each gradient tensor."""
     x, idx, w, p, go = micro_case(seed, T=4, H=5, I=3, E=3, k=2, r=2)
     s = 0.7
+    kw = {"act": act} if clamp is None else {"act": act, "clamp": clamp}
 
     def loss(x_, w_, p_):
-        return float(np.sum(go * m.forward(x_, idx, w_, p_, s, act=act)))
+        return float(np.sum(go * m.forward(x_, idx, w_, p_, s, **kw)))
 
-    g = m.backward(go, x, idx, w, p, s, base_grads=True, act=act)
+    g = m.backward(go, x, idx, w, p, s, base_grads=True, **kw)
     worst = 0.0
 
     def fd_of(arr_get, arr_set, shape):
@@ -298,6 +307,39 @@ def pin_closed_form_geglu(m=M) -> float:
     return max(abs(got[n] - expect[n]) for n in expect)
 
 
+def pin_closed_form_clamp(m=M) -> float:
+    """Scalar layer (H = I = r = 1, E = 2, T = 1, k = 2, x = 1, s = 0) with the
+    clamp c = ln 3, so that a clipped gate sits at sigmoid(ln 3) = 3/4:
+    expert 0: W1 = 5 -> g = 5 > c, g' = ln3, silu(g') = (3/4) ln3;
+              W3 = -7 -> v = -7 < -c, v' = -ln3;  h = -(3/4) (ln3)^2;
+              W2 = 2 -> y0 = -(3/2) (ln3)^2; both clipped: dg = dv = 0.
+    expert 1: W1 = 0 -> g = 0 (inside), silu(0) = 0, silu'(0) = 1/2;
+              W3 = 1/2 -> v = 1/2 (inside); h = 0; W2 = 3 -> y1 = 0;
+              dh = w1 * 3 * go; dg = dh v silu'(0) = dh / 4; dv = dh silu(0) = 0.
+    w = (1, 1/2), go = 1: out = y0 + y1 / 2; grad_w = (y0, 0);
+    grad_x = W1_1 dg_1 + W3_1 dv_1 = 0 (W1_1 = 0);  dW13_1 gate row = dg_1 = 3/8,
+    dW13_0 rows = 0; dW2_0 = w0 go h0 = h0, dW2_1 = 0 (h1 = 0)."""
+    ln3 = math.log(3.0)
+    z = lambda *shape: np.zeros(shape)  # noqa: E731
+    p = {"W13": np.array([[[5.0], [-7.0]], [[0.0], [0.5]]]), "W2": np.array([[[2.0]], [[3.0]]]),
+         "A1": z(1, 1), "A3": z(1, 1), "B1": z(2, 1, 1), "B3": z(2, 1, 1), "A2": z(2, 1, 1),
+         "B2": z(1, 1)}
+    x = np.array([[1.0]])
+    idx = np.array([[0, 1]], dtype=np.int32)
+    w = np.array([[1.0, 0.5]])
+    go = np.array([[1.0]])
+    out = m.forward(x, idx, w, p, 0.0, clamp=ln3)
+    g = m.backward(go, x, idx, w, p, 0.0, base_grads=True, clamp=ln3)
+    h0 = -0.75 * ln3 * ln3
+    expect = {"out": 2.0 * h0, "gw0": 2.0 * h0, "gw1": 0.0, "gx": 0.0,
+              "dW13_0g": 0.0, "dW13_0v": 0.0, "dW13_1g": 3.0 / 8.0, "dW13_1v": 0.0,
+              "dW2_0": h0, "dW2_1": 0.0}
+    got = {"out": out[0, 0], "gw0": g["grad_w"][0, 0], "gw1": g["grad_w"][0, 1], "gx": g["grad_x"][0, 0],
+           "dW13_0g": g["dW13"][0, 0, 0], "dW13_0v": g["dW13"][0, 1, 0], "dW13_1g": g["dW13"][1, 0, 0],
+           "dW13_1v": g["dW13"][1, 1, 0], "dW2_0": g["dW2"][0, 0, 0], "dW2_1": g["dW2"][1, 0, 0]}
+    return max(abs(got[n] - expect[n]) for n in expect)
+
+
 def pin_merged(m=M, seed=4) -> float:
     """Forward of the side-LoRA layer == forward of the plain MoE with merged
     weights and zero adapters; the adapter gradients equal the chain rule
@@ -340,6 +382,10 @@ ALL_PINS = {
     "textbook_geglu": (lambda m: pin_textbook(m, act="geglu"), 1e-12),
     "torch_autograd_geglu": (lambda m: pin_torch_moe_autograd(m, act="geglu"), 1e-12),
     "finite_difference_geglu": (lambda m: pin_finite_difference(m, act="geglu"), 1e-6),
+    "closed_form_clamp": (pin_closed_form_clamp, 1e-12),
+    "torch_autograd_clamp": (lambda m: pin_torch_moe_autograd(m, clamp=0.6), 1e-12),
+    "torch_autograd_clamp_geglu": (lambda m: pin_torch_moe_autograd(m, act="geglu", clamp=0.6), 1e-12),
+    "finite_difference_clamp": (lambda m: pin_finite_difference(m, clamp=0.6), 1e-6),
 }
 
 

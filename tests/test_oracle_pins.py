@@ -99,7 +99,12 @@ MUTANTS = {
     "router_grad_sign": [("gw[tt, jj] = np.sum(go[tt] * f[\"y\"], axis=1)",
                           "gw[tt, jj] = -np.sum(go[tt] * f[\"y\"], axis=1)")],
     "dh_missing_lora": [("dh = dy @ p[\"W2\"][e] + s * (b2dy @ p[\"A2\"][e])", "dh = dy @ p[\"W2\"][e]")],
-    "dv_uses_gate_grad": [("dv = dh * fa(f[\"g\"])", "dv = dh * fa_grad(f[\"g\"])")],
+    "dv_uses_gate_grad": [("dv = dh * fa(f[\"gc\"])", "dv = dh * fa_grad(f[\"gc\"])")],
+    "clamp_gate_only": [("vc = np.clip(v, -clamp, clamp)", "vc = v")],
+    "clamp_one_sided": [("gc = np.clip(g, -clamp, clamp)", "gc = np.minimum(g, clamp)")],
+    "clamp_grad_not_masked": [("* (np.abs(f[\"g\"]) <= clamp)", "")],
+    "clamp_up_mask_from_gate": [("* (np.abs(f[\"v\"]) <= clamp)", "* (np.abs(f[\"g\"]) <= clamp)")],
+    "clamp_on_output": [("h = ACTIVATIONS[act][0](gc) * vc", "h = np.clip(ACTIVATIONS[act][0](g) * v, -clamp, clamp)")],
     "gelu_tanh_approximation": [("return g * 0.5 * (1.0 + erf(g / np.sqrt(2.0)))",
                                  "return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))")],
     "gelu_grad_drops_density": [("+ g * np.exp(-0.5 * g * g) / np.sqrt(2.0 * np.pi)", "")],
