@@ -35,7 +35,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
      h = f(clip(g, -c, c)) * clip(v, -c, c); the derivative of clip is 1 for
      |x| <= c and 0 outside.  c = inf (the default) is no clamp.  The reading
      itself is parity unpinned against the pages (they define no clamp);
-     the pins below fix this oracle to it.
+     the pins below fix this oracle to it.  Whether a value is clipped is an
+     integer decision taken in floating point: with clamp_decide="fp16" it
+     is taken on the value rounded to float16 (the precision in which the
+     kernels keep the pre-activations between forward and backward); the
+     clipped and unclipped values themselves stay exact.
 
 Arithmetic: float64 numpy on the exact values of the bf16 inputs; per-route
 evaluation, one loop over experts.  No blocking or regrouping of the shared
@@ -94,8 +98,21 @@ def _expert_routes(topk_idx: np.ndarray, e: int):
     return tt, jj
 
 
+def _clip(a: np.ndarray, c: float, decide):
+    """(clip(a, -c, c), mask of clipped values); the mask is decided on
+    decide(a) when given (see clamp_decide)."""
+    d = a if decide is None else decide(a)
+    out = np.abs(d) > c
+    res = a.copy()
+    res[out] = np.sign(a[out]) * c
+    return res, out
+
+
+_DECIDE = {None: None, "fp16": lambda a: a.astype(np.float16).astype(np.float64)}
+
+
 def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float,
-                   act: str = "swiglu", clamp: float = np.inf):
+                   act: str = "swiglu", clamp: float = np.inf, clamp_decide=None):
     """One expert on a batch of its routes' inputs u [n, H].
 
     g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);
@@ -109,16 +126,17 @@ def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float
     a3u = u @ p["A3"].T
     g = u @ W1.T + scale * (a1u @ p["B1"][e].T)
     v = u @ W3.T + scale * (a3u @ p["B3"][e].T)
-    gc = np.clip(g, -clamp, clamp)
-    vc = np.clip(v, -clamp, clamp)
+    gc, gout = _clip(g, clamp, _DECIDE[clamp_decide])
+    vc, vout = _clip(v, clamp, _DECIDE[clamp_decide])
     h = ACTIVATIONS[act][0](gc) * vc
     a2h = h @ p["A2"][e].T
     y = h @ p["W2"][e].T + scale * (a2h @ p["B2"].T)
-    return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "gc": gc, "vc": vc, "h": h, "a2h": a2h, "y": y}
+    return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "gc": gc, "vc": vc, "gout": gout, "vout": vout,
+            "h": h, "a2h": a2h, "y": y}
 
 
 def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-            keep: bool = False, act: str = "swiglu", clamp: float = np.inf):
+            keep: bool = False, act: str = "swiglu", clamp: float = np.inf, clamp_decide=None):
     """out [T, H] = sum over unmasked slots j of w[t, j] * y_(t, j).
 
     With ``keep`` also returns per-route values Y [T, k, H], G/V/Hh [T, k, I]
@@ -139,7 +157,7 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
         tt, jj = _expert_routes(idx, e)
         if len(tt) == 0:
             continue
-        f = expert_forward(x[tt], e, p, scale, act, clamp)
+        f = expert_forward(x[tt], e, p, scale, act, clamp, clamp_decide)
         Y[tt, jj] = f["y"]
         if keep:
             G[tt, jj] = f["g"]
@@ -154,7 +172,8 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
 
 
 def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-             base_grads: bool = False, act: str = "swiglu", clamp: float = np.inf) -> Dict[str, np.ndarray]:
+             base_grads: bool = False, act: str = "swiglu", clamp: float = np.inf,
+             clamp_decide=None) -> Dict[str, np.ndarray]:
     """Gradients of L = <grad_out, out> with respect to x, the router weights
     and the six adapter factors (and, with ``base_grads``, W13 and W2).
 
@@ -196,7 +215,7 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         if len(tt) == 0:
             continue
         u = x[tt]
-        f = expert_forward(u, e, p, s, act, clamp)
+        f = expert_forward(u, e, p, s, act, clamp, clamp_decide)
         fa, fa_grad = ACTIVATIONS[act]
         gw[tt, jj] = np.sum(go[tt] * f["y"], axis=1)
         dy = w[tt, jj][:, None] * go[tt]
@@ -204,8 +223,8 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         W3 = p["W13"][e, I:]
         b2dy = dy @ p["B2"]                       # B2^T dy      [n, r]
         dh = dy @ p["W2"][e] + s * (b2dy @ p["A2"][e])
-        dg = dh * f["vc"] * fa_grad(f["gc"]) * (np.abs(f["g"]) <= clamp)
-        dv = dh * fa(f["gc"]) * (np.abs(f["v"]) <= clamp)
+        dg = dh * f["vc"] * fa_grad(f["gc"]) * ~f["gout"]
+        dv = dh * fa(f["gc"]) * ~f["vout"]
         b1dg = dg @ p["B1"][e]                    # B1_e^T dg    [n, r]
         b3dv = dv @ p["B3"][e]                    # B3_e^T dv    [n, r]
         du = dg @ W1 + dv @ W3 + s * (b1dg @ p["A1"]) + s * (b3dv @ p["A3"])
@@ -237,10 +256,11 @@ def params_f64(arrs: Dict[str, np.ndarray], widen=None) -> Dict[str, np.ndarray]
 
 def forward_backward(x, topk_idx, topk_w, params, scale, grad_out,
                      base_grads: bool = False, keep: bool = False, act: str = "swiglu",
-                     clamp: float = np.inf):
-    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act, clamp=clamp)
+                     clamp: float = np.inf, clamp_decide=None):
+    fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act, clamp=clamp,
+                  clamp_decide=clamp_decide)
     bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads, act=act,
-                   clamp=clamp)
+                   clamp=clamp, clamp_decide=clamp_decide)
     if keep:
         out, inter = fwd
         return out, bwd, inter

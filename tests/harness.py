@@ -51,14 +51,15 @@ def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX):
     return m
 
 
-def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False, act: str = "swiglu"):
+def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False, act: str = "swiglu",
+               clamp: float = np.inf):
     from oracle import moe_lora as OM
     x = f64(case["x"])
     go = f64(case["grad_out"])
     p = {n: f64(case[n]) for n in PARAMS}
-    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act)
+    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act, clamp=clamp)
     g = OM.backward(go, x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale,
-                    base_grads=base_grads, act=act)
+                    base_grads=base_grads, act=act, clamp=clamp)
     return out, g
 
 
@@ -68,11 +69,13 @@ class GpuRun:
 
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
                  scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None,
-                 base_grads: bool = False, activation: str = "swiglu", transformed: bool = False):
+                 base_grads: bool = False, activation: str = "swiglu", transformed: bool = False,
+                 clamp: float = 0.0):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
         then case's W13/W2 are not uploaded.  base_grads: also request the
         frozen-weight gradients dW13, dW2.  transformed: give the backward the
-        transformed base weights (W13T, W2T) written by moe_lora_transform_base."""
+        transformed base weights (W13T, W2T) written by moe_lora_transform_base.
+        clamp: the activation clamp c (0 = off)."""
         import torch
         from mixture_experts_grouped_amd import binding as B
         self.torch = torch
@@ -81,7 +84,7 @@ class GpuRun:
         fmt = B.MOE_BASE_MXFP4 if mx is not None else B.MOE_BASE_BF16
         act = {"swiglu": B.MOE_ACT_SWIGLU, "geglu": B.MOE_ACT_GEGLU}[activation]
         self.desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank,
-                                scale=s, block_m=block_m, base_format=fmt, activation=act)
+                                scale=s, block_m=block_m, base_format=fmt, activation=act, clamp=clamp)
         self.layer = B.MoeLoraLayer(self.desc, base_grads=base_grads)
         dev = "cuda"
 

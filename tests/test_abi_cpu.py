@@ -65,7 +65,7 @@ def test_workspace_sizes_grow_with_the_problem():
     ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 12, B.MOE_ERR_UNSUPPORTED),
     ("rank", 256, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
     ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 2, B.MOE_ERR_UNSUPPORTED),
-    ("clamp", 10.0, B.MOE_ERR_UNSUPPORTED), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
+    ("clamp", float("nan"), B.MOE_ERR_INVALID), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
     ("scale", float("nan"), B.MOE_ERR_INVALID),
 ])
 def test_desc_rejections(field, value, status):
@@ -214,3 +214,11 @@ def test_transformed_base_checks_before_any_launch():
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 2 + 4096, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, fake * 8 + 1024, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), byref(base), None, None, None) == B.MOE_OK
+
+
+@pytest.mark.parametrize("clamp", [0.0, -1.0, float("inf"), 10.0, 0.25])
+def test_activation_clamp_values_accepted(clamp):
+    """The activation clamp: c <= 0 or +inf is off, a finite c > 0 clips both
+    pre-activations (NaN is rejected, see test_desc_rejections)."""
+    d = B.make_desc(256, 512, 256, 16, 2, 8, clamp=clamp)
+    assert all(s > 0 for s in B.moe_lora_workspace_size(d))

@@ -100,10 +100,11 @@ MUTANTS = {
                           "gw[tt, jj] = -np.sum(go[tt] * f[\"y\"], axis=1)")],
     "dh_missing_lora": [("dh = dy @ p[\"W2\"][e] + s * (b2dy @ p[\"A2\"][e])", "dh = dy @ p[\"W2\"][e]")],
     "dv_uses_gate_grad": [("dv = dh * fa(f[\"gc\"])", "dv = dh * fa_grad(f[\"gc\"])")],
-    "clamp_gate_only": [("vc = np.clip(v, -clamp, clamp)", "vc = v")],
-    "clamp_one_sided": [("gc = np.clip(g, -clamp, clamp)", "gc = np.minimum(g, clamp)")],
-    "clamp_grad_not_masked": [("* (np.abs(f[\"g\"]) <= clamp)", "")],
-    "clamp_up_mask_from_gate": [("* (np.abs(f[\"v\"]) <= clamp)", "* (np.abs(f[\"g\"]) <= clamp)")],
+    "clamp_gate_only": [("vc, vout = _clip(v, clamp, _DECIDE[clamp_decide])",
+                         "vc, vout = v, np.zeros(v.shape, bool)")],
+    "clamp_one_sided": [("out = np.abs(d) > c", "out = d > c")],
+    "clamp_grad_not_masked": [("* ~f[\"gout\"]", "")],
+    "clamp_up_mask_from_gate": [("* ~f[\"vout\"]", "* ~f[\"gout\"]")],
     "clamp_on_output": [("h = ACTIVATIONS[act][0](gc) * vc", "h = np.clip(ACTIVATIONS[act][0](g) * v, -clamp, clamp)")],
     "gelu_tanh_approximation": [("return g * 0.5 * (1.0 + erf(g / np.sqrt(2.0)))",
                                  "return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))")],
@@ -123,3 +124,22 @@ MUTANTS = {
 def test_mutant_is_caught(name):
     bad = P.failing_pins(P.mutant(MUTANTS[name]))
     assert bad, f"mutant {name} passed every pin"
+
+
+def test_clamp_decision_in_fp16():
+    """clamp_decide="fp16" decides each clip on the float16 rounding of the
+    pre-activation and keeps the values exact: with c = 1, g = 1 + 2^-13
+    rounds to 1.0 in float16 (not clipped, stays 1 + 2^-13) while the exact
+    decision clips it to 1; far from the bound both decisions agree."""
+    c = 1.0
+    g = np.array([1.0 + 2.0 ** -13, -(1.0 + 2.0 ** -13), 0.3, 2.5, -2.5])
+    exact, out_e = M._clip(g, c, M._DECIDE[None])
+    half, out_h = M._clip(g, c, M._DECIDE["fp16"])
+    assert list(out_e) == [True, True, False, True, True]
+    assert list(out_h) == [False, False, False, True, True]
+    assert np.array_equal(exact, [1.0, -1.0, 0.3, 1.0, -1.0])
+    assert np.array_equal(half, [g[0], g[1], 0.3, 1.0, -1.0])
+    x, idx, w, p, go = P.micro_case(7)
+    a = M.forward_backward(x, idx, w, p, 0.7, go, clamp=0.6)
+    b = M.forward_backward(x, idx, w, p, 0.7, go, clamp=0.6, clamp_decide="fp16")
+    assert np.array_equal(a[0], b[0])  # no pre-activation of this case sits within float16 rounding of 0.6
