@@ -62,7 +62,13 @@ typedef int32_t moe_status;
  *     otherwise one of 16, 32, 64, 96, 128, 192, 240.
  *   activation: MOE_ACT_SWIGLU or MOE_ACT_GEGLU (the gated activations the
  *     pages list: PR #17 Summary; PR #9, "Correctness coverage").
- *   clamp: must be <= 0 or +inf (no clamp; the pages do not define one).
+ *   clamp: activation clamp c: when 0 < c < +inf both pre-activations are
+     clipped to [-c, c] before the gated activation, h = f(clip(g)) clip(v),
+     and the clip passes the gradient only where |x| <= c (the pages name the
+     clamp -- PR #9 "Correctness coverage", production clamp = 10 -- without
+     defining it; this is the plainest reading).  c <= 0 or +inf: no clamp;
+     NaN: MOE_ERR_INVALID.  The clip decision is taken on the fp16-rounded
+     pre-activation the forward saves, so forward and backward agree.
  * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
  *   1 <= topk <= 16, 1 <= rank <= 128 with rank % 8 == 0, T*H*2 and 4*I*H
  *   below 2^31 bytes (one 32-bit buffer offset per token-row tensor and per

@@ -34,7 +34,7 @@ moe_status check_desc(const moe_lora_desc* d) {
   if (d->H % 256 != 0 || d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->E > 512 || d->topk > 16 || d->rank > 128 || d->rank % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
-  if (!(d->clamp <= 0.0f || std::isinf(d->clamp))) return MOE_ERR_UNSUPPORTED;
+  if (std::isnan(d->clamp)) return MOE_ERR_INVALID;
   if (d->base_format != MOE_BASE_BF16 && d->base_format != MOE_BASE_MXFP4) return MOE_ERR_UNSUPPORTED;
   const int64_t routes = (int64_t)d->T * d->topk;
   const int64_t cap = routes + std::min<int64_t>(d->E, routes) * 239;
@@ -161,6 +161,7 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.W2T = (const uint16_t*)w->W2T;
   a.mx = d->base_format == MOE_BASE_MXFP4;
   a.act = d->activation;
+  a.clamp = (d->clamp > 0.0f && std::isfinite(d->clamp)) ? d->clamp : 0.0f;
   if (a.mx) {
     a.W13q = (const uint8_t*)w->W13;
     a.W2q = (const uint8_t*)w->W2;

@@ -191,7 +191,10 @@ struct LdW2dK {
 
 // ACT: 0 SwiGLU, 1 GeGLU (exact GELU): f'(g) = Phi(g) + g phi(g).
 // TW: read the transformed weights (bf16 base only).
-template <bool MX, int ACT, bool TW>
+// CL: activation clamp (as in the forward): g, v clipped to [-a.clamp,
+// a.clamp] before the activation; the clip passes gradient only where
+// |x| <= a.clamp, decided on the saved fp16 values as the forward decided.
+template <bool MX, int ACT, bool TW, bool CL>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   static_assert(!(MX && TW), "transformed weights are bf16");
   extern __shared__ __align__(16) char smem[];
@@ -314,21 +317,33 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float av = acc[nb][mb][4 * g + q];
+          float gq = gg[q], vq = vv[q];
+          bool pass_g = true, pass_v = true;
+          if constexpr (CL) {
+            pass_g = fabsf(gq) <= a.clamp;
+            pass_v = fabsf(vq) <= a.clamp;
+            if (!pass_g) gq = copysignf(a.clamp, gq);
+            if (!pass_v) vq = copysignf(a.clamp, vq);
+          }
           if constexpr (ACT == 0) {
             // silu'(g) = sg (1 + g (1 - sg)), so av silu'(g) = t + u - u sg
-            const float sg = sigmoidf_(gg[q]);
+            const float sg = sigmoidf_(gq);
             const float t = av * sg;
-            const float u = t * gg[q];  // unweighted dv = av silu(g)
-            dw[mb] += u * vv[q];
+            const float u = t * gq;  // unweighted dv = av silu(g)
+            dw[mb] += u * vq;
             dv[q] = wr[mb] * u;
-            dg[q] = wr[mb] * vv[q] * (t + fmaf(-u, sg, u));
+            dg[q] = wr[mb] * vq * (t + fmaf(-u, sg, u));
           } else {
             float cdf, pdf;
-            norm_cdf_pdf(gg[q], cdf, pdf);
-            const float u = av * gg[q] * cdf;  // unweighted dv
-            dw[mb] += u * vv[q];
+            norm_cdf_pdf(gq, cdf, pdf);
+            const float u = av * gq * cdf;  // unweighted dv
+            dw[mb] += u * vq;
             dv[q] = wr[mb] * u;
-            dg[q] = wr[mb] * av * vv[q] * fmaf(gg[q], pdf, cdf);
+            dg[q] = wr[mb] * av * vq * fmaf(gq, pdf, cdf);
+          }
+          if constexpr (CL) {
+            if (!pass_v) dv[q] = 0.0f;
+            if (!pass_g) dg[q] = 0.0f;
           }
         }
         // keep the running sum in place: otherwise the compiler sinks the
@@ -925,16 +940,37 @@ static void set_lds(const void* fn, int bytes) {
   hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <bool MX, int ACT, bool TW, bool CL>
+static void launch_w2d(const LayerArgs& a, dim3 grid, hipStream_t st) {
+  MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<MX, ACT, TW, CL>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+}
+template <bool MX, bool TW>
+static void launch_w2d_var(const LayerArgs& a, dim3 grid, hipStream_t st) {
+  const bool cl = a.clamp > 0.0f;
+  if (a.act == 1 && cl)
+    launch_w2d<MX, 1, TW, true>(a, grid, st);
+  else if (a.act == 1)
+    launch_w2d<MX, 1, TW, false>(a, grid, st);
+  else if (cl)
+    launch_w2d<MX, 0, TW, true>(a, grid, st);
+  else
+    launch_w2d<MX, 0, TW, false>(a, grid, st);
+}
+template <bool MX, bool TW>
+static void set_w2d_lds() {
+  set_lds((const void*)k_w2dgrad<MX, 0, TW, false>, W2D_LDS);
+  set_lds((const void*)k_w2dgrad<MX, 1, TW, false>, W2D_LDS);
+  set_lds((const void*)k_w2dgrad<MX, 0, TW, true>, W2D_LDS);
+  set_lds((const void*)k_w2dgrad<MX, 1, TW, true>, W2D_LDS);
+}
+
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_q, GS64::LDS_BYTES);
-    set_lds((const void*)k_w2dgrad<false, 0, false>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<true, 0, false>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<false, 1, false>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<true, 1, false>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<false, 0, true>, W2D_LDS);
-    set_lds((const void*)k_w2dgrad<false, 1, true>, W2D_LDS);
+    set_w2d_lds<false, false>();
+    set_w2d_lds<true, false>();
+    set_w2d_lds<false, true>();
     set_lds((const void*)k_w13dgrad<false, false>, W13D_LDS);
     set_lds((const void*)k_w13dgrad<true, false>, W13D_LDS);
     set_lds((const void*)k_w13dgrad<false, true>, W13D_LDS);
@@ -955,18 +991,12 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
       const hipError_t e = launch_transpose(a.A2, a.A2T, a.E, a.r, a.I, st);
       if (e != hipSuccess) return e;
     }
-    if (a.mx && a.act == 1)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 1, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
-    else if (a.mx)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<true, 0, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
-    else if (tw && a.act == 1)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1, true>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+    if (a.mx)
+      launch_w2d_var<true, false>(a, grid, st);
     else if (tw)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0, true>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
-    else if (a.act == 1)
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 1, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      launch_w2d_var<false, true>(a, grid, st);
     else
-      MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<false, 0, false>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+      launch_w2d_var<false, false>(a, grid, st);
   }
   const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);

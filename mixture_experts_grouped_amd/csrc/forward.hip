@@ -127,8 +127,13 @@ struct LdW13MX : LdW13Base {
   __device__ void finish(int, char* sN) const { nq.template finish<B>(sN); }
 };
 
-// ACT: 0 SwiGLU (h = silu(g) v), 1 GeGLU (h = gelu(g) v, exact GELU)
-template <bool MX, int ACT>
+// ACT: 0 SwiGLU (h = silu(g) v), 1 GeGLU (h = gelu(g) v, exact GELU).
+// CL: activation clamp, h = f(clip(g)) clip(v) with clip to [-a.clamp, a.clamp]
+// (PR #9 "Correctness coverage" names the clamp; the reading is the plainest
+// one: both pre-activations are clipped).  Whether a value is clipped is
+// decided on its fp16 rounding, the value saved for the backward, so that
+// both passes take the same decision.
+template <bool MX, int ACT, bool CL>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GW13;
@@ -196,13 +201,23 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
         for (int q = 0; q < 4; ++q) {
           gv[q] = acc[nb][mb][4 * g + q];
           vv[q] = acc[nb + NH][mb][4 * g + q];
-          if constexpr (ACT == 0)
-            hv[q] = gv[q] * sigmoidf_(gv[q]) * vv[q];
-          else
-            hv[q] = gv[q] * norm_cdf(gv[q]) * vv[q];
         }
-        *(f16x4*)(a.G + ob + 256 * g) = __builtin_convertvector(gv, f16x4);  // round to nearest even
-        *(f16x4*)(a.V + ob + 256 * g) = __builtin_convertvector(vv, f16x4);
+        const f16x4 g16 = __builtin_convertvector(gv, f16x4);  // round to nearest even
+        const f16x4 v16 = __builtin_convertvector(vv, f16x4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float gq = gv[q], vq = vv[q];
+          if constexpr (CL) {
+            if (fabsf((float)g16[q]) > a.clamp) gq = copysignf(a.clamp, gq);
+            if (fabsf((float)v16[q]) > a.clamp) vq = copysignf(a.clamp, vq);
+          }
+          if constexpr (ACT == 0)
+            hv[q] = gq * sigmoidf_(gq) * vq;
+          else
+            hv[q] = gq * norm_cdf(gq) * vq;
+        }
+        *(f16x4*)(a.G + ob + 256 * g) = g16;
+        *(f16x4*)(a.V + ob + 256 * g) = v16;
         ImgH::put(smem, ep.row(mb), ep.col(nb, g), hv);
       }
     }
@@ -362,14 +377,31 @@ static void set_lds(const void* fn, int bytes) {
   hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <bool MX, int ACT, bool CL>
+static void launch_w13(const LayerArgs& a, dim3 grid, hipStream_t st) {
+  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL>), grid, dim3(GW13::NT), W13_LDS, st, a);
+}
+template <bool MX, int ACT>
+static void launch_w13_cl(const LayerArgs& a, dim3 grid, hipStream_t st) {
+  if (a.clamp > 0.0f)
+    launch_w13<MX, ACT, true>(a, grid, st);
+  else
+    launch_w13<MX, ACT, false>(a, grid, st);
+}
+template <bool MX>
+static void set_w13_lds() {
+  set_lds((const void*)k_w13<MX, 0, false>, W13_LDS);
+  set_lds((const void*)k_w13<MX, 1, false>, W13_LDS);
+  set_lds((const void*)k_w13<MX, 0, true>, W13_LDS);
+  set_lds((const void*)k_w13<MX, 1, true>, W13_LDS);
+}
+
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static bool init = false;
   if (!init) {
     set_lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_lds((const void*)k_w13<false, 0>, W13_LDS);
-    set_lds((const void*)k_w13<true, 0>, W13_LDS);
-    set_lds((const void*)k_w13<false, 1>, W13_LDS);
-    set_lds((const void*)k_w13<true, 1>, W13_LDS);
+    set_w13_lds<false>();
+    set_w13_lds<true>();
     set_lds((const void*)k_a2, GS128::LDS_BYTES);
     set_lds((const void*)k_w2<false>, W2_LDS);
     set_lds((const void*)k_w2<true>, W2_LDS);
@@ -383,13 +415,13 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   {
     const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
     if (a.mx && a.act == 1)
-      MOE_LAUNCH_AS("k_w13", (k_w13<true, 1>), grid, dim3(GW13::NT), W13_LDS, st, a);
+      launch_w13_cl<true, 1>(a, grid, st);
     else if (a.mx)
-      MOE_LAUNCH_AS("k_w13", (k_w13<true, 0>), grid, dim3(GW13::NT), W13_LDS, st, a);
+      launch_w13_cl<true, 0>(a, grid, st);
     else if (a.act == 1)
-      MOE_LAUNCH_AS("k_w13", (k_w13<false, 1>), grid, dim3(GW13::NT), W13_LDS, st, a);
+      launch_w13_cl<false, 1>(a, grid, st);
     else
-      MOE_LAUNCH_AS("k_w13", (k_w13<false, 0>), grid, dim3(GW13::NT), W13_LDS, st, a);
+      launch_w13_cl<false, 0>(a, grid, st);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)

@@ -45,6 +45,7 @@ struct LayerArgs {
   // their e8m0 scales [E, 2I, H/32], [E, H, I/32]
   int mx;
   int act;          // MOE_ACT_SWIGLU or MOE_ACT_GEGLU
+  float clamp;      // activation clamp c > 0 (pre-activations clipped to [-c, c]); 0 = off
   const uint8_t *W13q, *W13s, *W2q, *W2s;
   // transformed bf16 base weights (optional, nullptr = read W13 / W2
   // transposed): W13T [E, H, 2I] = W13_e^T, W2T [E, I, H] = W2_e^T

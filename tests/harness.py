@@ -52,14 +52,15 @@ def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX):
 
 
 def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False, act: str = "swiglu",
-               clamp: float = np.inf):
+               clamp: float = np.inf, clamp_decide=None):
     from oracle import moe_lora as OM
     x = f64(case["x"])
     go = f64(case["grad_out"])
     p = {n: f64(case[n]) for n in PARAMS}
-    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act, clamp=clamp)
+    out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act, clamp=clamp,
+                     clamp_decide=clamp_decide)
     g = OM.backward(go, x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale,
-                    base_grads=base_grads, act=act, clamp=clamp)
+                    base_grads=base_grads, act=act, clamp=clamp, clamp_decide=clamp_decide)
     return out, g
 
 

@@ -1,0 +1,84 @@
+"""Activation clamp (both pre-activations clipped to [-c, c] before the gated
+activation; the pages name the clamp without defining it, see the oracle's
+reading 7): GPU parity.
+
+- against the oracle with the clip decided in float16, as the kernels decide
+  it (SwiGLU and GeGLU; c = 1 clips about a third of the pre-activations of
+  these N(0, 1)-scaled inputs), and the clamped results differ from the
+  unclamped ones;
+- a clamp no value reaches gives bitwise the unclamped results;
+- MXFP4 base with the clamp: bitwise the bf16 path on the dequantised weights;
+- transformed base with the clamp: bitwise the plain layout.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_grouped_amd import inputs as I
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": (I.TINY, (41,), 0.0),
+    "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (42,), 0.2),
+    "multi_tile": (I.Shape(T=1100, H=256, I=256, E=4, topk=2, rank=16), (43,), 0.0),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    Hn.ensure_built()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_clamp_against_oracle(name, act):
+    shape, key, mask = CASES[name]
+    c = 1.0
+    Hn.log(f"[clamp] case={name} act={act} c={c}")
+    case = I.layer_inputs(shape, key, mask_prob=mask)
+    res = Hn.GpuRun(shape, case, activation=act, clamp=c).run()
+    from oracle import moe_lora as OM
+    x = Hn.f64(case["x"])
+    p = {n: Hn.f64(case[n]) for n in Hn.PARAMS}
+    _, inter = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, shape.scale,
+                          keep=True, act=act, clamp=c, clamp_decide="fp16")
+    live = case["topk_idx"] >= 0
+    clipped = np.mean(np.abs(np.concatenate([inter["G"][live], inter["V"][live]])) > c)
+    assert 0.15 < clipped < 0.6, clipped  # the case exercises the clip
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale, act=act, clamp=c, clamp_decide="fp16")
+    Hn.compare_all(res, ref_out, ref_g, tag=f"{name}:{act}:clamp:")
+    plain = Hn.GpuRun(shape, case, activation=act).run()
+    assert not np.array_equal(plain["out"], res["out"])
+    assert not np.array_equal(plain["dB1"], res["dB1"])
+
+
+def test_unreached_clamp_is_bitwise_unclamped():
+    shape, key, mask = CASES["r128_masked"]
+    case = I.layer_inputs(shape, key, mask_prob=mask)
+    a = Hn.GpuRun(shape, case, clamp=1.0e4).run()
+    b = Hn.GpuRun(shape, case).run()
+    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+def test_clamp_mxfp4_bitwise_vs_dequantised(act):
+    shape, key, mask = CASES["r128_masked"]
+    case = I.layer_inputs(shape, key, mask_prob=mask)
+    mx, deq = Hn.mxfp4_base(case)
+    case_deq = dict(case, W13=deq["W13"], W2=deq["W2"])
+    a = Hn.GpuRun(shape, case, mx=mx, activation=act, clamp=1.0).run()
+    b = Hn.GpuRun(shape, case_deq, activation=act, clamp=1.0).run()
+    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+def test_clamp_transformed_base_bitwise(act):
+    shape, key, mask = CASES["r128_masked"]
+    case = I.layer_inputs(shape, key, mask_prob=mask)
+    a = Hn.GpuRun(shape, case, activation=act, clamp=1.0, transformed=True).run()
+    b = Hn.GpuRun(shape, case, activation=act, clamp=1.0).run()
+    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
