@@ -253,6 +253,9 @@ def main():
                          "written once by moe_lora_transform_base before the timed steps, so the "
                          "backward's data-gradient GEMMs read it in contraction order; plain: "
                          "transpose through LDS on every backward (same bits)")
+    ap.add_argument("--clamp", type=float, default=0.0,
+                    help="activation clamp c (> 0: both pre-activations clipped to [-c, c]; the "
+                         "pages' production runs use 10); default off, as in the headline workload")
     ap.add_argument("--activation", choices=("swiglu", "geglu"), default="swiglu",
                     help="gated activation (GeGLU: exact GELU)")
     ap.add_argument("--base-grads", action="store_true",
@@ -326,7 +329,8 @@ def main():
 
     desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank, shape.scale,
                        base_format=B.MOE_BASE_MXFP4 if mx else B.MOE_BASE_BF16,
-                       activation=B.MOE_ACT_GEGLU if args.activation == "geglu" else B.MOE_ACT_SWIGLU)
+                       activation=B.MOE_ACT_GEGLU if args.activation == "geglu" else B.MOE_ACT_SWIGLU,
+                       clamp=args.clamp)
     layer = B.MoeLoraLayer(desc, device=dev, base_grads=args.base_grads)
     stream = torch.cuda.current_stream()
     transformed = args.base_layout == "transformed" and not mx
@@ -423,11 +427,12 @@ def main():
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
                          f"over 64 experts (uniform), H={H}, I={Idim}, rank {r}, "
-                         f"{'GeGLU' if args.activation == 'geglu' else 'SwiGLU'}, s=1"),
+                         f"{'GeGLU' if args.activation == 'geglu' else 'SwiGLU'}"
+                         f"{f' clamp={args.clamp:g}' if args.clamp > 0 else ''}, s=1"),
             "tokens": T, "routed_rows": M, "experts": 64, "H": H, "I": Idim, "rank": r,
             "block_m": layer.block_m, "base": args.base, "base_grads": args.base_grads,
             "base_layout": "transformed" if transformed else "plain",
-            "activation": args.activation,
+            "activation": args.activation, "clamp": args.clamp if args.clamp > 0 else None,
         },
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),
