@@ -936,9 +936,6 @@ hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, in
   return hipGetLastError();
 }
 
-static void set_lds(const void* fn, int bytes) {
-  hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
 
 template <bool MX, int ACT, bool TW, bool CL>
 static void launch_w2d(const LayerArgs& a, dim3 grid, hipStream_t st) {
@@ -957,30 +954,32 @@ static void launch_w2d_var(const LayerArgs& a, dim3 grid, hipStream_t st) {
     launch_w2d<MX, 0, TW, false>(a, grid, st);
 }
 template <bool MX, bool TW>
-static void set_w2d_lds() {
-  set_lds((const void*)k_w2dgrad<MX, 0, TW, false>, W2D_LDS);
-  set_lds((const void*)k_w2dgrad<MX, 1, TW, false>, W2D_LDS);
-  set_lds((const void*)k_w2dgrad<MX, 0, TW, true>, W2D_LDS);
-  set_lds((const void*)k_w2dgrad<MX, 1, TW, true>, W2D_LDS);
+static void set_w2d_lds(AttrInit& ai) {
+  ai.lds((const void*)k_w2dgrad<MX, 0, TW, false>, W2D_LDS);
+  ai.lds((const void*)k_w2dgrad<MX, 1, TW, false>, W2D_LDS);
+  ai.lds((const void*)k_w2dgrad<MX, 0, TW, true>, W2D_LDS);
+  ai.lds((const void*)k_w2dgrad<MX, 1, TW, true>, W2D_LDS);
 }
 
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
-  static bool init = false;
-  if (!init) {
-    set_lds((const void*)k_q, GS64::LDS_BYTES);
-    set_w2d_lds<false, false>();
-    set_w2d_lds<true, false>();
-    set_w2d_lds<false, true>();
-    set_lds((const void*)k_w13dgrad<false, false>, W13D_LDS);
-    set_lds((const void*)k_w13dgrad<true, false>, W13D_LDS);
-    set_lds((const void*)k_w13dgrad<false, true>, W13D_LDS);
-    set_lds((const void*)k_p13, GS128::LDS_BYTES);
-    set_lds((const void*)k_rank_dx, RK_LDS);
-    set_lds((const void*)k_wgrad_local, WG_LDS);
-    set_lds((const void*)k_wgrad_base, WG_LDS);
-    set_lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
-    init = true;
-  }
+  static PerDeviceOnce attrs;
+  const hipError_t ierr = attrs.run([] {
+    AttrInit ai;
+    ai.lds((const void*)k_q, GS64::LDS_BYTES);
+    set_w2d_lds<false, false>(ai);
+    set_w2d_lds<true, false>(ai);
+    set_w2d_lds<false, true>(ai);
+    ai.lds((const void*)k_w13dgrad<false, false>, W13D_LDS);
+    ai.lds((const void*)k_w13dgrad<true, false>, W13D_LDS);
+    ai.lds((const void*)k_w13dgrad<false, true>, W13D_LDS);
+    ai.lds((const void*)k_p13, GS128::LDS_BYTES);
+    ai.lds((const void*)k_rank_dx, RK_LDS);
+    ai.lds((const void*)k_wgrad_local, WG_LDS);
+    ai.lds((const void*)k_wgrad_base, WG_LDS);
+    ai.lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
+    return ai.err;
+  });
+  if (ierr != hipSuccess) return ierr;
   const int tm = (a.T + GS64::TM - 1) / GS64::TM;
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
   {

@@ -373,9 +373,6 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-static void set_lds(const void* fn, int bytes) {
-  hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
 
 template <bool MX, int ACT, bool CL>
 static void launch_w13(const LayerArgs& a, dim3 grid, hipStream_t st) {
@@ -389,26 +386,28 @@ static void launch_w13_cl(const LayerArgs& a, dim3 grid, hipStream_t st) {
     launch_w13<MX, ACT, false>(a, grid, st);
 }
 template <bool MX>
-static void set_w13_lds() {
-  set_lds((const void*)k_w13<MX, 0, false>, W13_LDS);
-  set_lds((const void*)k_w13<MX, 1, false>, W13_LDS);
-  set_lds((const void*)k_w13<MX, 0, true>, W13_LDS);
-  set_lds((const void*)k_w13<MX, 1, true>, W13_LDS);
+static void set_w13_lds(AttrInit& ai) {
+  ai.lds((const void*)k_w13<MX, 0, false>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 1, false>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 0, true>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 1, true>, W13_LDS);
 }
 
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
-  static bool init = false;
-  if (!init) {
-    set_lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_w13_lds<false>();
-    set_w13_lds<true>();
-    set_lds((const void*)k_a2, GS128::LDS_BYTES);
-    set_lds((const void*)k_w2<false>, W2_LDS);
-    set_lds((const void*)k_w2<true>, W2_LDS);
-    set_lds((const void*)k_rank_combine, RK_LDS);
-    init = true;
-  }
-  hipError_t err = launch_pool_prologue(a, st);
+  static PerDeviceOnce attrs;
+  hipError_t err = attrs.run([] {
+    AttrInit ai;
+    ai.lds((const void*)k_shrink, GS64::LDS_BYTES);
+    set_w13_lds<false>(ai);
+    set_w13_lds<true>(ai);
+    ai.lds((const void*)k_a2, GS128::LDS_BYTES);
+    ai.lds((const void*)k_w2<false>, W2_LDS);
+    ai.lds((const void*)k_w2<true>, W2_LDS);
+    ai.lds((const void*)k_rank_combine, RK_LDS);
+    return ai.err;
+  });
+  if (err != hipSuccess) return err;
+  err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
   const int tm = (a.T + GS64::TM - 1) / GS64::TM;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);

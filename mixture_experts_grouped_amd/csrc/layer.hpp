@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "engine.hpp"
 
 namespace moelora {
@@ -81,6 +83,37 @@ struct LayerArgs {
   uint16_t* gx;
   float* gw;
   uint16_t *dA1, *dA3, *dB1, *dB3, *dA2, *dB2, *dW13, *dW2;
+};
+
+// The first error of a run of kernel-attribute calls.
+struct AttrInit {
+  hipError_t err = hipSuccess;
+  void lds(const void* fn, int bytes) {
+    if (err == hipSuccess) err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  }
+};
+
+// Kernel attributes are per device: run `init` (returning hipError_t) once
+// on each device the library is called on; concurrent first calls wait for
+// it.  A failed init is retried on the next call.
+class PerDeviceOnce {
+ public:
+  template <class F>
+  hipError_t run(F&& init) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu_);
+    const bool tracked = dev >= 0 && dev < 64;
+    if (tracked && ((done_ >> dev) & 1u)) return hipSuccess;
+    e = init();
+    if (e == hipSuccess && tracked) done_ |= 1ull << dev;
+    return e;
+  }
+
+ private:
+  std::mutex mu_;
+  uint64_t done_ = 0;  // bit d: device d initialised
 };
 
 hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,

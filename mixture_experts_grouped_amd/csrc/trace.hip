@@ -44,7 +44,10 @@ bool trace_on() { return g_on; }
 void trace_begin(hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_open = get_event();
-  if (g_open != nullptr) hipEventRecord(g_open, st);
+  if (g_open != nullptr && hipEventRecord(g_open, st) != hipSuccess) {  // not traced
+    g_free.push_back(g_open);
+    g_open = nullptr;
+  }
 }
 
 void trace_end(const char* name, hipStream_t st) {
@@ -52,7 +55,12 @@ void trace_end(const char* name, hipStream_t st) {
   if (g_open == nullptr) return;
   hipEvent_t b = get_event();
   if (b == nullptr) return;
-  hipEventRecord(b, st);
+  if (hipEventRecord(b, st) != hipSuccess) {  // drop this launch from the trace
+    g_free.push_back(g_open);
+    g_free.push_back(b);
+    g_open = nullptr;
+    return;
+  }
   g_pending.push_back(Pending{name, g_open, b});
   g_open = nullptr;
 }
