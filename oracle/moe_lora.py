@@ -17,7 +17,7 @@ What the layer computes, as the pages state it:
 * PR #17 Summary and PR #9 "Correctness coverage" list GeGLU next to SwiGLU
   as the layer's gated activation.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   1. every adapted projection is W x + s * B (A x), s the adapter scale;
   2. SwiGLU is h = silu(g) * v with g from the first I rows of W13 (W1) and v
      from the last I rows (W3), silu(g) = g * sigmoid(g);
