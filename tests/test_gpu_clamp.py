@@ -82,3 +82,15 @@ def test_clamp_transformed_base_bitwise(act):
     b = Hn.GpuRun(shape, case, activation=act, clamp=1.0).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
         assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+
+
+def test_clamp_with_frozen_weight_grads_against_oracle():
+    """The optional dW13 / dW2 with the clamp: dW13 contracts the masked
+    dg / dv, dW2 the clamped h; against the oracle (float16 clip decision)."""
+    shape, key, mask = CASES["multi_tile"]
+    case = I.layer_inputs(shape, key, mask_prob=mask)
+    res = Hn.GpuRun(shape, case, clamp=1.0, base_grads=True).run()
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale, base_grads=True, clamp=1.0, clamp_decide="fp16")
+    Hn.compare_all(res, ref_out, ref_g, tag="multi_tile:clamp:base:")
+    for n in ("dW13", "dW2"):
+        Hn.assert_close("multi_tile:clamp:" + n, Hn.f64(res[n]), ref_g[n])
