@@ -559,23 +559,33 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   }
 }
 
-// pc_t = s * sum_j P_(t,j), written as hi/lo [pc1 hi | pc1 lo | pc3 hi | pc3 lo]
+// pc_t = s * sum_j P_(t,j), written as hi/lo [pc1 hi | pc1 lo | pc3 hi | pc3 lo].
+// One thread per token and 4 columns (never straddling pc1 / pc3, r % 8 ==
+// 0): the token's route indices first, then one 16-byte P load per live
+// route, added in route order.
 __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const int r2 = 2 * a.r;
-  if (i >= (long)a.T * r2) return;
-  const int t = (int)(i / r2), c = (int)(i % r2);
-  float z = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
-    const int row = a.r2row[t * a.k + j];
-    if (row >= 0) z += a.P[(long)row * r2 + c];
+  const int r2 = 2 * a.r, g4 = r2 / 4;
+  if (i >= (long)a.T * g4) return;
+  const int t = (int)(i / g4), c = (int)(i % g4) * 4;
+  int rows[16];  // topk <= 16
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rows[j] = j < a.k ? a.r2row[t * a.k + j] : -1;
+  f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (rows[j] < 0) continue;
+    const f32x4 p = *(const f32x4*)(a.P + (long)rows[j] * r2 + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) z[q] += p[q];
   }
-  uint32_t hi, lo;
-  split_hl(a.s * z, hi, lo);
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_hl(a.s * z[q], hi[q], lo[q]);
   const int fac = c / a.r, cc = c - fac * a.r;
   uint16_t* d = a.pc + (long)t * 4 * a.r + fac * 2 * a.r + cc;
-  d[0] = (uint16_t)hi;
-  d[a.r] = (uint16_t)lo;
+  *(u32x2*)d = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+  *(u32x2*)(d + a.r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
 }
 
 // ----------------------------------------------------------------------------
@@ -1009,7 +1019,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }
   MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
-  const long npc = (long)a.T * 2 * a.r;
+  const long npc = (long)a.T * (2 * a.r / 4);
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK_T::TM - 1) / GRK_T::TM, a.H / GRK_T::TN), dim3(GRK_T::NT), RK_LDS, st,
              a);

@@ -330,19 +330,32 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a7: zc_t = sum_j w_tj Z2_(t,j);  out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
 // ----------------------------------------------------------------------------
+// One thread per token and 4 columns: all of the token's route indices are
+// loaded first, then one 16-byte Z2 load per live route (routes added in
+// route order); hi and lo go out as 8-byte stores.
 __global__ __launch_bounds__(256) void k_zc(LayerArgs a) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long)a.T * a.r) return;
-  const int t = (int)(i / a.r), c = (int)(i % a.r);
-  float z = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
-    const int row = a.r2row[t * a.k + j];
-    if (row >= 0) z += a.w[t * a.k + j] * a.Z2[(long)row * a.r + c];
+  const int g4 = a.r / 4;  // r % 8 == 0
+  if (i >= (long)a.T * g4) return;
+  const int t = (int)(i / g4), c = (int)(i % g4) * 4;
+  int rows[16];  // topk <= 16
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rows[j] = j < a.k ? a.r2row[t * a.k + j] : -1;
+  f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (rows[j] < 0) continue;  // a dropped route's weight is not read
+    const float wj = a.w[t * a.k + j];
+    const f32x4 p = *(const f32x4*)(a.Z2 + (long)rows[j] * a.r + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) z[q] += wj * p[q];
   }
-  uint32_t hi, lo;
-  split_hl(z, hi, lo);
-  a.zc[(long)t * 2 * a.r + c] = (uint16_t)hi;
-  a.zc[(long)t * 2 * a.r + a.r + c] = (uint16_t)lo;
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_hl(z[q], hi[q], lo[q]);
+  uint16_t* d = a.zc + (long)t * 2 * a.r + c;
+  *(u32x2*)d = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+  *(u32x2*)(d + a.r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
 }
 
 struct LdRankC {
@@ -427,7 +440,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     MOE_LAUNCH(k_w2<true>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   else
     MOE_LAUNCH(k_w2<false>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
-  const long nzc = (long)a.T * a.r;
+  const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_combine, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
   MOE_LAUNCH_AS("k_combine_sum", k_token_sum<true>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a, a.Yb,
