@@ -63,7 +63,7 @@ struct Plan {
   size_t saved, scratch;
   // byte offsets
   size_t o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
-  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T;
+  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -98,6 +98,8 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_ZAp = take(cap * 4 * r * 2);
   p.o_dwp = take((size_t)(I / 256) * cap * 4);
   p.o_A2T = take((size_t)d->E * I * r * 2);  // A2_e^T, with transformed base weights
+  p.o_A1T = take(H * r * 2);                  // A1^T, A3^T for the grad-x rank product
+  p.o_A3T = take(H * r * 2);
   // forward-only tensors share space with backward-only ones: the base
   // outputs and Z2 are read only by the forward's combine
   p.o_Yb = p.o_dU;  // [cap, H] bf16, same size
@@ -204,6 +206,8 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.Yb = (uint16_t*)(b + p.o_Yb);
   a.dwp = (float*)(b + p.o_dwp);
   a.A2T = (uint16_t*)(b + p.o_A2T);
+  a.A1T = (uint16_t*)(b + p.o_A1T);
+  a.A3T = (uint16_t*)(b + p.o_A3T);
 }
 
 }  // namespace

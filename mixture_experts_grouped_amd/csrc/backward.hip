@@ -591,44 +591,45 @@ __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a12: grad_x = [A1; A3]^T pc + sum_j dU
 // ----------------------------------------------------------------------------
-// Stages [0, nst): pc columns [0, 2r) against A1 (hi/lo halves fold onto the
-// same r rows); stages [nst, 2 nst): pc columns [2r, 4r) against A3.  The pc
-// window covers all 4r columns: past 2r in a pass the A rows read zero.
-struct LdRankDx {
-  using KM = v2::KLoad<GRK_T::TM, GRK_T::KT, GRK_T::NW>;
-  using TN = v2::TLoad<GRK_T::TN, v2::TStrided, GRK_T::KT, GRK_T::NW>;
-  static constexpr int INSTS = KM::NJ + TN::NJ;
-  KM m;
-  TN n;
-  rsrc_t rs1, rs3;
+// P = [A1; A3]^T pc_t for 256 tokens x 256 columns.  Stages [0, nst): pc
+// columns [0, 2r) against A1 (hi/lo halves fold onto the same r columns);
+// stages [nst, 2 nst): pc columns [2r, 4r) against A3.  The A factors come in
+// transposed per call (A1T, A3T = A1^T, A3^T, [H, r], by k_transpose), so the
+// N operand is a K tile of rows h0..; past 2r in a pass the A columns read
+// zero.
+struct LdRankDxK {
+  using KM = v2::KLoad<GRK::TM, GRK::KT, GRK::NW>;
+  static constexpr int INSTS = 2 * KM::NJ;
+  KM m, n1, n3;
   int nst, r;
   __device__ void issue(int s, char* sM, char* sN) {
     const bool second = s >= nst;
-    const int k0 = (second ? s - nst : s) * GRK_T::KT;
+    const int k0 = (second ? s - nst : s) * GRK::KT;
     m.issue((second ? 2 * r : 0) + k0, 0, false, sM);
-    n.kp.rs = second ? rs3 : rs1;
-    n.issue(k0, sN);
+    if (second)
+      n3.issue(k0, 0, false, sN);
+    else
+      n1.issue(k0, 0, false, sN);
   }
 };
 
-// P = [A1; A3]^T pc_t for 256 tokens x 256 columns
-__global__ __launch_bounds__(GRK_T::NT) void k_rank_dx(LayerArgs a) {
+__global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GRK_T::TM, h0 = blockIdx.y * GRK_T::TN;
+  const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
-  LdRankDx L;
+  LdRankDxK L;
   L.r = r;
-  L.nst = (2 * r + GRK_T::KT - 1) / GRK_T::KT;
+  L.nst = (2 * r + GRK::KT - 1) / GRK::KT;
   L.m.contig(a.pc, t0, a.T - t0, 4 * r);
   L.m.window(4 * r);
-  L.rs1 = make_rsrc(a.A1, (uint64_t)r * a.H * 2);
-  L.rs3 = make_rsrc(a.A3, (uint64_t)r * a.H * 2);
-  L.n.kp = v2::TStrided{L.rs1, (uint32_t)(2 * a.H), 0, 2 * r, r};
-  L.n.cols(h0, GRK_T::TN);
-  f32x16 acc[GRK_T::NB][GRK_T::MB];
-  zero_acc<GRK_T>(acc);
-  v2::run_stages2<GRK_T, 0>(L, 2 * L.nst, acc, smem);
-  store_rank_tile<GRK_T>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
+  L.n1.contig(a.A1T, h0, GRK::TN, r);
+  L.n1.window(2 * r, r);
+  L.n3.contig(a.A3T, h0, GRK::TN, r);
+  L.n3.window(2 * r, r);
+  f32x16 acc[GRK::NB][GRK::MB];
+  zero_acc<GRK>(acc);
+  v2::run_stages2<GRK, 0>(L, 2 * L.nst, acc, smem);
+  store_rank_tile<GRK>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1021,8 +1022,12 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
   const long npc = (long)a.T * (2 * a.r / 4);
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK_T::TM - 1) / GRK_T::TM, a.H / GRK_T::TN), dim3(GRK_T::NT), RK_LDS, st,
-             a);
+  {
+    hipError_t e = launch_transpose(a.A1, a.A1T, 1, a.r, a.H, st);
+    if (e == hipSuccess) e = launch_transpose(a.A3, a.A3T, 1, a.r, a.H, st);
+    if (e != hipSuccess) return e;
+  }
+  MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
   MOE_LAUNCH_AS("k_dx_sum", k_token_sum<false>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a,
              a.dU, a.Pt, a.gx);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once

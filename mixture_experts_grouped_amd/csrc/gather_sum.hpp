@@ -17,13 +17,10 @@
 
 namespace moelora {
 
-// 256-token x 256-column tiles of P; eight waves of 128 x 64.  GRK_T takes the
-// N operand K-outer.
+// 256-token x 256-column tiles of P; eight waves of 128 x 64.
 using GRK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
-using GRK_T = v2::Geo2<4, 2, 2, 4, false, true, 64>;
 using RankImg = v2::TileImage<GRK, GRK::TN / 2, float>;
 constexpr int RK_LDS = cmax(GRK::LDS_BYTES, RankImg::BYTES);
-static_assert(GRK_T::LDS_BYTES == GRK::LDS_BYTES, "same LDS footprint");
 
 // acc (a 256 x 256 tile of P, tokens t0.., columns h0..) -> P rows, through
 // LDS images of one column half at a time.

@@ -78,6 +78,7 @@ struct LayerArgs {
   float* Pt;         // [T, H]    per-token rank term of the combine / grad-x (scratch)
   float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
   uint16_t* A2T;     // [E, I, r]  A2_e^T (backward scratch, with W2T only)
+  uint16_t *A1T, *A3T;  // [H, r]  A1^T, A3^T (backward scratch)
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;
