@@ -10,8 +10,17 @@ A1/A3/B2, expert-local B1/B3/A2), SwiGLU, bf16 data with fp32 accumulation.
 
 Prints one JSON line.  `value` is the whole step's algorithmic throughput in
 TFLOP/s (shared factors counted once per token, hi/lo split work not counted);
-`ms_per_step` is the F+B time.  Per-kernel times come from HIP events the
-library records on its launch stream during the timed steps.
+`ms_per_step` is the F+B time.
+
+Timing protocol (the pages' matched production-shape measurements: CUDA-event
+samples, 3 warmups, 3 rounds x 10 samples, median, F+B timed directly): W
+warmup steps, then K steps (default 30 = 3 rounds of 10), each bracketed by
+HIP events on the launch stream; ms_per_step is the median sample (min, max
+and the per-round medians are reported beside it).  Forward (build_pool +
+forward) and backward are timed the same way in passes of their own.  The
+per-kernel times come from a separate pass of K steps in which the library
+records HIP events around every launch on its launch stream, so the timed
+rounds carry no per-kernel events.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--tokens T]
                     [--cpu-seconds S | --no-cpu-baseline]
@@ -149,6 +158,50 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
+def library_gemm(torch):
+    """Calibration only: the vendor GEMM library (hipBLASLt, through torch) on
+    plain bf16 GEMMs of the expert GEMMs' shapes at the production share, with
+    no gather, no low-rank extension and no fused epilogue.  It shows what a
+    plain GEMM reaches on this chip, next to the fused kernels' rates."""
+    import numpy as np
+    E, R, H, I = 64, 1536, 4096, 2048
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+
+    def timeit(name, fn, flops):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b) / 10)
+        ms = float(np.median(samples))
+        rows.append({"gemm": name, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
+        print(f"[library] {rows[-1]}", file=sys.stderr, flush=True)
+
+    # batched per expert, both operands contiguous (no transposed views)
+    x13 = torch.randn(E, R, H, device="cuda", dtype=bf, generator=g)
+    w13 = torch.randn(E, H, 2 * I, device="cuda", dtype=bf, generator=g)
+    timeit("bmm [64,1536,4096]x[64,4096,4096] (W13 shape)", lambda: torch.bmm(x13, w13), 2.0 * E * R * H * 2 * I)
+    del x13, w13
+    x2 = torch.randn(E, R, I, device="cuda", dtype=bf, generator=g)
+    w2 = torch.randn(E, I, H, device="cuda", dtype=bf, generator=g)
+    timeit("bmm [64,1536,2048]x[64,2048,4096] (W2 shape)", lambda: torch.bmm(x2, w2), 2.0 * E * R * I * H)
+    del x2, w2
+    a = torch.randn(E * R, H, device="cuda", dtype=bf, generator=g)
+    b = torch.randn(H, 2 * I, device="cuda", dtype=bf, generator=g)
+    timeit("mm 98304x4096 @ 4096x4096", lambda: a @ b, 2.0 * E * R * H * 2 * I)
+    print(json.dumps({"metric": "vendor GEMM library on the expert GEMM shapes (calibration)", "unit": "TFLOP/s",
+                      "peak": PEAK_BF16_TFLOPS, "dtype": "bf16", "rows": rows}), flush=True)
+
+
 SWEEP_T = (1, 15, 16, 17, 90, 91, 176, 177, 346, 347, 688, 689, 1029, 1030, 2048)
 
 
@@ -238,7 +291,7 @@ def token_sweep(torch, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=16384)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -267,6 +320,9 @@ def main():
                          "weight-read rate against HBM; prints one JSON line with a table")
     ap.add_argument("--graph", action="store_true",
                     help="with --sweep: capture each step once in a HIP graph and time its replays")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor GEMM library (hipBLASLt via torch) on plain bf16 GEMMs of "
+                         "the expert GEMM shapes, as a calibration of what a plain GEMM reaches here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -280,6 +336,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.library_gemm:
+        library_gemm(torch)
         return
     if args.sweep:
         token_sweep(torch, args)
@@ -345,33 +404,45 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    trace = not args.no_trace
-    if trace:
+    def sampled(fn, n):
+        """n samples of fn, each bracketed by events on the launch stream;
+        returns (per-sample ms list, wall-clock ms over all n)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return [a.elapsed_time(b) for a, b in evs], wall
+
+    def summary(samples, rounds):
+        per = max(1, len(samples) // rounds)
+        med = lambda v: float(np.median(v))  # noqa: E731
+        return {"median": round(med(samples), 4), "min": round(min(samples), 4), "max": round(max(samples), 4),
+                "round_medians": [round(med(samples[i * per:(i + 1) * per]), 4) for i in range(rounds)
+                                  if samples[i * per:(i + 1) * per]]}
+
+    rounds = 3 if args.steps >= 3 else 1
+    fb_samples, fb_wall = sampled(step, args.steps)  # the timed region: exactly K steps
+    ms = float(np.median(fb_samples))
+    fwd_samples, _ = sampled(lambda: (layer.build_pool(tidx, stream), layer.forward(x, tw, params, stream)),
+                             args.steps)
+    bwd_samples, _ = sampled(lambda: layer.backward(go, tw, params, stream), args.steps)
+    fwd_ms = float(np.median(fwd_samples))
+    bwd_ms = float(np.median(bwd_samples))
+
+    kernels = {}
+    if not args.no_trace:  # per-kernel events in a pass of their own
         B.moe_lora_trace_reset()
         B.moe_lora_trace_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernels = {}
-    if trace:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
         B.moe_lora_trace_enable(False)
         kernels = B.moe_lora_trace_collect()
-    ms = (t1 - t0) * 1e3 / args.steps
-
-    # forward and backward timed directly (outside the timed steps)
-    def timed(fn, n=5):
-        torch.cuda.synchronize()
-        a = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - a) * 1e3 / n
-
-    fwd_ms = timed(lambda: (layer.build_pool(tidx, stream), layer.forward(x, tw, params, stream)))
-    bwd_ms = timed(lambda: layer.backward(go, tw, params, stream))
 
     M = int((idx >= 0).sum())
     T, H, Idim, r = shape.T, shape.H, shape.I, shape.rank
@@ -436,6 +507,11 @@ def main():
         },
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),
+        "timing": {"protocol": f"{args.warmup} warmups, {rounds} rounds of {args.steps // rounds} "
+                               "event-timed samples, median; F, B and F+B each timed directly",
+                   "fb_ms": summary(fb_samples, rounds), "fwd_ms": summary(fwd_samples, rounds),
+                   "bwd_ms": summary(bwd_samples, rounds),
+                   "fb_wall_ms_per_step": round(fb_wall / args.steps, 4)},
         "algorithmic_tflop_per_step": round((fwd_fl + bwd_fl) / 1e12, 4),
         "gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "roofline": roofline,

@@ -55,6 +55,20 @@ typedef int32_t moe_status;
 #define MOE_BASE_BF16 0          /* W13 / W2 in bf16 */
 #define MOE_BASE_MXFP4 1         /* W13 / W2 as e2m1 with e8m0 scales per 32 along K */
 
+/* Device status word of the saved workspace: the int32 at byte offset
+ * MOE_SAVED_STATUS_OFFSET of `saved`, cleared by every moe_lora_forward and
+ * raised by its kernels (read it after the forward, on the same stream).
+ *   MOE_SAVED_FP16_RANGE  the gate/up pre-activations g, v are saved in fp16
+ *     for the backward.  Without a clamp they must stay below 65504 in
+ *     magnitude; the bit is set when some |g| or |v| reached 65520 or more
+ *     (it rounds to infinity in fp16).  The forward's `out` is still right
+ *     (the activation uses the fp32 values) but a backward from this saved
+ *     state returns non-finite gradients.  With a clamp 0 < c < 65504 such
+ *     values are clipped to c like any other value beyond it, and the bit is
+ *     never set. */
+#define MOE_SAVED_STATUS_OFFSET 0
+#define MOE_SAVED_FP16_RANGE 1
+
 /* Shape and options of one layer call.
  *   T tokens, H hidden, I intermediate, E local experts, topk routes per token,
  *   rank r of the side adapters, scale s of the adapter deltas (0 => plain MoE).
@@ -155,9 +169,11 @@ moe_status moe_lora_pool_capacity(const moe_lora_desc* desc, int64_t* rows);
 
 /* Bytes of the two workspaces:
  *   saved   -- written by moe_lora_forward, read by moe_lora_backward; holds
- *              a copy of the layer input (the saved-X reuse of PR #9,
- *              "2026-09-20" -> What changed), the gate/up pre-activations in
- *              fp16 and the activations.
+ *              the status word (MOE_SAVED_STATUS_OFFSET), a copy of the layer
+ *              input (the saved-X reuse of PR #9, "2026-09-20" -> What
+ *              changed), the gate/up pre-activations in fp16 (|g|, |v| must
+ *              stay below 65504 without a clamp: MOE_SAVED_FP16_RANGE) and
+ *              the activations.
  *   scratch -- temporary space of moe_lora_forward and moe_lora_backward
  *              (nothing in it survives a call; both need the full size). */
 moe_status moe_lora_workspace_size(const moe_lora_desc* desc, size_t* saved_bytes,

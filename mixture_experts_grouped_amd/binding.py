@@ -23,6 +23,9 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0
 MOE_ACT_SWIGLU = 0
 MOE_ACT_GEGLU = 1
 MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
+# the saved workspace's device status word (include/moelora.h)
+MOE_SAVED_STATUS_OFFSET = 0
+MOE_SAVED_FP16_RANGE = 1
 
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
@@ -284,6 +287,13 @@ def moe_lora_backward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], grad_out
     _check(st, "moe_lora_backward")
 
 
+def _sync(stream) -> None:
+    if hasattr(stream, "synchronize"):
+        stream.synchronize()
+    else:
+        torch.cuda.synchronize()
+
+
 def moe_lora_trace_enable(on: bool) -> None:
     library().moe_lora_trace_enable(1 if on else 0)
 
@@ -309,10 +319,16 @@ class MoeLoraLayer:
     """Device buffers for one layer shape (pool arrays, workspaces, outputs)
     and the three calls in order.  Convenience for tests and the benchmark."""
 
-    def __init__(self, desc: MoeLoraDesc, device="cuda", base_grads: bool = False):
-        """base_grads: also compute the frozen-weight gradients dW13, dW2."""
+    def __init__(self, desc: MoeLoraDesc, device="cuda", base_grads: bool = False,
+                 checked: bool = False):
+        """base_grads: also compute the frozen-weight gradients dW13, dW2.
+        checked: after build_pool read the device error count and after the
+        forward the saved status word (each a device-to-host sync), and raise
+        if either reports a problem (route ids outside [-1, E), or a gate/up
+        pre-activation beyond the fp16 range the backward needs)."""
         self.desc = desc
         self.device = device
+        self.checked = checked
         self.block_m = moe_lora_block_m(desc)
         self.capacity = moe_lora_pool_capacity(desc)
         self.saved_bytes, self.scratch_bytes = moe_lora_workspace_size(desc)
@@ -346,9 +362,28 @@ class MoeLoraLayer:
     def build_pool(self, topk_idx: torch.Tensor, stream=None) -> None:
         build_pool(self.desc, topk_idx, self.pool["counts"], self.pool["offsets"],
                    self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
+        if self.checked:
+            bad = self.invalid_routes(stream)
+            if bad:
+                raise ValueError(f"build_pool: {bad} route id(s) outside [-1, {self.desc.E}) were dropped")
+
+    def invalid_routes(self, stream=None) -> int:
+        """Route ids outside [-1, E) dropped by the last build_pool (syncs)."""
+        _sync(stream)
+        return int(self.device_error.item())
+
+    def saved_status(self, stream=None) -> int:
+        """The saved workspace's status word after the last forward (syncs):
+        0, or MOE_SAVED_* bits."""
+        _sync(stream)
+        off = MOE_SAVED_STATUS_OFFSET
+        return int(self.saved[off:off + 4].view(torch.int32).item())
 
     def forward(self, x, topk_w, params, stream=None) -> torch.Tensor:
         moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, self.scratch, stream)
+        if self.checked and self.saved_status(stream) & MOE_SAVED_FP16_RANGE:
+            raise FloatingPointError("moe_lora_forward: a gate/up pre-activation is beyond the fp16 range "
+                                     "(|g| or |v| >= 65520) without a clamp; the backward would not be finite")
         return self.out
 
     def backward(self, grad_out, topk_w, params, stream=None):

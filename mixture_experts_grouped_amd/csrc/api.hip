@@ -20,6 +20,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 static_assert(MOE_ACT_SWIGLU == 0 && MOE_ACT_GEGLU == 1, "kernels take the activation as template 0 / 1");
+static_assert(MOE_SAVED_STATUS_OFFSET == 0, "the status word is the first field of the saved plan");
 
 moe_status check_desc(const moe_lora_desc* d) {
   if (d == nullptr) return MOE_ERR_INVALID;
@@ -62,7 +63,7 @@ struct Plan {
   int maxtiles, nsplit;
   size_t saved, scratch;
   // byte offsets
-  size_t o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
+  size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
@@ -76,6 +77,7 @@ Plan make_plan(const moe_lora_desc* d) {
   const size_t T = d->T, H = d->H, I = d->I, r = d->rank, cap = (size_t)p.cap;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
+  p.o_status = take(sizeof(int32_t));  // MOE_SAVED_STATUS_OFFSET
   p.o_tiles = take(sizeof(TileInfo) * p.maxtiles);
   p.o_ntiles = take(sizeof(int));
   p.o_Xs = take(T * H * 2);
@@ -180,6 +182,7 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
 
 void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   char* b = (char*)saved;
+  a.status = (int*)(b + p.o_status);
   a.tiles = (TileInfo*)(b + p.o_tiles);
   a.ntiles = (int*)(b + p.o_ntiles);
   a.Xs = (uint16_t*)(b + p.o_Xs);

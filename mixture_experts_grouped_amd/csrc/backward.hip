@@ -92,10 +92,7 @@ using GW2D = v2::Geo2<4, 2, 2, 4, false, true, 64>;  // 256 x 256, weights K-out
 constexpr int W2D_IMG = v2::TileImage<GW2D, GW2D::TN / 2, uint16_t>::BYTES;
 constexpr int W2D_LDS = cmax(GW2D::LDS_BYTES, 2 * W2D_IMG + GW2D::WN * GW2D::TM * 4);
 // Stages [0, next): the A2^T (s q) extension (rank-r K); then the base K = H.
-#ifndef DGRAD_PINGPONG
-#define DGRAD_PINGPONG 1
-#endif
-constexpr int PPW = DGRAD_PINGPONG ? 4 : 8;  // waves that queue a stage
+constexpr int PPW = 4;  // waves that queue a stage in the ping-pong loops (group A)
 
 template <int NWL>
 struct LdW2dBase {
@@ -107,18 +104,6 @@ struct LdW2dBase {
   KA mm;
   TL ne;
   int next;
-};
-struct LdW2d : LdW2dBase<GW2D::NW> {
-  v2::TLoadA<256, GW2D::KT, GW2D::NW> nm;
-  __device__ void issue(int s, char* sM, char* sN) {
-    if (s < next) {
-      me.issue(s * GW2D::KT, 0, false, sM);
-      ne.issue(s * GW2D::KT, sN);
-    } else {
-      mm.issue((s - next) * GW2D::KT, sM);
-      nm.issue((s - next) * GW2D::KT, sN);
-    }
-  }
 };
 // ping-pong form: the rank-space extension (K = 2r) runs first through the
 // plain pipeline (LdW2dExt), then the base K = H through the ping-pong loop
@@ -199,8 +184,6 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   static_assert(!(MX && TW), "transformed weights are bf16");
   extern __shared__ __align__(16) char smem[];
   using G = typename std::conditional<TW, GW2DK, GW2D>::type;
-  using LD = typename std::conditional<MX, LdW2dMX, LdW2d>::type;
-  using KL = typename LD::KL;
   const int ntn = a.I / G::TN;
   int mt, nt;
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
@@ -225,7 +208,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     L.ne.window(2 * r, r);  // k in [r, 2r) reads A2T column k - r again (lo half)
     L.nm.contig(a.W2T + (long)ti.e * a.I * a.H, i0, G::TN, a.H);
     v2::run_stages2<G, 0>(L, next + a.H / G::KT, acc, smem);
-  } else if constexpr (!MX && DGRAD_PINGPONG) {
+  } else if constexpr (!MX) {
     {
       LdW2dExt X;
       int tk[LdW2dExt::KL::NJ];
@@ -246,7 +229,9 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     Mn.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
     v2::run_pingpong<G>(Mn, a.H / G::KT, acc, smem);
   } else {
-    LD L;
+    // MXFP4 base: the W2 tile is register-staged and expanded to bf16 in LDS
+    LdW2dMX L;
+    using KL = LdW2dMX::KL;
     L.next = next;
     {
       int tk[KL::NJ];
@@ -258,10 +243,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
                            (uint32_t)(2 * a.I), 0, 2 * r, r};
     L.ne.cols(i0, G::TN);
-    if constexpr (MX)
-      L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
-    else
-      L.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
+    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
     v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
   }
   // G and V come in accumulator-blocked (as the forward wrote them); dg and
@@ -482,10 +464,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
     LdW13dK L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
     L.n.contig(a.W13T + (long)ti.e * a.H * 2 * a.I, h0, G::TN, 2 * a.I);
-    if constexpr (DGRAD_PINGPONG)
-      v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
-    else
-      v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+    v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
   } else {
     typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
@@ -494,7 +473,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
                2 * a.I, a.H, h0);
     else
       L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
-    if constexpr (!MX && DGRAD_PINGPONG)
+    if constexpr (!MX)
       v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
     else
       v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);

@@ -6,7 +6,7 @@
 //               A u is the same for all k routes of a token)
 //   k_w13       g = W1_e u + B1_e ZA1_t, v = W3_e u + B3_e ZA3_t; the B terms
 //               ride as extra K on the W13 GEMM; SwiGLU in the epilogue;
-//               saves G, V (fp32) and h (bf16)
+//               saves G, V (fp16, accumulator-blocked) and h (bf16)
 //   k_a2        Z2 = s A2_e h
 //   k_w2        Ybase = W2_e h
 //   k_zc        zc_t = sum_j w_tj Z2_(t,j)          (slot order, fp32)
@@ -15,6 +15,7 @@
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
 #include <type_traits>
 
+#include "../../include/moelora.h"
 #include "engine2.hpp"
 #include "gather_sum.hpp"
 #include "layer.hpp"
@@ -188,6 +189,12 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   constexpr int NH = G::NB / 2;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform block offsets
   const int wm = wv / G::WN, wn = wv % G::WN, lane = threadIdx.x & 63;
+  // Without a clamp a saved pre-activation must fit fp16: a finite value at
+  // or beyond 65520 rounds to infinity, which would turn the backward's
+  // gradients non-finite.  Such a forward raises MOE_SAVED_FP16_RANGE in the
+  // status word (h and the forward output are computed from the fp32 values
+  // and stay right).  With a clamp every such value is clipped anyway.
+  bool wide = false;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
@@ -207,6 +214,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float gq = gv[q], vq = vv[q];
+          if constexpr (!CL) wide |= fabsf(gq) >= 65520.0f || fabsf(vq) >= 65520.0f;
           if constexpr (CL) {
             if (fabsf((float)g16[q]) > a.clamp) gq = copysignf(a.clamp, gq);
             if (fabsf((float)v16[q]) > a.clamp) vq = copysignf(a.clamp, vq);
@@ -221,6 +229,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
         ImgH::put(smem, ep.row(mb), ep.col(nb, g), hv);
       }
     }
+  if (wide) *a.status = MOE_SAVED_FP16_RANGE;  // only ever 0 -> this bit: racing stores agree
   __syncthreads();
   ImgH::flush(smem, a.Hh + ti.row0 * (long)a.I + i0, a.I, nrows);
 }
@@ -265,12 +274,9 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
 
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
 constexpr int W2_LDS = cmax(GW2::LDS_BYTES, v2::TileImage<GW2, GW2::TN, uint16_t>::BYTES);
-#ifndef W2_PINGPONG
-#define W2_PINGPONG 1
-#endif
 struct LdW2 {
-  // with the ping-pong loop the four waves of group A queue a whole stage
-  using KL = v2::KLoadS<256, GW2::KT, W2_PINGPONG ? 4 : GW2::NW>;
+  // the ping-pong loop: the four waves of group A queue a whole stage
+  using KL = v2::KLoadS<256, GW2::KT, 4>;
   static constexpr int INSTS = 2 * KL::NJ;
   KL m, n;
   __device__ void issue(int s, char* sM, char* sN) {
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
     L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (!MX && W2_PINGPONG)
+  if constexpr (!MX)
     v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
   else
     v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);

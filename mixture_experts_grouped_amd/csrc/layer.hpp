@@ -53,6 +53,7 @@ struct LayerArgs {
   // transposed): W13T [E, H, 2I] = W13_e^T, W2T [E, I, H] = W2_e^T
   const uint16_t *W13T, *W2T;
   // saved by the forward
+  int* status;       // [1] status word at offset 0 of saved (MOE_SAVED_* bits)
   TileInfo* tiles;   // [maxtiles]
   int* ntiles;       // [1]
   uint16_t* Xs;      // [T, H]    copy of x for the backward (the W13 GEMM gathers x rows itself)

@@ -177,7 +177,10 @@ __global__ __launch_bounds__(64) void k_tile_map(LayerArgs a) {
     }
     carry += __shfl(x, 63, 64);
   }
-  if (lane == 0) *a.ntiles = carry;
+  if (lane == 0) {
+    *a.ntiles = carry;
+    *a.status = 0;  // raised again by this forward's kernels only
+  }
 }
 
 // Saved copy of the layer input for the backward (which is not given x):

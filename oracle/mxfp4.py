@@ -30,3 +30,83 @@ def dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     K = val.shape[-1]
     sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
     return (val.reshape(*val.shape[:-1], K // 32, 32) * sc[..., None]).reshape(val.shape)
+
+
+# --------------------------------------------------------------------------
+# Two-term FP8 (E4M3) split of activations, the operand form of a scaled
+# fp8 x fp4 matrix product whose activations must keep about bf16 precision.
+#
+# Sources: DeepGEMM PR #9, "Historical implementation" -> Summary (a native
+# MXFP4-base forward with BF16 side adapters: activations stay bf16) and
+# "Correctness coverage" (the two references: against the full-precision
+# layer, and a native-boundary reference that carries the kernel's declared
+# operand precision).  Element and scale formats: OCP MX v1.0 / OCP 8-bit
+# floating point: E4M3 with bias 7, no infinities, subnormals m/8 2^-6, the
+# largest finite value 448; E8M0 scales 2^(e-127).
+#
+# The split, per row and aligned block of 32 along the contraction axis:
+#   s1 = 2^E1, E1 the smallest integer with amax|x| <= 448 s1 (no element
+#        saturates; an all-zero block gets E1 = -127);
+#   q1 = E4M3(x / s1), rounded to nearest, ties to even;
+#   r  = x - s1 q1 (exact), and (s2, q2) from r the same way;
+#   x ~ s1 q1 + s2 q2, error at most max(2^-4 |r|, 2^-10 s2) per element,
+#   |r| at most max(2^-4 |x|, 2^-10 s1).
+# Which codes a value gets is an integer decision taken in floating point;
+# this is the precision the kernels declare for it, so the oracle decides
+# it the same way (exactly: every step above is exact in float64).
+# --------------------------------------------------------------------------
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of E4M3 codes (uint8); NaN for the two NaN codes."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Round |v| <= 448 to the nearest E4M3 code, ties to the even mantissa."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    assert np.all(a <= 448.0), "e4m3_round: value beyond the largest finite E4M3"
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    sub = a < 2.0 ** -6                                   # subnormal range: spacing 2^-9, as 2^-6's binade
+    e = np.where(sub, -6, ex.astype(np.int64) - 1)        # binade of a
+    n = np.rint(a * np.ldexp(1.0, 3 - e)).astype(np.int64)  # multiples of the spacing 2^(e-3), half to even
+    # subnormal: code = n (n == 8 is the smallest normal, code 0x08);
+    # normal binade e: n in [8, 16], n == 16 carries into the next binade
+    code = np.where(sub, n, ((e + 7) << 3) + (n - 8))
+    code = np.where(a == 0, 0, code)
+    return (code | np.where((v < 0) & (code != 0), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer E with amax <= 448 * 2^E (amax = 0: -127), clamped to
+    the E8M0 range [-127, 127]."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, ex = np.frexp(np.where(a > 0, a, 1.0))      # a = m 2^ex, m in [0.5, 1)
+    p = ex.astype(np.int64) - 1                      # a = (2m) 2^p, 2m in [1, 2)
+    e = np.where(2.0 * m <= 1.75, p - 8, p - 7)
+    return np.clip(np.where(a > 0, e, -127), -127, 127)
+
+
+def _split1(x):
+    blk = x.reshape(*x.shape[:-1], x.shape[-1] // 32, 32)
+    E = e4m3_scale_exponent(np.abs(blk).max(axis=-1))
+    q = e4m3_round(blk * np.ldexp(1.0, -E)[..., None])
+    val = e4m3_value(q) * np.ldexp(1.0, E)[..., None]
+    return q.reshape(x.shape), (E + 127).astype(np.uint8), val.reshape(x.shape)
+
+
+def split_e4m3x2(x):
+    """Two-term E4M3 split of x [..., K] (K % 32 == 0) along its last axis.
+    Returns (q1, s1, q2, s2, xhat): codes uint8 [..., K], E8M0 scale bytes
+    uint8 [..., K/32], and xhat = s1 q1 + s2 q2 (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % 32 == 0
+    q1, s1, v1 = _split1(x)
+    r = x - v1
+    q2, s2, v2 = _split1(r)
+    return q1, s1, q2, s2, v1 + v2

@@ -59,7 +59,7 @@ def test_unreached_clamp_is_bitwise_unclamped():
     a = Hn.GpuRun(shape, case, clamp=1.0e4).run()
     b = Hn.GpuRun(shape, case).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+        assert Hn.same_bits(a[k], b[k]), k
 
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu"])
@@ -71,7 +71,7 @@ def test_clamp_mxfp4_bitwise_vs_dequantised(act):
     a = Hn.GpuRun(shape, case, mx=mx, activation=act, clamp=1.0).run()
     b = Hn.GpuRun(shape, case_deq, activation=act, clamp=1.0).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+        assert Hn.same_bits(a[k], b[k]), k
 
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu"])
@@ -81,7 +81,7 @@ def test_clamp_transformed_base_bitwise(act):
     a = Hn.GpuRun(shape, case, activation=act, clamp=1.0, transformed=True).run()
     b = Hn.GpuRun(shape, case, activation=act, clamp=1.0).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+        assert Hn.same_bits(a[k], b[k]), k
 
 
 def test_clamp_with_frozen_weight_grads_against_oracle():

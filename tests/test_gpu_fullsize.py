@@ -3,16 +3,14 @@ H 4096, I 2048, rank 128, uniform routing), in the launch configuration the
 benchmark times (library-chosen BLOCK_M, the transformed base W13^T / W2^T
 given to the backward); the plain base layout must give the same bits.
 
-The oracle cannot run the whole layer in seconds, so it checks exactly
-computable samples:
-- tokens: out, grad_x and grad_w of a token depend only on that token's
-  routes, so the oracle runs on the sub-batch of sampled tokens (with just
-  their experts' weights) and must match those rows;
-- experts: dB1_e, dB3_e, dA2_e (and dW13_e, dW2_e, checked on one expert)
-  depend only on expert e's routes, so the oracle runs on the tokens routed
-  to e with every other route masked;
+Every output is compared with the oracle: out, grad_x and grad_w for all
+tokens, dB1 / dB3 / dA2 of every expert (as whole tensors and expert by
+expert), and dA1 / dA3 / dB2 over all 16,384 tokens (the full split-K depth
+of the shared-factor reductions).  The oracle runs one expert at a time
+(tests/harness.py oracle_by_expert: exact, the layer being a sum over routes).
+The optional frozen-weight gradients dW13 / dW2 are checked on two experts,
 and one identity over the whole output: sum_tj w_tj grad_w_tj = <grad_out,
-out> (the loss is linear in the weights' combine).
+out>.
 """
 import concurrent.futures as cf
 import os
@@ -27,80 +25,62 @@ pytestmark = pytest.mark.gpu
 
 SHAPE = I.PROD
 KEY = (2,)
-SAMPLE_TOKENS = (0, 1, 4097, 9999, 16383)
-SAMPLE_EXPERTS = (0, 37, 63)
+BASE_GRAD_EXPERTS = (0, 37)
+
+
+def production_case(shape, key):
+    threads = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(threads) as ex:
+        fut_e = [ex.submit(I.expert_weights, shape, key, e) for e in range(shape.E)]
+        fut_x = ex.submit(I.tokens, shape, key)
+        fut_g = ex.submit(I.grad_out, shape, key)
+        idx, w = I.route_balanced(shape, key)
+        shared = I.shared_weights(shape, key)
+        experts = [f.result() for f in fut_e]
+        case = {"x": fut_x.result(), "grad_out": fut_g.result(), "topk_idx": idx, "topk_w": w}
+    for n in Hn.LOCAL:
+        case[n] = np.stack([experts[e][n] for e in range(shape.E)])
+    case.update(shared)
+    return case
 
 
 @pytest.fixture(scope="module")
 def run():
     Hn.ensure_built()
-    threads = min(16, len(os.sched_getaffinity(0)))
-    with cf.ThreadPoolExecutor(threads) as ex:
-        fut_e = [ex.submit(I.expert_weights, SHAPE, KEY, e) for e in range(SHAPE.E)]
-        fut_x = ex.submit(I.tokens, SHAPE, KEY)
-        fut_g = ex.submit(I.grad_out, SHAPE, KEY)
-        idx, w = I.route_balanced(SHAPE, KEY)
-        shared = I.shared_weights(SHAPE, KEY)
-        experts = [f.result() for f in fut_e]
-        case = {"x": fut_x.result(), "grad_out": fut_g.result(), "topk_idx": idx, "topk_w": w}
-    for n in ("W13", "W2", "B1", "B3", "A2"):
-        case[n] = np.stack([experts[e][n] for e in range(SHAPE.E)])
-    del experts
-    case.update(shared)
+    case = production_case(SHAPE, KEY)
     Hn.log(f"[fullsize] inputs ready, shape={SHAPE}")
     res = Hn.GpuRun(SHAPE, case, base_grads=True, transformed=True).run()
     Hn.log("[fullsize] GPU step done")
     return case, res
 
 
+@pytest.fixture(scope="module")
+def ref(run):
+    case, _ = run
+    Hn.log("[fullsize] oracle, expert by expert")
+    return Hn.oracle_by_expert(case, SHAPE.scale)
+
+
+def test_every_output_matches_oracle(run, ref):
+    case, res = run
+    ref_out, ref_g = ref
+    Hn.compare_all(res, ref_out, ref_g, tag="prod:", per_expert=True)
+
+
 def test_plain_base_layout_gives_the_same_bits(run):
     case, res = run
     plain = Hn.GpuRun(SHAPE, case, base_grads=True).run()
     for k in res:
-        if k == "device_error":
-            continue
-        assert np.array_equal(np.asarray(res[k]).view(np.uint8), np.asarray(plain[k]).view(np.uint8)), k
+        assert Hn.same_bits(res[k], plain[k]), k
 
 
-def _sub_problem(case, tokens, only_expert=None):
-    """Inputs of the oracle restricted to `tokens` (and, with only_expert, to
-    that expert's routes), experts renumbered to the ones used."""
-    idx = case["topk_idx"][tokens].copy()
-    if only_expert is not None:
-        idx[idx != only_expert] = -1
-    used = np.unique(idx[idx >= 0])
-    remap = np.full(SHAPE.E, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    idx_s = np.where(idx >= 0, remap[np.maximum(idx, 0)], -1).astype(np.int32)
-    sub = {"x": case["x"][tokens], "grad_out": case["grad_out"][tokens], "topk_idx": idx_s,
-           "topk_w": case["topk_w"][tokens]}
-    for n in ("W13", "W2", "B1", "B3", "A2"):
-        sub[n] = case[n][used]
-    for n in ("A1", "A3", "B2"):
-        sub[n] = case[n]
-    return sub, used
-
-
-def test_sampled_tokens_match_oracle(run):
+@pytest.mark.parametrize("e", BASE_GRAD_EXPERTS)
+def test_frozen_weight_grads_match_oracle(run, e):
     case, res = run
-    toks = np.array(SAMPLE_TOKENS)
-    sub, _ = _sub_problem(case, toks)
-    ref_out, ref_g = Hn.oracle_run(sub, SHAPE.scale)
-    Hn.assert_close("out[sample]", Hn.f64(res["out"][toks]), ref_out)
-    Hn.assert_close("grad_x[sample]", Hn.f64(res["grad_x"][toks]), ref_g["grad_x"])
-    Hn.assert_close("grad_w[sample]", res["grad_w"][toks], ref_g["grad_w"])
-
-
-@pytest.mark.parametrize("e", SAMPLE_EXPERTS)
-def test_sampled_expert_adapter_grads_match_oracle(run, e):
-    case, res = run
-    toks = np.nonzero((case["topk_idx"] == e).any(axis=1))[0]
-    assert len(toks) == 1536  # uniform routing: exactly 1536 routes per expert, distinct tokens
-    sub, used = _sub_problem(case, toks, only_expert=e)
-    assert used.tolist() == [e]
-    base = e == SAMPLE_EXPERTS[1]  # the frozen-weight gradients on one expert
-    _, ref_g = Hn.oracle_run(sub, SHAPE.scale, base_grads=base)
-    for n in ("dB1", "dB3", "dA2") + (("dW13", "dW2") if base else ()):
+    sub, tt, _ = Hn.expert_sub(case, e)
+    assert len(tt) == 1536  # uniform routing: exactly 1536 routes per expert
+    _, ref_g = Hn.oracle_run(sub, SHAPE.scale, base_grads=True)
+    for n in ("dW13", "dW2"):
         Hn.assert_close(f"{n}[{e}]", Hn.f64(res[n][e]), ref_g[n][0])
 
 

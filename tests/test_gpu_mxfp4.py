@@ -45,7 +45,7 @@ def test_mxfp4_bitwise_vs_bf16_dequantised_and_oracle(name):
     res_mx = Hn.GpuRun(shape, case, mx=mx).run()
     res_bf = Hn.GpuRun(shape, case_deq).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(res_mx[k]).view(np.uint8), np.asarray(res_bf[k]).view(np.uint8)), \
+        assert Hn.same_bits(res_mx[k], res_bf[k]), \
             f"{name}:{k} MXFP4 differs from the bf16 path on the dequantised weights"
 
     ref_out, ref_g = Hn.oracle_run(case_deq, shape.scale)
@@ -53,63 +53,85 @@ def test_mxfp4_bitwise_vs_bf16_dequantised_and_oracle(name):
     Hn.log(f"[mxfp4] {name} " + " ".join(f"{k}={v['rel_l2']:.2e}" for k, v in rep.items()))
 
 
-def test_mxfp4_production_share_bitwise_vs_dequantised():
+def _quantised_expert(shape, key, e):
+    """Expert e's weights with W13 / W2 quantised to MXFP4: the packed bytes
+    and scales, and the dequantised weights as bf16 bits (exact)."""
+    from oracle import mxfp4 as OMX
+    w = I.expert_weights(shape, key, e)
+    out = {n: w[n] for n in ("B1", "B3", "A2")}
+    for n in ("W13", "W2"):
+        q, sc = I.mxfp4_quantize(I.bf16_bits_to_f32(w[n]))
+        out[n + "_q"], out[n + "_s"] = q, sc
+        out[n] = I.f32_to_bf16_bits(OMX.dequantize(q, sc).astype(np.float32))
+    return out
+
+
+def _mx_case(shape, key, idx, w, experts):
+    """Inputs for the experts in `experts` (MXFP4 base); the other experts
+    hold NaN bf16 weights and NaN e8m0 scales (0xFF), which no kernel may
+    read."""
+    import concurrent.futures as cf
+    import os
+    threads = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(threads) as ex:
+        fut = dict(zip(experts, ex.map(lambda e: _quantised_expert(shape, key, e), experts)))
+        fx, fg = ex.submit(I.tokens, shape, key), ex.submit(I.grad_out, shape, key)
+        case = {"x": fx.result(), "grad_out": fg.result(), "topk_idx": idx, "topk_w": w}
+    first = fut[experts[0]]
+    mx = {}
+    for n in ("W13", "W2", "B1", "B3", "A2"):
+        arr = np.full((shape.E, *first[n].shape), 0x7FC0, dtype=np.uint16)
+        for e, d in fut.items():
+            arr[e] = d[n]
+        case[n] = arr  # W13 / W2: the dequantised bf16 weights
+    for n in ("W13", "W2"):
+        q = np.zeros((shape.E, *first[n + "_q"].shape), np.uint8)
+        sc = np.full((shape.E, *first[n + "_s"].shape), 0xFF, np.uint8)
+        for e, d in fut.items():
+            q[e], sc[e] = d[n + "_q"], d[n + "_s"]
+        mx[n], mx[n + "_scale"] = q, sc
+    case.update(I.shared_weights(shape, key))
+    return case, mx
+
+
+def test_mxfp4_production_share():
     """The production share (16,384 tokens x top-6 over 64 experts, H 4096,
     I 2048, rank 128) with an MXFP4 base, in the benchmark's launch
     configuration: bitwise equal to the bf16 path on the dequantised weights,
-    and sampled tokens against the oracle on them."""
-    import concurrent.futures as cf
-    import os
-    from oracle import mxfp4 as OMX
-
+    and every output against the oracle on them (expert by expert)."""
     shape = I.PROD
     key = I.config_key(4)
-    threads = min(16, len(os.sched_getaffinity(0)))
-
-    def expert(e):
-        w = I.expert_weights(shape, key, e)
-        out = {n: w[n] for n in ("B1", "B3", "A2")}
-        for n in ("W13", "W2"):
-            q, sc = I.mxfp4_quantize(I.bf16_bits_to_f32(w[n]))
-            out[n + "_q"], out[n + "_s"] = q, sc
-            out[n] = I.f32_to_bf16_bits(OMX.dequantize(q, sc).astype(np.float32))
-        return out
-
-    with cf.ThreadPoolExecutor(threads) as ex:
-        ex_fut = ex.map(expert, range(shape.E))
-        fx, fg = ex.submit(I.tokens, shape, key), ex.submit(I.grad_out, shape, key)
-        experts = list(ex_fut)
-        case = {"x": fx.result(), "grad_out": fg.result()}
-    case["topk_idx"], case["topk_w"] = I.route_balanced(shape, key)
-    for n in ("W13", "W2", "B1", "B3", "A2"):
-        case[n] = np.stack([d[n] for d in experts])  # W13/W2: the dequantised bf16 weights
-    mx = {n: np.stack([d[n + "_q"] for d in experts]) for n in ("W13", "W2")}
-    mx.update({n + "_scale": np.stack([d[n + "_s"] for d in experts]) for n in ("W13", "W2")})
-    del experts
-    case.update(I.shared_weights(shape, key))
+    idx, w = I.route_balanced(shape, key)
+    case, mx = _mx_case(shape, key, idx, w, list(range(shape.E)))
     Hn.log("[mxfp4] production share: inputs ready")
-
     res_mx = Hn.GpuRun(shape, case, mx=mx).run()
     res_bf = Hn.GpuRun(shape, case).run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(res_mx[k]).view(np.uint8), np.asarray(res_bf[k]).view(np.uint8)), \
+        assert Hn.same_bits(res_mx[k], res_bf[k]), \
             f"production:{k} MXFP4 differs from the bf16 path on the dequantised weights"
+    del res_bf
+    Hn.log("[mxfp4] oracle, expert by expert")
+    ref_out, ref_g = Hn.oracle_by_expert(case, shape.scale)
+    Hn.compare_all(res_mx, ref_out, ref_g, tag="production:mx:", per_expert=True)
 
-    toks = np.array([0, 1, 4097, 9999, 16383])
-    idx = case["topk_idx"][toks]
-    used = np.unique(idx[idx >= 0])
-    remap = np.full(shape.E, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    sub = {"x": case["x"][toks], "grad_out": case["grad_out"][toks], "topk_w": case["topk_w"][toks],
-           "topk_idx": np.where(idx >= 0, remap[np.maximum(idx, 0)], -1).astype(np.int32)}
-    for n in ("W13", "W2", "B1", "B3", "A2"):
-        sub[n] = case[n][used]
-    for n in ("A1", "A3", "B2"):
-        sub[n] = case[n]
-    ref_out, ref_g = Hn.oracle_run(sub, shape.scale)
-    Hn.assert_close("production:mx:out[sample]", Hn.f64(res_mx["out"][toks]), ref_out)
-    Hn.assert_close("production:mx:grad_x[sample]", Hn.f64(res_mx["grad_x"][toks]), ref_g["grad_x"])
-    Hn.assert_close("production:mx:grad_w[sample]", res_mx["grad_w"][toks], ref_g["grad_w"])
+
+SWEEP_T = (1, 15, 16, 17, 90, 91, 176, 177, 346, 347, 688, 689, 1029, 1030, 2048)
+
+
+@pytest.mark.parametrize("T", SWEEP_T)
+def test_mxfp4_token_sweep_against_oracle(T):
+    """The fifteen token-sweep points (H 4096, I 2048, 64 experts, top-6,
+    rank 128, 20 % of routes dropped) with an MXFP4 base: every output
+    against the oracle on the dequantised weights."""
+    shape = I.sweep_shape(T)
+    key = I.config_key(1, T)
+    idx, w = I.route_softmax_topk(shape, key, mask_prob=0.2)
+    used = np.unique(idx[idx >= 0]).tolist()
+    case, mx = _mx_case(shape, key, idx, w, used)
+    Hn.log(f"[mxfp4 sweep] T={T} routes={int((idx >= 0).sum())} experts={len(used)}")
+    res = Hn.GpuRun(shape, case, mx=mx).run()
+    ref_out, ref_g = Hn.oracle_by_expert(case, shape.scale, log_every=0)
+    Hn.compare_all(res, ref_out, ref_g, tag=f"mx:T{T}:", per_expert=True)
 
 
 def test_mxfp4_geglu_bitwise_vs_dequantised():
@@ -122,6 +144,6 @@ def test_mxfp4_geglu_bitwise_vs_dequantised():
     res_mx = Hn.GpuRun(shape, case, mx=mx, activation="geglu").run()
     res_bf = Hn.GpuRun(shape, case_deq, activation="geglu").run()
     for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert np.array_equal(np.asarray(res_mx[k]).view(np.uint8), np.asarray(res_bf[k]).view(np.uint8)), k
+        assert Hn.same_bits(res_mx[k], res_bf[k]), k
     ref_out, ref_g = Hn.oracle_run(case_deq, shape.scale, act="geglu")
     Hn.compare_all(res_mx, ref_out, ref_g, tag="mx:geglu:")

@@ -63,5 +63,4 @@ def test_transformed_base_is_bitwise_the_same(name):
     keys = [k for k in plain if k != "device_error"]
     assert set(keys) <= set(tw)
     for k in keys:
-        a, b = np.asarray(plain[k]), np.asarray(tw[k])
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{name}:{k} differs with the transformed base"
+        assert Hn.same_bits(plain[k], tw[k]), f"{name}:{k} differs with the transformed base"
