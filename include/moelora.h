@@ -211,6 +211,25 @@ moe_status moe_lora_forward(const moe_lora_desc* desc, const moe_pool* pool, con
                             void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
                             void* stream);
 
+/* moe_lora_forward without a scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks and results as
+ * moe_lora_forward (bitwise); the forward's temporary tensors live instead in
+ * a device array inside the library, 64 MiB on every device the library runs
+ * on, held until the process ends.  The call allocates and frees nothing.
+ *   - A layer whose forward needs more than 64 MiB of scratch returns
+ *     MOE_ERR_WORKSPACE before any launch (the production share needs far
+ *     more: use moe_lora_forward there; the token-sweep shapes up to a few
+ *     hundred tokens fit).
+ *   - All calls on one device share that device's array: calls that overlap
+ *     on one device (different streams, concurrent threads) race.  Order them
+ *     on one stream.
+ *   - The first call on a device looks the array's address up (a HIP
+ *     symbol query, no allocation); failure returns MOE_ERR_HIP. */
+moe_status moe_lora_forward_noalloc(const moe_lora_desc* desc, const moe_pool* pool, const void* x,
+                                    const float* topk_w, const moe_lora_params* params, void* out,
+                                    void* saved, size_t saved_bytes, void* stream);
+
 /* Backward of the layer for L = <grad_out, out>.
  *   grad_out [T, H] bf16; topk_w and params as given to the forward; `saved`
  *   as the forward left it (read only, may be reused by repeated calls).

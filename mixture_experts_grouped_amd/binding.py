@@ -29,7 +29,7 @@ MOE_SAVED_FP16_RANGE = 1
 
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
-    "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_backward",
+    "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
     "moe_lora_transform_base", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
     "moe_lora_trace_entry", "moe_lora_trace_reset",
 )
@@ -94,6 +94,8 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.build_pool.argtypes = [P(MoeLoraDesc), vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp]
     lib.moe_lora_forward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
                                      vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_forward_noalloc.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
+                                             vp, ctypes.c_size_t, vp]
     lib.moe_lora_backward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
@@ -108,7 +110,8 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_trace_reset.argtypes = []
     lib.moe_lora_trace_reset.restype = None
     for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
-               "build_pool", "moe_lora_forward", "moe_lora_backward", "moe_lora_transform_base"):
+               "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
+               "moe_lora_transform_base"):
         getattr(lib, fn).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -261,6 +264,24 @@ def moe_lora_forward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], x: torch.
         saved.numel(), _ptr(scratch, torch.uint8, None, "scratch"),
         0 if scratch is None else scratch.numel(), _stream(stream))
     _check(st, "moe_lora_forward")
+
+
+def moe_lora_forward_noalloc(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], x: torch.Tensor,
+                             topk_w: torch.Tensor, params: Dict[str, torch.Tensor], out: torch.Tensor,
+                             saved: torch.Tensor, stream=None) -> None:
+    """moe_lora_forward with the library's own static scratch (no scratch
+    argument; the library allocates nothing).  Raises MoeLoraError
+    (MOE_ERR_WORKSPACE) when the layer needs more than the static array."""
+    T, H, k = desc.T, desc.H, desc.topk
+    bm = moe_lora_block_m(desc)
+    ps = _pool_struct(pool, bm)
+    pp = _params_struct(params, desc)
+    st = library().moe_lora_forward_noalloc(
+        ctypes.byref(desc), ctypes.byref(ps), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(pp),
+        _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(saved, torch.uint8, None, "saved"),
+        saved.numel(), _stream(stream))
+    _check(st, "moe_lora_forward_noalloc")
 
 
 def moe_lora_backward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], grad_out: torch.Tensor,

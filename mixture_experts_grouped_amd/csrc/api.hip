@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moelora.h"
 #include "layer.hpp"
@@ -61,7 +62,7 @@ int64_t capacity_of(const moe_lora_desc* d, int bm) {
 struct Plan {
   int64_t cap;
   int maxtiles, nsplit;
-  size_t saved, scratch;
+  size_t saved, scratch, fwd_scratch;
   // byte offsets
   size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
@@ -88,13 +89,16 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
   o = 0;
+  // the forward's scratch first (Pt, Yb in dU's space, Z2 in P's), so that
+  // it is one prefix of the plan: fwd_scratch bytes
   p.o_Pt = take(T * H * 4);  // used by the forward and the backward
+  p.o_dU = take(cap * H * 2);
+  p.o_P = take(cap * 2 * r * 4);
+  p.fwd_scratch = p.o_P + up(cap * r * 4);  // Z2 = the first cap * r floats of P
   p.o_q = take(T * r * 4);
   p.o_sq = take(T * 2 * r * 2);
   p.o_wsq = take(cap * 2 * r * 2);
   p.o_dGV = take(cap * 2 * I * 2);
-  p.o_dU = take(cap * H * 2);
-  p.o_P = take(cap * 2 * r * 4);
   p.o_pc = take(T * 4 * r * 2);
   p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
   p.o_ZAp = take(cap * 4 * r * 2);
@@ -193,8 +197,8 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   a.zc = (uint16_t*)(b + p.o_zc);
 }
 
-void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
-  char* b = (char*)scratch;
+void fill_scratch(LayerArgs& a, const Plan& p, void* base) {
+  char* b = (char*)base;
   a.q = (float*)(b + p.o_q);
   a.sq = (uint16_t*)(b + p.o_sq);
   a.wsq = (uint16_t*)(b + p.o_wsq);
@@ -211,6 +215,80 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* scratch) {
   a.A2T = (uint16_t*)(b + p.o_A2T);
   a.A1T = (uint16_t*)(b + p.o_A1T);
   a.A3T = (uint16_t*)(b + p.o_A3T);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward (moe_lora_forward_noalloc) keeps its scratch in
+// this file-scope device array.  Each device holds its own copy for the life
+// of the process; its address on a device comes from hipGetSymbolAddress,
+// taken once per device with that device current (in host code the array's
+// name is not a device address).  Calls on one device share the array, so
+// calls that overlap on one device race; nothing in it needs to start at
+// zero (the forward writes every scratch element it later reads).
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (looked up on its first use).
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The forward behind both entry points.  noalloc: the scratch is the static
+// array above (scratch / scratch_bytes are ignored); only the forward's part
+// of the plan is used there.
+moe_status forward_checked(const moe_lora_desc* d, const moe_pool* pool, const void* x, const float* topk_w,
+                           const moe_lora_params* params, void* out, void* saved, size_t saved_bytes,
+                           void* scratch_arg, size_t scratch_bytes, bool noalloc, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(d);
+  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
+  if ((st = check_params(d, params)) != MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
+    return MOE_ERR_INVALID;
+  if (saved_bytes < p.saved) return MOE_ERR_WORKSPACE;
+  const size_t act = (size_t)d->T * d->H * 2;
+  const Range rx = rng(x, act), ro = rng(out, act), rs = rng(saved, p.saved);
+  if (overlap(rx, ro) || overlap(ro, rs) || overlap(rx, rs)) return MOE_ERR_INVALID;
+  void* sc = scratch_arg;
+  if (noalloc) {
+    if (p.fwd_scratch > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+    const hipError_t e = scratch_address(&sc);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else {
+    if (!aligned16(scratch_arg) || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
+    const Range rsc = rng(scratch_arg, p.scratch);
+    if (overlap(rsc, rx) || overlap(rsc, ro) || overlap(rsc, rs)) return MOE_ERR_INVALID;
+  }
+  LayerArgs a;
+  fill_common(a, d, pool, p, params);
+  fill_saved(a, p, saved);
+  fill_scratch(a, p, sc);
+  a.x = (const uint16_t*)x;
+  a.w = topk_w;
+  a.out = (uint16_t*)out;
+  const hipError_t e = launch_forward(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // namespace
@@ -277,30 +355,14 @@ moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const 
                             const float* topk_w, const moe_lora_params* params, void* out,
                             void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
                             void* stream) {
-  moe_status st = check_desc(d);
-  if (st != MOE_OK) return st;
-  const Plan p = make_plan(d);
-  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
-  if ((st = check_params(d, params)) != MOE_OK) return st;
-  if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
-    return MOE_ERR_INVALID;
-  if (saved_bytes < p.saved) return MOE_ERR_WORKSPACE;
-  if (!aligned16(scratch) || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
-  const size_t act = (size_t)d->T * d->H * 2;
-  const Range rx = rng(x, act), ro = rng(out, act), rs = rng(saved, p.saved),
-              rsc = rng(scratch, p.scratch);
-  if (overlap(rx, ro) || overlap(ro, rs) || overlap(rx, rs) || overlap(rsc, rx) || overlap(rsc, ro) ||
-      overlap(rsc, rs))
-    return MOE_ERR_INVALID;
-  LayerArgs a;
-  fill_common(a, d, pool, p, params);
-  fill_saved(a, p, saved);
-  fill_scratch(a, p, scratch);
-  a.x = (const uint16_t*)x;
-  a.w = topk_w;
-  a.out = (uint16_t*)out;
-  const hipError_t e = launch_forward(a, (hipStream_t)stream);
-  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return forward_checked(d, pool, x, topk_w, params, out, saved, saved_bytes, scratch, scratch_bytes, false,
+                         stream);
+}
+
+moe_status moe_lora_forward_noalloc(const moe_lora_desc* d, const moe_pool* pool, const void* x,
+                                    const float* topk_w, const moe_lora_params* params, void* out,
+                                    void* saved, size_t saved_bytes, void* stream) {
+  return forward_checked(d, pool, x, topk_w, params, out, saved, saved_bytes, nullptr, 0, true, stream);
 }
 
 moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,

@@ -222,3 +222,30 @@ def test_activation_clamp_values_accepted(clamp):
     pre-activations (NaN is rejected, see test_desc_rejections)."""
     d = B.make_desc(256, 512, 256, 16, 2, 8, clamp=clamp)
     assert all(s > 0 for s in B.moe_lora_workspace_size(d))
+
+
+def test_noalloc_forward_rejects_layers_beyond_its_static_scratch():
+    """moe_lora_forward_noalloc keeps the forward's scratch in a 64 MiB
+    device array of the library; a layer that needs more (the production
+    share) is refused on the host before any device call, and so are the
+    argument errors moe_lora_forward refuses."""
+    lib = B.library()
+    byref = ctypes.byref
+    fake = 1 << 20
+    big = B.make_desc(16384, 4096, 2048, 64, 6, 128)
+    saved, _ = B.moe_lora_workspace_size(big)
+    cap = B.moe_lora_pool_capacity(big)
+    pool = B.MoePool(fake, fake, fake, fake, cap, 16)
+    prm = B.MoeLoraParams(*([fake] * 2 + [None, None] + [fake] * 6))
+    x, out, sv = fake, fake * 512, fake * 4096
+    assert lib.moe_lora_forward_noalloc(byref(big), byref(pool), x, fake, byref(prm), out, sv, saved,
+                                        None) == B.MOE_ERR_WORKSPACE
+    small = B.make_desc(64, 256, 256, 8, 2, 8)
+    s_saved, _ = B.moe_lora_workspace_size(small)
+    s_pool = B.MoePool(fake, fake, fake, fake, B.moe_lora_pool_capacity(small), 16)
+    assert lib.moe_lora_forward_noalloc(None, byref(s_pool), x, fake, byref(prm), out, sv, s_saved,
+                                        None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_forward_noalloc(byref(small), byref(s_pool), x + 2, fake, byref(prm), out, sv,
+                                        s_saved, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_forward_noalloc(byref(small), byref(s_pool), x, fake, byref(prm), out, sv,
+                                        s_saved - 1, None) == B.MOE_ERR_WORKSPACE
