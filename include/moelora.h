@@ -200,6 +200,25 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
 moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
                                    void* W2T, void* stream);
 
+/* Two-term FP8 (E4M3) split of bf16 rows, the activation operand of the
+ * MXFP4 base's scaled fp8 x fp4 matrix products (PR #9 "Historical
+ * implementation" -> Summary: native MXFP4 base with bf16 side adapters, the
+ * activations keeping bf16 precision).  moe_lora_forward runs it internally
+ * on x and on the activations h; this call exposes it alone.
+ *   src [rows, K] bf16 (K % 64 == 0, else MOE_ERR_UNSUPPORTED).
+ *   Per row and aligned 32-block: s1 = 2^E1 with E1 the smallest integer such
+ *   that max|x| <= 448 s1 (E1 = -127 for an all-zero block), q1 = E4M3(x/s1)
+ *   rounded to nearest even (OCP 8-bit float E4M3: bias 7, subnormals kept,
+ *   largest 448), r = x - s1 q1 (exact), (s2, q2) from r the same way;
+ *   x ~ s1 q1 + s2 q2 to about 2^-8 of each element.
+ *   codes [rows, 2K bytes]: per 64-element chunk c, 128 bytes =
+ *     [q1 of elements 64c .. 64c+63 | q2 of the same];
+ *   scale_words [rows, K/64] uint32: per chunk, bytes {E1+127 of its first
+ *     32-block, of its second, E2+127 of the first, of the second}.
+ *   src, codes 16-byte aligned, scale_words 4-byte aligned, no overlaps. */
+moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
+                                 void* stream);
+
 /* Forward of the layer.
  *   x [T, H] bf16, topk_w [T, k] fp32 router weights (used as given),
  *   out [T, H] bf16 (overwritten), saved / scratch per moe_lora_workspace_size

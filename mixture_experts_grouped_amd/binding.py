@@ -30,7 +30,7 @@ MOE_SAVED_FP16_RANGE = 1
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
     "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
-    "moe_lora_transform_base", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
+    "moe_lora_transform_base", "moe_lora_split_e4m3x2", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
     "moe_lora_trace_entry", "moe_lora_trace_reset",
 )
 
@@ -100,6 +100,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
     lib.moe_lora_transform_base.argtypes = [P(MoeLoraDesc), P(MoeLoraParams), vp, vp, vp]
+    lib.moe_lora_split_e4m3x2.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_lora_trace_enable.argtypes = [ctypes.c_int32]
     lib.moe_lora_trace_enable.restype = None
     lib.moe_lora_trace_collect.argtypes = []
@@ -111,7 +112,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_trace_reset.restype = None
     for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
                "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
-               "moe_lora_transform_base"):
+               "moe_lora_transform_base", "moe_lora_split_e4m3x2"):
         getattr(lib, fn).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -313,6 +314,21 @@ def _sync(stream) -> None:
         stream.synchronize()
     else:
         torch.cuda.synchronize()
+
+
+def moe_lora_split_e4m3x2(src: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Two-term E4M3 split of bf16 rows src [rows, K] (see include/moelora.h):
+    returns (codes uint8 [rows, 2K], scale words int32 [rows, K/64])."""
+    if src.dim() != 2:
+        raise ValueError("src must be [rows, K]")
+    rows, K = src.shape
+    codes = torch.empty(rows, 2 * K, dtype=torch.uint8, device=src.device)
+    scales = torch.empty(rows, K // 64, dtype=torch.int32, device=src.device)
+    st = library().moe_lora_split_e4m3x2(_ptr(src, torch.bfloat16, None, "src"), rows, K,
+                                         _ptr(codes, torch.uint8, None, "codes"),
+                                         _ptr(scales, torch.int32, None, "scale_words"), _stream(stream))
+    _check(st, "moe_lora_split_e4m3x2")
+    return codes, scales
 
 
 def moe_lora_trace_enable(on: bool) -> None:

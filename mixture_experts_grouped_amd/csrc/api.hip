@@ -65,6 +65,7 @@ struct Plan {
   size_t saved, scratch, fwd_scratch;
   // byte offsets
   size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
+  size_t o_XQ, o_XS, o_HQ, o_HS;
   size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
@@ -95,6 +96,14 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_dU = take(cap * H * 2);
   p.o_P = take(cap * 2 * r * 4);
   p.fwd_scratch = p.o_P + up(cap * r * 4);  // Z2 = the first cap * r floats of P
+  if (d->base_format == MOE_BASE_MXFP4) {
+    // the split activations of the two base GEMMs (forward only)
+    p.o_XQ = take(T * 2 * H);
+    p.o_XS = take(T * (H / 64) * 4);
+    p.o_HQ = take(cap * 2 * I);
+    p.o_HS = take(cap * (I / 64) * 4);
+    p.fwd_scratch = o;
+  }
   p.o_q = take(T * r * 4);
   p.o_sq = take(T * 2 * r * 2);
   p.o_wsq = take(cap * 2 * r * 2);
@@ -214,6 +223,12 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* base) {
   a.dwp = (float*)(b + p.o_dwp);
   a.A2T = (uint16_t*)(b + p.o_A2T);
   a.A1T = (uint16_t*)(b + p.o_A1T);
+  if (a.mx) {
+    a.XQ = (uint8_t*)(b + p.o_XQ);
+    a.XS = (uint32_t*)(b + p.o_XS);
+    a.HQ = (uint8_t*)(b + p.o_HQ);
+    a.HS = (uint32_t*)(b + p.o_HS);
+  }
   a.A3T = (uint16_t*)(b + p.o_A3T);
 }
 
@@ -409,6 +424,20 @@ moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
   a.dW13 = (uint16_t*)grads->dW13;
   a.dW2 = (uint16_t*)grads->dW2;
   const hipError_t e = launch_backward(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
+                                 void* stream) {
+  if (rows < 1 || K < 1) return MOE_ERR_INVALID;
+  if (K % 64 != 0 || rows * (int64_t)(K / 32) >= ((int64_t)1 << 31) * 256) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(codes) || scale_words == nullptr || ((uintptr_t)scale_words & 3u) != 0)
+    return MOE_ERR_INVALID;
+  const size_t nsrc = (size_t)rows * K * 2, nscale = (size_t)rows * (K / 64) * 4;
+  const Range rs = rng(src, nsrc), rc = rng(codes, nsrc), rw = rng(scale_words, nscale);
+  if (overlap(rs, rc) || overlap(rs, rw) || overlap(rc, rw)) return MOE_ERR_INVALID;
+  const hipError_t e = launch_split_rows((const uint16_t*)src, (long)rows, K, (uint8_t*)codes,
+                                         (uint32_t*)scale_words, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

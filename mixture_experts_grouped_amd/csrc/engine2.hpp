@@ -363,11 +363,12 @@ struct TLoadA {
 // ---------------------------------------------------------------------------
 // MXFP4 weights (OCP MX v1.0): e2m1 elements, two per byte with element 2i in
 // the low nibble of byte i, and one e8m0 scale per 32 elements along the
-// weight's own K axis (the forward contraction axis).  The loaders read the
-// packed bytes into registers when a stage is queued and, after the stage
-// before it has been multiplied, expand them to bf16 into the same LDS layout
-// the bf16 loaders produce: e2m1 x 2^(e-127) is exact in bf16, so the
-// matrix-core path is the bf16 one.
+// weight's own K axis (the forward contraction axis).  The data-gradient
+// GEMMs contract the other axis, so the backward reads the packed bytes into
+// registers when a stage is queued and, after the stage before it has been
+// multiplied, expands them to bf16 into the T-tile layout the bf16 loaders
+// produce (e2m1 x 2^(e-127) is exact in bf16).  The forward runs on the
+// scaled matrix cores instead (engine_mx.hpp).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float e8m0_value(uint32_t e) {
   // 2^(e-127); e = 0 is the denormal 2^-127
@@ -388,38 +389,6 @@ __device__ __forceinline__ uint32_t bload_u8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0), others untouched
 }
-
-// K tile of R = NT/2 weight rows x 64 k from MXFP4: thread t takes row t/2,
-// k half t%2 (32 values = 16 bytes and their one scale).
-template <int R, int NT>
-struct KLoadMX {
-  static_assert(NT == 2 * R, "two threads per weight row");
-  rsrc_t rq, rs;         // packed values, scales
-  uint32_t qoff, soff;   // this thread's row: byte offsets at k = 0
-  u32x4 q[2];            // staged values, two stages (buffer = stage parity)
-  uint32_t e[2];         // staged scales
-  // weight row `row` (absolute) of a [*, K] MXFP4 matrix
-  __device__ __forceinline__ void set(const uint8_t* q_base, const uint8_t* s_base, long nrows, long K,
-                                      int row) {
-    rq = make_rsrc(q_base, (uint64_t)nrows * (K / 2));
-    rs = make_rsrc(s_base, (uint64_t)nrows * (K / 32));
-    qoff = (uint32_t)(row * (K / 2)) + 16u * (threadIdx.x & 1);
-    soff = (uint32_t)(row * (K / 32)) + (threadIdx.x & 1);
-  }
-  template <int B = 0>
-  __device__ __forceinline__ void issue(int k0) {
-    q[B] = bload(rq, qoff + (uint32_t)(k0 / 2));
-    e[B] = bload_u8(rs, soff + (uint32_t)(k0 / 32));
-  }
-  // expand buffer B into the K tile (the compiler waits for exactly its loads)
-  template <int B = 0>
-  __device__ __forceinline__ void finish(char* tile) const {
-    const float sc = e8m0_value(e[B]);
-    const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *(u32x4*)(tile + koff<64>(row, 4 * h + c)) = fp4x8_bf16(q[B][c], sc);
-  }
-};
 
 // T tile of 256 columns x 64 k-rows from an MXFP4 matrix stored [K rows][N]
 // with N the packed axis: thread t takes k-row t/8 and columns 32 (t%8) ..
@@ -483,9 +452,8 @@ __device__ __forceinline__ void wait_vm() {
 // caller has already waited for the loads the next stage needs.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-// Loaders with register-staged operands either provide finish(stage, sN),
-// run one stage ahead by step2, or declare MXI and run two stages ahead by
-// step_mx.
+// Loaders with a register-staged operand provide finish(stage, sN) and run
+// one stage ahead by step2.
 template <class T, class = void>
 struct HasFinish {
   static constexpr bool value = false;
@@ -494,15 +462,6 @@ template <class T>
 struct HasFinish<T, decltype((void)&T::finish)> {
   static constexpr bool value = true;
 };
-template <class T, class = void>
-struct HasMX {
-  static constexpr bool value = false;
-};
-template <class T>
-struct HasMX<T, decltype((void)T::MXI)> {
-  static constexpr bool value = true;
-};
-
 // One pipeline step: wait for stage s, release the buffer stage s - 1 used,
 // queue stage s + NBUF - 1 into it, multiply stage s.
 template <class G, bool SPLIT, class L>
@@ -531,47 +490,6 @@ __device__ __forceinline__ void step2(L& ld, int s, int nst, f32x16 (&acc)[G::NB
       wait_lgkm0();  // the next step's barrier publishes the expanded tile
     }
   }
-}
-
-// Loaders with MXI split a stage into
-// issue_dma(s, sM, sN) (its direct loads), issue_mx<B>(t) (the register loads
-// of stage t into buffer B = t & 1) and finish<B>(t, sN) (expand buffer B into
-// stage t's N tile); mx(t) tells whether stage t has such an operand.  The
-// register loads run two stages ahead of their expansion: step s queues the
-// direct loads of stage s + 1, then the register loads of stage s + 2, and
-// after its MFMAs expands stage s + 1 (loaded during step s - 1).  P = s & 1.
-template <class G, bool SPLIT, int P, class L>
-__device__ __forceinline__ void step_mx(L& ld, int s, int nst, f32x16 (&acc)[G::NB][G::MB],
-                                        char* smem, int wm, int wn, int lane) {
-  static_assert(G::NBUF == 2, "register-staged operands expand one stage ahead");
-  // stage s's direct loads were queued before the register loads of stage s + 1
-  if (s + 1 < nst && ld.mx(s + 1))
-    wait_vm<L::MXI>();
-  else
-    wait_vm<0>();
-  bar();
-  char* nxt = smem + ((s + 1) & 1) * G::STAGE;
-  if (s + 1 < nst) {
-    ld.issue_dma(s + 1, nxt, nxt + G::SM_BYTES);
-    if (s + 2 < nst && ld.mx(s + 2)) ld.template issue_mx<P>(s + 2);
-  }
-  const char* sM = smem + (s & 1) * G::STAGE;
-  mma_stage2<G, SPLIT>(sM, sM + G::SM_BYTES, acc, wm, wn, lane);
-  if (s + 1 < nst && ld.mx(s + 1)) {
-    ld.template finish<1 - P>(s + 1, nxt + G::SM_BYTES);
-    wait_lgkm0();  // the next step's barrier publishes the expanded tile
-  }
-}
-
-template <class G, bool SPLIT, class L>
-__device__ __forceinline__ void steps_mx(L& ld, int& s, int end, int nst, f32x16 (&acc)[G::NB][G::MB],
-                                         char* smem, int wm, int wn, int lane) {
-  if (s < end && (s & 1)) step_mx<G, SPLIT, 1>(ld, s++, nst, acc, smem, wm, wn, lane);
-  for (; s + 1 < end; s += 2) {
-    step_mx<G, SPLIT, 0>(ld, s, nst, acc, smem, wm, wn, lane);
-    step_mx<G, SPLIT, 1>(ld, s + 1, nst, acc, smem, wm, wn, lane);
-  }
-  if (s < end) step_mx<G, SPLIT, 0>(ld, s++, nst, acc, smem, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,18 +596,7 @@ __device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / G::WN, wn = w % G::WN;
   constexpr int NBUF = G::NBUF;
-  if constexpr (HasMX<L>::value) {
-    if (ld.mx(0)) ld.template issue_mx<0>(0);
-    ld.issue_dma(0, smem, smem + G::SM_BYTES);
-    if (nst > 1 && ld.mx(1)) ld.template issue_mx<1>(1);
-    if (ld.mx(0)) {
-      ld.template finish<0>(0, smem + G::SM_BYTES);
-      wait_lgkm0();
-    }
-    int s = 0;
-    if constexpr (SPLIT == 2) steps_mx<G, true>(ld, s, ld.nsplit < nst ? ld.nsplit : nst, nst, acc, smem, wm, wn, lane);
-    steps_mx<G, SPLIT == 1>(ld, s, nst, nst, acc, smem, wm, wn, lane);
-  } else {
+  {
 #pragma unroll
     for (int p = 0; p < NBUF - 1; ++p)
       if (p < nst) ld.issue(p, smem + p * G::STAGE, smem + p * G::STAGE + G::SM_BYTES);

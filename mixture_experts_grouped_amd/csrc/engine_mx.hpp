@@ -1,0 +1,290 @@
+// engine_mx.hpp -- MXFP4-base GEMM stages on gfx950's scaled matrix cores.
+//
+// The base weights are OCP MX v1.0 FP4 (E2M1, two per byte, element 2i in
+// the low nibble of byte i) with one E8M0 scale per 32 along K; the
+// activations are held as a two-term FP8 (E4M3) split with one E8M0 scale
+// per term and 32-block: x ~ s1 q1 + s2 q2 (split_block below).  Each k64
+// step is two v_mfma_scale_f32_32x32x64_f8f6f4 per output block (one per
+// term, weights as the fp4 first operand), accumulating into the same fp32
+// 32 x 32 accumulators as the bf16 engine, with the same lane layout: lanes
+// own output rows, registers four consecutive output columns.
+//
+// Operand lane layouts of the scaled instruction (probed on the device):
+//   fp4 operand: lane l holds row l % 32, k = 32 (l / 32) .. + 31 (16 bytes,
+//                low nibble first); its scale is that 32-block's;
+//   fp8 operand: lane l holds row l % 32, elements 0-15 at k = 16 (l / 32) ..
+//                and elements 16-31 at k = 32 + 16 (l / 32) ..; the scale the
+//                lane supplies is that of k-block l / 32;
+//   the op_sel field picks the scale byte of the 32-bit scale register.
+//
+// Storage (per row, per 64-k chunk c of the contraction):
+//   activation codes   128 bytes: [hi codes k 64c..64c+63 | lo codes ...],
+//                      i.e. the row pitch of a bf16 row, so the bf16 K-tile
+//                      loader (KLoadA / KLoadS) and its swizzle carry it;
+//   activation scales  one 32-bit word: bytes {hi b0, hi b1, lo b0, lo b1}
+//                      for the chunk's two 32-blocks;
+//   weight codes       32 bytes at 32c of the packed row;
+//   weight scales      byte 2c + b of the row's scale bytes.
+//
+// One stage = one k64 step: LDS [A 256 x 128 B | W 256 x 32 B | A scales
+// 256 x 4 B | W scales 256 x 4 B] = 42 KB, three stages in LDS (two in
+// flight while one is multiplied).  Each wave issues the same number of
+// direct-to-LDS loads per stage (INSTS), so one vmcnt wait per stage covers
+// the stage it is about to read.
+#pragma once
+#include "engine2.hpp"
+
+namespace moelora {
+namespace mx {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int TM = 256, TN = 256, NT = 512, NW = 8;
+constexpr int A_BYTES = TM * 128, W_BYTES = TN * 32, AS_BYTES = TM * 4, WS_BYTES = TN * 4;
+constexpr int STAGE = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;  // 43008
+constexpr int NBUF = 3;
+constexpr int LDS_BYTES = NBUF * STAGE;
+using KA = v2::KLoadA<TM, 64, NW>;  // activation rows: 128 bytes per stage, bf16-shaped
+using KS = v2::KLoadS<TM, 64, NW>;
+static_assert(KA::NJ == 4 && KS::NJ == 4, "four 1 KB activation loads per wave and stage");
+constexpr int INSTS = KA::NJ + 1 + 1;  // activation rows, weight rows, one scale word row
+
+// ---------------------------------------------------------------------------
+// Two-term E4M3 split of one aligned 32-block (values exactly bf16, in fp32).
+// s = 2^E with E the smallest integer such that amax <= 448 2^E (no element
+// saturates; amax = 0 or below 2^-126 gives E = -127), q = E4M3(x / s) to
+// nearest even (v_cvt_pk_fp8_f32, subnormals kept), r = x - s q exactly, and
+// the same again on r.  Scale bytes are E + 127.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int field = (int)(b >> 23);  // amax >= 0
+  if (field == 0) return -127;       // zero or subnormal
+  const int p = field - 127;
+  const int e = ((b & 0x7FFFFFu) <= 0x600000u) ? p - 8 : p - 7;  // mantissa 1.75 or less: p - 8
+  return e < -127 ? -127 : e;
+}
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-127, 127]
+  return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// 32 values -> 8 words of codes (byte j of word w = element 4w + j) and the
+// scale byte; also returns the residual x - s q in place of x.
+__device__ __forceinline__ uint32_t quant_term(float (&v)[32], uint32_t (&q)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int E = e4m3_scale_exp(amax);
+  const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, -E <= 127
+  const float s = pow2f(E);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t c = 0;
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w] * inv, v[4 * w + 1] * inv, c, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, c, true);
+    q[w] = c;
+    v[4 * w] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 0), s, v[4 * w]);
+    v[4 * w + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 1), s, v[4 * w + 1]);
+    v[4 * w + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 2), s, v[4 * w + 2]);
+    v[4 * w + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 3), s, v[4 * w + 3]);
+  }
+  return (uint32_t)(E + 127);
+}
+
+// Rows of a bf16 [*, K] matrix -> codes [*, 2K bytes] and scale words
+// [*, K/64]; one thread per (row, 32-block), threads of one row adjacent.
+// GATHERED: the rows are pool rows of the layer (`rows` pool rows, only real
+// ones -- row_to_route >= 0 below offsets[E] -- are written).
+template <bool POOL>
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
+                                                    uint32_t* __restrict__ scales, long nrows, int K,
+                                                    const int32_t* __restrict__ row2r,
+                                                    const int32_t* __restrict__ pool_end) {
+  const int bpr = K / 32;  // blocks per row (even: K % 256 == 0)
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = i / bpr;
+  const int j = (int)(i - row * bpr);
+  bool live = row < nrows;
+  if (POOL && live) live = row < (long)*pool_end && row2r[row] >= 0;
+  float v[32];
+  if (live) {
+    const u32x4* p = (const u32x4*)(src + row * (long)K + 32 * j);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = p[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[8 * c + 2 * q] = bf2f(w[q] & 0xffffu);
+        v[8 * c + 2 * q + 1] = bf2f(w[q] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v[c] = 0.0f;
+  }
+  uint32_t hi[8], lo[8];
+  const uint32_t s1 = quant_term(v, hi);
+  const uint32_t s2 = quant_term(v, lo);
+  // partner block of the same 64-chunk (j ^ 1) sits in the neighbouring lane
+  const uint32_t o1 = __shfl_xor(s1, 1, 64), o2 = __shfl_xor(s2, 1, 64);
+  if (!live) return;
+  uint8_t* base = codes + row * (long)(2 * K) + 128 * (j >> 1) + 32 * (j & 1);
+  *(u32x4*)(base) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  *(u32x4*)(base + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+  *(u32x4*)(base + 64) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  *(u32x4*)(base + 80) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  if ((j & 1) == 0) scales[row * (long)(K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
+}
+
+// ---------------------------------------------------------------------------
+// Stage loader.  Activation rows through KA/KS (set by the caller: 256 tile
+// rows, 128 bytes a stage), the weight tile and the two scale rows here.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_load4(rsrc_t rs, char* lds_wave_base, uint32_t off, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (v2::lds_void*)lds_wave_base, 4, off, soff, 0, 0);
+}
+
+struct WLoad {
+  rsrc_t rq, rs;     // packed weights (row pitch K/2 bytes), scale bytes (row pitch K/32)
+  uint32_t qoff;     // this lane's weight-tile slot: row 32 w + L/2, logical 16-byte chunk
+  rsrc_t ra;         // activation scale words
+  uint32_t soff;     // this lane's scale word (waves 0-3: activation rows, 4-7: weight rows)
+  // tile row n of the weight tile reads packed row wrow(n); tile rows of the
+  // activation side read scale-word row aoff(row) (byte offset of the row's
+  // word 0, OFF_NONE for no row)
+  template <class WROW, class AOFF>
+  __device__ __forceinline__ void set(const uint8_t* wq, const uint8_t* ws, long wrows, int K, WROW wrow,
+                                      const uint32_t* as, long arows, AOFF aoff) {
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    rq = make_rsrc(wq, (uint64_t)wrows * (K / 2));
+    rs = make_rsrc(ws, (uint64_t)wrows * (K / 32));
+    ra = make_rsrc(as, (uint64_t)arows * (K / 64) * 4);
+    const int n = 32 * w + (L >> 1);
+    const int lc = (L & 1) ^ ((n >> 3) & 1);
+    qoff = (uint32_t)wrow(n) * (uint32_t)(K / 2) + 16u * (uint32_t)lc;
+    if (w < 4)
+      soff = aoff(64 * w + L);
+    else
+      soff = (uint32_t)wrow(64 * (w - 4) + L) * (uint32_t)(K / 32);
+  }
+  // queue stage s (k = 64 s) into the stage buffer `st`
+  __device__ __forceinline__ void issue(int s, char* st) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    v2::lds_load16(rq, st + A_BYTES + 1024 * w, qoff, 32u * (uint32_t)s);
+    if (w < 4)
+      lds_load4(ra, st + A_BYTES + W_BYTES + 256 * w, soff, 4u * (uint32_t)s);
+    else
+      lds_load4(rs, st + A_BYTES + W_BYTES + AS_BYTES + 256 * (w - 4), soff, 4u * (uint32_t)(s >> 1));
+  }
+};
+
+// One k64 step from stage buffer `st` (stage index s: which half of the
+// weight scale word).  G: the bf16 geometry whose accumulator layout the
+// caller keeps (eight waves, 4 x 2 blocks of 32 x 32 per wave).
+template <class G>
+__device__ __forceinline__ void mma_mx(const char* st, int s, f32x16 (&acc)[G::NB][G::MB], int wm, int wn,
+                                       int lane) {
+  static_assert(G::TM == TM && G::TN == TN && G::NW == NW, "256 x 256 tile, eight waves");
+  const int h = lane >> 5, r = lane & 31;
+  const char* sA = st;
+  const char* sW = st + A_BYTES;
+  const uint32_t* sAs = (const uint32_t*)(st + A_BYTES + W_BYTES);
+  const uint32_t* sWs = (const uint32_t*)(st + A_BYTES + W_BYTES + AS_BYTES);
+  i32x8 wf[G::NB];
+  int ws[G::NB];
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb) {
+    const int n = G::n_local(wn, nb) + r;
+    const u32x4 q = *(const u32x4*)(sW + n * 32 + 16 * (h ^ ((n >> 3) & 1)));
+    wf[nb] = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+    ws[nb] = (int)(sWs[n] >> (8 * (2 * (s & 1) + h)));
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int row = G::m_local(wm, mb) + r;
+      const u32x4 a0 = *(const u32x4*)(sA + v2::koff<64>(row, 4 * t + h));
+      const u32x4 a1 = *(const u32x4*)(sA + v2::koff<64>(row, 4 * t + 2 + h));
+      const i32x8 xf = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      const int xs = (int)(sAs[row] >> (8 * (2 * t + h)));
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[nb], xf, acc[nb][mb], 4 /* first: fp4 */,
+                                                                      0 /* second: fp8 */, 0, ws[nb], 0, xs);
+    }
+}
+
+// Geometry of the low-rank extension stages that may precede the base K
+// range in the same pipeline (bf16, 32 k a stage: M and N tiles of 16 KB each
+// inside one stage buffer, the two halves of the N tile contracting the two
+// halves of the stage's k -- the SPLIT stages of the bf16 engine).
+using GE = v2::Geo2<4, 2, 2, 4, false, false, 32>;
+static_assert(GE::STAGE <= STAGE, "an extension stage fits a stage buffer");
+using KE = v2::KLoad<TM, 32, NW>;
+using KE2 = v2::KLoad<TM, 32, NW, true>;
+constexpr int EXT_INSTS = 2 * KE::NJ;
+
+// One extension stage (GE: 32 k, two k16 steps; the gate blocks contract the
+// first, the up blocks the second), fragments read just before their MFMAs.
+template <class G>
+__device__ __forceinline__ void mma_ext(const char* st, f32x16 (&acc)[G::NB][G::MB], int wm, int wn, int lane) {
+  const char* sM = st;
+  const char* sN = st + GE::SM_BYTES;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 b[G::MB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) b[mb] = v2::frag<false, GE::TM, 32>(sM, G::m_local(wm, mb), kk, lane);
+#pragma unroll
+    for (int nb = kk * (G::NB / 2); nb < (kk + 1) * (G::NB / 2); ++nb) {
+      const bf16x8 a = v2::frag<false, GE::TN, 32>(sN, G::n_local(wn, nb), kk, lane);
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+}
+
+// The base K range, nst k64 stages (ld.issue(s, buffer)), then -- in a loop
+// of its own, so that each loop keeps one fragment schedule -- next
+// extension stages (ld.issue_ext(s, buffer), bf16).  Three buffers, two
+// stages in flight.  Ends with a workgroup barrier (LDS free for the
+// epilogue).
+template <class G, class L>
+__device__ __forceinline__ void run_mx(const L& ld, int next, int nst, f32x16 (&acc)[G::NB][G::MB], char* smem) {
+  static_assert(GE::MB == G::MB && GE::NB == G::NB && GE::WM == G::WM && GE::WN == G::WN, "same accumulators");
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = w / G::WN, wn = w % G::WN;
+  if (nst > 0) {
+    ld.issue(0, smem);
+    if (nst > 1) ld.issue(1, smem + STAGE);
+    for (int s = 0; s < nst; ++s) {
+      if (s + 1 < nst)
+        v2::wait_vm<INSTS>();
+      else
+        v2::wait_vm<0>();
+      v2::bar();
+      if (s + 2 < nst) ld.issue(s + 2, smem + ((s + 2) % NBUF) * STAGE);
+      mma_mx<G>(smem + (s % NBUF) * STAGE, s, acc, wm, wn, lane);
+    }
+    __syncthreads();
+  }
+  if (next > 0) {
+    ld.issue_ext(0, smem);
+    if (next > 1) ld.issue_ext(1, smem + STAGE);
+    for (int s = 0; s < next; ++s) {
+      if (s + 1 < next)
+        v2::wait_vm<EXT_INSTS>();
+      else
+        v2::wait_vm<0>();
+      v2::bar();
+      if (s + 2 < next) ld.issue_ext(s + 2, smem + ((s + 2) % NBUF) * STAGE);
+      mma_ext<G>(smem + (s % NBUF) * STAGE, acc, wm, wn, lane);
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace mx
+}  // namespace moelora

@@ -17,6 +17,7 @@
 
 #include "../../include/moelora.h"
 #include "engine2.hpp"
+#include "engine_mx.hpp"
 #include "gather_sum.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
@@ -83,23 +84,18 @@ using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight w
 constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, uint16_t>::BYTES);
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
-// stage); stages [nsplit, ...): the base K = H.  With an MXFP4 base the W13
-// tile is register-staged and expanded to bf16 (finish), its loads queued two
-// stages ahead (step_mx): one stage ahead leaves their latency exposed here
-// (4.0 vs 3.5 ms at T = 16384, H = 4096, I = 2048, E = 64, k = 6), while the
-// backward's MX kernels run 5-8% slower two ahead (register pressure).
+// stage); stages [nsplit, ...): the base K = H.
 struct LdW13Base {
   using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
   using KL2 = v2::KLoad<256, GW13::KT, GW13::NW, true>;
   using KA = v2::KLoadA<256, GW13::KT, GW13::NW>;
-  static constexpr int INSTS = 2 * KL::NJ;
   KL me;
   KL2 ne;
-  KA mm;
   int r, nsplit;
 };
 struct LdW13 : LdW13Base {
-  KA nm;
+  static constexpr int INSTS = 2 * KL::NJ;
+  KA mm, nm;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < nsplit) {
       me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
@@ -110,23 +106,29 @@ struct LdW13 : LdW13Base {
     }
   }
 };
-struct LdW13MX : LdW13Base {
-  static constexpr int MXI = 2;  // register loads per stage (values, scales)
-  v2::KLoadMX<256, GW13::NT> nq;
-  __device__ bool mx(int t) const { return t >= nsplit; }
-  __device__ void issue_dma(int s, char* sM, char* sN) {
-    if (s < nsplit) {
-      me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
-      ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
-    } else {
-      mm.issue((s - nsplit) * GW13::KT, sM);
-    }
+// MXFP4 base (engine_mx.hpp): the split activation rows (x by token, or h
+// by pool row), the packed weight tile and the scale rows of each k64
+// stage; with an extension (W13), its 32-k bf16 stages run first in the same
+// pipeline.
+struct LdMX {
+  mx::KA xa;
+  mx::WLoad wl;
+  __device__ void issue(int s, char* st) const {
+    xa.issue(64 * s, st);
+    wl.issue(s, st);
   }
-  template <int B>
-  __device__ void issue_mx(int t) { nq.template issue<B>((t - nsplit) * GW13::KT); }
-  template <int B>
-  __device__ void finish(int, char* sN) const { nq.template finish<B>(sN); }
+  __device__ void issue_ext(int, char*) const {}  // no extension stages (next = 0)
 };
+struct LdW13MX : LdMX {
+  mx::KE me;   // s A1 x, s A3 x (hi/lo) by token
+  mx::KE2 ne;  // B1 rows (gate half of the tile), B3 rows (up half)
+  int r;
+  __device__ void issue_ext(int s, char* st) const {
+    me.issue(s * 16, 2 * r, true, st);
+    ne.issue(s * 16, 2 * r, true, st + mx::GE::SM_BYTES);
+  }
+};
+static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipeline's LDS");
 
 // ACT: 0 SwiGLU (h = silu(g) v), 1 GeGLU (h = gelu(g) v, exact GELU).
 // CL: activation clamp, h = f(clip(g)) clip(v) with clip to [-a.clamp, a.clamp]
@@ -147,40 +149,53 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   const int e = ti.e, i0 = nt * HALF;
   const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
-  typename std::conditional<MX, LdW13MX, LdW13>::type L;
-  L.r = r;
-  L.nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
-  {
-    // the tile's rows are gathered from x (and ZA) by token: rows past the
-    // expert's count read zero
-    int tk[KL::NJ];
-    KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
-    L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
-    L.mm.from_tokens(a.x, a.T, a.H, tk);
-  }
-  L.me.window(4 * r);
-  L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-  L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-#pragma unroll
-  for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
-  L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
-  if constexpr (MX) {
-    const int nl = threadIdx.x >> 1;  // this thread's W13 tile row
-    const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
-    L.nq.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2 * a.I,
-             a.H, wrow);
-  } else {
-    L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
-#pragma unroll
-    for (int j = 0; j < KL::NJ; ++j) {
-      const int nl = KL::row_of(j);
-      const int wrow = (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF);
-      L.nm.set_row(j, (uint32_t)((long)wrow * a.H * 2));
-    }
-  }
+  const int nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
+  int tk[KL::NJ];  // the tile's rows are gathered by token: rows past the expert's count read zero
+  KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  auto wrow = [&](int nl) { return (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF); };
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  v2::run_stages2<G, 2>(L, L.nsplit + a.H / G::KT, acc, smem);
+  if constexpr (!MX) {
+    LdW13 L;
+    L.r = r;
+    L.nsplit = nsplit;
+    L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
+    L.me.window(4 * r);
+    L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+#pragma unroll
+    for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
+    L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
+    L.mm.from_tokens(a.x, a.T, a.H, tk);
+    L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+#pragma unroll
+    for (int j = 0; j < KL::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KL::row_of(j)) * a.H * 2));
+    v2::run_stages2<G, 2>(L, nsplit + a.H / G::KT, acc, smem);
+  } else {
+    // extension stages of 32 k (16 of the gate's 2r, 16 of the up's), then
+    // the base K range as k64 stages on the scaled matrix cores
+    using KE = mx::KE;
+    LdW13MX L;
+    L.r = r;
+    {
+      int tke[KE::NJ];
+      KE::tokens(tke, a.row2r, a.k, ti.row0, nrows);
+      L.me.from_tokens(a.ZA, a.T, 4 * r, tke);
+    }
+    L.me.window(4 * r);
+    L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+#pragma unroll
+    for (int j = 0; j < KE::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KE::row_of(j) % HALF)) * r * 2);
+    L.ne.window(2 * r, r, HALF, 2 * r);
+    L.xa.from_tokens((const uint16_t*)a.XQ, a.T, a.H, tk);  // 2H bytes a row, like a bf16 row
+    const uint32_t sbytes = (uint32_t)(a.H / 64) * 4u;
+    L.wl.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2L * a.I, a.H, wrow,
+             a.XS, a.T, [&](int row) {
+               return row < nrows ? (uint32_t)(a.row2r[ti.row0 + row] / a.k) * sbytes : OFF_NONE;
+             });
+    mx::run_mx<G>(L, (2 * r + 15) / 16, a.H / 64, acc, smem);
+  }
   // G and V go out as fp16 in the accumulator-blocked layout (512 bytes per
   // wave access);
   // h (bf16, row-major for the next GEMM) through an LDS image of the tile
@@ -284,17 +299,6 @@ struct LdW2 {
     n.issue(s * GW2::KT, sN);
   }
 };
-struct LdW2MX {
-  using KL = v2::KLoadA<256, GW2::KT, GW2::NW>;
-  static constexpr int INSTS = KL::NJ;
-  KL m;
-  v2::KLoadMX<256, GW2::NT> nq;
-  __device__ void issue(int s, char* sM, char* sN) {
-    m.issue(s * GW2::KT, sM);
-    nq.issue(s * GW2::KT);
-  }
-  __device__ void finish(int, char* sN) const { nq.finish(sN); }
-};
 
 template <bool MX>
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
@@ -305,19 +309,24 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
-  typename std::conditional<MX, LdW2MX, LdW2>::type L;
-  L.m.contig(a.Hh, ti.row0, ti.row_end - ti.row0, a.I);
-  if constexpr (MX)
-    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I,
-             h0 + (threadIdx.x >> 1));
-  else
-    L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
+  const int nrows = ti.row_end - ti.row0;
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (!MX)
+  if constexpr (!MX) {
+    LdW2 L;
+    L.m.contig(a.Hh, ti.row0, nrows, a.I);
+    L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
     v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
-  else
-    v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  } else {
+    // MXFP4 base: h as its two-term split, W2 packed, on the scaled matrix cores
+    LdMX N;
+    N.xa.contig((const uint16_t*)a.HQ, ti.row0, nrows, a.I);  // 2I bytes a row, like a bf16 row
+    const uint32_t sbytes = (uint32_t)(a.I / 64) * 4u;
+    N.wl.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), (long)a.H, a.I,
+             [&](int n) { return h0 + n; }, a.HS + (long)ti.row0 * (a.I / 64), (long)(nrows < G::TM ? nrows : G::TM),
+             [&](int row) { return row < nrows ? (uint32_t)row * sbytes : OFF_NONE; });
+    mx::run_mx<G>(N, 0, a.I / 64, acc, smem);
+  }
   using Img = v2::TileImage<G, G::TN, uint16_t>;
   Epi<G> ep;
 #pragma unroll
@@ -412,6 +421,14 @@ static void set_w13_lds(AttrInit& ai) {
   ai.lds((const void*)k_w13<MX, 1, true>, W13_LDS);
 }
 
+hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
+                             hipStream_t st) {
+  const long n = rows * (K / 32);
+  MOE_LAUNCH_AS("k_quant_rows", mx::k_quant_rows<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                codes, scales, rows, K, nullptr, nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   static PerDeviceOnce attrs;
   hipError_t err = attrs.run([] {
@@ -430,6 +447,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   const int tm = (a.T + GS64::TM - 1) / GS64::TM;
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);
+  if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
+    const long n = (long)a.T * (a.H / 32);
+    MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
+                  a.XQ, a.XS, (long)a.T, a.H, nullptr, nullptr);
+  }
   {
     const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
     if (a.mx && a.act == 1)
@@ -440,6 +462,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
       launch_w13_cl<false, 1>(a, grid, st);
     else
       launch_w13_cl<false, 0>(a, grid, st);
+  }
+  if (a.mx) {  // h as its two-term E4M3 split for the scaled W2 GEMM (real pool rows)
+    const long n = a.cap * (a.I / 32);
+    MOE_LAUNCH_AS("k_quant_h", mx::k_quant_rows<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.Hh,
+                  a.HQ, a.HS, a.cap, a.I, a.row2r, a.offsets + a.E);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)

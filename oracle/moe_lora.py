@@ -41,6 +41,17 @@ Readings taken where the pages are silent:
      kernels keep the pre-activations between forward and backward); the
      clipped and unclipped values themselves stay exact.
 
+  8. the MXFP4 base's native boundary (PR #9 "Historical implementation" ->
+     Correctness coverage compares against both a full-precision reference
+     and a native-boundary one): with act_split="e4m3x2" the activations
+     entering the two base products -- u into W1/W3, h into W2 -- are
+     replaced by their two-term E4M3 split (oracle/mxfp4.py split_e4m3x2,
+     blocks of 32 along the contraction axis), the precision in which the
+     kernels feed them to the scaled fp8 x fp4 matrix instruction; the
+     low-rank paths (A1 u, A3 u, A2 h) and every other product keep the exact
+     values, and the backward treats the split as the identity (it is
+     piecewise constant; the kernels' data gradients are the plain ones).
+
 Arithmetic: float64 numpy on the exact values of the bf16 inputs; per-route
 evaluation, one loop over experts.  No blocking or regrouping of the shared
 factors (the kernels evaluate shared terms per token; this oracle does not).
@@ -111,8 +122,17 @@ def _clip(a: np.ndarray, c: float, decide):
 _DECIDE = {None: None, "fp16": lambda a: a.astype(np.float16).astype(np.float64)}
 
 
+def _split(a: np.ndarray, act_split) -> np.ndarray:
+    """The activations a base product sees (reading 8)."""
+    if act_split is None:
+        return a
+    assert act_split == "e4m3x2", act_split
+    from .mxfp4 import split_e4m3x2
+    return split_e4m3x2(a)[4]
+
+
 def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float,
-                   act: str = "swiglu", clamp: float = np.inf, clamp_decide=None):
+                   act: str = "swiglu", clamp: float = np.inf, clamp_decide=None, act_split=None):
     """One expert on a batch of its routes' inputs u [n, H].
 
     g = W1_e u + s B1_e (A1 u);  v = W3_e u + s B3_e (A3 u);
@@ -124,19 +144,21 @@ def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float
     W3 = p["W13"][e, I:]
     a1u = u @ p["A1"].T
     a3u = u @ p["A3"].T
-    g = u @ W1.T + scale * (a1u @ p["B1"][e].T)
-    v = u @ W3.T + scale * (a3u @ p["B3"][e].T)
+    ub = _split(u, act_split)
+    g = ub @ W1.T + scale * (a1u @ p["B1"][e].T)
+    v = ub @ W3.T + scale * (a3u @ p["B3"][e].T)
     gc, gout = _clip(g, clamp, _DECIDE[clamp_decide])
     vc, vout = _clip(v, clamp, _DECIDE[clamp_decide])
     h = ACTIVATIONS[act][0](gc) * vc
     a2h = h @ p["A2"][e].T
-    y = h @ p["W2"][e].T + scale * (a2h @ p["B2"].T)
+    y = _split(h, act_split) @ p["W2"][e].T + scale * (a2h @ p["B2"].T)
     return {"a1u": a1u, "a3u": a3u, "g": g, "v": v, "gc": gc, "vc": vc, "gout": gout, "vout": vout,
             "h": h, "a2h": a2h, "y": y}
 
 
 def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
-            keep: bool = False, act: str = "swiglu", clamp: float = np.inf, clamp_decide=None):
+            keep: bool = False, act: str = "swiglu", clamp: float = np.inf, clamp_decide=None,
+            act_split=None):
     """out [T, H] = sum over unmasked slots j of w[t, j] * y_(t, j).
 
     With ``keep`` also returns per-route values Y [T, k, H], G/V/Hh [T, k, I]
@@ -157,7 +179,7 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
         tt, jj = _expert_routes(idx, e)
         if len(tt) == 0:
             continue
-        f = expert_forward(x[tt], e, p, scale, act, clamp, clamp_decide)
+        f = expert_forward(x[tt], e, p, scale, act, clamp, clamp_decide, act_split)
         Y[tt, jj] = f["y"]
         if keep:
             G[tt, jj] = f["g"]
@@ -173,7 +195,7 @@ def forward(x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
 
 def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale: float,
              base_grads: bool = False, act: str = "swiglu", clamp: float = np.inf,
-             clamp_decide=None) -> Dict[str, np.ndarray]:
+             clamp_decide=None, act_split=None) -> Dict[str, np.ndarray]:
     """Gradients of L = <grad_out, out> with respect to x, the router weights
     and the six adapter factors (and, with ``base_grads``, W13 and W2).
 
@@ -215,7 +237,7 @@ def backward(grad_out, x, topk_idx, topk_w, params: Dict[str, np.ndarray], scale
         if len(tt) == 0:
             continue
         u = x[tt]
-        f = expert_forward(u, e, p, s, act, clamp, clamp_decide)
+        f = expert_forward(u, e, p, s, act, clamp, clamp_decide, act_split)
         fa, fa_grad = ACTIVATIONS[act]
         gw[tt, jj] = np.sum(go[tt] * f["y"], axis=1)
         dy = w[tt, jj][:, None] * go[tt]
@@ -256,11 +278,11 @@ def params_f64(arrs: Dict[str, np.ndarray], widen=None) -> Dict[str, np.ndarray]
 
 def forward_backward(x, topk_idx, topk_w, params, scale, grad_out,
                      base_grads: bool = False, keep: bool = False, act: str = "swiglu",
-                     clamp: float = np.inf, clamp_decide=None):
+                     clamp: float = np.inf, clamp_decide=None, act_split=None):
     fwd = forward(x, topk_idx, topk_w, params, scale, keep=keep, act=act, clamp=clamp,
-                  clamp_decide=clamp_decide)
+                  clamp_decide=clamp_decide, act_split=act_split)
     bwd = backward(grad_out, x, topk_idx, topk_w, params, scale, base_grads=base_grads, act=act,
-                   clamp=clamp, clamp_decide=clamp_decide)
+                   clamp=clamp, clamp_decide=clamp_decide, act_split=act_split)
     if keep:
         out, inter = fwd
         return out, bwd, inter

@@ -67,7 +67,10 @@ def e4m3_value(code) -> np.ndarray:
 
 
 def e4m3_round(v) -> np.ndarray:
-    """Round |v| <= 448 to the nearest E4M3 code, ties to the even mantissa."""
+    """Round |v| <= 448 to the nearest E4M3 code, ties to the even mantissa.
+    The rounding acts on the magnitude and the sign bit is the value's own
+    (IEEE-style sign-magnitude): a negative value that rounds to zero, and
+    -0, encode as -0 (0x80)."""
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     assert np.all(a <= 448.0), "e4m3_round: value beyond the largest finite E4M3"
@@ -79,7 +82,7 @@ def e4m3_round(v) -> np.ndarray:
     # normal binade e: n in [8, 16], n == 16 carries into the next binade
     code = np.where(sub, n, ((e + 7) << 3) + (n - 8))
     code = np.where(a == 0, 0, code)
-    return (code | np.where((v < 0) & (code != 0), 0x80, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
 def e4m3_scale_exponent(amax) -> np.ndarray:

@@ -52,7 +52,7 @@ def f64(bits: np.ndarray) -> np.ndarray:
     return I.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def metrics(got, ref, elem_scale: float = 1.0) -> Dict[str, float]:
+def metrics(got, ref, elem_scale: float = 1.0, elem_allow: float = 0.0) -> Dict[str, float]:
     """cos, relative L2 and max |got - ref| (float64), plus "elem": the
     largest |got - ref| / (ELEM_REL |ref| + ELEM_RMS scale(ref)) (times
     elem_scale; scale = the larger of the row and column rms), which the
@@ -76,6 +76,8 @@ def metrics(got, ref, elem_scale: float = 1.0) -> Dict[str, float]:
         with np.errstate(divide="ignore", invalid="ignore"):
             q = np.where(dd == 0, 0.0, dd / tol)  # 0 / 0 passes, x / 0 fails
         out["elem"] = float(np.max(q))
+        if elem_allow > 0:
+            out["elem_frac"] = float(np.mean(q > 1.0))
         if nr > 0:
             out["max_abs_over_rms"] = float(out["max_abs"] / (nr / np.sqrt(r.size)))
     else:
@@ -83,12 +85,14 @@ def metrics(got, ref, elem_scale: float = 1.0) -> Dict[str, float]:
     return out
 
 
-def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX, quiet=False):
+def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX, quiet=False, elem_allow: float = 0.0):
     """Per-tensor gates (cosine, relative L2) and the element-wise gate,
     whose two terms scale with rel_max (a looser tensor gate, e.g. for an
     MXFP4 base, loosens the element gate alike).  An all-zero reference
-    needs an all-zero result."""
-    m = metrics(got, ref, elem_scale=rel_max / REL_MAX)
+    needs an all-zero result.  elem_allow > 0: that fraction of the elements
+    may exceed the element gate (for results with legitimately flipped
+    integer decisions; the callers say why)."""
+    m = metrics(got, ref, elem_scale=rel_max / REL_MAX, elem_allow=elem_allow)
     ref = np.asarray(ref)
     if not quiet:
         log(f"  {name}: cos={m['cos']:.9f} rel_l2={m['rel_l2']:.3e} max_abs={m['max_abs']:.3e} "
@@ -97,20 +101,23 @@ def assert_close(name, got, ref, cos_min=COS_MIN, rel_max=REL_MAX, quiet=False):
         assert not np.any(np.asarray(got)), f"{name}: reference is zero, kernel is not"
         return m
     assert m["cos"] >= cos_min and m["rel_l2"] <= rel_max, f"{name}: {m}"
-    assert m["elem"] <= 1.0, f"{name}: element-wise gate: {m}"
+    if elem_allow > 0:
+        assert m["elem_frac"] <= elem_allow, f"{name}: element-wise gate: {m}"
+    else:
+        assert m["elem"] <= 1.0, f"{name}: element-wise gate: {m}"
     return m
 
 
 def oracle_run(case: Dict[str, np.ndarray], scale: float, base_grads: bool = False, act: str = "swiglu",
-               clamp: float = np.inf, clamp_decide=None):
+               clamp: float = np.inf, clamp_decide=None, act_split=None):
     from oracle import moe_lora as OM
     x = f64(case["x"])
     go = f64(case["grad_out"])
     p = {n: f64(case[n]) for n in PARAMS}
     out = OM.forward(x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale, act=act, clamp=clamp,
-                     clamp_decide=clamp_decide)
+                     clamp_decide=clamp_decide, act_split=act_split)
     g = OM.backward(go, x, case["topk_idx"], case["topk_w"].astype(np.float64), p, scale,
-                    base_grads=base_grads, act=act, clamp=clamp, clamp_decide=clamp_decide)
+                    base_grads=base_grads, act=act, clamp=clamp, clamp_decide=clamp_decide, act_split=act_split)
     return out, g
 
 
@@ -265,23 +272,24 @@ def mxfp4_base(case: Dict[str, np.ndarray]):
     return mx, deq
 
 
-def compare_all(res, ref_out, ref_g, tag="", per_expert: bool = False, rel_max=REL_MAX):
+def compare_all(res, ref_out, ref_g, tag="", per_expert: bool = False, rel_max=REL_MAX, elem_allow: float = 0.0):
     """Every output against the oracle: out, grad_x, grad_w and the six
     adapter gradients (per_expert: also each expert's slice of dB1 / dB3 /
     dA2 on its own, so one expert's fault cannot hide in the others' norm).
     The forward's status word must be clear."""
     assert res.get("saved_status", 0) == 0, f"{tag}saved status {res.get('saved_status')}"
     report = {}
-    report["out"] = assert_close(tag + "out", f64(res["out"]), ref_out, rel_max=rel_max)
-    report["grad_x"] = assert_close(tag + "grad_x", f64(res["grad_x"]), ref_g["grad_x"], rel_max=rel_max)
-    report["grad_w"] = assert_close(tag + "grad_w", res["grad_w"], ref_g["grad_w"], rel_max=rel_max)
+    kw = {"rel_max": rel_max, "elem_allow": elem_allow}
+    report["out"] = assert_close(tag + "out", f64(res["out"]), ref_out, **kw)
+    report["grad_x"] = assert_close(tag + "grad_x", f64(res["grad_x"]), ref_g["grad_x"], **kw)
+    report["grad_w"] = assert_close(tag + "grad_w", res["grad_w"], ref_g["grad_w"], **kw)
     for n in GRAD_NAMES:
-        report[n] = assert_close(tag + n, f64(res[n]), ref_g[n], rel_max=rel_max)
+        report[n] = assert_close(tag + n, f64(res[n]), ref_g[n], **kw)
     if per_expert:
         worst = {}
         for n in ("dB1", "dB3", "dA2"):
             for e in range(ref_g[n].shape[0]):
-                m = assert_close(f"{tag}{n}[{e}]", f64(res[n][e]), ref_g[n][e], rel_max=rel_max, quiet=True)
+                m = assert_close(f"{tag}{n}[{e}]", f64(res[n][e]), ref_g[n][e], quiet=True, **kw)
                 if m["rel_l2"] >= worst.get(n, (-1.0, None))[0]:
                     worst[n] = (m["rel_l2"], e, m)
         for n, (_, e, m) in worst.items():

@@ -7,7 +7,7 @@ reading 7): GPU parity.
   these N(0, 1)-scaled inputs), and the clamped results differ from the
   unclamped ones;
 - a clamp no value reaches gives bitwise the unclamped results;
-- MXFP4 base with the clamp: bitwise the bf16 path on the dequantised weights;
+- MXFP4 base with the clamp: against the native-boundary oracle;
 - transformed base with the clamp: bitwise the plain layout.
 """
 import numpy as np
@@ -63,15 +63,31 @@ def test_unreached_clamp_is_bitwise_unclamped():
 
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu"])
-def test_clamp_mxfp4_bitwise_vs_dequantised(act):
+def test_clamp_mxfp4_against_native_oracle(act):
+    """MXFP4 base with the clamp: against the oracle on the dequantised
+    weights with the kernels' activation split on the two base products
+    (the native boundary) and the fp16 clip decision.
+
+    The scaled matrix instruction adds its products with about 2^-16 of
+    their magnitude sum (measured), so the kernel's g and v sit about 1e-4
+    from the oracle's; the clip decisions of the values that close to +-c
+    (about 1e-4 of them at c = 1) can come out the other way, each an O(1)
+    change of one dg or dv and of the gradient terms built from it.  The
+    tensor gates hold as everywhere; in the gradients the element gate may be
+    exceeded by at most 1 % of the elements -- the flips and the gradient
+    rows they feed, far fewer than a tile or an expert (which a real fault
+    would hit).  The clip is continuous in the forward, so the output keeps
+    the strict element gate."""
     shape, key, mask = CASES["r128_masked"]
     case = I.layer_inputs(shape, key, mask_prob=mask)
     mx, deq = Hn.mxfp4_base(case)
     case_deq = dict(case, W13=deq["W13"], W2=deq["W2"])
-    a = Hn.GpuRun(shape, case, mx=mx, activation=act, clamp=1.0).run()
-    b = Hn.GpuRun(shape, case_deq, activation=act, clamp=1.0).run()
-    for k in ("out", "grad_x", "grad_w", *Hn.GRAD_NAMES):
-        assert Hn.same_bits(a[k], b[k]), k
+    res = Hn.GpuRun(shape, case, mx=mx, activation=act, clamp=1.0).run()
+    ref_out, ref_g = Hn.oracle_run(case_deq, shape.scale, act=act, clamp=1.0, clamp_decide="fp16",
+                                   act_split="e4m3x2")
+    Hn.compare_all(res, ref_out, ref_g, tag=f"mx:{act}:clamp:", elem_allow=1e-2)
+    # the clip is continuous in the forward: the output meets the element gate
+    Hn.assert_close(f"mx:{act}:clamp:out(strict)", Hn.f64(res["out"]), ref_out)
 
 
 @pytest.mark.parametrize("act", ["swiglu", "geglu"])

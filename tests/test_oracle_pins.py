@@ -91,10 +91,10 @@ MUTANTS = {
                          "W3 = p[\"W13\"][e, :I]\n    W1 = p[\"W13\"][e, I:]\n    a1u")],
     "silu_grad_wrong": [("return sg * (1.0 + g * (1.0 - sg))", "return sg")],
     "silu_wrong_sign": [("return 1.0 / (1.0 + np.exp(-g))", "return 1.0 / (1.0 + np.exp(g))")],
-    "drop_B1_term": [("g = u @ W1.T + scale * (a1u @ p[\"B1\"][e].T)", "g = u @ W1.T")],
+    "drop_B1_term": [("g = ub @ W1.T + scale * (a1u @ p[\"B1\"][e].T)", "g = ub @ W1.T")],
     "A1_for_up_path": [("a3u = u @ p[\"A3\"].T", "a3u = u @ p[\"A1\"].T")],
-    "scale_on_shared_only": [("y = h @ p[\"W2\"][e].T + scale * (a2h @ p[\"B2\"].T)",
-                              "y = h @ p[\"W2\"][e].T + (a2h @ p[\"B2\"].T)")],
+    "scale_on_shared_only": [("y = _split(h, act_split) @ p[\"W2\"][e].T + scale * (a2h @ p[\"B2\"].T)",
+                              "y = _split(h, act_split) @ p[\"W2\"][e].T + (a2h @ p[\"B2\"].T)")],
     "router_weight_squared": [("out += w[:, j:j + 1] * Y[:, j]", "out += w[:, j:j + 1] ** 2 * Y[:, j]")],
     "router_grad_sign": [("gw[tt, jj] = np.sum(go[tt] * f[\"y\"], axis=1)",
                           "gw[tt, jj] = -np.sum(go[tt] * f[\"y\"], axis=1)")],

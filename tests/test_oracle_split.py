@@ -29,7 +29,7 @@ def _nearest(v):
     if len(best) > 1:
         best = best[(best & 1) == 0]
     c = int(best[0])
-    return c | (0x80 if (v < 0 and c != 0) else 0)
+    return c | (0x80 if np.signbit(v) else 0)  # the sign is kept, also on a zero result
 
 
 def test_rounding_matches_exhaustive_search_with_ties_to_even():
@@ -37,7 +37,8 @@ def test_rounding_matches_exhaustive_search_with_ties_to_even():
     mids = (vals[1:] + vals[:-1]) / 2  # every tie between neighbours
     rng = np.random.default_rng(3)
     rand = rng.uniform(0, 448, 3000) * np.exp2(-rng.integers(0, 18, 3000))
-    vs = np.concatenate([vals, mids, rand, -mids, -rand])
+    tiny = np.array([0.0, -0.0, 2.0 ** -11, -2.0 ** -11, 2.0 ** -10, -2.0 ** -10, 3 * 2.0 ** -11])
+    vs = np.concatenate([vals, mids, rand, -mids, -rand, tiny])
     got = M.e4m3_round(vs)
     ref = np.array([_nearest(v) for v in vs], dtype=np.uint8)
     assert np.array_equal(got, ref)
@@ -82,3 +83,36 @@ def test_split_error_bound_and_exact_cases():
 def test_round_refuses_values_beyond_448(bad):
     with pytest.raises(AssertionError):
         M.e4m3_round(np.array([bad]))
+
+
+def _layer_case(seed=9):
+    rng = np.random.default_rng(seed)
+    T, H, I, E, k, r = 24, 64, 32, 3, 2, 4
+    p = {"W13": rng.standard_normal((E, 2 * I, H)) / 8, "W2": rng.standard_normal((E, H, I)) / 6,
+         "A1": rng.standard_normal((r, H)) / 8, "A3": rng.standard_normal((r, H)) / 8,
+         "B1": rng.standard_normal((E, I, r)) * 0.14, "B3": rng.standard_normal((E, I, r)) * 0.14,
+         "A2": rng.standard_normal((E, r, I)) / 6, "B2": rng.standard_normal((H, r)) * 0.14}
+    x = rng.standard_normal((T, H))
+    go = rng.standard_normal((T, H))
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    w = rng.random((T, k))
+    return x, idx, w, p, go
+
+
+def test_native_boundary_split_touches_only_the_base_products():
+    """With the base weights zero the base products vanish, so the split of
+    their activations cannot matter: every output is bitwise the same with
+    and without act_split.  With real base weights the outputs move, by
+    about the split's 2^-8 relative error."""
+    from oracle import moe_lora as OM
+    x, idx, w, p, go = _layer_case()
+    p0 = dict(p, W13=np.zeros_like(p["W13"]), W2=np.zeros_like(p["W2"]))
+    a = OM.forward_backward(x, idx, w, p0, 0.9, go)
+    b = OM.forward_backward(x, idx, w, p0, 0.9, go, act_split="e4m3x2")
+    assert np.array_equal(a[0], b[0])
+    for n in a[1]:
+        assert np.array_equal(a[1][n], b[1][n]), n
+    c = OM.forward_backward(x, idx, w, p, 0.9, go)
+    d = OM.forward_backward(x, idx, w, p, 0.9, go, act_split="e4m3x2")
+    rel = np.linalg.norm(d[0] - c[0]) / np.linalg.norm(c[0])
+    assert 1e-5 < rel < 2e-2, rel
