@@ -301,11 +301,12 @@ def main():
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
     ap.add_argument("--base-layout", choices=("plain", "transformed"), default="transformed",
-                    help="transformed (default): also hold the frozen bf16 base as W13^T / W2^T "
-                         "per expert (the reusable transformed weights of the pages' backward), "
-                         "written once by moe_lora_transform_base before the timed steps, so the "
-                         "backward's data-gradient GEMMs read it in contraction order; plain: "
-                         "transpose through LDS on every backward (same bits)")
+                    help="transformed (default): also hold the frozen base as bf16 W13^T / W2^T "
+                         "per expert (the reusable transformed weights of the pages' backward; for "
+                         "an MXFP4 base the dequantised weights), written once by "
+                         "moe_lora_transform_base before the timed steps, so the backward's "
+                         "data-gradient GEMMs read it in contraction order; plain: transpose (and "
+                         "expand) through LDS on every backward (same bits)")
     ap.add_argument("--clamp", type=float, default=0.0,
                     help="activation clamp c (> 0: both pre-activations clipped to [-c, c]; the "
                          "pages' production runs use 10); default off, as in the headline workload")
@@ -392,7 +393,7 @@ def main():
                        clamp=args.clamp)
     layer = B.MoeLoraLayer(desc, device=dev, base_grads=args.base_grads)
     stream = torch.cuda.current_stream()
-    transformed = args.base_layout == "transformed" and not mx
+    transformed = args.base_layout == "transformed"  # for MXFP4: the dequantised weights, transposed
     if transformed:  # once, outside the timed steps: the base weights are frozen
         params.update(B.transform_base(desc, params, stream))
         torch.cuda.synchronize()
@@ -489,11 +490,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4 x e4m3x2 fwd, bf16" if mx else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (("MXFP4 base (e2m1 + e8m0/32), " if mx else "") +
-                         ("bf16 base also held transposed for the backward (written once), "
+            "workload": (("MXFP4 base (e2m1 + e8m0/32) on scaled MFMA, " if mx else "") +
+                         (("base " + ("dequantised and " if mx else "") +
+                           "held transposed in bf16 for the backward (written once), ")
                           if transformed else "") +
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "

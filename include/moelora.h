@@ -124,10 +124,11 @@ typedef struct moe_pool {
  *     moe_lora_transform_base and reused by every backward (PR #9 Summary:
  *     reusable transformed weights).  With them the two data-gradient GEMMs
  *     read the weights in the order they contract them; without them (NULL)
- *     the backward transposes W13 / W2 on the fly.  Results are bitwise the
- *     same either way; the contents must match W13 / W2.  Each may be given
- *     alone; 16-byte aligned; MOE_BASE_MXFP4 with either: UNSUPPORTED.
- *     The forward ignores them. */
+ *     the backward transposes W13 / W2 on the fly (for an MXFP4 base also
+ *     expanding them to bf16).  Results are bitwise the same either way; the
+ *     contents must match W13 / W2 (for an MXFP4 base: their dequantised
+ *     values).  Each may be given alone; 16-byte aligned.  The forward
+ *     ignores them. */
 typedef struct moe_lora_params {
   const void* W13;
   const void* W2;
@@ -192,11 +193,13 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
                       int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
                       int64_t capacity, int32_t* device_error, void* stream);
 
-/* Write the transformed base weights of moe_lora_params (bf16 base only):
- * W13T[e] = W13[e]^T ([E, H, 2I]) and W2T[e] = W2[e]^T ([E, I, H]) from
- * params->W13 / params->W2.  Either output may be NULL (skipped); outputs are
- * 16-byte aligned device buffers that overlap neither input nor each other.
- * MOE_BASE_MXFP4: UNSUPPORTED.  Queued on `stream` like every call. */
+/* Write the transformed base weights of moe_lora_params: W13T[e] = W13[e]^T
+ * ([E, H, 2I]) and W2T[e] = W2[e]^T ([E, I, H]), bf16, from params->W13 /
+ * params->W2.  For MOE_BASE_MXFP4 they are the dequantised weights
+ * e2m1 x 2^(e-127) (exact in bf16) transposed, read from the packed W13 / W2
+ * and their scales (both required).  Either output may be NULL (skipped);
+ * outputs are 16-byte aligned device buffers that overlap neither input nor
+ * each other.  Queued on `stream` like every call. */
 moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
                                    void* W2T, void* stream);
 

@@ -227,10 +227,14 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraPara
 def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
                             W13T: Optional[torch.Tensor], W2T: Optional[torch.Tensor],
                             stream=None) -> None:
-    """W13T[e] = W13[e]^T, W2T[e] = W2[e]^T (bf16 base; either may be None)."""
+    """W13T[e] = W13[e]^T, W2T[e] = W2[e]^T in bf16 (either may be None); for an
+    MXFP4 base the dequantised weights, transposed."""
     E, H, I = desc.E, desc.H, desc.I
     bf = torch.bfloat16
-    base = {n: params[n] for n in ("W13", "W2", "A1", "A3", "B1", "B3", "A2", "B2")}
+    names = ("W13", "W2", "A1", "A3", "B1", "B3", "A2", "B2")
+    if desc.base_format == MOE_BASE_MXFP4:
+        names += ("W13_scale", "W2_scale")
+    base = {n: params[n] for n in names}
     pp = _params_struct(base, desc)
     st = library().moe_lora_transform_base(
         ctypes.byref(desc), ctypes.byref(pp), _ptr(W13T, bf, (E, H, 2 * I), "W13T"),

@@ -147,10 +147,10 @@ moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
   // scales: present exactly for an MXFP4 base (byte arrays, no alignment needed)
   const bool mx = d->base_format == MOE_BASE_MXFP4;
   if (mx != (w->W13_scale != nullptr) || mx != (w->W2_scale != nullptr)) return MOE_ERR_INVALID;
-  // transformed base weights: optional, bf16 base only
+  // transformed base weights: optional bf16 copies (for an MXFP4 base, of
+  // the dequantised weights)
   if ((w->W13T != nullptr && !aligned16(w->W13T)) || (w->W2T != nullptr && !aligned16(w->W2T)))
     return MOE_ERR_INVALID;
-  if (mx && (w->W13T != nullptr || w->W2T != nullptr)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -446,25 +446,32 @@ moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params
   const moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (params == nullptr) return MOE_ERR_INVALID;
-  if (d->base_format != MOE_BASE_BF16) return MOE_ERR_UNSUPPORTED;
-  const size_t b13 = (size_t)d->E * 2 * d->I * d->H * 2, b2 = (size_t)d->E * d->H * d->I * 2;
+  const bool mx = d->base_format == MOE_BASE_MXFP4;
+  const size_t n13 = (size_t)d->E * 2 * d->I * d->H, n2 = (size_t)d->E * d->H * d->I;  // elements
+  const size_t b13 = n13 * 2, b2 = n2 * 2;                                              // bf16 outputs
+  const size_t in13 = mx ? n13 / 2 : b13, in2 = mx ? n2 / 2 : b2;                      // inputs
+  if (mx && (params->W13_scale == nullptr || params->W2_scale == nullptr)) return MOE_ERR_INVALID;
   if (W13T != nullptr) {
     if (!aligned16(W13T) || !aligned16(params->W13)) return MOE_ERR_INVALID;
-    if (overlap(rng(W13T, b13), rng(params->W13, b13))) return MOE_ERR_INVALID;
+    if (overlap(rng(W13T, b13), rng(params->W13, in13))) return MOE_ERR_INVALID;
+    if (mx && overlap(rng(W13T, b13), rng(params->W13_scale, n13 / 32))) return MOE_ERR_INVALID;
   }
   if (W2T != nullptr) {
     if (!aligned16(W2T) || !aligned16(params->W2)) return MOE_ERR_INVALID;
-    if (overlap(rng(W2T, b2), rng(params->W2, b2))) return MOE_ERR_INVALID;
+    if (overlap(rng(W2T, b2), rng(params->W2, in2))) return MOE_ERR_INVALID;
+    if (mx && overlap(rng(W2T, b2), rng(params->W2_scale, n2 / 32))) return MOE_ERR_INVALID;
   }
   if (W13T != nullptr && W2T != nullptr && overlap(rng(W13T, b13), rng(W2T, b2))) return MOE_ERR_INVALID;
   const hipStream_t s = (hipStream_t)stream;
-  if (W13T != nullptr &&
-      launch_transpose((const uint16_t*)params->W13, (uint16_t*)W13T, d->E, 2 * d->I, d->H, s) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (W2T != nullptr &&
-      launch_transpose((const uint16_t*)params->W2, (uint16_t*)W2T, d->E, d->H, d->I, s) != hipSuccess)
-    return MOE_ERR_HIP;
-  return MOE_OK;
+  hipError_t e = hipSuccess;
+  if (W13T != nullptr)
+    e = mx ? launch_transpose_mx((const uint8_t*)params->W13, params->W13_scale, (uint16_t*)W13T, d->E, 2 * d->I,
+                                 d->H, s)
+           : launch_transpose((const uint16_t*)params->W13, (uint16_t*)W13T, d->E, 2 * d->I, d->H, s);
+  if (e == hipSuccess && W2T != nullptr)
+    e = mx ? launch_transpose_mx((const uint8_t*)params->W2, params->W2_scale, (uint16_t*)W2T, d->E, d->H, d->I, s)
+           : launch_transpose((const uint16_t*)params->W2, (uint16_t*)W2T, d->E, d->H, d->I, s);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

@@ -920,6 +920,45 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t
   }
 }
 
+// The transformed copy of an MXFP4 base: [B, R, C] e2m1 (element 2i in the
+// low nibble of byte i, one e8m0 scale per 32 along C) -> [B, C, R] bf16,
+// the dequantised values (exact in bf16).  R and C are multiples of 64: each
+// workgroup dequantises one 64 x 64 tile (a thread: one row, 16 values = 8
+// packed bytes under one scale) into LDS and writes it transposed.
+__global__ __launch_bounds__(256) void k_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int R,
+                                                      int C) {
+  __shared__ uint16_t t[64][72];
+  const long b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  q += b * (long)R * (C / 2);
+  sc += b * (long)R * (C / 32);
+  dst += b * (long)R * C;
+  {
+    const int rr = threadIdx.x / 4, cc = (threadIdx.x % 4) * 16;
+    const long row = r0 + rr;
+    const u32x2 w = *(const u32x2*)(q + row * (C / 2) + (c0 + cc) / 2);
+    const float s = v2::e8m0_value(sc[row * (C / 32) + (c0 + cc) / 32]);
+    *(u32x4*)&t[rr][cc] = v2::fp4x8_bf16(w[0], s);
+    *(u32x4*)&t[rr][cc + 8] = v2::fp4x8_bf16(w[1], s);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cr = threadIdx.x / 8 + 32 * p, rc = (threadIdx.x % 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)t[rc + 2 * j][cr] | ((uint32_t)t[rc + 2 * j + 1][cr] << 16);
+    *(u32x4*)(dst + (long)(c0 + cr) * R + r0 + rc) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int B, int R, int C,
+                               hipStream_t st) {
+  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  MOE_LAUNCH(k_transpose_mx, dim3(C / 64, R / 64, B), dim3(256), 0, st, q, sc, dst, R, C);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st) {
   if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
   MOE_LAUNCH(k_transpose, dim3((C + 63) / 64, (R + 63) / 64, B), dim3(256), 0, st, src, dst, R, C);
@@ -974,16 +1013,16 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
-    const bool tw = !a.mx && a.W2T != nullptr;
+    const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base
     if (tw) {
       // A2T = A2_e^T per expert ([E, I, r]), the K-tile rank operand
       const hipError_t e = launch_transpose(a.A2, a.A2T, a.E, a.r, a.I, st);
       if (e != hipSuccess) return e;
     }
-    if (a.mx)
-      launch_w2d_var<true, false>(a, grid, st);
-    else if (tw)
+    if (tw)
       launch_w2d_var<false, true>(a, grid, st);
+    else if (a.mx)
+      launch_w2d_var<true, false>(a, grid, st);
     else
       launch_w2d_var<false, false>(a, grid, st);
   }
@@ -991,10 +1030,10 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
   {
     const dim3 grid(a.maxtiles * (a.H / GW13D::TN));
-    if (a.mx)
-      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<true, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
-    else if (a.W13T != nullptr)
+    if (a.W13T != nullptr)
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, true>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+    else if (a.mx)
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<true, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
     else
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }

@@ -91,21 +91,16 @@ __device__ __forceinline__ uint32_t quant_term(float (&v)[32], uint32_t (&q)[8])
   return (uint32_t)(E + 127);
 }
 
-// Rows of a bf16 [*, K] matrix -> codes [*, 2K bytes] and scale words
-// [*, K/64]; one thread per (row, 32-block), threads of one row adjacent.
-// GATHERED: the rows are pool rows of the layer (`rows` pool rows, only real
-// ones -- row_to_route >= 0 below offsets[E] -- are written).
-template <bool POOL>
+// Rows of a bf16 [nrows, K] matrix -> codes [nrows, 2K bytes] and scale
+// words [nrows, K/64]; one thread per (row, 32-block), the threads of a row
+// adjacent (K % 64 == 0).
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
-                                                    uint32_t* __restrict__ scales, long nrows, int K,
-                                                    const int32_t* __restrict__ row2r,
-                                                    const int32_t* __restrict__ pool_end) {
-  const int bpr = K / 32;  // blocks per row (even: K % 256 == 0)
+                                                    uint32_t* __restrict__ scales, long nrows, int K) {
+  const int bpr = K / 32;  // blocks per row (even)
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = i / bpr;
   const int j = (int)(i - row * bpr);
-  bool live = row < nrows;
-  if (POOL && live) live = row < (long)*pool_end && row2r[row] >= 0;
+  const bool live = row < nrows;
   float v[32];
   if (live) {
     const u32x4* p = (const u32x4*)(src + row * (long)K + 32 * j);
@@ -134,6 +129,48 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
   *(u32x4*)(base + 64) = u32x4{lo[0], lo[1], lo[2], lo[3]};
   *(u32x4*)(base + 80) = u32x4{lo[4], lo[5], lo[6], lo[7]};
   if ((j & 1) == 0) scales[row * (long)(K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
+}
+
+// The split of a tile of bf16 rows parked in LDS (an epilogue image: rows of
+// `pitch` bytes, COLS values from global column c0, a multiple of 64): the
+// codes and scale words of rows [0, nrows) go to codes / scales (those rows'
+// first elements; the global rows have 2K bytes and K/64 words).  The same
+// result as k_quant_rows on the stored rows.  All NT threads call it.
+template <int COLS, int NTH>
+__device__ __forceinline__ void split_image_rows(const char* img, int pitch, int nrows, uint8_t* codes,
+                                                 uint32_t* scales, int K, int c0) {
+  constexpr int BPR = COLS / 32;  // 32-blocks per image row (even)
+  static_assert(BPR % 2 == 0 && (TM * BPR) % NTH == 0, "blocks of a chunk in neighbouring lanes");
+#pragma unroll
+  for (int q = 0; q < TM * BPR / NTH; ++q) {
+    const int b = threadIdx.x + NTH * q;
+    const int row = b / BPR, jb = b % BPR;
+    const bool live = row < nrows;
+    float v[32];
+    const u32x4* p = (const u32x4*)(img + row * pitch + jb * 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = p[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * c + 2 * e] = bf2f(w[e] & 0xffffu);
+        v[8 * c + 2 * e + 1] = bf2f(w[e] >> 16);
+      }
+    }
+    uint32_t hi[8], lo[8];
+    const uint32_t s1 = quant_term(v, hi);
+    const uint32_t s2 = quant_term(v, lo);
+    const uint32_t o1 = __shfl_xor(s1, 1, 64), o2 = __shfl_xor(s2, 1, 64);
+    if (live) {
+      const int j = c0 / 32 + jb;  // global 32-block
+      uint8_t* base = codes + (long)row * (2 * K) + 128 * (j >> 1) + 32 * (j & 1);
+      *(u32x4*)(base) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *(u32x4*)(base + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+      *(u32x4*)(base + 64) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      *(u32x4*)(base + 80) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+      if ((j & 1) == 0) scales[(long)row * (K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -215,30 +252,31 @@ __device__ __forceinline__ void mma_mx(const char* st, int s, f32x16 (&acc)[G::N
     }
 }
 
-// Geometry of the low-rank extension stages that may precede the base K
-// range in the same pipeline (bf16, 32 k a stage: M and N tiles of 16 KB each
-// inside one stage buffer, the two halves of the N tile contracting the two
-// halves of the stage's k -- the SPLIT stages of the bf16 engine).
-using GE = v2::Geo2<4, 2, 2, 4, false, false, 32>;
-static_assert(GE::STAGE <= STAGE, "an extension stage fits a stage buffer");
-using KE = v2::KLoad<TM, 32, NW>;
-using KE2 = v2::KLoad<TM, 32, NW, true>;
+// Geometry of the low-rank extension stages that follow the base K range
+// (bf16, the W13 tile's geometry: 64 k a stage, the two halves of the N tile
+// contracting the two halves of the stage's k -- the SPLIT stages of the
+// bf16 engine; two 64 KB buffers).
+using GE = v2::Geo2<4, 2, 2, 4, false, false, 64>;
+static_assert(GE::NBUF * GE::STAGE <= LDS_BYTES + 2048, "the extension stages reuse the MX stage buffers");
+using KE = v2::KLoad<TM, 64, NW>;
+using KE2 = v2::KLoad<TM, 64, NW, true>;
 constexpr int EXT_INSTS = 2 * KE::NJ;
 
-// One extension stage (GE: 32 k, two k16 steps; the gate blocks contract the
-// first, the up blocks the second), fragments read just before their MFMAs.
+// One extension stage (GE: 64 k, four k16 steps; the gate blocks contract
+// the first two, the up blocks the last two), fragments read just before
+// their MFMAs so that few are live next to the accumulators.
 template <class G>
 __device__ __forceinline__ void mma_ext(const char* st, f32x16 (&acc)[G::NB][G::MB], int wm, int wn, int lane) {
   const char* sM = st;
   const char* sN = st + GE::SM_BYTES;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < 4; ++kk) {
     bf16x8 b[G::MB];
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) b[mb] = v2::frag<false, GE::TM, 32>(sM, G::m_local(wm, mb), kk, lane);
+    for (int mb = 0; mb < G::MB; ++mb) b[mb] = v2::frag<false, GE::TM, 64>(sM, G::m_local(wm, mb), kk, lane);
 #pragma unroll
-    for (int nb = kk * (G::NB / 2); nb < (kk + 1) * (G::NB / 2); ++nb) {
-      const bf16x8 a = v2::frag<false, GE::TN, 32>(sN, G::n_local(wn, nb), kk, lane);
+    for (int nb = (kk / 2) * (G::NB / 2); nb < (kk / 2 + 1) * (G::NB / 2); ++nb) {
+      const bf16x8 a = v2::frag<false, GE::TN, 64>(sN, G::n_local(wn, nb), kk, lane);
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[mb], acc[nb][mb], 0, 0, 0);
@@ -246,11 +284,11 @@ __device__ __forceinline__ void mma_ext(const char* st, f32x16 (&acc)[G::NB][G::
   }
 }
 
-// The base K range, nst k64 stages (ld.issue(s, buffer)), then -- in a loop
-// of its own, so that each loop keeps one fragment schedule -- next
-// extension stages (ld.issue_ext(s, buffer), bf16).  Three buffers, two
-// stages in flight.  Ends with a workgroup barrier (LDS free for the
-// epilogue).
+// The base K range, nst k64 stages (ld.issue(s, buffer); three buffers, two
+// stages in flight), then -- in a loop of its own, so that each loop keeps
+// one fragment schedule and the accumulators one register assignment --
+// next extension stages (ld.issue_ext(s, buffer), bf16, two buffers).  Ends
+// with a workgroup barrier (LDS free for the epilogue).
 template <class G, class L>
 __device__ __forceinline__ void run_mx(const L& ld, int next, int nst, f32x16 (&acc)[G::NB][G::MB], char* smem) {
   static_assert(GE::MB == G::MB && GE::NB == G::NB && GE::WM == G::WM && GE::WN == G::WN, "same accumulators");
@@ -270,17 +308,13 @@ __device__ __forceinline__ void run_mx(const L& ld, int next, int nst, f32x16 (&
     }
     __syncthreads();
   }
-  if (next > 0) {
+  if (next > 0) {  // two 64 KB buffers, one stage in flight
     ld.issue_ext(0, smem);
-    if (next > 1) ld.issue_ext(1, smem + STAGE);
     for (int s = 0; s < next; ++s) {
-      if (s + 1 < next)
-        v2::wait_vm<EXT_INSTS>();
-      else
-        v2::wait_vm<0>();
+      v2::wait_vm<0>();
       v2::bar();
-      if (s + 2 < next) ld.issue_ext(s + 2, smem + ((s + 2) % NBUF) * STAGE);
-      mma_ext<G>(smem + (s % NBUF) * STAGE, acc, wm, wn, lane);
+      if (s + 1 < next) ld.issue_ext(s + 1, smem + ((s + 1) & 1) * GE::STAGE);
+      mma_ext<G>(smem + (s & 1) * GE::STAGE, acc, wm, wn, lane);
     }
     __syncthreads();
   }

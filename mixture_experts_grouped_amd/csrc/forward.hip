@@ -124,8 +124,8 @@ struct LdW13MX : LdMX {
   mx::KE2 ne;  // B1 rows (gate half of the tile), B3 rows (up half)
   int r;
   __device__ void issue_ext(int s, char* st) const {
-    me.issue(s * 16, 2 * r, true, st);
-    ne.issue(s * 16, 2 * r, true, st + mx::GE::SM_BYTES);
+    me.issue(s * 32, 2 * r, true, st);
+    ne.issue(s * 32, 2 * r, true, st + mx::GE::SM_BYTES);
   }
 };
 static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipeline's LDS");
@@ -172,8 +172,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     for (int j = 0; j < KL::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KL::row_of(j)) * a.H * 2));
     v2::run_stages2<G, 2>(L, nsplit + a.H / G::KT, acc, smem);
   } else {
-    // extension stages of 32 k (16 of the gate's 2r, 16 of the up's), then
-    // the base K range as k64 stages on the scaled matrix cores
+    // the base K range as k64 stages on the scaled matrix cores, then the
+    // extension stages of 64 k (32 of the gate's 2r, 32 of the up's)
     using KE = mx::KE;
     LdW13MX L;
     L.r = r;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
              a.XS, a.T, [&](int row) {
                return row < nrows ? (uint32_t)(a.row2r[ti.row0 + row] / a.k) * sbytes : OFF_NONE;
              });
-    mx::run_mx<G>(L, (2 * r + 15) / 16, a.H / 64, acc, smem);
+    mx::run_mx<G>(L, (2 * r + 31) / 32, a.H / 64, acc, smem);
   }
   // G and V go out as fp16 in the accumulator-blocked layout (512 bytes per
   // wave access);
@@ -247,6 +247,9 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   if (wide) *a.status = MOE_SAVED_FP16_RANGE;  // only ever 0 -> this bit: racing stores agree
   __syncthreads();
   ImgH::flush(smem, a.Hh + ti.row0 * (long)a.I + i0, a.I, nrows);
+  if constexpr (MX)  // the W2 GEMM's operand: the split of these bf16 rows of h
+    mx::split_image_rows<HALF, G::NT>(smem, ImgH::PITCH, nrows, a.HQ + ti.row0 * (long)(2 * a.I),
+                                      a.HS + ti.row0 * (long)(a.I / 64), a.I, i0);
 }
 
 // ----------------------------------------------------------------------------
@@ -424,8 +427,8 @@ static void set_w13_lds(AttrInit& ai) {
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
                              hipStream_t st) {
   const long n = rows * (K / 32);
-  MOE_LAUNCH_AS("k_quant_rows", mx::k_quant_rows<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
-                codes, scales, rows, K, nullptr, nullptr);
+  MOE_LAUNCH_AS("k_quant_rows", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                codes, scales, rows, K);
   return hipGetLastError();
 }
 
@@ -449,8 +452,8 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);
   if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
-    MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
-                  a.XQ, a.XS, (long)a.T, a.H, nullptr, nullptr);
+    MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
+                  a.XQ, a.XS, (long)a.T, a.H);
   }
   {
     const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
@@ -462,11 +465,6 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
       launch_w13_cl<false, 1>(a, grid, st);
     else
       launch_w13_cl<false, 0>(a, grid, st);
-  }
-  if (a.mx) {  // h as its two-term E4M3 split for the scaled W2 GEMM (real pool rows)
-    const long n = a.cap * (a.I / 32);
-    MOE_LAUNCH_AS("k_quant_h", mx::k_quant_rows<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.Hh,
-                  a.HQ, a.HS, a.cap, a.I, a.row2r, a.offsets + a.E);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)

@@ -133,6 +133,9 @@ hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* cod
                              hipStream_t st);
 // [B, R, C] -> [B, C, R] bf16 bits
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st);
+// [B, R, C] MXFP4 (packed + e8m0 per 32 along C) -> [B, C, R] bf16, R and C multiples of 64
+hipError_t launch_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int B, int R, int C,
+                               hipStream_t st);
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
 
 }  // namespace moelora

@@ -183,7 +183,7 @@ def test_frozen_weight_grad_pointers_must_be_aligned():
 
 def test_transformed_base_checks_before_any_launch():
     """The transformed base weights (W13T, W2T) are optional bf16 copies:
-    misaligned ones are rejected, an MXFP4 base refuses them, and
+    misaligned ones are rejected, an MXFP4 transform needs the scales, and
     moe_lora_transform_base validates its outputs on the host (with both
     outputs NULL it has nothing to do and returns ok without a launch)."""
     lib = B.library()
@@ -200,13 +200,12 @@ def test_transformed_base_checks_before_any_launch():
                                      saved, fake * 64, fake * 200, byref(grads), fake * 256,
                                      scratch, None) == B.MOE_ERR_INVALID
     dm = B.make_desc(64, 256, 256, 8, 2, 8, base_format=B.MOE_BASE_MXFP4)
-    savm, scrm = B.moe_lora_workspace_size(dm)
-    prm = B.MoeLoraParams(fake, fake, fake, fake, *([fake] * 6), fake * 5, None)
-    assert lib.moe_lora_backward(byref(dm), byref(pool), fake, fake, byref(prm), fake * 128,
-                                 savm, fake * 64, fake * 200, byref(grads), fake * 256,
-                                 scrm, None) == B.MOE_ERR_UNSUPPORTED
     base = B.MoeLoraParams(fake * 2, fake * 3, None, None, *([fake] * 6))
-    assert lib.moe_lora_transform_base(byref(dm), byref(base), fake * 5, None, None) == B.MOE_ERR_UNSUPPORTED
+    # an MXFP4 transform without its scales
+    assert lib.moe_lora_transform_base(byref(dm), byref(base), fake * 5, None, None) == B.MOE_ERR_INVALID
+    # W13T overlapping the packed W13 ([E, 2I, H/2] = 512 KiB here)
+    mxp = B.MoeLoraParams(fake * 2, fake * 3, fake * 4, fake * 4 + 65536, *([fake] * 6))
+    assert lib.moe_lora_transform_base(byref(dm), byref(mxp), fake * 2 + 4096, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(None, byref(base), fake * 5, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), None, fake * 5, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 5 + 8, None, None) == B.MOE_ERR_INVALID

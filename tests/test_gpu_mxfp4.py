@@ -117,14 +117,21 @@ def test_mxfp4_against_both_oracles(name):
     _both_oracles(res, case_deq, shape, f"{name}:mx:")
 
 
-def test_mxfp4_backward_is_the_bf16_backward_on_dequantised_weights():
-    """From the same saved forward state, the MXFP4 backward (weights
-    expanded to bf16 in LDS) gives bitwise the bf16 backward fed the
-    dequantised weights."""
+@pytest.mark.parametrize("transformed", [False, True])
+def test_mxfp4_backward_is_the_bf16_backward_on_dequantised_weights(transformed):
+    """From the same saved forward state, the MXFP4 backward gives bitwise
+    the bf16 backward fed the dequantised weights: expanding the packed
+    weights to bf16 in LDS (transformed=False), or reading the transformed
+    copy moe_lora_transform_base wrote from them (the dequantised weights
+    transposed; checked element for element here)."""
     shape, key, routing, mask = CASES["r128_masked"]
     case = I.layer_inputs(shape, key, routing=routing, mask_prob=mask)
     mx, deq = Hn.mxfp4_base(case)
-    run_mx = Hn.GpuRun(shape, case, mx=mx)
+    run_mx = Hn.GpuRun(shape, case, mx=mx, transformed=transformed)
+    if transformed:
+        for n, src in (("W13T", deq["W13"]), ("W2T", deq["W2"])):
+            got = run_mx.params[n].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, np.ascontiguousarray(src.transpose(0, 2, 1))), n
     res_mx = run_mx.run()
     run_bf = Hn.GpuRun(shape, dict(case, W13=deq["W13"], W2=deq["W2"]))
     Lb, Lm = run_bf.layer, run_mx.layer
@@ -185,7 +192,7 @@ def test_mxfp4_production_share():
     idx, w = I.route_balanced(shape, key)
     case, mx = _mx_case(shape, key, idx, w, list(range(shape.E)))
     Hn.log("[mxfp4] production share: inputs ready")
-    res = Hn.GpuRun(shape, case, mx=mx).run()
+    res = Hn.GpuRun(shape, case, mx=mx, transformed=True).run()  # the benchmark's configuration
     Hn.log("[mxfp4] oracles, expert by expert")
     _both_oracles(res, case, shape, "production:mx:", log_every=16)
 
