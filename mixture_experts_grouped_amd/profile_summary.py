@@ -3,10 +3,19 @@ under profiles/.
 
     python -m mixture_experts_grouped_amd.profile_summary --name NAME \\
         --stats DIR [--fetch DIR --write DIR --copy-fetch DIR --copy-write DIR] \\
-        [--bench BENCH_JSON] [--out profiles]
+        [--mfma DIR --cache DIR --copy-clock DIR] [--bench BENCH_JSON] [--out profiles]
 
 --stats: a ``rocprofv3 --kernel-trace --stats --output-format csv`` run
-(reads ``*_kernel_stats.csv``).  --fetch/--write: ``--pmc FETCH_SIZE`` and
+(reads ``*_kernel_stats.csv``).  --mfma: a ``--pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES
+SQ_WAVES --kernel-trace`` run; --cache: ``--pmc TCC_HIT_sum TCC_MISS_sum
+SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --kernel-trace``; --copy-clock:
+``--pmc GRBM_GUI_ACTIVE --kernel-trace`` over the copy calibration.  They give
+per kernel the matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+GRBM_GUI_ACTIVE x the 1024 SIMDs; the GRBM count is normalised so that the
+light copy kernel runs at the 2.4 GHz top clock), the mean shader clock over
+the dispatch (normalised GRBM_GUI_ACTIVE / traced duration), the L2 hit rate
+and the LDS bank conflicts per LDS instruction.
+--fetch/--write: ``--pmc FETCH_SIZE`` and
 ``--pmc WRITE_SIZE`` runs of the same command; --copy-fetch/--copy-write: the
 same counters over ``bench.py --copy-calibration`` (a plain device copy of a
 known size), whose reading gives the counter's scale.  The scaled per-dispatch
@@ -70,6 +79,50 @@ def read_counter(d: str, counter: str) -> Dict[str, float]:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def read_durations(d: str) -> Dict[str, float]:
+    """Average traced duration (ns) per kernel of a run with --kernel-trace."""
+    rows = csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv"))))
+    acc = defaultdict(list)
+    for r in rows:
+        acc[kernel_key(r["Kernel_Name"])].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+TOP_CLOCK_GHZ = 2.4   # MI355X shader clock ceiling
+SIMDS = 256 * 4
+
+
+def mfma_table(mfma_dir: str, cache_dir: str, clock_dir: str):
+    """Per kernel: duration, clock, MFMA busy, L2 hit, LDS conflicts (see module doc)."""
+    dur = read_durations(mfma_dir)
+    gui = read_counter(mfma_dir, "GRBM_GUI_ACTIVE")
+    busy = read_counter(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    waves = read_counter(mfma_dir, "SQ_WAVES")
+    # GRBM_GUI_ACTIVE counts each active clock once per unit that reports it;
+    # the copy kernel (memory-bound, light) runs at the top clock, which fixes
+    # the number of reporting units
+    cdur, cgui = read_durations(clock_dir), read_counter(clock_dir, "GRBM_GUI_ACTIVE")
+    ck = max((k for k in cgui if "copy" in k.lower()), key=lambda k: cdur.get(k, 0))
+    units = cgui[ck] / (cdur[ck] * TOP_CLOCK_GHZ)
+    hit, miss = read_counter(cache_dir, "TCC_HIT_sum"), read_counter(cache_dir, "TCC_MISS_sum")
+    lds, conf = read_counter(cache_dir, "SQ_INSTS_LDS"), read_counter(cache_dir, "SQ_LDS_BANK_CONFLICT")
+    rows = []
+    for k in dur:
+        if not k.startswith("k_") or k not in gui:
+            continue
+        cyc = gui[k] / units
+        e = {"kernel": k, "avg_us": dur[k] / 1e3, "clock_ghz": cyc / dur[k], "waves": waves.get(k)}
+        if k in busy:
+            e["mfma_busy"] = busy[k] / (cyc * SIMDS)
+        if k in hit and hit[k] + miss.get(k, 0) > 0:
+            e["l2_hit"] = hit[k] / (hit[k] + miss.get(k, 0))
+        if k in lds and lds[k] > 0:
+            e["lds_conflict_per_inst"] = conf.get(k, 0) / lds[k]
+        rows.append(e)
+    rows.sort(key=lambda e: -e["avg_us"])
+    return {"grbm_units": units, "copy_kernel": ck, "kernels": rows}
+
+
 def copy_scale(d: str, counter: str) -> float:
     vals = read_counter(d, counter)
     copy = [v for k, v in vals.items() if "copy" in k.lower()]
@@ -87,6 +140,10 @@ def main() -> None:
     ap.add_argument("--write")
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
+    ap.add_argument("--mfma")
+    ap.add_argument("--cache")
+    ap.add_argument("--copy-clock")
+    ap.add_argument("--flops", help="JSON {kernel: algorithmic FLOPs per launch} for the TFLOP/s column")
     ap.add_argument("--bench")
     ap.add_argument("--out", default="profiles")
     ap.add_argument("--workload", default="")
@@ -117,6 +174,40 @@ def main() -> None:
     os.makedirs(args.out, exist_ok=True)
     with open(os.path.join(args.out, f"{args.name}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+
+    if args.mfma and args.cache and args.copy_clock:
+        tab = mfma_table(args.mfma, args.cache, args.copy_clock)
+        flops = json.load(open(args.flops)) if args.flops else {}
+        if not flops and bench:  # algorithmic FLOPs per launch from the bench line's kernel table
+            flops = {k: v["tflops"] * 1e12 * v["avg_ms"] * 1e-3 for k, v in bench.get("kernels", {}).items()
+                     if "tflops" in v}
+        for e in tab["kernels"]:
+            if e["kernel"] in flops:
+                e["tflops"] = flops[e["kernel"]] / (e["avg_us"] * 1e-6) / 1e12
+        tab.update({"source_hash": build.source_hash(), "workload": args.workload})
+        with open(os.path.join(args.out, f"{args.name}_mfma.json"), "w") as f:
+            json.dump(tab, f, indent=1, sort_keys=True)
+        t = [f"# Matrix-core, clock, L2 and LDS counters per dispatch: {args.workload or args.name}", ""]
+        if args.commands:
+            t += ["Commands (run from the repository root on one MI355X, `$R` = the repository path):",
+                  "", "```", args.commands.strip(), "```", ""]
+        t += [f"Build hash `{tab['source_hash']}`. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x 1024 "
+              f"SIMDs); clock cycles = GRBM_GUI_ACTIVE / {tab['grbm_units']:.2f} (the count at which the plain "
+              f"copy `{tab['copy_kernel']}` runs at {TOP_CLOCK_GHZ} GHz); clock = cycles / traced duration; "
+              "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS); LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS. "
+              "Counter runs serialise dispatches, so durations are a little longer than in the timed steps.", "",
+              "| kernel | us | TFLOP/s | clock GHz | MFMA busy | L2 hit | LDS conflict / inst |",
+              "|---|---|---|---|---|---|---|"]
+        for e in tab["kernels"]:
+            if e["avg_us"] < 5:
+                continue
+            f = lambda v, fmt: (fmt % v) if v is not None else "-"  # noqa: E731
+            t.append(f"| {e['kernel']} | {e['avg_us']:.1f} | {f(e.get('tflops'), '%.0f')} | "
+                     f"{e['clock_ghz']:.2f} | {f(e.get('mfma_busy') and 100 * e['mfma_busy'], '%.1f %%')} | "
+                     f"{f(e.get('l2_hit') and 100 * e['l2_hit'], '%.1f %%')} | "
+                     f"{f(e.get('lds_conflict_per_inst'), '%.3f')} |")
+        with open(os.path.join(args.out, f"{args.name}_mfma.md"), "w") as f:
+            f.write("\n".join(t) + "\n")
 
     if args.fetch and args.write and args.copy_fetch and args.copy_write:
         sf = copy_scale(args.copy_fetch, "FETCH_SIZE")
