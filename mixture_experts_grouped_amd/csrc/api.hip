@@ -66,7 +66,7 @@ struct Plan {
   // byte offsets
   size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_XQ, o_XS, o_HQ, o_HS;
-  size_t o_Pt, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
+  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
 Plan make_plan(const moe_lora_desc* d) {
@@ -90,9 +90,8 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
   o = 0;
-  // the forward's scratch first (Pt, Yb in dU's space, Z2 in P's), so that
-  // it is one prefix of the plan: fwd_scratch bytes
-  p.o_Pt = take(T * H * 4);  // used by the forward and the backward
+  // the forward's scratch first (Yb in dU's space, Z2 in P's), so that it
+  // is one prefix of the plan: fwd_scratch bytes
   p.o_dU = take(cap * H * 2);
   p.o_P = take(cap * 2 * r * 4);
   p.fwd_scratch = p.o_P + up(cap * r * 4);  // Z2 = the first cap * r floats of P
@@ -217,7 +216,6 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* base) {
   a.pc = (uint16_t*)(b + p.o_pc);
   a.part = (float*)(b + p.o_part);
   a.ZAp = (uint16_t*)(b + p.o_ZAp);
-  a.Pt = (float*)(b + p.o_Pt);
   a.Z2 = (float*)(b + p.o_Z2);
   a.Yb = (uint16_t*)(b + p.o_Yb);
   a.dwp = (float*)(b + p.o_dwp);

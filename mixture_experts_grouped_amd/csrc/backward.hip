@@ -16,7 +16,7 @@
 //   (with the transformed base both dgrads read the weights as K tiles)
 //   k_p13           P = [B1_e^T dg ; B3_e^T dv]
 //   k_pc            pc_t = s sum_j P_(t,j)
-//   k_rank_dx, k_token_sum   grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
+//   k_rank_dx       grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
 //   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
 //   k_wgrad_shared  dA1, dA3, dB2: over tokens, deterministic split-K
 //   k_reduce_shared fixed-order sum of the split-K partials
@@ -592,10 +592,13 @@ struct LdRankDxK {
   }
 };
 
+// grad_x = [A1; A3]^T pc_t + sum_j dU_(t,j) for 256 tokens x 256 columns
 __global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
+  RouteVec rv;
+  load_routes<false>(a, t0, rv);
   LdRankDxK L;
   L.r = r;
   L.nst = (2 * r + GRK::KT - 1) / GRK::KT;
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
   f32x16 acc[GRK::NB][GRK::MB];
   zero_acc<GRK>(acc);
   v2::run_stages2<GRK, 0>(L, 2 * L.nst, acc, smem);
-  store_rank_tile<GRK>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
+  rank_route_sum<false>(acc, smem, a, rv, a.dU, a.gx, t0, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1046,8 +1049,6 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
-  MOE_LAUNCH_AS("k_dx_sum", k_token_sum<false>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a,
-             a.dU, a.Pt, a.gx);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);

@@ -10,7 +10,7 @@
 //   k_a2        Z2 = s A2_e h
 //   k_w2        Ybase = W2_e h
 //   k_zc        zc_t = sum_j w_tj Z2_(t,j)          (slot order, fp32)
-//   k_rank_combine, k_token_sum   out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
+//   k_rank_combine               out_t = B2 zc_t + sum_j w_tj Ybase_(t,j)
 // The per-token evaluation of the shared factors is exact algebra:
 // sum_j w_j B2 z_j = B2 sum_j w_j z_j.
 #include <type_traits>
@@ -386,12 +386,14 @@ struct LdRankC {
   }
 };
 
-// P = B2 zc_t for 256 tokens x 256 columns (zc carries s and the routing
-// weights; hi/lo halves fold onto B2's r columns)
+// out = B2 zc_t + sum_j w_tj Ybase_(t,j) for 256 tokens x 256 columns (zc
+// carries s and the routing weights; hi/lo halves fold onto B2's r columns)
 __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
+  RouteVec rv;
+  load_routes<true>(a, t0, rv);
   LdRankC L;
   L.m.contig(a.zc, t0, a.T - t0, 2 * r);
   L.m.window(2 * r);
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
   f32x16 acc[GRK::NB][GRK::MB];
   zero_acc<GRK>(acc);
   v2::run_stages2<GRK, 0>(L, (2 * r + GRK::KT - 1) / GRK::KT, acc, smem);
-  store_rank_tile<GRK>(acc, smem, a.Pt, a.H, t0, h0, a.T - t0);
+  rank_route_sum<true>(acc, smem, a, rv, a.Yb, a.out, t0, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -474,8 +476,6 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_combine, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
-  MOE_LAUNCH_AS("k_combine_sum", k_token_sum<true>, dim3((a.T + 3) / 4, (a.H + TS_COLS - 1) / TS_COLS), dim3(256), 0, st, a, a.Yb,
-             a.Pt, a.out);
   return hipGetLastError();
 }
 

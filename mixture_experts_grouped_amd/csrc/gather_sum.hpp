@@ -5,12 +5,14 @@
 // The forward combine (mixture output, c = routing weight, R = the routes'
 // base outputs, P = B2 zc_t with zc_t = s sum_j w_tj z_tj) and the input
 // gradient (c = 1, R = the routes' W13^T [dg; dv], P = [A1; A3]^T pc_t) have
-// this form.  P is a rank-r product per token, computed by a grouped-GEMM
-// style kernel into an fp32 [T, H] scratch (RankImage below); the sum then
-// runs as a pure streaming kernel (k_token_sum): one wave per token and
-// 512-column chunk, 16 bytes a lane from every route row, all of a token's
-// route rows in flight at once.  The route rows add in route order j = 0,
-// 1, ... after P, so the result does not depend on the pool layout.
+// this form.  P is a rank-r product per token: a 256-token x 256-column tile
+// of it is one MFMA GEMM (k_rank_combine, k_rank_dx), and the route sum is
+// that GEMM's epilogue (rank_route_sum below), so P never leaves the chip:
+// one column half of the tile at a time is parked in LDS as fp32, then each
+// 16-lane group takes one token, 8 columns a lane, loads the token's route
+// rows (two tokens and up to eight routes a lane in flight) and writes the
+// bf16 result.  The route rows add in route order j = 0, 1, ... after P, so
+// the result does not depend on the pool layout.
 #pragma once
 #include "engine2.hpp"
 #include "layer.hpp"
@@ -22,87 +24,111 @@ using GRK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
 using RankImg = v2::TileImage<GRK, GRK::TN / 2, float>;
 constexpr int RK_LDS = cmax(GRK::LDS_BYTES, RankImg::BYTES);
 
-// acc (a 256 x 256 tile of P, tokens t0.., columns h0..) -> P rows, through
-// LDS images of one column half at a time.
-template <class G>
-__device__ __forceinline__ void store_rank_tile(const f32x16 (&acc)[G::NB][G::MB], char* smem,
-                                                float* P, long H, int t0, int h0, int ntok) {
-  static_assert(G::NB == 2, "one block column per half");
-  Epi<G> ep;
+constexpr int RS_TPT = 2;   // tokens a thread carries per step
+constexpr int RS_JC = 8;    // route rows loaded per token before any is added
+constexpr int RS_TOK = GRK::TM / (GRK::NT / 16);  // tokens per thread over the tile (8)
+static_assert(GRK::TN / 2 == 16 * 8, "a 16-lane group covers one half row");
+static_assert(RS_TOK % RS_TPT == 0, "whole steps");
+
+// Lane-distributed routes of the thread's tokens: for token slot i, lane g*16
+// + j of each 16-lane group g holds route j's pool row (-1: dead route, or a
+// token past T) and its coefficient (0 for a dead route, whose weight is not
+// read).  topk <= 16.
+struct RouteVec {
+  int row[RS_TOK];
+  float c[RS_TOK];
+};
+
+// Token slot i of thread (wave w, lane): tile row i * 32 + 4 w + lane / 16.
+__device__ __forceinline__ int rs_token(int i) {
+  return i * (GRK::NT / 16) + 4 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 4);
+}
+
+// Issued before the GEMM, so the index loads are long done when the sum runs.
+template <bool WEIGHTED>
+__device__ __forceinline__ void load_routes(const LayerArgs& a, int t0, RouteVec& rv) {
+  const int j = threadIdx.x & 15;
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        RankImg::put(smem, ep.row(mb), ep.col(nb, g) - nb * (G::TN / 2),
-                     f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
-                           acc[nb][mb][4 * g + 3]});
-    __syncthreads();
-    RankImg::flush(smem, P + (long)t0 * H + h0 + nb * (G::TN / 2), H, ntok);
-    __syncthreads();
+  for (int i = 0; i < RS_TOK; ++i) {
+    const int t = t0 + rs_token(i);
+    int row = -1;
+    float c = 0.0f;
+    if (t < a.T && j < a.k) {
+      row = a.r2row[(long)t * a.k + j];
+      if (row >= 0) c = WEIGHTED ? a.w[(long)t * a.k + j] : 1.0f;
+    }
+    rv.row[i] = row;
+    rv.c[i] = c;
   }
 }
 
-constexpr int TS_COLS = 512;  // columns per wave of k_token_sum (8 per lane)
-constexpr int TS_JC = 8;      // route rows loaded before any is added
-
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) { return bload(r, off); }
-
-// out[t, h .. h + 7] for the wave's token t; lanes past H are idle.
+// acc holds the tile's P (tokens t0.., columns h0..); out rows t0 .. T-1.
 template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_token_sum(LayerArgs a, const uint16_t* R, const float* P,
-                                                   uint16_t* out) {
-  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int h = blockIdx.y * TS_COLS + 8 * (threadIdx.x & 63);
-  const bool live = h < a.H;
-  const uint32_t voff = 2u * (uint32_t)h;
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) {
-    const f32x4* pp = (const f32x4*)(P + (long)t * a.H + h);
-    const f32x4 p0 = pp[0], p1 = pp[1];
+__device__ __forceinline__ void rank_route_sum(const f32x16 (&acc)[GRK::NB][GRK::MB], char* smem,
+                                               const LayerArgs& a, const RouteVec& rv,
+                                               const uint16_t* __restrict__ R,
+                                               uint16_t* __restrict__ out, int t0, int h0) {
+  static_assert(GRK::NB == 2, "one block column per half");
+  Epi<GRK> ep;
+  const int lane = threadIdx.x & 63, gbase = lane & 48, li = lane & 15;
+  const long H = a.H;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[q] = p0[q];
-      o[4 + q] = p1[q];
-    }
-  }
-  // lane j holds route j's pool row and weight: one vector load for all
-  // routes, so the row loads below do not wait on each other's index
-  const int lane = threadIdx.x & 63;
-  int myrow = -1;
-  float myc = 0.0f;
-  if (lane < a.k) {
-    myrow = a.r2row[(long)t * a.k + lane];
-    myc = WEIGHTED ? a.w[(long)t * a.k + lane] : 1.0f;
-    if (myrow < 0) myc = 0.0f;  // a dead route's weight is not read
-  }
-  for (int j0 = 0; j0 < a.k; j0 += TS_JC) {
-    u32x4 y[TS_JC];
-    float c[TS_JC];
+  for (int nb = 0; nb < GRK::NB; ++nb) {
 #pragma unroll
-    for (int jj = 0; jj < TS_JC; ++jj) {
-      const int j = j0 + jj;  // < 64: lanes past k hold row -1, weight 0
-      const int row = __builtin_amdgcn_readlane(myrow, j);
-      c[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myc), j));
-      // a dead route gets an empty descriptor and reads zeros
-      const rsrc_t rs = make_rsrc(R + (long)(row < 0 ? 0 : row) * a.H, row < 0 ? 0 : (uint64_t)a.H * 2);
-      y[jj] = bload16(rs, voff);
-    }
-    // routes past k read zeros with weight 0 and add nothing
+    for (int mb = 0; mb < GRK::MB; ++mb)
 #pragma unroll
-    for (int jj = 0; jj < TS_JC; ++jj) {
+      for (int g = 0; g < 4; ++g)
+        RankImg::put(smem, ep.row(mb), ep.col(nb, g) - nb * (GRK::TN / 2),
+                     f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                           acc[nb][mb][4 * g + 3]});
+    __syncthreads();
+    const int hc = h0 + nb * (GRK::TN / 2) + 8 * li;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        o[2 * q] += c[jj] * bf2f(y[jj][q] & 0xffffu);
-        o[2 * q + 1] += c[jj] * bf2f(y[jj][q] >> 16);
+    for (int i0 = 0; i0 < RS_TOK; i0 += RS_TPT) {
+      float o[RS_TPT][8];
+#pragma unroll
+      for (int u = 0; u < RS_TPT; ++u) {
+        const char* pp = smem + rs_token(i0 + u) * RankImg::PITCH + 32 * li;
+        const f32x4 p0 = *(const f32x4*)pp, p1 = *(const f32x4*)(pp + 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[u][q] = p0[q];
+          o[u][4 + q] = p1[q];
+        }
+      }
+      for (int j0 = 0; j0 < a.k; j0 += RS_JC) {
+        u32x4 y[RS_TPT][RS_JC];
+        float c[RS_TPT][RS_JC];
+#pragma unroll
+        for (int u = 0; u < RS_TPT; ++u)
+#pragma unroll
+          for (int jj = 0; jj < RS_JC; ++jj) {
+            // j < 16: lanes past topk hold row -1 and weight 0
+            const int src = gbase | (j0 + jj);
+            const int row = __shfl(rv.row[i0 + u], src, 64);
+            c[u][jj] = __shfl(rv.c[i0 + u], src, 64);
+            y[u][jj] = row >= 0 ? *(const u32x4*)(R + (long)row * H + hc) : u32x4{0u, 0u, 0u, 0u};
+          }
+#pragma unroll
+        for (int u = 0; u < RS_TPT; ++u)
+#pragma unroll
+          for (int jj = 0; jj < RS_JC; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              o[u][2 * q] += c[u][jj] * bf2f(y[u][jj][q] & 0xffffu);
+              o[u][2 * q + 1] += c[u][jj] * bf2f(y[u][jj][q] >> 16);
+            }
+      }
+#pragma unroll
+      for (int u = 0; u < RS_TPT; ++u) {
+        const int t = t0 + rs_token(i0 + u);
+        if (t < a.T)
+          *(u32x4*)(out + (long)t * H + hc) = u32x4{pack2(o[u][0], o[u][1]), pack2(o[u][2], o[u][3]),
+                                                    pack2(o[u][4], o[u][5]), pack2(o[u][6], o[u][7])};
       }
     }
+    __syncthreads();
   }
-  if (live)
-    *(u32x4*)(out + (long)t * a.H + h) =
-        u32x4{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
 }
 
 }  // namespace moelora

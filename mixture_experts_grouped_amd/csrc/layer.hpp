@@ -82,7 +82,6 @@ struct LayerArgs {
   uint16_t* pc;      // [T, 4r]   s * sum_j P as hi/lo (pc1 | pc3)
   float* part;       // [3, nsplit, H*r] split-K partials of the shared-factor gradients
   uint16_t* ZAp;     // [cap, 4r] ZA gathered to pool rows (real rows only)
-  float* Pt;         // [T, H]    per-token rank term of the combine / grad-x (scratch)
   float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
   uint16_t* A2T;     // [E, I, r]  A2_e^T (backward scratch, with W2T only)
   uint16_t *A1T, *A3T;  // [H, r]  A1^T, A3^T (backward scratch)
