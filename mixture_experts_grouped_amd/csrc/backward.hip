@@ -29,7 +29,6 @@
 
 namespace moelora {
 
-using G256 = Geo<4, 4, 2, 2>;
 // thin GEMMs (N = r): smaller M tiles so the grid fills the 256 CUs
 using GS64 = Geo<1, 2, 2, 2>;   // 64 x 128 tile, wave 32 x 64
 using GS128 = Geo<2, 2, 2, 2>;  // 128 x 128 tile, wave 64 x 64
@@ -742,60 +741,49 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
 //   which 2: dB2[h][c] = sum_t go[t][h] zc[t][c]
 // Token range split in fixed chunks; partials summed in chunk order.
 // ----------------------------------------------------------------------------
-struct LdWg {
-  TransK<256, KRows> m, n;
-  __device__ void load(int s) { m.load(s * KT); n.load(s * KT); }
-  __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
-};
-
-__global__ __launch_bounds__(256) void k_wgrad_shared(LayerArgs a) {
+// Both operands K-outer (K = the split's tokens), as in k_wgrad_local.
+__global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
+  using G = GWG;
   const int ntm = a.H / 256;
   const int h0 = (blockIdx.x % ntm) * 256, sp = blockIdx.x / ntm, which = blockIdx.y;
   const int r = a.r;
   const int tb = sp * a.kspl;
   const int nt = min(a.kspl, a.T - tb);
-  LdWg L;
-  if (which < 2)  // x_t from the forward's saved copy
-    L.m.kp = KRows{make_rsrc(a.Xs + (long)tb * a.H, (uint64_t)nt * 2 * a.H), (uint32_t)(2 * a.H),
-                   nullptr, nullptr, 1, tb, nt, 0};
-  else
-    L.m.kp = KRows{make_rsrc(a.go + (long)tb * a.H, (uint64_t)nt * 2 * a.H), (uint32_t)(2 * a.H),
-                   nullptr, nullptr, 1, tb, nt, 0};
-  L.m.cols(h0, 256);
+  LdWg2 L;
+  const uint16_t* mrow0 = (which < 2 ? a.Xs : a.go) + (long)tb * a.H;  // x_t from the forward's saved copy
   if (which < 2) {
-    L.n.kp = KRows{make_rsrc(a.pc + (long)tb * 4 * r, (uint64_t)nt * 8 * r), (uint32_t)(8 * r),
-                   nullptr, nullptr, 1, tb, nt, 0};
+    L.set(mrow0, (uint32_t)(2 * a.H), a.pc + (long)tb * 4 * r, (uint32_t)(8 * r), nt);
     L.n.cols(which * 2 * r, r, 128, r);
   } else {
-    L.n.kp = KRows{make_rsrc(a.zc + (long)tb * 2 * r, (uint64_t)nt * 4 * r), (uint32_t)(4 * r),
-                   nullptr, nullptr, 1, tb, nt, 0};
+    L.set(mrow0, (uint32_t)(2 * a.H), a.zc + (long)tb * 2 * r, (uint32_t)(4 * r), nt);
     L.n.cols(0, r, 128, r);
   }
-  f32x16 acc[G256::NB][G256::MB];
-  mainloop<G256>(L, (nt + KT - 1) / KT, acc, smem);
-  Epi<G256> ep;
+  L.m.cols(h0, 256);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, (nt + G::KT - 1) / G::KT, acc, smem);
+  // hi + lo halves of the rank operand (tile columns c and c + 128) add up
+  Epi<G> ep;
+  static_assert(G::NB == 2, "one hi and one lo block per wave");
   float* part = a.part + ((long)which * a.nsplit + sp) * (long)a.H * r;
 #pragma unroll
-  for (int mb = 0; mb < G256::MB; ++mb) {
+  for (int mb = 0; mb < G::MB; ++mb) {
     const int h = h0 + ep.row(mb);
 #pragma unroll
-    for (int nb = 0; nb < G256::NB / 2; ++nb)
+    for (int g = 0; g < 4; ++g) {
+      const int c = ep.col(0, g);
+      if (c >= r) continue;
+      f32x4 v;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
-        if (c >= r) continue;
-        f32x4 v;
+      for (int q = 0; q < 4; ++q) v[q] = acc[0][mb][4 * g + q] + acc[1][mb][4 * g + q];
+      if (which < 2) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q] = acc[nb][mb][4 * g + q] + acc[nb + G256::NB / 2][mb][4 * g + q];
-        if (which < 2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) part[(long)(c + q) * a.H + h] = v[q];  // [c][h]
-        } else {
-          *(f32x4*)(part + (long)h * r + c) = v;  // [h][c]
-        }
+        for (int q = 0; q < 4; ++q) part[(long)(c + q) * a.H + h] = v[q];  // [c][h]
+      } else {
+        *(f32x4*)(part + (long)h * r + c) = v;  // [h][c]
       }
+    }
   }
 }
 
@@ -1008,12 +996,11 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     ai.lds((const void*)k_rank_dx, RK_LDS);
     ai.lds((const void*)k_wgrad_local, WG_LDS);
     ai.lds((const void*)k_wgrad_base, WG_LDS);
-    ai.lds((const void*)k_wgrad_shared, G256::LDS_BYTES);
+    ai.lds((const void*)k_wgrad_shared, GWG::LDS_BYTES);
     return ai.err;
   });
   if (ierr != hipSuccess) return ierr;
-  const int tm = (a.T + GS64::TM - 1) / GS64::TM;
-  MOE_LAUNCH(k_q, dim3(tm), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q, dim3((a.T + GS64::TM - 1) / GS64::TM), dim3(256), GS64::LDS_BYTES, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
     const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base
@@ -1052,7 +1039,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);
-  MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(256), G256::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(GWG::NT), GWG::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;
   MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
   if (a.dW13 != nullptr || a.dW2 != nullptr) {
