@@ -15,5 +15,6 @@ Modules:
   pool     -- expert-contiguous pool padded per expert (integer metadata)
   moe_lora -- forward and backward of the layer, per route
   mxfp4    -- exact dequantisation of e2m1 values with e8m0 block scales
+  multi_adapter -- several adapters in one pass, one root of tokens each
 """
-from . import pool, moe_lora, mxfp4  # noqa: F401
+from . import pool, moe_lora, mxfp4, multi_adapter  # noqa: F401
