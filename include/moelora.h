@@ -265,6 +265,64 @@ moe_status moe_lora_backward(const moe_lora_desc* desc, const moe_pool* pool,
                              const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------------------
+ * Several adapters in one pass (OpenPipe/ART PR #1139, Behavior: several
+ * adapters share one MoE pass; the router runs once per adapter; the
+ * dispatched expert rows carry adapter IDs so that each adapter's own LoRA
+ * factors serve its rows; Validation: the fused pass equals running the
+ * adapters one after another, bit for bit).
+ *
+ * The T tokens of a call form `count` roots, one per adapter: root a is the
+ * tokens offsets[a] .. offsets[a+1]-1 (contiguous; an empty root is
+ * allowed), and every route of a token carries its root's adapter.  For each
+ * root the calls compute exactly what the single-adapter calls above compute
+ * on that root's tokens with adapter a's factors: outputs, grad-x and router
+ * gradients by token, and each adapter's factor gradients over its own root
+ * (an adapter with an empty root gets exact zeros).  The base W13 / W2 (and
+ * W13T / W2T, the MXFP4 scales, s and every desc field) are common.
+ *
+ * Parameters and gradients are the single-adapter tensors stacked over the
+ * adapters: A1, A3 [count, r, H]; B1, B3 [count, E, I, r]; A2 [count, E, r,
+ * I]; B2 [count, H, r]; likewise dA1 .. dB2.  The frozen-weight gradients
+ * dW13 / dW2 are not offered with count > 1 (MOE_ERR_UNSUPPORTED).
+ *
+ * The pool groups rows by (expert e, adapter a) as group g = e * count + a:
+ * counts / offsets have E * count (+1) entries, and the capacity is
+ * T*k + min(E * count, T*k) * (BLOCK_M - 1) (moe_lora_multi_pool_capacity).
+ * A pool built by build_pool_multi serves only the *_multi calls with the
+ * same adapters.  count = 1 with offsets {0, T} is exactly the single-adapter
+ * path.
+ * ------------------------------------------------------------------------ */
+#define MOE_MAX_ADAPTERS 64
+
+/* offsets: HOST int32 array of count + 1 entries, 0 = offsets[0] <= ... <=
+ * offsets[count] = T (else MOE_ERR_INVALID); 1 <= count <= MOE_MAX_ADAPTERS
+ * (more: MOE_ERR_UNSUPPORTED).  Read during the call only. */
+typedef struct moe_adapters {
+  int32_t count;
+  const int32_t* offsets;
+} moe_adapters;
+
+moe_status moe_lora_multi_pool_capacity(const moe_lora_desc* desc, const moe_adapters* adapters,
+                                        int64_t* rows);
+moe_status moe_lora_multi_workspace_size(const moe_lora_desc* desc, const moe_adapters* adapters,
+                                         size_t* saved_bytes, size_t* scratch_bytes);
+/* build_pool with (expert, adapter) groups: counts [E*count], offsets
+ * [E*count + 1]; rows of a group follow ascending route index. */
+moe_status build_pool_multi(const moe_lora_desc* desc, const moe_adapters* adapters, const int32_t* topk_idx,
+                            int32_t* counts, int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
+                            int64_t capacity, int32_t* device_error, void* stream);
+/* moe_lora_forward / moe_lora_backward over the roots (adapters != NULL). */
+moe_status moe_lora_forward_multi(const moe_lora_desc* desc, const moe_adapters* adapters, const moe_pool* pool,
+                                  const void* x, const float* topk_w, const moe_lora_params* params, void* out,
+                                  void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                                  void* stream);
+moe_status moe_lora_backward_multi(const moe_lora_desc* desc, const moe_adapters* adapters, const moe_pool* pool,
+                                   const void* grad_out, const float* topk_w, const moe_lora_params* params,
+                                   const void* saved, size_t saved_bytes, void* grad_x, float* grad_topk_w,
+                                   const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
+                                   void* stream);
+
 /* Optional per-kernel timing (the pages' backward carries an optional kernel
  * trace: PR #9 review-bot Overview).  When enabled, every kernel the library
  * launches is bracketed by two HIP events recorded on its launch stream; the

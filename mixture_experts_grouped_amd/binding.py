@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional, Tuple
+from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
@@ -26,12 +26,14 @@ MOE_BASE_BF16, MOE_BASE_MXFP4 = 0, 1
 # the saved workspace's device status word (include/moelora.h)
 MOE_SAVED_STATUS_OFFSET = 0
 MOE_SAVED_FP16_RANGE = 1
+MOE_MAX_ADAPTERS = 64
 
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
     "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
     "moe_lora_transform_base", "moe_lora_split_e4m3x2", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
-    "moe_lora_trace_entry", "moe_lora_trace_reset",
+    "moe_lora_trace_entry", "moe_lora_trace_reset", "moe_lora_multi_pool_capacity",
+    "moe_lora_multi_workspace_size", "build_pool_multi", "moe_lora_forward_multi", "moe_lora_backward_multi",
 )
 
 
@@ -67,6 +69,20 @@ class MoeLoraGrads(ctypes.Structure):
     _fields_ = [("dA1", ctypes.c_void_p), ("dA3", ctypes.c_void_p), ("dB1", ctypes.c_void_p),
                 ("dB3", ctypes.c_void_p), ("dA2", ctypes.c_void_p), ("dB2", ctypes.c_void_p),
                 ("dW13", ctypes.c_void_p), ("dW2", ctypes.c_void_p)]
+
+
+class MoeAdapters(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("offsets", ctypes.POINTER(ctypes.c_int32))]
+
+
+def _adapters(roots: Optional[Sequence[int]]):
+    """The C struct for the roots 0 = r0 <= ... <= rNA = T (None: single adapter)."""
+    if roots is None:
+        return None
+    arr = (ctypes.c_int32 * len(roots))(*[int(v) for v in roots])
+    ad = MoeAdapters(len(roots) - 1, arr)
+    ad._keep = arr  # the offsets live as long as the struct
+    return ad
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -110,9 +126,19 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
                                          P(ctypes.c_double)]
     lib.moe_lora_trace_reset.argtypes = []
     lib.moe_lora_trace_reset.restype = None
+    A = P(MoeAdapters)
+    lib.moe_lora_multi_pool_capacity.argtypes = [P(MoeLoraDesc), A, P(ctypes.c_int64)]
+    lib.moe_lora_multi_workspace_size.argtypes = [P(MoeLoraDesc), A, P(ctypes.c_size_t), P(ctypes.c_size_t)]
+    lib.build_pool_multi.argtypes = [P(MoeLoraDesc), A, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp]
+    lib.moe_lora_forward_multi.argtypes = [P(MoeLoraDesc), A, P(MoePool), vp, vp, P(MoeLoraParams), vp,
+                                           vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_backward_multi.argtypes = [P(MoeLoraDesc), A, P(MoePool), vp, vp, P(MoeLoraParams), vp,
+                                            ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp, ctypes.c_size_t, vp]
     for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
                "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
-               "moe_lora_transform_base", "moe_lora_split_e4m3x2"):
+               "moe_lora_transform_base", "moe_lora_split_e4m3x2", "moe_lora_multi_pool_capacity",
+               "moe_lora_multi_workspace_size", "build_pool_multi", "moe_lora_forward_multi",
+               "moe_lora_backward_multi"):
         getattr(lib, fn).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -157,6 +183,21 @@ def moe_lora_workspace_size(desc: MoeLoraDesc) -> Tuple[int, int]:
     return a.value, b.value
 
 
+def moe_lora_multi_pool_capacity(desc: MoeLoraDesc, roots: Sequence[int]) -> int:
+    v = ctypes.c_int64()
+    _check(library().moe_lora_multi_pool_capacity(ctypes.byref(desc), ctypes.byref(_adapters(roots)),
+                                                  ctypes.byref(v)), "moe_lora_multi_pool_capacity")
+    return v.value
+
+
+def moe_lora_multi_workspace_size(desc: MoeLoraDesc, roots: Sequence[int]) -> Tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(library().moe_lora_multi_workspace_size(ctypes.byref(desc), ctypes.byref(_adapters(roots)),
+                                                   ctypes.byref(a), ctypes.byref(b)),
+           "moe_lora_multi_workspace_size")
+    return a.value, b.value
+
+
 def _ptr(t: Optional[torch.Tensor], dtype=None, shape=None, name="tensor") -> Optional[int]:
     if t is None:
         return None
@@ -191,22 +232,44 @@ def build_pool(desc: MoeLoraDesc, topk_idx: torch.Tensor, counts: torch.Tensor,
     _check(st, "build_pool")
 
 
+def build_pool_multi(desc: MoeLoraDesc, roots: Sequence[int], topk_idx: torch.Tensor, counts: torch.Tensor,
+                     offsets: torch.Tensor, route_to_row: torch.Tensor, row_to_route: torch.Tensor,
+                     device_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    """build_pool with (expert, adapter) groups: counts [E * NA], offsets [E * NA + 1]."""
+    T, k, G = desc.T, desc.topk, desc.E * (len(roots) - 1)
+    cap = row_to_route.numel()
+    i32 = torch.int32
+    st = library().build_pool_multi(
+        ctypes.byref(desc), ctypes.byref(_adapters(roots)), _ptr(topk_idx, i32, (T, k), "topk_idx"),
+        _ptr(counts, i32, (G,), "counts"), _ptr(offsets, i32, (G + 1,), "offsets"),
+        _ptr(route_to_row, i32, (T * k,), "route_to_row"), _ptr(row_to_route, i32, (cap,), "row_to_route"), cap,
+        _ptr(device_error, i32, (1,), "device_error"), _stream(stream))
+    _check(st, "build_pool_multi")
+
+
 def _pool_struct(pool: Dict[str, torch.Tensor], bm: int) -> MoePool:
     return MoePool(pool["counts"].data_ptr(), pool["offsets"].data_ptr(),
                    pool["route_to_row"].data_ptr(), pool["row_to_route"].data_ptr(),
                    pool["row_to_route"].numel(), bm)
 
 
-def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc) -> MoeLoraParams:
+def _factor_shapes(desc: MoeLoraDesc, na: Optional[int] = None) -> Dict[str, Tuple[int, ...]]:
+    """Adapter factor shapes; with na adapters stacked over a leading axis."""
+    E, H, I, r = desc.E, desc.H, desc.I, desc.rank
+    shapes = {"A1": (r, H), "A3": (r, H), "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I), "B2": (H, r)}
+    return shapes if na is None else {n: (na,) + s for n, s in shapes.items()}
+
+
+def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc, na: Optional[int] = None) -> MoeLoraParams:
     """bf16 base: W13, W2 bf16.  MXFP4 base (desc.base_format == MOE_BASE_MXFP4):
     W13 uint8 [E, 2I, H/2] and W2 uint8 [E, H, I/2] packed e2m1 (element 2i in
     the low nibble of byte i), W13_scale uint8 [E, 2I, H/32], W2_scale uint8
     [E, H, I/32] e8m0.  Optional "W13T" [E, H, 2I] and "W2T" [E, I, H] bf16: the
-    transformed base (transform_base), read by the backward."""
+    transformed base (transform_base), read by the backward.  With na adapters
+    the six factors are stacked [na, ...]."""
     E, H, I, r = desc.E, desc.H, desc.I, desc.rank
     bf = torch.bfloat16
-    shapes = {"A1": (r, H), "A3": (r, H), "B1": (E, I, r), "B3": (E, I, r), "A2": (E, r, I),
-              "B2": (H, r)}
+    shapes = _factor_shapes(desc, na)
     ptrs = {n: _ptr(p[n], bf, s, n) for n, s in shapes.items()}
     if desc.base_format == MOE_BASE_MXFP4:
         u8 = torch.uint8
@@ -313,6 +376,42 @@ def moe_lora_backward(desc: MoeLoraDesc, pool: Dict[str, torch.Tensor], grad_out
     _check(st, "moe_lora_backward")
 
 
+def moe_lora_forward_multi(desc: MoeLoraDesc, roots: Sequence[int], pool: Dict[str, torch.Tensor],
+                           x: torch.Tensor, topk_w: torch.Tensor, params: Dict[str, torch.Tensor],
+                           out: torch.Tensor, saved: torch.Tensor, scratch: torch.Tensor, stream=None) -> None:
+    """moe_lora_forward over the roots (adapter a: tokens roots[a] .. roots[a+1]-1), factors stacked."""
+    T, H, k = desc.T, desc.H, desc.topk
+    ps = _pool_struct(pool, moe_lora_block_m(desc))
+    pp = _params_struct(params, desc, len(roots) - 1)
+    st = library().moe_lora_forward_multi(
+        ctypes.byref(desc), ctypes.byref(_adapters(roots)), ctypes.byref(ps), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(pp),
+        _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(saved, torch.uint8, None, "saved"), saved.numel(),
+        _ptr(scratch, torch.uint8, None, "scratch"), scratch.numel(), _stream(stream))
+    _check(st, "moe_lora_forward_multi")
+
+
+def moe_lora_backward_multi(desc: MoeLoraDesc, roots: Sequence[int], pool: Dict[str, torch.Tensor],
+                            grad_out: torch.Tensor, topk_w: torch.Tensor, params: Dict[str, torch.Tensor],
+                            saved: torch.Tensor, grad_x: torch.Tensor, grad_topk_w: torch.Tensor,
+                            grads: Dict[str, torch.Tensor], scratch: torch.Tensor, stream=None) -> None:
+    """moe_lora_backward over the roots; the six factor gradients stacked per adapter."""
+    T, H, k = desc.T, desc.H, desc.topk
+    na = len(roots) - 1
+    ps = _pool_struct(pool, moe_lora_block_m(desc))
+    pp = _params_struct(params, desc, na)
+    bf = torch.bfloat16
+    gp = {n: _ptr(grads.get("d" + n), bf, s, "d" + n) for n, s in _factor_shapes(desc, na).items()}
+    gs = MoeLoraGrads(gp["A1"], gp["A3"], gp["B1"], gp["B3"], gp["A2"], gp["B2"], None, None)
+    st = library().moe_lora_backward_multi(
+        ctypes.byref(desc), ctypes.byref(_adapters(roots)), ctypes.byref(ps),
+        _ptr(grad_out, bf, (T, H), "grad_out"), _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(pp),
+        _ptr(saved, torch.uint8, None, "saved"), saved.numel(), _ptr(grad_x, bf, (T, H), "grad_x"),
+        _ptr(grad_topk_w, torch.float32, (T, k), "grad_topk_w"), ctypes.byref(gs),
+        _ptr(scratch, torch.uint8, None, "scratch"), scratch.numel(), _stream(stream))
+    _check(st, "moe_lora_backward_multi")
+
+
 def _sync(stream) -> None:
     if hasattr(stream, "synchronize"):
         stream.synchronize()
@@ -361,23 +460,33 @@ class MoeLoraLayer:
     and the three calls in order.  Convenience for tests and the benchmark."""
 
     def __init__(self, desc: MoeLoraDesc, device="cuda", base_grads: bool = False,
-                 checked: bool = False):
+                 checked: bool = False, roots: Optional[Sequence[int]] = None):
         """base_grads: also compute the frozen-weight gradients dW13, dW2.
         checked: after build_pool read the device error count and after the
         forward the saved status word (each a device-to-host sync), and raise
         if either reports a problem (route ids outside [-1, E), or a gate/up
-        pre-activation beyond the fp16 range the backward needs)."""
+        pre-activation beyond the fp16 range the backward needs).
+        roots: several adapters in one pass (the *_multi calls): adapter a
+        serves tokens roots[a] .. roots[a+1]-1; factors and their gradients
+        are stacked over the adapters."""
         self.desc = desc
         self.device = device
         self.checked = checked
+        self.roots = None if roots is None else [int(v) for v in roots]
+        na = None if roots is None else len(roots) - 1
         self.block_m = moe_lora_block_m(desc)
-        self.capacity = moe_lora_pool_capacity(desc)
-        self.saved_bytes, self.scratch_bytes = moe_lora_workspace_size(desc)
+        if roots is None:
+            self.capacity = moe_lora_pool_capacity(desc)
+            self.saved_bytes, self.scratch_bytes = moe_lora_workspace_size(desc)
+        else:
+            self.capacity = moe_lora_multi_pool_capacity(desc, self.roots)
+            self.saved_bytes, self.scratch_bytes = moe_lora_multi_workspace_size(desc, self.roots)
         T, H, I, E, k, r = desc.T, desc.H, desc.I, desc.E, desc.topk, desc.rank
+        G = E * (1 if na is None else na)
         i32 = torch.int32
         self.pool = {
-            "counts": torch.empty(E, dtype=i32, device=device),
-            "offsets": torch.empty(E + 1, dtype=i32, device=device),
+            "counts": torch.empty(G, dtype=i32, device=device),
+            "offsets": torch.empty(G + 1, dtype=i32, device=device),
             "route_to_row": torch.empty(T * k, dtype=i32, device=device),
             "row_to_route": torch.empty(self.capacity, dtype=i32, device=device),
         }
@@ -388,21 +497,19 @@ class MoeLoraLayer:
         self.out = torch.empty(T, H, dtype=bf, device=device)
         self.grad_x = torch.empty(T, H, dtype=bf, device=device)
         self.grad_topk_w = torch.empty(T, k, dtype=torch.float32, device=device)
-        self.grads = {
-            "dA1": torch.empty(r, H, dtype=bf, device=device),
-            "dA3": torch.empty(r, H, dtype=bf, device=device),
-            "dB1": torch.empty(E, I, r, dtype=bf, device=device),
-            "dB3": torch.empty(E, I, r, dtype=bf, device=device),
-            "dA2": torch.empty(E, r, I, dtype=bf, device=device),
-            "dB2": torch.empty(H, r, dtype=bf, device=device),
-        }
+        self.grads = {"d" + n: torch.empty(sh, dtype=bf, device=device)
+                      for n, sh in _factor_shapes(desc, na).items()}
         if base_grads:
             self.grads["dW13"] = torch.empty(E, 2 * I, H, dtype=bf, device=device)
             self.grads["dW2"] = torch.empty(E, H, I, dtype=bf, device=device)
 
     def build_pool(self, topk_idx: torch.Tensor, stream=None) -> None:
-        build_pool(self.desc, topk_idx, self.pool["counts"], self.pool["offsets"],
-                   self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
+        if self.roots is None:
+            build_pool(self.desc, topk_idx, self.pool["counts"], self.pool["offsets"],
+                       self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
+        else:
+            build_pool_multi(self.desc, self.roots, topk_idx, self.pool["counts"], self.pool["offsets"],
+                             self.pool["route_to_row"], self.pool["row_to_route"], self.device_error, stream)
         if self.checked:
             bad = self.invalid_routes(stream)
             if bad:
@@ -421,15 +528,23 @@ class MoeLoraLayer:
         return int(self.saved[off:off + 4].view(torch.int32).item())
 
     def forward(self, x, topk_w, params, stream=None) -> torch.Tensor:
-        moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, self.scratch, stream)
+        if self.roots is None:
+            moe_lora_forward(self.desc, self.pool, x, topk_w, params, self.out, self.saved, self.scratch, stream)
+        else:
+            moe_lora_forward_multi(self.desc, self.roots, self.pool, x, topk_w, params, self.out, self.saved,
+                                   self.scratch, stream)
         if self.checked and self.saved_status(stream) & MOE_SAVED_FP16_RANGE:
             raise FloatingPointError("moe_lora_forward: a gate/up pre-activation is beyond the fp16 range "
                                      "(|g| or |v| >= 65520) without a clamp; the backward would not be finite")
         return self.out
 
     def backward(self, grad_out, topk_w, params, stream=None):
-        moe_lora_backward(self.desc, self.pool, grad_out, topk_w, params, self.saved,
-                          self.grad_x, self.grad_topk_w, self.grads, self.scratch, stream)
+        if self.roots is None:
+            moe_lora_backward(self.desc, self.pool, grad_out, topk_w, params, self.saved,
+                              self.grad_x, self.grad_topk_w, self.grads, self.scratch, stream)
+        else:
+            moe_lora_backward_multi(self.desc, self.roots, self.pool, grad_out, topk_w, params, self.saved,
+                                    self.grad_x, self.grad_topk_w, self.grads, self.scratch, stream)
         return self.grad_x, self.grad_topk_w, self.grads
 
     def step(self, topk_idx, x, topk_w, params, grad_out, stream=None):

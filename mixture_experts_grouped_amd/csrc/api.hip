@@ -22,6 +22,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 static_assert(MOE_ACT_SWIGLU == 0 && MOE_ACT_GEGLU == 1, "kernels take the activation as template 0 / 1");
 static_assert(MOE_SAVED_STATUS_OFFSET == 0, "the status word is the first field of the saved plan");
+static_assert(MOE_MAX_ADAPTERS == MAX_ADAPTERS, "one adapter limit");
 
 moe_status check_desc(const moe_lora_desc* d) {
   if (d == nullptr) return MOE_ERR_INVALID;
@@ -48,15 +49,55 @@ moe_status check_desc(const moe_lora_desc* d) {
   return MOE_OK;
 }
 
+// The roots of a call: one adapter holding every token, or the caller's.
+struct Roots {
+  int na = 1;
+  int r[MAX_ADAPTERS + 1] = {};
+  int tiles(int tm) const {  // token tiles of tm tokens that never cross roots
+    int n = 0;
+    for (int q = 0; q < na; ++q) n += (r[q + 1] - r[q] + tm - 1) / tm;
+    return n;
+  }
+};
+
+// ad == nullptr: a single adapter.  Otherwise count in [1, MAX_ADAPTERS] and
+// host offsets 0 = o[0] <= o[1] <= ... <= o[count] = T.
+moe_status read_roots(const moe_lora_desc* d, const moe_adapters* ad, Roots& out) {
+  out = Roots{};
+  if (ad == nullptr) {
+    out.r[1] = d->T;
+    return MOE_OK;
+  }
+  if (ad->offsets == nullptr || ad->count < 1) return MOE_ERR_INVALID;
+  if (ad->count > MAX_ADAPTERS) return MOE_ERR_UNSUPPORTED;
+  if (ad->offsets[0] != 0 || ad->offsets[ad->count] != d->T) return MOE_ERR_INVALID;
+  for (int q = 0; q < ad->count; ++q)
+    if (ad->offsets[q + 1] < ad->offsets[q]) return MOE_ERR_INVALID;
+  out.na = ad->count;
+  for (int q = 0; q <= ad->count; ++q) out.r[q] = ad->offsets[q];
+  // the pool's row indices are int32 at any BLOCK_M
+  const int64_t routes = (int64_t)d->T * d->topk;
+  if (routes + std::min<int64_t>((int64_t)d->E * out.na, routes) * 239 >= (int64_t)1 << 31)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// check_desc, then the roots
+moe_status check_call(const moe_lora_desc* d, const moe_adapters* ad, Roots& R) {
+  const moe_status st = check_desc(d);
+  return st != MOE_OK ? st : read_roots(d, ad, R);
+}
+
 int resolve_bm(const moe_lora_desc* d) {
   // The grouped-GEMM tiles start at each expert's first row and mask at its
   // count, so BLOCK_M changes only the padding; the smallest value wastes least.
   return d->block_m != 0 ? d->block_m : 16;
 }
 
-int64_t capacity_of(const moe_lora_desc* d, int bm) {
+// Pool rows: every route plus the padding of each (expert, adapter) group.
+int64_t capacity_of(const moe_lora_desc* d, int bm, int na = 1) {
   const int64_t routes = (int64_t)d->T * d->topk;
-  return routes + std::min<int64_t>(d->E, routes) * (bm - 1);
+  return routes + std::min<int64_t>((int64_t)d->E * na, routes) * (bm - 1);
 }
 
 struct Plan {
@@ -69,13 +110,13 @@ struct Plan {
   size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
-Plan make_plan(const moe_lora_desc* d) {
+Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   Plan p{};
   const int bm = resolve_bm(d);
-  p.cap = capacity_of(d, bm);
+  p.cap = capacity_of(d, bm, R.na);
   const int64_t routes = (int64_t)d->T * d->topk;
-  p.maxtiles = (int)((routes + TMG - 1) / TMG + std::min<int64_t>(d->E, routes));
-  p.nsplit = (d->T + kSharedSplit - 1) / kSharedSplit;
+  p.maxtiles = (int)((routes + TMG - 1) / TMG + std::min<int64_t>((int64_t)d->E * R.na, routes));
+  p.nsplit = R.tiles(kSharedSplit);  // chunks of the shared-factor reductions, per root
   const size_t T = d->T, H = d->H, I = d->I, r = d->rank, cap = (size_t)p.cap;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
@@ -111,9 +152,10 @@ Plan make_plan(const moe_lora_desc* d) {
   p.o_part = take((size_t)3 * p.nsplit * H * r * 4);
   p.o_ZAp = take(cap * 4 * r * 2);
   p.o_dwp = take((size_t)(I / 256) * cap * 4);
-  p.o_A2T = take((size_t)d->E * I * r * 2);  // A2_e^T, with transformed base weights
-  p.o_A1T = take(H * r * 2);                  // A1^T, A3^T for the grad-x rank product
-  p.o_A3T = take(H * r * 2);
+  const size_t na = R.na;
+  p.o_A2T = take(na * d->E * I * r * 2);  // A2_e^T per adapter, with transformed base weights
+  p.o_A1T = take(na * H * r * 2);         // A1^T, A3^T per adapter for the grad-x rank product
+  p.o_A3T = take(na * H * r * 2);
   // forward-only tensors share space with backward-only ones: the base
   // outputs and Z2 are read only by the forward's combine
   p.o_Yb = p.o_dU;  // [cap, H] bf16, same size
@@ -154,12 +196,15 @@ moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
 }
 
 void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, const Plan& p,
-                 const moe_lora_params* w) {
+                 const moe_lora_params* w, const Roots& R) {
   std::memset(&a, 0, sizeof(a));
   a.T = d->T;
   a.H = d->H;
   a.I = d->I;
   a.E = d->E;
+  a.na = R.na;
+  a.EV = d->E * R.na;
+  for (int q = 0; q <= R.na; ++q) a.roots[q] = R.r[q];
   a.k = d->topk;
   a.r = d->rank;
   a.s = d->scale;
@@ -269,12 +314,14 @@ hipError_t scratch_address(void** ptr) {
 // The forward behind both entry points.  noalloc: the scratch is the static
 // array above (scratch / scratch_bytes are ignored); only the forward's part
 // of the plan is used there.
-moe_status forward_checked(const moe_lora_desc* d, const moe_pool* pool, const void* x, const float* topk_w,
-                           const moe_lora_params* params, void* out, void* saved, size_t saved_bytes,
-                           void* scratch_arg, size_t scratch_bytes, bool noalloc, void* stream) {
-  moe_status st = check_desc(d);
+moe_status forward_checked(const moe_lora_desc* d, const moe_adapters* ad, const moe_pool* pool, const void* x,
+                           const float* topk_w, const moe_lora_params* params, void* out, void* saved,
+                           size_t saved_bytes, void* scratch_arg, size_t scratch_bytes, bool noalloc,
+                           void* stream) {
+  Roots R;
+  moe_status st = check_call(d, ad, R);
   if (st != MOE_OK) return st;
-  const Plan p = make_plan(d);
+  const Plan p = make_plan(d, R);
   if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
   if ((st = check_params(d, params)) != MOE_OK) return st;
   if (!aligned16(x) || !aligned16(out) || !aligned16(saved) || topk_w == nullptr)
@@ -294,13 +341,61 @@ moe_status forward_checked(const moe_lora_desc* d, const moe_pool* pool, const v
     if (overlap(rsc, rx) || overlap(rsc, ro) || overlap(rsc, rs)) return MOE_ERR_INVALID;
   }
   LayerArgs a;
-  fill_common(a, d, pool, p, params);
+  fill_common(a, d, pool, p, params, R);
   fill_saved(a, p, saved);
   fill_scratch(a, p, sc);
   a.x = (const uint16_t*)x;
   a.w = topk_w;
   a.out = (uint16_t*)out;
   const hipError_t e = launch_forward(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status backward_checked(const moe_lora_desc* d, const moe_adapters* ad, const moe_pool* pool,
+                            const void* grad_out, const float* topk_w, const moe_lora_params* params,
+                            const void* saved, size_t saved_bytes, void* grad_x, float* grad_topk_w,
+                            const moe_lora_grads* grads, void* scratch, size_t scratch_bytes, void* stream) {
+  Roots R;
+  moe_status st = check_call(d, ad, R);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(d, R);
+  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
+  if ((st = check_params(d, params)) != MOE_OK) return st;
+  if (!aligned16(grad_out) || !aligned16(grad_x) || !aligned16(saved) || !aligned16(scratch) ||
+      topk_w == nullptr || grad_topk_w == nullptr || grads == nullptr)
+    return MOE_ERR_INVALID;
+  const void* gs[] = {grads->dA1, grads->dA3, grads->dB1, grads->dB3, grads->dA2, grads->dB2};
+  for (const void* g : gs)
+    if (!aligned16(g)) return MOE_ERR_INVALID;
+  // the frozen-weight gradients are optional (NULL: not computed)
+  if ((grads->dW13 != nullptr && !aligned16(grads->dW13)) || (grads->dW2 != nullptr && !aligned16(grads->dW2)))
+    return MOE_ERR_INVALID;
+  // frozen-weight gradients sum an expert's rows of every adapter: one adapter only
+  if (R.na > 1 && (grads->dW13 != nullptr || grads->dW2 != nullptr)) return MOE_ERR_UNSUPPORTED;
+  if (saved_bytes < p.saved || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
+  const size_t act = (size_t)d->T * d->H * 2;
+  const Range rgo = rng(grad_out, act), rgx = rng(grad_x, act), rs = rng(saved, p.saved),
+              rsc = rng(scratch, p.scratch);
+  if (overlap(rgo, rgx) || overlap(rgx, rs) || overlap(rgx, rsc) || overlap(rs, rsc) ||
+      overlap(rgo, rsc))
+    return MOE_ERR_INVALID;
+  LayerArgs a;
+  fill_common(a, d, pool, p, params, R);
+  fill_saved(a, p, const_cast<void*>(saved));
+  fill_scratch(a, p, scratch);
+  a.go = (const uint16_t*)grad_out;
+  a.w = topk_w;
+  a.gx = (uint16_t*)grad_x;
+  a.gw = grad_topk_w;
+  a.dA1 = (uint16_t*)grads->dA1;
+  a.dA3 = (uint16_t*)grads->dA3;
+  a.dB1 = (uint16_t*)grads->dB1;
+  a.dB3 = (uint16_t*)grads->dB3;
+  a.dA2 = (uint16_t*)grads->dA2;
+  a.dB2 = (uint16_t*)grads->dB2;
+  a.dW13 = (uint16_t*)grads->dW13;
+  a.dW2 = (uint16_t*)grads->dW2;
+  const hipError_t e = launch_backward(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -329,100 +424,101 @@ moe_status moe_lora_block_m(const moe_lora_desc* d, int32_t* block_m) {
   return MOE_OK;
 }
 
-moe_status moe_lora_pool_capacity(const moe_lora_desc* d, int64_t* rows) {
-  const moe_status st = check_desc(d);
+moe_status moe_lora_multi_pool_capacity(const moe_lora_desc* d, const moe_adapters* ad, int64_t* rows) {
+  Roots R;
+  const moe_status st = check_call(d, ad, R);
   if (st != MOE_OK) return st;
   if (rows == nullptr) return MOE_ERR_INVALID;
-  *rows = capacity_of(d, resolve_bm(d));
+  *rows = capacity_of(d, resolve_bm(d), R.na);
   return MOE_OK;
 }
 
-moe_status moe_lora_workspace_size(const moe_lora_desc* d, size_t* saved_bytes,
-                                   size_t* scratch_bytes) {
-  const moe_status st = check_desc(d);
+moe_status moe_lora_pool_capacity(const moe_lora_desc* d, int64_t* rows) {
+  return moe_lora_multi_pool_capacity(d, nullptr, rows);
+}
+
+moe_status moe_lora_multi_workspace_size(const moe_lora_desc* d, const moe_adapters* ad, size_t* saved_bytes,
+                                         size_t* scratch_bytes) {
+  Roots R;
+  const moe_status st = check_call(d, ad, R);
   if (st != MOE_OK) return st;
   if (saved_bytes == nullptr || scratch_bytes == nullptr) return MOE_ERR_INVALID;
-  const Plan p = make_plan(d);
+  const Plan p = make_plan(d, R);
   *saved_bytes = p.saved;
   *scratch_bytes = p.scratch;
   return MOE_OK;
 }
 
-moe_status build_pool(const moe_lora_desc* d, const int32_t* topk_idx, int32_t* counts,
-                      int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
-                      int64_t capacity, int32_t* device_error, void* stream) {
-  const moe_status st = check_desc(d);
+moe_status moe_lora_workspace_size(const moe_lora_desc* d, size_t* saved_bytes, size_t* scratch_bytes) {
+  return moe_lora_multi_workspace_size(d, nullptr, saved_bytes, scratch_bytes);
+}
+
+moe_status build_pool_multi(const moe_lora_desc* d, const moe_adapters* ad, const int32_t* topk_idx,
+                            int32_t* counts, int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
+                            int64_t capacity, int32_t* device_error, void* stream) {
+  Roots R;
+  const moe_status st = check_call(d, ad, R);
   if (st != MOE_OK) return st;
   if (topk_idx == nullptr || counts == nullptr || offsets == nullptr || route_to_row == nullptr ||
       row_to_route == nullptr)
     return MOE_ERR_INVALID;
   const int bm = resolve_bm(d);
-  if (capacity != capacity_of(d, bm)) return MOE_ERR_INVALID;
-  const hipError_t e = launch_build_pool(topk_idx, d->T * d->topk, d->E, bm, capacity, counts,
-                                         offsets, route_to_row, row_to_route, device_error,
-                                         (hipStream_t)stream);
+  if (capacity != capacity_of(d, bm, R.na)) return MOE_ERR_INVALID;
+  PoolRoots pr;
+  pr.na = R.na;
+  pr.k = d->topk;
+  for (int q = 0; q <= MAX_ADAPTERS; ++q) pr.roots[q] = q <= R.na ? R.r[q] : d->T;
+  const hipError_t e = launch_build_pool(topk_idx, d->T * d->topk, d->E, bm, capacity, counts, offsets,
+                                         route_to_row, row_to_route, device_error, pr, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status build_pool(const moe_lora_desc* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                      int32_t* route_to_row, int32_t* row_to_route, int64_t capacity, int32_t* device_error,
+                      void* stream) {
+  return build_pool_multi(d, nullptr, topk_idx, counts, offsets, route_to_row, row_to_route, capacity,
+                          device_error, stream);
 }
 
 moe_status moe_lora_forward(const moe_lora_desc* d, const moe_pool* pool, const void* x,
                             const float* topk_w, const moe_lora_params* params, void* out,
                             void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
                             void* stream) {
-  return forward_checked(d, pool, x, topk_w, params, out, saved, saved_bytes, scratch, scratch_bytes, false,
+  return forward_checked(d, nullptr, pool, x, topk_w, params, out, saved, saved_bytes, scratch, scratch_bytes,
+                         false, stream);
+}
+
+moe_status moe_lora_forward_multi(const moe_lora_desc* d, const moe_adapters* ad, const moe_pool* pool,
+                                  const void* x, const float* topk_w, const moe_lora_params* params, void* out,
+                                  void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                                  void* stream) {
+  if (ad == nullptr) return MOE_ERR_INVALID;
+  return forward_checked(d, ad, pool, x, topk_w, params, out, saved, saved_bytes, scratch, scratch_bytes, false,
                          stream);
 }
 
 moe_status moe_lora_forward_noalloc(const moe_lora_desc* d, const moe_pool* pool, const void* x,
                                     const float* topk_w, const moe_lora_params* params, void* out,
                                     void* saved, size_t saved_bytes, void* stream) {
-  return forward_checked(d, pool, x, topk_w, params, out, saved, saved_bytes, nullptr, 0, true, stream);
+  return forward_checked(d, nullptr, pool, x, topk_w, params, out, saved, saved_bytes, nullptr, 0, true, stream);
 }
 
-moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool,
-                             const void* grad_out, const float* topk_w,
-                             const moe_lora_params* params, const void* saved,
-                             size_t saved_bytes, void* grad_x, float* grad_topk_w,
-                             const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
-                             void* stream) {
-  moe_status st = check_desc(d);
-  if (st != MOE_OK) return st;
-  const Plan p = make_plan(d);
-  if ((st = check_pool(d, pool, p)) != MOE_OK) return st;
-  if ((st = check_params(d, params)) != MOE_OK) return st;
-  if (!aligned16(grad_out) || !aligned16(grad_x) || !aligned16(saved) || !aligned16(scratch) ||
-      topk_w == nullptr || grad_topk_w == nullptr || grads == nullptr)
-    return MOE_ERR_INVALID;
-  const void* gs[] = {grads->dA1, grads->dA3, grads->dB1, grads->dB3, grads->dA2, grads->dB2};
-  for (const void* g : gs)
-    if (!aligned16(g)) return MOE_ERR_INVALID;
-  // the frozen-weight gradients are optional (NULL: not computed)
-  if ((grads->dW13 != nullptr && !aligned16(grads->dW13)) || (grads->dW2 != nullptr && !aligned16(grads->dW2)))
-    return MOE_ERR_INVALID;
-  if (saved_bytes < p.saved || scratch_bytes < p.scratch) return MOE_ERR_WORKSPACE;
-  const size_t act = (size_t)d->T * d->H * 2;
-  const Range rgo = rng(grad_out, act), rgx = rng(grad_x, act), rs = rng(saved, p.saved),
-              rsc = rng(scratch, p.scratch);
-  if (overlap(rgo, rgx) || overlap(rgx, rs) || overlap(rgx, rsc) || overlap(rs, rsc) ||
-      overlap(rgo, rsc))
-    return MOE_ERR_INVALID;
-  LayerArgs a;
-  fill_common(a, d, pool, p, params);
-  fill_saved(a, p, const_cast<void*>(saved));
-  fill_scratch(a, p, scratch);
-  a.go = (const uint16_t*)grad_out;
-  a.w = topk_w;
-  a.gx = (uint16_t*)grad_x;
-  a.gw = grad_topk_w;
-  a.dA1 = (uint16_t*)grads->dA1;
-  a.dA3 = (uint16_t*)grads->dA3;
-  a.dB1 = (uint16_t*)grads->dB1;
-  a.dB3 = (uint16_t*)grads->dB3;
-  a.dA2 = (uint16_t*)grads->dA2;
-  a.dB2 = (uint16_t*)grads->dB2;
-  a.dW13 = (uint16_t*)grads->dW13;
-  a.dW2 = (uint16_t*)grads->dW2;
-  const hipError_t e = launch_backward(a, (hipStream_t)stream);
-  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+moe_status moe_lora_backward(const moe_lora_desc* d, const moe_pool* pool, const void* grad_out,
+                             const float* topk_w, const moe_lora_params* params, const void* saved,
+                             size_t saved_bytes, void* grad_x, float* grad_topk_w, const moe_lora_grads* grads,
+                             void* scratch, size_t scratch_bytes, void* stream) {
+  return backward_checked(d, nullptr, pool, grad_out, topk_w, params, saved, saved_bytes, grad_x, grad_topk_w,
+                          grads, scratch, scratch_bytes, stream);
+}
+
+moe_status moe_lora_backward_multi(const moe_lora_desc* d, const moe_adapters* ad, const moe_pool* pool,
+                                   const void* grad_out, const float* topk_w, const moe_lora_params* params,
+                                   const void* saved, size_t saved_bytes, void* grad_x, float* grad_topk_w,
+                                   const moe_lora_grads* grads, void* scratch, size_t scratch_bytes,
+                                   void* stream) {
+  if (ad == nullptr) return MOE_ERR_INVALID;
+  return backward_checked(d, ad, pool, grad_out, topk_w, params, saved, saved_bytes, grad_x, grad_topk_w, grads,
+                          scratch, scratch_bytes, stream);
 }
 
 moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,

@@ -44,14 +44,16 @@ struct LdQ {
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
+// One token tile (one root) per workgroup: B2 of the root's adapter.
 __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GS64::TM;
+  int t0, nt, ad;
+  if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
   const int r = a.r;
   LdQ L;
-  L.m.contig(a.go, t0, a.T - t0, a.H);
+  L.m.contig(a.go, t0, nt, a.H);
   L.m.window(a.H);
-  L.n.kp = KStrided{make_rsrc(a.B2, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
+  L.n.kp = KStrided{make_rsrc(a.B2 + (long)ad * a.H * r, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
   L.n.cols(0, r);
   f32x16 acc[GS64::NB][GS64::MB];
   mainloop<GS64>(L, a.H / KT, acc, smem);
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
 #pragma unroll
   for (int mb = 0; mb < GS64::MB; ++mb) {
     const int t = t0 + ep.row(mb);
-    if (t >= a.T) continue;
+    if (t >= t0 + nt) continue;
 #pragma unroll
     for (int nb = 0; nb < GS64::NB; ++nb)
 #pragma unroll
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   const int next = (2 * r + G::KT - 1) / G::KT;
+  const long e = grp_expert(a, ti.e), le = grp_local(a, ti.e);  // base expert; A2 of its adapter
   if constexpr (TW) {
     LdW2dK L;
     L.next = next;
@@ -203,9 +206,9 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
       L.mm.from_tokens(a.go, a.T, a.H, tk);
     }
     L.me.window(2 * r);
-    L.ne.contig(a.A2T + (long)ti.e * a.I * r, i0, G::TN, r);
+    L.ne.contig(a.A2T + le * a.I * r, i0, G::TN, r);
     L.ne.window(2 * r, r);  // k in [r, 2r) reads A2T column k - r again (lo half)
-    L.nm.contig(a.W2T + (long)ti.e * a.I * a.H, i0, G::TN, a.H);
+    L.nm.contig(a.W2T + e * a.I * a.H, i0, G::TN, a.H);
     v2::run_stages2<G, 0>(L, next + a.H / G::KT, acc, smem);
   } else if constexpr (!MX) {
     {
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
       LdW2dExt::KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
       X.me.from_tokens(a.sq, a.T, 2 * r, tk);
       X.me.window(2 * r);
-      X.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+      X.ne.kp = v2::TStrided{make_rsrc(a.A2 + le * r * a.I, (uint64_t)r * a.I * 2),
                              (uint32_t)(2 * a.I), 0, 2 * r, r};
       X.ne.cols(i0, G::TN);
       v2::run_stages2<G, 0>(X, next, acc, smem);
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
       v2::KLoad<256, G::KT, 4>::tokens(tk, a.row2r, a.k, ti.row0, nrows);
       Mn.mm.from_tokens(a.go, a.T, a.H, tk);
     }
-    Mn.nm.set(a.W2 + (long)ti.e * a.H * a.I, a.H, a.I, i0);
+    Mn.nm.set(a.W2 + e * a.H * a.I, a.H, a.I, i0);
     v2::run_pingpong<G>(Mn, a.H / G::KT, acc, smem);
   } else {
     // MXFP4 base: the W2 tile is register-staged and expanded to bf16 in LDS
@@ -239,10 +242,10 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
       L.mm.from_tokens(a.go, a.T, a.H, tk);
     }
     L.me.window(2 * r);
-    L.ne.kp = v2::TStrided{make_rsrc(a.A2 + (long)ti.e * r * a.I, (uint64_t)r * a.I * 2),
+    L.ne.kp = v2::TStrided{make_rsrc(a.A2 + le * r * a.I, (uint64_t)r * a.I * 2),
                            (uint32_t)(2 * a.I), 0, 2 * r, r};
     L.ne.cols(i0, G::TN);
-    L.nq.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), a.H, a.I, i0);
+    L.nq.set(a.W2q + e * a.H * (a.I / 2), a.W2s + e * a.H * (a.I / 32), a.H, a.I, i0);
     v2::run_stages2<G, 0>(L, L.next + a.H / G::KT, acc, smem);
   }
   // G and V come in accumulator-blocked (as the forward wrote them); dg and
@@ -457,21 +460,21 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int h0 = nt * G::TN;
+  const long e = grp_expert(a, ti.e);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   if constexpr (TW) {
     LdW13dK L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
-    L.n.contig(a.W13T + (long)ti.e * a.H * 2 * a.I, h0, G::TN, 2 * a.I);
+    L.n.contig(a.W13T + e * a.H * 2 * a.I, h0, G::TN, 2 * a.I);
     v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
   } else {
     typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
     if constexpr (MX)
-      L.nq.set(a.W13q + (long)ti.e * 2 * a.I * (a.H / 2), a.W13s + (long)ti.e * 2 * a.I * (a.H / 32),
-               2 * a.I, a.H, h0);
+      L.nq.set(a.W13q + e * 2 * a.I * (a.H / 2), a.W13s + e * 2 * a.I * (a.H / 32), 2 * a.I, a.H, h0);
     else
-      L.n.set(a.W13 + (long)ti.e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
+      L.n.set(a.W13 + e * 2 * a.I * a.H, 2 * a.I, a.H, h0);
     if constexpr (!MX)
       v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
     else
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   LdP L;
   L.m.contig(a.dGV + which * a.I, row0, ti.row_end - row0, 2 * a.I);
   L.m.window(a.I);
-  const uint16_t* Be = (which ? a.B3 : a.B1) + (long)ti.e * a.I * r;
+  const uint16_t* Be = (which ? a.B3 : a.B1) + grp_local(a, ti.e) * a.I * r;
   L.n.kp = KStrided{make_rsrc(Be, (uint64_t)a.I * r * 2), (uint32_t)(2 * r), 0, a.I, 0};
   L.n.cols(0, r);
   f32x16 acc[GS128::NB][GS128::MB];
@@ -594,23 +597,25 @@ struct LdRankDxK {
 // grad_x = [A1; A3]^T pc_t + sum_j dU_(t,j) for 256 tokens x 256 columns
 __global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
+  int t0, nt, ad;
+  if (!token_tile(a, blockIdx.x, GRK::TM, t0, nt, ad)) return;
+  const int h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
   RouteVec rv;
-  load_routes<false>(a, t0, rv);
+  load_routes<false>(a, t0, t0 + nt, rv);
   LdRankDxK L;
   L.r = r;
   L.nst = (2 * r + GRK::KT - 1) / GRK::KT;
-  L.m.contig(a.pc, t0, a.T - t0, 4 * r);
+  L.m.contig(a.pc, t0, nt, 4 * r);
   L.m.window(4 * r);
-  L.n1.contig(a.A1T, h0, GRK::TN, r);
+  L.n1.contig(a.A1T + (long)ad * a.H * r, h0, GRK::TN, r);  // the root's adapter's factors
   L.n1.window(2 * r, r);
-  L.n3.contig(a.A3T, h0, GRK::TN, r);
+  L.n3.contig(a.A3T + (long)ad * a.H * r, h0, GRK::TN, r);
   L.n3.window(2 * r, r);
   f32x16 acc[GRK::NB][GRK::MB];
   zero_acc<GRK>(acc);
   v2::run_stages2<GRK, 0>(L, 2 * L.nst, acc, smem);
-  rank_route_sum<false>(acc, smem, a, rv, a.dU, a.gx, t0, h0);
+  rank_route_sum<false>(acc, smem, a, rv, a.dU, a.gx, t0, t0 + nt, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
 __global__ __launch_bounds__(256) void k_gather_za(LayerArgs a) {
   const long p = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (p >= a.offsets[a.E]) return;
+  if (p >= a.offsets[a.EV]) return;
   const int f = a.row2r[p];
   if (f < 0) return;  // padding rows are never read
   const u32x4* src = (const u32x4*)(a.ZA + (long)(f / a.k) * 4 * a.r);
@@ -674,7 +679,8 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   // an expert's column tiles share its rank operand rows: keep them on one
   // XCD (each XCD walks a contiguous range of tiles), so its L2 serves them
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int e = b / nti, i0 = (b % nti) * 256, which = blockIdx.y;
+  const int e = b / nti, i0 = (b % nti) * 256, which = blockIdx.y;  // e: pool group
+  const long le = grp_local(a, e);  // output slot of the group's expert-local factors
   const int r = a.r;
   const int ne = a.counts[e], off = a.offsets[e];
   LdWg2 L;
@@ -708,7 +714,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
         *(u32x2*)(smem + ep.row(mb) * P + c * 2) = v;
       }
     __syncthreads();
-    uint16_t* d = (which ? a.dB3 : a.dB1) + ((long)e * a.I + i0) * r;
+    uint16_t* d = (which ? a.dB3 : a.dB1) + (le * a.I + i0) * r;
     for (int idx = threadIdx.x; idx < 256 * cpr; idx += G::NT) {
       const int row = idx / cpr, ch = idx - row * cpr;
       *(u32x4*)(d + (long)row * r + 8 * ch) = *(const u32x4*)(smem + row * P + 16 * ch);
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
           *(uint16_t*)(smem + (c + q) * P + i * 2) = (uint16_t)f2bf(acc[0][mb][4 * g + q] + acc[1][mb][4 * g + q]);
       }
     __syncthreads();
-    uint16_t* d = a.dA2 + (long)e * r * a.I + i0;
+    uint16_t* d = a.dA2 + le * r * a.I + i0;
     for (int idx = threadIdx.x; idx < r * 32; idx += G::NT) {
       const int c = idx / 32, ch = idx - c * 32;
       *(u32x4*)(d + (long)c * a.I + 8 * ch) = *(const u32x4*)(smem + c * P + 16 * ch);
@@ -739,7 +745,9 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
 //   which 0: dA1[c][h] = sum_t (s pc1)[t][c] x[t][h]   (x_t from the saved copy)
 //   which 1: dA3[c][h] = sum_t (s pc3)[t][c] x[t][h]
 //   which 2: dB2[h][c] = sum_t go[t][h] zc[t][c]
-// Token range split in fixed chunks; partials summed in chunk order.
+// Each root's token range split in fixed chunks of kspl tokens (the chunks
+// of all roots numbered in root order); a root's partials are summed in
+// chunk order into its adapter's gradients.
 // ----------------------------------------------------------------------------
 // Both operands K-outer (K = the split's tokens), as in k_wgrad_local.
 __global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
@@ -748,8 +756,8 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
   const int ntm = a.H / 256;
   const int h0 = (blockIdx.x % ntm) * 256, sp = blockIdx.x / ntm, which = blockIdx.y;
   const int r = a.r;
-  const int tb = sp * a.kspl;
-  const int nt = min(a.kspl, a.T - tb);
+  int tb, nt, ad;
+  if (!token_tile(a, sp, a.kspl, tb, nt, ad)) return;
   LdWg2 L;
   const uint16_t* mrow0 = (which < 2 ? a.Xs : a.go) + (long)tb * a.H;  // x_t from the forward's saved copy
   if (which < 2) {
@@ -787,16 +795,21 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
   }
 }
 
+// Adapter blockIdx.z: the partials of its root's chunks, in chunk order (an
+// empty root writes zeros).
 __global__ __launch_bounds__(256) void k_reduce_shared(LayerArgs a) {
   const long n = (long)a.H * a.r;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const int which = blockIdx.y;
+  const int which = blockIdx.y, ad = blockIdx.z;
   if (i >= n) return;
-  const float* p = a.part + (long)which * a.nsplit * n + i;
+  int c0 = 0;
+  for (int q = 0; q < ad; ++q) c0 += (a.roots[q + 1] - a.roots[q] + a.kspl - 1) / a.kspl;
+  const int nc = (a.roots[ad + 1] - a.roots[ad] + a.kspl - 1) / a.kspl;
+  const float* p = a.part + ((long)which * a.nsplit + c0) * n + i;
   float s = 0.0f;
-  for (int sp = 0; sp < a.nsplit; ++sp) s += p[(long)sp * n];
+  for (int sp = 0; sp < nc; ++sp) s += p[(long)sp * n];
   uint16_t* d = which == 0 ? a.dA1 : (which == 1 ? a.dA3 : a.dB2);
-  d[i] = (uint16_t)f2bf(s);
+  d[(long)ad * n + i] = (uint16_t)f2bf(s);
 }
 
 // ----------------------------------------------------------------------------
@@ -811,7 +824,7 @@ template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_pool_rows(LayerArgs a, const uint16_t* src, uint16_t* dst) {
   const long p = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (p >= a.offsets[a.E]) return;
+  if (p >= a.offsets[a.EV]) return;
   const int f = a.row2r[p];
   if (f < 0) return;  // padding rows are never read
   const u32x4* s = (const u32x4*)(src + (long)(f / a.k) * a.H);
@@ -1000,13 +1013,13 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     return ai.err;
   });
   if (ierr != hipSuccess) return ierr;
-  MOE_LAUNCH(k_q, dim3((a.T + GS64::TM - 1) / GS64::TM), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM)), dim3(256), GS64::LDS_BYTES, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
     const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base
     if (tw) {
-      // A2T = A2_e^T per expert ([E, I, r]), the K-tile rank operand
-      const hipError_t e = launch_transpose(a.A2, a.A2T, a.E, a.r, a.I, st);
+      // A2T = A2_e^T per expert and adapter ([na, E, I, r]), the K-tile rank operand
+      const hipError_t e = launch_transpose(a.A2, a.A2T, a.na * a.E, a.r, a.I, st);
       if (e != hipSuccess) return e;
     }
     if (tw)
@@ -1031,18 +1044,18 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   const long npc = (long)a.T * (2 * a.r / 4);
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   {
-    hipError_t e = launch_transpose(a.A1, a.A1T, 1, a.r, a.H, st);
-    if (e == hipSuccess) e = launch_transpose(a.A3, a.A3T, 1, a.r, a.H, st);
+    hipError_t e = launch_transpose(a.A1, a.A1T, a.na, a.r, a.H, st);
+    if (e == hipSuccess) e = launch_transpose(a.A3, a.A3T, a.na, a.r, a.H, st);
     if (e != hipSuccess) return e;
   }
-  MOE_LAUNCH(k_rank_dx, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
+  MOE_LAUNCH(k_rank_dx, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_wgrad_local, dim3(a.E * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);
+  MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);
   MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(GWG::NT), GWG::LDS_BYTES, st, a);
   const long nsh = (long)a.H * a.r;
-  MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3), dim3(256), 0, st, a);
-  if (a.dW13 != nullptr || a.dW2 != nullptr) {
+  MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3, a.na), dim3(256), 0, st, a);
+  if (a.dW13 != nullptr || a.dW2 != nullptr) {  // one adapter only (pool groups = experts)
     const unsigned prow = (unsigned)((a.cap + 3) / 4);  // rows past the pool's end return at once
     if (a.dW13 != nullptr) {
       MOE_LAUNCH(k_pool_rows<false>, dim3(prow), dim3(256), 0, st, a, a.Xs, a.dU);

@@ -451,7 +451,7 @@ __device__ __forceinline__ bool live_tile(int b, int ntm, int nn, int gm, int& m
 
 // Grouped-GEMM M tile: rows [row0, row_end) of expert e in the pool.
 struct TileInfo {
-  int e, row0, row_end, pad;
+  int e, row0, row_end, pad;  // e: the tile's pool group (its expert, with several adapters its adapter too)
 };
 
 }  // namespace moelora

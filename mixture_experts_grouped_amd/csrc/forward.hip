@@ -42,14 +42,17 @@ struct LdPlain {
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
+// One token tile (one root) per workgroup row: the root's adapter's factor.
 __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GS64::TM, fac = blockIdx.y;  // fac 0: A1, 1: A3
+  const int fac = blockIdx.y;  // fac 0: A1, 1: A3
+  int t0, nt, ad;
+  if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
   const int r = a.r;
   LdPlain<GS64::TM> L;
-  L.m.contig(a.x, t0, a.T - t0, a.H);
+  L.m.contig(a.x, t0, nt, a.H);
   L.m.window(a.H);
-  L.n.contig(fac ? a.A3 : a.A1, 0, r, a.H);
+  L.n.contig((fac ? a.A3 : a.A1) + (long)ad * r * a.H, 0, r, a.H);
   L.n.window(a.H);
   f32x16 acc[GS64::NB][GS64::MB];
   mainloop<GS64>(L, a.H / KT, acc, smem);
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
 #pragma unroll
     for (int mb = 0; mb < GS64::MB; ++mb) {
       const int t = t0 + ep.row(mb);
-      if (t >= a.T) continue;
+      if (t >= t0 + nt) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
@@ -146,7 +149,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   int mt, nt;
   if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
-  const int e = ti.e, i0 = nt * HALF;
+  const int e = grp_expert(a, ti.e), i0 = nt * HALF;
+  const long le = grp_local(a, ti.e);  // the tile's adapter's B1/B3 of expert e
   const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
   const int nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
@@ -161,8 +165,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     L.nsplit = nsplit;
     L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
     L.me.window(4 * r);
-    L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-    L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs = make_rsrc(a.B1 + le * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs2 = make_rsrc(a.B3 + le * a.I * r, (uint64_t)2 * r * a.I);
 #pragma unroll
     for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
     L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
@@ -183,8 +187,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
       L.me.from_tokens(a.ZA, a.T, 4 * r, tke);
     }
     L.me.window(4 * r);
-    L.ne.rs = make_rsrc(a.B1 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
-    L.ne.rs2 = make_rsrc(a.B3 + (long)e * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs = make_rsrc(a.B1 + le * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs2 = make_rsrc(a.B3 + le * a.I * r, (uint64_t)2 * r * a.I);
 #pragma unroll
     for (int j = 0; j < KE::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KE::row_of(j) % HALF)) * r * 2);
     L.ne.window(2 * r, r, HALF, 2 * r);
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const long row0 = ti.row0 + (long)(blockIdx.x % A2_SUB) * GS128::TM;  // this sub-tile's rows
   if (row0 >= ti.row_end) return;
-  const uint16_t* A2e = a.A2 + (long)ti.e * a.r * a.I;
+  const uint16_t* A2e = a.A2 + grp_local(a, ti.e) * a.r * a.I;
   LdPlain<GS128::TM> L;
   L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
   L.m.window(a.I);
@@ -318,14 +322,15 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   if constexpr (!MX) {
     LdW2 L;
     L.m.contig(a.Hh, ti.row0, nrows, a.I);
-    L.n.contig(a.W2 + (long)ti.e * a.H * a.I, h0, G::TN, a.I);
+    L.n.contig(a.W2 + (long)grp_expert(a, ti.e) * a.H * a.I, h0, G::TN, a.I);
     v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
   } else {
     // MXFP4 base: h as its two-term split, W2 packed, on the scaled matrix cores
     LdMX N;
     N.xa.contig((const uint16_t*)a.HQ, ti.row0, nrows, a.I);  // 2I bytes a row, like a bf16 row
     const uint32_t sbytes = (uint32_t)(a.I / 64) * 4u;
-    N.wl.set(a.W2q + (long)ti.e * a.H * (a.I / 2), a.W2s + (long)ti.e * a.H * (a.I / 32), (long)a.H, a.I,
+    const long e = grp_expert(a, ti.e);
+    N.wl.set(a.W2q + e * a.H * (a.I / 2), a.W2s + e * a.H * (a.I / 32), (long)a.H, a.I,
              [&](int n) { return h0 + n; }, a.HS + (long)ti.row0 * (a.I / 64), (long)(nrows < G::TM ? nrows : G::TM),
              [&](int row) { return row < nrows ? (uint32_t)row * sbytes : OFF_NONE; });
     mx::run_mx<G>(N, 0, a.I / 64, acc, smem);
@@ -386,23 +391,26 @@ struct LdRankC {
   }
 };
 
-// out = B2 zc_t + sum_j w_tj Ybase_(t,j) for 256 tokens x 256 columns (zc
-// carries s and the routing weights; hi/lo halves fold onto B2's r columns)
+// out = B2 zc_t + sum_j w_tj Ybase_(t,j) for 256 tokens (of one root) x 256
+// columns (zc carries s and the routing weights; hi/lo halves fold onto B2's
+// r columns; B2 of the root's adapter)
 __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int t0 = blockIdx.x * GRK::TM, h0 = blockIdx.y * GRK::TN;
+  int t0, nt, ad;
+  if (!token_tile(a, blockIdx.x, GRK::TM, t0, nt, ad)) return;
+  const int h0 = blockIdx.y * GRK::TN;
   const int r = a.r;
   RouteVec rv;
-  load_routes<true>(a, t0, rv);
+  load_routes<true>(a, t0, t0 + nt, rv);
   LdRankC L;
-  L.m.contig(a.zc, t0, a.T - t0, 2 * r);
+  L.m.contig(a.zc, t0, nt, 2 * r);
   L.m.window(2 * r);
-  L.n.contig(a.B2, h0, GRK::TN, r);
+  L.n.contig(a.B2 + (long)ad * a.H * r, h0, GRK::TN, r);
   L.n.window(2 * r, r);
   f32x16 acc[GRK::NB][GRK::MB];
   zero_acc<GRK>(acc);
   v2::run_stages2<GRK, 0>(L, (2 * r + GRK::KT - 1) / GRK::KT, acc, smem);
-  rank_route_sum<true>(acc, smem, a, rv, a.Yb, a.out, t0, h0);
+  rank_route_sum<true>(acc, smem, a, rv, a.Yb, a.out, t0, t0 + nt, h0);
 }
 
 // ----------------------------------------------------------------------------
@@ -450,8 +458,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
-  const int tm = (a.T + GS64::TM - 1) / GS64::TM;
-  MOE_LAUNCH(k_shrink, dim3(tm, 2), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2), dim3(256), GS64::LDS_BYTES, st, a);
   if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
     MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
@@ -475,7 +482,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     MOE_LAUNCH(k_w2<false>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_rank_combine, dim3((a.T + GRK::TM - 1) / GRK::TM, a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
+  MOE_LAUNCH(k_rank_combine, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ static_assert(RS_TOK % RS_TPT == 0, "whole steps");
 
 // Lane-distributed routes of the thread's tokens: for token slot i, lane g*16
 // + j of each 16-lane group g holds route j's pool row (-1: dead route, or a
-// token past T) and its coefficient (0 for a dead route, whose weight is not
+// token past the tile) and its coefficient (0 for a dead route, whose weight is not
 // read).  topk <= 16.
 struct RouteVec {
   int row[RS_TOK];
@@ -45,15 +45,16 @@ __device__ __forceinline__ int rs_token(int i) {
 }
 
 // Issued before the GEMM, so the index loads are long done when the sum runs.
+// The tile's tokens are t0 .. tend - 1.
 template <bool WEIGHTED>
-__device__ __forceinline__ void load_routes(const LayerArgs& a, int t0, RouteVec& rv) {
+__device__ __forceinline__ void load_routes(const LayerArgs& a, int t0, int tend, RouteVec& rv) {
   const int j = threadIdx.x & 15;
 #pragma unroll
   for (int i = 0; i < RS_TOK; ++i) {
     const int t = t0 + rs_token(i);
     int row = -1;
     float c = 0.0f;
-    if (t < a.T && j < a.k) {
+    if (t < tend && j < a.k) {
       row = a.r2row[(long)t * a.k + j];
       if (row >= 0) c = WEIGHTED ? a.w[(long)t * a.k + j] : 1.0f;
     }
@@ -62,12 +63,12 @@ __device__ __forceinline__ void load_routes(const LayerArgs& a, int t0, RouteVec
   }
 }
 
-// acc holds the tile's P (tokens t0.., columns h0..); out rows t0 .. T-1.
+// acc holds the tile's P (tokens t0.., columns h0..); out rows t0 .. tend-1.
 template <bool WEIGHTED>
 __device__ __forceinline__ void rank_route_sum(const f32x16 (&acc)[GRK::NB][GRK::MB], char* smem,
                                                const LayerArgs& a, const RouteVec& rv,
                                                const uint16_t* __restrict__ R,
-                                               uint16_t* __restrict__ out, int t0, int h0) {
+                                               uint16_t* __restrict__ out, int t0, int tend, int h0) {
   static_assert(GRK::NB == 2, "one block column per half");
   Epi<GRK> ep;
   const int lane = threadIdx.x & 63, gbase = lane & 48, li = lane & 15;
@@ -122,7 +123,7 @@ __device__ __forceinline__ void rank_route_sum(const f32x16 (&acc)[GRK::NB][GRK:
 #pragma unroll
       for (int u = 0; u < RS_TPT; ++u) {
         const int t = t0 + rs_token(i0 + u);
-        if (t < a.T)
+        if (t < tend)
           *(u32x4*)(out + (long)t * H + hc) = u32x4{pack2(o[u][0], o[u][1]), pack2(o[u][2], o[u][3]),
                                                     pack2(o[u][4], o[u][5]), pack2(o[u][6], o[u][7])};
       }

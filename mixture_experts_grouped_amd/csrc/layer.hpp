@@ -12,6 +12,7 @@ namespace moelora {
 
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
 constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
+constexpr int MAX_ADAPTERS = 64;  // adapters of one multi-adapter pass
 
 // Accumulator-blocked layout of a [tiles x 256, I] tensor (fp16 here) that is
 // written and read only by kernels holding it in 32 x 32 MFMA accumulator
@@ -32,6 +33,13 @@ struct LayerArgs {
   float s;
   long cap;
   int maxtiles;
+  // adapters (multi-adapter pass, OpenPipe/ART PR #1139, Behavior): na roots
+  // of tokens, root q = tokens roots[q] .. roots[q+1]-1, each with its own
+  // factors.  The pool groups rows by (expert e, adapter q) as group
+  // g = e * na + q (EV = E * na groups; na = 1: g = e).  Shared factors are
+  // stacked [na, ...], expert-local ones [na, E, ...].
+  int na, EV;
+  int roots[MAX_ADAPTERS + 1];
   // pool
   const int32_t* counts;
   const int32_t* offsets;
@@ -81,16 +89,55 @@ struct LayerArgs {
   float* P;          // [cap, 2r] B1_e^T dg | B3_e^T dv
   uint16_t* pc;      // [T, 4r]   s * sum_j P as hi/lo (pc1 | pc3)
   float* part;       // [3, nsplit, H*r] split-K partials of the shared-factor gradients
+                     // (chunks of kspl tokens, per root: token_tile(.., kspl, ..))
   uint16_t* ZAp;     // [cap, 4r] ZA gathered to pool rows (real rows only)
   float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
-  uint16_t* A2T;     // [E, I, r]  A2_e^T (backward scratch, with W2T only)
-  uint16_t *A1T, *A3T;  // [H, r]  A1^T, A3^T (backward scratch)
+  uint16_t* A2T;     // [na, E, I, r]  A2_e^T (backward scratch, with W2T only)
+  uint16_t *A1T, *A3T;  // [na, H, r]  A1^T, A3^T (backward scratch)
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;
   float* gw;
   uint16_t *dA1, *dA3, *dB1, *dB3, *dA2, *dB2, *dW13, *dW2;
 };
+
+// Pool group g -> its expert (base weights), its adapter, and the index
+// q * E + e of its expert-local factors in their [na, E, ...] stacks.
+__device__ __forceinline__ int grp_expert(const LayerArgs& a, int g) { return a.na == 1 ? g : g / a.na; }
+__device__ __forceinline__ int grp_adapter(const LayerArgs& a, int g) { return a.na == 1 ? 0 : g % a.na; }
+__device__ __forceinline__ long grp_local(const LayerArgs& a, int g) {
+  return a.na == 1 ? g : (long)(g % a.na) * a.E + g / a.na;
+}
+
+// Token tile b of TM tokens: tiles never cross roots, so every tile has one
+// adapter.  Tiles of root q follow those of roots < q.  Returns false past
+// the last tile.  (Wave-uniform: b is a block index.)
+__device__ __forceinline__ bool token_tile(const LayerArgs& a, int b, int TM, int& t0, int& nt, int& ad) {
+  if (a.na == 1) {
+    t0 = b * TM;
+    nt = a.T - t0 < TM ? a.T - t0 : TM;
+    ad = 0;
+    return nt > 0;
+  }
+  for (int q = 0; q < a.na; ++q) {
+    const int r0 = a.roots[q], r1 = a.roots[q + 1];
+    const int n = (r1 - r0 + TM - 1) / TM;
+    if (b < n) {
+      t0 = r0 + b * TM;
+      nt = r1 - t0 < TM ? r1 - t0 : TM;
+      ad = q;
+      return true;
+    }
+    b -= n;
+  }
+  return false;
+}
+// Host side: the number of such tiles.
+inline int token_tiles(const LayerArgs& a, int TM) {
+  int n = 0;
+  for (int q = 0; q < a.na; ++q) n += (a.roots[q + 1] - a.roots[q] + TM - 1) / TM;
+  return n;
+}
 
 // The first error of a run of kernel-attribute calls.
 struct AttrInit {
@@ -123,9 +170,14 @@ class PerDeviceOnce {
   uint64_t done_ = 0;  // bit d: device d initialised
 };
 
+// Roots of a multi-adapter pool build (na = 1: every route's group is its expert).
+struct PoolRoots {
+  int na, k;
+  int roots[MAX_ADAPTERS + 1];
+};
 hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
-                             int32_t* err, hipStream_t st);
+                             int32_t* err, const PoolRoots& pr, hipStream_t st);
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
 // two-term E4M3 split of bf16 rows [rows, K] (engine_mx.hpp storage)
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,

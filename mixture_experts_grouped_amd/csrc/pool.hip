@@ -7,6 +7,12 @@
 // are zero (PR #9, "Historical implementation" -> Summary).  Rows inside an
 // expert follow ascending route index t*k + j, so the pool is a deterministic
 // function of the routing (the pages' atomic dispatch order is not).
+//
+// With several adapters (OpenPipe/ART PR #1139, Behavior: dispatched rows
+// carry adapter IDs) the pool's groups are (expert e, adapter q) pairs,
+// group e * na + q, q the root of the route's token: each group's rows then
+// share one adapter's expert-local factors, and the groups of one expert
+// stay adjacent (its base weights serve them back to back).
 #include "layer.hpp"
 #include "trace.hpp"
 
@@ -33,11 +39,22 @@ __device__ __forceinline__ int pool_block_sum(int v, int* red) {
   return t;
 }
 
-// Workgroup e counts the routes of expert e (workgroup 0 also the invalid
+// Pool group of route f with expert id `id` (valid or not): -1 for a dropped
+// or invalid id, else id * na + the root of token f / k.
+__device__ __forceinline__ int route_group(int id, int f, int E, const PoolRoots& pr) {
+  if (!(id >= 0 && id < E)) return -1;
+  if (pr.na == 1) return id;
+  const int t = f / pr.k;
+  int q = 0;
+  for (int i = 1; i < pr.na; ++i) q += t >= pr.roots[i];  // roots nondecreasing
+  return id * pr.na + q;
+}
+
+// Workgroup e counts the routes of group e (workgroup 0 also the invalid
 // ids): compares and a workgroup sum, no atomics.
 __global__ __launch_bounds__(POOL_THREADS) void k_pool_count(const int32_t* __restrict__ idx, int nroutes,
                                                              int E, int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ err) {
+                                                             int32_t* __restrict__ err, PoolRoots pr) {
   __shared__ int red[POOL_WAVES];
   const int tid = threadIdx.x, e = blockIdx.x;
   int m = 0, bad = 0;
@@ -50,7 +67,7 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool_count(const int32_t* __re
     }
 #pragma unroll
     for (int v = 0; v < POOL_V; ++v) {
-      m += ids[v] == e;
+      m += route_group(ids[v], c0 + v * POOL_THREADS + tid, E, pr) == e;
       bad += !(ids[v] >= -1 && ids[v] < E);
     }
   }
@@ -62,8 +79,8 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool_count(const int32_t* __re
   }
 }
 
-// Workgroup e places the routes of expert e: its padded offset is the sum of
-// the padded counts before it; then it walks the routes in chunks of
+// Workgroup e places the routes of group e (EV = E na groups): its padded
+// offset is the sum of the padded counts before it; then it walks the routes in chunks of
 // POOL_CHUNK (thread tid reads routes c0 + v * POOL_THREADS + tid, coalesced)
 // and gives the routes of expert e consecutive rows in ascending route order:
 // a route's row is the matches before it, counted with one ballot per (v,
@@ -73,7 +90,8 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool_count(const int32_t* __re
 __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
     const int32_t* __restrict__ idx, int nroutes, int E, int bm, long cap,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ r2row,
-    int32_t* __restrict__ row2r) {
+    int32_t* __restrict__ row2r, PoolRoots pr) {
+  const int EV = E * pr.na;
   constexpr int NC = POOL_V * POOL_WAVES;  // (v, wave) counts per chunk
   static_assert(NC <= POOL_THREADS && NC % 64 == 0 && POOL_V <= 64, "scan layout");
   __shared__ int red[POOL_WAVES];
@@ -89,10 +107,10 @@ __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
   const int n = counts[e], padded = pool_pad(n, bm);
   if (tid == 0) {
     offsets[e] = off;
-    if (e == E - 1) offsets[E] = off + padded;
+    if (e == EV - 1) offsets[EV] = off + padded;
   }
   for (int p = off + n + tid; p < off + padded; p += POOL_THREADS) row2r[p] = -1;  // padding rows
-  if (e == E - 1)
+  if (e == EV - 1)
     for (long p = off + padded + tid; p < cap; p += POOL_THREADS) row2r[p] = -1;  // unused suffix
   const unsigned long long below = (1ull << lane) - 1ull;
   int run = off;  // next row of expert e (uniform)
@@ -102,7 +120,7 @@ __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
 #pragma unroll
     for (int v = 0; v < POOL_V; ++v) {
       const int f = c0 + v * POOL_THREADS + tid;
-      ids[v] = (f < nroutes) ? idx[f] : -1;
+      ids[v] = (f < nroutes) ? route_group(idx[f], f, E, pr) : -1;  // -1: dropped or invalid
     }
     int mine = 0;
 #pragma unroll
@@ -138,7 +156,7 @@ __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
         const int pos = run + pre[v * POOL_WAVES + wv] + __popcll(bal[v] & below);
         r2row[f] = pos;
         row2r[pos] = f;
-      } else if (e == 0 && f < nroutes && !(ids[v] >= 0 && ids[v] < E)) {
+      } else if (e == 0 && f < nroutes && ids[v] < 0) {
         r2row[f] = -1;  // dropped or invalid route
       }
     }
@@ -149,20 +167,21 @@ __global__ __launch_bounds__(POOL_THREADS) void k_build_pool(
 
 hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
-                             int32_t* err, hipStream_t st) {
-  MOE_LAUNCH(k_pool_count, dim3((unsigned)E), dim3(POOL_THREADS), 0, st, idx, nroutes, E, counts, err);
-  MOE_LAUNCH(k_build_pool, dim3((unsigned)E), dim3(POOL_THREADS), 0, st, idx, nroutes, E, bm, cap, counts,
-             offsets, r2row, row2r);
+                             int32_t* err, const PoolRoots& pr, hipStream_t st) {
+  const unsigned EV = (unsigned)(E * pr.na);
+  MOE_LAUNCH(k_pool_count, dim3(EV), dim3(POOL_THREADS), 0, st, idx, nroutes, E, counts, err, pr);
+  MOE_LAUNCH(k_build_pool, dim3(EV), dim3(POOL_THREADS), 0, st, idx, nroutes, E, bm, cap, counts,
+             offsets, r2row, row2r, pr);
   return hipGetLastError();
 }
 
-// Grouped-GEMM M tiles: TMG rows of one expert each, never crossing experts.
+// Grouped-GEMM M tiles: TMG rows of one pool group each, never crossing groups.
 __global__ __launch_bounds__(64) void k_tile_map(LayerArgs a) {
   const int lane = threadIdx.x;
   int carry = 0;
-  for (int b0 = 0; b0 < a.E; b0 += 64) {
+  for (int b0 = 0; b0 < a.EV; b0 += 64) {
     const int e = b0 + lane;
-    const int n = (e < a.E) ? a.counts[e] : 0;
+    const int n = (e < a.EV) ? a.counts[e] : 0;
     const int nt = (n + TMG - 1) / TMG;
     int x = nt;
 #pragma unroll
@@ -171,7 +190,7 @@ __global__ __launch_bounds__(64) void k_tile_map(LayerArgs a) {
       if (lane >= o) x += y;
     }
     const int start = carry + x - nt;
-    if (e < a.E) {
+    if (e < a.EV) {
       const int off = a.offsets[e];
       for (int t = 0; t < nt; ++t) a.tiles[start + t] = TileInfo{e, off + t * TMG, off + n, 0};
     }

@@ -122,6 +122,22 @@ def shared_weights(shape: Shape, key: Sequence[int]) -> Dict[str, np.ndarray]:
     }
 
 
+def adapter_factors(shape: Shape, key: Sequence[int], adapter: int) -> Dict[str, np.ndarray]:
+    """The six factors of one adapter of a multi-adapter pass (bf16 bits):
+    the expert-local B1/B3 [E, I, r], A2 [E, r, I] and the shared A1/A3
+    [r, H], B2 [H, r], drawn like the single adapter's under a key of the
+    adapter's own."""
+    ak = (*key, 7000 + adapter)
+    H, I, r = shape.H, shape.I, shape.rank
+    out = {
+        "B1": np.stack([_normal_bf16(_rng(ak, "B1", e), (I, r), 0.02 ** 0.5) for e in range(shape.E)]),
+        "B3": np.stack([_normal_bf16(_rng(ak, "B3", e), (I, r), 0.02 ** 0.5) for e in range(shape.E)]),
+        "A2": np.stack([_normal_bf16(_rng(ak, "A2", e), (r, I), (1.0 / I) ** 0.5) for e in range(shape.E)]),
+    }
+    out.update(shared_weights(shape, ak))
+    return out
+
+
 def all_weights(shape: Shape, key: Sequence[int]) -> Dict[str, np.ndarray]:
     per = [expert_weights(shape, key, e) for e in range(shape.E)]
     out = {n: np.stack([p[n] for p in per]) for n in ("W13", "W2", "B1", "B3", "A2")}

@@ -191,12 +191,13 @@ class GpuRun:
     def __init__(self, shape: I.Shape, case: Dict[str, np.ndarray], block_m: int = 0,
                  scale: Optional[float] = None, mx: Optional[Dict[str, np.ndarray]] = None,
                  base_grads: bool = False, activation: str = "swiglu", transformed: bool = False,
-                 clamp: float = 0.0):
+                 clamp: float = 0.0, roots=None):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
         then case's W13/W2 are not uploaded.  base_grads: also request the
         frozen-weight gradients dW13, dW2.  transformed: give the backward the
         transformed base weights (W13T, W2T) written by moe_lora_transform_base.
-        clamp: the activation clamp c (0 = off)."""
+        clamp: the activation clamp c (0 = off).  roots: several adapters in
+        one pass (the *_multi calls; case's six factors stacked per adapter)."""
         import torch
         from mixture_experts_grouped_amd import binding as B
         self.torch = torch
@@ -206,7 +207,7 @@ class GpuRun:
         act = {"swiglu": B.MOE_ACT_SWIGLU, "geglu": B.MOE_ACT_GEGLU}[activation]
         self.desc = B.make_desc(shape.T, shape.H, shape.I, shape.E, shape.topk, shape.rank,
                                 scale=s, block_m=block_m, base_format=fmt, activation=act, clamp=clamp)
-        self.layer = B.MoeLoraLayer(self.desc, base_grads=base_grads)
+        self.layer = B.MoeLoraLayer(self.desc, base_grads=base_grads, roots=roots)
         dev = "cuda"
 
         def bf(a):

@@ -248,3 +248,74 @@ def test_noalloc_forward_rejects_layers_beyond_its_static_scratch():
                                         s_saved, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_forward_noalloc(byref(small), byref(s_pool), x, fake, byref(prm), out, sv,
                                         s_saved - 1, None) == B.MOE_ERR_WORKSPACE
+
+
+def _adapters(offsets):
+    arr = (ctypes.c_int32 * len(offsets))(*offsets)
+    ad = B.MoeAdapters(len(offsets) - 1, arr)
+    ad._keep = arr
+    return ad
+
+
+def test_multi_adapter_sizes():
+    """One root holding every token is the single-adapter plan; more
+    adapters only add pool padding groups (E per adapter) and the
+    per-adapter transposed factors."""
+    d = B.make_desc(300, 512, 256, 16, 2, 8)
+    assert B.moe_lora_multi_pool_capacity(d, [0, 300]) == B.moe_lora_pool_capacity(d)
+    assert B.moe_lora_multi_workspace_size(d, [0, 300]) == B.moe_lora_workspace_size(d)
+    bm = B.moe_lora_block_m(d)
+    for roots in ([0, 100, 300], [0, 0, 7, 300], [0, 1, 2, 3, 300]):
+        na = len(roots) - 1
+        assert B.moe_lora_multi_pool_capacity(d, roots) == 300 * 2 + min(16 * na, 600) * (bm - 1)
+        sv, sc = B.moe_lora_multi_workspace_size(d, roots)
+        s1, c1 = B.moe_lora_workspace_size(d)
+        assert sv >= s1 and sc >= c1
+
+
+@pytest.mark.parametrize("offsets,status", [
+    ([0], B.MOE_ERR_INVALID),              # no adapter
+    ([1, 300], B.MOE_ERR_INVALID),         # first root must start at token 0
+    ([0, 299], B.MOE_ERR_INVALID),         # last root must end at T
+    ([0, 200, 100, 300], B.MOE_ERR_INVALID),  # decreasing
+    (list(range(0, 66)) + [300], B.MOE_ERR_UNSUPPORTED),  # 66 adapters
+])
+def test_multi_adapter_roots_rejected(offsets, status):
+    lib = B.library()
+    d = B.make_desc(300, 512, 256, 16, 2, 8)
+    rows = ctypes.c_int64()
+    assert lib.moe_lora_multi_pool_capacity(ctypes.byref(d), ctypes.byref(_adapters(offsets)),
+                                            ctypes.byref(rows)) == status
+    assert lib.moe_lora_multi_pool_capacity(ctypes.byref(d), None, ctypes.byref(rows)) == B.MOE_OK
+
+
+def test_multi_adapter_calls_reject_before_any_launch():
+    """Bad roots, NULL adapters on the *_multi calls, and frozen-weight
+    gradients with several adapters are refused on the host (fake device
+    pointers: any launch would fault)."""
+    lib = B.library()
+    byref = ctypes.byref
+    fake = 1 << 20
+    d = B.make_desc(64, 256, 256, 8, 2, 8)
+    roots = [0, 30, 64]
+    ad = _adapters(roots)
+    cap = B.moe_lora_multi_pool_capacity(d, roots)
+    saved, scratch = B.moe_lora_multi_workspace_size(d, roots)
+    pool = B.MoePool(fake, fake, fake, fake, cap, B.moe_lora_block_m(d))
+    prm = B.MoeLoraParams(*([fake] * 2 + [None, None] + [fake] * 6))
+    x, out, sv, sc = fake, fake * 512, fake * 4096, fake * 8192
+    assert lib.moe_lora_forward_multi(byref(d), None, byref(pool), x, fake, byref(prm), out, sv, saved, sc,
+                                      scratch, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_forward_multi(byref(d), byref(_adapters([0, 64, 63])), byref(pool), x, fake,
+                                      byref(prm), out, sv, saved, sc, scratch, None) == B.MOE_ERR_INVALID
+    # a single-adapter pool (smaller capacity) does not serve two adapters
+    pool1 = B.MoePool(fake, fake, fake, fake, B.moe_lora_pool_capacity(d), B.moe_lora_block_m(d))
+    assert lib.moe_lora_forward_multi(byref(d), byref(ad), byref(pool1), x, fake, byref(prm), out, sv, saved,
+                                      sc, scratch, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_forward_multi(byref(d), byref(ad), byref(pool), x, fake, byref(prm), out, sv,
+                                      saved - 1, sc, scratch, None) == B.MOE_ERR_WORKSPACE
+    g = B.MoeLoraGrads(*([fake * 16] * 6 + [fake * 32, None]))
+    assert lib.moe_lora_backward_multi(byref(d), byref(ad), byref(pool), x, fake, byref(prm), sv, saved, out,
+                                       fake, byref(g), sc, scratch, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.build_pool_multi(byref(d), byref(ad), fake, fake, fake, fake, fake, cap - 1, None,
+                                None) == B.MOE_ERR_INVALID
