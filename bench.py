@@ -276,6 +276,15 @@ def token_sweep(torch, args):
                      "ms_min": round(min(samples), 4), "ms_max": round(max(samples), 4),
                      "weight_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / 8000.0, 4),
                      "floor_ms": round(2.0 * active * per_expert / 8e12 * 1e3, 4)})
+        if not args.graph and not args.no_trace:  # per-kernel averages, in a pass of their own
+            B.moe_lora_trace_reset()
+            B.moe_lora_trace_enable(True)
+            for _ in range(10):
+                layer.step(tidx, x, tw, params, go, stream)
+            torch.cuda.synchronize()
+            tr = B.moe_lora_trace_collect()
+            B.moe_lora_trace_enable(False)
+            rows[-1]["kernels_us"] = {n: round(1e3 * t / 10, 1) for n, (c, t) in sorted(tr.items(), key=lambda kv: -kv[1][1])}
         print(f"[sweep] T={T} {rows[-1]}", file=sys.stderr, flush=True)
         del layer
         if args.graph:
@@ -286,6 +295,96 @@ def token_sweep(torch, args):
                       "config": {"workload": "H 4096, I 2048, 64 experts, top-6, rank 128, 20% of routes "
                                              "dropped, softmax routing; T per row"},
                       "sweep": rows}), flush=True)
+
+
+def multi_adapter(torch, args):
+    """Several adapters in one pass against the same adapters one after
+    another (OpenPipe/ART PR #1139, Validation: 2/4/8/16 adapters x 1K tokens
+    each at LoRA rank 1/8/32; rank 1 is below this library's rank granularity
+    of 8).  Layer: H 4096, I 2048, 64 experts, top-6 softmax routing, base
+    weights shared by the adapters (transformed copy for the backward),
+    N x 1024 tokens in N roots.  Per row: the fused F+B ms (build_pool_multi
+    + forward + backward) and the serial ms (N single-adapter steps on 1024
+    tokens each), medians of three rounds of ten."""
+    import numpy as np
+    from mixture_experts_grouped_amd import binding as B
+    from mixture_experts_grouped_amd import inputs as I
+    dev = "cuda"
+    threads = min(16, len(os.sched_getaffinity(0)))
+    key = (5,)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base_shape = I.Shape(T=1024, H=4096, I=2048, E=64, topk=6, rank=8, scale=1.0)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        experts = list(ex.map(lambda e: I.expert_weights(base_shape, key, e), range(base_shape.E)))
+    base = {}
+    for nm in ("W13", "W2"):
+        t = torch.empty((base_shape.E, *experts[0][nm].shape), dtype=torch.bfloat16, device=dev)
+        for e in range(base_shape.E):
+            t[e].copy_(bf(experts[e][nm]))
+        base[nm] = t
+    del experts
+    d0 = B.make_desc(1, base_shape.H, base_shape.I, base_shape.E, base_shape.topk, 8, 1.0)
+    base.update(B.transform_base(d0, base))
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        samples = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            samples.append((time.perf_counter() - t0) * 1e3 / 10)
+        return float(np.median(samples))
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    for r in (8, 32):
+        for na in (2, 4, 8, 16):
+            T = 1024 * na
+            shape = I.Shape(T=T, H=4096, I=2048, E=64, topk=6, rank=r, scale=1.0)
+            skey = (*key, r, na)
+            idx, w = I.route_softmax_topk(shape, skey)
+            x, go = bf(I.tokens(shape, skey)), bf(I.grad_out(shape, skey))
+            tidx, tw = torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev)
+            fac = [I.adapter_factors(shape, skey, a) for a in range(na)]
+            roots = [1024 * a for a in range(na + 1)]
+            params = dict(base)
+            for nm in ("A1", "A3", "B1", "B3", "A2", "B2"):
+                params[nm] = bf(np.stack([f[nm] for f in fac]))
+            desc = B.make_desc(T, shape.H, shape.I, shape.E, shape.topk, r, 1.0)
+            fused = B.MoeLoraLayer(desc, device=dev, roots=roots)
+            ms_fused = timed(lambda: fused.step(tidx, x, tw, params, go, stream))
+            del fused
+            d1 = B.make_desc(1024, shape.H, shape.I, shape.E, shape.topk, r, 1.0)
+            one = B.MoeLoraLayer(d1, device=dev)  # the serial steps reuse one set of buffers
+            parts = []
+            for a in range(na):
+                pa = dict(base)
+                for nm in ("A1", "A3", "B1", "B3", "A2", "B2"):
+                    pa[nm] = params[nm][a]
+                sl = slice(1024 * a, 1024 * (a + 1))
+                parts.append((tidx[sl], x[sl], tw[sl], pa, go[sl]))
+
+            def serial():
+                for (i_, x_, w_, p_, g_) in parts:
+                    one.step(i_, x_, w_, p_, g_, stream)
+            ms_serial = timed(serial)
+            del one
+            rows.append({"rank": r, "adapters": na, "tokens": T, "fused_ms": round(ms_fused, 4),
+                         "serial_ms": round(ms_serial, 4), "speedup": round(ms_serial / ms_fused, 3)})
+            print(f"[adapters] {rows[-1]}", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "multi-adapter pass: fused F+B ms vs the adapters one after another",
+                      "unit": "ms", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+                      "config": {"workload": "H 4096, I 2048, 64 experts, top-6 softmax routing, 1024 tokens "
+                                             "per adapter root, base transformed for the backward"},
+                      "rows": rows}), flush=True)
 
 
 def main():
@@ -319,6 +418,8 @@ def main():
                     help="instead of the headline: time F+B over the token sweep (H 4096, I 2048, "
                          "64 experts, top-6, rank 128, 20%% of routes dropped) and report the "
                          "weight-read rate against HBM; prints one JSON line with a table")
+    ap.add_argument("--adapters", action="store_true",
+                    help="time the multi-adapter pass against the adapters run one after another")
     ap.add_argument("--graph", action="store_true",
                     help="with --sweep: capture each step once in a HIP graph and time its replays")
     ap.add_argument("--library-gemm", action="store_true",
@@ -343,6 +444,9 @@ def main():
         return
     if args.sweep:
         token_sweep(torch, args)
+        return
+    if args.adapters:
+        multi_adapter(torch, args)
         return
     from mixture_experts_grouped_amd import binding as B
     from mixture_experts_grouped_amd import inputs as I

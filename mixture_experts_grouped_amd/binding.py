@@ -294,11 +294,14 @@ def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
     MXFP4 base the dequantised weights, transposed."""
     E, H, I = desc.E, desc.H, desc.I
     bf = torch.bfloat16
-    names = ("W13", "W2", "A1", "A3", "B1", "B3", "A2", "B2")
     if desc.base_format == MOE_BASE_MXFP4:
-        names += ("W13_scale", "W2_scale")
-    base = {n: params[n] for n in names}
-    pp = _params_struct(base, desc)
+        u8 = torch.uint8
+        pp = MoeLoraParams(_ptr(params["W13"], u8, (E, 2 * I, H // 2), "W13"),
+                           _ptr(params["W2"], u8, (E, H, I // 2), "W2"),
+                           _ptr(params["W13_scale"], u8, (E, 2 * I, H // 32), "W13_scale"),
+                           _ptr(params["W2_scale"], u8, (E, H, I // 32), "W2_scale"))
+    else:  # the base alone: the adapter factors are not read
+        pp = MoeLoraParams(_ptr(params["W13"], bf, (E, 2 * I, H), "W13"), _ptr(params["W2"], bf, (E, H, I), "W2"))
     st = library().moe_lora_transform_base(
         ctypes.byref(desc), ctypes.byref(pp), _ptr(W13T, bf, (E, H, 2 * I), "W13T"),
         _ptr(W2T, bf, (E, I, H), "W2T"), _stream(stream))
