@@ -400,12 +400,13 @@ def main():
                     help="base weight format: bf16, or MXFP4 (e2m1 + e8m0 per 32 along K) "
                          "quantised from the same seeded bf16 weights")
     ap.add_argument("--base-layout", choices=("plain", "transformed"), default="transformed",
-                    help="transformed (default): also hold the frozen base as bf16 W13^T / W2^T "
-                         "per expert (the reusable transformed weights of the pages' backward; for "
-                         "an MXFP4 base the dequantised weights), written once by "
-                         "moe_lora_transform_base before the timed steps, so the backward's "
-                         "data-gradient GEMMs read it in contraction order; plain: transpose (and "
-                         "expand) through LDS on every backward (same bits)")
+                    help="transformed (default): also hold the frozen base as packed bf16 stage "
+                         "tiles -- W13^T / W2^T for the backward (for an MXFP4 base the dequantised "
+                         "weights) and W13 / W2 for a bf16 forward -- written once by "
+                         "moe_lora_transform_base before the timed steps (the reusable transformed "
+                         "weights of the pages), so every base GEMM stage reads 32 KB in order; "
+                         "plain: read W13 / W2 as given, transposing (and expanding) them through "
+                         "LDS in the backward (same bits)")
     ap.add_argument("--clamp", type=float, default=0.0,
                     help="activation clamp c (> 0: both pre-activations clipped to [-c, c]; the "
                          "pages' production runs use 10); default off, as in the headline workload")
@@ -599,7 +600,8 @@ def main():
         "config": {
             "workload": (("MXFP4 base (e2m1 + e8m0/32) on scaled MFMA, " if mx else "") +
                          (("base " + ("dequantised and " if mx else "") +
-                           "held transposed in bf16 for the backward (written once), ")
+                           "held transposed in packed bf16 stage tiles for the backward" +
+                           ("" if mx else " and packed for the forward") + " (written once), ")
                           if transformed else "") +
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "

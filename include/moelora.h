@@ -119,16 +119,22 @@ typedef struct moe_pool {
  *   A1, A3 [r, H]   shared;   B1, B3 [E, I, r] expert-local
  *   A2  [E, r, I]   expert-local;   B2 [H, r] shared
  *   W13_scale, W2_scale: e8m0 block scales for MOE_BASE_MXFP4, NULL for bf16.
- *   W13T [E, H, 2I], W2T [E, I, H]: optional transformed copies of the frozen
- *     bf16 base (W13T[e] = W13[e]^T, W2T[e] = W2[e]^T), written once by
- *     moe_lora_transform_base and reused by every backward (PR #9 Summary:
- *     reusable transformed weights).  With them the two data-gradient GEMMs
- *     read the weights in the order they contract them; without them (NULL)
- *     the backward transposes W13 / W2 on the fly (for an MXFP4 base also
- *     expanding them to bf16).  Results are bitwise the same either way; the
- *     contents must match W13 / W2 (for an MXFP4 base: their dequantised
- *     values).  Each may be given alone; 16-byte aligned.  The forward
- *     ignores them. */
+ *   W13T, W2T, W13P, W2P: optional transformed copies of the frozen base,
+ *     written once by moe_lora_transform_base and reused by every call
+ *     (PR #9 Summary: reusable transformed weights).  Each holds E x 2I x H
+ *     (W13T, W13P) or E x H x I (W2T, W2P) bf16 values in a layout private to
+ *     the library: the weight tiles of one GEMM pipeline stage stored as the
+ *     bytes it loads, one stage after another, so that each stage reads one
+ *     contiguous 32 KB block instead of a short run from each of 256 rows.
+ *       W13T, W2T: W13[e]^T, W2[e]^T for the backward's two data-gradient
+ *         GEMMs (for an MXFP4 base, of the dequantised values); without them
+ *         (NULL) the backward transposes W13 / W2 on the fly (an MXFP4 base
+ *         also expanded to bf16).  The forward ignores them.
+ *       W13P, W2P: W13, W2 for the forward's two base GEMMs (bf16 base only;
+ *         with MOE_BASE_MXFP4 they must be NULL).  The backward ignores them.
+ *     Results are bitwise the same with or without any of them; their
+ *     contents must come from moe_lora_transform_base on the same W13 / W2.
+ *     Each may be given alone; 16-byte aligned. */
 typedef struct moe_lora_params {
   const void* W13;
   const void* W2;
@@ -137,6 +143,8 @@ typedef struct moe_lora_params {
   const void *A1, *A3, *B1, *B3, *A2, *B2;
   const void* W13T;
   const void* W2T;
+  const void* W13P;
+  const void* W2P;
 } moe_lora_params;
 
 /* Gradient outputs (device bf16, same layouts as the parameters).  The six
@@ -193,15 +201,17 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
                       int32_t* offsets, int32_t* route_to_row, int32_t* row_to_route,
                       int64_t capacity, int32_t* device_error, void* stream);
 
-/* Write the transformed base weights of moe_lora_params: W13T[e] = W13[e]^T
- * ([E, H, 2I]) and W2T[e] = W2[e]^T ([E, I, H]), bf16, from params->W13 /
- * params->W2.  For MOE_BASE_MXFP4 they are the dequantised weights
- * e2m1 x 2^(e-127) (exact in bf16) transposed, read from the packed W13 / W2
- * and their scales (both required).  Either output may be NULL (skipped);
- * outputs are 16-byte aligned device buffers that overlap neither input nor
- * each other.  Queued on `stream` like every call. */
+/* Write the transformed base weights of moe_lora_params from params->W13 /
+ * params->W2 (the adapter factors are not read): W13T and W2T (E*2I*H and
+ * E*H*I bf16 values: the transposed weights for the backward; for
+ * MOE_BASE_MXFP4 the dequantised weights e2m1 x 2^(e-127), exact in bf16,
+ * read from the packed W13 / W2 and their scales, both required) and W13P,
+ * W2P (the same sizes: the forward's weights, bf16 base only; non-NULL with
+ * MXFP4 is MOE_ERR_INVALID).  Any output may be NULL (skipped); outputs are
+ * 16-byte aligned device buffers that overlap no input and no other output.
+ * Queued on `stream` like every call. */
 moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
-                                   void* W2T, void* stream);
+                                   void* W2T, void* W13P, void* W2P, void* stream);
 
 /* Two-term FP8 (E4M3) split of bf16 rows, the activation operand of the
  * MXFP4 base's scaled fp8 x fp4 matrix products (PR #9 "Historical

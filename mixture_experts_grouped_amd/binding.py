@@ -62,7 +62,8 @@ class MoeLoraParams(ctypes.Structure):
                 ("W13_scale", ctypes.c_void_p), ("W2_scale", ctypes.c_void_p),
                 ("A1", ctypes.c_void_p), ("A3", ctypes.c_void_p), ("B1", ctypes.c_void_p),
                 ("B3", ctypes.c_void_p), ("A2", ctypes.c_void_p), ("B2", ctypes.c_void_p),
-                ("W13T", ctypes.c_void_p), ("W2T", ctypes.c_void_p)]
+                ("W13T", ctypes.c_void_p), ("W2T", ctypes.c_void_p),
+                ("W13P", ctypes.c_void_p), ("W2P", ctypes.c_void_p)]
 
 
 class MoeLoraGrads(ctypes.Structure):
@@ -115,7 +116,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_lora_backward.argtypes = [P(MoeLoraDesc), P(MoePool), vp, vp, P(MoeLoraParams), vp,
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
-    lib.moe_lora_transform_base.argtypes = [P(MoeLoraDesc), P(MoeLoraParams), vp, vp, vp]
+    lib.moe_lora_transform_base.argtypes = [P(MoeLoraDesc), P(MoeLoraParams), vp, vp, vp, vp, vp]
     lib.moe_lora_split_e4m3x2.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_lora_trace_enable.argtypes = [ctypes.c_int32]
     lib.moe_lora_trace_enable.restype = None
@@ -283,15 +284,20 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc, na: Optional[i
         s13 = s2 = None
     w13t = _ptr(p.get("W13T"), bf, (E, H, 2 * I), "W13T")
     w2t = _ptr(p.get("W2T"), bf, (E, I, H), "W2T")
+    w13p = _ptr(p.get("W13P"), bf, (E, 2 * I, H), "W13P")
+    w2p = _ptr(p.get("W2P"), bf, (E, H, I), "W2P")
     return MoeLoraParams(w13, w2, s13, s2, ptrs["A1"], ptrs["A3"], ptrs["B1"], ptrs["B3"],
-                         ptrs["A2"], ptrs["B2"], w13t, w2t)
+                         ptrs["A2"], ptrs["B2"], w13t, w2t, w13p, w2p)
 
 
 def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
                             W13T: Optional[torch.Tensor], W2T: Optional[torch.Tensor],
+                            W13P: Optional[torch.Tensor] = None, W2P: Optional[torch.Tensor] = None,
                             stream=None) -> None:
-    """W13T[e] = W13[e]^T, W2T[e] = W2[e]^T in bf16 (either may be None); for an
-    MXFP4 base the dequantised weights, transposed."""
+    """The transformed base copies (any may be None): W13T, W2T for the
+    backward (for an MXFP4 base of the dequantised weights) and W13P, W2P for
+    the forward (bf16 base only).  Library-private layouts of E x 2I x H and
+    E x H x I bf16 values (shapes below are storage only)."""
     E, H, I = desc.E, desc.H, desc.I
     bf = torch.bfloat16
     if desc.base_format == MOE_BASE_MXFP4:
@@ -304,19 +310,26 @@ def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
         pp = MoeLoraParams(_ptr(params["W13"], bf, (E, 2 * I, H), "W13"), _ptr(params["W2"], bf, (E, H, I), "W2"))
     st = library().moe_lora_transform_base(
         ctypes.byref(desc), ctypes.byref(pp), _ptr(W13T, bf, (E, H, 2 * I), "W13T"),
-        _ptr(W2T, bf, (E, I, H), "W2T"), _stream(stream))
+        _ptr(W2T, bf, (E, I, H), "W2T"), _ptr(W13P, bf, (E, 2 * I, H), "W13P"), _ptr(W2P, bf, (E, H, I), "W2P"),
+        _stream(stream))
     _check(st, "moe_lora_transform_base")
 
 
-def transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor], stream=None) -> Dict[str, torch.Tensor]:
-    """Allocate and fill the transformed base weights; merge the result into
-    the params dict given to moe_lora_backward.  Redo it whenever W13 / W2
+def transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor], stream=None,
+                   forward: bool = True) -> Dict[str, torch.Tensor]:
+    """Allocate and fill the transformed base copies -- W13T, W2T for the
+    backward, and (bf16 base, forward=True) W13P, W2P for the forward -- and
+    return them to merge into the params dict.  Redo it whenever W13 / W2
     change (they are frozen in the side-LoRA setting)."""
     E, H, I = desc.E, desc.H, desc.I
     dev = params["W13"].device
-    out = {"W13T": torch.empty(E, H, 2 * I, dtype=torch.bfloat16, device=dev),
-           "W2T": torch.empty(E, I, H, dtype=torch.bfloat16, device=dev)}
-    moe_lora_transform_base(desc, params, out["W13T"], out["W2T"], stream)
+    bf = torch.bfloat16
+    out = {"W13T": torch.empty(E, H, 2 * I, dtype=bf, device=dev),
+           "W2T": torch.empty(E, I, H, dtype=bf, device=dev)}
+    if forward and desc.base_format != MOE_BASE_MXFP4:
+        out["W13P"] = torch.empty(E, 2 * I, H, dtype=bf, device=dev)
+        out["W2P"] = torch.empty(E, H, I, dtype=bf, device=dev)
+    moe_lora_transform_base(desc, params, out["W13T"], out["W2T"], out.get("W13P"), out.get("W2P"), stream)
     return out
 
 

@@ -192,6 +192,9 @@ moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
   // the dequantised weights)
   if ((w->W13T != nullptr && !aligned16(w->W13T)) || (w->W2T != nullptr && !aligned16(w->W2T)))
     return MOE_ERR_INVALID;
+  // packed forward copies: of a bf16 base only
+  if ((w->W13P != nullptr && (mx || !aligned16(w->W13P))) || (w->W2P != nullptr && (mx || !aligned16(w->W2P))))
+    return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -219,6 +222,8 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.W13 = (const uint16_t*)w->W13;
   a.W2 = (const uint16_t*)w->W2;
   a.W13T = (const uint16_t*)w->W13T;
+  a.W13P = (const uint16_t*)w->W13P;
+  a.W2P = (const uint16_t*)w->W2P;
   a.W2T = (const uint16_t*)w->W2T;
   a.mx = d->base_format == MOE_BASE_MXFP4;
   a.act = d->activation;
@@ -536,7 +541,7 @@ moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void*
 }
 
 moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params* params, void* W13T,
-                                   void* W2T, void* stream) {
+                                   void* W2T, void* W13P, void* W2P, void* stream) {
   const moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (params == nullptr) return MOE_ERR_INVALID;
@@ -545,26 +550,34 @@ moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params
   const size_t b13 = n13 * 2, b2 = n2 * 2;                                              // bf16 outputs
   const size_t in13 = mx ? n13 / 2 : b13, in2 = mx ? n2 / 2 : b2;                      // inputs
   if (mx && (params->W13_scale == nullptr || params->W2_scale == nullptr)) return MOE_ERR_INVALID;
-  if (W13T != nullptr) {
-    if (!aligned16(W13T) || !aligned16(params->W13)) return MOE_ERR_INVALID;
-    if (overlap(rng(W13T, b13), rng(params->W13, in13))) return MOE_ERR_INVALID;
-    if (mx && overlap(rng(W13T, b13), rng(params->W13_scale, n13 / 32))) return MOE_ERR_INVALID;
+  if (mx && (W13P != nullptr || W2P != nullptr)) return MOE_ERR_INVALID;  // the MXFP4 forward reads e2m1
+  if (!aligned16(params->W13) || !aligned16(params->W2)) return MOE_ERR_INVALID;
+  // every output: aligned, and disjoint from the inputs and the other outputs
+  const Range ins[] = {rng(params->W13, in13), rng(params->W2, in2),
+                       rng(mx ? params->W13_scale : nullptr, mx ? n13 / 32 : 0),
+                       rng(mx ? params->W2_scale : nullptr, mx ? n2 / 32 : 0)};
+  void* outs[] = {W13T, W2T, W13P, W2P};
+  const size_t sizes[] = {b13, b2, b13, b2};
+  for (int i = 0; i < 4; ++i) {
+    if (outs[i] == nullptr) continue;
+    if (!aligned16(outs[i])) return MOE_ERR_INVALID;
+    for (const Range& r : ins)
+      if (overlap(rng(outs[i], sizes[i]), r)) return MOE_ERR_INVALID;
+    for (int j = 0; j < i; ++j)
+      if (outs[j] != nullptr && overlap(rng(outs[i], sizes[i]), rng(outs[j], sizes[j]))) return MOE_ERR_INVALID;
   }
-  if (W2T != nullptr) {
-    if (!aligned16(W2T) || !aligned16(params->W2)) return MOE_ERR_INVALID;
-    if (overlap(rng(W2T, b2), rng(params->W2, in2))) return MOE_ERR_INVALID;
-    if (mx && overlap(rng(W2T, b2), rng(params->W2_scale, n2 / 32))) return MOE_ERR_INVALID;
-  }
-  if (W13T != nullptr && W2T != nullptr && overlap(rng(W13T, b13), rng(W2T, b2))) return MOE_ERR_INVALID;
   const hipStream_t s = (hipStream_t)stream;
+  const uint16_t* w13 = mx ? nullptr : (const uint16_t*)params->W13;
+  const uint16_t* w2 = mx ? nullptr : (const uint16_t*)params->W2;
+  const uint8_t* q13 = mx ? (const uint8_t*)params->W13 : nullptr;
+  const uint8_t* q2 = mx ? (const uint8_t*)params->W2 : nullptr;
   hipError_t e = hipSuccess;
   if (W13T != nullptr)
-    e = mx ? launch_transpose_mx((const uint8_t*)params->W13, params->W13_scale, (uint16_t*)W13T, d->E, 2 * d->I,
-                                 d->H, s)
-           : launch_transpose((const uint16_t*)params->W13, (uint16_t*)W13T, d->E, 2 * d->I, d->H, s);
+    e = launch_pack(2, w13, q13, params->W13_scale, (uint16_t*)W13T, d->E, d->H, d->I, s);
   if (e == hipSuccess && W2T != nullptr)
-    e = mx ? launch_transpose_mx((const uint8_t*)params->W2, params->W2_scale, (uint16_t*)W2T, d->E, d->H, d->I, s)
-           : launch_transpose((const uint16_t*)params->W2, (uint16_t*)W2T, d->E, d->H, d->I, s);
+    e = launch_pack(3, w2, q2, params->W2_scale, (uint16_t*)W2T, d->E, d->H, d->I, s);
+  if (e == hipSuccess && W13P != nullptr) e = launch_pack(0, w13, nullptr, nullptr, (uint16_t*)W13P, d->E, d->H, d->I, s);
+  if (e == hipSuccess && W2P != nullptr) e = launch_pack(1, w2, nullptr, nullptr, (uint16_t*)W2P, d->E, d->H, d->I, s);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

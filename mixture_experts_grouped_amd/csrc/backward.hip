@@ -157,12 +157,12 @@ static_assert(GW2DK::TM == GW2D::TM && GW2DK::TN == GW2D::TN && GW2DK::STAGE == 
 struct LdW2dK {
   using KL = v2::KLoad<256, GW2DK::KT, GW2DK::NW>;
   using KA = v2::KLoadA<256, GW2DK::KT, GW2DK::NW>;
-  using KS = v2::KLoadS<256, GW2DK::KT, GW2DK::NW>;
-  static_assert(KA::NJ == KL::NJ && KS::NJ == KL::NJ, "one instruction count per stage");
+  using KP = v2::KLoadP<256, GW2DK::KT, GW2DK::NW>;
+  static_assert(KA::NJ == KL::NJ && KP::NJ == KL::NJ, "one instruction count per stage");
   static constexpr int INSTS = 2 * KL::NJ;
   KL me, ne;  // s q by token | A2T rows
   KA mm;      // go by token
-  KS nm;      // W2T rows
+  KP nm;      // W2T rows, packed (pack.hip, kind 3)
   int next;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < next) {
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     L.me.window(2 * r);
     L.ne.contig(a.A2T + le * a.I * r, i0, G::TN, r);
     L.ne.window(2 * r, r);  // k in [r, 2r) reads A2T column k - r again (lo half)
-    L.nm.contig(a.W2T + e * a.I * a.H, i0, G::TN, a.H);
+    L.nm.set(a.W2T + e * a.I * a.H, (uint64_t)a.I * a.H * 2, nt, a.H / G::KT);
     v2::run_stages2<G, 0>(L, next + a.H / G::KT, acc, smem);
   } else if constexpr (!MX) {
     {
@@ -441,8 +441,11 @@ static_assert(GW13DK::TM == GW13D::TM && GW13DK::TN == GW13D::TN && GW13DK::STAG
               "same tile and stage as the transposing form");
 struct LdW13dK {
   using KA = v2::KLoadS<256, GW13DK::KT, PPW>;
+  using KP = v2::KLoadP<256, GW13DK::KT, PPW>;
+  static_assert(KP::NJ == KA::NJ, "one instruction count per stage");
   static constexpr int INSTS = 2 * KA::NJ;
-  KA m, n;  // dGV rows | W13T rows
+  KA m;   // dGV rows
+  KP n;   // W13T rows, packed (pack.hip, kind 2)
   __device__ void issue(int s, char* sM, char* sN) {
     m.issue(s * GW13DK::KT, sM);
     n.issue(s * GW13DK::KT, sN);
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   if constexpr (TW) {
     LdW13dK L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
-    L.n.contig(a.W13T + e * a.H * 2 * a.I, h0, G::TN, 2 * a.I);
+    L.n.set(a.W13T + e * a.H * 2 * a.I, (uint64_t)a.H * 2 * a.I * 2, nt, 2 * a.I / G::KT);
     v2::run_pingpong<G>(L, 2 * a.I / G::KT, acc, smem);
   } else {
     typename std::conditional<MX, LdW13dMX, LdW13d>::type L;
@@ -924,44 +927,6 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t
   }
 }
 
-// The transformed copy of an MXFP4 base: [B, R, C] e2m1 (element 2i in the
-// low nibble of byte i, one e8m0 scale per 32 along C) -> [B, C, R] bf16,
-// the dequantised values (exact in bf16).  R and C are multiples of 64: each
-// workgroup dequantises one 64 x 64 tile (a thread: one row, 16 values = 8
-// packed bytes under one scale) into LDS and writes it transposed.
-__global__ __launch_bounds__(256) void k_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int R,
-                                                      int C) {
-  __shared__ uint16_t t[64][72];
-  const long b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  q += b * (long)R * (C / 2);
-  sc += b * (long)R * (C / 32);
-  dst += b * (long)R * C;
-  {
-    const int rr = threadIdx.x / 4, cc = (threadIdx.x % 4) * 16;
-    const long row = r0 + rr;
-    const u32x2 w = *(const u32x2*)(q + row * (C / 2) + (c0 + cc) / 2);
-    const float s = v2::e8m0_value(sc[row * (C / 32) + (c0 + cc) / 32]);
-    *(u32x4*)&t[rr][cc] = v2::fp4x8_bf16(w[0], s);
-    *(u32x4*)&t[rr][cc + 8] = v2::fp4x8_bf16(w[1], s);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int cr = threadIdx.x / 8 + 32 * p, rc = (threadIdx.x % 8) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)t[rc + 2 * j][cr] | ((uint32_t)t[rc + 2 * j + 1][cr] << 16);
-    *(u32x4*)(dst + (long)(c0 + cr) * R + r0 + rc) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
-hipError_t launch_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int B, int R, int C,
-                               hipStream_t st) {
-  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  MOE_LAUNCH(k_transpose_mx, dim3(C / 64, R / 64, B), dim3(256), 0, st, q, sc, dst, R, C);
-  return hipGetLastError();
-}
 
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st) {
   if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;

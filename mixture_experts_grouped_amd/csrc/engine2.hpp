@@ -332,6 +332,34 @@ struct KLoadS {
   }
 };
 
+// K tile of R rows x KT k from a packed copy of the matrix (pack.hip): each
+// stage tile stored as its LDS image, tiles consecutive per N tile, so a
+// stage is R * 2 * KT contiguous bytes and wave instruction j of wave w reads
+// the 1 KB that lands at tile + 1024 (w + NW j).  The LDS contents equal
+// those of KLoad / KLoadA / KLoadS on the plain matrix.
+template <int R, int KT, int NW>
+struct KLoadP {
+  static constexpr int TILE = R * 2 * KT;  // bytes per stage tile
+  static constexpr int NJ = TILE / (1024 * NW);
+  static_assert(NJ >= 1 && NJ * NW * 1024 == TILE, "whole wave instructions per stage");
+  rsrc_t rs;
+  uint32_t lane_off;  // 1024 w + 16 lane
+  uint32_t tile0;     // byte offset of the N tile's first stage tile
+  // base: the expert's packed matrix (`bytes` long); the N tile `nt` of a
+  // matrix with `nst` stages
+  __device__ __forceinline__ void set(const void* base, uint64_t bytes, int nt, int nst) {
+    rs = make_rsrc(base, bytes);
+    lane_off = 1024u * (uint32_t)(threadIdx.x >> 6) + 16u * (uint32_t)(threadIdx.x & 63);
+    tile0 = (uint32_t)nt * (uint32_t)nst * (uint32_t)TILE;
+  }
+  __device__ __forceinline__ void issue(int k0, char* tile) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS bases in SGPRs
+    const uint32_t st = tile0 + (uint32_t)(k0 / KT) * (uint32_t)TILE;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) lds_load16(rs, tile + 1024 * (w + NW * j), lane_off, st + 1024u * NW * j);
+  }
+};
+
 // T tile loader for a K range made of whole stages of a row-major [K, ld]
 // matrix, columns n0 .. n0 + R - 1 (all in range): offsets fixed at set-up,
 // the stage's first k-row in the scalar offset (as KLoadA).

@@ -96,9 +96,13 @@ struct LdW13Base {
   KL2 ne;
   int r, nsplit;
 };
+// NL: the weight tile loader (KLoadA on W13, or KLoadP on its packed copy)
+template <class NL>
 struct LdW13 : LdW13Base {
   static constexpr int INSTS = 2 * KL::NJ;
-  KA mm, nm;
+  static_assert(NL::NJ == KL::NJ, "one instruction count per stage");
+  KA mm;
+  NL nm;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < nsplit) {
       me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
@@ -139,8 +143,10 @@ static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipe
 // one: both pre-activations are clipped).  Whether a value is clipped is
 // decided on its fp16 rounding, the value saved for the backward, so that
 // both passes take the same decision.
-template <bool MX, int ACT, bool CL>
+// PK: the bf16 base read from its packed copy W13P (pack.hip, kind 0)
+template <bool MX, int ACT, bool CL, bool PK>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
+  static_assert(!(MX && PK), "the packed copy is of a bf16 base");
   extern __shared__ __align__(16) char smem[];
   using G = GW13;
   using KL = LdW13Base::KL;
@@ -160,7 +166,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   if constexpr (!MX) {
-    LdW13 L;
+    using NL = typename std::conditional<PK, v2::KLoadP<256, GW13::KT, GW13::NW>, LdW13Base::KA>::type;
+    LdW13<NL> L;
     L.r = r;
     L.nsplit = nsplit;
     L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
@@ -171,9 +178,13 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
     L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
     L.mm.from_tokens(a.x, a.T, a.H, tk);
-    L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+    if constexpr (PK) {
+      L.nm.set(a.W13P + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2, nt, a.H / G::KT);
+    } else {
+      L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
 #pragma unroll
-    for (int j = 0; j < KL::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KL::row_of(j)) * a.H * 2));
+      for (int j = 0; j < KL::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KL::row_of(j)) * a.H * 2));
+    }
     v2::run_stages2<G, 2>(L, nsplit + a.H / G::KT, acc, smem);
   } else {
     // the base K range as k64 stages on the scaled matrix cores, then the
@@ -296,19 +307,24 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
 
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
 constexpr int W2_LDS = cmax(GW2::LDS_BYTES, v2::TileImage<GW2, GW2::TN, uint16_t>::BYTES);
+template <class NL>  // the weight tile loader: KLoadS on W2, or KLoadP on its packed copy
 struct LdW2 {
   // the ping-pong loop: the four waves of group A queue a whole stage
   using KL = v2::KLoadS<256, GW2::KT, 4>;
   static constexpr int INSTS = 2 * KL::NJ;
-  KL m, n;
+  static_assert(NL::NJ == KL::NJ, "one instruction count per stage");
+  KL m;
+  NL n;
   __device__ void issue(int s, char* sM, char* sN) {
     m.issue(s * GW2::KT, sM);
     n.issue(s * GW2::KT, sN);
   }
 };
 
-template <bool MX>
+// PK: the bf16 base read from its packed copy W2P (pack.hip, kind 1)
+template <bool MX, bool PK>
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
+  static_assert(!(MX && PK), "the packed copy is of a bf16 base");
   extern __shared__ __align__(16) char smem[];
   using G = GW2;
   const int ntn = a.H / G::TN;
@@ -320,9 +336,14 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   if constexpr (!MX) {
-    LdW2 L;
+    using NL = typename std::conditional<PK, v2::KLoadP<256, GW2::KT, 4>, v2::KLoadS<256, GW2::KT, 4>>::type;
+    LdW2<NL> L;
     L.m.contig(a.Hh, ti.row0, nrows, a.I);
-    L.n.contig(a.W2 + (long)grp_expert(a, ti.e) * a.H * a.I, h0, G::TN, a.I);
+    const long e = grp_expert(a, ti.e);
+    if constexpr (PK)
+      L.n.set(a.W2P + e * a.H * a.I, (uint64_t)a.H * a.I * 2, nt, a.I / G::KT);
+    else
+      L.n.contig(a.W2 + e * a.H * a.I, h0, G::TN, a.I);
     v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
   } else {
     // MXFP4 base: h as its two-term split, W2 packed, on the scaled matrix cores
@@ -415,23 +436,23 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
 
 // ----------------------------------------------------------------------------
 
-template <bool MX, int ACT, bool CL>
+template <bool MX, int ACT, bool CL, bool PK>
 static void launch_w13(const LayerArgs& a, dim3 grid, hipStream_t st) {
-  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL>), grid, dim3(GW13::NT), W13_LDS, st, a);
+  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL, PK>), grid, dim3(GW13::NT), W13_LDS, st, a);
 }
-template <bool MX, int ACT>
+template <bool MX, int ACT, bool PK>
 static void launch_w13_cl(const LayerArgs& a, dim3 grid, hipStream_t st) {
   if (a.clamp > 0.0f)
-    launch_w13<MX, ACT, true>(a, grid, st);
+    launch_w13<MX, ACT, true, PK>(a, grid, st);
   else
-    launch_w13<MX, ACT, false>(a, grid, st);
+    launch_w13<MX, ACT, false, PK>(a, grid, st);
 }
-template <bool MX>
+template <bool MX, bool PK>
 static void set_w13_lds(AttrInit& ai) {
-  ai.lds((const void*)k_w13<MX, 0, false>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 1, false>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 0, true>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 1, true>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 0, false, PK>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 1, false, PK>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 0, true, PK>, W13_LDS);
+  ai.lds((const void*)k_w13<MX, 1, true, PK>, W13_LDS);
 }
 
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
@@ -447,11 +468,13 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   hipError_t err = attrs.run([] {
     AttrInit ai;
     ai.lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_w13_lds<false>(ai);
-    set_w13_lds<true>(ai);
+    set_w13_lds<false, false>(ai);
+    set_w13_lds<false, true>(ai);
+    set_w13_lds<true, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
-    ai.lds((const void*)k_w2<false>, W2_LDS);
-    ai.lds((const void*)k_w2<true>, W2_LDS);
+    ai.lds((const void*)k_w2<false, false>, W2_LDS);
+    ai.lds((const void*)k_w2<false, true>, W2_LDS);
+    ai.lds((const void*)k_w2<true, false>, W2_LDS);
     ai.lds((const void*)k_rank_combine, RK_LDS);
     return ai.err;
   });
@@ -466,20 +489,23 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   }
   {
     const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
+    const bool pk = a.W13P != nullptr;  // bf16 base only (checked on the host)
     if (a.mx && a.act == 1)
-      launch_w13_cl<true, 1>(a, grid, st);
+      launch_w13_cl<true, 1, false>(a, grid, st);
     else if (a.mx)
-      launch_w13_cl<true, 0>(a, grid, st);
+      launch_w13_cl<true, 0, false>(a, grid, st);
     else if (a.act == 1)
-      launch_w13_cl<false, 1>(a, grid, st);
+      pk ? launch_w13_cl<false, 1, true>(a, grid, st) : launch_w13_cl<false, 1, false>(a, grid, st);
     else
-      launch_w13_cl<false, 0>(a, grid, st);
+      pk ? launch_w13_cl<false, 0, true>(a, grid, st) : launch_w13_cl<false, 0, false>(a, grid, st);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)
-    MOE_LAUNCH(k_w2<true>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+    MOE_LAUNCH_AS("k_w2", (k_w2<true, false>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+  else if (a.W2P != nullptr)
+    MOE_LAUNCH_AS("k_w2", (k_w2<false, true>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   else
-    MOE_LAUNCH(k_w2<false>, dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+    MOE_LAUNCH_AS("k_w2", (k_w2<false, false>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
   const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_combine, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);

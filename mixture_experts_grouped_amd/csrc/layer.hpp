@@ -58,8 +58,9 @@ struct LayerArgs {
   float clamp;      // activation clamp c > 0 (pre-activations clipped to [-c, c]); 0 = off
   const uint8_t *W13q, *W13s, *W2q, *W2s;
   // transformed bf16 base weights (optional, nullptr = read W13 / W2
-  // transposed): W13T [E, H, 2I] = W13_e^T, W2T [E, I, H] = W2_e^T
-  const uint16_t *W13T, *W2T;
+  // directly), packed stage tiles (pack.hip): W13T = W13_e^T and W2T = W2_e^T
+  // for the data gradients; W13P, W2P = W13_e, W2_e for the forward (bf16 base)
+  const uint16_t *W13T, *W2T, *W13P, *W2P;
   // saved by the forward
   int* status;       // [1] status word at offset 0 of saved (MOE_SAVED_* bits)
   TileInfo* tiles;   // [maxtiles]
@@ -184,9 +185,9 @@ hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* cod
                              hipStream_t st);
 // [B, R, C] -> [B, C, R] bf16 bits
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st);
-// [B, R, C] MXFP4 (packed + e8m0 per 32 along C) -> [B, C, R] bf16, R and C multiples of 64
-hipError_t launch_transpose_mx(const uint8_t* q, const uint8_t* sc, uint16_t* dst, int B, int R, int C,
-                               hipStream_t st);
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
+// packed stage tiles of the base (kinds in pack.hip)
+hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const uint8_t* sc, uint16_t* dst, int E,
+                       int H, int I, hipStream_t st);
 
 }  // namespace moelora

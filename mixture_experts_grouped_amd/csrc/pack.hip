@@ -1,0 +1,116 @@
+// pack.hip -- packed copies of the frozen base weights.
+//
+// Each of the four base GEMMs reads its weights as the N operand: a K tile of
+// 256 weight rows x 64 k per pipeline stage (32 KB), which the direct loads
+// place in LDS with the chunk swizzle of engine2.hpp (row r's 16-byte chunk
+// c in slot c ^ kswz(r)).  Read from the plain matrix, a stage takes a
+// 128-byte run from each of 256 rows that lie K*2 bytes apart.  A packed
+// copy stores every stage tile as its LDS image -- rows consecutive, chunks
+// in their slots -- one tile after another (N tile major, K stage minor), so
+// a stage is 32 KB of consecutive bytes and each 1 KB wave load reads 1 KB in
+// order (v2::KLoadP).  The tile's bytes in LDS are the same either way, so
+// results do not change.  Written once per set of base weights by
+// moe_lora_transform_base (the pages' reusable transformed weights, DeepGEMM
+// PR #9 Summary), like the transposed copies of the backward.
+//
+//   kind 0  W13 for the forward: N tile t = gate rows 128t .. 128t+127 and
+//           up rows I + 128t .., K = H           ([E][I/128][H/64] tiles)
+//   kind 1  W2 for the forward: rows h, K = I     ([E][H/256][I/64])
+//   kind 2  W13^T for the W13 data gradient: rows h, K = 2I ([E][H/256][2I/64])
+//   kind 3  W2^T for the W2 data gradient: rows i, K = H    ([E][I/256][H/64])
+// Kinds 2 and 3 transpose through LDS; from an MXFP4 base they are the
+// dequantised values (e2m1 x 2^(e-127), exact in bf16).
+#include "engine2.hpp"
+#include "layer.hpp"
+#include "trace.hpp"
+
+namespace moelora {
+
+constexpr int PK_ROWS = 256, PK_KT = 64;
+constexpr int PK_TILE = PK_ROWS * PK_KT;  // elements per stage tile (32 KB)
+
+// 8 bf16 values -> the tile chunk (row r, slot p) at byte 16 (8 r + p)
+__device__ __forceinline__ void pk_store(uint16_t* tile, int r, int p, u32x4 v) {
+  *(u32x4*)(tile + 8 * (8 * r + p)) = v;
+}
+
+// kinds 0, 1: row-major source [N rows, K] (bf16); row map for kind 0
+__global__ __launch_bounds__(256) void k_pack_rows(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                   int kind, int N, int K, int I) {
+  const int nst = K / PK_KT, ntile = kind == 0 ? 2 * I / PK_ROWS : N / PK_ROWS;
+  const long b = blockIdx.x;
+  const int s = (int)(b % nst), t = (int)((b / nst) % ntile);
+  const long e = b / ((long)nst * ntile);
+  uint16_t* tile = dst + b * PK_TILE;
+  const uint16_t* m = src + e * (long)N * K;
+#pragma unroll
+  for (int u = 0; u < PK_TILE / 8 / 256; ++u) {
+    const int q = threadIdx.x + 256 * u;  // tile chunk
+    const int r = q / 8, p = q % 8;
+    const int c = p ^ v2::kswz<PK_KT>(r);
+    const int row = kind == 0 ? (r < 128 ? 128 * t + r : I + 128 * t + (r - 128)) : PK_ROWS * t + r;
+    pk_store(tile, r, p, *(const u32x4*)(m + (long)row * K + PK_KT * s + 8 * c));
+  }
+}
+
+// kinds 2, 3: the transpose of a source S [K, N] (bf16, or MXFP4 with scales
+// per 32 along N): tile rows n0 .. n0 + 255, k0 .. k0 + 63
+template <bool MX>
+__global__ __launch_bounds__(256) void k_pack_cols(const uint16_t* __restrict__ src, const uint8_t* __restrict__ q4,
+                                                   const uint8_t* __restrict__ sc, uint16_t* __restrict__ dst, int N,
+                                                   int K) {
+  __shared__ uint16_t t[PK_KT][PK_ROWS + 8];  // [k][n], rows padded by 16 bytes
+  const int nst = K / PK_KT, ntile = N / PK_ROWS;
+  const long b = blockIdx.x;
+  const int s = (int)(b % nst), nt = (int)((b / nst) % ntile);
+  const long e = b / ((long)nst * ntile);
+  const int k0 = PK_KT * s, n0 = PK_ROWS * nt;
+#pragma unroll
+  for (int u = 0; u < PK_TILE / 8 / 256; ++u) {
+    const int q = threadIdx.x + 256 * u;  // 8 consecutive n of one k-row
+    const int kr = q / 32, cc = q % 32;
+    const long row = e * (long)K + k0 + kr;
+    u32x4 v;
+    if constexpr (MX) {
+      const uint32_t w = *(const uint32_t*)(q4 + row * (N / 2) + (n0 + 8 * cc) / 2);
+      v = v2::fp4x8_bf16(w, v2::e8m0_value(sc[row * (N / 32) + (n0 + 8 * cc) / 32]));
+    } else {
+      v = *(const u32x4*)(src + row * N + n0 + 8 * cc);
+    }
+    *(u32x4*)&t[kr][8 * cc] = v;
+  }
+  __syncthreads();
+  uint16_t* tile = dst + b * PK_TILE;
+#pragma unroll
+  for (int u = 0; u < PK_TILE / 8 / 256; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    const int r = q / 8, p = q % 8;
+    const int c = p ^ v2::kswz<PK_KT>(r);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[8 * c + 2 * i][r] | ((uint32_t)t[8 * c + 2 * i + 1][r] << 16);
+    pk_store(tile, r, p, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// kind 0 / 1 from a bf16 base; kind 2 / 3 from a bf16 (q4 == nullptr) or an
+// MXFP4 base.  E experts of the kind's matrix.
+hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const uint8_t* sc, uint16_t* dst, int E,
+                       int H, int I, hipStream_t st) {
+  if (kind == 0 || kind == 1) {
+    const int N = kind == 0 ? 2 * I : H, K = kind == 0 ? H : I;
+    const long tiles = (long)E * (N / PK_ROWS) * (K / PK_KT);
+    MOE_LAUNCH(k_pack_rows, dim3((unsigned)tiles), dim3(256), 0, st, src, dst, kind, N, K, I);
+  } else {
+    // S = W13 [2I, H] -> rows h, K = 2I;  S = W2 [H, I] -> rows i, K = H
+    const int N = kind == 2 ? H : I, K = kind == 2 ? 2 * I : H;
+    const long tiles = (long)E * (N / PK_ROWS) * (K / PK_KT);
+    if (q4 != nullptr)
+      MOE_LAUNCH(k_pack_cols<true>, dim3((unsigned)tiles), dim3(256), 0, st, nullptr, q4, sc, dst, N, K);
+    else
+      MOE_LAUNCH(k_pack_cols<false>, dim3((unsigned)tiles), dim3(256), 0, st, src, nullptr, nullptr, dst, N, K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moelora

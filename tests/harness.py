@@ -298,6 +298,26 @@ def compare_all(res, ref_out, ref_g, tag="", per_expert: bool = False, rel_max=R
     return report
 
 
+def packed_tiles(m: np.ndarray, gate_up: bool = False) -> np.ndarray:
+    """The library's packed copy of a weight stack m [E, N, K] (uint16 bf16
+    bits), written out from its documented layout: per expert, per N tile of
+    256 rows (with gate_up, W13's forward tiles: gate rows 128t.. then up
+    rows I + 128t..), per stage of 64 k, the 256 x 64 tile as its LDS image
+    -- row r's 16-byte chunk c in slot c ^ ((r ^ (r >> 3)) & 7), rows in
+    order -- tiles in (N tile, stage) order."""
+    E, N, K = m.shape
+    if gate_up:
+        I = N // 2
+        t = np.arange(I // 128)[:, None]
+        rows = np.concatenate([128 * t + np.arange(128), I + 128 * t + np.arange(128)], axis=1).ravel()
+        m = m[:, rows]
+    tl = m.reshape(E, N // 256, 256, K // 64, 8, 8)           # [E, nt, r, s, chunk, 8]
+    r = np.arange(256)[:, None]
+    slot_chunk = np.arange(8)[None, :] ^ ((r ^ (r >> 3)) & 7)  # [r, slot] -> chunk
+    g = np.take_along_axis(tl, slot_chunk[None, None, :, None, :, None], axis=4)
+    return np.ascontiguousarray(g.transpose(0, 1, 3, 2, 4, 5)).reshape(E, N, K)
+
+
 def same_bits(a, b) -> bool:
     """Bitwise equality of two results (arrays by their bytes, ints by value)."""
     if isinstance(a, (int, np.integer)) or isinstance(b, (int, np.integer)):

@@ -202,17 +202,27 @@ def test_transformed_base_checks_before_any_launch():
     dm = B.make_desc(64, 256, 256, 8, 2, 8, base_format=B.MOE_BASE_MXFP4)
     base = B.MoeLoraParams(fake * 2, fake * 3, None, None, *([fake] * 6))
     # an MXFP4 transform without its scales
-    assert lib.moe_lora_transform_base(byref(dm), byref(base), fake * 5, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(dm), byref(base), fake * 5, None, None, None, None) == B.MOE_ERR_INVALID
     # W13T overlapping the packed W13 ([E, 2I, H/2] = 512 KiB here)
     mxp = B.MoeLoraParams(fake * 2, fake * 3, fake * 4, fake * 4 + 65536, *([fake] * 6))
-    assert lib.moe_lora_transform_base(byref(dm), byref(mxp), fake * 2 + 4096, None, None) == B.MOE_ERR_INVALID
-    assert lib.moe_lora_transform_base(None, byref(base), fake * 5, None, None) == B.MOE_ERR_INVALID
-    assert lib.moe_lora_transform_base(byref(d), None, fake * 5, None, None) == B.MOE_ERR_INVALID
-    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 5 + 8, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(dm), byref(mxp), fake * 2 + 4096, None, None, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(None, byref(base), fake * 5, None, None, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), None, fake * 5, None, None, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 5 + 8, None, None, None, None) == B.MOE_ERR_INVALID
     # W13T overlapping W13 ([E, 2I, H] bf16 = 2 MiB here) or W2T overlapping W13T
-    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 2 + 4096, None, None) == B.MOE_ERR_INVALID
-    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, fake * 8 + 1024, None) == B.MOE_ERR_INVALID
-    assert lib.moe_lora_transform_base(byref(d), byref(base), None, None, None) == B.MOE_OK
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 2 + 4096, None, None, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, fake * 8 + 1024, None, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), None, None, None, None, None) == B.MOE_OK
+    # the forward copies: bf16 base only, disjoint from the other outputs
+    mxs = B.MoeLoraParams(fake * 2, fake * 3, fake * 4, fake * 4 + 65536, *([fake] * 6))
+    assert lib.moe_lora_transform_base(byref(dm), byref(mxs), None, None, fake * 8, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, None, fake * 9, None,
+                                       None) == B.MOE_ERR_INVALID  # W13P overlaps W13T (2 MiB)
+    # a forward copy given with an MXFP4 base is refused by the layer calls too
+    prm_mx = B.MoeLoraParams(fake, fake, fake * 4, fake * 5, *([fake] * 6), None, None, fake * 9, None)
+    assert lib.moe_lora_backward(byref(dm), byref(pool), fake, fake, byref(prm_mx), fake * 128, saved, fake * 64,
+                                 fake * 200, byref(grads), fake * 256, scratch, None) == B.MOE_ERR_INVALID
+
 
 
 @pytest.mark.parametrize("clamp", [0.0, -1.0, float("inf"), 10.0, 0.25])

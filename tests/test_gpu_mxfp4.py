@@ -123,7 +123,7 @@ def test_mxfp4_backward_is_the_bf16_backward_on_dequantised_weights(transformed)
     the bf16 backward fed the dequantised weights: expanding the packed
     weights to bf16 in LDS (transformed=False), or reading the transformed
     copy moe_lora_transform_base wrote from them (the dequantised weights
-    transposed; checked element for element here)."""
+    transposed, in the packed layout; checked element for element here)."""
     shape, key, routing, mask = CASES["r128_masked"]
     case = I.layer_inputs(shape, key, routing=routing, mask_prob=mask)
     mx, deq = Hn.mxfp4_base(case)
@@ -131,7 +131,8 @@ def test_mxfp4_backward_is_the_bf16_backward_on_dequantised_weights(transformed)
     if transformed:
         for n, src in (("W13T", deq["W13"]), ("W2T", deq["W2"])):
             got = run_mx.params[n].view(torch.int16).cpu().numpy().view(np.uint16)
-            assert np.array_equal(got, np.ascontiguousarray(src.transpose(0, 2, 1))), n
+            want = Hn.packed_tiles(np.ascontiguousarray(src.transpose(0, 2, 1)))
+            assert np.array_equal(got.reshape(want.shape), want), n
     res_mx = run_mx.run()
     run_bf = Hn.GpuRun(shape, dict(case, W13=deq["W13"], W2=deq["W2"]))
     Lb, Lm = run_bf.layer, run_mx.layer

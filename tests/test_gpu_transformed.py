@@ -1,11 +1,13 @@
-"""Transformed base weights (W13T = W13_e^T, W2T = W2_e^T per expert, the
-reusable transformed weights of DeepGEMM PR #9's Summary): GPU checks.
+"""Transformed base weights (the reusable transformed weights of DeepGEMM
+PR #9's Summary): W13T, W2T (W13_e^T, W2_e^T for the backward) and W13P, W2P
+(W13_e, W2_e for the forward), each in the library's packed stage-tile
+layout.  GPU checks:
 
-- moe_lora_transform_base writes exactly the transposes (bit for bit);
+- moe_lora_transform_base writes exactly the documented packed copies (bit
+  for bit; the layout is restated in tests/harness.py packed_tiles);
 - the layer given them returns bit for bit what it returns without them:
-  the two data-gradient GEMMs then read the weights (and A2) as K tiles
-  instead of transposing them through LDS, with the same products summed in
-  the same order.  Cases span rank 8 and 128, masked routes, ragged M tiles,
+  the same tile bytes reach LDS, so the same products are summed in the
+  same order.  Cases span rank 8 and 128, masked routes, ragged M tiles,
   one expert at top-1, top-16, GeGLU and the frozen-weight gradients.
 """
 import numpy as np
@@ -22,7 +24,7 @@ def _built():
     Hn.ensure_built()
 
 
-def test_transform_base_writes_the_transposes():
+def test_transform_base_writes_the_packed_copies():
     import torch
     from mixture_experts_grouped_amd import binding as B
     E, H, Id = 3, 512, 256
@@ -30,15 +32,17 @@ def test_transform_base_writes_the_transposes():
     g = torch.Generator().manual_seed(5)
     p = {"W13": torch.randn(E, 2 * Id, H, generator=g).to(torch.bfloat16).cuda(),
          "W2": torch.randn(E, H, Id, generator=g).to(torch.bfloat16).cuda()}
-    for n, shp in (("A1", (8, H)), ("A3", (8, H)), ("B1", (E, Id, 8)), ("B3", (E, Id, 8)),
-                   ("A2", (E, 8, Id)), ("B2", (H, 8))):
-        p[n] = torch.zeros(shp, dtype=torch.bfloat16, device="cuda")
     t = B.transform_base(d, p)
     torch.cuda.synchronize()
-    for n, nt in (("W13", "W13T"), ("W2", "W2T")):
-        want = p[n].transpose(1, 2).contiguous().view(torch.int16).cpu().numpy()
-        got = t[nt].view(torch.int16).cpu().numpy()
-        assert np.array_equal(got, want), nt
+
+    def bits(x):
+        return x.view(torch.int16).cpu().numpy().view(np.uint16)
+    w13, w2 = bits(p["W13"]), bits(p["W2"])
+    want = {"W13T": Hn.packed_tiles(np.ascontiguousarray(w13.transpose(0, 2, 1))),
+            "W2T": Hn.packed_tiles(np.ascontiguousarray(w2.transpose(0, 2, 1))),
+            "W13P": Hn.packed_tiles(w13, gate_up=True), "W2P": Hn.packed_tiles(w2)}
+    for n, w in want.items():
+        assert np.array_equal(bits(t[n]).reshape(w.shape), w), n
 
 
 CASES = {
