@@ -107,7 +107,7 @@ struct Plan {
   // byte offsets
   size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_XQ, o_XS, o_HQ, o_HS;
-  size_t o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
+  size_t o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
 Plan make_plan(const moe_lora_desc* d, const Roots& R) {
@@ -131,9 +131,11 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   p.o_zc = take(T * 2 * r * 2);
   p.saved = o;
   o = 0;
-  // the forward's scratch first (Yb in dU's space, Z2 in P's), so that it
-  // is one prefix of the plan: fwd_scratch bytes
+  // the forward's scratch first (Yb in dU's space, the shrink's split
+  // partials, Z2 in P's), so that it is one prefix of the plan: fwd_scratch
+  // bytes
   p.o_dU = take(cap * H * 2);
+  p.o_zsp = take(KSPLIT * T * 2 * r * 4);
   p.o_P = take(cap * 2 * r * 4);
   p.fwd_scratch = p.o_P + up(cap * r * 4);  // Z2 = the first cap * r floats of P
   if (d->base_format == MOE_BASE_MXFP4) {
@@ -145,6 +147,7 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
     p.fwd_scratch = o;
   }
   p.o_q = take(T * r * 4);
+  p.o_qp = take(KSPLIT * T * r * 4);
   p.o_sq = take(T * 2 * r * 2);
   p.o_wsq = take(cap * 2 * r * 2);
   p.o_dGV = take(cap * 2 * I * 2);
@@ -258,6 +261,8 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
 void fill_scratch(LayerArgs& a, const Plan& p, void* base) {
   char* b = (char*)base;
   a.q = (float*)(b + p.o_q);
+  a.qp = (float*)(b + p.o_qp);
+  a.zsp = (float*)(b + p.o_zsp);
   a.sq = (uint16_t*)(b + p.o_sq);
   a.wsq = (uint16_t*)(b + p.o_wsq);
   a.dGV = (uint16_t*)(b + p.o_dGV);

@@ -40,24 +40,30 @@ constexpr int P13_SUB = TMG / GS128::TM;  // sub-tiles per pool M tile
 struct LdQ {
   RowsK<GS64::TM> m;
   TransK<128, KStrided> n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT); }
+  int k0;  // this split's first k
+  __device__ void load(int s) { m.load(k0 + s * KT, 0, false); n.load(k0 + s * KT); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
-// One token tile (one root) per workgroup: B2 of the root's adapter.
+// One token tile (one root) and one of KSPLIT quarters of H per workgroup
+// (B2 of the root's adapter): the partial products go to qp, summed in
+// split order by k_q_sum.  The split is fixed, so a token's q does not
+// depend on the batch.
 __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   int t0, nt, ad;
   if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
-  const int r = a.r;
+  const int r = a.r, ks = blockIdx.y, kh = a.H / KSPLIT;
   LdQ L;
+  L.k0 = ks * kh;
   L.m.contig(a.go, t0, nt, a.H);
   L.m.window(a.H);
   L.n.kp = KStrided{make_rsrc(a.B2 + (long)ad * a.H * r, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
   L.n.cols(0, r);
   f32x16 acc[GS64::NB][GS64::MB];
-  mainloop<GS64>(L, a.H / KT, acc, smem);
+  mainloop<GS64>(L, kh / KT, acc, smem);
   Epi<GS64> ep;
+  float* part = a.qp + (long)ks * a.T * r;
 #pragma unroll
   for (int mb = 0; mb < GS64::MB; ++mb) {
     const int t = t0 + ep.row(mb);
@@ -68,19 +74,33 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
         if (c >= r) continue;
-        f32x4 v;
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = acc[nb][mb][4 * g + q];
-          split_hl(a.s * v[q], hi[q], lo[q]);
-        }
-        *(f32x4*)(a.q + (long)t * r + c) = v;
-        uint16_t* d = a.sq + (long)t * 2 * r + c;
-        *(u32x2*)d = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-        *(u32x2*)(d + r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        *(f32x4*)(part + (long)t * r + c) =
+            f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
       }
   }
+}
+
+// q = the splits' partials in order; s q as hi/lo.  One thread per 4 columns.
+__global__ __launch_bounds__(256) void k_q_sum(LayerArgs a) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int g4 = a.r / 4;
+  if (i >= (long)a.T * g4) return;
+  const long t = i / g4;
+  const int c = (int)(i % g4) * 4;
+  f32x4 v = *(const f32x4*)(a.qp + t * a.r + c);
+#pragma unroll
+  for (int ks = 1; ks < KSPLIT; ++ks) {
+    const f32x4 p = *(const f32x4*)(a.qp + ((long)ks * a.T + t) * a.r + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += p[q];
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_hl(a.s * v[q], hi[q], lo[q]);
+  *(f32x4*)(a.q + t * a.r + c) = v;
+  uint16_t* d = a.sq + t * 2 * a.r + c;
+  *(u32x2*)d = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+  *(u32x2*)(d + a.r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
 }
 
 // one wave per route (t, j)
@@ -978,7 +998,8 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     return ai.err;
   });
   if (ierr != hipSuccess) return ierr;
-  MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM)), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM), KSPLIT), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q_sum, dim3((unsigned)(((long)a.T * (a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
     const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base

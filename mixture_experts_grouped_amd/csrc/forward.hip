@@ -38,25 +38,31 @@ template <int R>
 struct LdPlain {
   RowsK<R> m;
   RowsK<128> n;
-  __device__ void load(int s) { m.load(s * KT, 0, false); n.load(s * KT, 0, false); }
+  int k0 = 0;  // first k (a split's quarter of K)
+  __device__ void load(int s) { m.load(k0 + s * KT, 0, false); n.load(k0 + s * KT, 0, false); }
   __device__ void store(char* sM, char* sN) { m.store(sM); n.store(sN); }
 };
 
-// One token tile (one root) per workgroup row: the root's adapter's factor.
+// One token tile (one root: the root's adapter's factor), one factor and
+// one of KSPLIT quarters of H per workgroup: partial products to zsp, summed
+// in split order by k_shrink_sum.  The split is fixed, so a token's ZA does
+// not depend on the batch.
 __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int fac = blockIdx.y;  // fac 0: A1, 1: A3
   int t0, nt, ad;
   if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
-  const int r = a.r;
+  const int r = a.r, ks = blockIdx.z, kh = a.H / KSPLIT;
   LdPlain<GS64::TM> L;
+  L.k0 = ks * kh;
   L.m.contig(a.x, t0, nt, a.H);
   L.m.window(a.H);
   L.n.contig((fac ? a.A3 : a.A1) + (long)ad * r * a.H, 0, r, a.H);
   L.n.window(a.H);
   f32x16 acc[GS64::NB][GS64::MB];
-  mainloop<GS64>(L, a.H / KT, acc, smem);
+  mainloop<GS64>(L, kh / KT, acc, smem);
   Epi<GS64> ep;
+  float* part = a.zsp + (long)ks * a.T * 2 * r;
 #pragma unroll
   for (int nb = 0; nb < GS64::NB; ++nb)
 #pragma unroll
@@ -67,14 +73,32 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int c = ep.col(nb, g);
         if (c >= r) continue;
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) split_hl(a.s * acc[nb][mb][4 * g + q], hi[q], lo[q]);
-        uint16_t* dst = a.ZA + (long)t * 4 * r + fac * 2 * r + c;
-        *(u32x2*)dst = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-        *(u32x2*)(dst + r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        *(f32x4*)(part + (long)t * 2 * r + fac * r + c) =
+            f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
       }
     }
+}
+
+// ZA = s x the splits' partials in order, as hi/lo.  One thread per 4 columns.
+__global__ __launch_bounds__(256) void k_shrink_sum(LayerArgs a) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int g4 = 2 * a.r / 4;
+  if (i >= (long)a.T * g4) return;
+  const long t = i / g4;
+  const int c2 = (int)(i % g4) * 4, fac = c2 / a.r, c = c2 % a.r;  // r % 8 == 0: 4 columns of one factor
+  f32x4 v = *(const f32x4*)(a.zsp + t * 2 * a.r + c2);
+#pragma unroll
+  for (int ks = 1; ks < KSPLIT; ++ks) {
+    const f32x4 p = *(const f32x4*)(a.zsp + ((long)ks * a.T + t) * 2 * a.r + c2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += p[q];
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_hl(a.s * v[q], hi[q], lo[q]);
+  uint16_t* dst = a.ZA + t * 4 * a.r + fac * 2 * a.r + c;
+  *(u32x2*)dst = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+  *(u32x2*)(dst + a.r) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
 }
 
 // ----------------------------------------------------------------------------
@@ -481,7 +505,8 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
-  MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2, KSPLIT), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_shrink_sum, dim3((unsigned)(((long)a.T * (2 * a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
   if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
     MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,

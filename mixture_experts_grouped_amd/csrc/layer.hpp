@@ -13,6 +13,7 @@ namespace moelora {
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
 constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
 constexpr int MAX_ADAPTERS = 64;  // adapters of one multi-adapter pass
+constexpr int KSPLIT = 4;  // fixed K split of the long-K token GEMMs (ZA = A x, q = B2^T go)
 
 // Accumulator-blocked layout of a [tiles x 256, I] tensor (fp16 here) that is
 // written and read only by kernels holding it in 32 x 32 MFMA accumulator
@@ -79,10 +80,12 @@ struct LayerArgs {
   uint32_t* HS;      //     [cap, I/64]
   uint16_t* Yb;      // [cap, H]  W2_e h, unweighted base output (scratch, forward only)
   uint16_t* zc;      // [T, 2r]   sum_j w Z2 as hi/lo
+  float* zsp;        // [KSPLIT, T, 2r] partials of A1 x | A3 x (forward scratch)
   // forward output
   uint16_t* out;     // [T, H]
   // backward scratch
   float* q;          // [T, r]    B2^T grad_out
+  float* qp;         // [KSPLIT, T, r] its partials over the quarters of H
   uint16_t* sq;      // [T, 2r]   s*q as hi/lo
   uint16_t* wsq;     // [cap, 2r] s*w*q per route as hi/lo
   uint16_t* dGV;     // [cap, 2I] dgate | dup
