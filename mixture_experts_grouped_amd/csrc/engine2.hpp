@@ -74,11 +74,14 @@ __device__ __forceinline__ void lds_load16(rsrc_t rs, char* lds_wave_base, uint3
 // ---------------------------------------------------------------------------
 // geometry
 // ---------------------------------------------------------------------------
-template <int MB_, int NB_, int WM_, int WN_, bool MTR_ = false, bool NTR_ = false, int KT_ = 64>
+// NBUF_: stage buffers (0 = the depth's default); NBUF - 1 stages are queued
+// ahead of the one being multiplied.
+template <int MB_, int NB_, int WM_, int WN_, bool MTR_ = false, bool NTR_ = false, int KT_ = 64, int NBUF_ = 0>
 struct Geo2 {
   static constexpr int MB = MB_, NB = NB_, WM = WM_, WN = WN_, KT = KT_;
   static constexpr int NW = WM * WN, NT = 64 * NW;  // waves and threads per workgroup
-  static constexpr int NBUF = Depth<KT>::NBUF;
+  static constexpr int NBUF = NBUF_ > 0 ? NBUF_ : Depth<KT>::NBUF;
+  static_assert(NBUF >= 2 && NBUF <= 4, "stage buffers");
   static constexpr bool MTR = MTR_, NTR = NTR_;  // operand tile stored K-outer (T tile)
   static constexpr int TM = WM * MB * 32, TN = WN * NB * 32;
   static constexpr int SM_BYTES = TM * 2 * KT, SN_BYTES = TN * 2 * KT;  // same for both layouts

@@ -108,32 +108,43 @@ __global__ __launch_bounds__(256) void k_shrink_sum(LayerArgs a) {
 // N tile = TN/2 gate columns i0.. and the TN/2 up columns with the same i;
 // each wave holds a gate block and its up partner, so SwiGLU runs in registers.
 using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
-constexpr int W13_LDS = cmax(GW13::LDS_BYTES, v2::TileImage<GW13, GW13::TN / 2, uint16_t>::BYTES);
+// Few rows per expert (small T): 64-row parts of a pool tile, with the LDS
+// the smaller M tile frees spent on a third stage buffer (two weight stages
+// in flight instead of one).  Each element still sums the same products in
+// the same order, so the results are those of the full tile.
+using GW13S = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;  // 64 x 256, eight waves
+template <class G>
+constexpr int w13_lds() { return cmax(G::LDS_BYTES, v2::TileImage<G, G::TN / 2, uint16_t>::BYTES); }
+constexpr int W13_LDS = w13_lds<GW13>(), W13S_LDS = w13_lds<GW13S>();
 
 // Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
-// stage); stages [nsplit, ...): the base K = H.
+// stage); stages [nsplit, ...): the base K = H.  M loaders: G::TM rows by
+// token; N loaders: the 256 weight rows of the tile.
+template <class G>
 struct LdW13Base {
-  using KL = v2::KLoad<256, GW13::KT, GW13::NW>;
-  using KL2 = v2::KLoad<256, GW13::KT, GW13::NW, true>;
-  using KA = v2::KLoadA<256, GW13::KT, GW13::NW>;
+  using KL = v2::KLoad<G::TM, G::KT, G::NW>;          // ZA rows (M)
+  using KL2 = v2::KLoad<256, G::KT, G::NW, true>;     // B1 | B3 rows (N)
+  using KA = v2::KLoadA<G::TM, G::KT, G::NW>;         // x rows (M)
+  using KN = v2::KLoadA<256, G::KT, G::NW>;           // W13 rows (N)
   KL me;
   KL2 ne;
   int r, nsplit;
 };
 // NL: the weight tile loader (KLoadA on W13, or KLoadP on its packed copy)
-template <class NL>
-struct LdW13 : LdW13Base {
-  static constexpr int INSTS = 2 * KL::NJ;
-  static_assert(NL::NJ == KL::NJ, "one instruction count per stage");
-  KA mm;
+template <class G, class NL>
+struct LdW13 : LdW13Base<G> {
+  using B = LdW13Base<G>;
+  static constexpr int INSTS = B::KL::NJ + B::KL2::NJ;
+  static_assert(NL::NJ == B::KL2::NJ && B::KA::NJ == B::KL::NJ, "one instruction count per stage");
+  typename B::KA mm;
   NL nm;
   __device__ void issue(int s, char* sM, char* sN) {
-    if (s < nsplit) {
-      me.issue(s * (GW13::KT / 2), 2 * r, true, sM);
-      ne.issue(s * (GW13::KT / 2), 2 * r, true, sN);
+    if (s < this->nsplit) {
+      this->me.issue(s * (G::KT / 2), 2 * this->r, true, sM);
+      this->ne.issue(s * (G::KT / 2), 2 * this->r, true, sN);
     } else {
-      mm.issue((s - nsplit) * GW13::KT, sM);
-      nm.issue((s - nsplit) * GW13::KT, sN);
+      mm.issue((s - this->nsplit) * G::KT, sM);
+      nm.issue((s - this->nsplit) * G::KT, sN);
     }
   }
 };
@@ -167,31 +178,40 @@ static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipe
 // one: both pre-activations are clipped).  Whether a value is clipped is
 // decided on its fp16 rounding, the value saved for the backward, so that
 // both passes take the same decision.
-// PK: the bf16 base read from its packed copy W13P (pack.hip, kind 0)
-template <bool MX, int ACT, bool CL, bool PK>
+// PK: the bf16 base read from its packed copy W13P (pack.hip, kind 0).
+// SK: 64-row parts of the pool tiles (GW13S; bf16 base): the grid is SUB
+// times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
+// tile's rows return at once.
+template <bool MX, int ACT, bool CL, bool PK, bool SK>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
-  static_assert(!(MX && PK), "the packed copy is of a bf16 base");
+  static_assert(!(MX && PK) && !(MX && SK), "the packed copy and the small tiles are of a bf16 base");
   extern __shared__ __align__(16) char smem[];
-  using G = GW13;
-  using KL = LdW13Base::KL;
-  constexpr int TN = G::TN, HALF = TN / 2;
+  using G = typename std::conditional<SK, GW13S, GW13>::type;
+  static_assert(G::NT == GW13::NT && G::TN == GW13::TN, "same workgroup and N tile");
+  using KL = typename LdW13Base<G>::KL;
+  constexpr int TN = G::TN, HALF = TN / 2, SUB = TMG / G::TM;
   const int ntn = a.I / HALF;
+  const int nb = gridDim.x / SUB, b = blockIdx.x % nb, sub = blockIdx.x / nb;
   int mt, nt;
-  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
+  const int row0 = ti.row0 + sub * G::TM;
+  if (row0 >= ti.row_end) return;
+  const int nrows = ti.row_end - row0 < G::TM ? ti.row_end - row0 : G::TM;
   const int e = grp_expert(a, ti.e), i0 = nt * HALF;
   const long le = grp_local(a, ti.e);  // the tile's adapter's B1/B3 of expert e
-  const int nrows = ti.row_end - ti.row0;
   const int r = a.r;
   const int nsplit = (2 * r + G::KT / 2 - 1) / (G::KT / 2);
   int tk[KL::NJ];  // the tile's rows are gathered by token: rows past the expert's count read zero
-  KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+  KL::tokens(tk, a.row2r, a.k, row0, nrows);
   auto wrow = [&](int nl) { return (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF); };
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   if constexpr (!MX) {
-    using NL = typename std::conditional<PK, v2::KLoadP<256, GW13::KT, GW13::NW>, LdW13Base::KA>::type;
-    LdW13<NL> L;
+    using KN = typename LdW13Base<G>::KN;
+    using KL2 = typename LdW13Base<G>::KL2;
+    using NL = typename std::conditional<PK, v2::KLoadP<256, G::KT, G::NW>, KN>::type;
+    LdW13<G, NL> L;
     L.r = r;
     L.nsplit = nsplit;
     L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
@@ -199,7 +219,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     L.ne.rs = make_rsrc(a.B1 + le * a.I * r, (uint64_t)2 * r * a.I);
     L.ne.rs2 = make_rsrc(a.B3 + le * a.I * r, (uint64_t)2 * r * a.I);
 #pragma unroll
-    for (int j = 0; j < KL::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL::row_of(j) % HALF)) * r * 2);
+    for (int j = 0; j < KL2::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL2::row_of(j) % HALF)) * r * 2);
     L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
     L.mm.from_tokens(a.x, a.T, a.H, tk);
     if constexpr (PK) {
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     } else {
       L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
 #pragma unroll
-      for (int j = 0; j < KL::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KL::row_of(j)) * a.H * 2));
+      for (int j = 0; j < KN::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KN::row_of(j)) * a.H * 2));
     }
     v2::run_stages2<G, 2>(L, nsplit + a.H / G::KT, acc, smem);
   } else {
@@ -218,7 +238,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     L.r = r;
     {
       int tke[KE::NJ];
-      KE::tokens(tke, a.row2r, a.k, ti.row0, nrows);
+      KE::tokens(tke, a.row2r, a.k, row0, nrows);
       L.me.from_tokens(a.ZA, a.T, 4 * r, tke);
     }
     L.me.window(4 * r);
@@ -231,7 +251,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     const uint32_t sbytes = (uint32_t)(a.H / 64) * 4u;
     L.wl.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2L * a.I, a.H, wrow,
              a.XS, a.T, [&](int row) {
-               return row < nrows ? (uint32_t)(a.row2r[ti.row0 + row] / a.k) * sbytes : OFF_NONE;
+               return row < nrows ? (uint32_t)(a.row2r[row0 + row] / a.k) * sbytes : OFF_NONE;
              });
     mx::run_mx<G>(L, (2 * r + 31) / 32, a.H / 64, acc, smem);
   }
@@ -254,7 +274,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb) {
       const int cb = (i0 + G::n_local(wn, nb)) / 32;
-      const long ob = acc_block(mt, G::m_local(wm, mb) / 32, cb, a.I) + 4 * lane;
+      const long ob = acc_block(mt, G::m_local(wm, mb) / 32 + sub * (G::TM / 32), cb, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 gv, vv, hv;
@@ -285,10 +305,10 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     }
   if (wide) *a.status = MOE_SAVED_FP16_RANGE;  // only ever 0 -> this bit: racing stores agree
   __syncthreads();
-  ImgH::flush(smem, a.Hh + ti.row0 * (long)a.I + i0, a.I, nrows);
+  ImgH::flush(smem, a.Hh + row0 * (long)a.I + i0, a.I, nrows);
   if constexpr (MX)  // the W2 GEMM's operand: the split of these bf16 rows of h
-    mx::split_image_rows<HALF, G::NT>(smem, ImgH::PITCH, nrows, a.HQ + ti.row0 * (long)(2 * a.I),
-                                      a.HS + ti.row0 * (long)(a.I / 64), a.I, i0);
+    mx::split_image_rows<HALF, G::NT>(smem, ImgH::PITCH, nrows, a.HQ + row0 * (long)(2 * a.I),
+                                      a.HS + row0 * (long)(a.I / 64), a.I, i0);
 }
 
 // ----------------------------------------------------------------------------
@@ -460,23 +480,33 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
 
 // ----------------------------------------------------------------------------
 
-template <bool MX, int ACT, bool CL, bool PK>
-static void launch_w13(const LayerArgs& a, dim3 grid, hipStream_t st) {
-  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL, PK>), grid, dim3(GW13::NT), W13_LDS, st, a);
+template <bool MX, int ACT, bool CL, bool PK, bool SK>
+static void launch_w13(const LayerArgs& a, hipStream_t st) {
+  constexpr int SUB = SK ? TMG / GW13S::TM : 1;
+  const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)) * SUB);
+  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL, PK, SK>), grid, dim3(GW13::NT), SK ? W13S_LDS : W13_LDS, st, a);
+}
+template <bool MX, int ACT, bool PK, bool SK>
+static void launch_w13_cl(const LayerArgs& a, hipStream_t st) {
+  if (a.clamp > 0.0f)
+    launch_w13<MX, ACT, true, PK, SK>(a, st);
+  else
+    launch_w13<MX, ACT, false, PK, SK>(a, st);
 }
 template <bool MX, int ACT, bool PK>
-static void launch_w13_cl(const LayerArgs& a, dim3 grid, hipStream_t st) {
-  if (a.clamp > 0.0f)
-    launch_w13<MX, ACT, true, PK>(a, grid, st);
+static void launch_w13_sk(const LayerArgs& a, hipStream_t st) {
+  if (!MX && a.small_tiles)
+    launch_w13_cl<MX, ACT, PK, !MX>(a, st);
   else
-    launch_w13<MX, ACT, false, PK>(a, grid, st);
+    launch_w13_cl<MX, ACT, PK, false>(a, st);
 }
-template <bool MX, bool PK>
+template <bool MX, bool PK, bool SK>
 static void set_w13_lds(AttrInit& ai) {
-  ai.lds((const void*)k_w13<MX, 0, false, PK>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 1, false, PK>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 0, true, PK>, W13_LDS);
-  ai.lds((const void*)k_w13<MX, 1, true, PK>, W13_LDS);
+  const int lds = SK ? W13S_LDS : W13_LDS;
+  ai.lds((const void*)k_w13<MX, 0, false, PK, SK>, lds);
+  ai.lds((const void*)k_w13<MX, 1, false, PK, SK>, lds);
+  ai.lds((const void*)k_w13<MX, 0, true, PK, SK>, lds);
+  ai.lds((const void*)k_w13<MX, 1, true, PK, SK>, lds);
 }
 
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
@@ -492,9 +522,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   hipError_t err = attrs.run([] {
     AttrInit ai;
     ai.lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_w13_lds<false, false>(ai);
-    set_w13_lds<false, true>(ai);
-    set_w13_lds<true, false>(ai);
+    set_w13_lds<false, false, false>(ai);
+    set_w13_lds<false, true, false>(ai);
+    set_w13_lds<false, false, true>(ai);
+    set_w13_lds<false, true, true>(ai);
+    set_w13_lds<true, false, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
     ai.lds((const void*)k_w2<false, false>, W2_LDS);
     ai.lds((const void*)k_w2<false, true>, W2_LDS);
@@ -513,16 +545,15 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
                   a.XQ, a.XS, (long)a.T, a.H);
   }
   {
-    const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)));
     const bool pk = a.W13P != nullptr;  // bf16 base only (checked on the host)
     if (a.mx && a.act == 1)
-      launch_w13_cl<true, 1, false>(a, grid, st);
+      launch_w13_sk<true, 1, false>(a, st);
     else if (a.mx)
-      launch_w13_cl<true, 0, false>(a, grid, st);
+      launch_w13_sk<true, 0, false>(a, st);
     else if (a.act == 1)
-      pk ? launch_w13_cl<false, 1, true>(a, grid, st) : launch_w13_cl<false, 1, false>(a, grid, st);
+      pk ? launch_w13_sk<false, 1, true>(a, st) : launch_w13_sk<false, 1, false>(a, st);
     else
-      pk ? launch_w13_cl<false, 0, true>(a, grid, st) : launch_w13_cl<false, 0, false>(a, grid, st);
+      pk ? launch_w13_sk<false, 0, true>(a, st) : launch_w13_sk<false, 0, false>(a, st);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   if (a.mx)

@@ -41,6 +41,9 @@ struct LayerArgs {
   // stacked [na, ...], expert-local ones [na, E, ...].
   int na, EV;
   int roots[MAX_ADAPTERS + 1];
+  // few rows per pool group (bf16 base): the base GEMMs take 64-row parts of
+  // each pool tile (bitwise the same results as full tiles)
+  int small_tiles;
   // pool
   const int32_t* counts;
   const int32_t* offsets;

@@ -144,3 +144,24 @@ def test_fp16_range_is_flagged_without_clamp_and_clipped_with_it():
     # the same inputs without the large expert: the bit stays clear
     case["W13"][0] = I.layer_inputs(shape, (64,))["W13"][0]
     assert Hn.GpuRun(shape, case).run()["saved_status"] == 0
+
+
+def test_small_tile_parts_equal_full_tiles():
+    """With few routes per expert the base GEMMs take 64-row parts of each
+    pool tile; an expert holding more rows than a part is spread over several
+    parts.  The same tokens inside a batch large enough for full tiles give
+    bitwise the same out, grad_x and grad_w (each element sums the same
+    products in the same order)."""
+    shape_b = I.Shape(T=400, H=512, I=256, E=8, topk=2, rank=16)
+    case = I.layer_inputs(shape_b, (61,), routing="softmax_topk", mask_prob=0.1)
+    # the first 100 tokens all go to experts 0 and 1: 100 rows each (two parts)
+    case["topk_idx"][:100] = np.array([0, 1], np.int32)
+    big = Hn.GpuRun(shape_b, case).run()
+    shape_s = I.Shape(T=100, H=512, I=256, E=8, topk=2, rank=16)   # 200 routes <= 32 x 8: small tiles
+    small = dict(case)
+    for n in ("x", "grad_out", "topk_idx", "topk_w"):
+        small[n] = np.ascontiguousarray(case[n][:100])
+    for transformed in (False, True):
+        res = Hn.GpuRun(shape_s, small, transformed=transformed).run()
+        for n in ("out", "grad_x", "grad_w"):
+            assert Hn.same_bits(res[n], np.ascontiguousarray(big[n][:100])), (transformed, n)
