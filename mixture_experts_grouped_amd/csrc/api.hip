@@ -210,9 +210,9 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.E = d->E;
   a.na = R.na;
   a.EV = d->E * R.na;
-  // at most 32 routes per (expert, adapter) group on average: most tiles
+  // at most 48 routes per (expert, adapter) group on average: most groups
   // then fit one 64-row part (a larger group re-reads its weights per part)
-  a.small_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)32 * a.EV;
+  a.small_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)48 * a.EV;
   for (int q = 0; q <= R.na; ++q) a.roots[q] = R.r[q];
   a.k = d->topk;
   a.r = d->rank;

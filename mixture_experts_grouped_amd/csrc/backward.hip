@@ -174,23 +174,32 @@ struct LdW2dMX : LdW2dBase<GW2D::NW> {
 using GW2DK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
 static_assert(GW2DK::TM == GW2D::TM && GW2DK::TN == GW2D::TN && GW2DK::STAGE == GW2D::STAGE,
               "same tile and stage as the transposing form");
+// Few rows per expert (small T), with the transformed weights: 64-row parts
+// of each pool tile and a third stage buffer (bitwise the same products and
+// order as the full tile).
+using GW2DS = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;
+constexpr int W2DS_LDS = cmax(GW2DS::LDS_BYTES, 2 * v2::TileImage<GW2DS, GW2DS::TN / 2, uint16_t>::BYTES +
+                                                    GW2DS::WN * GW2DS::TM * 4);
+template <class G>
 struct LdW2dK {
-  using KL = v2::KLoad<256, GW2DK::KT, GW2DK::NW>;
-  using KA = v2::KLoadA<256, GW2DK::KT, GW2DK::NW>;
-  using KP = v2::KLoadP<256, GW2DK::KT, GW2DK::NW>;
-  static_assert(KA::NJ == KL::NJ && KP::NJ == KL::NJ, "one instruction count per stage");
-  static constexpr int INSTS = 2 * KL::NJ;
-  KL me, ne;  // s q by token | A2T rows
-  KA mm;      // go by token
-  KP nm;      // W2T rows, packed (pack.hip, kind 3)
+  using KL = v2::KLoad<G::TM, G::KT, G::NW>;   // s q by token (M)
+  using KN = v2::KLoad<256, G::KT, G::NW>;     // A2T rows (N)
+  using KA = v2::KLoadA<G::TM, G::KT, G::NW>;  // go by token (M)
+  using KP = v2::KLoadP<256, G::KT, G::NW>;    // W2T rows, packed (pack.hip, kind 3) (N)
+  static_assert(KA::NJ == KL::NJ && KP::NJ == KN::NJ, "one instruction count per stage");
+  static constexpr int INSTS = KL::NJ + KN::NJ;
+  KL me;
+  KN ne;
+  KA mm;
+  KP nm;
   int next;
   __device__ void issue(int s, char* sM, char* sN) {
     if (s < next) {
-      me.issue(s * GW2DK::KT, 0, false, sM);
-      ne.issue(s * GW2DK::KT, 0, false, sN);
+      me.issue(s * G::KT, 0, false, sM);
+      ne.issue(s * G::KT, 0, false, sN);
     } else {
-      mm.issue((s - next) * GW2DK::KT, sM);
-      nm.issue((s - next) * GW2DK::KT, sN);
+      mm.issue((s - next) * G::KT, sM);
+      nm.issue((s - next) * G::KT, sN);
     }
   }
 };
@@ -200,28 +209,39 @@ struct LdW2dK {
 // CL: activation clamp (as in the forward): g, v clipped to [-a.clamp,
 // a.clamp] before the activation; the clip passes gradient only where
 // |x| <= a.clamp, decided on the saved fp16 values as the forward decided.
-template <bool MX, int ACT, bool TW, bool CL>
+// SK (with TW): 64-row parts of the pool tiles (GW2DS); the grid is SUB
+// times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
+// tile's rows return at once.
+template <bool MX, int ACT, bool TW, bool CL, bool SK>
 __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
-  static_assert(!(MX && TW), "transformed weights are bf16");
+  static_assert(!(MX && TW) && (TW || !SK), "transformed weights are bf16; small parts read them");
   extern __shared__ __align__(16) char smem[];
-  using G = typename std::conditional<TW, GW2DK, GW2D>::type;
+  using G = typename std::conditional<SK, GW2DS, typename std::conditional<TW, GW2DK, GW2D>::type>::type;
+  constexpr int SUB = TMG / G::TM;
   const int ntn = a.I / G::TN;
+  // part `sub` of pool tile work item b (SUB == 1: the block index itself)
+  const int nb = SUB == 1 ? (int)gridDim.x : __builtin_amdgcn_readfirstlane(gridDim.x / SUB);
+  const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
+  const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
+  const int row0 = ti.row0 + sub * G::TM;
+  if (row0 >= ti.row_end) return;
   const int i0 = nt * G::TN;
-  const int nrows = ti.row_end - ti.row0;
+  const int nrows = ti.row_end - row0;  // rows to the expert's end (the tile holds at most TM of them)
   const int r = a.r;
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
   const int next = (2 * r + G::KT - 1) / G::KT;
   const long e = grp_expert(a, ti.e), le = grp_local(a, ti.e);  // base expert; A2 of its adapter
   if constexpr (TW) {
-    LdW2dK L;
+    using LT = LdW2dK<G>;
+    LT L;
     L.next = next;
     {
-      int tk[LdW2dK::KL::NJ];
-      LdW2dK::KL::tokens(tk, a.row2r, a.k, ti.row0, nrows);
+      int tk[LT::KL::NJ];
+      LT::KL::tokens(tk, a.row2r, a.k, row0, nrows);
       L.me.from_tokens(a.sq, a.T, 2 * r, tk);
       L.mm.from_tokens(a.go, a.T, a.H, tk);
     }
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   int rr[G::MB];
   float wr[G::MB];
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) rr[mb] = a.row2r[ti.row0 + min(ep.row(mb), nrows - 1)];
+  for (int mb = 0; mb < G::MB; ++mb) rr[mb] = a.row2r[row0 + min(ep.row(mb), nrows - 1)];
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
     const float wt = a.w[rr[mb]];
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   }
   char* img_g = smem;
   char* img_v = smem + Img::BYTES;
-  uint16_t* out = a.dGV + ti.row0 * 2 * (long)a.I + i0;
+  uint16_t* out = a.dGV + row0 * 2 * (long)a.I + i0;
   // router gradient: grad_w = <go, W2 h + s B2 A2 h> = <W2^T go + A2^T s q, h>,
   // i.e. the row dot product of the (unweighted) accumulator with h, which
   // the SwiGLU below recomputes in fp32 from G and V
@@ -304,7 +324,8 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     f16x4 gq[G::MB][4], vq[G::MB][4];
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const long ob = acc_block(mt, G::m_local(wm, mb) / 32, (i0 + G::n_local(wn, nb)) / 32, a.I) + 4 * lane;
+      const long ob =
+          acc_block(mt, G::m_local(wm, mb) / 32 + sub * (G::TM / 32), (i0 + G::n_local(wn, nb)) / 32, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         gq[mb][g] = *(const f16x4*)(a.G + ob + 256 * g);
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
     float t = 0.0f;
 #pragma unroll
     for (int c = 0; c < G::WN; ++c) t += red[c * G::TM + lr];
-    a.dwp[(long)nt * a.cap + ti.row0 + lr] = t;
+    a.dwp[(long)nt * a.cap + row0 + lr] = t;
   }
 }
 
@@ -472,21 +493,53 @@ struct LdW13dK {
   }
 };
 
-// TW: read the transformed weights (bf16 base only)
-template <bool MX, bool TW>
+// Few rows per expert (small T), with the transformed weights: 64-row parts
+// of each pool tile and a third stage buffer, one plain pipeline over all
+// eight waves (bitwise the same products and order as the full tile).
+using GW13DS = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;
+constexpr int W13DS_LDS = cmax(GW13DS::LDS_BYTES, v2::TileImage<GW13DS, GW13DS::TN, uint16_t>::BYTES);
+struct LdW13dS {
+  using KA = v2::KLoadS<GW13DS::TM, GW13DS::KT, GW13DS::NW>;
+  using KP = v2::KLoadP<256, GW13DS::KT, GW13DS::NW>;
+  static constexpr int INSTS = KA::NJ + KP::NJ;
+  KA m;   // dGV rows
+  KP n;   // W13T rows, packed
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GW13DS::KT, sM);
+    n.issue(s * GW13DS::KT, sN);
+  }
+};
+
+// TW: read the transformed weights (bf16 base only).  SK (with TW): 64-row
+// parts of the pool tiles; the grid is SUB times larger and part `sub` takes
+// rows row0 + 64 sub ..; parts past the tile's rows return at once.
+template <bool MX, bool TW, bool SK>
 __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
-  static_assert(!(MX && TW), "transformed weights are bf16");
+  static_assert(!(MX && TW) && (TW || !SK), "transformed weights are bf16; small parts read them");
   extern __shared__ __align__(16) char smem[];
-  using G = typename std::conditional<TW, GW13DK, GW13D>::type;
+  using G = typename std::conditional<SK, GW13DS, typename std::conditional<TW, GW13DK, GW13D>::type>::type;
+  constexpr int SUB = TMG / G::TM;
   const int ntn = a.H / G::TN;
+  // part `sub` of pool tile work item b (SUB == 1: the block index itself)
+  const int nb = SUB == 1 ? (int)gridDim.x : __builtin_amdgcn_readfirstlane(gridDim.x / SUB);
+  const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
+  const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
+  const int row0 = ti.row0 + sub * G::TM;
+  if (row0 >= ti.row_end) return;
+  const int nrows = ti.row_end - row0 < G::TM ? ti.row_end - row0 : G::TM;
   const int h0 = nt * G::TN;
   const long e = grp_expert(a, ti.e);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (TW) {
+  if constexpr (SK) {
+    LdW13dS L;
+    L.m.contig(a.dGV, row0, nrows, 2 * a.I);
+    L.n.set(a.W13T + e * a.H * 2 * a.I, (uint64_t)a.H * 2 * a.I * 2, nt, 2 * a.I / G::KT);
+    v2::run_stages2<G, 0>(L, 2 * a.I / G::KT, acc, smem);
+  } else if constexpr (TW) {
     LdW13dK L;
     L.m.contig(a.dGV, ti.row0, ti.row_end - ti.row0, 2 * a.I);
     L.n.set(a.W13T + e * a.H * 2 * a.I, (uint64_t)a.H * 2 * a.I * 2, nt, 2 * a.I / G::KT);
@@ -515,7 +568,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
                  f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
                        acc[nb][mb][4 * g + 3]});
   __syncthreads();
-  Img::flush(smem, a.dU + ti.row0 * (long)a.H + h0, a.H, ti.row_end - ti.row0);
+  Img::flush(smem, a.dU + row0 * (long)a.H + h0, a.H, nrows);
 }
 
 // ----------------------------------------------------------------------------
@@ -955,28 +1008,33 @@ hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, in
 }
 
 
-template <bool MX, int ACT, bool TW, bool CL>
+template <bool MX, int ACT, bool TW, bool CL, bool SK>
 static void launch_w2d(const LayerArgs& a, dim3 grid, hipStream_t st) {
-  MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<MX, ACT, TW, CL>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
+  if constexpr (SK)
+    MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<MX, ACT, TW, CL, SK>), dim3(grid.x * (TMG / GW2DS::TM)), dim3(GW2D::NT),
+                  W2DS_LDS, st, a);
+  else
+    MOE_LAUNCH_AS("k_w2dgrad", (k_w2dgrad<MX, ACT, TW, CL, SK>), grid, dim3(GW2D::NT), W2D_LDS, st, a);
 }
-template <bool MX, bool TW>
+template <bool MX, bool TW, bool SK>
 static void launch_w2d_var(const LayerArgs& a, dim3 grid, hipStream_t st) {
   const bool cl = a.clamp > 0.0f;
   if (a.act == 1 && cl)
-    launch_w2d<MX, 1, TW, true>(a, grid, st);
+    launch_w2d<MX, 1, TW, true, SK>(a, grid, st);
   else if (a.act == 1)
-    launch_w2d<MX, 1, TW, false>(a, grid, st);
+    launch_w2d<MX, 1, TW, false, SK>(a, grid, st);
   else if (cl)
-    launch_w2d<MX, 0, TW, true>(a, grid, st);
+    launch_w2d<MX, 0, TW, true, SK>(a, grid, st);
   else
-    launch_w2d<MX, 0, TW, false>(a, grid, st);
+    launch_w2d<MX, 0, TW, false, SK>(a, grid, st);
 }
-template <bool MX, bool TW>
+template <bool MX, bool TW, bool SK>
 static void set_w2d_lds(AttrInit& ai) {
-  ai.lds((const void*)k_w2dgrad<MX, 0, TW, false>, W2D_LDS);
-  ai.lds((const void*)k_w2dgrad<MX, 1, TW, false>, W2D_LDS);
-  ai.lds((const void*)k_w2dgrad<MX, 0, TW, true>, W2D_LDS);
-  ai.lds((const void*)k_w2dgrad<MX, 1, TW, true>, W2D_LDS);
+  const int lds = SK ? W2DS_LDS : W2D_LDS;
+  ai.lds((const void*)k_w2dgrad<MX, 0, TW, false, SK>, lds);
+  ai.lds((const void*)k_w2dgrad<MX, 1, TW, false, SK>, lds);
+  ai.lds((const void*)k_w2dgrad<MX, 0, TW, true, SK>, lds);
+  ai.lds((const void*)k_w2dgrad<MX, 1, TW, true, SK>, lds);
 }
 
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
@@ -984,12 +1042,14 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   const hipError_t ierr = attrs.run([] {
     AttrInit ai;
     ai.lds((const void*)k_q, GS64::LDS_BYTES);
-    set_w2d_lds<false, false>(ai);
-    set_w2d_lds<true, false>(ai);
-    set_w2d_lds<false, true>(ai);
-    ai.lds((const void*)k_w13dgrad<false, false>, W13D_LDS);
-    ai.lds((const void*)k_w13dgrad<true, false>, W13D_LDS);
-    ai.lds((const void*)k_w13dgrad<false, true>, W13D_LDS);
+    set_w2d_lds<false, false, false>(ai);
+    set_w2d_lds<true, false, false>(ai);
+    set_w2d_lds<false, true, false>(ai);
+    set_w2d_lds<false, true, true>(ai);
+    ai.lds((const void*)k_w13dgrad<false, false, false>, W13D_LDS);
+    ai.lds((const void*)k_w13dgrad<true, false, false>, W13D_LDS);
+    ai.lds((const void*)k_w13dgrad<false, true, false>, W13D_LDS);
+    ai.lds((const void*)k_w13dgrad<false, true, true>, W13DS_LDS);
     ai.lds((const void*)k_p13, GS128::LDS_BYTES);
     ai.lds((const void*)k_rank_dx, RK_LDS);
     ai.lds((const void*)k_wgrad_local, WG_LDS);
@@ -1009,22 +1069,25 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     if (tw)
-      launch_w2d_var<false, true>(a, grid, st);
+      a.small_tiles ? launch_w2d_var<false, true, true>(a, grid, st) : launch_w2d_var<false, true, false>(a, grid, st);
     else if (a.mx)
-      launch_w2d_var<true, false>(a, grid, st);
+      launch_w2d_var<true, false, false>(a, grid, st);
     else
-      launch_w2d_var<false, false>(a, grid, st);
+      launch_w2d_var<false, false, false>(a, grid, st);
   }
   const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
   {
     const dim3 grid(a.maxtiles * (a.H / GW13D::TN));
-    if (a.W13T != nullptr)
-      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, true>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+    if (a.W13T != nullptr && a.small_tiles)
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, true, true>), dim3(grid.x * (TMG / GW13DS::TM)),
+                    dim3(GW13D::NT), W13DS_LDS, st, a);
+    else if (a.W13T != nullptr)
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, true, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
     else if (a.mx)
-      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<true, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<true, false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
     else
-      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
+      MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }
   MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
   const long npc = (long)a.T * (2 * a.r / 4);

@@ -357,7 +357,9 @@ struct KLoadP {
   }
   __device__ __forceinline__ void issue(int k0, char* tile) const {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS bases in SGPRs
-    const uint32_t st = tile0 + (uint32_t)(k0 / KT) * (uint32_t)TILE;
+    // the stage's offset is workgroup-uniform: keep it in an SGPR (the scalar
+    // offset operand), whatever the compiler can prove about tile0
+    const uint32_t st = __builtin_amdgcn_readfirstlane(tile0 + (uint32_t)(k0 / KT) * (uint32_t)TILE);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) lds_load16(rs, tile + 1024 * (w + NW * j), lane_off, st + 1024u * NW * j);
   }

@@ -191,7 +191,10 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   using KL = typename LdW13Base<G>::KL;
   constexpr int TN = G::TN, HALF = TN / 2, SUB = TMG / G::TM;
   const int ntn = a.I / HALF;
-  const int nb = gridDim.x / SUB, b = blockIdx.x % nb, sub = blockIdx.x / nb;
+  // part `sub` of pool tile work item b (SUB == 1: the block index itself)
+  const int nb = SUB == 1 ? (int)gridDim.x : __builtin_amdgcn_readfirstlane(gridDim.x / SUB);
+  const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
+  const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
   if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
@@ -350,7 +353,22 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
 }
 
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
+// few rows per expert: 64-row parts of each pool tile, a third stage buffer
+using GW2S = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;
 constexpr int W2_LDS = cmax(GW2::LDS_BYTES, v2::TileImage<GW2, GW2::TN, uint16_t>::BYTES);
+constexpr int W2S_LDS = cmax(GW2S::LDS_BYTES, v2::TileImage<GW2S, GW2S::TN, uint16_t>::BYTES);
+// the small-part pipeline: all eight waves queue a stage
+template <class NL>
+struct LdW2S {
+  using KL = v2::KLoadS<GW2S::TM, GW2S::KT, GW2S::NW>;
+  static constexpr int INSTS = KL::NJ + NL::NJ;
+  KL m;
+  NL n;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GW2S::KT, sM);
+    n.issue(s * GW2S::KT, sN);
+  }
+};
 template <class NL>  // the weight tile loader: KLoadS on W2, or KLoadP on its packed copy
 struct LdW2 {
   // the ping-pong loop: the four waves of group A queue a whole stage
@@ -366,20 +384,40 @@ struct LdW2 {
 };
 
 // PK: the bf16 base read from its packed copy W2P (pack.hip, kind 1)
-template <bool MX, bool PK>
+template <bool MX, bool PK, bool SK>
+// SK: 64-row parts of the pool tiles (GW2S, bf16 base): the grid is SUB
+// times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
+// tile's rows return at once (bitwise the same as the full tile).
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
-  static_assert(!(MX && PK), "the packed copy is of a bf16 base");
+  static_assert(!(MX && PK) && !(MX && SK), "the packed copy and the small parts are of a bf16 base");
   extern __shared__ __align__(16) char smem[];
-  using G = GW2;
+  using G = typename std::conditional<SK, GW2S, GW2>::type;
+  constexpr int SUB = TMG / G::TM;
   const int ntn = a.H / G::TN;
+  // part `sub` of pool tile work item b (SUB == 1: the block index itself)
+  const int nb = SUB == 1 ? (int)gridDim.x : __builtin_amdgcn_readfirstlane(gridDim.x / SUB);
+  const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
+  const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(blockIdx.x, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
+  const int row0 = ti.row0 + sub * G::TM;
+  if (row0 >= ti.row_end) return;
   const int h0 = nt * G::TN;
-  const int nrows = ti.row_end - ti.row0;
+  const int nrows = ti.row_end - row0;  // rows to the expert's end (the tile holds at most TM of them)
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (!MX) {
+  if constexpr (SK) {
+    using NL = typename std::conditional<PK, v2::KLoadP<256, G::KT, G::NW>, v2::KLoadS<256, G::KT, G::NW>>::type;
+    LdW2S<NL> L;
+    L.m.contig(a.Hh, row0, nrows, a.I);
+    const long e = grp_expert(a, ti.e);
+    if constexpr (PK)
+      L.n.set(a.W2P + e * a.H * a.I, (uint64_t)a.H * a.I * 2, nt, a.I / G::KT);
+    else
+      L.n.contig(a.W2 + e * a.H * a.I, h0, G::TN, a.I);
+    v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  } else if constexpr (!MX) {
     using NL = typename std::conditional<PK, v2::KLoadP<256, GW2::KT, 4>, v2::KLoadS<256, GW2::KT, 4>>::type;
     LdW2<NL> L;
     L.m.contig(a.Hh, ti.row0, nrows, a.I);
@@ -412,7 +450,7 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
                  f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
                        acc[nb][mb][4 * g + 3]});
   __syncthreads();
-  Img::flush(smem, a.Yb + ti.row0 * (long)a.H + h0, a.H, ti.row_end - ti.row0);
+  Img::flush(smem, a.Yb + row0 * (long)a.H + h0, a.H, nrows);
 }
 
 // ----------------------------------------------------------------------------
@@ -528,9 +566,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_w13_lds<false, true, true>(ai);
     set_w13_lds<true, false, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
-    ai.lds((const void*)k_w2<false, false>, W2_LDS);
-    ai.lds((const void*)k_w2<false, true>, W2_LDS);
-    ai.lds((const void*)k_w2<true, false>, W2_LDS);
+    ai.lds((const void*)k_w2<false, false, false>, W2_LDS);
+    ai.lds((const void*)k_w2<false, true, false>, W2_LDS);
+    ai.lds((const void*)k_w2<false, false, true>, W2S_LDS);
+    ai.lds((const void*)k_w2<false, true, true>, W2S_LDS);
+    ai.lds((const void*)k_w2<true, false, false>, W2_LDS);
     ai.lds((const void*)k_rank_combine, RK_LDS);
     return ai.err;
   });
@@ -556,12 +596,19 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
       pk ? launch_w13_sk<false, 0, true>(a, st) : launch_w13_sk<false, 0, false>(a, st);
   }
   MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
-  if (a.mx)
-    MOE_LAUNCH_AS("k_w2", (k_w2<true, false>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
-  else if (a.W2P != nullptr)
-    MOE_LAUNCH_AS("k_w2", (k_w2<false, true>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
-  else
-    MOE_LAUNCH_AS("k_w2", (k_w2<false, false>), dim3(a.maxtiles * (a.H / GW2::TN)), dim3(GW2::NT), W2_LDS, st, a);
+  {
+    const dim3 g(a.maxtiles * (a.H / GW2::TN)), gs(g.x * (TMG / GW2S::TM));
+    if (a.mx)
+      MOE_LAUNCH_AS("k_w2", (k_w2<true, false, false>), g, dim3(GW2::NT), W2_LDS, st, a);
+    else if (a.small_tiles && a.W2P != nullptr)
+      MOE_LAUNCH_AS("k_w2", (k_w2<false, true, true>), gs, dim3(GW2::NT), W2S_LDS, st, a);
+    else if (a.small_tiles)
+      MOE_LAUNCH_AS("k_w2", (k_w2<false, false, true>), gs, dim3(GW2::NT), W2S_LDS, st, a);
+    else if (a.W2P != nullptr)
+      MOE_LAUNCH_AS("k_w2", (k_w2<false, true, false>), g, dim3(GW2::NT), W2_LDS, st, a);
+    else
+      MOE_LAUNCH_AS("k_w2", (k_w2<false, false, false>), g, dim3(GW2::NT), W2_LDS, st, a);
+  }
   const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_rank_combine, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
