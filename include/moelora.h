@@ -84,7 +84,10 @@ typedef int32_t moe_status;
      NaN: MOE_ERR_INVALID.  The clip decision is taken on the fp16-rounded
      pre-activation the forward saves, so forward and backward agree.
  * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
- *   1 <= topk <= 16, 1 <= rank <= 128 with rank % 8 == 0, T*H*2 and 4*I*H
+ *   1 <= topk <= 16, 1 <= rank <= 128 (a rank that is not a multiple of 8
+ *   runs on copies of the factors widened with zero rows or columns to the
+ *   next multiple, kept in the scratch workspace; the extra terms are exact
+ *   zeros and the gradients are cut back to the caller's rank), T*H*2 and 4*I*H
  *   below 2^31 bytes (one 32-bit buffer offset per token-row tensor and per
  *   expert's weights).  Other values: MOE_ERR_UNSUPPORTED (non-positive sizes:
  *   MOE_ERR_INVALID).  base_format: MOE_BASE_BF16 or MOE_BASE_MXFP4. */

@@ -35,7 +35,7 @@ moe_status check_desc(const moe_lora_desc* d) {
     if (!ok) return MOE_ERR_INVALID;
   }
   if (d->H % 256 != 0 || d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
-  if (d->E > 512 || d->topk > 16 || d->rank > 128 || d->rank % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->E > 512 || d->topk > 16 || d->rank > 128) return MOE_ERR_UNSUPPORTED;
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
   if (std::isnan(d->clamp)) return MOE_ERR_INVALID;
   if (d->base_format != MOE_BASE_BF16 && d->base_format != MOE_BASE_MXFP4) return MOE_ERR_UNSUPPORTED;
@@ -88,6 +88,31 @@ moe_status check_call(const moe_lora_desc* d, const moe_adapters* ad, Roots& R) 
   return st != MOE_OK ? st : read_roots(d, ad, R);
 }
 
+// The kernels' rank: a multiple of 8.  A caller's rank below it runs on
+// copies of the factors widened with zero rows or columns (the extra rank
+// terms are exactly zero), whose gradients are cut back afterwards.
+int rank_p(const moe_lora_desc* d) { return (d->rank + 7) & ~7; }
+bool padded(const moe_lora_desc* d) { return rank_p(d) != d->rank; }
+
+// Element offsets of the six factors of na adapters at rank rp in one
+// contiguous block: A1, A3 [na, rp, H]; B1, B3 [na, E, I, rp];
+// A2 [na, E, rp, I]; B2 [na, H, rp] (the gradients use the same layout).
+struct FacBlock {
+  size_t A1, A3, B1, B3, A2, B2, total;
+  FacBlock(const moe_lora_desc* d, int na) {
+    const size_t rp = rank_p(d), H = d->H, I = d->I, E = d->E;
+    size_t o = 0;
+    auto take = [&](size_t n) { const size_t at = o; o += (n + 127) & ~(size_t)127; return at; };  // 256-byte aligned
+    A1 = take(na * rp * H);
+    A3 = take(na * rp * H);
+    B1 = take(na * E * I * rp);
+    B3 = take(na * E * I * rp);
+    A2 = take(na * E * rp * I);
+    B2 = take(na * H * rp);
+    total = o;
+  }
+};
+
 int resolve_bm(const moe_lora_desc* d) {
   // The grouped-GEMM tiles start at each expert's first row and mask at its
   // count, so BLOCK_M changes only the padding; the smallest value wastes least.
@@ -107,7 +132,7 @@ struct Plan {
   // byte offsets
   size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_XQ, o_XS, o_HQ, o_HS;
-  size_t o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
+  size_t o_fac, o_gfac, o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
 
 Plan make_plan(const moe_lora_desc* d, const Roots& R) {
@@ -117,7 +142,8 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   const int64_t routes = (int64_t)d->T * d->topk;
   p.maxtiles = (int)((routes + TMG - 1) / TMG + std::min<int64_t>((int64_t)d->E * R.na, routes));
   p.nsplit = R.tiles(kSharedSplit);  // chunks of the shared-factor reductions, per root
-  const size_t T = d->T, H = d->H, I = d->I, r = d->rank, cap = (size_t)p.cap;
+  const size_t T = d->T, H = d->H, I = d->I, r = rank_p(d), cap = (size_t)p.cap;
+  const size_t facb = padded(d) ? FacBlock(d, R.na).total * 2 : 0;  // the zero-padded factor copies
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
   p.o_status = take(sizeof(int32_t));  // MOE_SAVED_STATUS_OFFSET
@@ -134,6 +160,7 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   // the forward's scratch first (Yb in dU's space, the shrink's split
   // partials, Z2 in P's), so that it is one prefix of the plan: fwd_scratch
   // bytes
+  p.o_fac = take(facb);
   p.o_dU = take(cap * H * 2);
   p.o_zsp = take(KSPLIT * T * 2 * r * 4);
   p.o_P = take(cap * 2 * r * 4);
@@ -146,6 +173,7 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
     p.o_HS = take(cap * (I / 64) * 4);
     p.fwd_scratch = o;
   }
+  p.o_gfac = take(facb);  // the padded rank's gradients, before they are cut back
   p.o_q = take(T * r * 4);
   p.o_qp = take(KSPLIT * T * r * 4);
   p.o_sq = take(T * 2 * r * 2);
@@ -215,7 +243,7 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.small_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)48 * a.EV;
   for (int q = 0; q <= R.na; ++q) a.roots[q] = R.r[q];
   a.k = d->topk;
-  a.r = d->rank;
+  a.r = rank_p(d);
   a.s = d->scale;
   a.cap = p.cap;
   a.maxtiles = p.maxtiles;
@@ -324,6 +352,62 @@ hipError_t scratch_address(void** ptr) {
   return hipSuccess;
 }
 
+// A rank that is not a multiple of 8 (rank_p): the six factors copied into
+// the plan's zero-padded block, the layer pointed at the copies; after the
+// backward its gradients are cut back into the caller's tensors.
+struct PadJob {
+  size_t off;     // in the factor block (elements)
+  long nb;        // [nb, rows, cols] caller view
+  int rows, cols, rows_p, cols_p;
+};
+void pad_jobs(const moe_lora_desc* d, int na, PadJob (&j)[6]) {
+  const FacBlock f(d, na);
+  const int r = d->rank, rp = rank_p(d), H = d->H, I = d->I;
+  const long nE = (long)na * d->E;
+  j[0] = PadJob{f.A1, na, r, H, rp, H};               // A1 [na, r, H]
+  j[1] = PadJob{f.A3, na, r, H, rp, H};               // A3
+  j[2] = PadJob{f.B1, nE * I, 1, r, 1, rp};           // B1 [na, E, I, r]
+  j[3] = PadJob{f.B3, nE * I, 1, r, 1, rp};           // B3
+  j[4] = PadJob{f.A2, nE, r, I, rp, I};               // A2 [na, E, r, I]
+  j[5] = PadJob{f.B2, (long)na * H, 1, r, 1, rp};     // B2 [na, H, r]
+}
+hipError_t pad_factors(LayerArgs& a, const moe_lora_desc* d, const Plan& p, int na, void* scratch,
+                       hipStream_t st) {
+  if (!padded(d)) return hipSuccess;
+  PadJob j[6];
+  pad_jobs(d, na, j);
+  uint16_t* b = (uint16_t*)((char*)scratch + p.o_fac);
+  const uint16_t** fac[6] = {&a.A1, &a.A3, &a.B1, &a.B3, &a.A2, &a.B2};
+  for (int i = 0; i < 6; ++i) {
+    const hipError_t e = launch_pad(*fac[i], b + j[i].off, j[i].nb, j[i].rows, j[i].cols, j[i].rows_p, j[i].cols_p, st);
+    if (e != hipSuccess) return e;
+    *fac[i] = b + j[i].off;
+  }
+  return hipSuccess;
+}
+// the backward's gradient outputs: the padded block while the kernels run
+void pad_grads(LayerArgs& a, const moe_lora_desc* d, const Plan& p, int na, void* scratch, uint16_t* (&user)[6]) {
+  uint16_t** g[6] = {&a.dA1, &a.dA3, &a.dB1, &a.dB3, &a.dA2, &a.dB2};
+  for (int i = 0; i < 6; ++i) user[i] = *g[i];
+  if (!padded(d)) return;
+  PadJob j[6];
+  pad_jobs(d, na, j);
+  uint16_t* b = (uint16_t*)((char*)scratch + p.o_gfac);
+  for (int i = 0; i < 6; ++i) *g[i] = b + j[i].off;
+}
+hipError_t crop_grads(const LayerArgs& a, const moe_lora_desc* d, int na, uint16_t* const (&user)[6],
+                      hipStream_t st) {
+  if (!padded(d)) return hipSuccess;
+  PadJob j[6];
+  pad_jobs(d, na, j);
+  const uint16_t* g[6] = {a.dA1, a.dA3, a.dB1, a.dB3, a.dA2, a.dB2};
+  for (int i = 0; i < 6; ++i) {
+    const hipError_t e = launch_pad(g[i], user[i], j[i].nb, j[i].rows_p, j[i].cols_p, j[i].rows, j[i].cols, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // The forward behind both entry points.  noalloc: the scratch is the static
 // array above (scratch / scratch_bytes are ignored); only the forward's part
 // of the plan is used there.
@@ -360,7 +444,8 @@ moe_status forward_checked(const moe_lora_desc* d, const moe_adapters* ad, const
   a.x = (const uint16_t*)x;
   a.w = topk_w;
   a.out = (uint16_t*)out;
-  const hipError_t e = launch_forward(a, (hipStream_t)stream);
+  hipError_t e = pad_factors(a, d, p, R.na, sc, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_forward(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -408,7 +493,11 @@ moe_status backward_checked(const moe_lora_desc* d, const moe_adapters* ad, cons
   a.dB2 = (uint16_t*)grads->dB2;
   a.dW13 = (uint16_t*)grads->dW13;
   a.dW2 = (uint16_t*)grads->dW2;
-  const hipError_t e = launch_backward(a, (hipStream_t)stream);
+  uint16_t* user[6];
+  pad_grads(a, d, p, R.na, scratch, user);
+  hipError_t e = pad_factors(a, d, p, R.na, scratch, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_backward(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = crop_grads(a, d, R.na, user, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

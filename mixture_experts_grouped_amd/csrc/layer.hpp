@@ -192,6 +192,8 @@ hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* cod
 // [B, R, C] -> [B, C, R] bf16 bits
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st);
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
+// [nb, rs, cs] -> [nb, rd, cd] bf16, zero outside the source (pack.hip)
+hipError_t launch_pad(const uint16_t* src, uint16_t* dst, long nb, int rs, int cs, int rd, int cd, hipStream_t st);
 // packed stage tiles of the base (kinds in pack.hip)
 hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const uint8_t* sc, uint16_t* dst, int E,
                        int H, int I, hipStream_t st);

@@ -1,4 +1,5 @@
-// pack.hip -- packed copies of the frozen base weights.
+// pack.hip -- packed copies of the frozen base weights, and the zero padding
+// of adapter factors whose rank is not a multiple of 8.
 //
 // Each of the four base GEMMs reads its weights as the N operand: a K tile of
 // 256 weight rows x 64 k per pipeline stage (32 KB), which the direct loads
@@ -110,6 +111,28 @@ hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const u
     else
       MOE_LAUNCH(k_pack_cols<false>, dim3((unsigned)tiles), dim3(256), 0, st, src, nullptr, nullptr, dst, N, K);
   }
+  return hipGetLastError();
+}
+
+// Rank padding: dst [nb, rd, cd] from src [nb, rs, cs] (bf16), zero where
+// the source has no element -- the adapter factors of a rank that is not a
+// multiple of 8 widened with zero rows or columns, and (rd <= rs, cd <= cs)
+// their gradients cut back to the caller's rank.
+__global__ __launch_bounds__(256) void k_pad(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, long n,
+                                             int rs, int cs, int rd, int cd) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % cd);
+  const long br = i / cd;
+  const int r = (int)(br % rd);
+  const long b = br / rd;
+  dst[i] = (r < rs && c < cs) ? src[(b * rs + r) * cs + c] : (uint16_t)0;
+}
+
+hipError_t launch_pad(const uint16_t* src, uint16_t* dst, long nb, int rs, int cs, int rd, int cd, hipStream_t st) {
+  const long n = nb * rd * cd;
+  if (n <= 0) return hipSuccess;
+  MOE_LAUNCH(k_pad, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst, n, rs, cs, rd, cd);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ def test_workspace_sizes_grow_with_the_problem():
 @pytest.mark.parametrize("field,value,status", [
     ("T", 0, B.MOE_ERR_INVALID), ("H", -4, B.MOE_ERR_INVALID), ("rank", 0, B.MOE_ERR_INVALID),
     ("block_m", 48, B.MOE_ERR_INVALID), ("H", 300, B.MOE_ERR_UNSUPPORTED),
-    ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 12, B.MOE_ERR_UNSUPPORTED),
+    ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 129, B.MOE_ERR_UNSUPPORTED),
     ("rank", 256, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
     ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 2, B.MOE_ERR_UNSUPPORTED),
     ("clamp", float("nan"), B.MOE_ERR_INVALID), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
@@ -329,3 +329,19 @@ def test_multi_adapter_calls_reject_before_any_launch():
                                        fake, byref(g), sc, scratch, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.build_pool_multi(byref(d), byref(ad), fake, fake, fake, fake, fake, cap - 1, None,
                                 None) == B.MOE_ERR_INVALID
+
+
+@pytest.mark.parametrize("rank", [1, 5, 12, 100, 127])
+def test_any_rank_up_to_128_is_accepted(rank):
+    """A rank that is not a multiple of 8 runs on zero-padded copies of the
+    factors: the workspaces grow by the padded copies and their gradients."""
+    d = B.make_desc(256, 512, 256, 16, 2, rank)
+    rp = (rank + 7) // 8 * 8
+    sv, sc = B.moe_lora_workspace_size(d)
+    sv_p, sc_p = B.moe_lora_workspace_size(B.make_desc(256, 512, 256, 16, 2, rp))
+    assert sv == sv_p                       # saved: the padded rank's activations
+    fac = 2 * (2 * rp * 512 + 2 * 16 * 256 * rp + 16 * rp * 256 + 512 * rp)
+    if rank % 8:
+        assert sc >= sc_p + 2 * fac          # the factor copies and their gradients
+    else:
+        assert sc == sc_p

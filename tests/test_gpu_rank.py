@@ -1,0 +1,82 @@
+"""Adapter ranks that are not a multiple of 8 (1 .. 128; the ART PR #1139
+page qualifies ranks 1, 8 and 32), through the C ABI:
+
+- every output against the oracle at ranks 1, 4, 12 and 100;
+- bitwise equal to the same call at the next multiple of 8 with the factors
+  zero-padded by hand and the gradients cut back (the padding adds exact
+  zeros and nothing else);
+- rank 1 with four adapters in one pass, against the multi-adapter oracle.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_grouped_amd import inputs as I
+from oracle import multi_adapter as MA
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+RANKS = (1, 4, 12, 100)
+FACTORS = ("A1", "A3", "B1", "B3", "A2", "B2")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    Hn.ensure_built()
+
+
+def _pad(case, r, rp):
+    """The factors widened to rank rp with zeros (A1/A3/A2 rows, B1/B3/B2 columns)."""
+    out = dict(case)
+    for n in ("A1", "A3"):
+        out[n] = np.zeros((rp, case[n].shape[1]), np.uint16)
+        out[n][:r] = case[n]
+    out["A2"] = np.zeros((case["A2"].shape[0], rp, case["A2"].shape[2]), np.uint16)
+    out["A2"][:, :r] = case["A2"]
+    for n in ("B1", "B3"):
+        out[n] = np.zeros((*case[n].shape[:2], rp), np.uint16)
+        out[n][..., :r] = case[n]
+    out["B2"] = np.zeros((case["B2"].shape[0], rp), np.uint16)
+    out["B2"][:, :r] = case["B2"]
+    return out
+
+
+def _crop(g, n, r):
+    if n in ("dA1", "dA3"):
+        return g[:r]
+    if n == "dA2":
+        return g[:, :r]
+    return g[..., :r]
+
+
+@pytest.mark.parametrize("rank", RANKS)
+def test_rank_against_oracle_and_padded_call(rank):
+    shape = I.Shape(T=300, H=512, I=256, E=8, topk=2, rank=rank, scale=1.0)
+    case = I.layer_inputs(shape, (70, rank), mask_prob=0.1)
+    Hn.log(f"[rank] r={rank}")
+    res = Hn.GpuRun(shape, case).run(fill=(0xFF,))
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale)
+    Hn.compare_all(res, ref_out, ref_g, tag=f"r{rank}:")
+    rp = (rank + 7) // 8 * 8
+    if rp != rank:
+        shp = I.Shape(T=300, H=512, I=256, E=8, topk=2, rank=rp, scale=1.0)
+        wide = Hn.GpuRun(shp, _pad(case, rank, rp)).run()
+        for n in ("out", "grad_x", "grad_w"):
+            assert Hn.same_bits(res[n], wide[n]), n
+        for n in Hn.GRAD_NAMES:
+            assert Hn.same_bits(res[n], np.ascontiguousarray(_crop(wide[n], n, rank))), n
+
+
+def test_rank_one_with_four_adapters():
+    shape = I.Shape(T=400, H=512, I=256, E=8, topk=2, rank=1, scale=1.0)
+    roots = (0, 100, 200, 300, 400)
+    case = I.layer_inputs(shape, (71,), mask_prob=0.1)
+    fac = [I.adapter_factors(shape, (71,), a) for a in range(4)]
+    for n in FACTORS:
+        case[n] = np.stack([f[n] for f in fac])
+    res = Hn.GpuRun(shape, case, roots=roots).run()
+    p = {n: Hn.f64(case[n]) for n in ("W13", "W2") + FACTORS}
+    x, go, w = Hn.f64(case["x"]), Hn.f64(case["grad_out"]), case["topk_w"].astype(np.float64)
+    ref_out = MA.forward(x, case["topk_idx"], w, p, shape.scale, roots)
+    ref_g = MA.backward(go, x, case["topk_idx"], w, p, shape.scale, roots)
+    Hn.compare_all(res, ref_out, ref_g, tag="r1x4:")
