@@ -180,6 +180,21 @@ static_assert(GW2DK::TM == GW2D::TM && GW2DK::TN == GW2D::TN && GW2DK::STAGE == 
 using GW2DS = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;
 constexpr int W2DS_LDS = cmax(GW2DS::LDS_BYTES, 2 * v2::TileImage<GW2DS, GW2DS::TN / 2, uint16_t>::BYTES +
                                                     GW2DS::WN * GW2DS::TM * 4);
+// The small parts' rank-space extension reads A2 itself (a T tile over its
+// rows, as the transposing form does), so no A2^T copy is made for them.
+using GW2DST = v2::Geo2<1, 2, 2, 4, false, true, 64, 3>;
+static_assert(GW2DST::STAGE == GW2DS::STAGE && GW2DST::NBUF == GW2DS::NBUF, "one LDS plan for both loops");
+struct LdW2dExtS {
+  using KL = v2::KLoad<GW2DST::TM, GW2DST::KT, GW2DST::NW>;
+  using TL = v2::TLoad<256, v2::TStrided, GW2DST::KT, GW2DST::NW>;
+  static constexpr int INSTS = KL::NJ + TL::NJ;
+  KL me;
+  TL ne;
+  __device__ void issue(int s, char* sM, char* sN) {
+    me.issue(s * GW2DST::KT, 0, false, sM);
+    ne.issue(s * GW2DST::KT, sN);
+  }
+};
 template <class G>
 struct LdW2dK {
   using KL = v2::KLoad<G::TM, G::KT, G::NW>;   // s q by token (M)
@@ -235,7 +250,29 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   zero_acc<G>(acc);
   const int next = (2 * r + G::KT - 1) / G::KT;
   const long e = grp_expert(a, ti.e), le = grp_local(a, ti.e);  // base expert; A2 of its adapter
-  if constexpr (TW) {
+  if constexpr (SK) {
+    // the extension through A2 (T tile), then the base through W2T (packed K tile)
+    {
+      LdW2dExtS X;
+      int tk[LdW2dExtS::KL::NJ];
+      LdW2dExtS::KL::tokens(tk, a.row2r, a.k, row0, nrows);
+      X.me.from_tokens(a.sq, a.T, 2 * r, tk);
+      X.me.window(2 * r);
+      X.ne.kp = v2::TStrided{make_rsrc(a.A2 + le * r * a.I, (uint64_t)r * a.I * 2), (uint32_t)(2 * a.I), 0, 2 * r, r};
+      X.ne.cols(i0, G::TN);
+      v2::run_stages2<GW2DST, 0>(X, next, acc, smem);
+    }
+    using LT = LdW2dK<G>;
+    LT L;
+    L.next = 0;
+    {
+      int tk[LT::KA::NJ];
+      LT::KL::tokens(tk, a.row2r, a.k, row0, nrows);
+      L.mm.from_tokens(a.go, a.T, a.H, tk);
+    }
+    L.nm.set(a.W2T + e * a.I * a.H, (uint64_t)a.I * a.H * 2, nt, a.H / G::KT);
+    v2::run_stages2<G, 0>(L, a.H / G::KT, acc, smem);
+  } else if constexpr (TW) {
     using LT = LdW2dK<G>;
     LT L;
     L.next = next;
@@ -1063,7 +1100,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
     const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base
-    if (tw) {
+    if (tw && !a.small_tiles) {  // the small parts read A2 directly
       // A2T = A2_e^T per expert and adapter ([na, E, I, r]), the K-tile rank operand
       const hipError_t e = launch_transpose(a.A2, a.A2T, a.na * a.E, a.r, a.I, st);
       if (e != hipSuccess) return e;
