@@ -352,6 +352,59 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   }
 }
 
+// Few rows per expert: 64-row parts on the direct-load engine with four
+// stage buffers (three stages queued), so the long K = I contraction is not
+// bound by one load latency per stage.  Each element sums the same products
+// in the same order as k_a2.
+using GA2S = v2::Geo2<1, 2, 2, 2, false, false, 64, 4>;  // 64 x 128, four waves
+struct LdA2S {
+  using KM = v2::KLoad<GA2S::TM, GA2S::KT, GA2S::NW>;  // h rows
+  using KN = v2::KLoad<128, GA2S::KT, GA2S::NW>;       // A2_e rows
+  static constexpr int INSTS = KM::NJ + KN::NJ;
+  KM m;
+  KN n;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GA2S::KT, 0, false, sM);
+    n.issue(s * GA2S::KT, 0, false, sN);
+  }
+};
+
+__global__ __launch_bounds__(GA2S::NT) void k_a2s(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  using G = GA2S;
+  constexpr int SUB = TMG / G::TM;
+  const int mt = blockIdx.x / SUB;
+  if (mt >= *a.ntiles) return;
+  const TileInfo ti = a.tiles[mt];
+  const long row0 = ti.row0 + (long)(blockIdx.x % SUB) * G::TM;  // this part's rows
+  if (row0 >= ti.row_end) return;
+  LdA2S L;
+  L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
+  L.m.window(a.I);
+  L.n.contig(a.A2 + grp_local(a, ti.e) * a.r * a.I, 0, a.r, a.I);
+  L.n.window(a.I);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  Epi<G> ep;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const long row = row0 + ep.row(mb);
+    if (row >= ti.row_end) continue;
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ep.col(nb, g);
+        if (c >= a.r) continue;
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = a.s * acc[nb][mb][4 * g + q];
+        *(f32x4*)(a.Z2 + row * a.r + c) = v;
+      }
+  }
+}
+
 using GW2 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight waves
 // few rows per expert: 64-row parts of each pool tile, a third stage buffer
 using GW2S = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;
@@ -566,6 +619,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_w13_lds<false, true, true>(ai);
     set_w13_lds<true, false, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
+    ai.lds((const void*)k_a2s, GA2S::LDS_BYTES);
     ai.lds((const void*)k_w2<false, false, false>, W2_LDS);
     ai.lds((const void*)k_w2<false, true, false>, W2_LDS);
     ai.lds((const void*)k_w2<false, false, true>, W2S_LDS);
@@ -595,7 +649,10 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     else
       pk ? launch_w13_sk<false, 0, true>(a, st) : launch_w13_sk<false, 0, false>(a, st);
   }
-  MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
+  if (a.small_tiles)
+    MOE_LAUNCH(k_a2s, dim3(a.maxtiles * (TMG / GA2S::TM)), dim3(GA2S::NT), GA2S::LDS_BYTES, st, a);
+  else
+    MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
   {
     const dim3 g(a.maxtiles * (a.H / GW2::TN)), gs(g.x * (TMG / GW2S::TM));
     if (a.mx)
