@@ -132,10 +132,55 @@ def copy_scale(d: str, counter: str) -> float:
     return COPY_BYTES / (kib * 1024.0)
 
 
+def _last_json(path: str):
+    with open(path) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def sweep_table(sweep_json: str, adapters_json: str, out: str, commands: str) -> None:
+    """profiles/token_sweep_fb.md (bench.py --sweep: F+B time, weight-read rate
+    and the per-kernel event times of each point) and
+    profiles/multi_adapter_fb.md (bench.py --adapters)."""
+    big = ("k_w13", "k_w2", "k_w13dgrad", "k_w2dgrad")
+    hdr = ["Commands (run from the repository root on one MI355X):", "", "```", commands.strip(), "```", "",
+           f"Build hash: `{build.source_hash()}` (device sources, ABI header, compile flags).", ""]
+    if sweep_json:
+        d = _last_json(sweep_json)
+        t = [f"# Token sweep, forward + backward: {d['config']['workload']}", ""] + hdr
+        t += ["F+B: median of three rounds of ten steps (wall clock around the rounds). Weight reads: the "
+              "active experts' W13 + W2 (50.3 MB bf16 each) once in the forward and once in the backward, "
+              "over the F+B time, against 8 TB/s. Kernel times: the library's HIP-event trace, a pass of "
+              "its own (10 steps).", "",
+              "| T | routes | experts | F+B ms | weight GB/s | of 8 TB/s | floor ms | four base GEMMs us | "
+              "other kernels us | largest other kernels (us) |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for r in d["sweep"]:
+            k = r.get("kernels_us", {})
+            b4 = sum(k.get(n, 0.0) for n in big)
+            rest = {n: v for n, v in k.items() if n not in big}
+            top = ", ".join(f"{n} {v:.0f}" for n, v in sorted(rest.items(), key=lambda kv: -kv[1])[:4])
+            t.append(f"| {r['T']} | {r['routes']} | {r['active_experts']} | {r['ms']:.3f} | {r['weight_GBps']:.0f} | "
+                     f"{100 * r['frac_of_8TBps']:.1f} % | {r['floor_ms']:.3f} | {b4:.0f} | {sum(rest.values()):.0f} | {top} |")
+        with open(os.path.join(out, "token_sweep_fb.md"), "w") as f:
+            f.write("\n".join(t) + "\n")
+    if adapters_json:
+        d = _last_json(adapters_json)
+        t = [f"# Multi-adapter pass against the adapters one after another: {d['config']['workload']}", ""] + hdr
+        t += ["Fused: build_pool_multi + forward + backward over all roots; serial: one single-adapter step "
+              "per root on its 1024 tokens. Medians of three rounds of ten steps.", "",
+              "| rank | adapters | tokens | fused ms | serial ms | serial / fused |", "|---|---|---|---|---|---|"]
+        for r in d["rows"]:
+            t.append(f"| {r['rank']} | {r['adapters']} | {r['tokens']} | {r['fused_ms']:.3f} | {r['serial_ms']:.3f} | "
+                     f"{r['speedup']:.3f} |")
+        with open(os.path.join(out, "multi_adapter_fb.md"), "w") as f:
+            f.write("\n".join(t) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--name", required=True)
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--sweep", help="bench.py --sweep output (writes token_sweep_fb.md; --stats not needed)")
+    ap.add_argument("--adapters", help="bench.py --adapters output (writes multi_adapter_fb.md)")
+    ap.add_argument("--name")
+    ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--copy-fetch")
@@ -149,6 +194,11 @@ def main() -> None:
     ap.add_argument("--workload", default="")
     ap.add_argument("--commands", default="", help="text block of the exact commands run")
     args = ap.parse_args()
+    if args.sweep or args.adapters:
+        sweep_table(args.sweep, args.adapters, args.out, args.commands)
+        return
+    if not (args.name and args.stats):
+        ap.error("--name and --stats are required for a kernel-trace summary")
 
     stats = read_stats(args.stats)
     bench = json.load(open(args.bench)) if args.bench else None
