@@ -84,7 +84,7 @@ typedef int32_t moe_status;
      NaN: MOE_ERR_INVALID.  The clip decision is taken on the fp16-rounded
      pre-activation the forward saves, so forward and backward agree.
  * Supported: T >= 1, H % 256 == 0, I % 256 == 0, 1 <= E <= 512,
- *   1 <= topk <= 16, 1 <= rank <= 128 (a rank that is not a multiple of 8
+ *   1 <= topk <= 16, 1 <= rank <= 256 (a rank that is not a multiple of 8
  *   runs on copies of the factors widened with zero rows or columns to the
  *   next multiple, kept in the scratch workspace; the extra terms are exact
  *   zeros and the gradients are cut back to the caller's rank), T*H*2 and 4*I*H

@@ -35,7 +35,7 @@ moe_status check_desc(const moe_lora_desc* d) {
     if (!ok) return MOE_ERR_INVALID;
   }
   if (d->H % 256 != 0 || d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
-  if (d->E > 512 || d->topk > 16 || d->rank > 128) return MOE_ERR_UNSUPPORTED;
+  if (d->E > 512 || d->topk > 16 || d->rank > 256) return MOE_ERR_UNSUPPORTED;
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
   if (std::isnan(d->clamp)) return MOE_ERR_INVALID;
   if (d->base_format != MOE_BASE_BF16 && d->base_format != MOE_BASE_MXFP4) return MOE_ERR_UNSUPPORTED;

@@ -53,13 +53,13 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   int t0, nt, ad;
   if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
-  const int r = a.r, ks = blockIdx.y, kh = a.H / KSPLIT;
+  const int r = a.r, ks = blockIdx.y, kh = a.H / KSPLIT, c0 = RBLK * blockIdx.z;  // rank block c0..
   LdQ L;
   L.k0 = ks * kh;
   L.m.contig(a.go, t0, nt, a.H);
   L.m.window(a.H);
   L.n.kp = KStrided{make_rsrc(a.B2 + (long)ad * a.H * r, (uint64_t)a.H * r * 2), (uint32_t)(2 * r), 0, a.H, 0};
-  L.n.cols(0, r);
+  L.n.cols(c0, r - c0);
   f32x16 acc[GS64::NB][GS64::MB];
   mainloop<GS64>(L, kh / KT, acc, smem);
   Epi<GS64> ep;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_q(LayerArgs a) {
     for (int nb = 0; nb < GS64::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
+        const int c = c0 + ep.col(nb, g);
         if (c >= r) continue;
         *(f32x4*)(part + (long)t * r + c) =
             f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
@@ -620,7 +620,7 @@ struct LdP {
 
 __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int mt = blockIdx.x / P13_SUB, which = blockIdx.y;
+  const int mt = blockIdx.x / P13_SUB, which = blockIdx.y & 1, c0 = RBLK * (blockIdx.y >> 1);  // rank block c0..
   if (mt >= *a.ntiles) return;
   const TileInfo ti = a.tiles[mt];
   const long row0 = ti.row0 + (long)(blockIdx.x % P13_SUB) * GS128::TM;  // this sub-tile's rows
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   L.m.window(a.I);
   const uint16_t* Be = (which ? a.B3 : a.B1) + grp_local(a, ti.e) * a.I * r;
   L.n.kp = KStrided{make_rsrc(Be, (uint64_t)a.I * r * 2), (uint32_t)(2 * r), 0, a.I, 0};
-  L.n.cols(0, r);
+  L.n.cols(c0, r - c0);
   f32x16 acc[GS128::NB][GS128::MB];
   mainloop<GS128>(L, a.I / KT, acc, smem);
   Epi<GS128> ep;
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
     for (int nb = 0; nb < GS128::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
+        const int c = c0 + ep.col(nb, g);
         if (c >= r) continue;
         f32x4 v;
 #pragma unroll
@@ -738,8 +738,10 @@ __global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
 //   which 2: dA2_e[c][i] = sum_rows (s w q)[c] * h[row][i]
 // K tiles start at the expert's first row and rows past its count read zero,
 // so the sum never touches another expert and does not depend on BLOCK_M.
-// The rank-r operand is hi/lo split along N (columns c and c + 128); the two
-// halves are added in the epilogue.  An expert with no rows writes zeros.
+// Each workgroup takes one block of RBLK rank columns c0 .. (blockIdx.y / 3);
+// that block's rank operand is hi/lo split along N (tile columns c and
+// c + 128), the two halves added in the epilogue.  An expert with no rows
+// writes zeros.
 // ----------------------------------------------------------------------------
 // ZA rows in pool order, so the weight-gradient kernel reads its rank
 // operand as contiguous rows of each expert.  One wave per pool row.
@@ -792,7 +794,8 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   // an expert's column tiles share its rank operand rows: keep them on one
   // XCD (each XCD walks a contiguous range of tiles), so its L2 serves them
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int e = b / nti, i0 = (b % nti) * 256, which = blockIdx.y;  // e: pool group
+  const int e = b / nti, i0 = (b % nti) * 256, which = blockIdx.y % 3;  // e: pool group
+  const int c0 = RBLK * (blockIdx.y / 3), rc = min(RBLK, a.r - c0);    // rank block c0 .. c0 + rc - 1
   const long le = grp_local(a, e);  // output slot of the group's expert-local factors
   const int r = a.r;
   const int ne = a.counts[e], off = a.offsets[e];
@@ -800,11 +803,11 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   if (which < 2) {
     L.set(a.dGV + (long)off * 2 * a.I, (uint32_t)(4 * a.I), a.ZAp + (long)off * 4 * r, (uint32_t)(8 * r), ne);
     L.m.cols(which * a.I + i0, 256);
-    L.n.cols(which * 2 * r, r, 128, r);
+    L.n.cols(which * 2 * r + c0, rc, 128, r);
   } else {
     L.set(a.Hh + (long)off * a.I, (uint32_t)(2 * a.I), a.wsq + (long)off * 2 * r, (uint32_t)(4 * r), ne);
     L.m.cols(i0, 256);
-    L.n.cols(0, r, 128, r);
+    L.n.cols(c0, rc, 128, r);
   }
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
@@ -812,7 +815,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
   // hi + lo halves of the rank operand (tile columns c and c + 128) add up
   Epi<G> ep;
   static_assert(G::NB == 2, "one hi and one lo block per wave");
-  const int cpr = r / 8;  // 16-byte chunks per output row of r bf16
+  const int cpr = rc / 8;  // 16-byte chunks of the block's columns in an output row (r % 8 == 0)
   if (which < 2) {
     // dB[e][i][c]: image rows i, columns c (pitch 128 + 8 bf16)
     constexpr int P = 128 * 2 + 16;
@@ -827,7 +830,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
         *(u32x2*)(smem + ep.row(mb) * P + c * 2) = v;
       }
     __syncthreads();
-    uint16_t* d = (which ? a.dB3 : a.dB1) + (le * a.I + i0) * r;
+    uint16_t* d = (which ? a.dB3 : a.dB1) + (le * a.I + i0) * r + c0;
     for (int idx = threadIdx.x; idx < 256 * cpr; idx += G::NT) {
       const int row = idx / cpr, ch = idx - row * cpr;
       *(u32x4*)(d + (long)row * r + 8 * ch) = *(const u32x4*)(smem + row * P + 16 * ch);
@@ -845,8 +848,8 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_local(LayerArgs a) {
           *(uint16_t*)(smem + (c + q) * P + i * 2) = (uint16_t)f2bf(acc[0][mb][4 * g + q] + acc[1][mb][4 * g + q]);
       }
     __syncthreads();
-    uint16_t* d = a.dA2 + le * r * a.I + i0;
-    for (int idx = threadIdx.x; idx < r * 32; idx += G::NT) {
+    uint16_t* d = a.dA2 + (le * r + c0) * a.I + i0;
+    for (int idx = threadIdx.x; idx < rc * 32; idx += G::NT) {
       const int c = idx / 32, ch = idx - c * 32;
       *(u32x4*)(d + (long)c * a.I + 8 * ch) = *(const u32x4*)(smem + c * P + 16 * ch);
     }
@@ -867,18 +870,18 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GWG;
   const int ntm = a.H / 256;
-  const int h0 = (blockIdx.x % ntm) * 256, sp = blockIdx.x / ntm, which = blockIdx.y;
-  const int r = a.r;
+  const int h0 = (blockIdx.x % ntm) * 256, sp = blockIdx.x / ntm, which = blockIdx.y % 3;
+  const int r = a.r, c0 = RBLK * (blockIdx.y / 3), rc = min(RBLK, r - c0);  // rank block c0 ..
   int tb, nt, ad;
   if (!token_tile(a, sp, a.kspl, tb, nt, ad)) return;
   LdWg2 L;
   const uint16_t* mrow0 = (which < 2 ? a.Xs : a.go) + (long)tb * a.H;  // x_t from the forward's saved copy
   if (which < 2) {
     L.set(mrow0, (uint32_t)(2 * a.H), a.pc + (long)tb * 4 * r, (uint32_t)(8 * r), nt);
-    L.n.cols(which * 2 * r, r, 128, r);
+    L.n.cols(which * 2 * r + c0, rc, 128, r);
   } else {
     L.set(mrow0, (uint32_t)(2 * a.H), a.zc + (long)tb * 2 * r, (uint32_t)(4 * r), nt);
-    L.n.cols(0, r, 128, r);
+    L.n.cols(c0, rc, 128, r);
   }
   L.m.cols(h0, 256);
   f32x16 acc[G::NB][G::MB];
@@ -893,7 +896,7 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_shared(LayerArgs a) {
     const int h = h0 + ep.row(mb);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int c = ep.col(0, g);
+      const int c = c0 + ep.col(0, g);
       if (c >= r) continue;
       f32x4 v;
 #pragma unroll
@@ -1095,7 +1098,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     return ai.err;
   });
   if (ierr != hipSuccess) return ierr;
-  MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM), KSPLIT), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM), KSPLIT, rank_blocks(a.r)), dim3(256), GS64::LDS_BYTES, st, a);
   MOE_LAUNCH(k_q_sum, dim3((unsigned)(((long)a.T * (a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
   {
     const dim3 grid(a.maxtiles * (a.I / GW2D::TN));
@@ -1126,7 +1129,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     else
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }
-  MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2), dim3(256), GS128::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2 * rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
   const long npc = (long)a.T * (2 * a.r / 4);
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   {
@@ -1137,8 +1140,9 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_rank_dx, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3), dim3(GWG::NT), WG_LDS, st, a);
-  MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3), dim3(GWG::NT), GWG::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3 * rank_blocks(a.r)), dim3(GWG::NT), WG_LDS, st, a);
+  MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3 * rank_blocks(a.r)), dim3(GWG::NT), GWG::LDS_BYTES,
+             st, a);
   const long nsh = (long)a.H * a.r;
   MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3, a.na), dim3(256), 0, st, a);
   if (a.dW13 != nullptr || a.dW2 != nullptr) {  // one adapter only (pool groups = experts)

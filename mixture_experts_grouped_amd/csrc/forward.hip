@@ -49,7 +49,7 @@ struct LdPlain {
 // not depend on the batch.
 __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int fac = blockIdx.y;  // fac 0: A1, 1: A3
+  const int fac = blockIdx.y & 1, c0 = RBLK * (blockIdx.y >> 1);  // fac 0: A1, 1: A3; rank block c0..
   int t0, nt, ad;
   if (!token_tile(a, blockIdx.x, GS64::TM, t0, nt, ad)) return;
   const int r = a.r, ks = blockIdx.z, kh = a.H / KSPLIT;
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
   L.k0 = ks * kh;
   L.m.contig(a.x, t0, nt, a.H);
   L.m.window(a.H);
-  L.n.contig((fac ? a.A3 : a.A1) + (long)ad * r * a.H, 0, r, a.H);
+  L.n.contig((fac ? a.A3 : a.A1) + ((long)ad * r + c0) * a.H, 0, r - c0, a.H);
   L.n.window(a.H);
   f32x16 acc[GS64::NB][GS64::MB];
   mainloop<GS64>(L, kh / KT, acc, smem);
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_shrink(LayerArgs a) {
       if (t >= t0 + nt) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
+        const int c = c0 + ep.col(nb, g);
         if (c >= r) continue;
         *(f32x4*)(part + (long)t * 2 * r + fac * r + c) =
             f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
@@ -325,11 +325,12 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const long row0 = ti.row0 + (long)(blockIdx.x % A2_SUB) * GS128::TM;  // this sub-tile's rows
   if (row0 >= ti.row_end) return;
-  const uint16_t* A2e = a.A2 + grp_local(a, ti.e) * a.r * a.I;
+  const int c0 = RBLK * blockIdx.y;  // rank block
+  const uint16_t* A2e = a.A2 + (grp_local(a, ti.e) * a.r + c0) * a.I;
   LdPlain<GS128::TM> L;
   L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
   L.m.window(a.I);
-  L.n.contig(A2e, 0, a.r, a.I);
+  L.n.contig(A2e, 0, a.r - c0, a.I);
   L.n.window(a.I);
   f32x16 acc[GS128::NB][GS128::MB];
   mainloop<GS128>(L, a.I / KT, acc, smem);
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
     for (int nb = 0; nb < GS128::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
+        const int c = c0 + ep.col(nb, g);
         if (c >= a.r) continue;
         f32x4 v;
 #pragma unroll
@@ -378,10 +379,11 @@ __global__ __launch_bounds__(GA2S::NT) void k_a2s(LayerArgs a) {
   const TileInfo ti = a.tiles[mt];
   const long row0 = ti.row0 + (long)(blockIdx.x % SUB) * G::TM;  // this part's rows
   if (row0 >= ti.row_end) return;
+  const int c0 = RBLK * blockIdx.y;  // rank block
   LdA2S L;
   L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
   L.m.window(a.I);
-  L.n.contig(a.A2 + grp_local(a, ti.e) * a.r * a.I, 0, a.r, a.I);
+  L.n.contig(a.A2 + (grp_local(a, ti.e) * a.r + c0) * a.I, 0, a.r - c0, a.I);
   L.n.window(a.I);
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(GA2S::NT) void k_a2s(LayerArgs a) {
     for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = ep.col(nb, g);
+        const int c = c0 + ep.col(nb, g);
         if (c >= a.r) continue;
         f32x4 v;
 #pragma unroll
@@ -631,7 +633,8 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   if (err != hipSuccess) return err;
   err = launch_pool_prologue(a, st);
   if (err != hipSuccess) return err;
-  MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2, KSPLIT), dim3(256), GS64::LDS_BYTES, st, a);
+  MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2 * rank_blocks(a.r), KSPLIT), dim3(256), GS64::LDS_BYTES,
+             st, a);
   MOE_LAUNCH(k_shrink_sum, dim3((unsigned)(((long)a.T * (2 * a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
   if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
@@ -650,9 +653,10 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
       pk ? launch_w13_sk<false, 0, true>(a, st) : launch_w13_sk<false, 0, false>(a, st);
   }
   if (a.small_tiles)
-    MOE_LAUNCH(k_a2s, dim3(a.maxtiles * (TMG / GA2S::TM)), dim3(GA2S::NT), GA2S::LDS_BYTES, st, a);
+    MOE_LAUNCH(k_a2s, dim3(a.maxtiles * (TMG / GA2S::TM), rank_blocks(a.r)), dim3(GA2S::NT), GA2S::LDS_BYTES, st,
+               a);
   else
-    MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB), dim3(256), GS128::LDS_BYTES, st, a);
+    MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB, rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
   {
     const dim3 g(a.maxtiles * (a.H / GW2::TN)), gs(g.x * (TMG / GW2S::TM));
     if (a.mx)

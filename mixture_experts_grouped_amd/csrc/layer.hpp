@@ -14,6 +14,10 @@ constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
 constexpr int TILE_GM = 4;  // M tiles per group in the XCD-aware tile order
 constexpr int MAX_ADAPTERS = 64;  // adapters of one multi-adapter pass
 constexpr int KSPLIT = 4;  // fixed K split of the long-K token GEMMs (ZA = A x, q = B2^T go)
+// Kernels whose output tile spans the rank (ZA, Z2, q, P and the adapter
+// gradients) cover it in blocks of RBLK columns, one block per workgroup.
+constexpr int RBLK = 128;
+__host__ __device__ inline int rank_blocks(int r) { return (r + RBLK - 1) / RBLK; }
 
 // Accumulator-blocked layout of a [tiles x 256, I] tensor (fp16 here) that is
 // written and read only by kernels holding it in 32 x 32 MFMA accumulator

@@ -62,8 +62,8 @@ def test_workspace_sizes_grow_with_the_problem():
 @pytest.mark.parametrize("field,value,status", [
     ("T", 0, B.MOE_ERR_INVALID), ("H", -4, B.MOE_ERR_INVALID), ("rank", 0, B.MOE_ERR_INVALID),
     ("block_m", 48, B.MOE_ERR_INVALID), ("H", 300, B.MOE_ERR_UNSUPPORTED),
-    ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 129, B.MOE_ERR_UNSUPPORTED),
-    ("rank", 256, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
+    ("I", 320, B.MOE_ERR_UNSUPPORTED), ("rank", 257, B.MOE_ERR_UNSUPPORTED),
+    ("rank", 1000, B.MOE_ERR_UNSUPPORTED), ("E", 1024, B.MOE_ERR_UNSUPPORTED),
     ("topk", 17, B.MOE_ERR_UNSUPPORTED), ("activation", 2, B.MOE_ERR_UNSUPPORTED),
     ("clamp", float("nan"), B.MOE_ERR_INVALID), ("base_format", 7, B.MOE_ERR_UNSUPPORTED),
     ("scale", float("nan"), B.MOE_ERR_INVALID),
@@ -331,8 +331,8 @@ def test_multi_adapter_calls_reject_before_any_launch():
                                 None) == B.MOE_ERR_INVALID
 
 
-@pytest.mark.parametrize("rank", [1, 5, 12, 100, 127])
-def test_any_rank_up_to_128_is_accepted(rank):
+@pytest.mark.parametrize("rank", [1, 5, 12, 100, 127, 129, 200, 255, 256])
+def test_any_rank_up_to_256_is_accepted(rank):
     """A rank that is not a multiple of 8 runs on zero-padded copies of the
     factors: the workspaces grow by the padded copies and their gradients."""
     d = B.make_desc(256, 512, 256, 16, 2, rank)

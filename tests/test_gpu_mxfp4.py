@@ -15,7 +15,7 @@ weights to bf16 (exact).  Pins, in order of strength:
   gates, each expert's local gradients on their own;
 - every output against the full-precision oracle on the dequantised weights
   at the MXFP4 gate, relative L2 <= 2e-2 (cosine >= 0.9998).
-Cases span several tiles, a ragged tail, masked routes, rank 8 and 128, an
+Cases span several tiles, a ragged tail, masked routes, rank 8, 128 and 256, an
 all-zero weight block (scale byte 0), all fifteen token-sweep points and the
 production share.  Unused experts hold NaN weights and NaN scale bytes.
 """
@@ -42,6 +42,8 @@ CASES = {
     "tiny": (I.Shape(T=256, H=512, I=256, E=16, topk=2, rank=8), (21,), "softmax_topk", 0.0),
     # rank 128, masked routes, several M tiles with ragged tails
     "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (22,), "softmax_topk", 0.2),
+    # rank 256: a 512-k extension and two rank blocks
+    "r256_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=256), (24,), "softmax_topk", 0.2),
 }
 
 

@@ -1,11 +1,14 @@
-"""Adapter ranks that are not a multiple of 8 (1 .. 128; the ART PR #1139
-page qualifies ranks 1, 8 and 32), through the C ABI:
+"""Adapter ranks from 1 to 256 (the ART PR #1139 page qualifies ranks 1, 8
+and 32; the layer's boundary takes any rank up to 256), through the C ABI:
 
-- every output against the oracle at ranks 1, 4, 12 and 100;
+- every output against the oracle at ranks 1, 4, 12 and 100, and at 129,
+  200 and 256, whose rank spans two column blocks of the rank-tiled kernels
+  (the second one ragged at 129 and 200);
 - bitwise equal to the same call at the next multiple of 8 with the factors
   zero-padded by hand and the gradients cut back (the padding adds exact
   zeros and nothing else);
-- rank 1 with four adapters in one pass, against the multi-adapter oracle.
+- ranks 1 and 200 with four adapters in one pass, against the multi-adapter
+  oracle.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from tests import harness as Hn
 
 pytestmark = pytest.mark.gpu
 
-RANKS = (1, 4, 12, 100)
+RANKS = (1, 4, 12, 100, 129, 200, 256)
 FACTORS = ("A1", "A3", "B1", "B3", "A2", "B2")
 
 
@@ -67,8 +70,9 @@ def test_rank_against_oracle_and_padded_call(rank):
             assert Hn.same_bits(res[n], np.ascontiguousarray(_crop(wide[n], n, rank))), n
 
 
-def test_rank_one_with_four_adapters():
-    shape = I.Shape(T=400, H=512, I=256, E=8, topk=2, rank=1, scale=1.0)
+@pytest.mark.parametrize("rank", [1, 200])
+def test_rank_with_four_adapters(rank):
+    shape = I.Shape(T=400, H=512, I=256, E=8, topk=2, rank=rank, scale=1.0)
     roots = (0, 100, 200, 300, 400)
     case = I.layer_inputs(shape, (71,), mask_prob=0.1)
     fac = [I.adapter_factors(shape, (71,), a) for a in range(4)]
@@ -79,4 +83,19 @@ def test_rank_one_with_four_adapters():
     x, go, w = Hn.f64(case["x"]), Hn.f64(case["grad_out"]), case["topk_w"].astype(np.float64)
     ref_out = MA.forward(x, case["topk_idx"], w, p, shape.scale, roots)
     ref_g = MA.backward(go, x, case["topk_idx"], w, p, shape.scale, roots)
-    Hn.compare_all(res, ref_out, ref_g, tag="r1x4:")
+    Hn.compare_all(res, ref_out, ref_g, tag=f"r{rank}x4:")
+
+
+@pytest.mark.parametrize("transformed", [False, True])
+@pytest.mark.parametrize("rank", [136, 256])
+def test_rank_above_128_with_few_rows_per_expert(rank, transformed):
+    """Few rows per expert (the 64-row parts of the base GEMMs, the A2
+    shrink's direct-load engine, the W2 data gradient reading A2 through a
+    transposing tile), with and without the packed base copies, at a rank of
+    two column blocks: every output against the oracle."""
+    shape = I.Shape(T=40, H=512, I=256, E=8, topk=2, rank=rank, scale=1.0)
+    case = I.layer_inputs(shape, (72, rank), mask_prob=0.1)
+    Hn.log(f"[rank] small T, r={rank}, transformed={transformed}")
+    res = Hn.GpuRun(shape, case, transformed=transformed).run()
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale)
+    Hn.compare_all(res, ref_out, ref_g, tag=f"r{rank}:T40:")
