@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
 // ----------------------------------------------------------------------------
 // a12: grad_x = [A1; A3]^T pc + sum_j dU
 // ----------------------------------------------------------------------------
-// P = [A1; A3]^T pc_t for 256 tokens x 256 columns.  Stages [0, nst): pc
+// P = [A1; A3]^T pc_t for 128 tokens x 256 columns.  Stages [0, nst): pc
 // columns [0, 2r) against A1 (hi/lo halves fold onto the same r columns);
 // stages [nst, 2 nst): pc columns [2r, 4r) against A3.  The A factors come in
 // transposed per call (A1T, A3T = A1^T, A3^T, [H, r], by k_transpose), so the
@@ -693,8 +693,10 @@ __global__ __launch_bounds__(256) void k_pc(LayerArgs a) {
 // zero.
 struct LdRankDxK {
   using KM = v2::KLoad<GRK::TM, GRK::KT, GRK::NW>;
-  static constexpr int INSTS = 2 * KM::NJ;
-  KM m, n1, n3;
+  using KN = v2::KLoad<GRK::TN, GRK::KT, GRK::NW>;
+  static constexpr int INSTS = KM::NJ + KN::NJ;
+  KM m;
+  KN n1, n3;
   int nst, r;
   __device__ void issue(int s, char* sM, char* sN) {
     const bool second = s >= nst;
@@ -707,12 +709,12 @@ struct LdRankDxK {
   }
 };
 
-// grad_x = [A1; A3]^T pc_t + sum_j dU_(t,j) for 256 tokens x 256 columns
-__global__ __launch_bounds__(GRK::NT) void k_rank_dx(LayerArgs a) {
+// grad_x = [A1; A3]^T pc_t + sum_j dU_(t,j) for 128 tokens x 256 columns
+__global__ __launch_bounds__(GRK::NT, 2) void k_rank_dx(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   int t0, nt, ad;
-  if (!token_tile(a, blockIdx.x, GRK::TM, t0, nt, ad)) return;
-  const int h0 = blockIdx.y * GRK::TN;
+  if (!token_tile(a, blockIdx.y, GRK::TM, t0, nt, ad)) return;
+  const int h0 = blockIdx.x * GRK::TN;  // the column tiles of a token tile run side by side
   const int r = a.r;
   RouteVec rv;
   load_routes<false>(a, t0, t0 + nt, rv);
@@ -1137,7 +1139,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     if (e == hipSuccess) e = launch_transpose(a.A3, a.A3T, a.na, a.r, a.H, st);
     if (e != hipSuccess) return e;
   }
-  MOE_LAUNCH(k_rank_dx, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
+  MOE_LAUNCH(k_rank_dx, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);
   const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
   MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
   MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3 * rank_blocks(a.r)), dim3(GWG::NT), WG_LDS, st, a);

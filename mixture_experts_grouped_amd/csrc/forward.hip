@@ -540,23 +540,25 @@ __global__ __launch_bounds__(256) void k_zc(LayerArgs a) {
 }
 
 struct LdRankC {
-  using KL = v2::KLoad<GRK::TM, GRK::KT, GRK::NW>;
-  static constexpr int INSTS = 2 * KL::NJ;
-  KL m, n;
+  using KM = v2::KLoad<GRK::TM, GRK::KT, GRK::NW>;
+  using KN = v2::KLoad<GRK::TN, GRK::KT, GRK::NW>;
+  static constexpr int INSTS = KM::NJ + KN::NJ;
+  KM m;
+  KN n;
   __device__ void issue(int s, char* sM, char* sN) {
     m.issue(s * GRK::KT, 0, false, sM);
     n.issue(s * GRK::KT, 0, false, sN);
   }
 };
 
-// out = B2 zc_t + sum_j w_tj Ybase_(t,j) for 256 tokens (of one root) x 256
+// out = B2 zc_t + sum_j w_tj Ybase_(t,j) for 128 tokens (of one root) x 256
 // columns (zc carries s and the routing weights; hi/lo halves fold onto B2's
 // r columns; B2 of the root's adapter)
-__global__ __launch_bounds__(GRK::NT) void k_rank_combine(LayerArgs a) {
+__global__ __launch_bounds__(GRK::NT, 2) void k_rank_combine(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   int t0, nt, ad;
-  if (!token_tile(a, blockIdx.x, GRK::TM, t0, nt, ad)) return;
-  const int h0 = blockIdx.y * GRK::TN;
+  if (!token_tile(a, blockIdx.y, GRK::TM, t0, nt, ad)) return;
+  const int h0 = blockIdx.x * GRK::TN;  // the column tiles of a token tile run side by side
   const int r = a.r;
   RouteVec rv;
   load_routes<true>(a, t0, t0 + nt, rv);
@@ -672,7 +674,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   }
   const long nzc = (long)a.T * (a.r / 4);
   MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_rank_combine, dim3(token_tiles(a, GRK::TM), a.H / GRK::TN), dim3(GRK::NT), RK_LDS, st, a);
+  MOE_LAUNCH(k_rank_combine, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);
   return hipGetLastError();
 }
 

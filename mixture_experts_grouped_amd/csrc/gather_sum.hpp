@@ -5,22 +5,25 @@
 // The forward combine (mixture output, c = routing weight, R = the routes'
 // base outputs, P = B2 zc_t with zc_t = s sum_j w_tj z_tj) and the input
 // gradient (c = 1, R = the routes' W13^T [dg; dv], P = [A1; A3]^T pc_t) have
-// this form.  P is a rank-r product per token: a 256-token x 256-column tile
+// this form.  P is a rank-r product per token: a 128-token x 256-column tile
 // of it is one MFMA GEMM (k_rank_combine, k_rank_dx), and the route sum is
 // that GEMM's epilogue (rank_route_sum below), so P never leaves the chip:
 // one column half of the tile at a time is parked in LDS as fp32, then each
 // 16-lane group takes one token, 8 columns a lane, loads the token's route
 // rows (two tokens and up to eight routes a lane in flight) and writes the
 // bf16 result.  The route rows add in route order j = 0, 1, ... after P, so
-// the result does not depend on the pool layout.
+// the result does not depend on the pool layout.  A workgroup holds under
+// half of a CU's LDS and registers, so two run on each CU and one's GEMM
+// overlaps the other's route stream.
 #pragma once
 #include "engine2.hpp"
 #include "layer.hpp"
 
 namespace moelora {
 
-// 256-token x 256-column tiles of P; eight waves of 128 x 64.
-using GRK = v2::Geo2<4, 2, 2, 4, false, false, 64>;
+// 128-token x 256-column tiles of P; four waves of 64 x 128, 32-k stages,
+// three stage buffers.
+using GRK = v2::Geo2<2, 4, 2, 2, false, false, 32, 3>;
 using RankImg = v2::TileImage<GRK, GRK::TN / 2, float>;
 constexpr int RK_LDS = cmax(GRK::LDS_BYTES, RankImg::BYTES);
 
@@ -28,6 +31,7 @@ constexpr int RS_TPT = 2;   // tokens a thread carries per step
 constexpr int RS_JC = 8;    // route rows loaded per token before any is added
 constexpr int RS_TOK = GRK::TM / (GRK::NT / 16);  // tokens per thread over the tile (8)
 static_assert(GRK::TN / 2 == 16 * 8, "a 16-lane group covers one half row");
+static_assert(2 * RK_LDS <= 160 * 1024, "two workgroups a CU");
 static_assert(RS_TOK % RS_TPT == 0, "whole steps");
 
 // Lane-distributed routes of the thread's tokens: for token slot i, lane g*16
@@ -39,7 +43,7 @@ struct RouteVec {
   float c[RS_TOK];
 };
 
-// Token slot i of thread (wave w, lane): tile row i * 32 + 4 w + lane / 16.
+// Token slot i of thread (wave w, lane): tile row i * NT / 16 + 4 w + lane / 16.
 __device__ __forceinline__ int rs_token(int i) {
   return i * (GRK::NT / 16) + 4 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 4);
 }
@@ -69,21 +73,25 @@ __device__ __forceinline__ void rank_route_sum(const f32x16 (&acc)[GRK::NB][GRK:
                                                const LayerArgs& a, const RouteVec& rv,
                                                const uint16_t* __restrict__ R,
                                                uint16_t* __restrict__ out, int t0, int tend, int h0) {
-  static_assert(GRK::NB == 2, "one block column per half");
+  constexpr int NH = GRK::NB / 2;  // block columns per half (n_local: blocks [0, NH) in the first half)
   Epi<GRK> ep;
   const int lane = threadIdx.x & 63, gbase = lane & 48, li = lane & 15;
   const long H = a.H;
 #pragma unroll
-  for (int nb = 0; nb < GRK::NB; ++nb) {
+  for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int mb = 0; mb < GRK::MB; ++mb)
+    for (int nn = 0; nn < NH; ++nn)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        RankImg::put(smem, ep.row(mb), ep.col(nb, g) - nb * (GRK::TN / 2),
-                     f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
-                           acc[nb][mb][4 * g + 3]});
+      for (int mb = 0; mb < GRK::MB; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nb = hf * NH + nn;
+          RankImg::put(smem, ep.row(mb), ep.col(nb, g) - hf * (GRK::TN / 2),
+                       f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                             acc[nb][mb][4 * g + 3]});
+        }
     __syncthreads();
-    const int hc = h0 + nb * (GRK::TN / 2) + 8 * li;
+    const int hc = h0 + hf * (GRK::TN / 2) + 8 * li;
 #pragma unroll
     for (int i0 = 0; i0 < RS_TOK; i0 += RS_TPT) {
       float o[RS_TPT][8];
