@@ -196,7 +196,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W13, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
+  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W2, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
