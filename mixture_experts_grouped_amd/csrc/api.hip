@@ -127,10 +127,10 @@ int64_t capacity_of(const moe_lora_desc* d, int bm, int na = 1) {
 
 struct Plan {
   int64_t cap;
-  int maxtiles, nsplit;
+  int maxtiles, maxtiles3, nsplit;
   size_t saved, scratch, fwd_scratch;
   // byte offsets
-  size_t o_status, o_tiles, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
+  size_t o_status, o_tiles, o_tiles3, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_XQ, o_XS, o_HQ, o_HS;
   size_t o_fac, o_gfac, o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
 };
@@ -141,6 +141,7 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   p.cap = capacity_of(d, bm, R.na);
   const int64_t routes = (int64_t)d->T * d->topk;
   p.maxtiles = (int)((routes + TMG - 1) / TMG + std::min<int64_t>((int64_t)d->E * R.na, routes));
+  p.maxtiles3 = (int)((routes + TML - 1) / TML + std::min<int64_t>((int64_t)d->E * R.na, routes));
   p.nsplit = R.tiles(kSharedSplit);  // chunks of the shared-factor reductions, per root
   const size_t T = d->T, H = d->H, I = d->I, r = rank_p(d), cap = (size_t)p.cap;
   const size_t facb = padded(d) ? FacBlock(d, R.na).total * 2 : 0;  // the zero-padded factor copies
@@ -148,7 +149,8 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   auto take = [&](size_t bytes) { const size_t at = o; o = up(o + bytes); return at; };
   p.o_status = take(sizeof(int32_t));  // MOE_SAVED_STATUS_OFFSET
   p.o_tiles = take(sizeof(TileInfo) * p.maxtiles);
-  p.o_ntiles = take(sizeof(int));
+  p.o_tiles3 = take(sizeof(TileInfo) * p.maxtiles3);
+  p.o_ntiles = take(2 * sizeof(int));
   p.o_Xs = take(T * H * 2);
   p.o_ZA = take(T * 4 * r * 2);
   p.o_G = take((size_t)p.maxtiles * TMG * I * 2);  // fp16, accumulator-blocked per M tile
@@ -241,12 +243,16 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   // at most 48 routes per (expert, adapter) group on average: most groups
   // then fit one 64-row part (a larger group re-reads its weights per part)
   a.small_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)48 * a.EV;
+  // at least 768 routes per group on average: the TML-row tiles then pad
+  // little more than TMG-row ones
+  a.large_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk >= (int64_t)768 * a.EV;
   for (int q = 0; q <= R.na; ++q) a.roots[q] = R.r[q];
   a.k = d->topk;
   a.r = rank_p(d);
   a.s = d->scale;
   a.cap = p.cap;
   a.maxtiles = p.maxtiles;
+  a.maxtiles3 = p.maxtiles3;
   a.nsplit = p.nsplit;
   a.kspl = kSharedSplit;
   a.counts = pool->counts;
@@ -280,6 +286,7 @@ void fill_saved(LayerArgs& a, const Plan& p, void* saved) {
   char* b = (char*)saved;
   a.status = (int*)(b + p.o_status);
   a.tiles = (TileInfo*)(b + p.o_tiles);
+  a.tiles3 = (TileInfo*)(b + p.o_tiles3);
   a.ntiles = (int*)(b + p.o_ntiles);
   a.Xs = (uint16_t*)(b + p.o_Xs);
   a.ZA = (uint16_t*)(b + p.o_ZA);

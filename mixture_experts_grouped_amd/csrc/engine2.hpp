@@ -28,6 +28,8 @@
 //           4q + (i >> 2), q = 0..3 (probed on the device), which turns four
 //           k-rows of 16 columns into four consecutive k of one column.
 #pragma once
+#include <type_traits>
+
 #include "engine.hpp"
 
 namespace moelora {
@@ -618,10 +620,10 @@ struct TileImage {
   }
 };
 
-// SPLIT: 0 = no stage is split, 1 = every stage, 2 = stages s < ld.nsplit
-// (a low-rank extension run first, in the same pipeline as the base K range;
-// the two kinds of stage run in loops of their own so that each loop body
-// holds one fragment schedule).
+// SPLIT: 0 = no stage is split, 1 = every stage, 2 = the last ld.nsplit
+// stages (a low-rank extension run after the base K range, in the same
+// pipeline; the two kinds of stage run in loops of their own so that each
+// loop body holds one fragment schedule).
 template <class G, int SPLIT, class L>
 __device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB][G::MB],
                                             char* smem) {
@@ -640,13 +642,163 @@ __device__ __forceinline__ void run_stages2(L& ld, int nst, f32x16 (&acc)[G::NB]
     }
     int s = 0;
     if constexpr (SPLIT == 2) {
-      const int ns = ld.nsplit < nst ? ld.nsplit : nst;
-      for (; s < ns; ++s) step2<G, true>(ld, s, nst, acc, smem, wm, wn, lane);
+      const int nb = nst - ld.nsplit > 0 ? nst - ld.nsplit : 0;
+      for (; s < nb; ++s) step2<G, false>(ld, s, nst, acc, smem, wm, wn, lane);
+      for (; s < nst; ++s) step2<G, true>(ld, s, nst, acc, smem, wm, wn, lane);
+    } else {
+      for (; s < nst; ++s) step2<G, SPLIT == 1>(ld, s, nst, acc, smem, wm, wn, lane);
     }
-    for (; s < nst; ++s) step2<G, SPLIT == 1>(ld, s, nst, acc, smem, wm, wn, lane);
   }
   __syncthreads();
 }
+
+
+// ---------------------------------------------------------------------------
+// Large wave tiles: twelve accumulator blocks (192 of the 256 registers a
+// wave has at two waves per SIMD), both operands K tiles of 64 k, two stage
+// buffers.  Fragment addresses: the chunk swizzle of tile row 32 j + l is
+// (l & 7) ^ (l >> 3) ^ 4 (j & 1), so the fragment of row block j at k-step kk
+// lies at 4096 j + o[kk ^ 2 (j & 1)]: four lane offsets serve every fragment
+// of both tiles (the general frag() leaves the compiler one address per
+// fragment and k-step, which does not fit beside the accumulators).  Each
+// fragment is read once per k-step; a fragment of the next step is read
+// right after the last product of this step that uses its register.
+// ---------------------------------------------------------------------------
+template <class G>
+struct FragLT {
+  static_assert(!G::MTR && !G::NTR && G::KT == 64 && G::NBUF == 2, "K tiles of 64 k, two buffers");
+  static_assert((G::NB / 2) % 2 == 0 && (G::TN / 64) % 2 == 0, "N row block parity fixed by nb");
+  uint32_t om[4], on[4];  // M tile (this wave's row block parity folded in), N tile
+  __device__ __forceinline__ void init(int wm, int lane) {
+    const int l = lane & 31;
+    const uint32_t u = (uint32_t)((lane >> 5) ^ (l & 7) ^ (l >> 3));
+    const bool odd = ((wm * G::MB) & 1) != 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) on[v] = 128u * (uint32_t)l + ((((uint32_t)(2 * v)) ^ u) << 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) om[v] = odd ? on[v ^ 2] : on[v];
+  }
+  // M row block mb of this wave (sM: the wave's first row block)
+  __device__ __forceinline__ bf16x8 m(const char* sM, int mb, int kk) const {
+    return *(const bf16x8*)(sM + om[kk ^ (2 * (mb & 1))] + 4096 * mb);
+  }
+  // N block nb of this wave (sN: the tile plus the wave's column offset)
+  __device__ __forceinline__ bf16x8 n(const char* sN, int nb, int kk) const {
+    constexpr int H2 = G::NB / 2;
+    const int j = (nb < H2 ? 0 : G::TN / 64) + nb % H2;
+    return *(const bf16x8*)(sN + on[kk ^ (2 * ((nb % H2) & 1))] + 4096 * j);
+  }
+};
+
+template <class G, bool SPLIT>
+__device__ __forceinline__ void mma_stage_lt(const char* sM, const char* sN, const FragLT<G>& fo,
+                                             f32x16 (&acc)[G::NB][G::MB]) {
+  constexpr int KS = 4;
+  auto active = [](int nb, int kk) { return !SPLIT || ((nb < G::NB / 2) == (kk < KS / 2)); };
+  bf16x8 a[G::NB], b[G::MB];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) b[mb] = fo.m(sM, mb, 0);
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb)
+    if (active(nb, 0)) a[nb] = fo.n(sN, nb, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        if (active(nb, kk))
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+        if (mb == G::MB - 1 && kk + 1 < KS && active(nb, kk + 1)) a[nb] = fo.n(sN, nb, kk + 1);
+      }
+      if (kk + 1 < KS) b[mb] = fo.m(sM, mb, kk + 1);
+    }
+  }
+}
+
+// Stages [0, nbase) plain, then next SPLIT stages; `ld.base(s, sM, sN)` and
+// `ld.ext(s, sM, sN)` queue base stage s and extension stage s.  One barrier
+// per stage; a stage is queued into the buffer the previous one used once
+// every wave has passed that barrier.  The stage that queues the first
+// extension stage is peeled, so that each loop issues one kind of stage
+// (the loaders of the other kind hold no registers meanwhile).
+template <class G, class L>
+__device__ __forceinline__ void run_stages_lt(L& ld, int nbase, int next, f32x16 (&acc)[G::NB][G::MB],
+                                              char* smem) {
+  const int nst = nbase + next;
+  if (nst <= 0) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = w / G::WN, wn = w % G::WN;
+  FragLT<G> fo;
+  fo.init(wm, lane);
+  const int om = 4096 * G::MB * wm, on = G::SM_BYTES + 4096 * (G::NB / 2) * wn;
+  auto buf = [&](int s) { return smem + (s & 1) * G::STAGE; };
+  if (nbase > 0)
+    ld.base(0, smem, smem + G::SM_BYTES);
+  else
+    ld.ext(0, smem, smem + G::SM_BYTES);
+  int s = 0;
+  for (; s + 1 < nbase; ++s) {
+    wait_vm<0>();
+    bar();
+    ld.base(s + 1, buf(s + 1), buf(s + 1) + G::SM_BYTES);
+    mma_stage_lt<G, false>(buf(s) + om, buf(s) + on, fo, acc);
+  }
+  if (s < nbase) {  // the last base stage
+    wait_vm<0>();
+    bar();
+    if (next > 0) ld.ext(0, buf(s + 1), buf(s + 1) + G::SM_BYTES);
+    mma_stage_lt<G, false>(buf(s) + om, buf(s) + on, fo, acc);
+    ++s;
+  }
+  for (; s < nst; ++s) {
+    wait_vm<0>();
+    bar();
+    if (s + 1 < nst) ld.ext(s + 1 - nbase, buf(s + 1), buf(s + 1) + G::SM_BYTES);
+    mma_stage_lt<G, true>(buf(s) + om, buf(s) + on, fo, acc);
+  }
+  __syncthreads();
+}
+
+// K tile of R rows gathered by token, offsets formed at issue from the
+// token ids (one register a tile row; the byte offsets would need one each
+// for every source).  issue(): whole stages of a [*, ldb / 2] bf16 matrix;
+// issue_split(): SPLIT stages (chunks c < CPR/2 read k = k0 + 8c, the others
+// khalf + k0 + 8 (c - CPR/2); k past span reads zero).
+template <int R, int KT, int NW>
+struct KLoadTk {
+  static constexpr int CPR = Depth<KT>::CPR, RPI = Depth<KT>::RPI;
+  static constexpr int NJ = R / (NW * RPI);
+  static_assert(NJ >= 1 && NJ * NW * RPI == R, "tile rows per stage");
+  int tk[NJ];  // token of tile row j of this lane, -1: zeros
+  __device__ static __forceinline__ int row_of(int j) { return KLoad<R, KT, NW>::row_of(j); }
+  __device__ static __forceinline__ int slot(int j) { return (int)(threadIdx.x % CPR) ^ kswz<KT>(row_of(j)); }
+  __device__ __forceinline__ void tokens(const int32_t* row2r, int topk, long row0, long nvalid) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) tk[j] = (row_of(j) < nvalid) ? row2r[row0 + row_of(j)] / topk : -1;
+  }
+  __device__ __forceinline__ void issue(rsrc_t rs, uint32_t ldb, int k0, char* tile) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      asm volatile("" : "+v"(tk[j]));  // form the offset here, not once for the loop in another register
+      const uint32_t off = tk[j] >= 0 ? (uint32_t)tk[j] * ldb + 16u * (uint32_t)slot(j) : OFF_NONE;
+      lds_load16(rs, tile + 1024 * (w + NW * j), off, 2u * (uint32_t)k0);
+    }
+  }
+  __device__ __forceinline__ void issue_split(rsrc_t rs, uint32_t ldb, int k0, int khalf, int span,
+                                              char* tile) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      asm volatile("" : "+v"(tk[j]));
+      const int c = slot(j);
+      const int k = (c < CPR / 2) ? k0 + 8 * c : khalf + k0 + 8 * (c - CPR / 2);
+      const bool ok = tk[j] >= 0 && k < span;
+      lds_load16(rs, tile + 1024 * (w + NW * j), ok ? (uint32_t)tk[j] * ldb + 2u * (uint32_t)k : OFF_NONE);
+    }
+  }
+};
 
 }  // namespace v2
 }  // namespace moelora

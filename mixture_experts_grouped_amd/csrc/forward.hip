@@ -113,13 +113,20 @@ using GW13 = v2::Geo2<4, 2, 2, 4, false, false, 64>;  // 256 x 256 tile, eight w
 // in flight instead of one).  Each element still sums the same products in
 // the same order, so the results are those of the full tile.
 using GW13S = v2::Geo2<1, 2, 2, 4, false, false, 64, 3>;  // 64 x 256, eight waves
+// Large tile (bf16 base, enough rows per expert): 384 x 256, eight waves of
+// 96 x 128 (three row blocks by two gate/up block pairs).  Two stages fill
+// the 160 KB of LDS; per product it reads 22 % fewer LDS fragment bytes and
+// 17 % fewer operand bytes from L2 than the 256 x 256 tile, and each stage
+// multiplies half as long again while the next one loads.
+using GW13L = v2::Geo2<3, 4, 4, 2, false, false, 64>;
 template <class G>
 constexpr int w13_lds() { return cmax(G::LDS_BYTES, v2::TileImage<G, G::TN / 2, uint16_t>::BYTES); }
-constexpr int W13_LDS = w13_lds<GW13>(), W13S_LDS = w13_lds<GW13S>();
+constexpr int W13_LDS = w13_lds<GW13>(), W13S_LDS = w13_lds<GW13S>(), W13L_LDS = w13_lds<GW13L>();
+static_assert(W13L_LDS <= 160 * 1024, "the large tile fits the LDS of a CU");
 
-// Stages [0, nsplit): the B1/B3 extension, SPLIT (KT/2 k of each half per
-// stage); stages [nsplit, ...): the base K = H.  M loaders: G::TM rows by
-// token; N loaders: the 256 weight rows of the tile.
+// Stages [0, H/KT): the base K = H; the last nsplit stages: the B1/B3
+// extension, SPLIT (KT/2 k of each half per stage).  M loaders: G::TM rows
+// by token; N loaders: the 256 weight rows of the tile.
 template <class G>
 struct LdW13Base {
   using KL = v2::KLoad<G::TM, G::KT, G::NW>;          // ZA rows (M)
@@ -138,14 +145,37 @@ struct LdW13 : LdW13Base<G> {
   static_assert(NL::NJ == B::KL2::NJ && B::KA::NJ == B::KL::NJ, "one instruction count per stage");
   typename B::KA mm;
   NL nm;
+  int nbase;
   __device__ void issue(int s, char* sM, char* sN) {
-    if (s < this->nsplit) {
-      this->me.issue(s * (G::KT / 2), 2 * this->r, true, sM);
-      this->ne.issue(s * (G::KT / 2), 2 * this->r, true, sN);
+    if (s >= nbase) {
+      const int se = s - nbase;
+      this->me.issue(se * (G::KT / 2), 2 * this->r, true, sM);
+      this->ne.issue(se * (G::KT / 2), 2 * this->r, true, sN);
     } else {
-      mm.issue((s - this->nsplit) * G::KT, sM);
-      nm.issue((s - this->nsplit) * G::KT, sN);
+      mm.issue(s * G::KT, sM);
+      nm.issue(s * G::KT, sN);
     }
+  }
+};
+// The large tile (GW13L): x rows and ZA rows by token through one token
+// list, B1 | B3 rows, the weight tile loader NL.
+template <class G, class NL>
+struct LdW13L {
+  using KT = v2::KLoadTk<G::TM, G::KT, G::NW>;
+  using KL2 = typename LdW13Base<G>::KL2;
+  KT m;
+  KL2 ne;
+  NL nm;
+  rsrc_t rx, rza;
+  uint32_t ldx, ldza;
+  int r, nbase;
+  __device__ void base(int s, char* sM, char* sN) {
+    m.issue(rx, ldx, s * G::KT, sM);
+    nm.issue(s * G::KT, sN);
+  }
+  __device__ void ext(int s, char* sM, char* sN) {
+    m.issue_split(rza, ldza, s * (G::KT / 2), 2 * r, 4 * r, sM);
+    ne.issue(s * (G::KT / 2), 2 * r, true, sN);
   }
 };
 // MXFP4 base (engine_mx.hpp): the split activation rows (x by token, or h
@@ -182,22 +212,24 @@ static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipe
 // SK: 64-row parts of the pool tiles (GW13S; bf16 base): the grid is SUB
 // times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
 // tile's rows return at once.
-template <bool MX, int ACT, bool CL, bool PK, bool SK>
+// LT: the large tile (GW13L; bf16 base) over the TML-row tile list.
+template <bool MX, int ACT, bool CL, bool PK, bool SK, bool LT>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   static_assert(!(MX && PK) && !(MX && SK), "the packed copy and the small tiles are of a bf16 base");
+  static_assert(!(LT && (MX || SK)), "the large tile is of a bf16 base with full tiles");
   extern __shared__ __align__(16) char smem[];
-  using G = typename std::conditional<SK, GW13S, GW13>::type;
+  using G = typename std::conditional<SK, GW13S, typename std::conditional<LT, GW13L, GW13>::type>::type;
   static_assert(G::NT == GW13::NT && G::TN == GW13::TN, "same workgroup and N tile");
   using KL = typename LdW13Base<G>::KL;
-  constexpr int TN = G::TN, HALF = TN / 2, SUB = TMG / G::TM;
+  constexpr int TN = G::TN, HALF = TN / 2, SUB = LT ? 1 : TMG / G::TM;
   const int ntn = a.I / HALF;
   // part `sub` of pool tile work item b (SUB == 1: the block index itself)
   const int nb = SUB == 1 ? (int)gridDim.x : __builtin_amdgcn_readfirstlane(gridDim.x / SUB);
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W13, mt, nt)) return;
-  const TileInfo ti = a.tiles[mt];
+  if (!live_tile(b, a.ntiles[LT ? 1 : 0], ntn, LT ? TILE_GM_W13L : TILE_GM_W13, mt, nt)) return;
+  const TileInfo ti = (LT ? a.tiles3 : a.tiles)[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
   const int nrows = ti.row_end - row0 < G::TM ? ti.row_end - row0 : G::TM;
@@ -210,13 +242,39 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   auto wrow = [&](int nl) { return (nl < HALF) ? i0 + nl : a.I + i0 + (nl - HALF); };
   f32x16 acc[G::NB][G::MB];
   zero_acc<G>(acc);
-  if constexpr (!MX) {
+  if constexpr (LT) {
+    using KN = typename LdW13Base<G>::KN;
+    using KL2 = typename LdW13Base<G>::KL2;
+    using NL = typename std::conditional<PK, v2::KLoadP<256, G::KT, G::NW>, KN>::type;
+    LdW13L<G, NL> L;
+    L.r = r;
+    L.nbase = a.H / G::KT;
+    L.m.tokens(a.row2r, a.k, row0, nrows);
+    L.rx = make_rsrc(a.x, (uint64_t)a.T * a.H * 2);
+    L.ldx = (uint32_t)a.H * 2u;
+    L.rza = make_rsrc(a.ZA, (uint64_t)a.T * 4 * r * 2);
+    L.ldza = (uint32_t)(4 * r) * 2u;
+    L.ne.rs = make_rsrc(a.B1 + le * a.I * r, (uint64_t)2 * r * a.I);
+    L.ne.rs2 = make_rsrc(a.B3 + le * a.I * r, (uint64_t)2 * r * a.I);
+#pragma unroll
+    for (int j = 0; j < KL2::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KL2::row_of(j) % HALF)) * r * 2);
+    L.ne.window(2 * r, r, HALF, 2 * r);  // gate rows read k in [0, 2r), up rows [2r, 4r)
+    if constexpr (PK) {
+      L.nm.set(a.W13P + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2, nt, a.H / G::KT);
+    } else {
+      L.nm.rs = make_rsrc(a.W13 + (long)e * 2 * a.I * a.H, (uint64_t)2 * a.I * a.H * 2);
+#pragma unroll
+      for (int j = 0; j < KN::NJ; ++j) L.nm.set_row(j, (uint32_t)((long)wrow(KN::row_of(j)) * a.H * 2));
+    }
+    v2::run_stages_lt<G>(L, L.nbase, nsplit, acc, smem);
+  } else if constexpr (!MX) {
     using KN = typename LdW13Base<G>::KN;
     using KL2 = typename LdW13Base<G>::KL2;
     using NL = typename std::conditional<PK, v2::KLoadP<256, G::KT, G::NW>, KN>::type;
     LdW13<G, NL> L;
     L.r = r;
     L.nsplit = nsplit;
+    L.nbase = a.H / G::KT;
     L.me.from_tokens(a.ZA, a.T, 4 * r, tk);
     L.me.window(4 * r);
     L.ne.rs = make_rsrc(a.B1 + le * a.I * r, (uint64_t)2 * r * a.I);
@@ -272,12 +330,22 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   // status word (h and the forward output are computed from the fp32 values
   // and stay right).  With a clamp every such value is clipped anyway.
   bool wide = false;
+  // G, V are blocked by TMG-row tiles: a large tile writes the 32-row blocks
+  // inside the group's TMG tiles (rows past its count hold zeros, as a TMG
+  // tile writes them; blocks past its last TMG tile belong to the next
+  // group); a TMG tile writes all of its blocks
+  int rlim = G::TM;
+  if constexpr (LT) {
+    const int off = a.offsets[ti.e];
+    rlim = off + (ti.row_end - off + TMG - 1) / TMG * TMG - row0;
+  }
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb) {
+      if (LT && G::m_local(wm, mb) >= rlim) continue;
       const int cb = (i0 + G::n_local(wn, nb)) / 32;
-      const long ob = acc_block(mt, G::m_local(wm, mb) / 32 + sub * (G::TM / 32), cb, a.I) + 4 * lane;
+      const long ob = acc_blk(ti.pad + G::m_local(wm, mb) / 32 + sub * (G::TM / 32), cb, a.I) + 4 * lane;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 gv, vv, hv;
@@ -575,33 +643,36 @@ __global__ __launch_bounds__(GRK::NT, 2) void k_rank_combine(LayerArgs a) {
 
 // ----------------------------------------------------------------------------
 
-template <bool MX, int ACT, bool CL, bool PK, bool SK>
+template <bool MX, int ACT, bool CL, bool PK, bool SK, bool LT>
 static void launch_w13(const LayerArgs& a, hipStream_t st) {
   constexpr int SUB = SK ? TMG / GW13S::TM : 1;
-  const dim3 grid(a.maxtiles * (a.I / (GW13::TN / 2)) * SUB);
-  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL, PK, SK>), grid, dim3(GW13::NT), SK ? W13S_LDS : W13_LDS, st, a);
+  const dim3 grid((LT ? a.maxtiles3 : a.maxtiles) * (a.I / (GW13::TN / 2)) * SUB);
+  MOE_LAUNCH_AS("k_w13", (k_w13<MX, ACT, CL, PK, SK, LT>), grid, dim3(GW13::NT),
+                SK ? W13S_LDS : (LT ? W13L_LDS : W13_LDS), st, a);
 }
-template <bool MX, int ACT, bool PK, bool SK>
+template <bool MX, int ACT, bool PK, bool SK, bool LT>
 static void launch_w13_cl(const LayerArgs& a, hipStream_t st) {
   if (a.clamp > 0.0f)
-    launch_w13<MX, ACT, true, PK, SK>(a, st);
+    launch_w13<MX, ACT, true, PK, SK, LT>(a, st);
   else
-    launch_w13<MX, ACT, false, PK, SK>(a, st);
+    launch_w13<MX, ACT, false, PK, SK, LT>(a, st);
 }
 template <bool MX, int ACT, bool PK>
 static void launch_w13_sk(const LayerArgs& a, hipStream_t st) {
   if (!MX && a.small_tiles)
-    launch_w13_cl<MX, ACT, PK, !MX>(a, st);
+    launch_w13_cl<MX, ACT, PK, !MX, false>(a, st);
+  else if (!MX && a.large_tiles)
+    launch_w13_cl<MX, ACT, PK, false, !MX>(a, st);
   else
-    launch_w13_cl<MX, ACT, PK, false>(a, st);
+    launch_w13_cl<MX, ACT, PK, false, false>(a, st);
 }
-template <bool MX, bool PK, bool SK>
+template <bool MX, bool PK, bool SK, bool LT>
 static void set_w13_lds(AttrInit& ai) {
-  const int lds = SK ? W13S_LDS : W13_LDS;
-  ai.lds((const void*)k_w13<MX, 0, false, PK, SK>, lds);
-  ai.lds((const void*)k_w13<MX, 1, false, PK, SK>, lds);
-  ai.lds((const void*)k_w13<MX, 0, true, PK, SK>, lds);
-  ai.lds((const void*)k_w13<MX, 1, true, PK, SK>, lds);
+  const int lds = SK ? W13S_LDS : (LT ? W13L_LDS : W13_LDS);
+  ai.lds((const void*)k_w13<MX, 0, false, PK, SK, LT>, lds);
+  ai.lds((const void*)k_w13<MX, 1, false, PK, SK, LT>, lds);
+  ai.lds((const void*)k_w13<MX, 0, true, PK, SK, LT>, lds);
+  ai.lds((const void*)k_w13<MX, 1, true, PK, SK, LT>, lds);
 }
 
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
@@ -617,11 +688,13 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   hipError_t err = attrs.run([] {
     AttrInit ai;
     ai.lds((const void*)k_shrink, GS64::LDS_BYTES);
-    set_w13_lds<false, false, false>(ai);
-    set_w13_lds<false, true, false>(ai);
-    set_w13_lds<false, false, true>(ai);
-    set_w13_lds<false, true, true>(ai);
-    set_w13_lds<true, false, false>(ai);
+    set_w13_lds<false, false, false, false>(ai);
+    set_w13_lds<false, true, false, false>(ai);
+    set_w13_lds<false, false, true, false>(ai);
+    set_w13_lds<false, true, true, false>(ai);
+    set_w13_lds<false, false, false, true>(ai);
+    set_w13_lds<false, true, false, true>(ai);
+    set_w13_lds<true, false, false, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
     ai.lds((const void*)k_a2s, GA2S::LDS_BYTES);
     ai.lds((const void*)k_w2<false, false, false>, W2_LDS);

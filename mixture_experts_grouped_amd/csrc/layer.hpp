@@ -11,10 +11,13 @@
 namespace moelora {
 
 constexpr int TMG = 256;  // M tile of the grouped GEMMs (rows of one expert)
+// M tile of the large W13 tile (384 x 256: the whole 160 KB of LDS for two
+// stages, a third fewer operand bytes per product than 256 x 256)
+constexpr int TML = 384;
 // M tiles per group in the XCD-aware tile order of each base GEMM (same-box
 // sweeps over 1, 2, 4 and 8 at the production share: 4, except the W2
 // forward, whose 8 is 3 % faster)
-constexpr int TILE_GM_W13 = 4, TILE_GM_W2 = 8, TILE_GM_W2D = 4, TILE_GM_W13D = 4;
+constexpr int TILE_GM_W13 = 4, TILE_GM_W2 = 8, TILE_GM_W2D = 4, TILE_GM_W13D = 4, TILE_GM_W13L = 4;
 constexpr int MAX_ADAPTERS = 64;  // adapters of one multi-adapter pass
 constexpr int KSPLIT = 4;  // fixed K split of the long-K token GEMMs (ZA = A x, q = B2^T go)
 // Kernels whose output tile spans the rank (ZA, Z2, q, P and the adapter
@@ -27,10 +30,9 @@ __host__ __device__ inline int rank_blocks(int r) { return (r + RBLK - 1) / RBLK
 // blocks: block (M tile mt, row block rb of 8, column block cb of I/32) is
 // 1024 elements, ordered [g (4)][lane (64)][q (4)] so that the lane's
 // accumulator values 4g .. 4g + 3 are one access (8 bytes in fp16) and a
-// wave's access is contiguous (512 bytes).
-__device__ __forceinline__ long acc_block(int mt, int rb, int cb, int I) {
-  return ((long)(mt * 8 + rb) * (I / 32) + cb) * 1024;
-}
+// wave's access is contiguous (512 bytes).  Row block index rbi = 8 mt + rb.
+__device__ __forceinline__ long acc_blk(int rbi, int cb, int I) { return ((long)rbi * (I / 32) + cb) * 1024; }
+__device__ __forceinline__ long acc_block(int mt, int rb, int cb, int I) { return acc_blk(mt * 8 + rb, cb, I); }
 
 // Everything a kernel may touch, passed by value as the kernel argument.
 // Pool-shaped tensors have `cap` rows; token-shaped tensors have T rows.
@@ -40,7 +42,7 @@ struct LayerArgs {
   int T, H, I, E, k, r;
   float s;
   long cap;
-  int maxtiles;
+  int maxtiles, maxtiles3;
   // adapters (multi-adapter pass, OpenPipe/ART PR #1139, Behavior): na roots
   // of tokens, root q = tokens roots[q] .. roots[q+1]-1, each with its own
   // factors.  The pool groups rows by (expert e, adapter q) as group
@@ -51,6 +53,8 @@ struct LayerArgs {
   // few rows per pool group (bf16 base): the base GEMMs take 64-row parts of
   // each pool tile (bitwise the same results as full tiles)
   int small_tiles;
+  // many rows per pool group (bf16 base): the W13 GEMM takes TML-row tiles
+  int large_tiles;
   // pool
   const int32_t* counts;
   const int32_t* offsets;
@@ -74,8 +78,9 @@ struct LayerArgs {
   const uint16_t *W13T, *W2T, *W13P, *W2P;
   // saved by the forward
   int* status;       // [1] status word at offset 0 of saved (MOE_SAVED_* bits)
-  TileInfo* tiles;   // [maxtiles]
-  int* ntiles;       // [1]
+  TileInfo* tiles;   // [maxtiles]   M tiles of TMG rows (pad: 8 x the tile's index)
+  int* ntiles;       // [2]          live tiles of `tiles`, then of `tiles3`
+  TileInfo* tiles3;  // [maxtiles3]  M tiles of TML rows (pad: the row block index of row0)
   uint16_t* Xs;      // [T, H]    copy of x for the backward (the W13 GEMM gathers x rows itself)
   uint16_t* ZA;      // [T, 4r]   s*A1 x, s*A3 x as hi/lo
   _Float16* G;       // gate pre-activation, fp16, accumulator-blocked (acc_block)

@@ -175,29 +175,39 @@ hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, lon
   return hipGetLastError();
 }
 
-// Grouped-GEMM M tiles: TMG rows of one pool group each, never crossing groups.
+// Grouped-GEMM M tiles: TMG rows of one pool group each, never crossing
+// groups; and the same for TML-row tiles, whose `pad` is the accumulator-
+// blocked row block index (acc_blk) of their first row: 8 x the TMG tile
+// holding it plus its 32-row block inside that tile.
 __global__ __launch_bounds__(64) void k_tile_map(LayerArgs a) {
   const int lane = threadIdx.x;
-  int carry = 0;
+  int carry = 0, carry3 = 0;
   for (int b0 = 0; b0 < a.EV; b0 += 64) {
     const int e = b0 + lane;
     const int n = (e < a.EV) ? a.counts[e] : 0;
-    const int nt = (n + TMG - 1) / TMG;
-    int x = nt;
+    const int nt = (n + TMG - 1) / TMG, nt3 = (n + TML - 1) / TML;
+    int x = nt, x3 = nt3;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      const int y = __shfl_up(x, o, 64), y3 = __shfl_up(x3, o, 64);
+      if (lane >= o) {
+        x += y;
+        x3 += y3;
+      }
     }
-    const int start = carry + x - nt;
+    const int start = carry + x - nt, start3 = carry3 + x3 - nt3;
     if (e < a.EV) {
       const int off = a.offsets[e];
-      for (int t = 0; t < nt; ++t) a.tiles[start + t] = TileInfo{e, off + t * TMG, off + n, 0};
+      for (int t = 0; t < nt; ++t) a.tiles[start + t] = TileInfo{e, off + t * TMG, off + n, 8 * (start + t)};
+      for (int t = 0; t < nt3; ++t)
+        a.tiles3[start3 + t] = TileInfo{e, off + t * TML, off + n, 8 * start + t * (TML / 32)};
     }
     carry += __shfl(x, 63, 64);
+    carry3 += __shfl(x3, 63, 64);
   }
   if (lane == 0) {
-    *a.ntiles = carry;
+    a.ntiles[0] = carry;
+    a.ntiles[1] = carry3;
     *a.status = 0;  // raised again by this forward's kernels only
   }
 }

@@ -165,3 +165,26 @@ def test_small_tile_parts_equal_full_tiles():
         res = Hn.GpuRun(shape_s, small, transformed=transformed).run()
         for n in ("out", "grad_x", "grad_w"):
             assert Hn.same_bits(res[n], np.ascontiguousarray(big[n][:100])), (transformed, n)
+
+
+def test_large_tiles_equal_full_tiles():
+    """With many routes per expert (at least 768 on average) the W13 GEMM takes
+    384-row tiles of eight 96 x 128 wave tiles; fewer routes take 256-row
+    tiles.  The same tokens in a batch of each kind give bitwise the same
+    out, grad_x and grad_w (each element sums the same products in the same
+    order), with the plain and the transformed base; the large-tile batch is
+    also checked against the oracle.  Ragged: expert 3 ends inside a 384-row
+    tile and inside a 256-row tile."""
+    shape_b = I.Shape(T=1700, H=512, I=512, E=4, topk=2, rank=128)
+    case = I.layer_inputs(shape_b, (62,), routing="softmax_topk", mask_prob=0.05)
+    shape_s = I.Shape(T=240, H=512, I=512, E=4, topk=2, rank=128)  # 480 routes: 256-row tiles
+    small = dict(case)
+    for n in ("x", "grad_out", "topk_idx", "topk_w"):
+        small[n] = np.ascontiguousarray(case[n][:240])
+    for transformed in (False, True):
+        big = Hn.GpuRun(shape_b, case, transformed=transformed).run()
+        res = Hn.GpuRun(shape_s, small, transformed=transformed).run()
+        for n in ("out", "grad_x", "grad_w"):
+            assert Hn.same_bits(res[n], np.ascontiguousarray(big[n][:240])), (transformed, n)
+    ref_out, ref_g = Hn.oracle_run(case, shape_b.scale)
+    Hn.compare_all(big, ref_out, ref_g, tag="large:", per_expert=True)
