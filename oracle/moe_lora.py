@@ -43,11 +43,11 @@ Readings taken where the pages are silent:
 
   8. the MXFP4 base's native boundary (PR #9 "Historical implementation" ->
      Correctness coverage compares against both a full-precision reference
-     and a native-boundary one): with act_split="e4m3x2" the activations
+     and a native-boundary one): with act_split="e2m3x2" the activations
      entering the two base products -- u into W1/W3, h into W2 -- are
-     replaced by their two-term E4M3 split (oracle/mxfp4.py split_e4m3x2,
+     replaced by their two-term E2M3 split (oracle/mxfp4.py split_e2m3x2,
      blocks of 32 along the contraction axis), the precision in which the
-     kernels feed them to the scaled fp8 x fp4 matrix instruction; the
+     kernels feed them to the scaled fp6 x fp4 matrix instruction; the
      low-rank paths (A1 u, A3 u, A2 h) and every other product keep the exact
      values, and the backward treats the split as the identity (it is
      piecewise constant; the kernels' data gradients are the plain ones).
@@ -126,9 +126,9 @@ def _split(a: np.ndarray, act_split) -> np.ndarray:
     """The activations a base product sees (reading 8)."""
     if act_split is None:
         return a
-    assert act_split == "e4m3x2", act_split
-    from .mxfp4 import split_e4m3x2
-    return split_e4m3x2(a)[4]
+    assert act_split == "e2m3x2", act_split
+    from .mxfp4 import split_e2m3x2
+    return split_e2m3x2(a)[4]
 
 
 def expert_forward(u: np.ndarray, e: int, p: Dict[str, np.ndarray], scale: float,
