@@ -595,7 +595,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 x e4m3x2 fwd, bf16" if mx else "bf16",
+        "dtype": "mxfp4 x e2m3x2 fwd, bf16" if mx else "bf16",
         "data": "synthetic",
         "config": {
             "workload": (("MXFP4 base (e2m1 + e8m0/32) on scaled MFMA, " if mx else "") +

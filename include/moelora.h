@@ -216,23 +216,27 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
 moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
                                    void* W2T, void* W13P, void* W2P, void* stream);
 
-/* Two-term FP8 (E4M3) split of bf16 rows, the activation operand of the
- * MXFP4 base's scaled fp8 x fp4 matrix products (PR #9 "Historical
+/* Two-term FP6 (E2M3) split of bf16 rows, the activation operand of the
+ * MXFP4 base's scaled fp6 x fp4 matrix products (PR #9 "Historical
  * implementation" -> Summary: native MXFP4 base with bf16 side adapters, the
  * activations keeping bf16 precision).  moe_lora_forward runs it internally
  * on x and on the activations h; this call exposes it alone.
  *   src [rows, K] bf16 (K % 64 == 0, else MOE_ERR_UNSUPPORTED).
  *   Per row and aligned 32-block: s1 = 2^E1 with E1 the smallest integer such
- *   that max|x| <= 448 s1 (E1 = -127 for an all-zero block), q1 = E4M3(x/s1)
- *   rounded to nearest even (OCP 8-bit float E4M3: bias 7, subnormals kept,
- *   largest 448), r = x - s1 q1 (exact), (s2, q2) from r the same way;
- *   x ~ s1 q1 + s2 q2 to about 2^-8 of each element.
- *   codes [rows, 2K bytes]: per 64-element chunk c, 128 bytes =
- *     [q1 of elements 64c .. 64c+63 | q2 of the same];
+ *   that max|x| <= 7.5 s1 (E1 = -127 for an all-zero block), q1 = E2M3(x/s1)
+ *   rounded to nearest, ties to even (OCP MX v1.0 FP6 E2M3: bias 1,
+ *   subnormals m/8, largest 7.5; code 8e + m, sign in bit 5), r = x - s1 q1
+ *   (exact), (s2, q2) from r the same way; |x - (s1 q1 + s2 q2)| <=
+ *   2^-8 max(|x|, s1).
+ *   codes [rows, 2K bytes]: per 64-element chunk c, 128 bytes; term t (q1,
+ *     then q2) at 64t; the 32 six-bit codes of the chunk's 32-block h packed
+ *     into six little-endian dwords (element i in bits 6i .. 6i+5), dwords
+ *     0-3 at 64t + 16h and dwords 4-5 at 64t + 32 + 8h; bytes 64t + 48 ..
+ *     64t + 63 are not written;
  *   scale_words [rows, K/64] uint32: per chunk, bytes {E1+127 of its first
  *     32-block, of its second, E2+127 of the first, of the second}.
  *   src, codes 16-byte aligned, scale_words 4-byte aligned, no overlaps. */
-moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
+moe_status moe_lora_split_e2m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
                                  void* stream);
 
 /* Forward of the layer.

@@ -31,7 +31,7 @@ MOE_MAX_ADAPTERS = 64
 EXPORTS = (
     "moe_lora_status_string", "moe_lora_version", "moe_lora_block_m", "moe_lora_pool_capacity",
     "moe_lora_workspace_size", "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
-    "moe_lora_transform_base", "moe_lora_split_e4m3x2", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
+    "moe_lora_transform_base", "moe_lora_split_e2m3x2", "moe_lora_trace_enable", "moe_lora_trace_collect", "moe_lora_trace_count",
     "moe_lora_trace_entry", "moe_lora_trace_reset", "moe_lora_multi_pool_capacity",
     "moe_lora_multi_workspace_size", "build_pool_multi", "moe_lora_forward_multi", "moe_lora_backward_multi",
 )
@@ -117,7 +117,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
                                       ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp,
                                       ctypes.c_size_t, vp]
     lib.moe_lora_transform_base.argtypes = [P(MoeLoraDesc), P(MoeLoraParams), vp, vp, vp, vp, vp]
-    lib.moe_lora_split_e4m3x2.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    lib.moe_lora_split_e2m3x2.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_lora_trace_enable.argtypes = [ctypes.c_int32]
     lib.moe_lora_trace_enable.restype = None
     lib.moe_lora_trace_collect.argtypes = []
@@ -137,7 +137,7 @@ def library(path: Optional[str] = None) -> ctypes.CDLL:
                                             ctypes.c_size_t, vp, vp, P(MoeLoraGrads), vp, ctypes.c_size_t, vp]
     for fn in ("moe_lora_trace_collect", "moe_lora_trace_entry", "moe_lora_block_m", "moe_lora_pool_capacity", "moe_lora_workspace_size",
                "build_pool", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_backward",
-               "moe_lora_transform_base", "moe_lora_split_e4m3x2", "moe_lora_multi_pool_capacity",
+               "moe_lora_transform_base", "moe_lora_split_e2m3x2", "moe_lora_multi_pool_capacity",
                "moe_lora_multi_workspace_size", "build_pool_multi", "moe_lora_forward_multi",
                "moe_lora_backward_multi"):
         getattr(lib, fn).restype = ctypes.c_int32
@@ -435,18 +435,18 @@ def _sync(stream) -> None:
         torch.cuda.synchronize()
 
 
-def moe_lora_split_e4m3x2(src: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Two-term E4M3 split of bf16 rows src [rows, K] (see include/moelora.h):
+def moe_lora_split_e2m3x2(src: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Two-term E2M3 split of bf16 rows src [rows, K] (see include/moelora.h):
     returns (codes uint8 [rows, 2K], scale words int32 [rows, K/64])."""
     if src.dim() != 2:
         raise ValueError("src must be [rows, K]")
     rows, K = src.shape
     codes = torch.empty(rows, 2 * K, dtype=torch.uint8, device=src.device)
     scales = torch.empty(rows, K // 64, dtype=torch.int32, device=src.device)
-    st = library().moe_lora_split_e4m3x2(_ptr(src, torch.bfloat16, None, "src"), rows, K,
+    st = library().moe_lora_split_e2m3x2(_ptr(src, torch.bfloat16, None, "src"), rows, K,
                                          _ptr(codes, torch.uint8, None, "codes"),
                                          _ptr(scales, torch.int32, None, "scale_words"), _stream(stream))
-    _check(st, "moe_lora_split_e4m3x2")
+    _check(st, "moe_lora_split_e2m3x2")
     return codes, scales
 
 

@@ -630,7 +630,7 @@ moe_status moe_lora_backward_multi(const moe_lora_desc* d, const moe_adapters* a
                           scratch, scratch_bytes, stream);
 }
 
-moe_status moe_lora_split_e4m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
+moe_status moe_lora_split_e2m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,
                                  void* stream) {
   if (rows < 1 || K < 1) return MOE_ERR_INVALID;
   if (K % 64 != 0 || rows * (int64_t)(K / 32) >= ((int64_t)1 << 31) * 256) return MOE_ERR_UNSUPPORTED;

@@ -2,26 +2,31 @@
 //
 // The base weights are OCP MX v1.0 FP4 (E2M1, two per byte, element 2i in
 // the low nibble of byte i) with one E8M0 scale per 32 along K; the
-// activations are held as a two-term FP8 (E4M3) split with one E8M0 scale
-// per term and 32-block: x ~ s1 q1 + s2 q2 (split_block below).  Each k64
+// activations are held as a two-term FP6 (E2M3) split with one E8M0 scale
+// per term and 32-block: x ~ s1 q1 + s2 q2 (quant_term below).  Each k64
 // step is two v_mfma_scale_f32_32x32x64_f8f6f4 per output block (one per
-// term, weights as the fp4 first operand), accumulating into the same fp32
-// 32 x 32 accumulators as the bf16 engine, with the same lane layout: lanes
-// own output rows, registers four consecutive output columns.
+// term, weights as the fp4 first operand, activations as the fp6 second
+// operand: with both operands of six bits or fewer the instruction runs at
+// twice its fp8 rate), accumulating into the same fp32 32 x 32 accumulators
+// as the bf16 engine, with the same lane layout: lanes own output rows,
+// registers four consecutive output columns.
 //
 // Operand lane layouts of the scaled instruction (probed on the device):
 //   fp4 operand: lane l holds row l % 32, k = 32 (l / 32) .. + 31 (16 bytes,
 //                low nibble first); its scale is that 32-block's;
-//   fp8 operand: lane l holds row l % 32, elements 0-15 at k = 16 (l / 32) ..
-//                and elements 16-31 at k = 32 + 16 (l / 32) ..; the scale the
-//                lane supplies is that of k-block l / 32;
+//   fp6 operand: lane l holds row l % 32, k = 32 (l / 32) .. + 31: element
+//                e in bits 6e .. 6e + 5 of six dwords (little-endian across
+//                them); its scale is that 32-block's;
 //   the op_sel field picks the scale byte of the 32-bit scale register.
 //
 // Storage (per row, per 64-k chunk c of the contraction):
-//   activation codes   128 bytes: [hi codes k 64c..64c+63 | lo codes ...],
-//                      i.e. the row pitch of a bf16 row, so the bf16 K-tile
-//                      loader (KLoadA / KLoadS) and its swizzle carry it;
-//   activation scales  one 32-bit word: bytes {hi b0, hi b1, lo b0, lo b1}
+//   activation codes   128 bytes: term t (0: s1 q1, 1: s2 q2) at 64 t, its
+//                      32-block h (k 64c + 32h ..) as dwords 0-3 at 16 h and
+//                      dwords 4-5 at 32 + 8 h (bytes 48-63 unused): the row
+//                      pitch of a bf16 row, so the bf16 K-tile loader
+//                      (KLoadA / KLoadS) and its swizzle carry it, and each
+//                      lane's six dwords are one 16-byte and one 8-byte read;
+//   activation scales  one 32-bit word: bytes {s1 b0, s1 b1, s2 b0, s2 b1}
 //                      for the chunk's two 32-blocks;
 //   weight codes       32 bytes at 32c of the packed row;
 //   weight scales      byte 2c + b of the row's scale bytes.
@@ -50,45 +55,59 @@ static_assert(KA::NJ == 4 && KS::NJ == 4, "four 1 KB activation loads per wave a
 constexpr int INSTS = KA::NJ + 1 + 1;  // activation rows, weight rows, one scale word row
 
 // ---------------------------------------------------------------------------
-// Two-term E4M3 split of one aligned 32-block (values exactly bf16, in fp32).
-// s = 2^E with E the smallest integer such that amax <= 448 2^E (no element
-// saturates; amax = 0 or below 2^-126 gives E = -127), q = E4M3(x / s) to
-// nearest even (v_cvt_pk_fp8_f32, subnormals kept), r = x - s q exactly, and
-// the same again on r.  Scale bytes are E + 127.
+// Two-term E2M3 split of one aligned 32-block (values exactly bf16, in fp32).
+// s = 2^E with E the smallest integer such that amax <= 7.5 2^E (no element
+// saturates; amax = 0 or below 2^-126 gives E = -127), q = E2M3(x / s) to
+// nearest, ties to even, r = x - s q exactly, and the same again on r.
+// Scale bytes are E + 127.  E2M3 (OCP MX v1.0 FP6): bias 1, subnormals m/8,
+// normals (1 + m/8) 2^(e-1), largest 7.5; code 8 e + m, sign in bit 5.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+__device__ __forceinline__ int e2m3_scale_exp(float amax) {
   const uint32_t b = __float_as_uint(amax);
   const int field = (int)(b >> 23);  // amax >= 0
   if (field == 0) return -127;       // zero or subnormal
   const int p = field - 127;
-  const int e = ((b & 0x7FFFFFu) <= 0x600000u) ? p - 8 : p - 7;  // mantissa 1.75 or less: p - 8
+  const int e = ((b & 0x7FFFFFu) <= 0x700000u) ? p - 2 : p - 1;  // mantissa 1.875 or less: p - 2
   return e < -127 ? -127 : e;
 }
 __device__ __forceinline__ float pow2f(int e) {  // 2^e for e in [-127, 127]
   return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
-// 32 values -> 8 words of codes (byte j of word w = element 4w + j) and the
+// 32 values -> six dwords of codes (element i in bits 6i .. 6i + 5) and the
 // scale byte; also returns the residual x - s q in place of x.
-__device__ __forceinline__ uint32_t quant_term(float (&v)[32], uint32_t (&q)[8]) {
+__device__ __forceinline__ uint32_t quant_term(float (&v)[32], uint32_t (&q)[6]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int E = e4m3_scale_exp(amax);
+  const int E = e2m3_scale_exp(amax);
   const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, -E <= 127
   const float s = pow2f(E);
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t c = 0;
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w] * inv, v[4 * w + 1] * inv, c, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, c, true);
-    q[w] = c;
-    v[4 * w] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 0), s, v[4 * w]);
-    v[4 * w + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 1), s, v[4 * w + 1]);
-    v[4 * w + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 2), s, v[4 * w + 2]);
-    v[4 * w + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8((int)c, 3), s, v[4 * w + 3]);
+  for (int w = 0; w < 6; ++w) q[w] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = v[i] * inv;  // exact, |y| <= 7.5
+    const uint32_t ab = __float_as_uint(y) & 0x7FFFFFFFu;
+    // binade e of |y| from its exponent field, 0 below 2 (the step 1/8 of the
+    // subnormals and of [1, 2)); integer arithmetic, no per-element masks
+    const int e = min(max((int)(ab >> 23) - 127, 0), 2);
+    const float mul = __uint_as_float((uint32_t)(130 - e) << 23);   // 2^(3-e)
+    const float step = __uint_as_float((uint32_t)(124 + e) << 23);  // 2^(e-3)
+    const float n = __builtin_rintf(__uint_as_float(ab) * mul);     // multiples of the step, half to even
+    const uint32_t c = (8u * (uint32_t)e + (uint32_t)n) | ((__float_as_uint(y) >> 31) << 5);
+    v[i] = fmaf(-copysignf(n * step, y), s, v[i]);  // exact residual
+    const int b = 6 * i, wd = b >> 5, sh = b & 31;
+    q[wd] |= c << sh;
+    if (sh > 26) q[wd + 1] |= c >> (32 - sh);
   }
   return (uint32_t)(E + 127);
+}
+
+// One term's codes of 32-block h of a 64-k chunk at `chunk` (128 bytes).
+__device__ __forceinline__ void store_term(uint8_t* chunk, int t, int h, const uint32_t (&q)[6]) {
+  *(u32x4*)(chunk + 64 * t + 16 * h) = u32x4{q[0], q[1], q[2], q[3]};
+  *(u32x2*)(chunk + 64 * t + 32 + 8 * h) = u32x2{q[4], q[5]};
 }
 
 // Rows of a bf16 [nrows, K] matrix -> codes [nrows, 2K bytes] and scale
@@ -117,17 +136,15 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
 #pragma unroll
     for (int c = 0; c < 32; ++c) v[c] = 0.0f;
   }
-  uint32_t hi[8], lo[8];
+  uint32_t hi[6], lo[6];
   const uint32_t s1 = quant_term(v, hi);
   const uint32_t s2 = quant_term(v, lo);
   // partner block of the same 64-chunk (j ^ 1) sits in the neighbouring lane
   const uint32_t o1 = __shfl_xor(s1, 1, 64), o2 = __shfl_xor(s2, 1, 64);
   if (!live) return;
-  uint8_t* base = codes + row * (long)(2 * K) + 128 * (j >> 1) + 32 * (j & 1);
-  *(u32x4*)(base) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  *(u32x4*)(base + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
-  *(u32x4*)(base + 64) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-  *(u32x4*)(base + 80) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  uint8_t* chunk = codes + row * (long)(2 * K) + 128 * (j >> 1);
+  store_term(chunk, 0, j & 1, hi);
+  store_term(chunk, 1, j & 1, lo);
   if ((j & 1) == 0) scales[row * (long)(K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
 }
 
@@ -157,17 +174,15 @@ __device__ __forceinline__ void split_image_rows(const char* img, int pitch, int
         v[8 * c + 2 * e + 1] = bf2f(w[e] >> 16);
       }
     }
-    uint32_t hi[8], lo[8];
+    uint32_t hi[6], lo[6];
     const uint32_t s1 = quant_term(v, hi);
     const uint32_t s2 = quant_term(v, lo);
     const uint32_t o1 = __shfl_xor(s1, 1, 64), o2 = __shfl_xor(s2, 1, 64);
     if (live) {
       const int j = c0 / 32 + jb;  // global 32-block
-      uint8_t* base = codes + (long)row * (2 * K) + 128 * (j >> 1) + 32 * (j & 1);
-      *(u32x4*)(base) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      *(u32x4*)(base + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
-      *(u32x4*)(base + 64) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      *(u32x4*)(base + 80) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+      uint8_t* chunk = codes + (long)row * (2 * K) + 128 * (j >> 1);
+      store_term(chunk, 0, j & 1, hi);
+      store_term(chunk, 1, j & 1, lo);
       if ((j & 1) == 0) scales[(long)row * (K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
     }
   }
@@ -242,13 +257,13 @@ __device__ __forceinline__ void mma_mx(const char* st, int s, f32x16 (&acc)[G::N
     for (int mb = 0; mb < G::MB; ++mb) {
       const int row = G::m_local(wm, mb) + r;
       const u32x4 a0 = *(const u32x4*)(sA + v2::koff<64>(row, 4 * t + h));
-      const u32x4 a1 = *(const u32x4*)(sA + v2::koff<64>(row, 4 * t + 2 + h));
-      const i32x8 xf = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      const u32x2 a1 = *(const u32x2*)(sA + v2::koff<64>(row, 4 * t + 2) + 8 * h);
+      const i32x8 xf = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
       const int xs = (int)(sAs[row] >> (8 * (2 * t + h)));
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb)
         acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[nb], xf, acc[nb][mb], 4 /* first: fp4 */,
-                                                                      0 /* second: fp8 */, 0, ws[nb], 0, xs);
+                                                                      2 /* second: fp6 E2M3 */, 0, ws[nb], 0, xs);
     }
 }
 

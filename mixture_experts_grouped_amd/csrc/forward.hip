@@ -711,7 +711,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2 * rank_blocks(a.r), KSPLIT), dim3(256), GS64::LDS_BYTES,
              st, a);
   MOE_LAUNCH(k_shrink_sum, dim3((unsigned)(((long)a.T * (2 * a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
-  if (a.mx) {  // x as its two-term E4M3 split for the scaled W13 GEMM
+  if (a.mx) {  // x as its two-term E2M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
     MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
                   a.XQ, a.XS, (long)a.T, a.H);

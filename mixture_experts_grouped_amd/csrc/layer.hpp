@@ -87,7 +87,7 @@ struct LayerArgs {
   _Float16* V;       // up pre-activation, same layout
   uint16_t* Hh;      // [cap, I]  silu(G) * V
   float* Z2;         // [cap, r]  s * A2_e h (scratch, forward only)
-  // MXFP4 base, forward scratch: the two-term E4M3 split of the base GEMMs'
+  // MXFP4 base, forward scratch: the two-term E2M3 split of the base GEMMs'
   // activations (engine_mx.hpp): codes [rows, 2K bytes], scale words [rows, K/64]
   uint8_t* XQ;       // x:  [T, 2H bytes]
   uint32_t* XS;      //     [T, H/64]
@@ -198,7 +198,7 @@ hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, lon
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
                              int32_t* err, const PoolRoots& pr, hipStream_t st);
 hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
-// two-term E4M3 split of bf16 rows [rows, K] (engine_mx.hpp storage)
+// two-term E2M3 split of bf16 rows [rows, K] (engine_mx.hpp storage)
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
                              hipStream_t st);
 // [B, R, C] -> [B, C, R] bf16 bits

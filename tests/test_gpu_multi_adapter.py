@@ -117,9 +117,9 @@ def test_multi_adapter_mxfp4_base_matches_serial_calls():
     Hn.log(f"[multi] mxfp4: roots={roots}")
     res = Hn.GpuRun(shape, case, mx=mx, roots=roots).run()
     # against the native-boundary oracle on the dequantised weights (the
-    # activations entering the two base products as their two-term E4M3 split)
+    # activations entering the two base products as their two-term E2M3 split)
     ref_case = dict(case, W13=deq["W13"], W2=deq["W2"])
-    ref_out, ref_g = _oracle(ref_case, roots, shape.scale, act_split="e4m3x2")
+    ref_out, ref_g = _oracle(ref_case, roots, shape.scale, act_split="e2m3x2")
     _compare(res, ref_out, ref_g, roots, "mx-multi:")
     _bitwise_against_serial(res, case, shape, roots, mx=mx)
 

@@ -2,7 +2,7 @@
 axis): GPU parity of the native path.
 
 The forward runs both base GEMMs on the scaled fp8 x fp4 matrix cores, the
-activations (x into W13, h into W2) fed as a two-term E4M3 split; the
+activations (x into W13, h into W2) fed as a two-term E2M3 split; the
 low-rank paths stay bf16.  The backward's data gradients expand the packed
 weights to bf16 (exact).  Pins, in order of strength:
 - the split's codes and scale bytes, bit-exact against the oracle's split
@@ -35,7 +35,7 @@ pytestmark = pytest.mark.gpu
 
 MX_REL = 2e-2      # the MXFP4 gate against the full-precision oracle
 MX_COS = 0.9998    # ~ 1 - MX_REL^2 / 2
-SPLIT = "e4m3x2"
+SPLIT = "e2m3x2"
 
 CASES = {
     # small oracle shape, rank 8
@@ -65,30 +65,48 @@ def _both_oracles(res, case, shape, tag, log_every=0, **kw):
         Hn.assert_close(tag + "full:" + n, got, ref, cos_min=MX_COS, rel_max=MX_REL)
 
 
+def _unpack_codes(codes: np.ndarray, rows: int, K: int):
+    """The codes layout of moe_lora_split_e2m3x2 (include/moelora.h): per
+    64-element chunk, term t at byte 64t, the 32-block h as six little-endian
+    dwords (element i in bits 6i .. 6i+5), dwords 0-3 at 64t + 16h and 4-5 at
+    64t + 32 + 8h.  Returns the codes of both terms, [rows, K] each."""
+    c = codes.reshape(rows, K // 64, 2, 64)
+    out = []
+    for t in range(2):
+        terms = np.zeros((rows, K // 64, 2, 32), np.uint8)
+        for h in range(2):
+            words = np.concatenate([c[:, :, t, 16 * h:16 * h + 16], c[:, :, t, 32 + 8 * h:40 + 8 * h]], axis=-1)
+            bits = np.unpackbits(words, axis=-1, bitorder="little")  # 192 bits, element i at 6i
+            for i in range(32):
+                terms[:, :, h, i] = (bits[..., 6 * i:6 * i + 6] * (1 << np.arange(6))).sum(-1)
+        out.append(terms.reshape(rows, K))
+    return out
+
+
 def test_split_codes_bit_exact_against_oracle():
-    """moe_lora_split_e4m3x2 (the forward's activation split) against the
+    """moe_lora_split_e2m3x2 (the forward's activation split) against the
     oracle's split: codes and scale bytes identical, over rows of very
     different magnitudes, an all-zero block, a block spanning 2^-30 .. 1,
-    bf16 subnormals, and blocks whose maximum sits on 448 2^k and just above
-    1.75 2^k (the scale rule's boundaries)."""
+    bf16 subnormals, blocks whose maximum sits on 7.5 2^k and just above
+    1.875 2^k (the scale rule's boundaries), and values on E2M3 ties."""
     rng = np.random.default_rng(23)
     rows, K = 96, 512
     x = rng.standard_normal((rows, K)) * np.exp2(rng.integers(-30, 30, (rows, 1)))
     x[0, :32] = 0.0
     x[1, :32] = np.exp2(-np.arange(32.0))
     x[2, :64] = rng.standard_normal(64) * 2.0 ** -128           # bf16 subnormal range
-    x[3, :32] = np.linspace(-1, 1, 32) * 448 * 8; x[3, 5] = 448 * 8
-    x[4, :32] = 1.75 * np.exp2(3) * (1 + 2.0 ** -7) * np.sign(rng.standard_normal(32))
+    x[3, :32] = np.linspace(-1, 1, 32) * 7.5 * 8; x[3, 5] = 7.5 * 8
+    x[4, :32] = 1.875 * np.exp2(3) * (1 + 2.0 ** -7) * np.sign(rng.standard_normal(32))
+    x[5, :32] = (np.arange(32) % 16 + 0.5) / 8 * np.sign(rng.standard_normal(32)); x[5, 0] = 7.5  # ties of the step 1/8
     bits = I.f32_to_bf16_bits(x.astype(np.float32))
     xb = I.bf16_bits_to_f32(bits).astype(np.float64)
     src = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    codes, words = B.moe_lora_split_e4m3x2(src)
+    codes, words = B.moe_lora_split_e2m3x2(src)
     torch.cuda.synchronize()
-    codes = codes.cpu().numpy()
+    codes = codes.cpu().numpy().view(np.uint8)
     words = words.cpu().numpy().view(np.uint32)
-    q1, s1, q2, s2, _ = OMX.split_e4m3x2(xb)
-    got_q1 = codes.reshape(rows, K // 64, 2, 64)[:, :, 0, :].reshape(rows, K)
-    got_q2 = codes.reshape(rows, K // 64, 2, 64)[:, :, 1, :].reshape(rows, K)
+    q1, s1, q2, s2, _ = OMX.split_e2m3x2(xb)
+    got_q1, got_q2 = _unpack_codes(codes, rows, K)
     sb = words.view(np.uint8).reshape(rows, K // 64, 4)
     got_s1, got_s2 = sb[:, :, :2].reshape(rows, K // 32), sb[:, :, 2:].reshape(rows, K // 32)
     for name, g, r in (("q1", got_q1, q1), ("q2", got_q2, q2), ("s1", got_s1, s1), ("s2", got_s2, s2)):
