@@ -124,17 +124,20 @@ typedef struct moe_pool {
  *   W13_scale, W2_scale: e8m0 block scales for MOE_BASE_MXFP4, NULL for bf16.
  *   W13T, W2T, W13P, W2P: optional transformed copies of the frozen base,
  *     written once by moe_lora_transform_base and reused by every call
- *     (PR #9 Summary: reusable transformed weights).  Each holds E x 2I x H
- *     (W13T, W13P) or E x H x I (W2T, W2P) bf16 values in a layout private to
+ *     (PR #9 Summary: reusable transformed weights), in a layout private to
  *     the library: the weight tiles of one GEMM pipeline stage stored as the
  *     bytes it loads, one stage after another, so that each stage reads one
- *     contiguous 32 KB block instead of a short run from each of 256 rows.
+ *     contiguous block (32 KB of bf16, or 9 KB of MXFP4 codes and scales)
+ *     instead of a short run from each of 256 rows.
  *       W13T, W2T: W13[e]^T, W2[e]^T for the backward's two data-gradient
- *         GEMMs (for an MXFP4 base, of the dequantised values); without them
- *         (NULL) the backward transposes W13 / W2 on the fly (an MXFP4 base
- *         also expanded to bf16).  The forward ignores them.
- *       W13P, W2P: W13, W2 for the forward's two base GEMMs (bf16 base only;
- *         with MOE_BASE_MXFP4 they must be NULL).  The backward ignores them.
+ *         GEMMs, E x 2I x H and E x H x I bf16 values (for an MXFP4 base, of
+ *         the dequantised values); without them (NULL) the backward
+ *         transposes W13 / W2 on the fly (an MXFP4 base also expanded to
+ *         bf16).  The forward ignores them.
+ *       W13P, W2P: W13, W2 for the forward's two base GEMMs: E x 2I x H and
+ *         E x H x I bf16 values; for MOE_BASE_MXFP4, E*2I*H*9/16 and
+ *         E*H*I*9/16 bytes (the e2m1 codes and e8m0 scales).  The backward
+ *         ignores them.
  *     Results are bitwise the same with or without any of them; their
  *     contents must come from moe_lora_transform_base on the same W13 / W2.
  *     Each may be given alone; 16-byte aligned. */
@@ -209,10 +212,11 @@ moe_status build_pool(const moe_lora_desc* desc, const int32_t* topk_idx, int32_
  * E*H*I bf16 values: the transposed weights for the backward; for
  * MOE_BASE_MXFP4 the dequantised weights e2m1 x 2^(e-127), exact in bf16,
  * read from the packed W13 / W2 and their scales, both required) and W13P,
- * W2P (the same sizes: the forward's weights, bf16 base only; non-NULL with
- * MXFP4 is MOE_ERR_INVALID).  Any output may be NULL (skipped); outputs are
- * 16-byte aligned device buffers that overlap no input and no other output.
- * Queued on `stream` like every call. */
+ * W2P (the forward's weights: the same sizes for a bf16 base; for
+ * MOE_BASE_MXFP4 E*2I*H*9/16 and E*H*I*9/16 bytes of codes and scales).
+ * Any output may be NULL (skipped); outputs are 16-byte aligned device
+ * buffers that overlap no input and no other output.  Queued on `stream`
+ * like every call. */
 moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_params* params, void* W13T,
                                    void* W2T, void* W13P, void* W2P, void* stream);
 
@@ -233,7 +237,8 @@ moe_status moe_lora_transform_base(const moe_lora_desc* desc, const moe_lora_par
  *     into six little-endian dwords (element i in bits 6i .. 6i+5), dwords
  *     0-3 at 64t + 16h and dwords 4-5 at 64t + 32 + 8h; bytes 64t + 48 ..
  *     64t + 63 are not written;
- *   scale_words [rows, K/64] uint32: per chunk, bytes {E1+127 of its first
+ *   scale_words [K/64, rows] uint32 (stage-major: the words of one chunk
+ *     for all rows are consecutive): per chunk, bytes {E1+127 of its first
  *     32-block, of its second, E2+127 of the first, of the second}.
  *   src, codes 16-byte aligned, scale_words 4-byte aligned, no overlaps. */
 moe_status moe_lora_split_e2m3x2(const void* src, int64_t rows, int32_t K, void* codes, void* scale_words,

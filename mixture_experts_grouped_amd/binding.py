@@ -266,8 +266,10 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc, na: Optional[i
     W13 uint8 [E, 2I, H/2] and W2 uint8 [E, H, I/2] packed e2m1 (element 2i in
     the low nibble of byte i), W13_scale uint8 [E, 2I, H/32], W2_scale uint8
     [E, H, I/32] e8m0.  Optional "W13T" [E, H, 2I] and "W2T" [E, I, H] bf16: the
-    transformed base (transform_base), read by the backward.  With na adapters
-    the six factors are stacked [na, ...]."""
+    transformed base (transform_base), read by the backward; optional "W13P",
+    "W2P": the forward's packed copies (bf16 [E, 2I, H] and [E, H, I], or for an
+    MXFP4 base uint8 of 9/16 byte per weight, see mx_packed_shapes).  With na
+    adapters the six factors are stacked [na, ...]."""
     E, H, I, r = desc.E, desc.H, desc.I, desc.rank
     bf = torch.bfloat16
     shapes = _factor_shapes(desc, na)
@@ -284,10 +286,27 @@ def _params_struct(p: Dict[str, torch.Tensor], desc: MoeLoraDesc, na: Optional[i
         s13 = s2 = None
     w13t = _ptr(p.get("W13T"), bf, (E, H, 2 * I), "W13T")
     w2t = _ptr(p.get("W2T"), bf, (E, I, H), "W2T")
-    w13p = _ptr(p.get("W13P"), bf, (E, 2 * I, H), "W13P")
-    w2p = _ptr(p.get("W2P"), bf, (E, H, I), "W2P")
+    w13p, w2p = _packed_ptrs(desc, p.get("W13P"), p.get("W2P"))
     return MoeLoraParams(w13, w2, s13, s2, ptrs["A1"], ptrs["A3"], ptrs["B1"], ptrs["B3"],
                          ptrs["A2"], ptrs["B2"], w13t, w2t, w13p, w2p)
+
+
+def mx_packed_shapes(desc: MoeLoraDesc):
+    """Storage shapes of the forward's packed copies of an MXFP4 base: per
+    expert, N tiles x K stages of 9216-byte stage tiles (256 rows of 32 code
+    bytes, then 256 scale words) -- W13P [E, 2I/256, H/64, 9216] and W2P
+    [E, H/256, I/64, 9216] uint8."""
+    E, H, I = desc.E, desc.H, desc.I
+    return (E, 2 * I // 256, H // 64, 9216), (E, H // 256, I // 64, 9216)
+
+
+def _packed_ptrs(desc: MoeLoraDesc, W13P, W2P):
+    E, H, I = desc.E, desc.H, desc.I
+    if desc.base_format == MOE_BASE_MXFP4:
+        s13, s2 = mx_packed_shapes(desc)
+        return _ptr(W13P, torch.uint8, s13, "W13P"), _ptr(W2P, torch.uint8, s2, "W2P")
+    bf = torch.bfloat16
+    return _ptr(W13P, bf, (E, 2 * I, H), "W13P"), _ptr(W2P, bf, (E, H, I), "W2P")
 
 
 def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
@@ -296,8 +315,9 @@ def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
                             stream=None) -> None:
     """The transformed base copies (any may be None): W13T, W2T for the
     backward (for an MXFP4 base of the dequantised weights) and W13P, W2P for
-    the forward (bf16 base only).  Library-private layouts of E x 2I x H and
-    E x H x I bf16 values (shapes below are storage only)."""
+    the forward.  Library-private layouts of E x 2I x H and E x H x I bf16
+    values, or for the forward copies of an MXFP4 base the byte tiles of
+    mx_packed_shapes (shapes are storage only)."""
     E, H, I = desc.E, desc.H, desc.I
     bf = torch.bfloat16
     if desc.base_format == MOE_BASE_MXFP4:
@@ -310,23 +330,26 @@ def moe_lora_transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor],
         pp = MoeLoraParams(_ptr(params["W13"], bf, (E, 2 * I, H), "W13"), _ptr(params["W2"], bf, (E, H, I), "W2"))
     st = library().moe_lora_transform_base(
         ctypes.byref(desc), ctypes.byref(pp), _ptr(W13T, bf, (E, H, 2 * I), "W13T"),
-        _ptr(W2T, bf, (E, I, H), "W2T"), _ptr(W13P, bf, (E, 2 * I, H), "W13P"), _ptr(W2P, bf, (E, H, I), "W2P"),
-        _stream(stream))
+        _ptr(W2T, bf, (E, I, H), "W2T"), *_packed_ptrs(desc, W13P, W2P), _stream(stream))
     _check(st, "moe_lora_transform_base")
 
 
 def transform_base(desc: MoeLoraDesc, params: Dict[str, torch.Tensor], stream=None,
                    forward: bool = True) -> Dict[str, torch.Tensor]:
     """Allocate and fill the transformed base copies -- W13T, W2T for the
-    backward, and (bf16 base, forward=True) W13P, W2P for the forward -- and
-    return them to merge into the params dict.  Redo it whenever W13 / W2
-    change (they are frozen in the side-LoRA setting)."""
+    backward, and (forward=True) W13P, W2P for the forward -- and return
+    them to merge into the params dict.  Redo it whenever W13 / W2 change
+    (they are frozen in the side-LoRA setting)."""
     E, H, I = desc.E, desc.H, desc.I
     dev = params["W13"].device
     bf = torch.bfloat16
     out = {"W13T": torch.empty(E, H, 2 * I, dtype=bf, device=dev),
            "W2T": torch.empty(E, I, H, dtype=bf, device=dev)}
-    if forward and desc.base_format != MOE_BASE_MXFP4:
+    if forward and desc.base_format == MOE_BASE_MXFP4:
+        s13, s2 = mx_packed_shapes(desc)
+        out["W13P"] = torch.empty(s13, dtype=torch.uint8, device=dev)
+        out["W2P"] = torch.empty(s2, dtype=torch.uint8, device=dev)
+    elif forward:
         out["W13P"] = torch.empty(E, 2 * I, H, dtype=bf, device=dev)
         out["W2P"] = torch.empty(E, H, I, dtype=bf, device=dev)
     moe_lora_transform_base(desc, params, out["W13T"], out["W2T"], out.get("W13P"), out.get("W2P"), stream)
@@ -437,12 +460,12 @@ def _sync(stream) -> None:
 
 def moe_lora_split_e2m3x2(src: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Two-term E2M3 split of bf16 rows src [rows, K] (see include/moelora.h):
-    returns (codes uint8 [rows, 2K], scale words int32 [rows, K/64])."""
+    returns (codes uint8 [rows, 2K], scale words int32 [K/64, rows], stage-major)."""
     if src.dim() != 2:
         raise ValueError("src must be [rows, K]")
     rows, K = src.shape
     codes = torch.empty(rows, 2 * K, dtype=torch.uint8, device=src.device)
-    scales = torch.empty(rows, K // 64, dtype=torch.int32, device=src.device)
+    scales = torch.empty(K // 64, rows, dtype=torch.int32, device=src.device)
     st = library().moe_lora_split_e2m3x2(_ptr(src, torch.bfloat16, None, "src"), rows, K,
                                          _ptr(codes, torch.uint8, None, "codes"),
                                          _ptr(scales, torch.int32, None, "scale_words"), _stream(stream))

@@ -225,8 +225,8 @@ moe_status check_params(const moe_lora_desc* d, const moe_lora_params* w) {
   // the dequantised weights)
   if ((w->W13T != nullptr && !aligned16(w->W13T)) || (w->W2T != nullptr && !aligned16(w->W2T)))
     return MOE_ERR_INVALID;
-  // packed forward copies: of a bf16 base only
-  if ((w->W13P != nullptr && (mx || !aligned16(w->W13P))) || (w->W2P != nullptr && (mx || !aligned16(w->W2P))))
+  // packed forward copies (bf16 stage tiles, or MXFP4 codes + scale words)
+  if ((w->W13P != nullptr && !aligned16(w->W13P)) || (w->W2P != nullptr && !aligned16(w->W2P)))
     return MOE_ERR_INVALID;
   return MOE_OK;
 }
@@ -654,14 +654,14 @@ moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params
   const size_t b13 = n13 * 2, b2 = n2 * 2;                                              // bf16 outputs
   const size_t in13 = mx ? n13 / 2 : b13, in2 = mx ? n2 / 2 : b2;                      // inputs
   if (mx && (params->W13_scale == nullptr || params->W2_scale == nullptr)) return MOE_ERR_INVALID;
-  if (mx && (W13P != nullptr || W2P != nullptr)) return MOE_ERR_INVALID;  // the MXFP4 forward reads e2m1
   if (!aligned16(params->W13) || !aligned16(params->W2)) return MOE_ERR_INVALID;
   // every output: aligned, and disjoint from the inputs and the other outputs
   const Range ins[] = {rng(params->W13, in13), rng(params->W2, in2),
                        rng(mx ? params->W13_scale : nullptr, mx ? n13 / 32 : 0),
                        rng(mx ? params->W2_scale : nullptr, mx ? n2 / 32 : 0)};
   void* outs[] = {W13T, W2T, W13P, W2P};
-  const size_t sizes[] = {b13, b2, b13, b2};
+  // the forward's copies of an MXFP4 base: 9 bytes per 16 weights (codes and scale words)
+  const size_t sizes[] = {b13, b2, mx ? n13 / 16 * 9 : b13, mx ? n2 / 16 * 9 : b2};
   for (int i = 0; i < 4; ++i) {
     if (outs[i] == nullptr) continue;
     if (!aligned16(outs[i])) return MOE_ERR_INVALID;
@@ -680,8 +680,10 @@ moe_status moe_lora_transform_base(const moe_lora_desc* d, const moe_lora_params
     e = launch_pack(2, w13, q13, params->W13_scale, (uint16_t*)W13T, d->E, d->H, d->I, s);
   if (e == hipSuccess && W2T != nullptr)
     e = launch_pack(3, w2, q2, params->W2_scale, (uint16_t*)W2T, d->E, d->H, d->I, s);
-  if (e == hipSuccess && W13P != nullptr) e = launch_pack(0, w13, nullptr, nullptr, (uint16_t*)W13P, d->E, d->H, d->I, s);
-  if (e == hipSuccess && W2P != nullptr) e = launch_pack(1, w2, nullptr, nullptr, (uint16_t*)W2P, d->E, d->H, d->I, s);
+  if (e == hipSuccess && W13P != nullptr)
+    e = launch_pack(mx ? 4 : 0, w13, q13, mx ? params->W13_scale : nullptr, (uint16_t*)W13P, d->E, d->H, d->I, s);
+  if (e == hipSuccess && W2P != nullptr)
+    e = launch_pack(mx ? 5 : 1, w2, q2, mx ? params->W2_scale : nullptr, (uint16_t*)W2P, d->E, d->H, d->I, s);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

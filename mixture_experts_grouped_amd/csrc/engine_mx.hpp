@@ -27,9 +27,13 @@
 //                      (KLoadA / KLoadS) and its swizzle carry it, and each
 //                      lane's six dwords are one 16-byte and one 8-byte read;
 //   activation scales  one 32-bit word: bytes {s1 b0, s1 b1, s2 b0, s2 b1}
-//                      for the chunk's two 32-blocks;
+//                      for the chunk's two 32-blocks, stored stage-major
+//                      ([K/64][rows]: the words of one chunk for all rows
+//                      are consecutive);
 //   weight codes       32 bytes at 32c of the packed row;
-//   weight scales      byte 2c + b of the row's scale bytes.
+//   weight scales      byte 2c + b of the row's scale bytes;
+//   or, from a packed copy of the weights (pack.hip kinds 4 and 5), each
+//   stage's 256 rows of codes and scale words as one 9 KB block.
 //
 // One stage = one k64 step: LDS [A 256 x 128 B | W 256 x 32 B | A scales
 // 256 x 4 B | W scales 256 x 4 B] = 42 KB, three stages in LDS (two in
@@ -38,6 +42,7 @@
 // the stage it is about to read.
 #pragma once
 #include "engine2.hpp"
+#include "layer.hpp"
 
 namespace moelora {
 namespace mx {
@@ -111,7 +116,7 @@ __device__ __forceinline__ void store_term(uint8_t* chunk, int t, int h, const u
 }
 
 // Rows of a bf16 [nrows, K] matrix -> codes [nrows, 2K bytes] and scale
-// words [nrows, K/64]; one thread per (row, 32-block), the threads of a row
+// words [K/64, nrows]; one thread per (row, 32-block), the threads of a row
 // adjacent (K % 64 == 0).
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
                                                     uint32_t* __restrict__ scales, long nrows, int K) {
@@ -145,17 +150,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
   uint8_t* chunk = codes + row * (long)(2 * K) + 128 * (j >> 1);
   store_term(chunk, 0, j & 1, hi);
   store_term(chunk, 1, j & 1, lo);
-  if ((j & 1) == 0) scales[row * (long)(K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
+  if ((j & 1) == 0) scales[(long)(j >> 1) * nrows + row] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
 }
 
 // The split of a tile of bf16 rows parked in LDS (an epilogue image: rows of
 // `pitch` bytes, COLS values from global column c0, a multiple of 64): the
 // codes and scale words of rows [0, nrows) go to codes / scales (those rows'
-// first elements; the global rows have 2K bytes and K/64 words).  The same
-// result as k_quant_rows on the stored rows.  All NT threads call it.
+// first elements; the global rows have 2K bytes, the scale words of chunk c
+// sit sld words after those of chunk c - 1).  The same result as
+// k_quant_rows on the stored rows.  All NT threads call it.
 template <int COLS, int NTH>
 __device__ __forceinline__ void split_image_rows(const char* img, int pitch, int nrows, uint8_t* codes,
-                                                 uint32_t* scales, int K, int c0) {
+                                                 uint32_t* scales, long sld, int K, int c0) {
   constexpr int BPR = COLS / 32;  // 32-blocks per image row (even)
   static_assert(BPR % 2 == 0 && (TM * BPR) % NTH == 0, "blocks of a chunk in neighbouring lanes");
 #pragma unroll
@@ -183,7 +189,7 @@ __device__ __forceinline__ void split_image_rows(const char* img, int pitch, int
       uint8_t* chunk = codes + (long)row * (2 * K) + 128 * (j >> 1);
       store_term(chunk, 0, j & 1, hi);
       store_term(chunk, 1, j & 1, lo);
-      if ((j & 1) == 0) scales[(long)row * (K / 64) + (j >> 1)] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
+      if ((j & 1) == 0) scales[(long)(j >> 1) * sld + row] = s1 | (o1 << 8) | (s2 << 16) | (o2 << 24);
     }
   }
 }
@@ -196,21 +202,28 @@ __device__ __forceinline__ void lds_load4(rsrc_t rs, char* lds_wave_base, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (v2::lds_void*)lds_wave_base, 4, off, soff, 0, 0);
 }
 
+// PK: the weight codes and scale words from a packed copy (pack.hip kinds 4,
+// 5: 9 KB stage tiles in order), else gathered from the packed rows and the
+// scale rows.  The activation scale words are stage-major in both.
+template <bool PK>
 struct WLoad {
-  rsrc_t rq, rs;     // packed weights (row pitch K/2 bytes), scale bytes (row pitch K/32)
-  uint32_t qoff;     // this lane's weight-tile slot: row 32 w + L/2, logical 16-byte chunk
-  rsrc_t ra;         // activation scale words
+  rsrc_t rq, rs;     // packed rows (row pitch K/2 bytes) and scale bytes (K/32); PK: rq = the copy
+  uint32_t qoff;     // this lane's weight-tile slot: row 32 w + L/2, logical 16-byte chunk (PK: 1024 w + 16 L)
+  uint32_t tile0;    // PK: byte offset of the N tile's first stage tile in the copy
+  rsrc_t ra;         // activation scale words, [K/64][arows]
+  uint32_t astage;   // bytes between two chunks' words of ra
   uint32_t soff;     // this lane's scale word (waves 0-3: activation rows, 4-7: weight rows)
   // tile row n of the weight tile reads packed row wrow(n); tile rows of the
   // activation side read scale-word row aoff(row) (byte offset of the row's
-  // word 0, OFF_NONE for no row)
+  // word of chunk 0, OFF_NONE for no row)
   template <class WROW, class AOFF>
   __device__ __forceinline__ void set(const uint8_t* wq, const uint8_t* ws, long wrows, int K, WROW wrow,
                                       const uint32_t* as, long arows, AOFF aoff) {
+    static_assert(!PK, "rows of the plain layout");
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     rq = make_rsrc(wq, (uint64_t)wrows * (K / 2));
     rs = make_rsrc(ws, (uint64_t)wrows * (K / 32));
-    ra = make_rsrc(as, (uint64_t)arows * (K / 64) * 4);
+    set_act(as, arows, K);
     const int n = 32 * w + (L >> 1);
     const int lc = (L & 1) ^ ((n >> 3) & 1);
     qoff = (uint32_t)wrow(n) * (uint32_t)(K / 2) + 16u * (uint32_t)lc;
@@ -219,16 +232,43 @@ struct WLoad {
     else
       soff = (uint32_t)wrow(64 * (w - 4) + L) * (uint32_t)(K / 32);
   }
+  // PK: the expert's copy (`bytes` long), N tile nt of a matrix with nst
+  // stages
+  template <class AOFF>
+  __device__ __forceinline__ void set_packed(const uint8_t* copy, uint64_t bytes, int nt, int nst, int K,
+                                             const uint32_t* as, long arows, AOFF aoff) {
+    static_assert(PK, "the packed copy");
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    rq = make_rsrc(copy, bytes);
+    set_act(as, arows, K);
+    tile0 = (uint32_t)nt * (uint32_t)nst * (uint32_t)MX_TILE;
+    qoff = 1024u * (uint32_t)w + 16u * (uint32_t)L;
+    soff = (w < 4) ? aoff(64 * w + L) : W_BYTES + 256u * (uint32_t)(w - 4) + 4u * (uint32_t)L;
+  }
+  __device__ __forceinline__ void set_act(const uint32_t* as, long arows, int K) {
+    ra = make_rsrc(as, (uint64_t)arows * (K / 64) * 4);
+    astage = (uint32_t)arows * 4u;
+  }
   // queue stage s (k = 64 s) into the stage buffer `st`
   __device__ __forceinline__ void issue(int s, char* st) const {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    v2::lds_load16(rq, st + A_BYTES + 1024 * w, qoff, 32u * (uint32_t)s);
-    if (w < 4)
-      lds_load4(ra, st + A_BYTES + W_BYTES + 256 * w, soff, 4u * (uint32_t)s);
-    else
-      lds_load4(rs, st + A_BYTES + W_BYTES + AS_BYTES + 256 * (w - 4), soff, 4u * (uint32_t)(s >> 1));
+    if constexpr (PK) {
+      const uint32_t t = __builtin_amdgcn_readfirstlane(tile0 + (uint32_t)s * (uint32_t)MX_TILE);
+      v2::lds_load16(rq, st + A_BYTES + 1024 * w, qoff, t);
+      if (w < 4)
+        lds_load4(ra, st + A_BYTES + W_BYTES + 256 * w, soff, astage * (uint32_t)s);
+      else
+        lds_load4(rq, st + A_BYTES + W_BYTES + AS_BYTES + 256 * (w - 4), soff, t);
+    } else {
+      v2::lds_load16(rq, st + A_BYTES + 1024 * w, qoff, 32u * (uint32_t)s);
+      if (w < 4)
+        lds_load4(ra, st + A_BYTES + W_BYTES + 256 * w, soff, astage * (uint32_t)s);
+      else
+        lds_load4(rs, st + A_BYTES + W_BYTES + AS_BYTES + 256 * (w - 4), soff, 4u * (uint32_t)(s >> 1));
+    }
   }
 };
+static_assert(MX_TILE == W_BYTES + WS_BYTES, "a packed stage tile is the weight part of an LDS stage");
 
 // One k64 step from stage buffer `st` (stage index s: which half of the
 // weight scale word).  G: the bf16 geometry whose accumulator layout the

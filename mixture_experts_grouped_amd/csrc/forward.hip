@@ -179,19 +179,21 @@ struct LdW13L {
   }
 };
 // MXFP4 base (engine_mx.hpp): the split activation rows (x by token, or h
-// by pool row), the packed weight tile and the scale rows of each k64
-// stage; with an extension (W13), its 32-k bf16 stages run first in the same
-// pipeline.
+// by pool row), the weight tile and the scale words of each k64 stage (PK:
+// from the packed copy); with an extension (W13), its 32-k bf16 stages run
+// after the base range.
+template <bool PK>
 struct LdMX {
   mx::KA xa;
-  mx::WLoad wl;
+  mx::WLoad<PK> wl;
   __device__ void issue(int s, char* st) const {
     xa.issue(64 * s, st);
     wl.issue(s, st);
   }
   __device__ void issue_ext(int, char*) const {}  // no extension stages (next = 0)
 };
-struct LdW13MX : LdMX {
+template <bool PK>
+struct LdW13MX : LdMX<PK> {
   mx::KE me;   // s A1 x, s A3 x (hi/lo) by token
   mx::KE2 ne;  // B1 rows (gate half of the tile), B3 rows (up half)
   int r;
@@ -208,14 +210,15 @@ static_assert(mx::LDS_BYTES <= GW13::LDS_BYTES, "the MX stages fit the bf16 pipe
 // one: both pre-activations are clipped).  Whether a value is clipped is
 // decided on its fp16 rounding, the value saved for the backward, so that
 // both passes take the same decision.
-// PK: the bf16 base read from its packed copy W13P (pack.hip, kind 0).
+// PK: the base read from its packed copy W13P (pack.hip, kind 0; MXFP4:
+// kind 4).
 // SK: 64-row parts of the pool tiles (GW13S; bf16 base): the grid is SUB
 // times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
 // tile's rows return at once.
 // LT: the large tile (GW13L; bf16 base) over the TML-row tile list.
 template <bool MX, int ACT, bool CL, bool PK, bool SK, bool LT>
 __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
-  static_assert(!(MX && PK) && !(MX && SK), "the packed copy and the small tiles are of a bf16 base");
+  static_assert(!(MX && SK), "the small tiles are of a bf16 base");
   static_assert(!(LT && (MX || SK)), "the large tile is of a bf16 base with full tiles");
   extern __shared__ __align__(16) char smem[];
   using G = typename std::conditional<SK, GW13S, typename std::conditional<LT, GW13L, GW13>::type>::type;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     // the base K range as k64 stages on the scaled matrix cores, then the
     // extension stages of 64 k (32 of the gate's 2r, 32 of the up's)
     using KE = mx::KE;
-    LdW13MX L;
+    LdW13MX<PK> L;
     L.r = r;
     {
       int tke[KE::NJ];
@@ -309,11 +312,15 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
     for (int j = 0; j < KE::NJ; ++j) L.ne.roff[j] = (uint32_t)((i0 + (KE::row_of(j) % HALF)) * r * 2);
     L.ne.window(2 * r, r, HALF, 2 * r);
     L.xa.from_tokens((const uint16_t*)a.XQ, a.T, a.H, tk);  // 2H bytes a row, like a bf16 row
-    const uint32_t sbytes = (uint32_t)(a.H / 64) * 4u;
-    L.wl.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2L * a.I, a.H, wrow,
-             a.XS, a.T, [&](int row) {
-               return row < nrows ? (uint32_t)(a.row2r[row0 + row] / a.k) * sbytes : OFF_NONE;
-             });
+    // the scale words of x are stage-major [H/64][T]: token t's at 4 t
+    auto xsw = [&](int row) { return row < nrows ? (uint32_t)(a.row2r[row0 + row] / a.k) * 4u : OFF_NONE; };
+    if constexpr (PK) {
+      const uint64_t bytes = (uint64_t)(2 * a.I / 256) * (a.H / 64) * MX_TILE;  // one expert's copy
+      L.wl.set_packed((const uint8_t*)a.W13P + e * bytes, bytes, nt, a.H / 64, a.H, a.XS, a.T, xsw);
+    } else {
+      L.wl.set(a.W13q + (long)e * 2 * a.I * (a.H / 2), a.W13s + (long)e * 2 * a.I * (a.H / 32), 2L * a.I, a.H, wrow,
+               a.XS, a.T, xsw);
+    }
     mx::run_mx<G>(L, (2 * r + 31) / 32, a.H / 64, acc, smem);
   }
   // G and V go out as fp16 in the accumulator-blocked layout (512 bytes per
@@ -378,8 +385,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   __syncthreads();
   ImgH::flush(smem, a.Hh + row0 * (long)a.I + i0, a.I, nrows);
   if constexpr (MX)  // the W2 GEMM's operand: the split of these bf16 rows of h
-    mx::split_image_rows<HALF, G::NT>(smem, ImgH::PITCH, nrows, a.HQ + row0 * (long)(2 * a.I),
-                                      a.HS + row0 * (long)(a.I / 64), a.I, i0);
+    mx::split_image_rows<HALF, G::NT>(smem, ImgH::PITCH, nrows, a.HQ + row0 * (long)(2 * a.I), a.HS + row0,
+                                      a.cap, a.I, i0);
 }
 
 // ----------------------------------------------------------------------------
@@ -506,13 +513,13 @@ struct LdW2 {
   }
 };
 
-// PK: the bf16 base read from its packed copy W2P (pack.hip, kind 1)
+// PK: the base read from its packed copy W2P (pack.hip, kind 1; MXFP4: kind 5)
 template <bool MX, bool PK, bool SK>
 // SK: 64-row parts of the pool tiles (GW2S, bf16 base): the grid is SUB
 // times larger and part `sub` takes rows row0 + 64 sub ..; parts past the
 // tile's rows return at once (bitwise the same as the full tile).
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
-  static_assert(!(MX && PK) && !(MX && SK), "the packed copy and the small parts are of a bf16 base");
+  static_assert(!(MX && SK), "the small parts are of a bf16 base");
   extern __shared__ __align__(16) char smem[];
   using G = typename std::conditional<SK, GW2S, GW2>::type;
   constexpr int SUB = TMG / G::TM;
@@ -552,13 +559,18 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
     v2::run_pingpong<G>(L, a.I / G::KT, acc, smem);
   } else {
     // MXFP4 base: h as its two-term split, W2 packed, on the scaled matrix cores
-    LdMX N;
+    LdMX<PK> N;
     N.xa.contig((const uint16_t*)a.HQ, ti.row0, nrows, a.I);  // 2I bytes a row, like a bf16 row
-    const uint32_t sbytes = (uint32_t)(a.I / 64) * 4u;
     const long e = grp_expert(a, ti.e);
-    N.wl.set(a.W2q + e * a.H * (a.I / 2), a.W2s + e * a.H * (a.I / 32), (long)a.H, a.I,
-             [&](int n) { return h0 + n; }, a.HS + (long)ti.row0 * (a.I / 64), (long)(nrows < G::TM ? nrows : G::TM),
-             [&](int row) { return row < nrows ? (uint32_t)row * sbytes : OFF_NONE; });
+    // the scale words of h are stage-major [I/64][cap]: pool row p's at 4 p
+    auto hsw = [&](int row) { return row < nrows ? (uint32_t)(ti.row0 + row) * 4u : OFF_NONE; };
+    if constexpr (PK) {
+      const uint64_t bytes = (uint64_t)(a.H / 256) * (a.I / 64) * MX_TILE;  // one expert's copy
+      N.wl.set_packed((const uint8_t*)a.W2P + e * bytes, bytes, nt, a.I / 64, a.I, a.HS, a.cap, hsw);
+    } else {
+      N.wl.set(a.W2q + e * a.H * (a.I / 2), a.W2s + e * a.H * (a.I / 32), (long)a.H, a.I,
+               [&](int n) { return h0 + n; }, a.HS, a.cap, hsw);
+    }
     mx::run_mx<G>(N, 0, a.I / 64, acc, smem);
   }
   using Img = v2::TileImage<G, G::TN, uint16_t>;
@@ -695,6 +707,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     set_w13_lds<false, false, false, true>(ai);
     set_w13_lds<false, true, false, true>(ai);
     set_w13_lds<true, false, false, false>(ai);
+    set_w13_lds<true, true, false, false>(ai);
     ai.lds((const void*)k_a2, GS128::LDS_BYTES);
     ai.lds((const void*)k_a2s, GA2S::LDS_BYTES);
     ai.lds((const void*)k_w2<false, false, false>, W2_LDS);
@@ -702,6 +715,7 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     ai.lds((const void*)k_w2<false, false, true>, W2S_LDS);
     ai.lds((const void*)k_w2<false, true, true>, W2S_LDS);
     ai.lds((const void*)k_w2<true, false, false>, W2_LDS);
+    ai.lds((const void*)k_w2<true, true, false>, W2_LDS);
     ai.lds((const void*)k_rank_combine, RK_LDS);
     return ai.err;
   });
@@ -717,11 +731,11 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
                   a.XQ, a.XS, (long)a.T, a.H);
   }
   {
-    const bool pk = a.W13P != nullptr;  // bf16 base only (checked on the host)
+    const bool pk = a.W13P != nullptr;
     if (a.mx && a.act == 1)
-      launch_w13_sk<true, 1, false>(a, st);
+      pk ? launch_w13_sk<true, 1, true>(a, st) : launch_w13_sk<true, 1, false>(a, st);
     else if (a.mx)
-      launch_w13_sk<true, 0, false>(a, st);
+      pk ? launch_w13_sk<true, 0, true>(a, st) : launch_w13_sk<true, 0, false>(a, st);
     else if (a.act == 1)
       pk ? launch_w13_sk<false, 1, true>(a, st) : launch_w13_sk<false, 1, false>(a, st);
     else
@@ -734,7 +748,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB, rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
   {
     const dim3 g(a.maxtiles * (a.H / GW2::TN)), gs(g.x * (TMG / GW2S::TM));
-    if (a.mx)
+    if (a.mx && a.W2P != nullptr)
+      MOE_LAUNCH_AS("k_w2", (k_w2<true, true, false>), g, dim3(GW2::NT), W2_LDS, st, a);
+    else if (a.mx)
       MOE_LAUNCH_AS("k_w2", (k_w2<true, false, false>), g, dim3(GW2::NT), W2_LDS, st, a);
     else if (a.small_tiles && a.W2P != nullptr)
       MOE_LAUNCH_AS("k_w2", (k_w2<false, true, true>), gs, dim3(GW2::NT), W2S_LDS, st, a);

@@ -206,6 +206,9 @@ hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, in
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
 // [nb, rs, cs] -> [nb, rd, cd] bf16, zero outside the source (pack.hip)
 hipError_t launch_pad(const uint16_t* src, uint16_t* dst, long nb, int rs, int cs, int rd, int cd, hipStream_t st);
+// bytes of one stage tile of an MXFP4 packed copy (kinds 4, 5 in pack.hip):
+// 256 rows x 32 code bytes, then 256 scale words
+constexpr int MX_TILE = 256 * 32 + 256 * 4;
 // packed stage tiles of the base (kinds in pack.hip)
 hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const uint8_t* sc, uint16_t* dst, int E,
                        int H, int I, hipStream_t st);

@@ -21,6 +21,14 @@
 //   kind 3  W2^T for the W2 data gradient: rows i, K = H    ([E][I/256][H/64])
 // Kinds 2 and 3 transpose through LDS; from an MXFP4 base they are the
 // dequantised values (e2m1 x 2^(e-127), exact in bf16).
+//   kind 4  an MXFP4 W13 for the forward's scaled GEMM (rows as kind 0,
+//           K = H), kind 5 an MXFP4 W2 (rows h, K = I): each stage tile of
+//           256 rows x 64 k is MX_TILE = 9 KB, [codes | scale words]: row n's
+//           32 code bytes of the stage at 32 n, its two 16-byte halves
+//           swapped when (n >> 3) & 1 (the LDS slots of mx::WLoad), then one
+//           32-bit word per row, the row's scale bytes 4 (s / 2) .. + 3 (the
+//           stage pair's four 32-blocks).  A stage is then 9 KB in order
+//           instead of 32 bytes and 4 bytes from each of 256 rows.
 #include "engine2.hpp"
 #include "layer.hpp"
 #include "trace.hpp"
@@ -94,11 +102,41 @@ __global__ __launch_bounds__(256) void k_pack_cols(const uint16_t* __restrict__ 
   }
 }
 
+// kinds 4, 5: [E][N/256][K/64] tiles of MX_TILE bytes from packed e2m1 rows
+// q4 [N, K/2] and scale rows sc [N, K/32] of each expert (N = 2I or H)
+__global__ __launch_bounds__(256) void k_pack_mx(const uint8_t* __restrict__ q4, const uint8_t* __restrict__ sc,
+                                                 uint8_t* __restrict__ dst, int kind, int N, int K, int I) {
+  const int nst = K / PK_KT, ntile = N / PK_ROWS;
+  const long b = blockIdx.x;
+  const int s = (int)(b % nst), t = (int)((b / nst) % ntile);
+  const long e = b / ((long)nst * ntile);
+  uint8_t* tile = dst + b * MX_TILE;
+  const uint8_t* q = q4 + e * (long)N * (K / 2);
+  const uint8_t* scl = sc + e * (long)N * (K / 32);
+  auto row_of = [&](int n) { return kind == 4 ? (n < 128 ? 128 * t + n : I + 128 * t + (n - 128)) : PK_ROWS * t + n; };
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int qi = threadIdx.x + 256 * u;  // 16-byte slot p of row n
+    const int n = qi / 2, p = qi % 2;
+    const int c = p ^ ((n >> 3) & 1);
+    *(u32x4*)(tile + 32 * n + 16 * p) = *(const u32x4*)(q + (long)row_of(n) * (K / 2) + 32 * s + 16 * c);
+  }
+  const int n = threadIdx.x;
+  const uint8_t* sb = scl + (long)row_of(n) * (K / 32) + 4 * (s / 2);  // scale rows need no alignment
+  *(uint32_t*)(tile + 32 * PK_ROWS + 4 * n) =
+      (uint32_t)sb[0] | ((uint32_t)sb[1] << 8) | ((uint32_t)sb[2] << 16) | ((uint32_t)sb[3] << 24);
+}
+
 // kind 0 / 1 from a bf16 base; kind 2 / 3 from a bf16 (q4 == nullptr) or an
-// MXFP4 base.  E experts of the kind's matrix.
+// MXFP4 base; kind 4 / 5 from an MXFP4 base (dst: bytes).  E experts of the
+// kind's matrix.
 hipError_t launch_pack(int kind, const uint16_t* src, const uint8_t* q4, const uint8_t* sc, uint16_t* dst, int E,
                        int H, int I, hipStream_t st) {
-  if (kind == 0 || kind == 1) {
+  if (kind == 4 || kind == 5) {
+    const int N = kind == 4 ? 2 * I : H, K = kind == 4 ? H : I;
+    const long tiles = (long)E * (N / PK_ROWS) * (K / PK_KT);
+    MOE_LAUNCH(k_pack_mx, dim3((unsigned)tiles), dim3(256), 0, st, q4, sc, (uint8_t*)dst, kind, N, K, I);
+  } else if (kind == 0 || kind == 1) {
     const int N = kind == 0 ? 2 * I : H, K = kind == 0 ? H : I;
     const long tiles = (long)E * (N / PK_ROWS) * (K / PK_KT);
     MOE_LAUNCH(k_pack_rows, dim3((unsigned)tiles), dim3(256), 0, st, src, dst, kind, N, K, I);

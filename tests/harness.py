@@ -194,8 +194,9 @@ class GpuRun:
                  clamp: float = 0.0, roots=None):
         """mx: MXFP4 base weights {W13, W13_scale, W2, W2_scale} (uint8 arrays);
         then case's W13/W2 are not uploaded.  base_grads: also request the
-        frozen-weight gradients dW13, dW2.  transformed: give the backward the
-        transformed base weights (W13T, W2T) written by moe_lora_transform_base.
+        frozen-weight gradients dW13, dW2.  transformed: give the layer the
+        transformed base weights written by moe_lora_transform_base (W13T, W2T
+        for the backward, W13P, W2P for the forward).
         clamp: the activation clamp c (0 = off).  roots: several adapters in
         one pass (the *_multi calls; case's six factors stacked per adapter)."""
         import torch
@@ -316,6 +317,32 @@ def packed_tiles(m: np.ndarray, gate_up: bool = False) -> np.ndarray:
     slot_chunk = np.arange(8)[None, :] ^ ((r ^ (r >> 3)) & 7)  # [r, slot] -> chunk
     g = np.take_along_axis(tl, slot_chunk[None, None, :, None, :, None], axis=4)
     return np.ascontiguousarray(g.transpose(0, 1, 3, 2, 4, 5)).reshape(E, N, K)
+
+
+def mx_packed_tiles(q: np.ndarray, sc: np.ndarray, gate_up: bool = False) -> np.ndarray:
+    """The library's packed forward copy of an MXFP4 weight stack -- codes q
+    [E, N, K/2] and scale bytes sc [E, N, K/32] (uint8) -- written out from its
+    documented layout: per expert, per N tile of 256 rows (gate_up: W13's
+    tiles, gate rows 128t.. then up rows I + 128t..), per stage s of 64 k, a
+    9216-byte tile: row n's 32 code bytes of the stage at 32n with its two
+    16-byte halves swapped when (n >> 3) & 1, then one little-endian word per
+    row: its scale bytes 4 (s // 2) .. + 3.  Returns [E, N/256, K/64, 9216]."""
+    E, N, KB = q.shape
+    K = 2 * KB
+    if gate_up:
+        I = N // 2
+        t = np.arange(I // 128)[:, None]
+        rows = np.concatenate([128 * t + np.arange(128), I + 128 * t + np.arange(128)], axis=1).ravel()
+        q, sc = q[:, rows], sc[:, rows]
+    nt, ns = N // 256, K // 64
+    codes = q.reshape(E, nt, 256, ns, 2, 16)                  # [E, nt, n, s, half, 16]
+    n = np.arange(256)
+    halves = np.stack([n >> 3 & 1, 1 - (n >> 3 & 1)], axis=1)  # [n, slot] -> half
+    codes = np.take_along_axis(codes, halves[None, None, :, None, :, None], axis=4)
+    codes = codes.transpose(0, 1, 3, 2, 4, 5).reshape(E, nt, ns, 256 * 32)
+    words = sc.reshape(E, nt, 256, K // 128, 4)[:, :, :, np.arange(ns) // 2, :]  # [E, nt, n, s, 4]
+    words = words.transpose(0, 1, 3, 2, 4).reshape(E, nt, ns, 256 * 4)
+    return np.ascontiguousarray(np.concatenate([codes, words], axis=-1))
 
 
 def same_bits(a, b) -> bool:

@@ -213,13 +213,16 @@ def test_transformed_base_checks_before_any_launch():
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 2 + 4096, None, None, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, fake * 8 + 1024, None, None, None) == B.MOE_ERR_INVALID
     assert lib.moe_lora_transform_base(byref(d), byref(base), None, None, None, None, None) == B.MOE_OK
-    # the forward copies: bf16 base only, disjoint from the other outputs
+    # the forward copies: disjoint from the inputs and the other outputs, aligned
     mxs = B.MoeLoraParams(fake * 2, fake * 3, fake * 4, fake * 4 + 65536, *([fake] * 6))
-    assert lib.moe_lora_transform_base(byref(dm), byref(mxs), None, None, fake * 8, None, None) == B.MOE_ERR_INVALID
+    assert lib.moe_lora_transform_base(byref(dm), byref(mxs), None, None, fake * 2 + 4096, None,
+                                       None) == B.MOE_ERR_INVALID  # MXFP4 W13P overlaps the packed W13
+    assert lib.moe_lora_transform_base(byref(dm), byref(mxs), None, None, fake * 8 + 8, None,
+                                       None) == B.MOE_ERR_INVALID  # misaligned
     assert lib.moe_lora_transform_base(byref(d), byref(base), fake * 8, None, fake * 9, None,
                                        None) == B.MOE_ERR_INVALID  # W13P overlaps W13T (2 MiB)
-    # a forward copy given with an MXFP4 base is refused by the layer calls too
-    prm_mx = B.MoeLoraParams(fake, fake, fake * 4, fake * 5, *([fake] * 6), None, None, fake * 9, None)
+    # a misaligned forward copy is refused by the layer calls too
+    prm_mx = B.MoeLoraParams(fake, fake, fake * 4, fake * 5, *([fake] * 6), None, None, fake * 9 + 8, None)
     assert lib.moe_lora_backward(byref(dm), byref(pool), fake, fake, byref(prm_mx), fake * 128, saved, fake * 64,
                                  fake * 200, byref(grads), fake * 256, scratch, None) == B.MOE_ERR_INVALID
 

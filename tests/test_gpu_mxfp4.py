@@ -104,10 +104,10 @@ def test_split_codes_bit_exact_against_oracle():
     codes, words = B.moe_lora_split_e2m3x2(src)
     torch.cuda.synchronize()
     codes = codes.cpu().numpy().view(np.uint8)
-    words = words.cpu().numpy().view(np.uint32)
+    words = words.cpu().numpy().view(np.uint32)  # stage-major [K/64, rows]
     q1, s1, q2, s2, _ = OMX.split_e2m3x2(xb)
     got_q1, got_q2 = _unpack_codes(codes, rows, K)
-    sb = words.view(np.uint8).reshape(rows, K // 64, 4)
+    sb = words.view(np.uint8).reshape(K // 64, rows, 4).transpose(1, 0, 2)
     got_s1, got_s2 = sb[:, :, :2].reshape(rows, K // 32), sb[:, :, 2:].reshape(rows, K // 32)
     for name, g, r in (("q1", got_q1, q1), ("q2", got_q2, q2), ("s1", got_s1, s1), ("s2", got_s2, s2)):
         bad = np.argwhere(g != r)

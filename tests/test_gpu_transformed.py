@@ -45,6 +45,46 @@ def test_transform_base_writes_the_packed_copies():
         assert np.array_equal(bits(t[n]).reshape(w.shape), w), n
 
 
+def test_transform_base_writes_the_mxfp4_forward_copies():
+    """The MXFP4 base's forward copies: codes and scale words of every stage
+    tile, bit for bit (layout restated in tests/harness.py mx_packed_tiles),
+    and the backward's dequantised transposes beside them."""
+    import torch
+    from mixture_experts_grouped_amd import binding as B
+    E, H, Id = 3, 512, 256
+    d = B.make_desc(64, H, Id, E, 2, 8, base_format=B.MOE_BASE_MXFP4)
+    rng = np.random.default_rng(6)
+    case = {"W13": I.f32_to_bf16_bits(rng.standard_normal((E, 2 * Id, H)).astype(np.float32)),
+            "W2": I.f32_to_bf16_bits(rng.standard_normal((E, H, Id)).astype(np.float32))}
+    mx, deq = Hn.mxfp4_base(case)
+    p = {n: torch.from_numpy(np.ascontiguousarray(mx[n])).cuda() for n in mx}
+    t = B.transform_base(d, p)
+    torch.cuda.synchronize()
+    got = {n: t[n].cpu().numpy() for n in ("W13P", "W2P")}
+    want = {"W13P": Hn.mx_packed_tiles(mx["W13"], mx["W13_scale"], gate_up=True),
+            "W2P": Hn.mx_packed_tiles(mx["W2"], mx["W2_scale"])}
+    for n, w in want.items():
+        assert got[n].shape == w.shape and np.array_equal(got[n], w), n
+    bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    assert np.array_equal(bits(t["W13T"]).reshape(E, H, 2 * Id),
+                          Hn.packed_tiles(np.ascontiguousarray(deq["W13"].transpose(0, 2, 1))).reshape(E, H, 2 * Id))
+
+
+@pytest.mark.parametrize("name", ["r128_masked", "multi_tile", "geglu"])
+def test_mxfp4_transformed_base_is_bitwise_the_same(name):
+    """An MXFP4 base with its forward copies (W13P, W2P) and transposes gives
+    bit for bit what the plain MXFP4 layout gives."""
+    shape, key, mask, kw = CASES[name]
+    Hn.log(f"[transformed mxfp4] case={name} shape={shape}")
+    case = I.layer_inputs(shape, key, routing="softmax_topk", mask_prob=mask)
+    mx, _ = Hn.mxfp4_base(case)
+    plain = Hn.GpuRun(shape, case, mx=mx, **kw).run()
+    tw = Hn.GpuRun(shape, case, mx=mx, transformed=True, **kw).run()
+    keys = [k for k in plain if k != "device_error"]
+    for k in keys:
+        assert Hn.same_bits(plain[k], tw[k]), f"{name}:{k} differs with the transformed MXFP4 base"
+
+
 CASES = {
     "tiny": (I.Shape(T=256, H=512, I=256, E=16, topk=2, rank=8), (31,), 0.0, {}),
     "r128_masked": (I.Shape(T=300, H=512, I=512, E=8, topk=3, rank=128), (32,), 0.2, {}),
