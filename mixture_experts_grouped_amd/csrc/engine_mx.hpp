@@ -307,11 +307,18 @@ __device__ __forceinline__ void mma_mx(const char* st, int s, f32x16 (&acc)[G::N
     }
 }
 
+// Geometry of the MXFP4 base GEMMs: the 256 x 256 tile as eight waves of
+// 64 x 128 (two activation row blocks by four weight blocks).  Per k64 step
+// a wave reads 48 bytes a lane of activation codes per row block and 16 of
+// weight codes per weight block: the wider weight side reads 29 % fewer LDS
+// bytes per product than 128 x 64 waves (k_w13 2.68 -> 2.60 ms, k_w2 1.054
+// -> 1.031 ms at 98,304 rows with the packed weights).
+using GMX = v2::Geo2<2, 4, 4, 2, false, false, 64>;
 // Geometry of the low-rank extension stages that follow the base K range
-// (bf16, the W13 tile's geometry: 64 k a stage, the two halves of the N tile
+// (bf16, the same accumulators: 64 k a stage, the two halves of the N tile
 // contracting the two halves of the stage's k -- the SPLIT stages of the
 // bf16 engine; two 64 KB buffers).
-using GE = v2::Geo2<4, 2, 2, 4, false, false, 64>;
+using GE = GMX;
 static_assert(GE::NBUF * GE::STAGE <= LDS_BYTES + 2048, "the extension stages reuse the MX stage buffers");
 using KE = v2::KLoad<TM, 64, NW>;
 using KE2 = v2::KLoad<TM, 64, NW, true>;

@@ -221,7 +221,8 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   static_assert(!(MX && SK), "the small tiles are of a bf16 base");
   static_assert(!(LT && (MX || SK)), "the large tile is of a bf16 base with full tiles");
   extern __shared__ __align__(16) char smem[];
-  using G = typename std::conditional<SK, GW13S, typename std::conditional<LT, GW13L, GW13>::type>::type;
+  using G = typename std::conditional<
+      MX, mx::GMX, typename std::conditional<SK, GW13S, typename std::conditional<LT, GW13L, GW13>::type>::type>::type;
   static_assert(G::NT == GW13::NT && G::TN == GW13::TN, "same workgroup and N tile");
   using KL = typename LdW13Base<G>::KL;
   constexpr int TN = G::TN, HALF = TN / 2, SUB = LT ? 1 : TMG / G::TM;
@@ -521,7 +522,8 @@ template <bool MX, bool PK, bool SK>
 __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   static_assert(!(MX && SK), "the small parts are of a bf16 base");
   extern __shared__ __align__(16) char smem[];
-  using G = typename std::conditional<SK, GW2S, GW2>::type;
+  using G = typename std::conditional<MX, mx::GMX, typename std::conditional<SK, GW2S, GW2>::type>::type;
+  static_assert(G::NT == GW2::NT, "one workgroup size");
   constexpr int SUB = TMG / G::TM;
   const int ntn = a.H / G::TN;
   // part `sub` of pool tile work item b (SUB == 1: the block index itself)
