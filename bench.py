@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE side-LoRA F+B ms and grouped-GEMM TFLOP/s (64 experts, 98K rows, H4096)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0
 
 GEMM_KERNELS = ("k_shrink", "k_w13", "k_a2", "k_w2", "k_rank_combine", "k_q", "k_w2dgrad",
@@ -577,6 +578,23 @@ def main():
                     "traffic": stored_traffic(dom, args) if T == 16384 else None,
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "flops_per_launch": kfl[dom], "avg_ms": round(tot / n, 4)}
+    mx_forward = None
+    if mx and kernels:
+        # the forward's two base GEMMs on the scaled fp6 x fp4 matrix cores:
+        # their algorithmic rate, and the rate of the products issued (two
+        # activation terms per base product) against the dense fp4/fp6 peak
+        mx_forward = {}
+        base_fl = {"k_w13": 4.0 * M * H * Idim, "k_w2": 2.0 * M * H * Idim}
+        for nm, bfl in base_fl.items():
+            if nm not in kernels:
+                continue
+            n, tot = kernels[nm]
+            avg_s = tot / n * 1e-3
+            mx_forward[nm] = {"avg_ms": round(tot / n, 4),
+                              "algorithmic_tflops": round(kfl[nm] / avg_s / 1e12, 1),
+                              "issued_fp6xfp4_tflops": round(2 * bfl / avg_s / 1e12, 1),
+                              "peak": PEAK_FP4_TFLOPS,
+                              "frac_of_fp4_peak": round(2 * bfl / avg_s / 1e12 / PEAK_FP4_TFLOPS, 4)}
     cpu = None
     if not args.no_cpu_baseline and not mx and not args.base_grads and args.activation == "swiglu":
         cpu = cpu_baseline(shape, key, experts, shared, x_bits, go_bits, idx, w, args.cpu_seconds)
@@ -598,10 +616,11 @@ def main():
         "dtype": "mxfp4 x e2m3x2 fwd, bf16" if mx else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (("MXFP4 base (e2m1 + e8m0/32) on scaled MFMA, " if mx else "") +
+            "workload": (("MXFP4 base (e2m1 + e8m0/32) on scaled fp6 x fp4 MFMA, " if mx else "") +
                          (("base " + ("dequantised and " if mx else "") +
                            "held transposed in packed bf16 stage tiles for the backward" +
-                           ("" if mx else " and packed for the forward") + " (written once), ")
+                           (" and as packed MXFP4 stage tiles for the forward" if mx
+                            else " and packed for the forward") + " (written once), ")
                           if transformed else "") +
                          ("with dW13/dW2, " if args.base_grads else "") +
                          f"one EP4 rank's share on one GPU: {T} tokens x top-6 = {M} routed rows "
@@ -623,6 +642,7 @@ def main():
         "algorithmic_tflop_per_step": round((fwd_fl + bwd_fl) / 1e12, 4),
         "gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "roofline": roofline,
+        **({"mx_forward": mx_forward} if mx_forward else {}),
         "cpu_baseline": cpu,
         "kernels": per_kernel,
     }
