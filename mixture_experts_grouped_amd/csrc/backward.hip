@@ -239,7 +239,7 @@ __global__ __launch_bounds__(GW2D::NT) void k_w2dgrad(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W2D, mt, nt)) return;
+  if (!group_tile(a, a.tiles, TMG, b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(GW13D::NT) void k_w13dgrad(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W13D, mt, nt)) return;
+  if (!group_tile(a, a.tiles, TMG, b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;

@@ -421,34 +421,6 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   const int q = nblocks >> 3, rem = nblocks & 7;
   return x * q + (x < rem ? x : rem) + j;
 }
-// Logical tile L of an (nm x nn) grid, visited in groups of gm M tiles: inside
-// a group the M index runs fastest, so concurrent tiles share both the row
-// slabs (M) and the weight slabs (N) in L2.
-__device__ __forceinline__ void grouped_tile(int L, int nm, int nn, int gm, int& mt, int& nt) {
-  const int per = gm * nn;
-  const int g = L / per, r = L - g * per;
-  const int size = (nm - g * gm < gm) ? nm - g * gm : gm;
-  mt = g * gm + r % size;
-  nt = r / size;
-}
-
-// Workgroup b of a grid over (at most) maxtiles x nn tiles, of which the first
-// ntm M tiles are live: false for a dead workgroup; else the live tiles are
-// dealt so that each XCD owns a contiguous range of them, visited in groups of
-// gm M tiles.  The ranges are cut from the live count, not the grid size, so
-// every XCD gets the same share.  gm <= 0 keeps the plain row-major order.
-__device__ __forceinline__ bool live_tile(int b, int ntm, int nn, int gm, int& mt, int& nt) {
-  const int n = ntm * nn;
-  if (b >= n) return false;
-  if (gm <= 0) {
-    mt = b / nn;
-    nt = b - mt * nn;
-  } else {
-    grouped_tile(xcd_remap(b, n), ntm, nn, gm, mt, nt);
-  }
-  return true;
-}
-
 // Grouped-GEMM M tile: rows [row0, row_end) of expert e in the pool.
 struct TileInfo {
   int e, row0, row_end, pad;  // e: the tile's pool group (its expert, with several adapters its adapter too)

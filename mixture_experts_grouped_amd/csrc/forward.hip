@@ -232,8 +232,9 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, a.ntiles[LT ? 1 : 0], ntn, LT ? TILE_GM_W13L : TILE_GM_W13, mt, nt)) return;
-  const TileInfo ti = (LT ? a.tiles3 : a.tiles)[mt];
+  const TileInfo* tl = LT ? a.tiles3 : a.tiles;
+  if (!group_tile(a, tl, LT ? TML : TMG, b, a.ntiles[LT ? 1 : 0], ntn, TILE_GM, mt, nt)) return;
+  const TileInfo ti = tl[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
   const int nrows = ti.row_end - row0 < G::TM ? ti.row_end - row0 : G::TM;
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(GW2::NT) void k_w2(LayerArgs a) {
   const int b = SUB == 1 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(blockIdx.x % nb);
   const int sub = SUB == 1 ? 0 : __builtin_amdgcn_readfirstlane(blockIdx.x / nb);
   int mt, nt;
-  if (!live_tile(b, *a.ntiles, ntn, TILE_GM_W2, mt, nt)) return;
+  if (!group_tile(a, a.tiles, TMG, b, *a.ntiles, ntn, TILE_GM, mt, nt)) return;
   const TileInfo ti = a.tiles[mt];
   const int row0 = ti.row0 + sub * G::TM;
   if (row0 >= ti.row_end) return;
