@@ -33,6 +33,10 @@ CASES = {
                          tuple(range(0, 513, 32)), 0.2),
     "root_past_one_chunk": (I.Shape(T=1400, H=512, I=256, E=16, topk=2, rank=16, scale=1.0),
                             (0, 1100, 1400), 0.0),
+    # 800 routes per (expert, adapter) group: the W13 GEMM on 384-row tiles,
+    # in the pass and in each root's own call
+    "large_tiles_two_roots": (I.Shape(T=3200, H=512, I=256, E=4, topk=2, rank=16, scale=1.0),
+                              (0, 1600, 3200), 0.0),
 }
 
 
@@ -122,6 +126,10 @@ def test_multi_adapter_mxfp4_base_matches_serial_calls():
     ref_out, ref_g = _oracle(ref_case, roots, shape.scale, act_split="e2m3x2")
     _compare(res, ref_out, ref_g, roots, "mx-multi:")
     _bitwise_against_serial(res, case, shape, roots, mx=mx)
+    # with the packed MXFP4 forward copies and the transposed backward copies
+    tw = Hn.GpuRun(shape, case, mx=mx, roots=roots, transformed=True).run()
+    for n in [k for k in res if k != "device_error"]:
+        assert Hn.same_bits(res[n], tw[n]), f"mx-multi transformed: {n}"
 
 
 def test_single_root_is_the_single_adapter_call():
