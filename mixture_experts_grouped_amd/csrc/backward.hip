@@ -620,10 +620,11 @@ struct LdP {
 
 __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int mt = blockIdx.x / P13_SUB, which = blockIdx.y & 1, c0 = RBLK * (blockIdx.y >> 1);  // rank block c0..
-  if (mt >= *a.ntiles) return;
+  int mt, sub, y;
+  if (!sub_tile(a, P13_SUB, mt, sub, y)) return;
+  const int which = y & 1, c0 = RBLK * (y >> 1);  // rank block c0..
   const TileInfo ti = a.tiles[mt];
-  const long row0 = ti.row0 + (long)(blockIdx.x % P13_SUB) * GS128::TM;  // this sub-tile's rows
+  const long row0 = ti.row0 + (long)sub * GS128::TM;  // this sub-tile's rows
   if (row0 >= ti.row_end) return;
   const int r = a.r;
   LdP L;

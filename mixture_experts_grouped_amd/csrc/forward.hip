@@ -397,12 +397,12 @@ __global__ __launch_bounds__(GW13::NT) void k_w13(LayerArgs a) {
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_a2(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int mt = blockIdx.x / A2_SUB;
-  if (mt >= *a.ntiles) return;
+  int mt, sub, y;
+  if (!sub_tile(a, A2_SUB, mt, sub, y)) return;
   const TileInfo ti = a.tiles[mt];
-  const long row0 = ti.row0 + (long)(blockIdx.x % A2_SUB) * GS128::TM;  // this sub-tile's rows
+  const long row0 = ti.row0 + (long)sub * GS128::TM;  // this sub-tile's rows
   if (row0 >= ti.row_end) return;
-  const int c0 = RBLK * blockIdx.y;  // rank block
+  const int c0 = RBLK * y;  // rank block
   const uint16_t* A2e = a.A2 + (grp_local(a, ti.e) * a.r + c0) * a.I;
   LdPlain<GS128::TM> L;
   L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
@@ -451,12 +451,12 @@ __global__ __launch_bounds__(GA2S::NT) void k_a2s(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   using G = GA2S;
   constexpr int SUB = TMG / G::TM;
-  const int mt = blockIdx.x / SUB;
-  if (mt >= *a.ntiles) return;
+  int mt, sub, y;
+  if (!sub_tile(a, SUB, mt, sub, y)) return;
   const TileInfo ti = a.tiles[mt];
-  const long row0 = ti.row0 + (long)(blockIdx.x % SUB) * G::TM;  // this part's rows
+  const long row0 = ti.row0 + (long)sub * G::TM;  // this part's rows
   if (row0 >= ti.row_end) return;
-  const int c0 = RBLK * blockIdx.y;  // rank block
+  const int c0 = RBLK * y;  // rank block
   LdA2S L;
   L.m.contig(a.Hh, row0, ti.row_end - row0, a.I);
   L.m.window(a.I);

@@ -149,6 +149,25 @@ __device__ __forceinline__ bool group_tile(const LayerArgs& a, const TileInfo* t
   return true;
 }
 
+// Grids of nsub sub-tiles per M tile along x (at most maxtiles M tiles) and
+// column blocks along y, whose workgroups of one pool group all read that
+// group's rank-r factor slice: the live workgroups (the first ntiles x nsub
+// x gridDim.y in dispatch order, x fastest) are dealt so that each XCD owns a
+// contiguous range of the order (y, M tile, sub-tile), so one group's slice
+// is fetched from HBM by about one XCD instead of by all eight.  False for a
+// dead workgroup.  (Wave-uniform.)
+__device__ __forceinline__ bool sub_tile(const LayerArgs& a, int nsub, int& mt, int& sub, int& y) {
+  const int nx = *a.ntiles * nsub, n = nx * (int)gridDim.y;
+  const int b = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  if (b >= n) return false;
+  const int L = xcd_remap(b, n);
+  y = L / nx;
+  const int x = L - y * nx;
+  mt = x / nsub;
+  sub = x - mt * nsub;
+  return true;
+}
+
 // Pool group g -> its expert (base weights), its adapter, and the index
 // q * E + e of its expert-local factors in their [na, E, ...] stacks.
 __device__ __forceinline__ int grp_expert(const LayerArgs& a, int g) { return a.na == 1 ? g : g / a.na; }
