@@ -125,6 +125,19 @@ int64_t capacity_of(const moe_lora_desc* d, int bm, int na = 1) {
   return routes + std::min<int64_t>((int64_t)d->E * na, routes) * (bm - 1);
 }
 
+// At most 48 routes per (expert, adapter) group on average (bf16 base): most
+// groups then fit one 64-row part, so the base GEMMs take 64-row parts (a
+// larger group re-reads its weights per part).
+bool small_tiles_of(const moe_lora_desc* d, int na) {
+  return d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)48 * d->E * na;
+}
+
+// At most half as many routes as (expert, adapter) groups: the P product
+// reads B1_e^T, B3_e^T copied for the groups that hold rows.
+bool few_routes_of(const moe_lora_desc* d, int na) {
+  return 2 * (int64_t)d->T * d->topk <= (int64_t)d->E * na;
+}
+
 struct Plan {
   int64_t cap;
   int maxtiles, maxtiles3, nsplit;
@@ -132,7 +145,7 @@ struct Plan {
   // byte offsets
   size_t o_status, o_tiles, o_tiles3, o_ntiles, o_Xs, o_ZA, o_G, o_V, o_Hh, o_Z2, o_Yb, o_zc;
   size_t o_XQ, o_XS, o_HQ, o_HS;
-  size_t o_fac, o_gfac, o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T;
+  size_t o_fac, o_gfac, o_zsp, o_qp, o_q, o_sq, o_wsq, o_dGV, o_dU, o_P, o_pc, o_part, o_ZAp, o_dwp, o_A2T, o_A1T, o_A3T, o_B1T, o_B3T;
 };
 
 Plan make_plan(const moe_lora_desc* d, const Roots& R) {
@@ -189,6 +202,9 @@ Plan make_plan(const moe_lora_desc* d, const Roots& R) {
   p.o_A2T = take(na * d->E * I * r * 2);  // A2_e^T per adapter, with transformed base weights
   p.o_A1T = take(na * H * r * 2);         // A1^T, A3^T per adapter for the grad-x rank product
   p.o_A3T = take(na * H * r * 2);
+  const size_t nbt = few_routes_of(d, R.na) ? na * d->E * I * r * 2 : 0;
+  p.o_B1T = take(nbt);  // B1_e^T, B3_e^T for the few-route P product
+  p.o_B3T = take(nbt);
   // forward-only tensors share space with backward-only ones: the base
   // outputs and Z2 are read only by the forward's combine
   p.o_Yb = p.o_dU;  // [cap, H] bf16, same size
@@ -240,9 +256,8 @@ void fill_common(LayerArgs& a, const moe_lora_desc* d, const moe_pool* pool, con
   a.E = d->E;
   a.na = R.na;
   a.EV = d->E * R.na;
-  // at most 48 routes per (expert, adapter) group on average: most groups
-  // then fit one 64-row part (a larger group re-reads its weights per part)
-  a.small_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk <= (int64_t)48 * a.EV;
+  a.small_tiles = small_tiles_of(d, R.na);
+  a.few_routes = few_routes_of(d, R.na);
   // at least 768 routes per group on average: the TML-row tiles then pad
   // little more than TMG-row ones
   a.large_tiles = d->base_format == MOE_BASE_BF16 && (int64_t)d->T * d->topk >= (int64_t)768 * a.EV;
@@ -313,6 +328,8 @@ void fill_scratch(LayerArgs& a, const Plan& p, void* base) {
   a.Yb = (uint16_t*)(b + p.o_Yb);
   a.dwp = (float*)(b + p.o_dwp);
   a.A2T = (uint16_t*)(b + p.o_A2T);
+  a.B1T = (uint16_t*)(b + p.o_B1T);
+  a.B3T = (uint16_t*)(b + p.o_B3T);
   a.A1T = (uint16_t*)(b + p.o_A1T);
   if (a.mx) {
     a.XQ = (uint8_t*)(b + p.o_XQ);

@@ -14,7 +14,8 @@
 //                   s w q_t per route for dA2
 //   k_w13dgrad      dU = W1_e^T dg + W3_e^T dv
 //   (with the transformed base both dgrads read the weights as K tiles)
-//   k_p13           P = [B1_e^T dg ; B3_e^T dv]
+//   k_p13           P = [B1_e^T dg ; B3_e^T dv] (at most half as many routes
+//                   as pool groups: k_p13s on B1_e^T, B3_e^T copied by k_transpose)
 //   k_pc            pc_t = s sum_j P_(t,j)
 //   k_rank_dx       grad_x_t = [A1; A3]^T pc_t + sum_j dU_(t,j)
 //   k_wgrad_local   dB1_e, dB3_e, dA2_e: K-grouped over the expert's rows
@@ -654,6 +655,65 @@ __global__ __launch_bounds__(256) void k_p13(LayerArgs a) {
   }
 }
 
+// At most half as many routes as pool groups (a few tokens): 64-row parts on
+// the direct-load engine with four stage buffers (three stages queued), as
+// k_a2s does for Z2, so the long K = I contraction is not bound by one load
+// latency per stage.  The weight operand is B1_e^T / B3_e^T (K = I
+// contiguous), transposed per call for the groups that hold rows (a cost that
+// grows with them: at T = 90 on 64 experts the copies took longer than the
+// faster product saved); the LDS tiles then hold what k_p13's transposing
+// loads produce, and each element sums the same products in the same order.
+using GP13S = v2::Geo2<1, 2, 2, 2, false, false, 64, 4>;  // 64 x 128, four waves
+struct LdP13S {
+  using KM = v2::KLoad<GP13S::TM, GP13S::KT, GP13S::NW>;  // dg or dv rows
+  using KN = v2::KLoad<128, GP13S::KT, GP13S::NW>;        // B1_e^T or B3_e^T rows
+  static constexpr int INSTS = KM::NJ + KN::NJ;
+  KM m;
+  KN n;
+  __device__ void issue(int s, char* sM, char* sN) {
+    m.issue(s * GP13S::KT, 0, false, sM);
+    n.issue(s * GP13S::KT, 0, false, sN);
+  }
+};
+
+__global__ __launch_bounds__(GP13S::NT) void k_p13s(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  using G = GP13S;
+  constexpr int SUB = TMG / G::TM;
+  int mt, sub, y;
+  if (!sub_tile(a, SUB, mt, sub, y)) return;
+  const int which = y & 1, c0 = RBLK * (y >> 1);  // rank block c0..
+  const TileInfo ti = a.tiles[mt];
+  const long row0 = ti.row0 + (long)sub * G::TM;  // this part's rows
+  if (row0 >= ti.row_end) return;
+  const int r = a.r;
+  LdP13S L;
+  L.m.contig(a.dGV + which * a.I, row0, ti.row_end - row0, 2 * a.I);
+  L.m.window(a.I);
+  L.n.contig((which ? a.B3T : a.B1T) + (grp_local(a, ti.e) * r + c0) * a.I, 0, r - c0, a.I);
+  L.n.window(a.I);
+  f32x16 acc[G::NB][G::MB];
+  zero_acc<G>(acc);
+  v2::run_stages2<G, 0>(L, a.I / G::KT, acc, smem);
+  Epi<G> ep;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const long row = row0 + ep.row(mb);
+    if (row >= ti.row_end) continue;
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = c0 + ep.col(nb, g);
+        if (c >= r) continue;
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[nb][mb][4 * g + q];
+        *(f32x4*)(a.P + row * 2 * r + which * r + c) = v;
+      }
+  }
+}
+
 // pc_t = s * sum_j P_(t,j), written as hi/lo [pc1 hi | pc1 lo | pc3 hi | pc3 lo].
 // One thread per token and 4 columns (never straddling pc1 / pc3, r % 8 ==
 // 0): the token's route indices first, then one 16-byte P load per live
@@ -1007,9 +1067,20 @@ __global__ __launch_bounds__(GWG::NT) void k_wgrad_base(LayerArgs a, int which) 
 // A2T = A2_e^T for the transformed-weight W2 dgrad.  16-byte row accesses
 // where the row is whole, element accesses at ragged edges.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t* dst, int R, int C) {
+// A second pair (src2, dst2) of the same shape is done by the same launch
+// (grid z 2B).  With counts, matrix b = q E + e of an [na, E, ...] stack is
+// skipped when its pool group e na + q holds no rows (nothing reads its copy).
+__global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t* dst, const uint16_t* src2,
+                                                   uint16_t* dst2, int B, int R, int C, const int32_t* counts,
+                                                   int na, int E) {
   __shared__ uint16_t t[64][72];  // padded rows: 144 bytes, keeps the 16-byte writes aligned
-  const long b = blockIdx.z;
+  long b = blockIdx.z;
+  if (b >= B) {
+    b -= B;
+    src = src2;
+    dst = dst2;
+  }
+  if (counts != nullptr && counts[(b % E) * na + b / E] == 0) return;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   src += b * (long)R * C;
   dst += b * (long)R * C;
@@ -1044,9 +1115,13 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* src, uint16_t
 }
 
 
-hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st) {
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st,
+                            const int32_t* counts, int na, int E, const uint16_t* src2, uint16_t* dst2) {
   if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  MOE_LAUNCH(k_transpose, dim3((C + 63) / 64, (R + 63) / 64, B), dim3(256), 0, st, src, dst, R, C);
+  if (counts != nullptr && (E <= 0 || B != na * E)) return hipErrorInvalidValue;
+  const unsigned nz = (unsigned)B * (src2 != nullptr ? 2u : 1u);
+  MOE_LAUNCH(k_transpose, dim3((C + 63) / 64, (R + 63) / 64, nz), dim3(256), 0, st, src, dst, src2, dst2, B, R, C,
+             counts, na, E);
   return hipGetLastError();
 }
 
@@ -1094,6 +1169,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     ai.lds((const void*)k_w13dgrad<false, true, false>, W13D_LDS);
     ai.lds((const void*)k_w13dgrad<false, true, true>, W13DS_LDS);
     ai.lds((const void*)k_p13, GS128::LDS_BYTES);
+    ai.lds((const void*)k_p13s, GP13S::LDS_BYTES);
     ai.lds((const void*)k_rank_dx, RK_LDS);
     ai.lds((const void*)k_wgrad_local, WG_LDS);
     ai.lds((const void*)k_wgrad_base, WG_LDS);
@@ -1132,12 +1208,19 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     else
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }
-  MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2 * rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
+  if (a.few_routes) {
+    const hipError_t e =
+        launch_transpose(a.B1, a.B1T, a.na * a.E, a.I, a.r, st, a.counts, a.na, a.E, a.B3, a.B3T);
+    if (e != hipSuccess) return e;
+    MOE_LAUNCH(k_p13s, dim3(a.maxtiles * (TMG / GP13S::TM), 2 * rank_blocks(a.r)), dim3(GP13S::NT),
+               GP13S::LDS_BYTES, st, a);
+  } else {
+    MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2 * rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
+  }
   const long npc = (long)a.T * (2 * a.r / 4);
   MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
   {
-    hipError_t e = launch_transpose(a.A1, a.A1T, a.na, a.r, a.H, st);
-    if (e == hipSuccess) e = launch_transpose(a.A3, a.A3T, a.na, a.r, a.H, st);
+    const hipError_t e = launch_transpose(a.A1, a.A1T, a.na, a.r, a.H, st, nullptr, 1, 0, a.A3, a.A3T);
     if (e != hipSuccess) return e;
   }
   MOE_LAUNCH(k_rank_dx, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);

@@ -59,6 +59,8 @@ struct LayerArgs {
   int small_tiles;
   // many rows per pool group (bf16 base): the W13 GEMM takes TML-row tiles
   int large_tiles;
+  // at most half as many routes as pool groups: the P product takes k_p13s
+  int few_routes;
   // pool
   const int32_t* counts;
   const int32_t* offsets;
@@ -117,6 +119,7 @@ struct LayerArgs {
   float* dwp;        // [I/256, cap] router-gradient partials of the W2 dgrad's column tiles
   uint16_t* A2T;     // [na, E, I, r]  A2_e^T (backward scratch, with W2T only)
   uint16_t *A1T, *A3T;  // [na, H, r]  A1^T, A3^T (backward scratch)
+  uint16_t *B1T, *B3T;  // [na, E, r, I]  B1_e^T, B3_e^T of the groups with rows (few_routes only)
   int nsplit, kspl;
   // backward outputs
   uint16_t* gx;
@@ -250,7 +253,9 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
                              hipStream_t st);
 // [B, R, C] -> [B, C, R] bf16 bits
-hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st);
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t st,
+                            const int32_t* counts = nullptr, int na = 1, int E = 0,
+                            const uint16_t* src2 = nullptr, uint16_t* dst2 = nullptr);
 hipError_t launch_backward(const LayerArgs& a, hipStream_t st);
 // [nb, rs, cs] -> [nb, rd, cd] bf16, zero outside the source (pack.hip)
 hipError_t launch_pad(const uint16_t* src, uint16_t* dst, long nb, int rs, int cs, int rd, int cd, hipStream_t st);
