@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoelora.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["pool.hip", "forward.hip", "backward.hip", "pack.hip", "api.hip", "trace.hip"]
+SOURCES = ["pool.hip", "forward.hip", "backward.hip", "pack.hip", "api.hip", "trace.hip", "branch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -469,7 +469,7 @@ moe_status forward_checked(const moe_lora_desc* d, const moe_adapters* ad, const
   a.w = topk_w;
   a.out = (uint16_t*)out;
   hipError_t e = pad_factors(a, d, p, R.na, sc, (hipStream_t)stream);
-  if (e == hipSuccess) e = launch_forward(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_forward(a, (hipStream_t)stream, !noalloc);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -1177,6 +1177,28 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     return ai.err;
   });
   if (ierr != hipSuccess) return ierr;
+  // Two streams: the branch gathers ZA to pool order and copies the rank
+  // factors' transposes while the caller's stream runs q and the W2 dgrad;
+  // once dG, dV and s w q exist the branch computes P, pc and the adapter
+  // gradients while the caller's stream runs the W13 dgrad, then grad-x
+  // (after pc); the optional frozen-weight gradients follow the join.  With
+  // 768 or more routes per pool group the W13 dgrad fills the device alone
+  // (the concurrent branch slowed the backward at the production share,
+  // 5.81 -> 5.88 ms, same box), so that second part stays on the caller's
+  // stream.
+  Branch br;
+  hipError_t e = br.open(st, true);
+  if (e != hipSuccess) return e;
+  const hipStream_t sd = br.side();
+  const bool deep = (long)a.T * a.k >= 768L * a.EV;
+  const hipStream_t sp = deep ? st : sd;  // stream of P, pc and the adapter gradients
+  const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
+  MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, sd, a);
+  if ((e = launch_transpose(a.A1, a.A1T, a.na, a.r, a.H, sd, nullptr, 1, 0, a.A3, a.A3T)) != hipSuccess) return e;
+  if (a.few_routes &&
+      (e = launch_transpose(a.B1, a.B1T, a.na * a.E, a.I, a.r, sd, a.counts, a.na, a.E, a.B3, a.B3T)) != hipSuccess)
+    return e;
+  if ((e = br.signal(sd, 3)) != hipSuccess) return e;  // ZA rows and the transposes written
   MOE_LAUNCH(k_q, dim3(token_tiles(a, GS64::TM), KSPLIT, rank_blocks(a.r)), dim3(256), GS64::LDS_BYTES, st, a);
   MOE_LAUNCH(k_q_sum, dim3((unsigned)(((long)a.T * (a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
   {
@@ -1184,8 +1206,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     const bool tw = a.W2T != nullptr;  // bf16 base, or the dequantised copy of an MXFP4 base
     if (tw && !a.small_tiles) {  // the small parts read A2 directly
       // A2T = A2_e^T per expert and adapter ([na, E, I, r]), the K-tile rank operand
-      const hipError_t e = launch_transpose(a.A2, a.A2T, a.na * a.E, a.r, a.I, st);
-      if (e != hipSuccess) return e;
+      if ((e = launch_transpose(a.A2, a.A2T, a.na * a.E, a.r, a.I, st)) != hipSuccess) return e;
     }
     if (tw)
       a.small_tiles ? launch_w2d_var<false, true, true>(a, grid, st) : launch_w2d_var<false, true, false>(a, grid, st);
@@ -1196,6 +1217,7 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
   }
   const long nr = (long)a.T * a.k, dw_per_block = 256 / DW_LANES;
   MOE_LAUNCH(k_dw, dim3((unsigned)((nr + dw_per_block - 1) / dw_per_block)), dim3(256), 0, st, a);
+  if ((e = br.signal(st, 1)) != hipSuccess) return e;  // dG, dV, s w q written
   {
     const dim3 grid(a.maxtiles * (a.H / GW13D::TN));
     if (a.W13T != nullptr && a.small_tiles)
@@ -1208,29 +1230,27 @@ hipError_t launch_backward(const LayerArgs& a, hipStream_t st) {
     else
       MOE_LAUNCH_AS("k_w13dgrad", (k_w13dgrad<false, false, false>), grid, dim3(GW13D::NT), W13D_LDS, st, a);
   }
-  if (a.few_routes) {
-    const hipError_t e =
-        launch_transpose(a.B1, a.B1T, a.na * a.E, a.I, a.r, st, a.counts, a.na, a.E, a.B3, a.B3T);
-    if (e != hipSuccess) return e;
+  // P, pc and the adapter gradients: on the branch once the W2 dgrad's
+  // outputs exist (event 1); deep, on the caller's stream once the branch's
+  // first part (ZA rows, transposes: event 3) is done
+  if ((e = br.await(sp, deep ? 3 : 1)) != hipSuccess) return e;
+  if (a.few_routes)
     MOE_LAUNCH(k_p13s, dim3(a.maxtiles * (TMG / GP13S::TM), 2 * rank_blocks(a.r)), dim3(GP13S::NT),
-               GP13S::LDS_BYTES, st, a);
-  } else {
-    MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2 * rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
-  }
+               GP13S::LDS_BYTES, sp, a);
+  else
+    MOE_LAUNCH(k_p13, dim3(a.maxtiles * P13_SUB, 2 * rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, sp, a);
   const long npc = (long)a.T * (2 * a.r / 4);
-  MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, st, a);
-  {
-    const hipError_t e = launch_transpose(a.A1, a.A1T, a.na, a.r, a.H, st, nullptr, 1, 0, a.A3, a.A3T);
-    if (e != hipSuccess) return e;
-  }
-  MOE_LAUNCH(k_rank_dx, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);
-  const long used_rows = a.cap;  // grid bound; rows past the pool's end return at once
-  MOE_LAUNCH(k_gather_za, dim3((unsigned)((used_rows + 3) / 4)), dim3(256), 0, st, a);
-  MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3 * rank_blocks(a.r)), dim3(GWG::NT), WG_LDS, st, a);
+  MOE_LAUNCH(k_pc, dim3((unsigned)((npc + 255) / 256)), dim3(256), 0, sp, a);
+  if ((e = br.signal(sp, 2)) != hipSuccess) return e;  // pc written (and A1^T, A3^T before it)
+  MOE_LAUNCH(k_wgrad_local, dim3(a.EV * (a.I / 256), 3 * rank_blocks(a.r)), dim3(GWG::NT), WG_LDS, sp, a);
   MOE_LAUNCH(k_wgrad_shared, dim3((a.H / 256) * a.nsplit, 3 * rank_blocks(a.r)), dim3(GWG::NT), GWG::LDS_BYTES,
-             st, a);
+             sp, a);
   const long nsh = (long)a.H * a.r;
-  MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3, a.na), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_reduce_shared, dim3((unsigned)((nsh + 255) / 256), 3, a.na), dim3(256), 0, sp, a);
+  if (!deep && (e = br.await(st, 2)) != hipSuccess) return e;
+  MOE_LAUNCH(k_rank_dx, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = br.close()) != hipSuccess) return e;
   if (a.dW13 != nullptr || a.dW2 != nullptr) {  // one adapter only (pool groups = experts)
     const unsigned prow = (unsigned)((a.cap + 3) / 4);  // rows past the pool's end return at once
     if (a.dW13 != nullptr) {

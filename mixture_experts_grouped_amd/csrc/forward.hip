@@ -24,7 +24,8 @@
 
 namespace moelora {
 
-hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st);
+hipError_t launch_tile_map(const LayerArgs& a, hipStream_t st);
+hipError_t launch_save_x(const LayerArgs& a, hipStream_t st);
 
 // thin GEMMs (N = r): smaller M tiles so the grid fills the 256 CUs
 using GS64 = Geo<1, 2, 2, 2>;   // 64 x 128 tile, wave 32 x 64
@@ -698,7 +699,7 @@ hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* cod
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
+hipError_t launch_forward(const LayerArgs& a, hipStream_t st, bool branch) {
   static PerDeviceOnce attrs;
   hipError_t err = attrs.run([] {
     AttrInit ai;
@@ -723,16 +724,25 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     return ai.err;
   });
   if (err != hipSuccess) return err;
-  err = launch_pool_prologue(a, st);
-  if (err != hipSuccess) return err;
+  // Two streams: the branch computes ZA (and an MXFP4 base's split of x)
+  // and the saved copy of x while the caller's stream builds the tile map;
+  // after the W13 GEMM the branch computes Z2 = s A2_e h and zc while the
+  // caller's stream runs the W2 GEMM; the combine follows the join.
+  Branch br;
+  if ((err = br.open(st, branch)) != hipSuccess) return err;
+  const hipStream_t sd = br.side();
   MOE_LAUNCH(k_shrink, dim3(token_tiles(a, GS64::TM), 2 * rank_blocks(a.r), KSPLIT), dim3(256), GS64::LDS_BYTES,
-             st, a);
-  MOE_LAUNCH(k_shrink_sum, dim3((unsigned)(((long)a.T * (2 * a.r / 4) + 255) / 256)), dim3(256), 0, st, a);
+             sd, a);
+  MOE_LAUNCH(k_shrink_sum, dim3((unsigned)(((long)a.T * (2 * a.r / 4) + 255) / 256)), dim3(256), 0, sd, a);
   if (a.mx) {  // x as its two-term E2M3 split for the scaled W13 GEMM
     const long n = (long)a.T * (a.H / 32);
-    MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.x,
+    MOE_LAUNCH_AS("k_quant_x", mx::k_quant_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, sd, a.x,
                   a.XQ, a.XS, (long)a.T, a.H);
   }
+  if ((err = br.signal(sd, 1)) != hipSuccess) return err;  // ZA (and the split of x) written
+  if ((err = launch_save_x(a, sd)) != hipSuccess) return err;
+  if ((err = launch_tile_map(a, st)) != hipSuccess) return err;
+  if ((err = br.await(st, 1)) != hipSuccess) return err;
   {
     const bool pk = a.W13P != nullptr;
     if (a.mx && a.act == 1)
@@ -744,11 +754,15 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     else
       pk ? launch_w13_sk<false, 0, true>(a, st) : launch_w13_sk<false, 0, false>(a, st);
   }
+  if ((err = br.signal(st, 2)) != hipSuccess) return err;  // h (and its split) written
+  if ((err = br.await(sd, 2)) != hipSuccess) return err;
   if (a.small_tiles)
-    MOE_LAUNCH(k_a2s, dim3(a.maxtiles * (TMG / GA2S::TM), rank_blocks(a.r)), dim3(GA2S::NT), GA2S::LDS_BYTES, st,
+    MOE_LAUNCH(k_a2s, dim3(a.maxtiles * (TMG / GA2S::TM), rank_blocks(a.r)), dim3(GA2S::NT), GA2S::LDS_BYTES, sd,
                a);
   else
-    MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB, rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, st, a);
+    MOE_LAUNCH(k_a2, dim3(a.maxtiles * A2_SUB, rank_blocks(a.r)), dim3(256), GS128::LDS_BYTES, sd, a);
+  const long nzc = (long)a.T * (a.r / 4);
+  MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, sd, a);
   {
     const dim3 g(a.maxtiles * (a.H / GW2::TN)), gs(g.x * (TMG / GW2S::TM));
     if (a.mx && a.W2P != nullptr)
@@ -764,8 +778,8 @@ hipError_t launch_forward(const LayerArgs& a, hipStream_t st) {
     else
       MOE_LAUNCH_AS("k_w2", (k_w2<false, false, false>), g, dim3(GW2::NT), W2_LDS, st, a);
   }
-  const long nzc = (long)a.T * (a.r / 4);
-  MOE_LAUNCH(k_zc, dim3((unsigned)((nzc + 255) / 256)), dim3(256), 0, st, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = br.close()) != hipSuccess) return err;
   MOE_LAUNCH(k_rank_combine, dim3(a.H / GRK::TN, token_tiles(a, GRK::TM)), dim3(GRK::NT), RK_LDS, st, a);
   return hipGetLastError();
 }

@@ -240,6 +240,33 @@ class PerDeviceOnce {
   uint64_t done_ = 0;  // bit d: device d initialised
 };
 
+// The independent branches of one layer call run on a second stream of the
+// device (non-blocking, default priority), ordered against the caller's
+// stream by events: open() makes the branch wait for the caller's stream so
+// far, signal / await order the two at the call's branch points (events
+// 1 .. NEV-1), close() makes the caller's stream wait for all of the branch,
+// so the call's work is complete in the caller's stream order as before.
+// One call at a time holds a device's branch (a host lock from open to
+// close; the destructor closes an open branch).  While the caller's stream
+// is being captured into a graph, when `allow` is false, or if the stream
+// cannot be made, the branch is the caller's stream itself and signal /
+// await do nothing.
+class Branch {
+ public:
+  static constexpr int NEV = 4;
+  hipError_t open(hipStream_t st, bool allow);
+  hipStream_t side() const { return side_; }
+  hipError_t signal(hipStream_t from, int i);
+  hipError_t await(hipStream_t to, int i);
+  hipError_t close();
+  ~Branch() { (void)close(); }
+
+ private:
+  hipStream_t main_ = nullptr, side_ = nullptr;
+  hipEvent_t* ev_ = nullptr;  // the device's events; nullptr: one stream
+  std::unique_lock<std::mutex> lk_;
+};
+
 // Roots of a multi-adapter pool build (na = 1: every route's group is its expert).
 struct PoolRoots {
   int na, k;
@@ -248,7 +275,8 @@ struct PoolRoots {
 hipError_t launch_build_pool(const int32_t* idx, int nroutes, int E, int bm, long cap,
                              int32_t* counts, int32_t* offsets, int32_t* r2row, int32_t* row2r,
                              int32_t* err, const PoolRoots& pr, hipStream_t st);
-hipError_t launch_forward(const LayerArgs& a, hipStream_t st);
+// branch = false: every kernel on st (the allocation-free entry)
+hipError_t launch_forward(const LayerArgs& a, hipStream_t st, bool branch = true);
 // two-term E2M3 split of bf16 rows [rows, K] (engine_mx.hpp storage)
 hipError_t launch_split_rows(const uint16_t* src, long rows, int K, uint8_t* codes, uint32_t* scales,
                              hipStream_t st);

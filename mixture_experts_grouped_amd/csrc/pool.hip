@@ -220,8 +220,12 @@ __global__ __launch_bounds__(256) void k_save_x(LayerArgs a) {
   if (i < n) ((u32x4*)a.Xs)[i] = ((const u32x4*)a.x)[i];
 }
 
-hipError_t launch_pool_prologue(const LayerArgs& a, hipStream_t st) {
+hipError_t launch_tile_map(const LayerArgs& a, hipStream_t st) {
   MOE_LAUNCH(k_tile_map, dim3(1), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_save_x(const LayerArgs& a, hipStream_t st) {
   const long n = (long)a.T * a.H / 8;  // H % 256 == 0
   MOE_LAUNCH(k_save_x, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
