@@ -30,6 +30,15 @@
  *   - Outputs are overwritten, never accumulated; empty experts and dropped
  *     routes get exact zeros.
  *   - Calls that share a workspace or outputs must be ordered on one stream.
+ *   - The forward and backward run independent parts of their work on a
+ *     second stream of the device that the library creates on first use
+ *     (non-blocking, default priority), ordered against the caller's stream
+ *     by events: it waits for the caller's stream at the call's start, and
+ *     the caller's stream waits for it before the call's last kernel, so in
+ *     the caller's stream order the call's work is complete as before.
+ *     Calls on one device hold a host lock while they enqueue.  While the
+ *     caller's stream is being captured into a graph, and in
+ *     moe_lora_forward_noalloc, every kernel runs on the caller's stream.
  */
 #ifndef MOELORA_H
 #define MOELORA_H
