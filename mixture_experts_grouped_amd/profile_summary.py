@@ -36,6 +36,16 @@ from typing import Dict, List
 
 from . import build
 
+# Kernels that a layer call runs on its second stream overlap kernels of the
+# caller's stream; a traced duration then includes time shared with them.
+OVERLAP_NOTE = ("Kernels of a call's second stream (forward: k_shrink, k_shrink_sum, k_save_x, k_quant_x "
+                "beside k_tile_map; k_a2/k_a2s, k_zc beside k_w2. Backward: k_gather_za and k_transpose "
+                "beside k_q and the W2 dgrad; below 768 routes per pool group also k_p13/k_p13s, k_pc, "
+                "k_wgrad_local, k_wgrad_shared, k_reduce_shared beside k_w13dgrad) run concurrently with "
+                "those of the caller's stream: their durations include time shared with them, and the "
+                "durations add up to more than the step.")
+
+
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration copies this many bytes per launch
 
 
@@ -150,7 +160,7 @@ def sweep_table(sweep_json: str, adapters_json: str, out: str, commands: str) ->
         t += ["F+B: median of three rounds of ten steps (wall clock around the rounds). Weight reads: the "
               "active experts' W13 + W2 (50.3 MB bf16 each) once in the forward and once in the backward, "
               "over the F+B time, against 8 TB/s. Kernel times: the library's HIP-event trace, a pass of "
-              "its own (10 steps).", "",
+              "its own (10 steps). " + OVERLAP_NOTE, "",
               "| T | routes | experts | F+B ms | weight GB/s | of 8 TB/s | floor ms | four base GEMMs us | "
               "other kernels us | largest other kernels (us) |", "|---|---|---|---|---|---|---|---|---|---|"]
         for r in d["sweep"]:
@@ -207,6 +217,7 @@ def main() -> None:
         lines += ["Commands (run from the repository root on one MI355X, `$R` = the repository path):",
                   "", "```", args.commands.strip(), "```", ""]
     lines += [f"Build hash: `{build.source_hash()}` (device sources, ABI header, compile flags).", "",
+              OVERLAP_NOTE, "",
               "| kernel | calls | total us | average us | % of GPU time |", "|---|---|---|---|---|"]
     for e in stats:
         lines.append(f"| {e['kernel']} | {e['calls']} | {e['total_ns'] / 1e3:.0f} | {e['avg_us']:.1f} | "
