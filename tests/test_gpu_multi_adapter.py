@@ -9,7 +9,8 @@ equal to the adapters run one after another), through the C ABI:
 
 Roots follow the page's workloads: uniform roots, unequal ones (257 and 129
 tokens), an empty root, sixteen adapters; a root longer than the
-shared-gradient chunk (1024 tokens); an MXFP4 base.
+shared-gradient chunk (1024 tokens); roots on the 384-row W13 tiles; a pass
+of a few tokens (the few-route P product); an MXFP4 base.
 """
 import numpy as np
 import pytest
@@ -37,6 +38,11 @@ CASES = {
     # in the pass and in each root's own call
     "large_tiles_two_roots": (I.Shape(T=3200, H=512, I=256, E=4, topk=2, rank=16, scale=1.0),
                               (0, 1600, 3200), 0.0),
+    # 24 routes for 48 (expert, adapter) groups: the pass takes the few-route
+    # P product on B1^T / B3^T copies of the groups with rows; each root's own
+    # call (10 and 14 routes for 16 experts) the plain one
+    "few_routes_three_roots": (I.Shape(T=12, H=512, I=256, E=16, topk=2, rank=8, scale=1.0),
+                               (0, 5, 5, 12), 0.0),
 }
 
 
