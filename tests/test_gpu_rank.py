@@ -8,7 +8,10 @@ and 32; the layer's boundary takes any rank up to 256), through the C ABI:
   zero-padded by hand and the gradients cut back (the padding adds exact
   zeros and nothing else);
 - ranks 1 and 200 with four adapters in one pass, against the multi-adapter
-  oracle.
+  oracle;
+- ranks 4 and 200 with fewer routes than pool groups (the few-route P
+  product), against the oracle and bitwise against the same tokens in a
+  larger batch.
 """
 import numpy as np
 import pytest
@@ -99,3 +102,25 @@ def test_rank_above_128_with_few_rows_per_expert(rank, transformed):
     res = Hn.GpuRun(shape, case, transformed=transformed).run()
     ref_out, ref_g = Hn.oracle_run(case, shape.scale)
     Hn.compare_all(res, ref_out, ref_g, tag=f"r{rank}:T40:")
+
+
+@pytest.mark.parametrize("rank", [4, 200])
+def test_rank_with_fewer_routes_than_groups(rank):
+    """Three tokens over 16 experts (6 routes, at most half as many as the
+    groups): the P product runs on the B1^T / B3^T copies of the groups with
+    rows (k_p13s), at a padded rank and at a rank of two column blocks (the
+    second ragged): every output against the oracle, and the same tokens
+    inside a batch of 200 (the plain P product) bitwise."""
+    shape = I.Shape(T=3, H=512, I=256, E=16, topk=2, rank=rank, scale=1.0)
+    big_shape = I.Shape(T=200, H=512, I=256, E=16, topk=2, rank=rank, scale=1.0)
+    big_case = I.layer_inputs(big_shape, (73, rank), mask_prob=0.0)
+    case = dict(big_case)
+    for n in ("x", "grad_out", "topk_idx", "topk_w"):
+        case[n] = np.ascontiguousarray(big_case[n][:3])
+    Hn.log(f"[rank] three tokens, r={rank}")
+    res = Hn.GpuRun(shape, case).run(fill=(0xFF,))
+    ref_out, ref_g = Hn.oracle_run(case, shape.scale)
+    Hn.compare_all(res, ref_out, ref_g, tag=f"r{rank}:T3:")
+    big = Hn.GpuRun(big_shape, big_case).run()
+    for n in ("out", "grad_x", "grad_w"):
+        assert Hn.same_bits(res[n], np.ascontiguousarray(big[n][:3])), n
